@@ -1,0 +1,44 @@
+"""Ternary {-1, 0, +1} weights with a per-row scale (oracle).  Test infrastructure only.
+
+[BitNet] "Hệ Thống Trọng Số Ternary": each parameter takes one of the three
+values -1, 0, +1 (about 1.58 bits); EWQ ([EWQ] step 2) names 1.58-bit as the
+aggressive option for its lowest-entropy blocks.  The page's own weight
+formula, Sign(W - alpha) with alpha the mean, yields only +-1, and its
+BitLinear scale beta is described only as a factor that reduces the
+approximation error.  Reading used here, the plainest closed form that keeps
+the three values and a per-row scale: beta_i = mean_j |W_ij| (no centring),
+q = clamp(rne(W_ij / beta_i), -1, 1), stored as the 2-bit code q + 1, LSB-first
+as in ``rtn.pack_codes``.  A row with beta = 0 gets q = 0.
+
+beta is a mean over the row, so it is computed in fp64 and rounded once to
+fp32; the code decision is taken in fp32 as w * (1/beta) with the reciprocal
+correctly rounded, matching the kernels.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F32 = np.float32
+
+
+def ternary_quantize(w, beta=None):
+    """Return (q in {-1,0,1} int8 [rows, cols], beta fp32 [rows]).
+
+    ``beta`` may be given (stage isolation: decide codes from another
+    implementation's scale); otherwise it is mean |W| per row.
+    """
+    a = np.asarray(w)
+    if beta is None:
+        beta = np.mean(np.abs(a.astype(np.float64)), axis=1).astype(F32)
+    beta = np.asarray(beta, dtype=F32)
+    x = a.astype(F32)
+    with np.errstate(divide="ignore", over="ignore", invalid="ignore"):
+        inv = (F32(1.0) / beta).astype(F32)
+        ok = np.isfinite(inv)
+        q = np.clip(np.rint(x * np.where(ok, inv, F32(0))[:, None]), -1, 1)
+    q = np.where(ok[:, None], q, 0)
+    return q.astype(np.int8), beta
+
+
+def ternary_dequantize(q, beta) -> np.ndarray:
+    return (np.asarray(q, dtype=F32) * np.asarray(beta, dtype=F32)[:, None]).astype(F32)

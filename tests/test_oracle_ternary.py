@@ -1,0 +1,46 @@
+"""Pins for the oracle's ternary {-1, 0, +1} per-row-scale quantiser."""
+import numpy as np
+import torch
+
+import oracle
+import woqdata
+
+
+def test_codes_and_values():
+    w = woqdata.random_matrix(32, 256, 3).float().numpy()
+    q, beta = oracle.ternary_quantize(w)
+    assert set(np.unique(q).tolist()) <= {-1, 0, 1}
+    # beta = mean |W| per row (checked with torch's mean/abs)
+    ref = torch.from_numpy(w).double().abs().mean(dim=1).float().numpy()
+    assert np.array_equal(beta, ref)
+    deq = oracle.ternary_dequantize(q, beta)
+    for i in range(32):
+        assert set(np.unique(deq[i]).tolist()) <= {-beta[i], 0.0, beta[i]}
+
+
+def test_brute_force_argmin():
+    w = woqdata.random_matrix(8, 64, 4).float().numpy()
+    q, beta = oracle.ternary_quantize(w)
+    for i in range(8):
+        for j in range(64):
+            errs = {c: abs(float(w[i, j]) - c * float(beta[i])) for c in (-1, 0, 1)}
+            best = min(errs.values())
+            assert errs[int(q[i, j])] <= best * (1 + 1e-6) + 1e-12
+
+
+def test_exact_half_rounds_to_zero_and_clamps():
+    beta = np.array([1.0], dtype=np.float32)
+    w = np.array([[0.5, -0.5, 0.5000001, 1.5, -7.0, 0.0]], dtype=np.float32)
+    q, _ = oracle.ternary_quantize(w, beta)
+    assert q.tolist() == [[0, 0, 1, 1, -1, 0]]
+
+
+def test_zero_row():
+    w = np.zeros((2, 16), dtype=np.float32)
+    w[1, :4] = [0.2, -0.4, 0.0, 0.1]
+    q, beta = oracle.ternary_quantize(w)
+    assert beta[0] == 0 and np.all(q[0] == 0)
+    assert beta[1] == np.float32(np.mean(np.abs(w[1].astype(np.float64))))
+    # codes q + 1 pack as 2-bit LSB-first
+    packed = oracle.pack_codes((q + 1).astype(np.uint8), 2)
+    assert packed.shape == (2, 4) and packed[0].tobytes() == bytes([0x55] * 4)

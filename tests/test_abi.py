@@ -1,0 +1,115 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects invalid arguments on the host before any HIP
+call (no compute is launched here; no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from weight_only_quantization_softmax_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "woq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libwoq.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_five_entry_points():
+    names = _declared()
+    for n in ("ewq_block_entropy", "sinq_balance", "quant_pack_groupwise", "dequant_unpack",
+              "ternary_pack"):
+        assert n in names
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = _lib.load()
+    for code in range(0, 11):
+        s = lib.woq_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.woq_status_string(99).decode() == "unknown status"
+
+
+FAKE = 0x10000  # 16-byte aligned non-null address; never dereferenced
+
+
+def _mat(rows=16, cols=64, dtype=_lib.WOQ_BF16, ptr=FAKE):
+    return _lib.mat_array([(ptr, dtype, rows, cols)])
+
+
+def _ws_size(op, mats, n=1, group=0):
+    out = ctypes.c_size_t(0)
+    st = _lib.load().woq_workspace_size(op, mats, n, group, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_size_and_validation():
+    st, b = _ws_size(_lib.OP_ENTROPY, _mat())
+    assert st == 0 and b >= 65536 * 4
+    st, b = _ws_size(_lib.OP_SINQ, _mat())
+    assert st == 0 and b > 0
+    assert _ws_size(_lib.OP_QUANT, _mat(), group=64)[0] == 0
+    assert _ws_size(_lib.OP_QUANT, _mat(cols=64), group=40)[0] == 2   # 64 % 40
+    assert _ws_size(_lib.OP_QUANT, _mat(cols=64), group=12)[0] == 2   # not a multiple of 8
+    assert _ws_size(_lib.OP_SINQ, _mat(cols=60))[0] == 2               # cols % 8
+    assert _ws_size(_lib.OP_ENTROPY, _mat(cols=60))[0] == 0            # any size
+    assert _ws_size(_lib.OP_ENTROPY, _mat(dtype=7))[0] == 3
+    assert _ws_size(_lib.OP_ENTROPY, _mat(ptr=FAKE + 4))[0] == 9
+    assert _ws_size(_lib.OP_ENTROPY, _mat(ptr=0))[0] == 1
+    assert _ws_size(_lib.OP_ENTROPY, _mat(rows=1 << 16, cols=1 << 15))[0] == 2
+    assert _ws_size(99, _mat())[0] == 2
+
+
+def test_entry_points_reject_before_any_hip_call():
+    lib = _lib.load()
+    m = _mat()
+    nullpp = None
+    one = (ctypes.c_void_p * 1)(FAKE)
+    pp = ctypes.cast(one, _lib.PP)
+    # entropy: NULL matrices, NULL h_mat, bad block ids, empty block, tiny workspace
+    assert lib.ewq_block_entropy(None, 1, None, 1, 1.0, FAKE, None, None, None, None, FAKE, 1 << 30, None) == 1
+    assert lib.ewq_block_entropy(m, 1, None, 1, 1.0, None, None, None, None, None, FAKE, 1 << 30, None) == 1
+    assert lib.ewq_block_entropy(m, 1, None, 2, 1.0, FAKE, None, None, None, None, FAKE, 1 << 30, None) == 7
+    bid = (ctypes.c_int32 * 1)(3)
+    assert lib.ewq_block_entropy(m, 1, bid, 2, 1.0, FAKE, None, None, None, None, FAKE, 1 << 30, None) == 7
+    bid = (ctypes.c_int32 * 1)(0)
+    assert lib.ewq_block_entropy(m, 1, bid, 2, 1.0, FAKE, None, None, None, None, FAKE, 1 << 30, None) == 7
+    assert lib.ewq_block_entropy(m, 1, None, 0, 1.0, FAKE, None, None, None, None, FAKE, 1 << 30, None) == 10
+    assert lib.ewq_block_entropy(m, 0, None, 1, 1.0, FAKE, None, None, None, None, FAKE, 1 << 30, None) == 10
+    assert lib.ewq_block_entropy(m, 1, None, 1, 1.0, FAKE, None, None, None, None, FAKE, 16, None) == 6
+    assert lib.ewq_block_entropy(m, 1, None, 1, 1.0, FAKE, None, None, None, None, None, 1 << 30, None) == 6
+    assert lib.ewq_block_entropy(m, 1, None, 1, 1.0, FAKE, None, None, None, None, FAKE + 16, 1 << 30, None) == 6
+    # sinq: iters out of range, NULL scale arrays, cols % 8
+    assert lib.sinq_balance(m, 1, -1, pp, pp, FAKE, 1 << 30, None) == 5
+    assert lib.sinq_balance(m, 1, 5000, pp, pp, FAKE, 1 << 30, None) == 5
+    assert lib.sinq_balance(m, 1, 4, nullpp, pp, FAKE, 1 << 30, None) == 1
+    assert lib.sinq_balance(_mat(cols=20), 1, 4, pp, pp, FAKE, 1 << 30, None) == 2
+    assert lib.sinq_balance(m, 1, 4, pp, pp, FAKE, 8, None) == 6
+    # quant: bits, group, NULL outputs
+    assert lib.quant_pack_groupwise(m, 1, None, None, 5, 64, pp, pp, pp, FAKE, 1 << 30, None) == 4
+    assert lib.quant_pack_groupwise(m, 1, None, None, 4, 24, pp, pp, pp, FAKE, 1 << 30, None) == 2
+    assert lib.quant_pack_groupwise(m, 1, None, None, 4, -8, pp, pp, pp, FAKE, 1 << 30, None) == 2
+    assert lib.quant_pack_groupwise(m, 1, None, None, 4, 64, nullpp, pp, pp, FAKE, 1 << 30, None) == 1
+    assert lib.quant_pack_groupwise(_mat(cols=1 << 16, rows=1), 1, None, None, 8, 0, pp, pp, pp, FAKE, 1 << 30, None) == 2
+    assert lib.quant_pack_groupwise(m, 1, None, None, 4, 64, pp, pp, pp, FAKE, 64, None) == 6
+    # dequant / ternary
+    assert lib.dequant_unpack(m, 1, pp, pp, None, None, None, 3, 64, FAKE, 8, None) == 6
+    assert lib.dequant_unpack(m, 1, nullpp, pp, None, None, None, 4, 64, FAKE, 1 << 30, None) == 1
+    assert lib.dequant_unpack(m, 1, pp, pp, None, None, None, 1, 64, FAKE, 1 << 30, None) == 4
+    assert lib.ternary_pack(m, 1, nullpp, pp, FAKE, 1 << 30, None) == 1
+    assert lib.ternary_pack(_mat(cols=1 << 16, rows=1), 1, pp, pp, FAKE, 1 << 30, None) == 2
+    assert lib.ternary_pack(m, 1, pp, pp, FAKE, 4, None) == 6

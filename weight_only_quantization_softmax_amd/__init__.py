@@ -1,0 +1,172 @@
+"""MI355X-native calibration-free weight-quantisation pass.
+
+Python binding over libwoq.so (hand-written HIP kernels for gfx950 behind the
+C ABI of include/woq.h).  Each function has the name of the C entry point it
+wraps and does argument marshalling only: torch tensors provide device memory
+and the current HIP stream; every step of the pass runs in the library's
+kernels.  There is no CPU or PyTorch fallback: if libwoq.so is missing the
+calls raise.
+
+  ewq_block_entropy     EWQ per-matrix softmax entropy, block entropy, tiers
+  sinq_balance          SINQ dual-axis Sinkhorn std balancing -> (s, t)
+  quant_pack_groupwise  group-wise asymmetric RTN with LSB-first bit packing
+  dequant_unpack        inverse map (codes -> weights)
+  ternary_pack          ternary {-1, 0, +1} codes with a per-row scale
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import WoqError  # noqa: F401
+
+__all__ = ["ewq_block_entropy", "sinq_balance", "quant_pack_groupwise",
+           "dequant_unpack", "ternary_pack", "workspace_size", "WoqError"]
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _lib.WOQ_BF16
+    if t.dtype == torch.float32:
+        return _lib.WOQ_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _mats(tensors: Sequence[torch.Tensor]):
+    for t in tensors:
+        if t.dim() != 2 or not t.is_contiguous():
+            raise ValueError("matrices must be 2-D and contiguous")
+    return _lib.mat_array((t.data_ptr(), _dtype_code(t), t.shape[0], t.shape[1])
+                          for t in tensors)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptrs(ts):
+    if ts is None:
+        return None
+    return _lib.ptr_array(None if t is None else t.data_ptr() for t in ts)
+
+
+def workspace_size(op: int, mats: Sequence[torch.Tensor], group: int = 0) -> int:
+    lib = _lib.load()
+    arr = _mats(mats)
+    out = ctypes.c_size_t(0)
+    _lib.check("woq_workspace_size", lib.woq_workspace_size(op, arr, len(mats), group,
+                                                             ctypes.byref(out)))
+    return out.value
+
+
+def _workspace(op, mats, group, ws, device):
+    need = workspace_size(op, mats, group)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return ws
+
+
+def ewq_block_entropy(mats: Sequence[torch.Tensor], block_id: Optional[Sequence[int]] = None,
+                      n_blocks: int = 1, x: float = 1.0, *, ws=None, stream=None):
+    """Per-matrix entropy, block entropy, (mu, sigma, T), tiers and order (device tensors)."""
+    lib = _lib.load()
+    dev = mats[0].device
+    arr = _mats(mats)
+    n = len(mats)
+    h_mat = torch.empty(n, dtype=torch.float64, device=dev)
+    h_block = torch.empty(n_blocks, dtype=torch.float64, device=dev)
+    stats = torch.empty(3, dtype=torch.float64, device=dev)
+    tier = torch.empty(n_blocks, dtype=torch.int32, device=dev)
+    order = torch.empty(n_blocks, dtype=torch.int32, device=dev)
+    ws = _workspace(_lib.OP_ENTROPY, mats, 0, ws, dev)
+    bid = None
+    if block_id is not None:
+        bid = (ctypes.c_int32 * n)(*[int(b) for b in block_id])
+    st = lib.ewq_block_entropy(arr, n, bid, n_blocks, float(x), h_mat.data_ptr(),
+                               h_block.data_ptr(), stats.data_ptr(), tier.data_ptr(),
+                               order.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream))
+    _lib.check("ewq_block_entropy", st)
+    return {"h_mat": h_mat, "h_block": h_block, "stats": stats, "tier": tier, "order": order}
+
+
+def sinq_balance(mats: Sequence[torch.Tensor], iters: int, *, row_scale=None, col_scale=None,
+                 ws=None, stream=None):
+    """Row scales s [rows] and column scales t [cols] (fp32) per matrix."""
+    lib = _lib.load()
+    dev = mats[0].device
+    arr = _mats(mats)
+    if row_scale is None:
+        row_scale = [torch.empty(m.shape[0], dtype=torch.float32, device=dev) for m in mats]
+    if col_scale is None:
+        col_scale = [torch.empty(m.shape[1], dtype=torch.float32, device=dev) for m in mats]
+    ws = _workspace(_lib.OP_SINQ, mats, 0, ws, dev)
+    st = lib.sinq_balance(arr, len(mats), int(iters), _ptrs(row_scale), _ptrs(col_scale),
+                          ws.data_ptr(), ws.numel(), _stream(stream))
+    _lib.check("sinq_balance", st)
+    return row_scale, col_scale
+
+
+def quant_pack_groupwise(mats: Sequence[torch.Tensor], bits: int, group: int, *,
+                         row_scale=None, col_scale=None, codes=None, scales=None, zeros=None,
+                         ws=None, stream=None):
+    """Packed codes (uint8 [rows, cols*bits/8]), deltas (fp32) and zero-points (uint8)."""
+    lib = _lib.load()
+    dev = mats[0].device
+    arr = _mats(mats)
+
+    def g(m):
+        return group if group else m.shape[1]
+    if codes is None:
+        codes = [torch.empty(m.shape[0], m.shape[1] * bits // 8, dtype=torch.uint8, device=dev)
+                 for m in mats]
+    if scales is None:
+        scales = [torch.empty(m.shape[0], m.shape[1] // g(m), dtype=torch.float32, device=dev)
+                  for m in mats]
+    if zeros is None:
+        zeros = [torch.empty(m.shape[0], m.shape[1] // g(m), dtype=torch.uint8, device=dev)
+                 for m in mats]
+    ws = _workspace(_lib.OP_QUANT, mats, group, ws, dev)
+    st = lib.quant_pack_groupwise(arr, len(mats), _ptrs(row_scale), _ptrs(col_scale), int(bits),
+                                  int(group), _ptrs(codes), _ptrs(scales), _ptrs(zeros),
+                                  ws.data_ptr(), ws.numel(), _stream(stream))
+    _lib.check("quant_pack_groupwise", st)
+    return codes, scales, zeros
+
+
+def dequant_unpack(shapes, codes, scales, bits: int, group: int, *, zeros=None, row_scale=None,
+                   col_scale=None, out_dtype=torch.float32, out=None, ws=None, stream=None):
+    """Decode packed codes back to weights W' = (((q - z) delta) s_i) t_j."""
+    lib = _lib.load()
+    dev = codes[0].device
+    if out is None:
+        out = [torch.empty(r, c, dtype=out_dtype, device=dev) for (r, c) in shapes]
+    arr = _mats(out)
+    ws = _workspace(_lib.OP_DEQUANT, out, group, ws, dev)
+    st = lib.dequant_unpack(arr, len(out), _ptrs(codes), _ptrs(scales), _ptrs(zeros),
+                            _ptrs(row_scale), _ptrs(col_scale), int(bits), int(group),
+                            ws.data_ptr(), ws.numel(), _stream(stream))
+    _lib.check("dequant_unpack", st)
+    return out
+
+
+def ternary_pack(mats: Sequence[torch.Tensor], *, codes=None, row_scale=None, ws=None,
+                 stream=None):
+    """2-bit ternary codes (q + 1) and per-row beta."""
+    lib = _lib.load()
+    dev = mats[0].device
+    arr = _mats(mats)
+    if codes is None:
+        codes = [torch.empty(m.shape[0], m.shape[1] // 4, dtype=torch.uint8, device=dev)
+                 for m in mats]
+    if row_scale is None:
+        row_scale = [torch.empty(m.shape[0], dtype=torch.float32, device=dev) for m in mats]
+    ws = _workspace(_lib.OP_TERNARY, mats, 0, ws, dev)
+    st = lib.ternary_pack(arr, len(mats), _ptrs(codes), _ptrs(row_scale), ws.data_ptr(),
+                          ws.numel(), _stream(stream))
+    _lib.check("ternary_pack", st)
+    return codes, row_scale

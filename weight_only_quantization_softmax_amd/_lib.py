@@ -1,0 +1,104 @@
+"""ctypes view of libwoq.so: the C ABI declared in include/woq.h.
+
+Argument marshalling only.  The library must be built in-tree
+(``python -m weight_only_quantization_softmax_amd.build``); there is no
+fallback of any kind when it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwoq.so")
+
+WOQ_OK = 0
+STATUS = {
+    0: "WOQ_OK", 1: "WOQ_ERR_NULL", 2: "WOQ_ERR_SHAPE", 3: "WOQ_ERR_DTYPE",
+    4: "WOQ_ERR_BITS", 5: "WOQ_ERR_ITERS", 6: "WOQ_ERR_WORKSPACE",
+    7: "WOQ_ERR_BLOCK", 8: "WOQ_ERR_HIP", 9: "WOQ_ERR_ALIGN", 10: "WOQ_ERR_COUNT",
+}
+WOQ_F32, WOQ_BF16 = 0, 1
+OP_ENTROPY, OP_SINQ, OP_QUANT, OP_DEQUANT, OP_TERNARY = 1, 2, 3, 4, 5
+
+# every symbol include/woq.h declares
+EXPORTS = ("woq_status_string", "woq_workspace_size", "ewq_block_entropy",
+           "sinq_balance", "quant_pack_groupwise", "dequant_unpack", "ternary_pack")
+
+
+class WoqMat(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64)]
+
+
+class WoqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}")
+
+
+_lib = None
+
+P = ctypes.c_void_p
+PP = ctypes.POINTER(ctypes.c_void_p)
+I32 = ctypes.c_int32
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m weight_only_quantization_softmax_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.woq_status_string.argtypes = [I32]
+    lib.woq_status_string.restype = ctypes.c_char_p
+    lib.woq_workspace_size.argtypes = [I32, ctypes.POINTER(WoqMat), I32, I32,
+                                       ctypes.POINTER(ctypes.c_size_t)]
+    lib.woq_workspace_size.restype = I32
+    lib.ewq_block_entropy.argtypes = [ctypes.POINTER(WoqMat), I32, ctypes.POINTER(I32), I32,
+                                      ctypes.c_double, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.ewq_block_entropy.restype = I32
+    lib.sinq_balance.argtypes = [ctypes.POINTER(WoqMat), I32, I32, PP, PP, P, ctypes.c_size_t, P]
+    lib.sinq_balance.restype = I32
+    lib.quant_pack_groupwise.argtypes = [ctypes.POINTER(WoqMat), I32, PP, PP, I32, I32,
+                                         PP, PP, PP, P, ctypes.c_size_t, P]
+    lib.quant_pack_groupwise.restype = I32
+    lib.dequant_unpack.argtypes = [ctypes.POINTER(WoqMat), I32, PP, PP, PP, PP, PP, I32, I32,
+                                   P, ctypes.c_size_t, P]
+    lib.dequant_unpack.restype = I32
+    lib.ternary_pack.argtypes = [ctypes.POINTER(WoqMat), I32, PP, PP, P, ctypes.c_size_t, P]
+    lib.ternary_pack.restype = I32
+    _lib = lib
+    return lib
+
+
+def check(fn: str, status: int) -> None:
+    if status != WOQ_OK:
+        raise WoqError(fn, status)
+
+
+def mat_array(descs):
+    """descs: iterable of (data_ptr, dtype, rows, cols) -> ctypes WoqMat array."""
+    descs = list(descs)
+    arr = (WoqMat * len(descs))()
+    for i, (ptr, dt, r, c) in enumerate(descs):
+        arr[i].data = ptr
+        arr[i].dtype = dt
+        arr[i].reserved = 0
+        arr[i].rows = r
+        arr[i].cols = c
+    return arr
+
+
+def ptr_array(ptrs):
+    """Host array of device pointers (None entries become NULL); None -> NULL array."""
+    if ptrs is None:
+        return None
+    ptrs = list(ptrs)
+    arr = (ctypes.c_void_p * len(ptrs))()
+    for i, p in enumerate(ptrs):
+        arr[i] = p
+    return ctypes.cast(arr, PP)

@@ -1,0 +1,520 @@
+// C-ABI entry points of libwoq: argument validation, workspace layout,
+// descriptor staging and kernel sequencing on the caller's stream.
+//
+// Every argument check runs on the host before the first HIP call, so an
+// invalid call enqueues nothing.  Descriptor tables are built in host memory
+// and copied into the head of the caller's workspace with one
+// hipMemcpyAsync (pageable source: the runtime stages it before returning,
+// so the host vector may go out of scope).  The rest of the workspace holds
+// per-call scratch (histograms, reciprocal scales, Sinkhorn partials).
+#include "launch.h"
+
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+using namespace woq;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
+constexpr int32_t kMaxMats = 1 << 20;
+constexpr int32_t kMaxBlocks = 4096;
+constexpr int32_t kMaxIters = 4096;
+constexpr int kSinqChunkRows = 128;
+
+size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+struct Arena {
+    size_t off = 0;
+    size_t take(size_t bytes, size_t a = kAlign) {
+        off = align_up(off, a);
+        const size_t o = off;
+        off += bytes;
+        return o;
+    }
+    size_t end() const { return align_up(off); }
+};
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int32_t check_mats(const woq_mat* mats, int32_t n, bool cols8) {
+    if (!mats) return WOQ_ERR_NULL;
+    if (n < 1 || n > kMaxMats) return WOQ_ERR_COUNT;
+    for (int32_t i = 0; i < n; ++i) {
+        const woq_mat& m = mats[i];
+        if (!m.data) return WOQ_ERR_NULL;
+        if (m.dtype != WOQ_F32 && m.dtype != WOQ_BF16) return WOQ_ERR_DTYPE;
+        if (m.reserved != 0 || m.rows < 1 || m.cols < 1) return WOQ_ERR_SHAPE;
+        if (m.rows > kMaxElems / m.cols) return WOQ_ERR_SHAPE;
+        if (cols8 && (m.cols % 8)) return WOQ_ERR_SHAPE;
+        if (!aligned(m.data, 16)) return WOQ_ERR_ALIGN;
+    }
+    return WOQ_OK;
+}
+
+int32_t check_ptrs(const void* const* arr, int32_t n, size_t align) {
+    if (!arr) return WOQ_ERR_NULL;
+    for (int32_t i = 0; i < n; ++i) {
+        if (!arr[i]) return WOQ_ERR_NULL;
+        if (!aligned(arr[i], align)) return WOQ_ERR_ALIGN;
+    }
+    return WOQ_OK;
+}
+
+int32_t check_opt_ptrs(const void* const* arr, int32_t n, size_t align) {
+    if (!arr) return WOQ_OK;
+    for (int32_t i = 0; i < n; ++i)
+        if (arr[i] && !aligned(arr[i], align)) return WOQ_ERR_ALIGN;
+    return WOQ_OK;
+}
+
+int32_t check_ws(const void* ws, size_t ws_bytes, size_t need) {
+    if (!ws || !aligned(ws, kAlign) || ws_bytes < need) return WOQ_ERR_WORKSPACE;
+    return WOQ_OK;
+}
+
+int64_t elems(const woq_mat& m) { return m.rows * m.cols; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+template <class T>
+T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
+
+// ------------------------------------------------------------------ entropy
+struct EntLayout {
+    int nb = 0, nf = 0;
+    int64_t units_b = 0, units_f = 0;
+    size_t tab_b, ubeg_b, tab_f, ubeg_f, bmats, bbeg, nsz, table_end;
+    size_t hb, keys, part_f, ghist, total;
+};
+
+EntLayout ent_layout(const woq_mat* mats, int32_t n, int32_t n_blocks) {
+    EntLayout L;
+    for (int32_t i = 0; i < n; ++i) {
+        if (mats[i].dtype == WOQ_BF16) { ++L.nb; L.units_b += cdiv(elems(mats[i]), kEntChunk); }
+        else { ++L.nf; L.units_f += cdiv(elems(mats[i]), kEntChunk); }
+    }
+    Arena a;
+    L.tab_b = a.take(sizeof(EntMat) * L.nb);
+    L.ubeg_b = a.take(sizeof(int64_t) * (L.nb + 1));
+    L.tab_f = a.take(sizeof(EntMat) * L.nf);
+    L.ubeg_f = a.take(sizeof(int64_t) * (L.nf + 1));
+    L.bmats = a.take(sizeof(int32_t) * n);
+    L.bbeg = a.take(sizeof(int32_t) * (n_blocks + 1));
+    L.nsz = a.take(sizeof(double) * n);
+    L.table_end = a.end();
+    L.hb = a.take(sizeof(double) * n_blocks);
+    L.keys = a.take(sizeof(uint32_t) * 2 * L.nf);
+    L.part_f = a.take(sizeof(double2) * L.units_f);
+    L.ghist = a.take(sizeof(uint32_t) * 65536 * (size_t)std::min(L.nb, kHistSlots));
+    L.total = a.end();
+    return L;
+}
+
+// ------------------------------------------------------------------ sinkhorn
+struct SinqLayout {
+    size_t tab, ubeg_r, ubeg_cp, ubeg_cf, table_end, total;
+    std::vector<size_t> v, u, part;
+    int64_t units_r = 0, units_cp = 0, units_cf = 0;
+};
+
+int32_t sinq_chunks(const woq_mat& m) { return (int32_t)cdiv(m.rows, kSinqChunkRows); }
+int32_t sinq_tiles(const woq_mat& m) { return (int32_t)cdiv(m.cols / 8, 256); }
+
+SinqLayout sinq_layout(const woq_mat* mats, int32_t n) {
+    SinqLayout L;
+    Arena a;
+    L.tab = a.take(sizeof(SinqMat) * n);
+    L.ubeg_r = a.take(sizeof(int64_t) * (n + 1));
+    L.ubeg_cp = a.take(sizeof(int64_t) * (n + 1));
+    L.ubeg_cf = a.take(sizeof(int64_t) * (n + 1));
+    L.table_end = a.end();
+    L.v.resize(n); L.u.resize(n); L.part.resize(n);
+    for (int32_t i = 0; i < n; ++i) {
+        const woq_mat& m = mats[i];
+        L.v[i] = a.take(sizeof(float) * m.rows, 64);
+        L.u[i] = a.take(sizeof(float) * m.cols, 64);
+        L.part[i] = a.take(sizeof(float2) * (size_t)sinq_chunks(m) * m.cols, 64);
+        L.units_r += cdiv(m.rows, 4);
+        L.units_cp += (int64_t)sinq_chunks(m) * sinq_tiles(m);
+        L.units_cf += cdiv(m.cols, 256);
+    }
+    L.total = a.end();
+    return L;
+}
+
+// ------------------------------------------------------------------ quant
+bool small_group(int32_t g) { return g >= 8 && g <= 512 && (g & (g - 1)) == 0; }
+
+int32_t eff_group(const woq_mat& m, int32_t group) { return group ? group : (int32_t)m.cols; }
+
+// group == 0 means one group per row.  quant additionally bounds large groups
+// by what one workgroup keeps in registers.
+int32_t check_group(const woq_mat* mats, int32_t n, int32_t group, bool quant) {
+    if (group < 0 || (group && (group < 8 || group % 8))) return WOQ_ERR_SHAPE;
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t g = eff_group(mats[i], group);
+        if (mats[i].cols % g) return WOQ_ERR_SHAPE;
+        if (quant && !(group && small_group(group))) {
+            const int32_t lim = mats[i].dtype == WOQ_BF16 ? 32768 : 16384;
+            if (g > lim) return WOQ_ERR_SHAPE;
+        }
+    }
+    return WOQ_OK;
+}
+
+// Matrices are split into a bf16 list and an f32 list (one launch each).
+struct QLayout {
+    int nb = 0, nf = 0;
+    size_t tab_b, ubeg_b, tab_f, ubeg_f, segs, ubeg_s, table_end, total;
+    int64_t units_b = 0, units_f = 0, units_s = 0;
+    int nseg = 0;
+    std::vector<size_t> rs, ct;  // per matrix, 0 = none
+};
+
+// op: 0 quant, 1 dequant, 2 ternary
+QLayout q_layout(const woq_mat* mats, int32_t n, int op, int32_t group,
+                 const float* const* row_scale, const float* const* col_scale) {
+    QLayout L;
+    auto units = [&](const woq_mat& m) -> int64_t {
+        if (op == 2) return m.rows;
+        if (op == 0 && !(group && small_group(group))) return elems(m) / eff_group(m, group);
+        return cdiv(elems(m), kQTile);
+    };
+    for (int32_t i = 0; i < n; ++i) {
+        if (mats[i].dtype == WOQ_BF16) { ++L.nb; L.units_b += units(mats[i]); }
+        else { ++L.nf; L.units_f += units(mats[i]); }
+    }
+    L.rs.assign(n, 0);
+    L.ct.assign(n, 0);
+    if (op == 0) {
+        for (int32_t i = 0; i < n; ++i) {
+            if (row_scale && row_scale[i]) { ++L.nseg; L.units_s += cdiv(mats[i].rows, 256); }
+            if (col_scale && col_scale[i]) { ++L.nseg; L.units_s += cdiv(mats[i].cols, 256); }
+        }
+    }
+    Arena a;
+    L.tab_b = a.take(sizeof(QMat) * L.nb);
+    L.ubeg_b = a.take(sizeof(int64_t) * (L.nb + 1));
+    L.tab_f = a.take(sizeof(QMat) * L.nf);
+    L.ubeg_f = a.take(sizeof(int64_t) * (L.nf + 1));
+    L.segs = a.take(sizeof(RecipSeg) * L.nseg);
+    L.ubeg_s = a.take(sizeof(int64_t) * (L.nseg + 1));
+    L.table_end = a.end();
+    if (op == 0) {
+        for (int32_t i = 0; i < n; ++i) {
+            if (row_scale && row_scale[i]) L.rs[i] = a.take(sizeof(float) * mats[i].rows, 64);
+            if (col_scale && col_scale[i]) L.ct[i] = a.take(sizeof(float) * mats[i].cols, 64);
+        }
+    }
+    L.total = a.end();
+    return L;
+}
+
+#define WOQ_HIP(call)                                  \
+    do {                                               \
+        if ((call) != hipSuccess) return WOQ_ERR_HIP;  \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* woq_status_string(int32_t s) {
+    switch (s) {
+        case WOQ_OK: return "ok";
+        case WOQ_ERR_NULL: return "required pointer is NULL";
+        case WOQ_ERR_SHAPE: return "shape / group / size constraint violated";
+        case WOQ_ERR_DTYPE: return "unsupported dtype";
+        case WOQ_ERR_BITS: return "bits must be 2, 3, 4 or 8";
+        case WOQ_ERR_ITERS: return "iters out of range";
+        case WOQ_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case WOQ_ERR_BLOCK: return "block id out of range or empty block";
+        case WOQ_ERR_HIP: return "HIP call or kernel launch failed";
+        case WOQ_ERR_ALIGN: return "pointer not sufficiently aligned";
+        case WOQ_ERR_COUNT: return "matrix or block count out of range";
+        default: return "unknown status";
+    }
+}
+
+int32_t woq_workspace_size(int32_t op, const woq_mat* mats, int32_t n_mats, int32_t group,
+                           size_t* bytes) {
+    if (!bytes) return WOQ_ERR_NULL;
+    int32_t st = check_mats(mats, n_mats, op != WOQ_OP_ENTROPY);
+    if (st) return st;
+    switch (op) {
+        case WOQ_OP_ENTROPY: *bytes = ent_layout(mats, n_mats, kMaxBlocks).total; return WOQ_OK;
+        case WOQ_OP_SINQ: *bytes = sinq_layout(mats, n_mats).total; return WOQ_OK;
+        case WOQ_OP_QUANT: {
+            if ((st = check_group(mats, n_mats, group, true))) return st;
+            // worst case: every matrix has both scale vectors
+            std::vector<const float*> dummy(n_mats, reinterpret_cast<const float*>(16));
+            *bytes = q_layout(mats, n_mats, 0, group, dummy.data(), dummy.data()).total;
+            return WOQ_OK;
+        }
+        case WOQ_OP_DEQUANT:
+            if ((st = check_group(mats, n_mats, group, false))) return st;
+            *bytes = q_layout(mats, n_mats, 1, group, nullptr, nullptr).total;
+            return WOQ_OK;
+        case WOQ_OP_TERNARY: *bytes = q_layout(mats, n_mats, 2, 0, nullptr, nullptr).total; return WOQ_OK;
+        default: return WOQ_ERR_SHAPE;
+    }
+}
+
+int32_t ewq_block_entropy(const woq_mat* mats, int32_t n_mats, const int32_t* block_id,
+                          int32_t n_blocks, double x, double* h_mat, double* h_block,
+                          double* stats, int32_t* tier, int32_t* order, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+    int32_t st = check_mats(mats, n_mats, false);
+    if (st) return st;
+    if (!h_mat) return WOQ_ERR_NULL;
+    if (n_blocks < 1 || n_blocks > kMaxBlocks) return WOQ_ERR_COUNT;
+    if (!block_id && n_blocks != 1) return WOQ_ERR_BLOCK;
+    std::vector<int32_t> cnt(n_blocks, 0);
+    for (int32_t i = 0; i < n_mats; ++i) {
+        const int32_t b = block_id ? block_id[i] : 0;
+        if (b < 0 || b >= n_blocks) return WOQ_ERR_BLOCK;
+        ++cnt[b];
+    }
+    for (int32_t b = 0; b < n_blocks; ++b)
+        if (!cnt[b]) return WOQ_ERR_BLOCK;
+    const EntLayout L = ent_layout(mats, n_mats, n_blocks);
+    if ((st = check_ws(ws, ws_bytes, L.total))) return st;
+
+    std::vector<char> host(L.table_end, 0);
+    EntMat* tb = at<EntMat>(host.data(), L.tab_b);
+    EntMat* tf = at<EntMat>(host.data(), L.tab_f);
+    int64_t* ub = at<int64_t>(host.data(), L.ubeg_b);
+    int64_t* uf = at<int64_t>(host.data(), L.ubeg_f);
+    int ib = 0, jf = 0;
+    ub[0] = 0;
+    uf[0] = 0;
+    for (int32_t i = 0; i < n_mats; ++i) {
+        EntMat e{mats[i].data, elems(mats[i]), mats[i].dtype, i};
+        const int64_t u = cdiv(e.n, kEntChunk);
+        if (e.dtype == WOQ_BF16) { tb[ib] = e; ub[ib + 1] = ub[ib] + u; ++ib; }
+        else { tf[jf] = e; uf[jf + 1] = uf[jf] + u; ++jf; }
+    }
+    int32_t* bm = at<int32_t>(host.data(), L.bmats);
+    int32_t* bb = at<int32_t>(host.data(), L.bbeg);
+    double* nsz = at<double>(host.data(), L.nsz);
+    bb[0] = 0;
+    for (int32_t b = 0; b < n_blocks; ++b) bb[b + 1] = bb[b] + cnt[b];
+    std::vector<int32_t> fillp(bb, bb + n_blocks);
+    for (int32_t i = 0; i < n_mats; ++i) {
+        bm[fillp[block_id ? block_id[i] : 0]++] = i;
+        nsz[i] = (double)elems(mats[i]);
+    }
+
+    WOQ_HIP(hipMemcpyAsync(ws, host.data(), L.table_end, hipMemcpyHostToDevice, stream));
+    const EntMat* dtb = at<EntMat>(ws, L.tab_b);
+    const int64_t* dub = at<int64_t>(ws, L.ubeg_b);
+    uint32_t* ghist = at<uint32_t>(ws, L.ghist);
+    for (int b0 = 0; b0 < L.nb; b0 += kHistSlots) {
+        const int b1 = std::min(L.nb, b0 + kHistSlots);
+        WOQ_HIP(fill_u32(ghist, (size_t)(b1 - b0) * 65536, 0u, stream));
+        WOQ_HIP(ent_hist_bf16(dtb + b0, dub + b0, b1 - b0, ub[b0], ub[b1] - ub[b0], ghist, stream));
+        WOQ_HIP(ent_hist_final(dtb + b0, b1 - b0, ghist, h_mat, stream));
+    }
+    if (L.nf)
+        WOQ_HIP(ent_f32(at<EntMat>(ws, L.tab_f), at<int64_t>(ws, L.ubeg_f), L.nf, L.units_f,
+                        at<uint32_t>(ws, L.keys), at<double2>(ws, L.part_f), h_mat, stream));
+    WOQ_HIP(ent_blocks(at<int32_t>(ws, L.bmats), at<int32_t>(ws, L.bbeg), at<double>(ws, L.nsz),
+                       h_mat, n_blocks, x, at<double>(ws, L.hb), h_block, stats, tier, order,
+                       stream));
+    return WOQ_OK;
+}
+
+int32_t sinq_balance(const woq_mat* mats, int32_t n_mats, int32_t iters, float* const* row_scale,
+                     float* const* col_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int32_t st = check_mats(mats, n_mats, true);
+    if (st) return st;
+    if (iters < 0 || iters > kMaxIters) return WOQ_ERR_ITERS;
+    if ((st = check_ptrs(reinterpret_cast<const void* const*>(row_scale), n_mats, 4))) return st;
+    if ((st = check_ptrs(reinterpret_cast<const void* const*>(col_scale), n_mats, 4))) return st;
+    const SinqLayout L = sinq_layout(mats, n_mats);
+    if ((st = check_ws(ws, ws_bytes, L.total))) return st;
+
+    std::vector<char> host(L.table_end, 0);
+    SinqMat* tab = at<SinqMat>(host.data(), L.tab);
+    int64_t* ur = at<int64_t>(host.data(), L.ubeg_r);
+    int64_t* ucp = at<int64_t>(host.data(), L.ubeg_cp);
+    int64_t* ucf = at<int64_t>(host.data(), L.ubeg_cf);
+    ur[0] = ucp[0] = ucf[0] = 0;
+    for (int32_t i = 0; i < n_mats; ++i) {
+        const woq_mat& m = mats[i];
+        SinqMat s;
+        s.data = m.data;
+        s.s = row_scale[i];
+        s.t = col_scale[i];
+        s.v = at<float>(ws, L.v[i]);
+        s.u = at<float>(ws, L.u[i]);
+        s.part = at<float2>(ws, L.part[i]);
+        s.rows = (int32_t)m.rows;
+        s.cols = (int32_t)m.cols;
+        s.dtype = m.dtype;
+        s.n_chunks = sinq_chunks(m);
+        s.chunk_rows = kSinqChunkRows;
+        s.col_tiles = sinq_tiles(m);
+        tab[i] = s;
+        ur[i + 1] = ur[i] + cdiv(m.rows, 4);
+        ucp[i + 1] = ucp[i] + (int64_t)s.n_chunks * s.col_tiles;
+        ucf[i + 1] = ucf[i] + cdiv(m.cols, 256);
+    }
+    WOQ_HIP(hipMemcpyAsync(ws, host.data(), L.table_end, hipMemcpyHostToDevice, stream));
+    const SinqMat* dt = at<SinqMat>(ws, L.tab);
+    if (iters == 0) {
+        for (int32_t i = 0; i < n_mats; ++i) {
+            WOQ_HIP(fill_f32(row_scale[i], (size_t)mats[i].rows, 1.0f, stream));
+            WOQ_HIP(fill_f32(col_scale[i], (size_t)mats[i].cols, 1.0f, stream));
+        }
+        return WOQ_OK;
+    }
+    for (int32_t it = 0; it < iters; ++it) {
+        WOQ_HIP(sinq_rows(dt, at<int64_t>(ws, L.ubeg_r), n_mats, ur[n_mats], it == 0, false, stream));
+        WOQ_HIP(sinq_colpart(dt, at<int64_t>(ws, L.ubeg_cp), n_mats, ucp[n_mats], false, stream));
+        WOQ_HIP(sinq_colfin(dt, at<int64_t>(ws, L.ubeg_cf), n_mats, ucf[n_mats], stream));
+    }
+    return WOQ_OK;
+}
+
+int32_t quant_pack_groupwise(const woq_mat* mats, int32_t n_mats, const float* const* row_scale,
+                             const float* const* col_scale, int32_t bits, int32_t group,
+                             uint8_t* const* codes, float* const* scales, uint8_t* const* zeros,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+    int32_t st = check_mats(mats, n_mats, true);
+    if (st) return st;
+    if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return WOQ_ERR_BITS;
+    if ((st = check_group(mats, n_mats, group, true))) return st;
+    if ((st = check_ptrs(reinterpret_cast<const void* const*>(codes), n_mats, 16))) return st;
+    if ((st = check_ptrs(reinterpret_cast<const void* const*>(scales), n_mats, 4))) return st;
+    if ((st = check_ptrs(reinterpret_cast<const void* const*>(zeros), n_mats, 1))) return st;
+    if ((st = check_opt_ptrs(reinterpret_cast<const void* const*>(row_scale), n_mats, 4))) return st;
+    if ((st = check_opt_ptrs(reinterpret_cast<const void* const*>(col_scale), n_mats, 4))) return st;
+    const QLayout L = q_layout(mats, n_mats, 0, group, row_scale, col_scale);
+    if ((st = check_ws(ws, ws_bytes, L.total))) return st;
+
+    std::vector<char> host(L.table_end, 0);
+    QMat* tb = at<QMat>(host.data(), L.tab_b);
+    QMat* tf = at<QMat>(host.data(), L.tab_f);
+    int64_t* ub = at<int64_t>(host.data(), L.ubeg_b);
+    int64_t* uf = at<int64_t>(host.data(), L.ubeg_f);
+    RecipSeg* sg = at<RecipSeg>(host.data(), L.segs);
+    int64_t* us = at<int64_t>(host.data(), L.ubeg_s);
+    ub[0] = uf[0] = us[0] = 0;
+    int ib = 0, jf = 0, ks = 0;
+    const bool small = group && small_group(group);
+    for (int32_t i = 0; i < n_mats; ++i) {
+        const woq_mat& m = mats[i];
+        QMat q{};
+        q.data = m.data;
+        q.codes = codes[i];
+        q.scales = scales[i];
+        q.zeros = zeros[i];
+        q.rs = L.rs[i] ? at<float>(ws, L.rs[i]) : nullptr;
+        q.ct = L.ct[i] ? at<float>(ws, L.ct[i]) : nullptr;
+        q.rows = (int32_t)m.rows;
+        q.cols = (int32_t)m.cols;
+        q.dtype = m.dtype;
+        q.group = eff_group(m, group);
+        const int64_t u = small ? cdiv(elems(m), kQTile) : elems(m) / q.group;
+        if (m.dtype == WOQ_BF16) { tb[ib] = q; ub[ib + 1] = ub[ib] + u; ++ib; }
+        else { tf[jf] = q; uf[jf + 1] = uf[jf] + u; ++jf; }
+        if (q.rs) { sg[ks] = RecipSeg{row_scale[i], const_cast<float*>(q.rs), m.rows, 0}; us[ks + 1] = us[ks] + cdiv(m.rows, 256); ++ks; }
+        if (q.ct) { sg[ks] = RecipSeg{col_scale[i], const_cast<float*>(q.ct), m.cols, 0}; us[ks + 1] = us[ks] + cdiv(m.cols, 256); ++ks; }
+    }
+    WOQ_HIP(hipMemcpyAsync(ws, host.data(), L.table_end, hipMemcpyHostToDevice, stream));
+    if (L.nseg) WOQ_HIP(recip(at<RecipSeg>(ws, L.segs), at<int64_t>(ws, L.ubeg_s), L.nseg, us[L.nseg], stream));
+    auto launch = [&](size_t tab, size_t ubeg, int nm, int64_t units, int dt) -> hipError_t {
+        if (!nm) return hipSuccess;
+        return small ? quant_small(at<QMat>(ws, tab), at<int64_t>(ws, ubeg), nm, units, dt, bits, stream)
+                     : quant_big(at<QMat>(ws, tab), at<int64_t>(ws, ubeg), nm, units, dt, bits, stream);
+    };
+    WOQ_HIP(launch(L.tab_b, L.ubeg_b, L.nb, ub[L.nb], WOQ_BF16));
+    WOQ_HIP(launch(L.tab_f, L.ubeg_f, L.nf, uf[L.nf], WOQ_F32));
+    return WOQ_OK;
+}
+
+int32_t dequant_unpack(const woq_mat* out, int32_t n_mats, const uint8_t* const* codes,
+                       const float* const* scales, const uint8_t* const* zeros,
+                       const float* const* row_scale, const float* const* col_scale, int32_t bits,
+                       int32_t group, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int32_t st = check_mats(out, n_mats, true);
+    if (st) return st;
+    if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return WOQ_ERR_BITS;
+    if ((st = check_group(out, n_mats, group, false))) return st;
+    if ((st = check_ptrs(reinterpret_cast<const void* const*>(codes), n_mats, 16))) return st;
+    if ((st = check_ptrs(reinterpret_cast<const void* const*>(scales), n_mats, 4))) return st;
+    if ((st = check_opt_ptrs(reinterpret_cast<const void* const*>(row_scale), n_mats, 4))) return st;
+    if ((st = check_opt_ptrs(reinterpret_cast<const void* const*>(col_scale), n_mats, 16))) return st;
+    const QLayout L = q_layout(out, n_mats, 1, group, nullptr, nullptr);
+    if ((st = check_ws(ws, ws_bytes, L.total))) return st;
+
+    std::vector<char> host(L.table_end, 0);
+    QMat* tb = at<QMat>(host.data(), L.tab_b);
+    QMat* tf = at<QMat>(host.data(), L.tab_f);
+    int64_t* ub = at<int64_t>(host.data(), L.ubeg_b);
+    int64_t* uf = at<int64_t>(host.data(), L.ubeg_f);
+    ub[0] = uf[0] = 0;
+    int ib = 0, jf = 0;
+    for (int32_t i = 0; i < n_mats; ++i) {
+        const woq_mat& m = out[i];
+        QMat q{};
+        q.data = m.data;
+        q.codes = const_cast<uint8_t*>(codes[i]);
+        q.scales = const_cast<float*>(scales[i]);
+        q.zeros = zeros ? const_cast<uint8_t*>(zeros[i]) : nullptr;
+        q.rs = row_scale ? row_scale[i] : nullptr;
+        q.ct = col_scale ? col_scale[i] : nullptr;
+        q.rows = (int32_t)m.rows;
+        q.cols = (int32_t)m.cols;
+        q.dtype = m.dtype;
+        q.group = eff_group(m, group);
+        const int64_t u = cdiv(elems(m), kQTile);
+        if (m.dtype == WOQ_BF16) { tb[ib] = q; ub[ib + 1] = ub[ib] + u; ++ib; }
+        else { tf[jf] = q; uf[jf + 1] = uf[jf] + u; ++jf; }
+    }
+    WOQ_HIP(hipMemcpyAsync(ws, host.data(), L.table_end, hipMemcpyHostToDevice, stream));
+    if (L.nb) WOQ_HIP(dequant(at<QMat>(ws, L.tab_b), at<int64_t>(ws, L.ubeg_b), L.nb, ub[L.nb], WOQ_BF16, bits, stream));
+    if (L.nf) WOQ_HIP(dequant(at<QMat>(ws, L.tab_f), at<int64_t>(ws, L.ubeg_f), L.nf, uf[L.nf], WOQ_F32, bits, stream));
+    return WOQ_OK;
+}
+
+int32_t ternary_pack(const woq_mat* mats, int32_t n_mats, uint8_t* const* codes,
+                     float* const* row_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int32_t st = check_mats(mats, n_mats, true);
+    if (st) return st;
+    for (int32_t i = 0; i < n_mats; ++i)
+        if (mats[i].cols > (mats[i].dtype == WOQ_BF16 ? 32768 : 16384)) return WOQ_ERR_SHAPE;
+    if ((st = check_ptrs(reinterpret_cast<const void* const*>(codes), n_mats, 16))) return st;
+    if ((st = check_ptrs(reinterpret_cast<const void* const*>(row_scale), n_mats, 4))) return st;
+    const QLayout L = q_layout(mats, n_mats, 2, 0, nullptr, nullptr);
+    if ((st = check_ws(ws, ws_bytes, L.total))) return st;
+
+    std::vector<char> host(L.table_end, 0);
+    QMat* tb = at<QMat>(host.data(), L.tab_b);
+    QMat* tf = at<QMat>(host.data(), L.tab_f);
+    int64_t* ub = at<int64_t>(host.data(), L.ubeg_b);
+    int64_t* uf = at<int64_t>(host.data(), L.ubeg_f);
+    ub[0] = uf[0] = 0;
+    int ib = 0, jf = 0;
+    for (int32_t i = 0; i < n_mats; ++i) {
+        const woq_mat& m = mats[i];
+        QMat q{};
+        q.data = m.data;
+        q.codes = codes[i];
+        q.scales = row_scale[i];
+        q.rows = (int32_t)m.rows;
+        q.cols = (int32_t)m.cols;
+        q.dtype = m.dtype;
+        if (m.dtype == WOQ_BF16) { tb[ib] = q; ub[ib + 1] = ub[ib] + m.rows; ++ib; }
+        else { tf[jf] = q; uf[jf + 1] = uf[jf] + m.rows; ++jf; }
+    }
+    WOQ_HIP(hipMemcpyAsync(ws, host.data(), L.table_end, hipMemcpyHostToDevice, stream));
+    if (L.nb) WOQ_HIP(ternary(at<QMat>(ws, L.tab_b), at<int64_t>(ws, L.ubeg_b), L.nb, ub[L.nb], WOQ_BF16, stream));
+    if (L.nf) WOQ_HIP(ternary(at<QMat>(ws, L.tab_f), at<int64_t>(ws, L.ubeg_f), L.nf, uf[L.nf], WOQ_F32, stream));
+    return WOQ_OK;
+}
+
+}  // extern "C"

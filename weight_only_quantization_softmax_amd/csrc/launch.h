@@ -1,0 +1,59 @@
+// Host-side launchers implemented by the kernel translation units and used
+// by the C-ABI entry points.  Each returns the hipError_t of its launches.
+#pragma once
+
+#include "woq_internal.h"
+
+namespace woq {
+
+// ---- entropy ([EWQ] step 1 and 2)
+constexpr int64_t kEntChunk = int64_t(1) << 19;   // elements per work unit
+constexpr int kHistSlots = 256;                    // bf16 matrices per batch
+
+hipError_t fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
+hipError_t fill_f32(float* p, size_t n, float v, hipStream_t s);
+
+hipError_t ent_hist_bf16(const EntMat* mats, const int64_t* ubeg, int nmat,
+                         int64_t u0, int64_t n_units, uint32_t* ghist,
+                         hipStream_t s);
+hipError_t ent_hist_final(const EntMat* mats, int nmat, const uint32_t* ghist,
+                          double* h_mat, hipStream_t s);
+hipError_t ent_f32(const EntMat* mats, const int64_t* ubeg, int nmat,
+                   int64_t n_units, uint32_t* keys, double2* part,
+                   double* h_mat, hipStream_t s);
+hipError_t ent_blocks(const int32_t* bmats, const int32_t* bbeg,
+                      const double* nsz, const double* h_mat, int n_blocks,
+                      double x, double* hb, double* h_block, double* stats,
+                      int32_t* tier, int32_t* order, hipStream_t s);
+
+// ---- Sinkhorn ([SINQ])
+constexpr int kSinqTileCols = 2048;  // columns per column-pass work unit
+
+hipError_t sinq_rows(const SinqMat* mats, const int64_t* ubeg, int nmat,
+                     int64_t n_units, bool first, bool any_f32, hipStream_t s);
+hipError_t sinq_colpart(const SinqMat* mats, const int64_t* ubeg, int nmat,
+                        int64_t n_units, bool any_f32, hipStream_t s);
+hipError_t sinq_colfin(const SinqMat* mats, const int64_t* ubeg, int nmat,
+                       int64_t n_units, hipStream_t s);
+
+// ---- quantise / dequantise / ternary
+constexpr int kQTile = 2048;          // elements per small-group work unit
+
+struct RecipSeg {
+    const float* src;
+    float* dst;
+    int64_t n;
+    int64_t unit_begin;               // units of 256 elements
+};
+hipError_t recip(const RecipSeg* segs, const int64_t* ubeg, int nseg,
+                 int64_t n_units, hipStream_t s);
+hipError_t quant_small(const QMat* mats, const int64_t* ubeg, int nmat,
+                       int64_t n_units, int dtype, int bits, hipStream_t s);
+hipError_t quant_big(const QMat* mats, const int64_t* ubeg, int nmat,
+                     int64_t n_units, int dtype, int bits, hipStream_t s);
+hipError_t dequant(const QMat* mats, const int64_t* ubeg, int nmat,
+                   int64_t n_units, int out_dtype, int bits, hipStream_t s);
+hipError_t ternary(const QMat* mats, const int64_t* ubeg, int nmat,
+                   int64_t n_units, int dtype, hipStream_t s);
+
+}  // namespace woq

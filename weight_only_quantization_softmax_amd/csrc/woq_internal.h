@@ -1,0 +1,112 @@
+// Internal declarations shared by the HIP translation units of libwoq.
+// Device-side descriptor tables live in the caller's workspace; the host
+// fills them, copies them in with one hipMemcpyAsync per call, and the
+// kernels map their block index to a matrix by binary search over
+// per-matrix unit offsets.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "woq.h"
+
+namespace woq {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- helpers
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// 8 consecutive elements (index e is a multiple of 8) of a BF16 / F32 matrix.
+template <int DT>
+__device__ __forceinline__ void load8(const void* base, int64_t e, float (&x)[8]) {
+    if constexpr (DT == WOQ_BF16) {
+        const uint4 v = *reinterpret_cast<const uint4*>(
+            reinterpret_cast<const uint16_t*>(base) + e);
+        x[0] = bf_lo(v.x); x[1] = bf_hi(v.x); x[2] = bf_lo(v.y); x[3] = bf_hi(v.y);
+        x[4] = bf_lo(v.z); x[5] = bf_hi(v.z); x[6] = bf_lo(v.w); x[7] = bf_hi(v.w);
+    } else {
+        const float4* p = reinterpret_cast<const float4*>(
+            reinterpret_cast<const float*>(base) + e);
+        const float4 a = p[0], b = p[1];
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+}
+
+__device__ __forceinline__ void load8f(const float* p, float (&x)[8]) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// Butterfly reductions over a full wave.  Every lane ends with the same
+// value (IEEE addition is commutative, so partners compute identical sums),
+// and the combination order is fixed, so results are deterministic.
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+__device__ __forceinline__ float wave_sumf(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+__device__ __forceinline__ float wave_maxf(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// Largest m in [0, n) with begin[m] <= u (begin ascending, begin[0] == 0).
+__device__ __forceinline__ int find_unit_owner(const int64_t* begin, int n, int64_t u) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (begin[mid] <= u) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// ------------------------------------------------------------ descriptors
+// Entropy: one entry per matrix.
+struct EntMat {
+    const void* data;
+    int64_t n;          // rows * cols
+    int32_t dtype;
+    int32_t slot;       // index of this matrix in the caller's h_mat
+};
+
+// Sinkhorn: one entry per matrix.
+struct SinqMat {
+    const void* data;
+    float* s;           // caller's row scales [rows]
+    float* t;           // caller's column scales [cols]
+    float* v;           // workspace 1/s [rows]
+    float* u;           // workspace 1/t [cols]
+    float2* part;       // workspace column partials [n_chunks][cols]
+    int32_t rows, cols;
+    int32_t dtype;
+    int32_t n_chunks;   // row chunks of the column pass
+    int32_t chunk_rows;
+    int32_t col_tiles;  // 2048-column tiles of the column pass
+};
+
+// Quantise / dequantise / ternary: one entry per matrix.
+struct QMat {
+    const void* data;   // input weights (quant, ternary) or output (dequant)
+    uint8_t* codes;
+    float* scales;      // delta per group (or beta per row)
+    uint8_t* zeros;
+    const float* rs;    // 1/s (quant) or s (dequant), NULL = 1
+    const float* ct;    // 1/t (quant) or t (dequant), NULL = 1
+    int32_t rows, cols;
+    int32_t dtype;
+    int32_t group;      // group size for this matrix (cols for per-row groups)
+};
+
+}  // namespace woq

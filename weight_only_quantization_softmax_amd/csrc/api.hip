@@ -10,6 +10,7 @@
 #include "launch.h"
 
 #include <algorithm>
+#include <tuple>
 #include <cstring>
 #include <vector>
 
@@ -22,7 +23,11 @@ constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
 constexpr int32_t kMaxMats = 1 << 20;
 constexpr int32_t kMaxBlocks = 4096;
 constexpr int32_t kMaxIters = 4096;
-constexpr int kSinqChunkRows = 128;
+// Sinkhorn: matrices of one shape class run in one launch per iteration
+// (MI355X's Infinity Cache serves re-reads barely faster than HBM, so there
+// is no point in cache-sized groups; one big launch amortises everything).
+constexpr int kSinqTargetWGs = 512;    // workgroup mode: ~2 resident per CU
+constexpr int kSinqTargetWaves = 2048; // wave mode: ~8 resident waves per CU
 
 size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 
@@ -113,33 +118,80 @@ EntLayout ent_layout(const woq_mat* mats, int32_t n, int32_t n_blocks) {
 }
 
 // ------------------------------------------------------------------ sinkhorn
-struct SinqLayout {
-    size_t tab, ubeg_r, ubeg_cp, ubeg_cf, table_end, total;
-    std::vector<size_t> v, u, part;
-    int64_t units_r = 0, units_cp = 0, units_cf = 0;
+struct SinqGroup {
+    int first = 0, count = 0, dtype = 0, cols_max = 0;
+    SinqShape sh{0, 0};
+    int64_t n_strips = 0, n_cunits = 0;
+    size_t arr_off = 0;  // index of this group's first entry in sbeg / cbeg
 };
 
-int32_t sinq_chunks(const woq_mat& m) { return (int32_t)cdiv(m.rows, kSinqChunkRows); }
-int32_t sinq_tiles(const woq_mat& m) { return (int32_t)cdiv(m.cols / 8, 256); }
+struct SinqLayout {
+    std::vector<int> order;          // table position -> caller's matrix index
+    std::vector<int32_t> n_strips, strip_rows;  // per table position
+    std::vector<SinqGroup> groups;
+    size_t tab, sbeg, cbeg, table_end, total;
+    std::vector<size_t> u, part;     // per table position
+};
 
 SinqLayout sinq_layout(const woq_mat* mats, int32_t n) {
     SinqLayout L;
+    // launch sets: same dtype and same (threads, vectors per thread)
+    std::vector<int> idx(n);
+    for (int i = 0; i < n; ++i) idx[i] = i;
+    auto key = [&](int i) {
+        const SinqShape sh = sinq_shape((int)mats[i].cols, mats[i].dtype);
+        return std::make_tuple(mats[i].dtype, sh.mode, sh.nv, sh.nt);
+    };
+    std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return key(a) < key(b); });
+    L.order = idx;
+    L.n_strips.assign(n, 0);
+    L.strip_rows.assign(n, 0);
+    int p = 0;
+    while (p < n) {
+        SinqGroup g;
+        g.first = p;
+        g.dtype = mats[idx[p]].dtype;
+        g.sh = sinq_shape((int)mats[idx[p]].cols, mats[idx[p]].dtype);
+        int64_t elems_g = 0;
+        int q = p;
+        while (q < n && key(idx[q]) == key(idx[p])) {
+            elems_g += elems(mats[idx[q]]);
+            ++q;
+        }
+        g.count = q - p;
+        const int R = g.sh.mode == 1 ? 1 : sinq_tile_rows(g.dtype, g.sh.nv);
+        const int target = g.sh.mode == 1 ? kSinqTargetWaves : kSinqTargetWGs;
+        for (int k = p; k < q; ++k) {
+            const woq_mat& m = mats[idx[k]];
+            const double share = (double)elems(m) / (double)elems_g;
+            int64_t want = (int64_t)(share * target + 0.5);
+            want = std::max<int64_t>(1, std::min<int64_t>(want, cdiv(m.rows, R)));
+            int64_t srows = cdiv(cdiv(m.rows, want), R) * R;
+            L.strip_rows[k] = (int32_t)srows;
+            L.n_strips[k] = (int32_t)cdiv(m.rows, srows);
+            g.n_strips += L.n_strips[k];
+            g.n_cunits += cdiv(m.cols, 16);
+            g.cols_max = std::max<int>(g.cols_max, (int)m.cols);
+        }
+        L.groups.push_back(g);
+        p = q;
+    }
     Arena a;
     L.tab = a.take(sizeof(SinqMat) * n);
-    L.ubeg_r = a.take(sizeof(int64_t) * (n + 1));
-    L.ubeg_cp = a.take(sizeof(int64_t) * (n + 1));
-    L.ubeg_cf = a.take(sizeof(int64_t) * (n + 1));
+    const size_t narr = (size_t)n + L.groups.size();
+    L.sbeg = a.take(sizeof(int64_t) * narr);
+    L.cbeg = a.take(sizeof(int64_t) * narr);
     L.table_end = a.end();
-    L.v.resize(n); L.u.resize(n); L.part.resize(n);
-    for (int32_t i = 0; i < n; ++i) {
-        const woq_mat& m = mats[i];
-        L.v[i] = a.take(sizeof(float) * m.rows, 64);
-        L.u[i] = a.take(sizeof(float) * m.cols, 64);
-        L.part[i] = a.take(sizeof(float2) * (size_t)sinq_chunks(m) * m.cols, 64);
-        L.units_r += cdiv(m.rows, 4);
-        L.units_cp += (int64_t)sinq_chunks(m) * sinq_tiles(m);
-        L.units_cf += cdiv(m.cols, 256);
+    L.u.resize(n);
+    L.part.resize(n);
+    for (int k = 0; k < n; ++k) {
+        const woq_mat& m = mats[idx[k]];
+        const size_t psz = m.dtype == WOQ_BF16 ? sizeof(float2) : sizeof(float4);
+        L.u[k] = a.take(sizeof(float) * m.cols, 64);
+        L.part[k] = a.take(psz * (size_t)L.n_strips[k] * m.cols, 64);
     }
+    size_t off = 0;
+    for (auto& g : L.groups) { g.arr_off = off; off += g.count + 1; }
     L.total = a.end();
     return L;
 }
@@ -336,34 +388,6 @@ int32_t sinq_balance(const woq_mat* mats, int32_t n_mats, int32_t iters, float* 
     const SinqLayout L = sinq_layout(mats, n_mats);
     if ((st = check_ws(ws, ws_bytes, L.total))) return st;
 
-    std::vector<char> host(L.table_end, 0);
-    SinqMat* tab = at<SinqMat>(host.data(), L.tab);
-    int64_t* ur = at<int64_t>(host.data(), L.ubeg_r);
-    int64_t* ucp = at<int64_t>(host.data(), L.ubeg_cp);
-    int64_t* ucf = at<int64_t>(host.data(), L.ubeg_cf);
-    ur[0] = ucp[0] = ucf[0] = 0;
-    for (int32_t i = 0; i < n_mats; ++i) {
-        const woq_mat& m = mats[i];
-        SinqMat s;
-        s.data = m.data;
-        s.s = row_scale[i];
-        s.t = col_scale[i];
-        s.v = at<float>(ws, L.v[i]);
-        s.u = at<float>(ws, L.u[i]);
-        s.part = at<float2>(ws, L.part[i]);
-        s.rows = (int32_t)m.rows;
-        s.cols = (int32_t)m.cols;
-        s.dtype = m.dtype;
-        s.n_chunks = sinq_chunks(m);
-        s.chunk_rows = kSinqChunkRows;
-        s.col_tiles = sinq_tiles(m);
-        tab[i] = s;
-        ur[i + 1] = ur[i] + cdiv(m.rows, 4);
-        ucp[i + 1] = ucp[i] + (int64_t)s.n_chunks * s.col_tiles;
-        ucf[i + 1] = ucf[i] + cdiv(m.cols, 256);
-    }
-    WOQ_HIP(hipMemcpyAsync(ws, host.data(), L.table_end, hipMemcpyHostToDevice, stream));
-    const SinqMat* dt = at<SinqMat>(ws, L.tab);
     if (iters == 0) {
         for (int32_t i = 0; i < n_mats; ++i) {
             WOQ_HIP(fill_f32(row_scale[i], (size_t)mats[i].rows, 1.0f, stream));
@@ -371,11 +395,44 @@ int32_t sinq_balance(const woq_mat* mats, int32_t n_mats, int32_t iters, float* 
         }
         return WOQ_OK;
     }
-    for (int32_t it = 0; it < iters; ++it) {
-        WOQ_HIP(sinq_rows(dt, at<int64_t>(ws, L.ubeg_r), n_mats, ur[n_mats], it == 0, false, stream));
-        WOQ_HIP(sinq_colpart(dt, at<int64_t>(ws, L.ubeg_cp), n_mats, ucp[n_mats], false, stream));
-        WOQ_HIP(sinq_colfin(dt, at<int64_t>(ws, L.ubeg_cf), n_mats, ucf[n_mats], stream));
+    std::vector<char> host(L.table_end, 0);
+    SinqMat* tab = at<SinqMat>(host.data(), L.tab);
+    int64_t* sb = at<int64_t>(host.data(), L.sbeg);
+    int64_t* cb = at<int64_t>(host.data(), L.cbeg);
+    for (int32_t k = 0; k < n_mats; ++k) {
+        const int i = L.order[k];
+        const woq_mat& m = mats[i];
+        SinqMat sm{};
+        sm.data = m.data;
+        sm.s = row_scale[i];
+        sm.t = col_scale[i];
+        sm.u = at<float>(ws, L.u[k]);
+        sm.part = at<void>(ws, L.part[k]);
+        sm.rows = (int32_t)m.rows;
+        sm.cols = (int32_t)m.cols;
+        sm.dtype = m.dtype;
+        sm.n_strips = L.n_strips[k];
+        sm.strip_rows = L.strip_rows[k];
+        tab[k] = sm;
     }
+    for (const SinqGroup& g : L.groups) {
+        int64_t* gs = sb + g.arr_off;
+        int64_t* gc = cb + g.arr_off;
+        gs[0] = gc[0] = 0;
+        for (int k = 0; k < g.count; ++k) {
+            gs[k + 1] = gs[k] + tab[g.first + k].n_strips;
+            gc[k + 1] = gc[k] + cdiv(tab[g.first + k].cols, 16);
+        }
+    }
+    WOQ_HIP(hipMemcpyAsync(ws, host.data(), L.table_end, hipMemcpyHostToDevice, stream));
+    const SinqMat* dt = at<SinqMat>(ws, L.tab);
+    const int64_t* dsb = at<int64_t>(ws, L.sbeg);
+    const int64_t* dcb = at<int64_t>(ws, L.cbeg);
+    for (const SinqGroup& g : L.groups)
+        for (int32_t it = 0; it < iters; ++it)
+            WOQ_HIP(sinq_iteration(dt + g.first, dsb + g.arr_off, dcb + g.arr_off, g.count,
+                                   g.n_strips, g.n_cunits, g.dtype, g.sh, g.cols_max, it == 0,
+                                   stream));
     return WOQ_OK;
 }
 

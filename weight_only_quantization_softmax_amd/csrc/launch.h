@@ -27,14 +27,19 @@ hipError_t ent_blocks(const int32_t* bmats, const int32_t* bbeg,
                       int32_t* tier, int32_t* order, hipStream_t s);
 
 // ---- Sinkhorn ([SINQ])
-constexpr int kSinqTileCols = 2048;  // columns per column-pass work unit
-
-hipError_t sinq_rows(const SinqMat* mats, const int64_t* ubeg, int nmat,
-                     int64_t n_units, bool first, bool any_f32, hipStream_t s);
-hipError_t sinq_colpart(const SinqMat* mats, const int64_t* ubeg, int nmat,
-                        int64_t n_units, bool any_f32, hipStream_t s);
-hipError_t sinq_colfin(const SinqMat* mats, const int64_t* ubeg, int nmat,
-                       int64_t n_units, hipStream_t s);
+// Launch shape for a matrix width: mode 1 = one wave per row (rows of at
+// most 4096 bf16 / 2048 fp32 columns, nv = vectors per lane), mode 0 = one
+// workgroup of nt threads per row strip (nv vectors per thread).
+struct SinqShape { int nt, nv, mode; };
+SinqShape sinq_shape(int cols, int dtype);
+// Rows per register tile of the fused pass (depends on dtype and nv).
+int sinq_tile_rows(int dtype, int nv);
+// One iteration over a group of same-shape matrices: the fused row / column
+// pass (one workgroup per strip) then the fixed-order column reduction.
+hipError_t sinq_iteration(const SinqMat* mats, const int64_t* strip_begin,
+                          const int64_t* col_begin, int nmat, int64_t n_strips,
+                          int64_t n_col_units, int dtype, SinqShape sh, int cols_max,
+                          bool first, hipStream_t s);
 
 // ---- quantise / dequantise / ternary
 constexpr int kQTile = 2048;          // elements per small-group work unit

@@ -7,171 +7,706 @@
 // standard deviations reach the target; not a doubly stochastic matrix).
 //
 // One iteration: s_i = std_j(W_ij / t_j), then t_j = std_i(W_ij / s_i),
-// centred population std, zero std -> 1; t starts at 1.  The kernels hold
-// u = 1/t and v = 1/s (correctly rounded fp32) and compute x = w * u (or
-// w * v) in fp32; per-lane fp32 sums of x and x^2 are combined in fp64 in a
-// fixed order, so the result is deterministic.  The variance is
-// E[x^2] - E[x]^2 in fp64.  For fp32 inputs every line is first shifted by
-// its first element (exact zero variance for constant lines); bf16 values
-// make the unshifted sums exact in that case already.
+// centred population std, zero std -> 1; t starts at 1.  Kernels hold
+// u = 1/t and v = 1/s (correctly rounded fp32) and form x = w * u (w * v).
 //
-// Kernels per iteration (all matrices of the call in each launch):
-//   k_rows     one wave per row: s_i and v_i.
-//   k_colpart  one thread per 8 columns over a chunk of rows: fp32 partial
-//              (sum, sum of squares) per column and chunk.
-//   k_colfin   one thread per column: fp64 combine of the chunk partials,
-//              t_j and u_j.
+// Fused pass (one read of W per iteration).  A workgroup owns a strip of
+// whole rows of one matrix; thread t owns the 8-column vectors t, t + NT,
+// ..., so its column partial sums stay in registers for the whole strip.
+// The strip is walked in tiles of R rows held in registers (the next tile's
+// loads are in flight while the current one is processed):
+//   1. row statistics in two passes over the registers: the row sums of
+//      x = w*u, then the centred sums of squares.  Each pass reduces the R
+//      per-thread partials over the wave with a butterfly reduce-scatter on
+//      permlane swaps and DPP, then over the waves through LDS (every wave
+//      adds the wave totals in wave order) -> s_i, v_i = 1/s_i;
+//   2. the same registers give z = w*v_i, accumulated into the thread's
+//      column (sum, sum of squares).
+// At the end of the strip the column partials are written per strip; a
+// second kernel combines them per column in fp64 in strip order -> t_j, u_j.
+// Everything runs in a fixed order, so results are deterministic.
+//
+// Row variance is the centred second moment (two-pass: no cancellation,
+// exactly 0 for a constant row: bf16 sums of equal values are exact in fp32
+// for rows up to 2^15 wide; fp32 rows are first shifted by their first
+// element).  Column variance is E[z^2] - E[z]^2 in fp64 from fp32 strip
+// partials: relative accuracy ~1e-7 (1 + mean^2/var), ample for the
+// near-zero column means of weight matrices.  bf16 columns that are
+// constant at the first step (or all zero) sum exactly; fp32 inputs also
+// track per-column min/max (a constant column has std 0).
+//
+// Matrices of one launch share (NT, NV): NV = vectors per thread (1..8), NT =
+// threads per workgroup (<= 512).  For NV >= 3 the u vector lives in LDS.
 #include "launch.h"
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace woq {
 namespace {
 
-constexpr int kT = 256;
+constexpr int kMaxT = 512;
+
+template <int DT> struct Vec8;
+template <> struct Vec8<WOQ_BF16> { uint4 v; };
+template <> struct Vec8<WOQ_F32> { float4 a, b; };
 
 template <int DT>
-__device__ __forceinline__ void rows_body(const SinqMat& sm, int row, int lane, bool first) {
-    const int nv = sm.cols >> 3;
-    const int64_t rb = (int64_t)row * sm.cols;
-    float K = 0.f;
-    if constexpr (DT == WOQ_F32) {
-        K = reinterpret_cast<const float*>(sm.data)[rb];
-        if (!first) K = K * sm.u[0];
+__device__ __forceinline__ Vec8<DT> ldv(const void* base, int64_t e) {
+    Vec8<DT> r;
+    if constexpr (DT == WOQ_BF16) {
+        r.v = gload_u4(reinterpret_cast<const uint16_t*>(base) + e);
+    } else {
+        const float* p = reinterpret_cast<const float*>(base) + e;
+        r.a = gload_f4(p);
+        r.b = gload_f4(p + 4);
     }
-    float S = 0.f, Q = 0.f;
-    for (int j = lane; j < nv; j += kWave) {
-        float x[8];
-        load8<DT>(sm.data, rb + 8 * j, x);
-        if (!first) {
-            float uu[8];
-            load8f(sm.u + 8 * j, uu);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) x[k] = x[k] * uu[k];
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float y = x[k] - K;
-            S += y;
-            Q = fmaf(y, y, Q);
-        }
-    }
-    const double Sd = wave_sum((double)S);
-    const double Qd = wave_sum((double)Q);
-    if (lane == 0) {
-        const double n = (double)sm.cols;
-        const double mean = Sd / n;
-        const double var = Qd / n - mean * mean;
-        const float s = var > 0.0 ? (float)sqrt(var) : 1.0f;
-        sm.s[row] = s;
-        sm.v[row] = __fdiv_rn(1.0f, s);
+    return r;
+}
+
+template <int DT>
+__device__ __forceinline__ float ld1(const void* base, int64_t e) {
+    if constexpr (DT == WOQ_BF16) return __uint_as_float((uint32_t)gload<uint16_t>(reinterpret_cast<const uint16_t*>(base) + e) << 16);
+    else return gload<float>(reinterpret_cast<const float*>(base) + e);
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack(const Vec8<DT>& r, float (&x)[8]) {
+    if constexpr (DT == WOQ_BF16) {
+        x[0] = bf_lo(r.v.x); x[1] = bf_hi(r.v.x); x[2] = bf_lo(r.v.y); x[3] = bf_hi(r.v.y);
+        x[4] = bf_lo(r.v.z); x[5] = bf_hi(r.v.z); x[6] = bf_lo(r.v.w); x[7] = bf_hi(r.v.w);
+    } else {
+        x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+        x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
     }
 }
 
-__global__ __launch_bounds__(kT) void k_rows(const SinqMat* __restrict__ mats,
-                                             const int64_t* __restrict__ ubeg, int nmat,
-                                             int first) {
-    const int64_t u = blockIdx.x;
-    const int m = find_unit_owner(ubeg, nmat, u);
+template <int N> struct Log2 { static constexpr int v = 1 + Log2<N / 2>::v; };
+template <> struct Log2<1> { static constexpr int v = 0; };
+
+// One split level of the reduce-scatter through a DPP pairing: lanes with
+// `up` set keep the upper half of the values.
+template <int CTRL, int HALF>
+__device__ __forceinline__ void split_dpp(float* a, bool up) {
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) {
+        const float send = up ? a[i] : a[i + HALF];
+        const float keep = up ? a[i + HALF] : a[i];
+        a[i] = keep + dpp<CTRL>(send);
+    }
+}
+
+// Butterfly reduce-scatter of N values (power of two <= 64) over a wave:
+// afterwards lane l holds the wave total of value index l >> (6 - log2 N).
+// Partners per level: lane ^ 32, ^ 16 (permlane swaps), ^ 8, the mirror
+// within 8 lanes, ^ 2, ^ 1 (DPP); the kept half is chosen by lane bits
+// 5, 4, 3, 2, 1, 0 in that order.
+template <int N>
+__device__ __forceinline__ float wave_reduce_scatter(float (&a)[N], int lane) {
+    constexpr int L = Log2<N>::v;
+    if constexpr (L >= 1) {
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) { swap32(a[i], a[i + N / 2]); a[i] += a[i + N / 2]; }
+    }
+    if constexpr (L >= 2) {
+#pragma unroll
+        for (int i = 0; i < N / 4; ++i) { swap16(a[i], a[i + N / 4]); a[i] += a[i + N / 4]; }
+    }
+    if constexpr (L >= 3) split_dpp<kDppXor8, N / 8>(a, (lane & 8) != 0);
+    if constexpr (L >= 4) split_dpp<kDppMirror8, N / 16>(a, (lane & 4) != 0);
+    if constexpr (L >= 5) split_dpp<kDppXor2, N / 32>(a, (lane & 2) != 0);
+    if constexpr (L >= 6) split_dpp<kDppXor1, N / 64>(a, (lane & 1) != 0);
+    float r = a[0];
+    if constexpr (L < 1) { float b = r; swap32(r, b); r += b; }
+    if constexpr (L < 2) { float b = r; swap16(r, b); r += b; }
+    if constexpr (L < 3) r += dpp<kDppXor8>(r);
+    if constexpr (L < 4) r += dpp<kDppMirror8>(r);
+    if constexpr (L < 5) r += dpp<kDppXor2>(r);
+    if constexpr (L < 6) r += dpp<kDppXor1>(r);
+    return r;
+}
+
+// Rows per register tile, per dtype and vectors per thread.
+constexpr int tile_rows(int dt, int nv) {
+    return dt == WOQ_BF16 ? (nv == 1 ? 8 : (nv == 2 ? 4 : (nv <= 4 ? 2 : 1))) : (nv == 1 ? 4 : (nv == 2 ? 2 : 1));
+}
+
+template <int DT, int NV>
+struct PassCfg {
+    static constexpr int R = tile_rows(DT, NV);
+    static constexpr int NVAL = 2 * R;
+    static constexpr bool U_LDS = NV >= 3;
+    static constexpr bool F32 = DT == WOQ_F32;
+    // wide rows: unpack bf16 again for each pass instead of keeping the
+    // unpacked tile live across the barriers (register pressure)
+    static constexpr bool REUNPACK = DT == WOQ_BF16 && NV >= 3;
+};
+
+// Empty asm that claims to modify the packed registers, so the compiler
+// cannot reuse values unpacked before it (ALU registers only, no memory).
+template <int DT>
+__device__ __forceinline__ void opaque(Vec8<DT>& r) {
+    if constexpr (DT == WOQ_BF16) asm volatile("" : "+v"(r.v.x), "+v"(r.v.y), "+v"(r.v.z), "+v"(r.v.w));
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations: global
+// loads already in flight (the next tile) stay in flight across it.  The
+// "memory" clobber keeps the compiler from moving LDS accesses across.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int DT, int NV, bool FIRST>
+__global__ __launch_bounds__(kMaxT) void k_sinq_pass(const SinqMat* __restrict__ mats,
+                                                     const int64_t* __restrict__ sbeg, int nmat) {
+    using C = PassCfg<DT, NV>;
+    constexpr int R = C::R;
+    constexpr int NVAL = C::NVAL;
+    __shared__ float red[2][kMaxT / 64][NVAL];
+    extern __shared__ float ulds[];  // u [cols + 8] when U_LDS
+
+    const int m = find_unit_owner(sbeg, nmat, (int64_t)blockIdx.x);
     const SinqMat sm = mats[m];
-    const int row = (int)(u - ubeg[m]) * (kT / kWave) + (threadIdx.x >> 6);
-    if (row >= sm.rows) return;  // no block-level synchronisation below
+    const int strip = (int)(blockIdx.x - sbeg[m]);
+    const int r0 = strip * sm.strip_rows;
+    const int r1 = min(sm.rows, r0 + sm.strip_rows);
+    const int NT = blockDim.x;
+    const int nw = NT >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int nvec = sm.cols >> 3;
+    const int64_t cols = sm.cols;
+    const float fn = (float)sm.cols;
+
+    int vk[NV], ui[NV];
+    bool own[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        own[k] = tid + NT * k < nvec;
+        vk[k] = own[k] ? tid + NT * k : nvec - 1;  // clamped: loads stay in bounds
+        ui[k] = own[k] ? vk[k] : nvec;              // LDS index: zero pad for non-owned
+    }
+    // Row multipliers u (0 for vectors this thread does not own).
+    float uu[C::U_LDS ? 1 : NV][8];
+    const float u0 = FIRST ? 1.0f : gload<float>(sm.u);
+    if constexpr (C::U_LDS) {
+        for (int j = tid; j < sm.cols + 8; j += NT)
+            ulds[j] = j < sm.cols ? (FIRST ? 1.0f : gload<float>(sm.u + j)) : 0.0f;
+        __syncthreads();
+    } else {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const float o = own[k] ? 1.0f : 0.0f;
+            if constexpr (FIRST) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) uu[k][e] = o;
+            } else {
+                const float4 a = gload_f4(sm.u + 8 * vk[k]);
+                const float4 b = gload_f4(sm.u + 8 * vk[k] + 4);
+                uu[k][0] = a.x * o; uu[k][1] = a.y * o; uu[k][2] = a.z * o; uu[k][3] = a.w * o;
+                uu[k][4] = b.x * o; uu[k][5] = b.y * o; uu[k][6] = b.z * o; uu[k][7] = b.w * o;
+            }
+        }
+    }
+
+    float cs[NV][8], cq[NV][8];
+    float cmn[C::F32 ? NV : 1][8], cmx[C::F32 ? NV : 1][8];
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            cs[k][e] = 0.f;
+            cq[k][e] = 0.f;
+            if constexpr (C::F32) { cmn[k][e] = INFINITY; cmx[k][e] = -INFINITY; }
+        }
+
+    int buf = 0;
+    // Sum `val` over the workgroup: wave reduce-scatter, LDS exchange, then
+    // every wave adds the wave totals in wave order; lane r (< N) returns
+    // total r.  N values, power of two.
+    auto wg_sum = [&](auto& val, auto nconst) -> float {
+        constexpr int N = decltype(nconst)::value;
+        constexpr int SHN = 6 - Log2<N>::v;
+        const float tot = wave_reduce_scatter<N>(val, lane);
+        if ((lane & ((1 << SHN) - 1)) == 0) red[buf][wid][lane >> SHN] = tot;
+        lds_barrier();
+        float acc = 0.f;
+        if (lane < N)
+            for (int w = 0; w < nw; ++w) acc += red[buf][w][lane];
+        buf ^= 1;
+        return acc;
+    };
+
+    // F32 rows are first shifted by their first element (exactly 0 for a
+    // constant row whatever the rounding of the sums); bf16 sums of a
+    // constant row are exact, so no shift is needed there.
+    auto load_tile = [&](Vec8<DT> (&d)[R][NV], float (&km)[R], int rb) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t row = min(rb + r, r1 - 1);  // clamped into the strip
+            if constexpr (C::F32) km[r] = ld1<DT>(sm.data, row * cols);
+            else km[r] = 0.f;
+#pragma unroll
+            for (int k = 0; k < NV; ++k) d[r][k] = ldv<DT>(sm.data, row * cols + 8 * vk[k]);
+        }
+    };
+    auto uval = [&](int k, int e) -> float { return C::U_LDS ? ulds[8 * ui[k] + e] : uu[k][e]; };
+
+    // FULLT: every row of the tile lies in the strip (no masking needed)
+    auto process = [&](Vec8<DT> (&d)[R][NV], const float (&km)[R], int rb, auto fullc) {
+        constexpr bool FULLT = decltype(fullc)::value;
+        // values of the tile as floats (kept when registers allow)
+        float xf[C::REUNPACK ? 1 : R][C::REUNPACK ? 1 : NV][8];
+        if constexpr (!C::REUNPACK) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int k = 0; k < NV; ++k) unpack<DT>(d[r][k], xf[r][k]);
+        }
+        auto xval = [&](int r, int k, float (&x)[8]) {
+            if constexpr (C::REUNPACK) { opaque<DT>(d[r][k]); unpack<DT>(d[r][k], x); }
+            else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = xf[r][k][e];
+            }
+        };
+        // ---- row statistics of x = w * u, two passes (mean, then centred
+        //      squares): exact zero for constant rows, no cancellation
+        float sv[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float K = km[r] * (FIRST ? 1.0f : u0);
+            float S = 0.f;
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                const float Kk = own[k] ? K : 0.f;
+                float x[8];
+                xval(r, k, x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if constexpr (C::F32) S += fmaf(x[e], uval(k, e), -Kk);
+                    else S = fmaf(x[e], uval(k, e), S);
+                }
+            }
+            sv[r] = S;
+        }
+        const float St = wg_sum(sv, std::integral_constant<int, R>{});
+        const float ms = __fdiv_rn(St, fn);  // lane r: mean of row r (shifted)
+        float qv[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float M = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(ms), r)) +
+                            km[r] * (FIRST ? 1.0f : u0);
+            float Q = 0.f;
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                const float Mk = own[k] ? M : 0.f;
+                float x[8];
+                xval(r, k, x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float y = fmaf(x[e], uval(k, e), -Mk);
+                    Q = fmaf(y, y, Q);
+                }
+            }
+            qv[r] = Q;
+        }
+        const float Qt = wg_sum(qv, std::integral_constant<int, R>{});
+        // ---- s, v for rows rb + lane (lanes < R); wave 0 writes s
+        float vv = 0.f;
+        if (lane < R) {
+            const int row = rb + lane;
+            const float var = Qt / fn;
+            const float s = var > 0.f ? __fsqrt_rn(var) : 1.0f;
+            if (row < r1) {
+                vv = __fdiv_rn(1.0f, s);
+                if (wid == 0) gstore<float>(sm.s + row, s);
+            }
+        }
+        // ---- column partials of z = w * v with the new row scales
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float vr = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(vv), r));
+            const bool valid = rb + r < r1;
+            const float rv = valid ? 1.0f : 0.0f;  // rows past the strip add nothing
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                float x[8];
+                xval(r, k, x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float z = x[e] * vr;
+                    if constexpr (!FULLT) z *= rv;
+                    cs[k][e] += z;
+                    cq[k][e] = fmaf(z, z, cq[k][e]);
+                    if constexpr (C::F32) {
+                        if (FULLT || valid) { cmn[k][e] = fminf(cmn[k][e], z); cmx[k][e] = fmaxf(cmx[k][e], z); }
+                    }
+                }
+            }
+        }
+    };
+
+    // ---- tiles in pairs: the next tile's loads are issued before the
+    //      current tile is processed (two register buffers)
+    Vec8<DT> dA[R][NV], dB[R][NV];
+    float kA[R], kB[R];
+    int rb = r0;
+    if (rb < r1) load_tile(dA, kA, rb);
+    auto run = [&](Vec8<DT> (&d)[R][NV], const float (&km)[R], int at) {
+        if (at + R <= r1) process(d, km, at, std::true_type{});
+        else process(d, km, at, std::false_type{});
+    };
+    while (rb < r1) {
+        const int rn = rb + R;
+        if (rn < r1) load_tile(dB, kB, rn);
+        run(dA, kA, rb);
+        if (rn >= r1) break;
+        const int rn2 = rn + R;
+        if (rn2 < r1) load_tile(dA, kA, rn2);
+        run(dB, kB, rn);
+        rb = rn2;
+    }
+
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        if (!own[k]) continue;
+        const int64_t c0 = (int64_t)strip * cols + 8 * vk[k];
+        if constexpr (C::F32) {
+            float4* p = reinterpret_cast<float4*>(sm.part) + c0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gstore_f4(p + e, cs[k][e], cq[k][e], cmn[k][e], cmx[k][e]);
+        } else {
+            float4* p = reinterpret_cast<float4*>(reinterpret_cast<float2*>(sm.part) + c0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                gstore_f4(p + e, cs[k][2 * e], cq[k][2 * e], cs[k][2 * e + 1], cq[k][2 * e + 1]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Wave-per-row pass for rows of at most 4096 columns (NVL = cols/512 vectors
+// of 8 per lane).  A wave owns a strip of whole rows: row statistics are
+// wave-local (DPP / permlane reductions, no workgroup barrier), lane l owns
+// columns 8*l + 512*k + e, and the column partials of each wave's strip go to
+// part[strip] directly.  The next row is loaded into the packed registers as
+// soon as the current row has been unpacked.  u lives in LDS (shared by the
+// four waves of a workgroup).
+__device__ __forceinline__ float wave_allsum(float v) {
+    float b = v;
+    swap32(v, b);
+    v += b;
+    b = v;
+    swap16(v, b);
+    v += b;
+    v += dpp<kDppXor8>(v);
+    v += dpp<kDppMirror8>(v);
+    v += dpp<kDppXor2>(v);
+    v += dpp<kDppXor1>(v);
+    return v;
+}
+
+template <int DT, int NVL, bool FIRST>
+__global__ __launch_bounds__(256) void k_sinq_wave(const SinqMat* __restrict__ mats,
+                                                   const int64_t* __restrict__ wbeg, int nmat) {
+    constexpr bool F32 = DT == WOQ_F32;
+    extern __shared__ float ul[];  // [cols_max + 8]: u (1 at the first step), zero pad
     const int lane = threadIdx.x & 63;
-    if (sm.dtype == WOQ_BF16) rows_body<WOQ_BF16>(sm, row, lane, first != 0);
-    else rows_body<WOQ_F32>(sm, row, lane, first != 0);
+    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);  // global wave index
+    // the workgroup's four waves may belong to different matrices: each wave
+    // looks up its own; u is staged per wave in its own LDS quarter
+    const int m = find_unit_owner(wbeg, nmat, (int64_t)gw);
+    const bool live = gw < wbeg[nmat];
+    const SinqMat sm = mats[live ? m : 0];
+    const int strip = gw - (int)wbeg[m];
+    const int cols = sm.cols;
+    const int nvec = cols >> 3;
+    float* u = ul + (threadIdx.x >> 6) * (4096 + 8);
+    for (int j = lane; j < 4096 + 8; j += 64)
+        u[j] = (j < cols) ? (FIRST ? 1.0f : gload<float>(sm.u + j)) : 0.0f;
+    if (!live) return;
+    const int r0 = strip * sm.strip_rows;
+    const int r1 = min(sm.rows, r0 + sm.strip_rows);
+
+    int vk[NVL];
+    bool own[NVL];
+#pragma unroll
+    for (int k = 0; k < NVL; ++k) {
+        own[k] = lane + 64 * k < nvec;
+        vk[k] = own[k] ? lane + 64 * k : nvec - 1;
+    }
+    const float fn = (float)cols;
+
+    float cs[NVL][8], cq[NVL][8];
+    float cmn[F32 ? NVL : 1][8], cmx[F32 ? NVL : 1][8];
+#pragma unroll
+    for (int k = 0; k < NVL; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            cs[k][e] = 0.f;
+            cq[k][e] = 0.f;
+            if constexpr (F32) { cmn[k][e] = INFINITY; cmx[k][e] = -INFINITY; }
+        }
+
+    // Wide rows (NVL >= 5) keep only the packed row and unpack it again in
+    // each of the three passes (registers: 2 waves per SIMD with the
+    // prefetch); narrower rows keep the unpacked floats.
+    constexpr bool KEEP = F32 || NVL <= 4;
+    Vec8<DT> P[NVL], Cur[KEEP ? 1 : NVL];
+    float xf[KEEP ? NVL : 1][8];
+    float K = 0.f, Kn = 0.f;
+    auto load_row = [&](int row) {
+#pragma unroll
+        for (int k = 0; k < NVL; ++k) P[k] = ldv<DT>(sm.data, (int64_t)row * cols + 8 * vk[k]);
+        if constexpr (F32) Kn = ld1<DT>(sm.data, (int64_t)row * cols);
+    };
+    auto xval = [&](int k, float (&x)[8]) {
+        if constexpr (KEEP) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = xf[k][e];
+        } else {
+            opaque<DT>(Cur[k]);
+            unpack<DT>(Cur[k], x);
+        }
+    };
+    if (r0 < r1) load_row(r0);
+    for (int row = r0; row < r1; ++row) {
+#pragma unroll
+        for (int k = 0; k < NVL; ++k) {
+            if constexpr (KEEP) unpack<DT>(P[k], xf[k]);
+            else Cur[k] = P[k];
+        }
+        K = Kn;
+        if (row + 1 < r1) load_row(row + 1);   // prefetch into the freed registers
+        // pass A: row sum of x * u (fp32 rows shifted by their first element)
+        const float Ks = FIRST ? K : K * u[0];
+        float S = 0.f;
+#pragma unroll
+        for (int k = 0; k < NVL; ++k) {
+            const float Kk = own[k] ? Ks : 0.f;
+            float x[8];
+            xval(k, x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float uu = u[8 * (own[k] ? vk[k] : nvec) + e];
+                if constexpr (F32) S += fmaf(x[e], uu, -Kk);
+                else S = fmaf(x[e], uu, S);
+            }
+        }
+        S = wave_allsum(S);
+        const float M = __fdiv_rn(S, fn) + Ks;
+        // pass B: centred sum of squares
+        float Q = 0.f;
+#pragma unroll
+        for (int k = 0; k < NVL; ++k) {
+            const float Mk = own[k] ? M : 0.f;
+            float x[8];
+            xval(k, x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float y = fmaf(x[e], u[8 * (own[k] ? vk[k] : nvec) + e], -Mk);
+                Q = fmaf(y, y, Q);
+            }
+        }
+        Q = wave_allsum(Q);
+        const float var = Q / fn;
+        const float s = var > 0.f ? __fsqrt_rn(var) : 1.0f;
+        const float v = __fdiv_rn(1.0f, s);
+        if (lane == 0) gstore<float>(sm.s + row, s);
+        // column partials with this row's scale
+#pragma unroll
+        for (int k = 0; k < NVL; ++k) {
+            float x[8];
+            xval(k, x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float z = x[e] * v;
+                cs[k][e] += z;
+                cq[k][e] = fmaf(z, z, cq[k][e]);
+                if constexpr (F32) { cmn[k][e] = fminf(cmn[k][e], z); cmx[k][e] = fmaxf(cmx[k][e], z); }
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < NVL; ++k) {
+        if (!own[k]) continue;
+        const int64_t c0 = (int64_t)strip * cols + 8 * vk[k];
+        if constexpr (F32) {
+            float4* p = reinterpret_cast<float4*>(sm.part) + c0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gstore_f4(p + e, cs[k][e], cq[k][e], cmn[k][e], cmx[k][e]);
+        } else {
+            float4* p = reinterpret_cast<float4*>(reinterpret_cast<float2*>(sm.part) + c0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                gstore_f4(p + e, cs[k][2 * e], cq[k][2 * e], cs[k][2 * e + 1], cq[k][2 * e + 1]);
+        }
+    }
+}
+
+template <int DT, int NVL>
+hipError_t launch_wave(const SinqMat* mats, const int64_t* wbeg, int nmat, int64_t n_waves,
+                       bool first, hipStream_t s) {
+    const size_t lds = 4 * sizeof(float) * (4096 + 8);
+    const unsigned grid = (unsigned)((n_waves + 3) / 4);
+    if (first) k_sinq_wave<DT, NVL, true><<<dim3(grid), dim3(256), lds, s>>>(mats, wbeg, nmat);
+    else k_sinq_wave<DT, NVL, false><<<dim3(grid), dim3(256), lds, s>>>(mats, wbeg, nmat);
+    return hipGetLastError();
 }
 
 template <int DT>
-__device__ __forceinline__ void colpart_body(const SinqMat& sm, int chunk, int cv) {
-    const int r0 = chunk * sm.chunk_rows;
-    const int r1 = min(sm.rows, r0 + sm.chunk_rows);
-    const int c0 = 8 * cv;
-    float K[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) K[k] = 0.f;
-    if constexpr (DT == WOQ_F32) {
-        float x0[8];
-        load8<DT>(sm.data, c0, x0);
-        const float v0 = sm.v[0];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) K[k] = x0[k] * v0;
+hipError_t launch_wave_dt(const SinqMat* mats, const int64_t* wbeg, int nmat, int64_t n_waves,
+                          int nvl, bool first, hipStream_t s) {
+    switch (nvl) {
+        case 1: return launch_wave<DT, 1>(mats, wbeg, nmat, n_waves, first, s);
+        case 2: return launch_wave<DT, 2>(mats, wbeg, nmat, n_waves, first, s);
+        case 3: return launch_wave<DT, 3>(mats, wbeg, nmat, n_waves, first, s);
+        case 4: return launch_wave<DT, 4>(mats, wbeg, nmat, n_waves, first, s);
+        case 5: return launch_wave<DT, 5>(mats, wbeg, nmat, n_waves, first, s);
+        case 6: return launch_wave<DT, 6>(mats, wbeg, nmat, n_waves, first, s);
+        case 7: return launch_wave<DT, 7>(mats, wbeg, nmat, n_waves, first, s);
+        default: return launch_wave<DT, 8>(mats, wbeg, nmat, n_waves, first, s);
     }
-    float cs[8], cq[8];
+}
+
+// Column combine: a workgroup takes 16 columns; 16 slices of threads each
+// sum every 16th strip (16 loads in flight), then slice totals are added in
+// slice order.  The summation order is fixed, so results are deterministic.
+constexpr int kRedCols = 16;
+constexpr int kRedSlices = 16;
+constexpr int kRedInflight = 16;
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_sinq_reduce(const SinqMat* __restrict__ mats,
+                                                     const int64_t* __restrict__ cbeg, int nmat,
+                                                     int first) {
+    __shared__ double sS[kRedSlices][kRedCols], sQ[kRedSlices][kRedCols];
+    __shared__ float sMn[kRedSlices][kRedCols], sMx[kRedSlices][kRedCols];
+    const int64_t u = blockIdx.x;
+    const int m = find_unit_owner(cbeg, nmat, u);
+    const SinqMat sm = mats[m];
+    const int c = threadIdx.x % kRedCols, sl = threadIdx.x / kRedCols;
+    const int j = (int)(u - cbeg[m]) * kRedCols + c;
+    double S = 0.0, Q = 0.0;
+    float mn = INFINITY, mx = -INFINITY;
+    if (j < sm.cols) {
+        for (int g0 = sl; g0 < sm.n_strips; g0 += kRedInflight * kRedSlices) {
+            if constexpr (DT == WOQ_F32) {
+                float4 p[kRedInflight];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) { cs[k] = 0.f; cq[k] = 0.f; }
-    for (int r = r0; r < r1; ++r) {
-        float x[8];
-        load8<DT>(sm.data, (int64_t)r * sm.cols + c0, x);
-        const float vr = sm.v[r];
+                for (int q = 0; q < kRedInflight; ++q) {
+                    const int g = g0 + q * kRedSlices;
+                    p[q] = g < sm.n_strips ? gload_f4(reinterpret_cast<const float4*>(sm.part) + (int64_t)g * sm.cols + j)
+                                           : make_float4(0.f, 0.f, INFINITY, -INFINITY);
+                }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float y = x[k] * vr - K[k];
-            cs[k] += y;
-            cq[k] = fmaf(y, y, cq[k]);
+                for (int q = 0; q < kRedInflight; ++q) {
+                    S += (double)p[q].x;
+                    Q += (double)p[q].y;
+                    mn = fminf(mn, p[q].z);
+                    mx = fmaxf(mx, p[q].w);
+                }
+            } else {
+                float2 p[kRedInflight];
+#pragma unroll
+                for (int q = 0; q < kRedInflight; ++q) {
+                    const int g = g0 + q * kRedSlices;
+                    p[q] = g < sm.n_strips ? gload_f2(reinterpret_cast<const float2*>(sm.part) + (int64_t)g * sm.cols + j)
+                                           : make_float2(0.f, 0.f);
+                }
+#pragma unroll
+                for (int q = 0; q < kRedInflight; ++q) { S += (double)p[q].x; Q += (double)p[q].y; }
+            }
         }
     }
-    float4* out = reinterpret_cast<float4*>(sm.part + (size_t)chunk * sm.cols + c0);
-    out[0] = make_float4(cs[0], cq[0], cs[1], cq[1]);
-    out[1] = make_float4(cs[2], cq[2], cs[3], cq[3]);
-    out[2] = make_float4(cs[4], cq[4], cs[5], cq[5]);
-    out[3] = make_float4(cs[6], cq[6], cs[7], cq[7]);
-}
-
-__global__ __launch_bounds__(kT) void k_colpart(const SinqMat* __restrict__ mats,
-                                                const int64_t* __restrict__ ubeg, int nmat) {
-    const int64_t u = blockIdx.x;
-    const int m = find_unit_owner(ubeg, nmat, u);
-    const SinqMat sm = mats[m];
-    const int local = (int)(u - ubeg[m]);
-    const int chunk = local / sm.col_tiles;
-    const int tile = local - chunk * sm.col_tiles;
-    const int cv = tile * kT + threadIdx.x;
-    if (cv >= (sm.cols >> 3)) return;
-    if (sm.dtype == WOQ_BF16) colpart_body<WOQ_BF16>(sm, chunk, cv);
-    else colpart_body<WOQ_F32>(sm, chunk, cv);
-}
-
-__global__ __launch_bounds__(kT) void k_colfin(const SinqMat* __restrict__ mats,
-                                               const int64_t* __restrict__ ubeg, int nmat) {
-    const int64_t u = blockIdx.x;
-    const int m = find_unit_owner(ubeg, nmat, u);
-    const SinqMat sm = mats[m];
-    const int j = (int)(u - ubeg[m]) * kT + threadIdx.x;
-    if (j >= sm.cols) return;
-    double S = 0.0, Q = 0.0;
-    for (int c = 0; c < sm.n_chunks; ++c) {
-        const float2 p = sm.part[(size_t)c * sm.cols + j];
-        S += (double)p.x;
-        Q += (double)p.y;
+    sS[sl][c] = S;
+    sQ[sl][c] = Q;
+    sMn[sl][c] = mn;
+    sMx[sl][c] = mx;
+    __syncthreads();
+    if (sl != 0 || j >= sm.cols) return;
+    S = 0.0;
+    Q = 0.0;
+#pragma unroll
+    for (int q = 0; q < kRedSlices; ++q) {
+        S += sS[q][c];
+        Q += sQ[q][c];
+        mn = fminf(mn, sMn[q][c]);
+        mx = fmaxf(mx, sMx[q][c]);
     }
     const double n = (double)sm.rows;
     const double mean = S / n;
     const double var = Q / n - mean * mean;
-    const float t = var > 0.0 ? (float)sqrt(var) : 1.0f;
-    sm.t[j] = t;
-    sm.u[j] = __fdiv_rn(1.0f, t);
+    const bool constant = (DT == WOQ_F32) && !(mx > mn);
+    const float t = (var > 0.0 && !constant) ? (float)sqrt(var) : 1.0f;
+    gstore<float>(sm.t + j, t);
+    gstore<float>(sm.u + j, __fdiv_rn(1.0f, t));
+}
+
+template <int DT, int NV>
+hipError_t launch_pass(const SinqMat* mats, const int64_t* sbeg, int nmat, int64_t n_strips,
+                       int nt, int cols_max, bool first, hipStream_t s) {
+    const size_t lds = PassCfg<DT, NV>::U_LDS ? sizeof(float) * ((size_t)cols_max + 8) : 0;
+    if (first)
+        k_sinq_pass<DT, NV, true><<<dim3((unsigned)n_strips), dim3(nt), lds, s>>>(mats, sbeg, nmat);
+    else
+        k_sinq_pass<DT, NV, false><<<dim3((unsigned)n_strips), dim3(nt), lds, s>>>(mats, sbeg, nmat);
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_pass_dt(const SinqMat* mats, const int64_t* sbeg, int nmat, int64_t n_strips,
+                          SinqShape sh, int cols_max, bool first, hipStream_t s) {
+    switch (sh.nv) {
+        case 1: return launch_pass<DT, 1>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
+        case 2: return launch_pass<DT, 2>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
+        case 3: return launch_pass<DT, 3>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
+        case 4: return launch_pass<DT, 4>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
+        case 5: return launch_pass<DT, 5>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
+        case 6: return launch_pass<DT, 6>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
+        case 7: return launch_pass<DT, 7>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
+        default: return launch_pass<DT, 8>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
+    }
 }
 
 }  // namespace
 
-hipError_t sinq_rows(const SinqMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                     bool first, bool /*any_f32*/, hipStream_t s) {
-    if (n_units <= 0) return hipSuccess;
-    k_rows<<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, first ? 1 : 0);
-    return hipGetLastError();
+// NV = ceil(vectors / 256) (up to 256 threads, two workgroups per CU) while
+// that is <= 8, else ceil(vectors / 512) (up to 512 threads); NT is the
+// smallest multiple of 64 covering the row, e.g. 14336 columns -> 256
+// threads x 7 vectors.
+SinqShape sinq_shape(int cols, int dtype) {
+    const int nvec = cols / 8;
+    if (cols <= (dtype == WOQ_BF16 ? 4096 : 2048)) {
+        const int nvl = (nvec + 63) / 64;
+        return SinqShape{256, nvl < 1 ? 1 : nvl, 1};
+    }
+    int nv = (nvec + 255) / 256;
+    if (nv > 8) nv = (nvec + 511) / 512;
+    if (nv < 1) nv = 1;
+    const int nt = ((nvec + nv - 1) / nv + 63) / 64 * 64;
+    return SinqShape{nt, nv, 0};
 }
 
-hipError_t sinq_colpart(const SinqMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                        bool /*any_f32*/, hipStream_t s) {
-    if (n_units <= 0) return hipSuccess;
-    k_colpart<<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat);
-    return hipGetLastError();
-}
+int sinq_tile_rows(int dtype, int nv) { return tile_rows(dtype, nv); }
 
-hipError_t sinq_colfin(const SinqMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                       hipStream_t s) {
-    if (n_units <= 0) return hipSuccess;
-    k_colfin<<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat);
+hipError_t sinq_iteration(const SinqMat* mats, const int64_t* sbeg, const int64_t* cbeg, int nmat,
+                          int64_t n_strips, int64_t n_col_units, int dtype, SinqShape sh,
+                          int cols_max, bool first, hipStream_t s) {
+    hipError_t e;
+    if (sh.mode == 1)
+        e = dtype == WOQ_BF16 ? launch_wave_dt<WOQ_BF16>(mats, sbeg, nmat, n_strips, sh.nv, first, s)
+                              : launch_wave_dt<WOQ_F32>(mats, sbeg, nmat, n_strips, sh.nv, first, s);
+    else
+        e = dtype == WOQ_BF16
+                ? launch_pass_dt<WOQ_BF16>(mats, sbeg, nmat, n_strips, sh, cols_max, first, s)
+                : launch_pass_dt<WOQ_F32>(mats, sbeg, nmat, n_strips, sh, cols_max, first, s);
+    if (e != hipSuccess) return e;
+    if (dtype == WOQ_BF16)
+        k_sinq_reduce<WOQ_BF16><<<dim3((unsigned)n_col_units), dim3(256), 0, s>>>(mats, cbeg, nmat, first ? 1 : 0);
+    else
+        k_sinq_reduce<WOQ_F32><<<dim3((unsigned)n_col_units), dim3(256), 0, s>>>(mats, cbeg, nmat, first ? 1 : 0);
     return hipGetLastError();
 }
 

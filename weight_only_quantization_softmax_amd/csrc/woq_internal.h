@@ -16,6 +16,61 @@ namespace woq {
 constexpr int kWave = 64;
 
 // ---------------------------------------------------------------- helpers
+// Loads / stores through global (address space 1) pointers: the descriptor
+// tables hold generic pointers, which would otherwise become flat accesses.
+template <class T>
+__device__ __forceinline__ T gload(const void* p) {
+    typedef const __attribute__((address_space(1))) T* gptr;
+    return *(gptr)(p);
+}
+template <class T>
+__device__ __forceinline__ void gstore(void* p, T v) {
+    typedef __attribute__((address_space(1))) T* gptr;
+    *(gptr)(p) = v;
+}
+// 16- and 8-byte vector forms (HIP's uint4 / float4 wrappers do not bind to
+// address-space-qualified pointers, native vector types do).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 gload_u4(const void* p) {
+    const u32x4 v = gload<u32x4>(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 gload_f4(const void* p) {
+    const f32x4 v = gload<f32x4>(p);
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float2 gload_f2(const void* p) {
+    const f32x2 v = gload<f32x2>(p);
+    return make_float2(v.x, v.y);
+}
+__device__ __forceinline__ void gstore_f4(void* p, float a, float b, float c, float d) {
+    f32x4 v;
+    v.x = a; v.y = b; v.z = c; v.w = d;
+    gstore<f32x4>(p, v);
+}
+
+// Cross-lane exchanges on VALU (no LDS round trip): gfx950 permlane swaps
+// exchange 32- and 16-lane halves; DPP handles partners within a row.
+__device__ __forceinline__ void swap32(float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap16(float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppMirror8 = 0x141;     // row_half_mirror: lane i <-> 7 - i in each 8
+constexpr int kDppXor8 = 0x128;        // row_ror:8 within 16-lane rows
 __device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
@@ -81,19 +136,19 @@ struct EntMat {
     int32_t slot;       // index of this matrix in the caller's h_mat
 };
 
-// Sinkhorn: one entry per matrix.
+// Sinkhorn: one entry per matrix.  A matrix is cut into row strips, one
+// workgroup per strip; each strip writes its column partial sums to part.
 struct SinqMat {
     const void* data;
     float* s;           // caller's row scales [rows]
     float* t;           // caller's column scales [cols]
-    float* v;           // workspace 1/s [rows]
     float* u;           // workspace 1/t [cols]
-    float2* part;       // workspace column partials [n_chunks][cols]
+    void* part;         // workspace column partials [n_strips][cols] (float2 / float4)
     int32_t rows, cols;
     int32_t dtype;
-    int32_t n_chunks;   // row chunks of the column pass
-    int32_t chunk_rows;
-    int32_t col_tiles;  // 2048-column tiles of the column pass
+    int32_t n_strips;
+    int32_t strip_rows;
+    int32_t pad;
 };
 
 // Quantise / dequantise / ternary: one entry per matrix.

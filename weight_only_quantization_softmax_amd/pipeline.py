@@ -1,0 +1,221 @@
+"""EWQ tier dispatch over the five entry points (host orchestration only).
+
+[EWQ] "Giai ma EWQ & FastEWQ" (2kvn.com), section "EWQ hoat dong nhu the
+nao?", step 2: the lowest-entropy blocks (H <= T) are quantised
+aggressively, the middle ones (T < H < mu) moderately, the rest are kept.
+What each tier does is a parameter of the pass:
+
+  "sinq"     SINQ Sinkhorn balancing, then group RTN at (bits, group)
+  "int8row"  8-bit RTN with one group per row, no balancing
+  "ternary"  ternary {-1, 0, +1} with a per-row scale
+  "keep"     left as is
+
+A :class:`QuantPass` is prepared once for a fixed set of device-resident
+matrices: every output buffer and workspace is allocated up front (per tier
+assignment), so :meth:`QuantPass.run` only launches library calls and reads
+the tiers back (the one host synchronisation of the pass).
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, List, Optional, Sequence
+
+import torch
+
+from . import _lib
+
+ACTIONS = ("sinq", "int8row", "ternary", "keep")
+
+
+def _mat_arr(ts):
+    return _lib.mat_array((t.data_ptr(), _lib.WOQ_BF16 if t.dtype == torch.bfloat16 else _lib.WOQ_F32,
+                           t.shape[0], t.shape[1]) for t in ts)
+
+
+def _ws(op, mats, group, dev):
+    lib = _lib.load()
+    out = ctypes.c_size_t(0)
+    _lib.check("woq_workspace_size", lib.woq_workspace_size(op, _mat_arr(mats), len(mats), group,
+                                                             ctypes.byref(out)))
+    return torch.empty(max(out.value, 256), dtype=torch.uint8, device=dev)
+
+
+class _Call:
+    """One prepared library call: name, bound ctypes arguments, kept-alive objects."""
+
+    def __init__(self, name: str, fn, args, keep, kind: str, nbytes: int):
+        self.name, self.fn, self.args, self.keep, self.kind, self.nbytes = name, fn, args, keep, kind, nbytes
+
+    def __call__(self, stream_handle):
+        _lib.check(self.name, self.fn(*self.args, stream_handle))
+
+
+class QuantPass:
+    def __init__(self, mats: Sequence[torch.Tensor], block_id: Sequence[int], n_blocks: int, *,
+                 iters: int, bits: int, group: int, x: float = 1.0, tiered: bool = True,
+                 actions: Sequence[str] = ("sinq", "int8row", "keep"),
+                 sinq_batch_bytes: int = 0):
+        for a in actions:
+            if a not in ACTIONS:
+                raise ValueError(a)
+        self.lib = _lib.load()
+        self.mats = list(mats)
+        self.block_id = [int(b) for b in block_id]
+        self.n_blocks = n_blocks
+        self.iters, self.bits, self.group, self.x = iters, bits, group, x
+        self.tiered = tiered
+        self.actions = tuple(actions)
+        self.sinq_batch_bytes = sinq_batch_bytes
+        dev = self.mats[0].device
+        self.device = dev
+        n = len(self.mats)
+        self.h_mat = torch.empty(n, dtype=torch.float64, device=dev)
+        self.h_block = torch.empty(n_blocks, dtype=torch.float64, device=dev)
+        self.stats = torch.empty(3, dtype=torch.float64, device=dev)
+        self.tier = torch.empty(n_blocks, dtype=torch.int32, device=dev)
+        self.order = torch.empty(n_blocks, dtype=torch.int32, device=dev)
+        self._ent_ws = _ws(_lib.OP_ENTROPY, self.mats, 0, dev)
+        self._ent_mats = _mat_arr(self.mats)
+        self._bid = (ctypes.c_int32 * n)(*self.block_id)
+        self._plans: Dict[tuple, List[_Call]] = {}
+        self.outputs: Dict[int, dict] = {}
+        self.bytes_in = sum(m.numel() * m.element_size() for m in self.mats)
+
+    # ------------------------------------------------------------ planning
+    def _entropy_call(self) -> _Call:
+        args = (self._ent_mats, len(self.mats), self._bid, self.n_blocks, float(self.x),
+                self.h_mat.data_ptr(), self.h_block.data_ptr(), self.stats.data_ptr(),
+                self.tier.data_ptr(), self.order.data_ptr(), self._ent_ws.data_ptr(),
+                self._ent_ws.numel())
+        return _Call("ewq_block_entropy", self.lib.ewq_block_entropy, args, None, "entropy",
+                     self.bytes_in)
+
+    def _sinq_calls(self, idx: List[int]) -> List[_Call]:
+        dev = self.device
+        mats = [self.mats[i] for i in idx]
+        s = [torch.empty(m.shape[0], dtype=torch.float32, device=dev) for m in mats]
+        t = [torch.empty(m.shape[1], dtype=torch.float32, device=dev) for m in mats]
+        codes = [torch.empty(m.shape[0], m.shape[1] * self.bits // 8, dtype=torch.uint8, device=dev)
+                 for m in mats]
+        g = self.group
+        scales = [torch.empty(m.shape[0], m.shape[1] // g, dtype=torch.float32, device=dev) for m in mats]
+        zeros = [torch.empty(m.shape[0], m.shape[1] // g, dtype=torch.uint8, device=dev) for m in mats]
+        for k, i in enumerate(idx):
+            self.outputs[i] = {"action": "sinq", "s": s[k], "t": t[k], "codes": codes[k],
+                               "scales": scales[k], "zeros": zeros[k]}
+        calls = []
+        # optional batching of the Sinkhorn step (bytes per call)
+        batches, cur, cur_b = [], [], 0
+        for k, m in enumerate(mats):
+            b = m.numel() * m.element_size()
+            if cur and self.sinq_batch_bytes and cur_b + b > self.sinq_batch_bytes:
+                batches.append(cur)
+                cur, cur_b = [], 0
+            cur.append(k)
+            cur_b += b
+        if cur:
+            batches.append(cur)
+        for bk in batches:
+            bm = [mats[k] for k in bk]
+            arr = _mat_arr(bm)
+            sp = _lib.ptr_array(s[k].data_ptr() for k in bk)
+            tp = _lib.ptr_array(t[k].data_ptr() for k in bk)
+            ws = _ws(_lib.OP_SINQ, bm, 0, dev)
+            nb = sum(m.numel() * m.element_size() for m in bm)
+            calls.append(_Call("sinq_balance", self.lib.sinq_balance,
+                               (arr, len(bm), self.iters, sp, tp, ws.data_ptr(), ws.numel()),
+                               (arr, sp, tp, ws), "sinq", nb))
+            cp = _lib.ptr_array(codes[k].data_ptr() for k in bk)
+            scp = _lib.ptr_array(scales[k].data_ptr() for k in bk)
+            zp = _lib.ptr_array(zeros[k].data_ptr() for k in bk)
+            wsq = _ws(_lib.OP_QUANT, bm, g, dev)
+            calls.append(_Call("quant_pack_groupwise", self.lib.quant_pack_groupwise,
+                               (arr, len(bm), sp, tp, self.bits, g, cp, scp, zp, wsq.data_ptr(),
+                                wsq.numel()),
+                               (arr, sp, tp, cp, scp, zp, wsq), "quant", nb))
+        return calls
+
+    def _int8_calls(self, idx: List[int]) -> List[_Call]:
+        dev = self.device
+        mats = [self.mats[i] for i in idx]
+        codes = [torch.empty(m.shape[0], m.shape[1], dtype=torch.uint8, device=dev) for m in mats]
+        scales = [torch.empty(m.shape[0], 1, dtype=torch.float32, device=dev) for m in mats]
+        zeros = [torch.empty(m.shape[0], 1, dtype=torch.uint8, device=dev) for m in mats]
+        for k, i in enumerate(idx):
+            self.outputs[i] = {"action": "int8row", "codes": codes[k], "scales": scales[k],
+                               "zeros": zeros[k]}
+        arr = _mat_arr(mats)
+        cp = _lib.ptr_array(c.data_ptr() for c in codes)
+        scp = _lib.ptr_array(c.data_ptr() for c in scales)
+        zp = _lib.ptr_array(c.data_ptr() for c in zeros)
+        ws = _ws(_lib.OP_QUANT, mats, 0, dev)
+        nb = sum(m.numel() * m.element_size() for m in mats)
+        return [_Call("quant_pack_groupwise", self.lib.quant_pack_groupwise,
+                      (arr, len(mats), None, None, 8, 0, cp, scp, zp, ws.data_ptr(), ws.numel()),
+                      (arr, cp, scp, zp, ws), "int8row", nb)]
+
+    def _ternary_calls(self, idx: List[int]) -> List[_Call]:
+        dev = self.device
+        mats = [self.mats[i] for i in idx]
+        codes = [torch.empty(m.shape[0], m.shape[1] // 4, dtype=torch.uint8, device=dev) for m in mats]
+        beta = [torch.empty(m.shape[0], dtype=torch.float32, device=dev) for m in mats]
+        for k, i in enumerate(idx):
+            self.outputs[i] = {"action": "ternary", "codes": codes[k], "beta": beta[k]}
+        arr = _mat_arr(mats)
+        cp = _lib.ptr_array(c.data_ptr() for c in codes)
+        bp = _lib.ptr_array(c.data_ptr() for c in beta)
+        ws = _ws(_lib.OP_TERNARY, mats, 0, dev)
+        nb = sum(m.numel() * m.element_size() for m in mats)
+        return [_Call("ternary_pack", self.lib.ternary_pack,
+                      (arr, len(mats), cp, bp, ws.data_ptr(), ws.numel()),
+                      (arr, cp, bp, ws), "ternary", nb)]
+
+    def action_of_block(self, tiers) -> List[str]:
+        if not self.tiered:
+            return [self.actions[0]] * self.n_blocks
+        return [self.actions[int(t) - 1] for t in tiers]
+
+    def plan(self, tiers) -> List[_Call]:
+        key = tuple(int(t) for t in tiers)
+        if key in self._plans:
+            return self._plans[key]
+        acts = self.action_of_block(key)
+        by_action: Dict[str, List[int]] = {a: [] for a in ACTIONS}
+        for i, b in enumerate(self.block_id):
+            by_action[acts[b]].append(i)
+        calls: List[_Call] = []
+        if by_action["sinq"]:
+            calls += self._sinq_calls(by_action["sinq"])
+        if by_action["int8row"]:
+            calls += self._int8_calls(by_action["int8row"])
+        if by_action["ternary"]:
+            calls += self._ternary_calls(by_action["ternary"])
+        for i in by_action["keep"]:
+            self.outputs[i] = {"action": "keep"}
+        self._plans[key] = calls
+        return calls
+
+    # ------------------------------------------------------------ running
+    def run(self, stream: Optional[torch.cuda.Stream] = None, timers: Optional[dict] = None):
+        """One whole pass; returns the tiers (host list).  ``timers`` collects
+        (kind -> list of (start_event, end_event, bytes)) around each call."""
+        stream = stream or torch.cuda.current_stream()
+        h = stream.cuda_stream
+        calls = [self._entropy_call()]
+        self._run_calls(calls, stream, h, timers)
+        tiers = self.tier.cpu().tolist()   # the one host synchronisation
+        self._run_calls(self.plan(tiers), stream, h, timers)
+        return tiers
+
+    @staticmethod
+    def _run_calls(calls, stream, h, timers):
+        for c in calls:
+            if timers is not None:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                c(h)
+                e1.record(stream)
+                timers.setdefault(c.kind, []).append((e0, e1, c.nbytes))
+            else:
+                c(h)

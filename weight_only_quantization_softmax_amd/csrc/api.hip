@@ -120,7 +120,7 @@ EntLayout ent_layout(const woq_mat* mats, int32_t n, int32_t n_blocks) {
 // ------------------------------------------------------------------ sinkhorn
 struct SinqGroup {
     int first = 0, count = 0, dtype = 0, cols_max = 0;
-    SinqShape sh{0, 0};
+    SinqShape sh{0, 0, 0, 0};
     int64_t n_strips = 0, n_cunits = 0;
     size_t arr_off = 0;  // index of this group's first entry in sbeg / cbeg
 };
@@ -140,7 +140,7 @@ SinqLayout sinq_layout(const woq_mat* mats, int32_t n) {
     for (int i = 0; i < n; ++i) idx[i] = i;
     auto key = [&](int i) {
         const SinqShape sh = sinq_shape((int)mats[i].cols, mats[i].dtype);
-        return std::make_tuple(mats[i].dtype, sh.mode, sh.nv, sh.nt);
+        return std::make_tuple(mats[i].dtype, sh.mode, sh.nv, sh.nt, sh.rag);
     };
     std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return key(a) < key(b); });
     L.order = idx;

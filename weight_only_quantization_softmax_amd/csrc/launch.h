@@ -28,9 +28,10 @@ hipError_t ent_blocks(const int32_t* bmats, const int32_t* bbeg,
 
 // ---- Sinkhorn ([SINQ])
 // Launch shape for a matrix width: mode 1 = one wave per row (rows of at
-// most 4096 bf16 / 2048 fp32 columns, nv = vectors per lane), mode 0 = one
+// most 4096 bf16 / 1536 fp32 columns, nv = vectors per lane), mode 0 = one
 // workgroup of nt threads per row strip (nv vectors per thread).
-struct SinqShape { int nt, nv, mode; };
+// rag: lanes own unequal numbers of 8-column vectors.
+struct SinqShape { int nt, nv, mode, rag; };
 SinqShape sinq_shape(int cols, int dtype);
 // Rows per register tile of the fused pass (depends on dtype and nv).
 int sinq_tile_rows(int dtype, int nv);

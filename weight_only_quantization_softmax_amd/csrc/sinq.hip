@@ -386,57 +386,135 @@ __global__ __launch_bounds__(kMaxT) void k_sinq_pass(const SinqMat* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Wave-per-row pass for rows of at most 4096 columns (NVL = cols/512 vectors
-// of 8 per lane).  A wave owns a strip of whole rows: row statistics are
-// wave-local (DPP / permlane reductions, no workgroup barrier), lane l owns
-// columns 8*l + 512*k + e, and the column partials of each wave's strip go to
-// part[strip] directly.  The next row is loaded into the packed registers as
-// soon as the current row has been unpacked.  u lives in LDS (shared by the
-// four waves of a workgroup).
-__device__ __forceinline__ float wave_allsum(float v) {
-    float b = v;
-    swap32(v, b);
-    v += b;
-    b = v;
-    swap16(v, b);
-    v += b;
-    v += dpp<kDppXor8>(v);
-    v += dpp<kDppMirror8>(v);
-    v += dpp<kDppXor2>(v);
-    v += dpp<kDppXor1>(v);
-    return v;
+// Row moments with one pass over the registers.  Each lane accumulates its
+// own elements y = x*u - K around a lane-local shift K (its first element),
+// giving its mean and centred sum of squares M2 = sum y^2 - (sum y)^2 / n.
+// The cancellation in M2 is bounded by the lane's own spread: since K is one
+// of the lane's values, n (mean - K)^2 <= n * M2_lane, so the rounding error
+// is about eps * (n + 1) * M2_lane (n <= 64 here), far below the 1e-4
+// tolerance on the scales.  A constant row at the first step (u = 1) gives
+// y = 0 exactly and hence std 0.  Lane moments are then merged over the wave
+// with the pairwise update of Chan, Golub and LeVeque (1979):
+//   mean = (m_a n_a + m_b n_b) / n,  M2 = M2_a + M2_b + d^2 n_a n_b / n.
+// For equal counts the update is symmetric in (a, b), so every lane of the
+// butterfly computes the identical result.
+
+// Equal counts n_a = n_b: hn = n_a / 2.
+__device__ __forceinline__ void merge_eq(float& m, float& q, float pm, float pq, float hn) {
+    const float d = m - pm;
+    q = fmaf(d * d, hn, q + pq);
+    m = (m + pm) * 0.5f;
+}
+// General counts (a = own, b = partner).
+__device__ __forceinline__ void merge_gen(float& m, float& q, float& n, float pm, float pq, float pn) {
+    const float nt = n + pn;
+    const float w = nt > 0.f ? pn * __builtin_amdgcn_rcpf(nt) : 0.f;  // n_b / n
+    const float d = pm - m;
+    q = fmaf(d * d, n * w, q + pq);
+    m = fmaf(d, w, m);
+    n = nt;
 }
 
-template <int DT, int NVL, bool FIRST>
+// Merge (m, q) over the 64 lanes; every lane holds n elements.
+__device__ __forceinline__ void wave_moments_eq(float& m, float& q, float n) {
+    float bm = m, bq = q;
+    swap32(m, bm);
+    swap32(q, bq);
+    merge_eq(m, q, bm, bq, 0.5f * n);
+    bm = m;
+    bq = q;
+    swap16(m, bm);
+    swap16(q, bq);
+    merge_eq(m, q, bm, bq, n);
+    merge_eq(m, q, dpp<kDppXor8>(m), dpp<kDppXor8>(q), 2.f * n);
+    merge_eq(m, q, dpp<kDppMirror8>(m), dpp<kDppMirror8>(q), 4.f * n);
+    merge_eq(m, q, dpp<kDppXor2>(m), dpp<kDppXor2>(q), 8.f * n);
+    merge_eq(m, q, dpp<kDppXor1>(m), dpp<kDppXor1>(q), 16.f * n);
+}
+// Merge (m, q, n) over the 64 lanes with per-lane counts.  Lanes may end
+// with results that differ in the last bits; callers use lane 0's.
+__device__ __forceinline__ void wave_moments_gen(float& m, float& q, float& n) {
+    float bm = m, bq = q, bn = n;
+    swap32(m, bm);
+    swap32(q, bq);
+    swap32(n, bn);
+    merge_gen(m, q, n, bm, bq, bn);
+    bm = m;
+    bq = q;
+    bn = n;
+    swap16(m, bm);
+    swap16(q, bq);
+    swap16(n, bn);
+    merge_gen(m, q, n, bm, bq, bn);
+    merge_gen(m, q, n, dpp<kDppXor8>(m), dpp<kDppXor8>(q), dpp<kDppXor8>(n));
+    merge_gen(m, q, n, dpp<kDppMirror8>(m), dpp<kDppMirror8>(q), dpp<kDppMirror8>(n));
+    merge_gen(m, q, n, dpp<kDppXor2>(m), dpp<kDppXor2>(q), dpp<kDppXor2>(n));
+    merge_gen(m, q, n, dpp<kDppXor1>(m), dpp<kDppXor1>(q), dpp<kDppXor1>(n));
+}
+
+__device__ __forceinline__ float first_lane(float v) {
+    return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(v)));
+}
+
+// Lane moments from the shifted sums: mean K + S/n and M2 = Q - S^2/n
+// (clamped at 0 against rounding); a lane without elements gives (0, 0).
+__device__ __forceinline__ void lane_moments(float K, float S, float Q, float n, float rn,
+                                             float& m, float& q) {
+    m = n > 0.f ? fmaf(S, rn, K) : 0.f;
+    q = n > 0.f ? fmaxf(fmaf(-S, S * rn, Q), 0.f) : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// Wave-per-row pass for rows of at most 4096 bf16 (2048 fp32) columns.  A
+// wave owns a strip of whole rows, lane l owns the 8-column vectors
+// l + 64 k (k < NVL), so row statistics need no workgroup barrier and the
+// column partials of the strip stay in the lane's registers.  Rows go
+// through two packed register buffers: row r + 1 is loaded while row r is
+// processed.  u = 1/t is staged in LDS, one copy per wave (the four waves of
+// a workgroup may serve different matrices).  RAG: the row is not a
+// multiple of 512 columns, so lanes own unequal numbers of vectors.
+constexpr int kWaveU = 4096 + 8;  // LDS floats per wave: u and a zero pad
+
+template <int DT, int NVL, bool FIRST, bool RAG>
 __global__ __launch_bounds__(256) void k_sinq_wave(const SinqMat* __restrict__ mats,
                                                    const int64_t* __restrict__ wbeg, int nmat) {
     constexpr bool F32 = DT == WOQ_F32;
-    extern __shared__ float ul[];  // [cols_max + 8]: u (1 at the first step), zero pad
+    // wide bf16 rows keep only the packed row and unpack it once per pass
+    constexpr bool KEEP = F32 || NVL <= 4;
+    extern __shared__ float ul[];
     const int lane = threadIdx.x & 63;
     const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);  // global wave index
-    // the workgroup's four waves may belong to different matrices: each wave
-    // looks up its own; u is staged per wave in its own LDS quarter
     const int m = find_unit_owner(wbeg, nmat, (int64_t)gw);
     const bool live = gw < wbeg[nmat];
     const SinqMat sm = mats[live ? m : 0];
-    const int strip = gw - (int)wbeg[m];
     const int cols = sm.cols;
     const int nvec = cols >> 3;
-    float* u = ul + (threadIdx.x >> 6) * (4096 + 8);
-    for (int j = lane; j < 4096 + 8; j += 64)
-        u[j] = (j < cols) ? (FIRST ? 1.0f : gload<float>(sm.u + j)) : 0.0f;
+    float* u = ul + (threadIdx.x >> 6) * kWaveU;
+    for (int j = 4 * lane; j < kWaveU; j += 256) {
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (j < cols) v = FIRST ? f32x4{1.f, 1.f, 1.f, 1.f} : gload<f32x4>(sm.u + j);
+        *reinterpret_cast<f32x4*>(u + j) = v;
+    }
+    // the wave reads entries other lanes wrote: wait for its LDS writes
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (!live) return;
+    const int strip = gw - (int)wbeg[m];
     const int r0 = strip * sm.strip_rows;
     const int r1 = min(sm.rows, r0 + sm.strip_rows);
 
     int vk[NVL];
     bool own[NVL];
+    int nown = 0;
 #pragma unroll
     for (int k = 0; k < NVL; ++k) {
-        own[k] = lane + 64 * k < nvec;
-        vk[k] = own[k] ? lane + 64 * k : nvec - 1;
+        own[k] = !RAG || lane + 64 * k < nvec;
+        vk[k] = own[k] ? lane + 64 * k : nvec - 1;  // clamped: loads stay in bounds
+        nown += own[k] ? 1 : 0;
     }
+    const float nl = 8.f * (float)nown;           // elements of the row in this lane
+    const float rnl = nown ? 1.0f / nl : 0.f;
     const float fn = (float)cols;
+    const f32x4* u4 = reinterpret_cast<const f32x4*>(u);
 
     float cs[NVL][8], cq[NVL][8];
     float cmn[F32 ? NVL : 1][8], cmx[F32 ? NVL : 1][8];
@@ -449,71 +527,62 @@ __global__ __launch_bounds__(256) void k_sinq_wave(const SinqMat* __restrict__ m
             if constexpr (F32) { cmn[k][e] = INFINITY; cmx[k][e] = -INFINITY; }
         }
 
-    // Wide rows (NVL >= 5) keep only the packed row and unpack it again in
-    // each of the three passes (registers: 2 waves per SIMD with the
-    // prefetch); narrower rows keep the unpacked floats.
-    constexpr bool KEEP = F32 || NVL <= 4;
-    Vec8<DT> P[NVL], Cur[KEEP ? 1 : NVL];
-    float xf[KEEP ? NVL : 1][8];
-    float K = 0.f, Kn = 0.f;
-    auto load_row = [&](int row) {
+    auto load_row = [&](Vec8<DT> (&P)[NVL], int row) {
 #pragma unroll
         for (int k = 0; k < NVL; ++k) P[k] = ldv<DT>(sm.data, (int64_t)row * cols + 8 * vk[k]);
-        if constexpr (F32) Kn = ld1<DT>(sm.data, (int64_t)row * cols);
     };
-    auto xval = [&](int k, float (&x)[8]) {
+    auto process = [&](Vec8<DT> (&P)[NVL], int row) {
+        float xk[KEEP ? NVL : 1][8];
         if constexpr (KEEP) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = xf[k][e];
+            for (int k = 0; k < NVL; ++k) unpack<DT>(P[k], xk[k]);
         } else {
-            opaque<DT>(Cur[k]);
-            unpack<DT>(Cur[k], x);
+#pragma unroll
+            for (int k = 0; k < NVL; ++k) opaque<DT>(P[k]);
         }
-    };
-    if (r0 < r1) load_row(r0);
-    for (int row = r0; row < r1; ++row) {
+        auto xval = [&](int k, float (&x)[8]) {
+            if constexpr (KEEP) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = xk[k][e];
+            } else {
+                unpack<DT>(P[k], x);
+            }
+        };
+        // lane moments of x*u around K = the lane's first product
+        float S0 = 0.f, S1 = 0.f, Q0 = 0.f, Q1 = 0.f, K = 0.f;
 #pragma unroll
         for (int k = 0; k < NVL; ++k) {
-            if constexpr (KEEP) unpack<DT>(P[k], xf[k]);
-            else Cur[k] = P[k];
-        }
-        K = Kn;
-        if (row + 1 < r1) load_row(row + 1);   // prefetch into the freed registers
-        // pass A: row sum of x * u (fp32 rows shifted by their first element)
-        const float Ks = FIRST ? K : K * u[0];
-        float S = 0.f;
-#pragma unroll
-        for (int k = 0; k < NVL; ++k) {
-            const float Kk = own[k] ? Ks : 0.f;
             float x[8];
             xval(k, x);
+            const f32x4 ua = u4[2 * vk[k]], ub = u4[2 * vk[k] + 1];
+            const float uu[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
+            if (k == 0) K = x[0] * uu[0];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float uu = u[8 * (own[k] ? vk[k] : nvec) + e];
-                if constexpr (F32) S += fmaf(x[e], uu, -Kk);
-                else S = fmaf(x[e], uu, S);
+            for (int e = 0; e < 8; e += 2) {
+                float y0 = fmaf(x[e], uu[e], -K), y1 = fmaf(x[e + 1], uu[e + 1], -K);
+                if (RAG && !own[k]) { y0 = 0.f; y1 = 0.f; }
+                S0 += y0;
+                S1 += y1;
+                Q0 = fmaf(y0, y0, Q0);
+                Q1 = fmaf(y1, y1, Q1);
             }
         }
-        S = wave_allsum(S);
-        const float M = __fdiv_rn(S, fn) + Ks;
-        // pass B: centred sum of squares
-        float Q = 0.f;
-#pragma unroll
-        for (int k = 0; k < NVL; ++k) {
-            const float Mk = own[k] ? M : 0.f;
-            float x[8];
-            xval(k, x);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float y = fmaf(x[e], u[8 * (own[k] ? vk[k] : nvec) + e], -Mk);
-                Q = fmaf(y, y, Q);
-            }
+        float mm, qq;
+        lane_moments(K, S0 + S1, Q0 + Q1, nl, rnl, mm, qq);
+        if constexpr (RAG) {
+            float nn = nl;
+            wave_moments_gen(mm, qq, nn);
+        } else {
+            wave_moments_eq(mm, qq, nl);
         }
-        Q = wave_allsum(Q);
-        const float var = Q / fn;
+        const float var = first_lane(qq) / fn;
         const float s = var > 0.f ? __fsqrt_rn(var) : 1.0f;
         const float v = __fdiv_rn(1.0f, s);
         if (lane == 0) gstore<float>(sm.s + row, s);
+        if constexpr (!KEEP) {
+#pragma unroll
+            for (int k = 0; k < NVL; ++k) opaque<DT>(P[k]);
+        }
         // column partials with this row's scale
 #pragma unroll
         for (int k = 0; k < NVL; ++k) {
@@ -527,6 +596,16 @@ __global__ __launch_bounds__(256) void k_sinq_wave(const SinqMat* __restrict__ m
                 if constexpr (F32) { cmn[k][e] = fminf(cmn[k][e], z); cmx[k][e] = fmaxf(cmx[k][e], z); }
             }
         }
+    };
+
+    Vec8<DT> PA[NVL], PB[NVL];
+    if (r0 < r1) load_row(PA, r0);
+    for (int row = r0; row < r1; row += 2) {
+        if (row + 1 < r1) load_row(PB, row + 1);
+        process(PA, row);
+        if (row + 1 >= r1) break;
+        if (row + 2 < r1) load_row(PA, row + 2);
+        process(PB, row + 1);
     }
 #pragma unroll
     for (int k = 0; k < NVL; ++k) {
@@ -545,6 +624,16 @@ __global__ __launch_bounds__(256) void k_sinq_wave(const SinqMat* __restrict__ m
     }
 }
 
+template <int DT, int NVL, bool RAG>
+hipError_t launch_wave(const SinqMat* mats, const int64_t* wbeg, int nmat, int64_t n_waves,
+                       bool first, hipStream_t s) {
+    const size_t lds = 4 * sizeof(float) * kWaveU;
+    const unsigned grid = (unsigned)((n_waves + 3) / 4);
+    if (first) k_sinq_wave<DT, NVL, true, RAG><<<dim3(grid), dim3(256), lds, s>>>(mats, wbeg, nmat);
+    else k_sinq_wave<DT, NVL, false, RAG><<<dim3(grid), dim3(256), lds, s>>>(mats, wbeg, nmat);
+    return hipGetLastError();
+}
+
 template <int DT, int NVL>
 hipError_t launch_wave(const SinqMat* mats, const int64_t* wbeg, int nmat, int64_t n_waves,
                        bool first, hipStream_t s) {
@@ -555,18 +644,35 @@ hipError_t launch_wave(const SinqMat* mats, const int64_t* wbeg, int nmat, int64
     return hipGetLastError();
 }
 
-template <int DT>
-hipError_t launch_wave_dt(const SinqMat* mats, const int64_t* wbeg, int nmat, int64_t n_waves,
+template <int DT, bool RAG>
+hipError_t launch_wave_nv(const SinqMat* mats, const int64_t* wbeg, int nmat, int64_t n_waves,
                           int nvl, bool first, hipStream_t s) {
     switch (nvl) {
-        case 1: return launch_wave<DT, 1>(mats, wbeg, nmat, n_waves, first, s);
-        case 2: return launch_wave<DT, 2>(mats, wbeg, nmat, n_waves, first, s);
-        case 3: return launch_wave<DT, 3>(mats, wbeg, nmat, n_waves, first, s);
-        case 4: return launch_wave<DT, 4>(mats, wbeg, nmat, n_waves, first, s);
-        case 5: return launch_wave<DT, 5>(mats, wbeg, nmat, n_waves, first, s);
-        case 6: return launch_wave<DT, 6>(mats, wbeg, nmat, n_waves, first, s);
-        case 7: return launch_wave<DT, 7>(mats, wbeg, nmat, n_waves, first, s);
-        default: return launch_wave<DT, 8>(mats, wbeg, nmat, n_waves, first, s);
+        case 1: return launch_wave<DT, 1, RAG>(mats, wbeg, nmat, n_waves, first, s);
+        case 2: return launch_wave<DT, 2, RAG>(mats, wbeg, nmat, n_waves, first, s);
+        case 3: return launch_wave<DT, 3, RAG>(mats, wbeg, nmat, n_waves, first, s);
+        case 4: return launch_wave<DT, 4, RAG>(mats, wbeg, nmat, n_waves, first, s);
+        case 5: return launch_wave<DT, 5, RAG>(mats, wbeg, nmat, n_waves, first, s);
+        case 6: return launch_wave<DT, 6, RAG>(mats, wbeg, nmat, n_waves, first, s);
+        case 7: return launch_wave<DT, 7, RAG>(mats, wbeg, nmat, n_waves, first, s);
+        default: return launch_wave<DT, 8, RAG>(mats, wbeg, nmat, n_waves, first, s);
+    }
+}
+
+template <int DT>
+hipError_t launch_wave_dt(const SinqMat* mats, const int64_t* wbeg, int nmat, int64_t n_waves,
+                          SinqShape sh, bool first, hipStream_t s) {
+    if (sh.rag) return launch_wave_nv<DT, true>(mats, wbeg, nmat, n_waves, sh.nv, first, s);
+    return launch_wave_nv<DT, false>(mats, wbeg, nmat, n_waves, sh.nv, first, s);
+}
+// fp32 rows use the wave pass up to kWaveMaxF32 vectors per lane only.
+template <bool RAG>
+hipError_t launch_wave_f32(const SinqMat* mats, const int64_t* wbeg, int nmat, int64_t n_waves,
+                           int nvl, bool first, hipStream_t s) {
+    switch (nvl) {
+        case 1: return launch_wave<WOQ_F32, 1, RAG>(mats, wbeg, nmat, n_waves, first, s);
+        case 2: return launch_wave<WOQ_F32, 2, RAG>(mats, wbeg, nmat, n_waves, first, s);
+        default: return launch_wave<WOQ_F32, 3, RAG>(mats, wbeg, nmat, n_waves, first, s);
     }
 }
 
@@ -678,15 +784,15 @@ hipError_t launch_pass_dt(const SinqMat* mats, const int64_t* sbeg, int nmat, in
 // threads x 7 vectors.
 SinqShape sinq_shape(int cols, int dtype) {
     const int nvec = cols / 8;
-    if (cols <= (dtype == WOQ_BF16 ? 4096 : 2048)) {
+    if (cols <= (dtype == WOQ_BF16 ? 4096 : 1536)) {
         const int nvl = (nvec + 63) / 64;
-        return SinqShape{256, nvl < 1 ? 1 : nvl, 1};
+        return SinqShape{256, nvl < 1 ? 1 : nvl, 1, (nvec % 64) != 0};
     }
     int nv = (nvec + 255) / 256;
     if (nv > 8) nv = (nvec + 511) / 512;
     if (nv < 1) nv = 1;
     const int nt = ((nvec + nv - 1) / nv + 63) / 64 * 64;
-    return SinqShape{nt, nv, 0};
+    return SinqShape{nt, nv, 0, nt * nv != nvec};
 }
 
 int sinq_tile_rows(int dtype, int nv) { return tile_rows(dtype, nv); }
@@ -696,8 +802,9 @@ hipError_t sinq_iteration(const SinqMat* mats, const int64_t* sbeg, const int64_
                           int cols_max, bool first, hipStream_t s) {
     hipError_t e;
     if (sh.mode == 1)
-        e = dtype == WOQ_BF16 ? launch_wave_dt<WOQ_BF16>(mats, sbeg, nmat, n_strips, sh.nv, first, s)
-                              : launch_wave_dt<WOQ_F32>(mats, sbeg, nmat, n_strips, sh.nv, first, s);
+        e = dtype == WOQ_BF16 ? launch_wave_dt<WOQ_BF16>(mats, sbeg, nmat, n_strips, sh, first, s)
+                              : (sh.rag ? launch_wave_f32<true>(mats, sbeg, nmat, n_strips, sh.nv, first, s)
+                                        : launch_wave_f32<false>(mats, sbeg, nmat, n_strips, sh.nv, first, s));
     else
         e = dtype == WOQ_BF16
                 ? launch_pass_dt<WOQ_BF16>(mats, sbeg, nmat, n_strips, sh, cols_max, first, s)

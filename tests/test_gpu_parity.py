@@ -94,9 +94,13 @@ def test_single_block_is_tier_one():
 
 
 # ------------------------------------------------------------------ sinkhorn
+# wave pass (rows <= 4096 bf16 / 1536 fp32 columns) and workgroup pass, each
+# with rows that are and are not a whole number of lane vectors
 SINQ_CASES = [((256, 512), torch.float32), ((300, 1024), torch.bfloat16),
               ((64, 2056), torch.bfloat16), ((129, 4104), torch.bfloat16),
-              ((1408, 2048), torch.bfloat16), ((2048, 1408), torch.bfloat16), ((5, 8), torch.float32)]
+              ((1408, 2048), torch.bfloat16), ((2048, 1408), torch.bfloat16), ((5, 8), torch.float32),
+              ((96, 14336), torch.bfloat16), ((17, 8192), torch.bfloat16),
+              ((40, 2048), torch.float32), ((33, 3000), torch.float32)]
 
 
 @pytest.mark.parametrize("iters", [0, 1, 16])
@@ -117,7 +121,13 @@ def test_sinq_degenerate_lines():
     w[3, :] = 0
     w[5, :] = 0.015625       # constant row (exact bf16)
     w[:, 10] = 0
-    mats = [w.to(torch.bfloat16), torch.full((16, 32), 0.25, device=DEV).to(torch.bfloat16)]
+    wide = _rm(24, 8192, 8).float()
+    wide[2, :] = -0.5        # constant rows and a zero column through the workgroup pass
+    wide[:, 77] = 0
+    wf = _rm(20, 2048, 9, torch.float32)
+    wf[4, :] = 0.1           # constant fp32 row (not exact in bf16)
+    mats = [w.to(torch.bfloat16), torch.full((16, 32), 0.25, device=DEV).to(torch.bfloat16),
+            wide.to(torch.bfloat16), wf]
     s, t = woq.sinq_balance(mats, 6)
     for i, m in enumerate(mats):
         s_ref, t_ref = oracle.sinkhorn_std(_np(m), 6)
@@ -125,6 +135,7 @@ def test_sinq_degenerate_lines():
         np.testing.assert_allclose(t[i].cpu().numpy(), t_ref, rtol=1e-5)
     assert s[0][3].item() == 1.0 and t[0][10].item() == 1.0
     assert torch.all(s[1] == 1) and torch.all(t[1] == 1)
+    assert t[2][77].item() == 1.0
 
 
 def test_sinq_deterministic():

@@ -82,51 +82,6 @@ __device__ __forceinline__ void unpack(const Vec8<DT>& r, float (&x)[8]) {
     }
 }
 
-template <int N> struct Log2 { static constexpr int v = 1 + Log2<N / 2>::v; };
-template <> struct Log2<1> { static constexpr int v = 0; };
-
-// One split level of the reduce-scatter through a DPP pairing: lanes with
-// `up` set keep the upper half of the values.
-template <int CTRL, int HALF>
-__device__ __forceinline__ void split_dpp(float* a, bool up) {
-#pragma unroll
-    for (int i = 0; i < HALF; ++i) {
-        const float send = up ? a[i] : a[i + HALF];
-        const float keep = up ? a[i + HALF] : a[i];
-        a[i] = keep + dpp<CTRL>(send);
-    }
-}
-
-// Butterfly reduce-scatter of N values (power of two <= 64) over a wave:
-// afterwards lane l holds the wave total of value index l >> (6 - log2 N).
-// Partners per level: lane ^ 32, ^ 16 (permlane swaps), ^ 8, the mirror
-// within 8 lanes, ^ 2, ^ 1 (DPP); the kept half is chosen by lane bits
-// 5, 4, 3, 2, 1, 0 in that order.
-template <int N>
-__device__ __forceinline__ float wave_reduce_scatter(float (&a)[N], int lane) {
-    constexpr int L = Log2<N>::v;
-    if constexpr (L >= 1) {
-#pragma unroll
-        for (int i = 0; i < N / 2; ++i) { swap32(a[i], a[i + N / 2]); a[i] += a[i + N / 2]; }
-    }
-    if constexpr (L >= 2) {
-#pragma unroll
-        for (int i = 0; i < N / 4; ++i) { swap16(a[i], a[i + N / 4]); a[i] += a[i + N / 4]; }
-    }
-    if constexpr (L >= 3) split_dpp<kDppXor8, N / 8>(a, (lane & 8) != 0);
-    if constexpr (L >= 4) split_dpp<kDppMirror8, N / 16>(a, (lane & 4) != 0);
-    if constexpr (L >= 5) split_dpp<kDppXor2, N / 32>(a, (lane & 2) != 0);
-    if constexpr (L >= 6) split_dpp<kDppXor1, N / 64>(a, (lane & 1) != 0);
-    float r = a[0];
-    if constexpr (L < 1) { float b = r; swap32(r, b); r += b; }
-    if constexpr (L < 2) { float b = r; swap16(r, b); r += b; }
-    if constexpr (L < 3) r += dpp<kDppXor8>(r);
-    if constexpr (L < 4) r += dpp<kDppMirror8>(r);
-    if constexpr (L < 5) r += dpp<kDppXor2>(r);
-    if constexpr (L < 6) r += dpp<kDppXor1>(r);
-    return r;
-}
-
 // Rows per register tile, per dtype and vectors per thread.
 constexpr int tile_rows(int dt, int nv) {
     return dt == WOQ_BF16 ? (nv == 1 ? 8 : (nv == 2 ? 4 : (nv <= 4 ? 2 : 1))) : (nv == 1 ? 4 : (nv == 2 ? 2 : 1));
@@ -135,7 +90,6 @@ constexpr int tile_rows(int dt, int nv) {
 template <int DT, int NV>
 struct PassCfg {
     static constexpr int R = tile_rows(DT, NV);
-    static constexpr int NVAL = 2 * R;
     static constexpr bool U_LDS = NV >= 3;
     static constexpr bool F32 = DT == WOQ_F32;
     // wide rows: unpack bf16 again for each pass instead of keeping the
@@ -155,234 +109,6 @@ __device__ __forceinline__ void opaque(Vec8<DT>& r) {
 // "memory" clobber keeps the compiler from moving LDS accesses across.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-template <int DT, int NV, bool FIRST>
-__global__ __launch_bounds__(kMaxT) void k_sinq_pass(const SinqMat* __restrict__ mats,
-                                                     const int64_t* __restrict__ sbeg, int nmat) {
-    using C = PassCfg<DT, NV>;
-    constexpr int R = C::R;
-    constexpr int NVAL = C::NVAL;
-    __shared__ float red[2][kMaxT / 64][NVAL];
-    extern __shared__ float ulds[];  // u [cols + 8] when U_LDS
-
-    const int m = find_unit_owner(sbeg, nmat, (int64_t)blockIdx.x);
-    const SinqMat sm = mats[m];
-    const int strip = (int)(blockIdx.x - sbeg[m]);
-    const int r0 = strip * sm.strip_rows;
-    const int r1 = min(sm.rows, r0 + sm.strip_rows);
-    const int NT = blockDim.x;
-    const int nw = NT >> 6;
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int nvec = sm.cols >> 3;
-    const int64_t cols = sm.cols;
-    const float fn = (float)sm.cols;
-
-    int vk[NV], ui[NV];
-    bool own[NV];
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-        own[k] = tid + NT * k < nvec;
-        vk[k] = own[k] ? tid + NT * k : nvec - 1;  // clamped: loads stay in bounds
-        ui[k] = own[k] ? vk[k] : nvec;              // LDS index: zero pad for non-owned
-    }
-    // Row multipliers u (0 for vectors this thread does not own).
-    float uu[C::U_LDS ? 1 : NV][8];
-    const float u0 = FIRST ? 1.0f : gload<float>(sm.u);
-    if constexpr (C::U_LDS) {
-        for (int j = tid; j < sm.cols + 8; j += NT)
-            ulds[j] = j < sm.cols ? (FIRST ? 1.0f : gload<float>(sm.u + j)) : 0.0f;
-        __syncthreads();
-    } else {
-#pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            const float o = own[k] ? 1.0f : 0.0f;
-            if constexpr (FIRST) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) uu[k][e] = o;
-            } else {
-                const float4 a = gload_f4(sm.u + 8 * vk[k]);
-                const float4 b = gload_f4(sm.u + 8 * vk[k] + 4);
-                uu[k][0] = a.x * o; uu[k][1] = a.y * o; uu[k][2] = a.z * o; uu[k][3] = a.w * o;
-                uu[k][4] = b.x * o; uu[k][5] = b.y * o; uu[k][6] = b.z * o; uu[k][7] = b.w * o;
-            }
-        }
-    }
-
-    float cs[NV][8], cq[NV][8];
-    float cmn[C::F32 ? NV : 1][8], cmx[C::F32 ? NV : 1][8];
-#pragma unroll
-    for (int k = 0; k < NV; ++k)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            cs[k][e] = 0.f;
-            cq[k][e] = 0.f;
-            if constexpr (C::F32) { cmn[k][e] = INFINITY; cmx[k][e] = -INFINITY; }
-        }
-
-    int buf = 0;
-    // Sum `val` over the workgroup: wave reduce-scatter, LDS exchange, then
-    // every wave adds the wave totals in wave order; lane r (< N) returns
-    // total r.  N values, power of two.
-    auto wg_sum = [&](auto& val, auto nconst) -> float {
-        constexpr int N = decltype(nconst)::value;
-        constexpr int SHN = 6 - Log2<N>::v;
-        const float tot = wave_reduce_scatter<N>(val, lane);
-        if ((lane & ((1 << SHN) - 1)) == 0) red[buf][wid][lane >> SHN] = tot;
-        lds_barrier();
-        float acc = 0.f;
-        if (lane < N)
-            for (int w = 0; w < nw; ++w) acc += red[buf][w][lane];
-        buf ^= 1;
-        return acc;
-    };
-
-    // F32 rows are first shifted by their first element (exactly 0 for a
-    // constant row whatever the rounding of the sums); bf16 sums of a
-    // constant row are exact, so no shift is needed there.
-    auto load_tile = [&](Vec8<DT> (&d)[R][NV], float (&km)[R], int rb) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int64_t row = min(rb + r, r1 - 1);  // clamped into the strip
-            if constexpr (C::F32) km[r] = ld1<DT>(sm.data, row * cols);
-            else km[r] = 0.f;
-#pragma unroll
-            for (int k = 0; k < NV; ++k) d[r][k] = ldv<DT>(sm.data, row * cols + 8 * vk[k]);
-        }
-    };
-    auto uval = [&](int k, int e) -> float { return C::U_LDS ? ulds[8 * ui[k] + e] : uu[k][e]; };
-
-    // FULLT: every row of the tile lies in the strip (no masking needed)
-    auto process = [&](Vec8<DT> (&d)[R][NV], const float (&km)[R], int rb, auto fullc) {
-        constexpr bool FULLT = decltype(fullc)::value;
-        // values of the tile as floats (kept when registers allow)
-        float xf[C::REUNPACK ? 1 : R][C::REUNPACK ? 1 : NV][8];
-        if constexpr (!C::REUNPACK) {
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int k = 0; k < NV; ++k) unpack<DT>(d[r][k], xf[r][k]);
-        }
-        auto xval = [&](int r, int k, float (&x)[8]) {
-            if constexpr (C::REUNPACK) { opaque<DT>(d[r][k]); unpack<DT>(d[r][k], x); }
-            else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = xf[r][k][e];
-            }
-        };
-        // ---- row statistics of x = w * u, two passes (mean, then centred
-        //      squares): exact zero for constant rows, no cancellation
-        float sv[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const float K = km[r] * (FIRST ? 1.0f : u0);
-            float S = 0.f;
-#pragma unroll
-            for (int k = 0; k < NV; ++k) {
-                const float Kk = own[k] ? K : 0.f;
-                float x[8];
-                xval(r, k, x);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    if constexpr (C::F32) S += fmaf(x[e], uval(k, e), -Kk);
-                    else S = fmaf(x[e], uval(k, e), S);
-                }
-            }
-            sv[r] = S;
-        }
-        const float St = wg_sum(sv, std::integral_constant<int, R>{});
-        const float ms = __fdiv_rn(St, fn);  // lane r: mean of row r (shifted)
-        float qv[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const float M = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(ms), r)) +
-                            km[r] * (FIRST ? 1.0f : u0);
-            float Q = 0.f;
-#pragma unroll
-            for (int k = 0; k < NV; ++k) {
-                const float Mk = own[k] ? M : 0.f;
-                float x[8];
-                xval(r, k, x);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float y = fmaf(x[e], uval(k, e), -Mk);
-                    Q = fmaf(y, y, Q);
-                }
-            }
-            qv[r] = Q;
-        }
-        const float Qt = wg_sum(qv, std::integral_constant<int, R>{});
-        // ---- s, v for rows rb + lane (lanes < R); wave 0 writes s
-        float vv = 0.f;
-        if (lane < R) {
-            const int row = rb + lane;
-            const float var = Qt / fn;
-            const float s = var > 0.f ? __fsqrt_rn(var) : 1.0f;
-            if (row < r1) {
-                vv = __fdiv_rn(1.0f, s);
-                if (wid == 0) gstore<float>(sm.s + row, s);
-            }
-        }
-        // ---- column partials of z = w * v with the new row scales
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const float vr = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(vv), r));
-            const bool valid = rb + r < r1;
-            const float rv = valid ? 1.0f : 0.0f;  // rows past the strip add nothing
-#pragma unroll
-            for (int k = 0; k < NV; ++k) {
-                float x[8];
-                xval(r, k, x);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float z = x[e] * vr;
-                    if constexpr (!FULLT) z *= rv;
-                    cs[k][e] += z;
-                    cq[k][e] = fmaf(z, z, cq[k][e]);
-                    if constexpr (C::F32) {
-                        if (FULLT || valid) { cmn[k][e] = fminf(cmn[k][e], z); cmx[k][e] = fmaxf(cmx[k][e], z); }
-                    }
-                }
-            }
-        }
-    };
-
-    // ---- tiles in pairs: the next tile's loads are issued before the
-    //      current tile is processed (two register buffers)
-    Vec8<DT> dA[R][NV], dB[R][NV];
-    float kA[R], kB[R];
-    int rb = r0;
-    if (rb < r1) load_tile(dA, kA, rb);
-    auto run = [&](Vec8<DT> (&d)[R][NV], const float (&km)[R], int at) {
-        if (at + R <= r1) process(d, km, at, std::true_type{});
-        else process(d, km, at, std::false_type{});
-    };
-    while (rb < r1) {
-        const int rn = rb + R;
-        if (rn < r1) load_tile(dB, kB, rn);
-        run(dA, kA, rb);
-        if (rn >= r1) break;
-        const int rn2 = rn + R;
-        if (rn2 < r1) load_tile(dA, kA, rn2);
-        run(dB, kB, rn);
-        rb = rn2;
-    }
-
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-        if (!own[k]) continue;
-        const int64_t c0 = (int64_t)strip * cols + 8 * vk[k];
-        if constexpr (C::F32) {
-            float4* p = reinterpret_cast<float4*>(sm.part) + c0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) gstore_f4(p + e, cs[k][e], cq[k][e], cmn[k][e], cmx[k][e]);
-        } else {
-            float4* p = reinterpret_cast<float4*>(reinterpret_cast<float2*>(sm.part) + c0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                gstore_f4(p + e, cs[k][2 * e], cq[k][2 * e], cs[k][2 * e + 1], cq[k][2 * e + 1]);
-        }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -462,6 +188,245 @@ __device__ __forceinline__ void lane_moments(float K, float S, float Q, float n,
                                              float& m, float& q) {
     m = n > 0.f ? fmaf(S, rn, K) : 0.f;
     q = n > 0.f ? fmaxf(fmaf(-S, S * rn, Q), 0.f) : 0.f;
+}
+
+// Workgroup pass for wider rows: a workgroup owns a strip of whole rows and
+// thread t owns the 8-column vectors t + NT k (k < NV).  The strip is walked
+// in tiles of R rows held in registers (the next tile's loads are in flight
+// while the current one is processed).  Per row: lane moments, merged over
+// the wave (Chan), then over the waves through LDS in wave order (one
+// barrier per tile); then the column partials of z = w * v.  RAG: NT * NV
+// exceeds the row's vectors, so threads own unequal numbers of them.
+template <int DT, int NV, bool FIRST, bool RAG>
+__global__ __launch_bounds__(kMaxT) void k_sinq_pass(const SinqMat* __restrict__ mats,
+                                                     const int64_t* __restrict__ sbeg, int nmat) {
+    using C = PassCfg<DT, NV>;
+    constexpr int R = C::R;
+    __shared__ float2 red[2][kMaxT / 64][R];
+    extern __shared__ float ulds[];  // u [cols + 8] when U_LDS
+
+    const int m = find_unit_owner(sbeg, nmat, (int64_t)blockIdx.x);
+    const SinqMat sm = mats[m];
+    const int strip = (int)(blockIdx.x - sbeg[m]);
+    const int r0 = strip * sm.strip_rows;
+    const int r1 = min(sm.rows, r0 + sm.strip_rows);
+    const int NT = blockDim.x;
+    const int nw = NT >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int nvec = sm.cols >> 3;
+    const int64_t cols = sm.cols;
+    const float fn = (float)sm.cols;
+
+    int vk[NV], ui[NV];
+    bool own[NV];
+    int nown = 0;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        own[k] = !RAG || tid + NT * k < nvec;
+        vk[k] = own[k] ? tid + NT * k : nvec - 1;  // clamped: loads stay in bounds
+        ui[k] = own[k] ? vk[k] : nvec;              // LDS index: zero pad for non-owned
+        nown += own[k] ? 1 : 0;
+    }
+    const float nl = 8.f * (float)nown;
+    const float rnl = nown ? 1.0f / nl : 0.f;
+    // elements of a row held by wave w
+    auto wave_count = [&](int w) -> float {
+        if constexpr (!RAG) return 512.f * NV;
+        int c = 0;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) c += min(64, max(0, nvec - NT * k - 64 * w));
+        return 8.f * (float)c;
+    };
+    // Row multipliers u (0 for vectors this thread does not own).
+    float uu[C::U_LDS ? 1 : NV][8];
+    if constexpr (C::U_LDS) {
+        for (int j = tid; j < sm.cols + 8; j += NT)
+            ulds[j] = j < sm.cols ? (FIRST ? 1.0f : gload<float>(sm.u + j)) : 0.0f;
+        __syncthreads();
+    } else {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const float o = own[k] ? 1.0f : 0.0f;
+            if constexpr (FIRST) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) uu[k][e] = o;
+            } else {
+                const float4 a = gload_f4(sm.u + 8 * vk[k]);
+                const float4 b = gload_f4(sm.u + 8 * vk[k] + 4);
+                uu[k][0] = a.x * o; uu[k][1] = a.y * o; uu[k][2] = a.z * o; uu[k][3] = a.w * o;
+                uu[k][4] = b.x * o; uu[k][5] = b.y * o; uu[k][6] = b.z * o; uu[k][7] = b.w * o;
+            }
+        }
+    }
+    const f32x4* u4 = reinterpret_cast<const f32x4*>(ulds);
+    auto uvec = [&](int k, float (&w)[8]) {
+        if constexpr (C::U_LDS) {
+            const f32x4 a = u4[2 * ui[k]], b = u4[2 * ui[k] + 1];
+            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+            w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] = uu[k][e];
+        }
+    };
+
+    float cs[NV][8], cq[NV][8];
+    float cmn[C::F32 ? NV : 1][8], cmx[C::F32 ? NV : 1][8];
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            cs[k][e] = 0.f;
+            cq[k][e] = 0.f;
+            if constexpr (C::F32) { cmn[k][e] = INFINITY; cmx[k][e] = -INFINITY; }
+        }
+
+    int buf = 0;
+    auto load_tile = [&](Vec8<DT> (&d)[R][NV], int rb) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t row = min(rb + r, r1 - 1);  // clamped into the strip
+#pragma unroll
+            for (int k = 0; k < NV; ++k) d[r][k] = ldv<DT>(sm.data, row * cols + 8 * vk[k]);
+        }
+    };
+
+    // FULLT: every row of the tile lies in the strip (no masking needed)
+    auto process = [&](Vec8<DT> (&d)[R][NV], int rb, auto fullc) {
+        constexpr bool FULLT = decltype(fullc)::value;
+        float xf[C::REUNPACK ? 1 : R][C::REUNPACK ? 1 : NV][8];
+        if constexpr (!C::REUNPACK) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int k = 0; k < NV; ++k) unpack<DT>(d[r][k], xf[r][k]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int k = 0; k < NV; ++k) opaque<DT>(d[r][k]);
+        }
+        auto xval = [&](int r, int k, float (&x)[8]) {
+            if constexpr (C::REUNPACK) unpack<DT>(d[r][k], x);
+            else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = xf[r][k][e];
+            }
+        };
+        // ---- lane moments per row, merged over the wave
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float S0 = 0.f, S1 = 0.f, Q0 = 0.f, Q1 = 0.f, K = 0.f;
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                float x[8], w[8];
+                xval(r, k, x);
+                uvec(k, w);
+                if (k == 0) K = x[0] * w[0];
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    float y0 = fmaf(x[e], w[e], -K), y1 = fmaf(x[e + 1], w[e + 1], -K);
+                    if (RAG && !own[k]) { y0 = 0.f; y1 = 0.f; }
+                    S0 += y0;
+                    S1 += y1;
+                    Q0 = fmaf(y0, y0, Q0);
+                    Q1 = fmaf(y1, y1, Q1);
+                }
+            }
+            float mm, qq;
+            lane_moments(K, S0 + S1, Q0 + Q1, nl, rnl, mm, qq);
+            if constexpr (RAG) {
+                float nn = nl;
+                wave_moments_gen(mm, qq, nn);
+            } else {
+                wave_moments_eq(mm, qq, nl);
+            }
+            if (lane == 0) red[buf][wid][r] = make_float2(mm, qq);
+        }
+        lds_barrier();
+        // ---- lane r < R merges row r over the waves in wave order
+        float vv = 0.f;
+        if (lane < R) {
+            const int row = rb + lane;
+            float2 a = red[buf][0][lane];
+            float M = a.x, Q = a.y, N = wave_count(0);
+            for (int w = 1; w < nw; ++w) {
+                a = red[buf][w][lane];
+                merge_gen(M, Q, N, a.x, a.y, wave_count(w));
+            }
+            const float var = Q / fn;
+            const float s = var > 0.f ? __fsqrt_rn(var) : 1.0f;
+            if (row < r1) {
+                vv = __fdiv_rn(1.0f, s);
+                if (wid == 0) gstore<float>(sm.s + row, s);
+            }
+        }
+        buf ^= 1;
+        if constexpr (C::REUNPACK) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int k = 0; k < NV; ++k) opaque<DT>(d[r][k]);
+        }
+        // ---- column partials of z = w * v with the new row scales
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float vr = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(vv), r));
+            const bool valid = rb + r < r1;
+            const float rv = valid ? 1.0f : 0.0f;  // rows past the strip add nothing
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                float x[8];
+                xval(r, k, x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float z = x[e] * vr;
+                    if constexpr (!FULLT) z *= rv;
+                    cs[k][e] += z;
+                    cq[k][e] = fmaf(z, z, cq[k][e]);
+                    if constexpr (C::F32) {
+                        if (FULLT || valid) { cmn[k][e] = fminf(cmn[k][e], z); cmx[k][e] = fmaxf(cmx[k][e], z); }
+                    }
+                }
+            }
+        }
+    };
+
+    // ---- tiles in pairs: the next tile's loads are issued before the
+    //      current tile is processed (two register buffers)
+    Vec8<DT> dA[R][NV], dB[R][NV];
+    int rb = r0;
+    if (rb < r1) load_tile(dA, rb);
+    auto run = [&](Vec8<DT> (&d)[R][NV], int at) {
+        if (at + R <= r1) process(d, at, std::true_type{});
+        else process(d, at, std::false_type{});
+    };
+    while (rb < r1) {
+        const int rn = rb + R;
+        if (rn < r1) load_tile(dB, rn);
+        run(dA, rb);
+        if (rn >= r1) break;
+        const int rn2 = rn + R;
+        if (rn2 < r1) load_tile(dA, rn2);
+        run(dB, rn);
+        rb = rn2;
+    }
+
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        if (!own[k]) continue;
+        const int64_t c0 = (int64_t)strip * cols + 8 * vk[k];
+        if constexpr (C::F32) {
+            float4* p = reinterpret_cast<float4*>(sm.part) + c0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gstore_f4(p + e, cs[k][e], cq[k][e], cmn[k][e], cmx[k][e]);
+        } else {
+            float4* p = reinterpret_cast<float4*>(reinterpret_cast<float2*>(sm.part) + c0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                gstore_f4(p + e, cs[k][2 * e], cq[k][2 * e], cs[k][2 * e + 1], cq[k][2 * e + 1]);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -750,36 +715,44 @@ __global__ __launch_bounds__(256) void k_sinq_reduce(const SinqMat* __restrict__
     gstore<float>(sm.u + j, __fdiv_rn(1.0f, t));
 }
 
-template <int DT, int NV>
+template <int DT, int NV, bool RAG>
 hipError_t launch_pass(const SinqMat* mats, const int64_t* sbeg, int nmat, int64_t n_strips,
                        int nt, int cols_max, bool first, hipStream_t s) {
     const size_t lds = PassCfg<DT, NV>::U_LDS ? sizeof(float) * ((size_t)cols_max + 8) : 0;
     if (first)
-        k_sinq_pass<DT, NV, true><<<dim3((unsigned)n_strips), dim3(nt), lds, s>>>(mats, sbeg, nmat);
+        k_sinq_pass<DT, NV, true, RAG><<<dim3((unsigned)n_strips), dim3(nt), lds, s>>>(mats, sbeg, nmat);
     else
-        k_sinq_pass<DT, NV, false><<<dim3((unsigned)n_strips), dim3(nt), lds, s>>>(mats, sbeg, nmat);
+        k_sinq_pass<DT, NV, false, RAG><<<dim3((unsigned)n_strips), dim3(nt), lds, s>>>(mats, sbeg, nmat);
     return hipGetLastError();
+}
+
+template <int DT, bool RAG>
+hipError_t launch_pass_nv(const SinqMat* mats, const int64_t* sbeg, int nmat, int64_t n_strips,
+                          SinqShape sh, int cols_max, bool first, hipStream_t s) {
+    switch (sh.nv) {
+        case 1: return launch_pass<DT, 1, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
+        case 2: return launch_pass<DT, 2, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
+        case 3: return launch_pass<DT, 3, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
+        case 4: return launch_pass<DT, 4, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
+        case 5: return launch_pass<DT, 5, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
+        case 6: return launch_pass<DT, 6, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
+        case 7: return launch_pass<DT, 7, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
+        default: return launch_pass<DT, 8, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
+    }
 }
 
 template <int DT>
 hipError_t launch_pass_dt(const SinqMat* mats, const int64_t* sbeg, int nmat, int64_t n_strips,
                           SinqShape sh, int cols_max, bool first, hipStream_t s) {
-    switch (sh.nv) {
-        case 1: return launch_pass<DT, 1>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
-        case 2: return launch_pass<DT, 2>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
-        case 3: return launch_pass<DT, 3>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
-        case 4: return launch_pass<DT, 4>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
-        case 5: return launch_pass<DT, 5>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
-        case 6: return launch_pass<DT, 6>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
-        case 7: return launch_pass<DT, 7>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
-        default: return launch_pass<DT, 8>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
-    }
+    if (sh.rag) return launch_pass_nv<DT, true>(mats, sbeg, nmat, n_strips, sh, cols_max, first, s);
+    return launch_pass_nv<DT, false>(mats, sbeg, nmat, n_strips, sh, cols_max, first, s);
 }
 
 }  // namespace
 
 // NV = ceil(vectors / 256) (up to 256 threads, two workgroups per CU) while
-// that is <= 8, else ceil(vectors / 512) (up to 512 threads); NT is the
+// that is <= 8 (bf16) or 4 (fp32), else ceil(vectors / 512) (up to 512
+// threads); NT is the
 // smallest multiple of 64 covering the row, e.g. 14336 columns -> 256
 // threads x 7 vectors.
 SinqShape sinq_shape(int cols, int dtype) {
@@ -789,7 +762,7 @@ SinqShape sinq_shape(int cols, int dtype) {
         return SinqShape{256, nvl < 1 ? 1 : nvl, 1, (nvec % 64) != 0};
     }
     int nv = (nvec + 255) / 256;
-    if (nv > 8) nv = (nvec + 511) / 512;
+    if (nv > (dtype == WOQ_BF16 ? 8 : 4)) nv = (nvec + 511) / 512;
     if (nv < 1) nv = 1;
     const int nt = ((nvec + nv - 1) / nv + 63) / 64 * 64;
     return SinqShape{nt, nv, 0, nt * nv != nvec};

@@ -11,9 +11,18 @@ transformer blocks (6.98e9 weights, 13.96 GB), resident in HBM before the
 timed region; outputs are preallocated.  The value is bf16 input bytes per
 second of wall time (GB/s, 1e9 bytes).
 
-Printed as one JSON line.  ``roofline`` describes the dominant call, timed
-with HIP events on the stream it is launched on; ``cpu_baseline`` times the
-CPU oracle on a bounded sample of the same workload.
+Printed as one JSON line.  ``roofline`` describes the dominant call (the
+Sinkhorn sweep on this workload), timed with HIP events on the stream it is
+launched on, against its algorithmic bytes (one read of every weight per
+iteration); ``traffic`` is the measured HBM traffic per call from the
+rocprofv3 FETCH_SIZE / WRITE_SIZE summary under profiles/, valid while the
+kernel source it was taken on is unchanged.  ``cpu_baseline`` times the CPU
+oracle on a bounded sample of the same workload.
+
+Two "% of HBM peak" figures are given: input bytes / time, and compulsory
+traffic / time, where compulsory traffic is the entropy read of every
+weight, a second read of every weight that is quantised (the tiers need the
+global entropy statistics first) and every output written.
 """
 from __future__ import annotations
 
@@ -28,43 +37,54 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GB/s bf16 weights quantised (+% HBM peak), Llama-8B-shaped stack, 1 GPU"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
-# plain (non-packed) fp32 VALU: 256 CU x 64 lanes x 2.4 GHz x 2 flop per FMA
-VALU_F32_PEAK_TFLOPS = 256 * 64 * 2.4e9 * 2 / 1e12
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sinq_sweep_stack8b_traffic.md")
+SINQ_SOURCES = [os.path.join(ROOT, "weight_only_quantization_softmax_amd", "csrc", f)
+                for f in ("sinq.hip", "api.hip", "woq_internal.h")]
 
 
 def _log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(wl, specs, mats, qp, tiers, budget_s=30.0):
-    """Oracle (numpy fp64 / fp32 decisions) on host cores over a sample.
+def cpu_baseline(wl, specs, mats, qp, tiers):
+    """The oracle (numpy fp64, fp32 where the decisions are fp32) on host
+    cores over a bounded sample of the workload.
 
-    Sample: one k-projection matrix (1024 x 4096 bf16) of the workload, run
-    through each stage the workload uses; the per-byte cost of each stage is
-    then applied to the workload's own tier mix.
+    Sample: the attention matrices (q, k, v, o) and the gate projection of the
+    first block (5 of the 7 matrices, 92.3 M weights), each taken through
+    every stage the workload uses (entropy; Sinkhorn + int4 group RTN + pack;
+    int8 per-row + pack; ternary + pack).  Each stage's seconds per byte on
+    the sample are applied to the workload's own tier mix.
     """
     import numpy as np
     import oracle
 
-    k = next(i for i, m in enumerate(specs) if m.name.endswith(".k"))
-    w = mats[k].float().cpu().numpy()
-    nbytes = mats[k].numel() * mats[k].element_size()
-    t0 = time.perf_counter()
-    oracle.matrix_entropy(w)
-    t_ent = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    s, t = oracle.sinkhorn_std(w, wl.iters)
-    q = oracle.quantize_groupwise_f32(w, s.astype(np.float32), t.astype(np.float32), wl.bits, wl.group)
-    oracle.pack_codes(q[0], wl.bits)
-    t_sinq = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    q = oracle.quantize_groupwise_f32(w, None, None, 8, w.shape[1])
-    oracle.pack_codes(q[0], 8)
-    t_i8 = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    qt, _ = oracle.ternary_quantize(w)
-    oracle.pack_codes((qt + 1).astype(np.uint8), 2)
-    t_ter = time.perf_counter() - t0
+    first = specs[0].block
+    pick = [i for i, m in enumerate(specs)
+            if m.block == first and m.name.split(".")[-1] in ("q", "k", "v", "o", "gate")]
+    t_ent = t_sinq = t_i8 = t_ter = 0.0
+    nbytes = 0
+    for i in pick:
+        w = mats[i].float().cpu().numpy()
+        nbytes += mats[i].numel() * mats[i].element_size()
+        t0 = time.perf_counter()
+        oracle.matrix_entropy(w)
+        t1 = time.perf_counter()
+        s, t = oracle.sinkhorn_std(w, wl.iters)
+        q = oracle.quantize_groupwise_f32(w, s.astype(np.float32), t.astype(np.float32), wl.bits,
+                                          wl.group)
+        oracle.pack_codes(q[0], wl.bits)
+        t2 = time.perf_counter()
+        q = oracle.quantize_groupwise_f32(w, None, None, 8, w.shape[1])
+        oracle.pack_codes(q[0], 8)
+        t3 = time.perf_counter()
+        qt, _ = oracle.ternary_quantize(w)
+        oracle.pack_codes((qt + 1).astype(np.uint8), 2)
+        t4 = time.perf_counter()
+        t_ent += t1 - t0
+        t_sinq += t2 - t1
+        t_i8 += t3 - t2
+        t_ter += t4 - t3
     per_byte = {"sinq": t_sinq / nbytes, "int8row": t_i8 / nbytes, "ternary": t_ter / nbytes,
                 "keep": 0.0}
     acts = qp.action_of_block(tiers)
@@ -73,10 +93,58 @@ def cpu_baseline(wl, specs, mats, qp, tiers, budget_s=30.0):
         total += m.numel() * m.element_size() * per_byte[acts[sp.block]]
     return {"value": round(qp.bytes_in / total / 1e9, 6), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": (f"one {w.shape[0]}x{w.shape[1]} bf16 matrix of the workload through entropy "
-                       f"({t_ent:.2f}s), Sinkhorn K={wl.iters} + int{wl.bits} g{wl.group} "
-                       f"({t_sinq:.2f}s), int8 per-row ({t_i8:.2f}s), ternary ({t_ter:.2f}s); "
+            "sample": (f"q, k, v, o and gate of block {first} ({nbytes / 1e9:.3f} GB bf16) through "
+                       f"entropy ({t_ent:.1f}s), Sinkhorn K={wl.iters} + int{wl.bits} g{wl.group} "
+                       f"({t_sinq:.1f}s), int8 per-row ({t_i8:.1f}s), ternary ({t_ter:.1f}s); "
                        "per-byte costs applied to the workload's tier mix; numpy, one thread")}
+
+
+def _sources_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in SINQ_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per Sinkhorn call from the committed counter summary, or None
+    if the summary is missing or the kernel sources changed since."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            vals[k.strip("`")] = v.strip().strip("`")
+    if vals.get("source_sha256") != _sources_hash():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
+def compulsory_bytes(mats, specs, acts, bits, group):
+    """Entropy read of every weight, plus a second read of each quantised
+    weight and its outputs (codes, fp32 delta + uint8 zero per group, fp32
+    per-row / per-column scales)."""
+    total = 0
+    for m, sp in zip(mats, specs):
+        r, c = m.shape
+        nb = m.numel() * m.element_size()
+        total += nb
+        a = acts[sp.block]
+        if a == "sinq":
+            total += nb + r * c * bits // 8 + r * (c // group) * 5 + 4 * (r + c)
+        elif a == "int8row":
+            total += nb + r * c + r * 5
+        elif a == "ternary":
+            total += nb + r * c // 4 + 4 * r
+    return total
 
 
 def main() -> int:
@@ -87,6 +155,8 @@ def main() -> int:
     ap.add_argument("--workload", default="stack8b")
     ap.add_argument("--sinq-batch-mb", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="run one device copy of this size first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this pass runs on one GPU; --gpus {args.gpus} is not supported "
@@ -98,6 +168,13 @@ def main() -> int:
     from weight_only_quantization_softmax_amd.pipeline import QuantPass
 
     torch.cuda.set_device(0)
+    if args.copy_probe_mb:
+        # an elementwise kernel that reads N bytes and writes N bytes
+        src = torch.zeros((args.copy_probe_mb << 20) // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     _log(f"[bench] generating workload {args.workload}")
     wl, specs, mats = woqdata.generate(args.workload, device="cuda")
     torch.cuda.synchronize()
@@ -108,17 +185,24 @@ def main() -> int:
     _log(f"[bench] {len(mats)} matrices, {qp.bytes_in / 1e9:.3f} GB; warmup {args.warmup}")
     for _ in range(args.warmup):
         tiers = qp.run()
+        _log(f"[bench] tiers {tiers}")
     torch.cuda.synchronize()
-    _log(f"[bench] tiers {tiers}")
     timers = {}
     _log(f"[bench] timing {args.steps} steps")
+    stream = torch.cuda.current_stream()
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        tiers = qp.run(timers=timers)
+    for i in range(args.steps):
+        step_ev[i][0].record(stream)
+        tiers = qp.run(stream=stream, timers=timers)
+        step_ev[i][1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
     value = qp.bytes_in / (ms / 1e3) / 1e9
+    step_ms = sorted(a.elapsed_time(b) for a, b in step_ev)
 
     per_kind = {}
     for kind, evs in timers.items():
@@ -128,18 +212,22 @@ def main() -> int:
     dominant = max(per_kind, key=lambda k: per_kind[k]["ms_per_step"])
     d = per_kind[dominant]
     launch_ms = d["ms_per_step"] / max(d["calls"], 1)
+    traffic = None
     if dominant == "sinq":
-        elems = d["bytes"] / 2
-        flops = elems * wl.iters * 8.0   # per element and iteration: 2 x (mul, add, fma)
-        achieved = flops / (launch_ms / 1e3) / 1e12
-        roof = {"bound": "alu", "achieved": round(achieved, 3), "peak": round(VALU_F32_PEAK_TFLOPS, 1),
-                "unit": "TFLOP/s", "frac": round(achieved / VALU_F32_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": "sinq_balance"}
+        # one read of every weight per iteration (row scales, column partials
+        # and the column reduction are not counted)
+        alg = d["bytes"] * wl.iters
+        kernel = "sinq_balance (K fused row/column sweeps + column reductions)"
+        traffic = measured_traffic()
     else:
-        achieved = d["bytes"] / (launch_ms / 1e3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": {"entropy": "ewq_block_entropy"}.get(dominant, dominant)}
+        alg = d["bytes"]
+        kernel = {"entropy": "ewq_block_entropy"}.get(dominant, dominant)
+    achieved = alg / (launch_ms / 1e3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
+            "algorithmic_bytes_per_launch": int(alg), "launch_ms": round(launch_ms, 4)}
+    acts = qp.action_of_block(tiers)
+    comp = compulsory_bytes(mats, specs, acts, wl.bits, wl.group)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -149,7 +237,11 @@ def main() -> int:
         "config": {"workload": args.workload, "matrices": len(mats), "blocks": wl.n_blocks,
                    "bf16_bytes": qp.bytes_in, "iters": wl.iters, "bits": wl.bits, "group": wl.group,
                    "tiers": {str(k): tiers.count(k) for k in (1, 2, 3)},
-                   "hbm_frac_input_bytes": round(value / HBM_PEAK_GBS, 4)},
+                   "hbm_frac_input_bytes": round(value / HBM_PEAK_GBS, 4),
+                   "compulsory_bytes": comp,
+                   "hbm_frac_compulsory": round(comp / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "step_ms": {"median": round(step_ms[len(step_ms) // 2], 3), "min": round(step_ms[0], 3),
+                    "max": round(step_ms[-1], 3)},
         "roofline": roof,
         "calls": {k: {"ms_per_step": round(v["ms_per_step"], 3), "calls": v["calls"]}
                   for k, v in per_kind.items()},

@@ -153,6 +153,10 @@ QUANT_CASES = [  # (rows, cols, bits, group, dtype)
     (3, 14336, 8, 0, torch.bfloat16), (20, 2048, 4, 1024, torch.bfloat16),
     (256, 512, 4, 64, torch.float32), (11, 1408, 4, 64, torch.bfloat16),
     (4, 3072, 3, 0, torch.float32), (2, 64, 8, 16, torch.float32),
+    # several 2048-column tiles with a ragged last one; groups of 600 (one
+    # wave, lanes with no vector); two 8192-column groups per row (workgroup)
+    (13, 2560, 4, 64, torch.bfloat16), (9, 6144, 4, 128, torch.bfloat16),
+    (10, 1800, 4, 600, torch.bfloat16), (4, 16384, 4, 8192, torch.bfloat16),
 ]
 
 

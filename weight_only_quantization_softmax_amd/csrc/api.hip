@@ -222,21 +222,59 @@ struct QLayout {
     size_t tab_b, ubeg_b, tab_f, ubeg_f, segs, ubeg_s, table_end, total;
     int64_t units_b = 0, units_f = 0, units_s = 0;
     int nseg = 0;
+    int nsets = 0;               // quant: number of launch sets
     std::vector<size_t> rs, ct;  // per matrix, 0 = none
 };
 
-// op: 0 quant, 1 dequant, 2 ternary
+// Quantise launch sets: kernel kind 0 = row tiles (power-of-two groups of
+// at most 512 columns), 1 = one wave per group (up to kQWaveMax columns,
+// nvl 8-column vectors per lane), 2 = one workgroup per group.
+struct QKey {
+    int dtype, kind, nvl;
+    bool operator<(const QKey& o) const {
+        return std::tie(dtype, kind, nvl) < std::tie(o.dtype, o.kind, o.nvl);
+    }
+    bool operator==(const QKey& o) const { return dtype == o.dtype && kind == o.kind && nvl == o.nvl; }
+};
+
+QKey q_key(const woq_mat& m, int32_t group) {
+    const int32_t g = eff_group(m, group);
+    if (group && small_group(group)) return QKey{m.dtype, 0, 0};
+    if (g <= kQWaveMax) {
+        int nvl = 1;
+        while (nvl * 64 * 8 < g) nvl *= 2;
+        return QKey{m.dtype, 1, nvl};
+    }
+    return QKey{m.dtype, 2, 0};
+}
+
+int64_t q_units(const woq_mat& m, int32_t group) {
+    const QKey k = q_key(m, group);
+    const int64_t ng = elems(m) / eff_group(m, group);
+    if (k.kind == 0) return cdiv(m.rows, kQTileRows) * cdiv(m.cols, kQTileCols);
+    if (k.kind == 1) return cdiv(ng, 4);
+    return ng;
+}
+
+// op: 0 quant, 1 dequant, 2 ternary.  For quant every matrix goes to the
+// "b" table, ordered by launch set, and ubeg_b holds one offset run per set.
 QLayout q_layout(const woq_mat* mats, int32_t n, int op, int32_t group,
                  const float* const* row_scale, const float* const* col_scale) {
     QLayout L;
     auto units = [&](const woq_mat& m) -> int64_t {
         if (op == 2) return m.rows;
-        if (op == 0 && !(group && small_group(group))) return elems(m) / eff_group(m, group);
+        if (op == 0) return q_units(m, group);
         return cdiv(elems(m), kQTile);
     };
     for (int32_t i = 0; i < n; ++i) {
-        if (mats[i].dtype == WOQ_BF16) { ++L.nb; L.units_b += units(mats[i]); }
+        if (op == 0 || mats[i].dtype == WOQ_BF16) { ++L.nb; L.units_b += units(mats[i]); }
         else { ++L.nf; L.units_f += units(mats[i]); }
+    }
+    if (op == 0) {
+        std::vector<QKey> keys;
+        for (int32_t i = 0; i < n; ++i) keys.push_back(q_key(mats[i], group));
+        std::sort(keys.begin(), keys.end());
+        L.nsets = (int)(std::unique(keys.begin(), keys.end()) - keys.begin());
     }
     L.rs.assign(n, 0);
     L.ct.assign(n, 0);
@@ -248,7 +286,7 @@ QLayout q_layout(const woq_mat* mats, int32_t n, int op, int32_t group,
     }
     Arena a;
     L.tab_b = a.take(sizeof(QMat) * L.nb);
-    L.ubeg_b = a.take(sizeof(int64_t) * (L.nb + 1));
+    L.ubeg_b = a.take(sizeof(int64_t) * (L.nb + std::max(L.nsets, 1)));
     L.tab_f = a.take(sizeof(QMat) * L.nf);
     L.ubeg_f = a.take(sizeof(int64_t) * (L.nf + 1));
     L.segs = a.take(sizeof(RecipSeg) * L.nseg);
@@ -454,16 +492,42 @@ int32_t quant_pack_groupwise(const woq_mat* mats, int32_t n_mats, const float* c
 
     std::vector<char> host(L.table_end, 0);
     QMat* tb = at<QMat>(host.data(), L.tab_b);
-    QMat* tf = at<QMat>(host.data(), L.tab_f);
     int64_t* ub = at<int64_t>(host.data(), L.ubeg_b);
-    int64_t* uf = at<int64_t>(host.data(), L.ubeg_f);
     RecipSeg* sg = at<RecipSeg>(host.data(), L.segs);
     int64_t* us = at<int64_t>(host.data(), L.ubeg_s);
-    ub[0] = uf[0] = us[0] = 0;
-    int ib = 0, jf = 0, ks = 0;
-    const bool small = group && small_group(group);
+    us[0] = 0;
+    int ks = 0;
     for (int32_t i = 0; i < n_mats; ++i) {
         const woq_mat& m = mats[i];
+        if (L.rs[i]) {
+            sg[ks] = RecipSeg{row_scale[i], at<float>(ws, L.rs[i]), m.rows, 0};
+            us[ks + 1] = us[ks] + cdiv(m.rows, 256);
+            ++ks;
+        }
+        if (L.ct[i]) {
+            sg[ks] = RecipSeg{col_scale[i], at<float>(ws, L.ct[i]), m.cols, 0};
+            us[ks + 1] = us[ks] + cdiv(m.cols, 256);
+            ++ks;
+        }
+    }
+    // matrices in launch-set order; each set has its own run of offsets
+    std::vector<int> idx(n_mats);
+    for (int32_t i = 0; i < n_mats; ++i) idx[i] = i;
+    std::stable_sort(idx.begin(), idx.end(),
+                     [&](int a, int b) { return q_key(mats[a], group) < q_key(mats[b], group); });
+    struct Set { QKey key; int first, count; size_t uoff; int64_t units; };
+    std::vector<Set> sets;
+    size_t uoff = 0;
+    for (int p = 0; p < n_mats; ++p) {
+        const int i = idx[p];
+        const woq_mat& m = mats[i];
+        const QKey key = q_key(m, group);
+        if (sets.empty() || !(sets.back().key == key)) {
+            if (!sets.empty()) uoff += sets.back().count + 1;
+            sets.push_back(Set{key, p, 0, uoff, 0});
+            ub[uoff] = 0;
+        }
+        Set& st_ = sets.back();
         QMat q{};
         q.data = m.data;
         q.codes = codes[i];
@@ -475,21 +539,23 @@ int32_t quant_pack_groupwise(const woq_mat* mats, int32_t n_mats, const float* c
         q.cols = (int32_t)m.cols;
         q.dtype = m.dtype;
         q.group = eff_group(m, group);
-        const int64_t u = small ? cdiv(elems(m), kQTile) : elems(m) / q.group;
-        if (m.dtype == WOQ_BF16) { tb[ib] = q; ub[ib + 1] = ub[ib] + u; ++ib; }
-        else { tf[jf] = q; uf[jf + 1] = uf[jf] + u; ++jf; }
-        if (q.rs) { sg[ks] = RecipSeg{row_scale[i], const_cast<float*>(q.rs), m.rows, 0}; us[ks + 1] = us[ks] + cdiv(m.rows, 256); ++ks; }
-        if (q.ct) { sg[ks] = RecipSeg{col_scale[i], const_cast<float*>(q.ct), m.cols, 0}; us[ks + 1] = us[ks] + cdiv(m.cols, 256); ++ks; }
+        tb[p] = q;
+        ub[uoff + st_.count + 1] = ub[uoff + st_.count] + q_units(m, group);
+        ++st_.count;
+        st_.units = ub[uoff + st_.count];
     }
     WOQ_HIP(hipMemcpyAsync(ws, host.data(), L.table_end, hipMemcpyHostToDevice, stream));
     if (L.nseg) WOQ_HIP(recip(at<RecipSeg>(ws, L.segs), at<int64_t>(ws, L.ubeg_s), L.nseg, us[L.nseg], stream));
-    auto launch = [&](size_t tab, size_t ubeg, int nm, int64_t units, int dt) -> hipError_t {
-        if (!nm) return hipSuccess;
-        return small ? quant_small(at<QMat>(ws, tab), at<int64_t>(ws, ubeg), nm, units, dt, bits, stream)
-                     : quant_big(at<QMat>(ws, tab), at<int64_t>(ws, ubeg), nm, units, dt, bits, stream);
-    };
-    WOQ_HIP(launch(L.tab_b, L.ubeg_b, L.nb, ub[L.nb], WOQ_BF16));
-    WOQ_HIP(launch(L.tab_f, L.ubeg_f, L.nf, uf[L.nf], WOQ_F32));
+    for (const Set& st_ : sets) {
+        const QMat* dt = at<QMat>(ws, L.tab_b) + st_.first;
+        const int64_t* du = at<int64_t>(ws, L.ubeg_b) + st_.uoff;
+        if (st_.key.kind == 0)
+            WOQ_HIP(quant_tile(dt, du, st_.count, st_.units, st_.key.dtype, bits, stream));
+        else if (st_.key.kind == 1)
+            WOQ_HIP(quant_wave(dt, du, st_.count, st_.units, st_.key.dtype, bits, st_.key.nvl, stream));
+        else
+            WOQ_HIP(quant_big(dt, du, st_.count, st_.units, st_.key.dtype, bits, stream));
+    }
     return WOQ_OK;
 }
 

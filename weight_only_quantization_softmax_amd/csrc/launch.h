@@ -53,8 +53,16 @@ struct RecipSeg {
 };
 hipError_t recip(const RecipSeg* segs, const int64_t* ubeg, int nseg,
                  int64_t n_units, hipStream_t s);
-hipError_t quant_small(const QMat* mats, const int64_t* ubeg, int nmat,
-                       int64_t n_units, int dtype, int bits, hipStream_t s);
+// Group kinds of quant_pack_groupwise: tiles of kQTileRows x kQTileCols for
+// power-of-two groups of at most 512 columns, one wave per group up to
+// kQWaveMax columns, else one workgroup per group.
+constexpr int kQTileRows = 8;
+constexpr int kQTileCols = 2048;
+constexpr int kQWaveMax = 4096;
+hipError_t quant_tile(const QMat* mats, const int64_t* ubeg, int nmat,
+                      int64_t n_units, int dtype, int bits, hipStream_t s);
+hipError_t quant_wave(const QMat* mats, const int64_t* ubeg, int nmat,
+                      int64_t n_units, int dtype, int bits, int nvl, hipStream_t s);
 hipError_t quant_big(const QMat* mats, const int64_t* ubeg, int nmat,
                      int64_t n_units, int dtype, int bits, hipStream_t s);
 hipError_t dequant(const QMat* mats, const int64_t* ubeg, int nmat,

@@ -13,15 +13,14 @@
 // so codes, deltas and zero-points are reproducible bit for bit.
 //
 // Work mapping:
-//  k_quant_small  groups of 8..512 columns: a work unit is 2048 consecutive
-//                 elements of one matrix; each thread owns 8 consecutive
-//                 elements (one 16-byte bf16 load), a group is owned by
-//                 group/8 consecutive lanes of one wave and reduced with
-//                 shuffles.  Groups tile the row-major matrix contiguously,
-//                 so group g starts at element g*group.
-//  k_quant_big    larger groups (e.g. one group per row): one workgroup per
-//                 group, raw values kept in registers between the min/max
-//                 reduction and the coding pass.
+//  k_quant_tile   groups of 8..512 columns (powers of two): a workgroup
+//                 takes 8 rows x 2048 columns; each thread owns 8
+//                 consecutive columns (one 16-byte bf16 load per row), a
+//                 group is group/8 consecutive lanes reduced with DPP and
+//                 permlane swaps.
+//  k_quant_wave   groups of 513..4096 columns: one wave per group.
+//  k_quant_big    wider groups (e.g. one group per 14336-column row): one
+//                 workgroup per group, one LDS exchange.
 //  k_dequant      2048-element units, 8 elements per thread.
 //  k_ternary      one workgroup per row.
 #include "launch.h"
@@ -40,28 +39,28 @@ __device__ __forceinline__ float clampf(float v, float lo, float hi) {
 template <int BITS>
 __device__ __forceinline__ void store_codes(uint8_t* codes, uint32_t e0, const uint32_t (&c)[8]) {
     if constexpr (BITS == 8) {
-        uint2 w;
-        w.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-        w.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-        *reinterpret_cast<uint2*>(codes + e0) = w;
+        f32x2 w;  // 8 bytes as two raw 32-bit words
+        w.x = __uint_as_float(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24));
+        w.y = __uint_as_float(c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+        gstore<f32x2>(codes + e0, w);
     } else if constexpr (BITS == 4) {
         uint32_t w = 0;
 #pragma unroll
         for (int k = 0; k < 8; ++k) w |= c[k] << (4 * k);
-        *reinterpret_cast<uint32_t*>(codes + (e0 >> 1)) = w;
+        gstore<uint32_t>(codes + (e0 >> 1), w);
     } else if constexpr (BITS == 2) {
         uint32_t w = 0;
 #pragma unroll
         for (int k = 0; k < 8; ++k) w |= c[k] << (2 * k);
-        *reinterpret_cast<uint16_t*>(codes + (e0 >> 2)) = (uint16_t)w;
+        gstore<uint16_t>(codes + (e0 >> 2), (uint16_t)w);
     } else {  // 3 bits: 8 codes fill exactly 3 bytes
         uint32_t w = 0;
 #pragma unroll
         for (int k = 0; k < 8; ++k) w |= c[k] << (3 * k);
         uint8_t* p = codes + (size_t)(e0 >> 3) * 3;
-        p[0] = (uint8_t)w;
-        p[1] = (uint8_t)(w >> 8);
-        p[2] = (uint8_t)(w >> 16);
+        gstore<uint8_t>(p, (uint8_t)w);
+        gstore<uint8_t>(p + 1, (uint8_t)(w >> 8));
+        gstore<uint8_t>(p + 2, (uint8_t)(w >> 16));
     }
 }
 
@@ -82,27 +81,6 @@ __device__ __forceinline__ void load_codes(const uint8_t* codes, uint32_t e0, ui
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) c[k] = (w >> (BITS * k)) & mask;
-    }
-}
-
-// x = (w * rs_row) * ct_col, each product rounded once; absent scales skipped.
-template <int DT>
-__device__ __forceinline__ void balanced8(const QMat& q, uint32_t e0, float (&x)[8]) {
-    load8<DT>(q.data, e0, x);
-    if (q.rs || q.ct) {
-        const uint32_t row = e0 / (uint32_t)q.cols;
-        const uint32_t col = e0 - row * (uint32_t)q.cols;
-        if (q.rs) {
-            const float r = q.rs[row];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) x[k] = __fmul_rn(x[k], r);
-        }
-        if (q.ct) {
-            float c[8];
-            load8f(q.ct + col, c);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) x[k] = __fmul_rn(x[k], c[k]);
-        }
     }
 }
 
@@ -134,78 +112,6 @@ __device__ __forceinline__ void code8(const float (&x)[8], const GroupParams& g,
     }
 }
 
-template <int DT, int BITS>
-__global__ __launch_bounds__(kT) void k_quant_small(const QMat* __restrict__ mats,
-                                                    const int64_t* __restrict__ ubeg,
-                                                    int nmat) {
-    const int64_t u = blockIdx.x;
-    const int m = find_unit_owner(ubeg, nmat, u);
-    const QMat q = mats[m];
-    const int group = q.group;
-    const uint32_t n = (uint32_t)q.rows * (uint32_t)q.cols;
-    const uint32_t e0 = (uint32_t)(u - ubeg[m]) * kQTile + 8u * threadIdx.x;
-    const bool active = e0 < n;
-    float x[8];
-    if (active) {
-        balanced8<DT>(q, e0, x);
-    } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = 0.f;
-    }
-    float lo = x[0], hi = x[0];
-#pragma unroll
-    for (int k = 1; k < 8; ++k) { lo = fminf(lo, x[k]); hi = fmaxf(hi, x[k]); }
-    const int lanes = group >> 3;  // power of two, <= 64
-    for (int o = 1; o < lanes; o <<= 1) {
-        lo = fminf(lo, __shfl_xor(lo, o, kWave));
-        hi = fmaxf(hi, __shfl_xor(hi, o, kWave));
-    }
-    const GroupParams g = group_params<BITS>(lo, hi);
-    if (!active) return;
-    uint32_t c[8];
-    code8<BITS>(x, g, c);
-    store_codes<BITS>(q.codes, e0, c);
-    if ((threadIdx.x & (lanes - 1)) == 0) {
-        const uint32_t gi = e0 / (uint32_t)group;
-        q.scales[gi] = g.delta;
-        q.zeros[gi] = (uint8_t)g.z;
-    }
-}
-
-__device__ __forceinline__ float block_min_f(float v, float* sh) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-    __syncthreads();
-    float r = sh[0];
-#pragma unroll
-    for (int w = 1; w < kT / 64; ++w) r = fminf(r, sh[w]);
-    return r;
-}
-
-__device__ __forceinline__ float block_max_f(float v, float* sh) {
-    v = wave_maxf(v);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-    __syncthreads();
-    float r = sh[0];
-#pragma unroll
-    for (int w = 1; w < kT / 64; ++w) r = fmaxf(r, sh[w]);
-    return r;
-}
-
-__device__ __forceinline__ double block_sum_d(double v, double* sh) {
-    v = wave_sum(v);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-    __syncthreads();
-    double r = 0.0;
-#pragma unroll
-    for (int w = 0; w < kT / 64; ++w) r += sh[w];
-    return r;
-}
-
 // Raw storage of 8 elements: a 16-byte bf16 vector or two float4.
 template <int DT> struct Raw8;
 template <> struct Raw8<WOQ_BF16> { uint4 v; };
@@ -215,18 +121,17 @@ template <int DT>
 __device__ __forceinline__ Raw8<DT> load_raw(const void* base, uint32_t e) {
     Raw8<DT> r;
     if constexpr (DT == WOQ_BF16) {
-        r.v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + e);
+        r.v = gload_u4(reinterpret_cast<const uint16_t*>(base) + e);
     } else {
-        const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + e);
-        r.a = p[0];
-        r.b = p[1];
+        const float* p = reinterpret_cast<const float*>(base) + e;
+        r.a = gload_f4(p);
+        r.b = gload_f4(p + 4);
     }
     return r;
 }
 
 template <int DT>
-__device__ __forceinline__ void raw_to_x(const Raw8<DT>& r, const QMat& q, float rsv,
-                                         uint32_t col, float (&x)[8]) {
+__device__ __forceinline__ void unpack_raw(const Raw8<DT>& r, float (&x)[8]) {
     if constexpr (DT == WOQ_BF16) {
         x[0] = bf_lo(r.v.x); x[1] = bf_hi(r.v.x); x[2] = bf_lo(r.v.y); x[3] = bf_hi(r.v.y);
         x[4] = bf_lo(r.v.z); x[5] = bf_hi(r.v.z); x[6] = bf_lo(r.v.w); x[7] = bf_hi(r.v.w);
@@ -234,65 +139,234 @@ __device__ __forceinline__ void raw_to_x(const Raw8<DT>& r, const QMat& q, float
         x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
         x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
     }
-    if (q.rs) {
+}
+
+// 1/t for 8 consecutive columns.
+__device__ __forceinline__ void load_ct(const float* ct, uint32_t col, float (&c)[8]) {
+    const float4 a = gload_f4(ct + col), b = gload_f4(ct + col + 4);
+    c[0] = a.x; c[1] = a.y; c[2] = a.z; c[3] = a.w;
+    c[4] = b.x; c[5] = b.y; c[6] = b.z; c[7] = b.w;
+}
+
+// x = (w * (1/s_i)) * (1/t_j), each product rounded once; absent scales skipped.
+template <int DT>
+__device__ __forceinline__ void balance(const Raw8<DT>& r, bool has_rs, float rsv, bool has_ct,
+                                        const float (&c)[8], float (&x)[8]) {
+    unpack_raw<DT>(r, x);
+    if (has_rs) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) x[k] = __fmul_rn(x[k], rsv);
     }
-    if (q.ct) {
-        float c[8];
-        load8f(q.ct + col, c);
+    if (has_ct) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) x[k] = __fmul_rn(x[k], c[k]);
     }
 }
 
+// min / max over aligned groups of `lanes` lanes (a power of two <= 64):
+// DPP within rows of 16 lanes, permlane swaps across them.
+__device__ __forceinline__ void group_minmax(float& lo, float& hi, int lanes) {
+    if (lanes >= 2) { lo = fminf(lo, dpp<kDppXor1>(lo)); hi = fmaxf(hi, dpp<kDppXor1>(hi)); }
+    if (lanes >= 4) { lo = fminf(lo, dpp<kDppXor2>(lo)); hi = fmaxf(hi, dpp<kDppXor2>(hi)); }
+    if (lanes >= 8) { lo = fminf(lo, dpp<kDppMirror8>(lo)); hi = fmaxf(hi, dpp<kDppMirror8>(hi)); }
+    if (lanes >= 16) { lo = fminf(lo, dpp<kDppMirror16>(lo)); hi = fmaxf(hi, dpp<kDppMirror16>(hi)); }
+    if (lanes >= 32) {
+        float a = lo, b = lo, c = hi, d = hi;
+        swap16(a, b);
+        swap16(c, d);
+        lo = fminf(a, b);
+        hi = fmaxf(c, d);
+    }
+    if (lanes >= 64) {
+        float a = lo, b = lo, c = hi, d = hi;
+        swap32(a, b);
+        swap32(c, d);
+        lo = fminf(a, b);
+        hi = fmaxf(c, d);
+    }
+}
+
+// Groups of 8..512 columns (powers of two).  A workgroup takes a tile of
+// kTileRows rows x kTileCols columns of one matrix; thread t owns the 8
+// columns 8t.. of the tile, so its 1/t factors are loaded once and the
+// tile's rows are all in flight before the first is coded.  A group is
+// group/8 consecutive lanes; groups never straddle the tile's edge because
+// cols is a multiple of the group size.
+constexpr int kTileRows = kQTileRows;
+constexpr int kTileCols = kQTileCols;
+static_assert(kTileCols == 8 * kT, "one 8-column vector per thread");
+
+template <int DT, int BITS>
+__global__ __launch_bounds__(kT) void k_quant_tile(const QMat* __restrict__ mats,
+                                                   const int64_t* __restrict__ ubeg, int nmat) {
+    const int64_t u = blockIdx.x;
+    const int m = find_unit_owner(ubeg, nmat, u);
+    const QMat q = mats[m];
+    const int ctiles = (q.cols + kTileCols - 1) / kTileCols;
+    const int tl = (int)(u - ubeg[m]);
+    const int rt = tl / ctiles;
+    const uint32_t col = (uint32_t)(tl - rt * ctiles) * kTileCols + 8u * threadIdx.x;
+    const bool active = col < (uint32_t)q.cols;
+    const int r0 = rt * kTileRows;
+    const int nr = min(kTileRows, q.rows - r0);
+    const int lanes = q.group >> 3;
+    const bool has_rs = q.rs != nullptr, has_ct = q.ct != nullptr;
+    float c[8];
+    if (has_ct && active) load_ct(q.ct, col, c);
+    else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) c[k] = 1.0f;
+    }
+    Raw8<DT> raw[kTileRows];
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r)
+        if (r < nr && active) raw[r] = load_raw<DT>(q.data, (uint32_t)(r0 + r) * (uint32_t)q.cols + col);
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) {
+        if (r >= nr) break;
+        const uint32_t row = (uint32_t)(r0 + r);
+        const float rsv = has_rs ? gload<float>(q.rs + row) : 1.0f;
+        float x[8];
+        if (active) balance<DT>(raw[r], has_rs, rsv, has_ct, c, x);
+        else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) x[k] = 0.f;
+        }
+        float lo = x[0], hi = x[0];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) { lo = fminf(lo, x[k]); hi = fmaxf(hi, x[k]); }
+        group_minmax(lo, hi, lanes);
+        const GroupParams g = group_params<BITS>(lo, hi);
+        if (active) {
+            const uint32_t e0 = row * (uint32_t)q.cols + col;
+            uint32_t cd[8];
+            code8<BITS>(x, g, cd);
+            store_codes<BITS>(q.codes, e0, cd);
+            if ((threadIdx.x & (lanes - 1)) == 0) {
+                const uint32_t gi = e0 / (uint32_t)q.group;
+                gstore<float>(q.scales + gi, g.delta);
+                gstore<uint8_t>(q.zeros + gi, (uint8_t)g.z);
+            }
+        }
+    }
+}
+
+// Groups of more than 512 and at most 64 * 8 * NVL columns: one wave per
+// group (four per workgroup), values kept packed in registers between the
+// min / max reduction and the coding pass.
+template <int DT, int BITS, int NVL>
+__global__ __launch_bounds__(kT) void k_quant_wave(const QMat* __restrict__ mats,
+                                                   const int64_t* __restrict__ ubeg, int nmat) {
+    const int64_t u = blockIdx.x;
+    const int m = find_unit_owner(ubeg, nmat, u);
+    const QMat q = mats[m];
+    const int lane = threadIdx.x & 63;
+    const uint32_t ng = (uint32_t)q.rows * (uint32_t)q.cols / (uint32_t)q.group;
+    const uint32_t gi = (uint32_t)(u - ubeg[m]) * (kT / 64) + (threadIdx.x >> 6);
+    if (gi >= ng) return;  // whole wave; no workgroup barrier below
+    const uint32_t gbase = gi * (uint32_t)q.group;
+    const uint32_t row = gbase / (uint32_t)q.cols;
+    const uint32_t col0 = gbase - row * (uint32_t)q.cols;
+    const int nvg = q.group >> 3;
+    const bool has_rs = q.rs != nullptr, has_ct = q.ct != nullptr;
+    const float rsv = has_rs ? gload<float>(q.rs + row) : 1.0f;
+    Raw8<DT> raw[NVL];
+    float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NVL; ++k) {
+        const int v = lane + 64 * k;
+        if (v < nvg) raw[k] = load_raw<DT>(q.data, gbase + 8u * v);
+    }
+#pragma unroll
+    for (int k = 0; k < NVL; ++k) {
+        const int v = lane + 64 * k;
+        if (v < nvg) {
+            float c[8], x[8];
+            if (has_ct) load_ct(q.ct, col0 + 8u * v, c);
+            balance<DT>(raw[k], has_rs, rsv, has_ct, c, x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { lo = fminf(lo, x[e]); hi = fmaxf(hi, x[e]); }
+        }
+    }
+    group_minmax(lo, hi, 64);
+    const GroupParams g = group_params<BITS>(lo, hi);
+#pragma unroll
+    for (int k = 0; k < NVL; ++k) {
+        const int v = lane + 64 * k;
+        if (v < nvg) {
+            float c[8], x[8];
+            if (has_ct) load_ct(q.ct, col0 + 8u * v, c);
+            balance<DT>(raw[k], has_rs, rsv, has_ct, c, x);
+            uint32_t cd[8];
+            code8<BITS>(x, g, cd);
+            store_codes<BITS>(q.codes, gbase + 8u * v, cd);
+        }
+    }
+    if (lane == 0) {
+        gstore<float>(q.scales + gi, g.delta);
+        gstore<uint8_t>(q.zeros + gi, (uint8_t)g.z);
+    }
+}
+
+// Wider groups (e.g. one group per row of 14336 columns): one workgroup per
+// group, raw values kept in registers between the min / max reduction
+// (waves, then one LDS exchange) and the coding pass.
 template <int DT, int BITS>
 __global__ __launch_bounds__(kT) void k_quant_big(const QMat* __restrict__ mats,
                                                   const int64_t* __restrict__ ubeg,
                                                   int nmat) {
     constexpr int MAXV = (DT == WOQ_BF16) ? 16 : 8;
-    __shared__ float sh[kT / 64];
+    __shared__ float2 sh[kT / 64];
     const int64_t u = blockIdx.x;
     const int m = find_unit_owner(ubeg, nmat, u);
     const QMat q = mats[m];
-    const int group = q.group;
     const uint32_t gl = (uint32_t)(u - ubeg[m]);
-    const uint32_t gbase = gl * (uint32_t)group;
+    const uint32_t gbase = gl * (uint32_t)q.group;
     const uint32_t row = gbase / (uint32_t)q.cols;
     const uint32_t col0 = gbase - row * (uint32_t)q.cols;
-    const float rsv = q.rs ? q.rs[row] : 1.0f;
-    const int nvg = group >> 3;
+    const int nvg = q.group >> 3;
+    const bool has_rs = q.rs != nullptr, has_ct = q.ct != nullptr;
+    const float rsv = has_rs ? gload<float>(q.rs + row) : 1.0f;
 
     Raw8<DT> raw[MAXV];
+#pragma unroll
+    for (int k = 0; k < MAXV; ++k) {
+        const int v = threadIdx.x + kT * k;
+        if (v < nvg) raw[k] = load_raw<DT>(q.data, gbase + 8u * v);
+    }
     float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
     for (int k = 0; k < MAXV; ++k) {
         const int v = threadIdx.x + kT * k;
         if (v < nvg) {
-            raw[k] = load_raw<DT>(q.data, gbase + 8u * v);
-            float x[8];
-            raw_to_x<DT>(raw[k], q, rsv, col0 + 8u * v, x);
+            float c[8], x[8];
+            if (has_ct) load_ct(q.ct, col0 + 8u * v, c);
+            balance<DT>(raw[k], has_rs, rsv, has_ct, c, x);
 #pragma unroll
             for (int e = 0; e < 8; ++e) { lo = fminf(lo, x[e]); hi = fmaxf(hi, x[e]); }
         }
     }
-    lo = block_min_f(lo, sh);
-    hi = block_max_f(hi, sh);
+    group_minmax(lo, hi, 64);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = make_float2(lo, hi);
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kT / 64; ++w) { lo = fminf(lo, sh[w].x); hi = fmaxf(hi, sh[w].y); }
     const GroupParams g = group_params<BITS>(lo, hi);
 #pragma unroll
     for (int k = 0; k < MAXV; ++k) {
         const int v = threadIdx.x + kT * k;
         if (v < nvg) {
-            float x[8];
-            raw_to_x<DT>(raw[k], q, rsv, col0 + 8u * v, x);
-            uint32_t c[8];
-            code8<BITS>(x, g, c);
-            store_codes<BITS>(q.codes, gbase + 8u * v, c);
+            float c[8], x[8];
+            if (has_ct) load_ct(q.ct, col0 + 8u * v, c);
+            balance<DT>(raw[k], has_rs, rsv, has_ct, c, x);
+            uint32_t cd[8];
+            code8<BITS>(x, g, cd);
+            store_codes<BITS>(q.codes, gbase + 8u * v, cd);
         }
     }
     if (threadIdx.x == 0) {
-        q.scales[gl] = g.delta;
-        q.zeros[gl] = (uint8_t)g.z;
+        gstore<float>(q.scales + gl, g.delta);
+        gstore<uint8_t>(q.zeros + gl, (uint8_t)g.z);
     }
 }
 
@@ -364,22 +438,29 @@ __global__ __launch_bounds__(kT) void k_ternary(const QMat* __restrict__ mats,
     const uint32_t rbase = row * (uint32_t)q.cols;
     const int nv = q.cols >> 3;
     Raw8<DT> raw[MAXV];
+#pragma unroll
+    for (int k = 0; k < MAXV; ++k) {
+        const int v = threadIdx.x + kT * k;
+        if (v < nv) raw[k] = load_raw<DT>(q.data, rbase + 8u * v);
+    }
     double acc = 0.0;
 #pragma unroll
     for (int k = 0; k < MAXV; ++k) {
         const int v = threadIdx.x + kT * k;
         if (v < nv) {
-            raw[k] = load_raw<DT>(q.data, rbase + 8u * v);
             float x[8];
-            QMat plain = q;
-            plain.rs = nullptr;
-            plain.ct = nullptr;
-            raw_to_x<DT>(raw[k], plain, 1.0f, 0, x);
+            unpack_raw<DT>(raw[k], x);
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc += (double)fabsf(x[e]);
         }
     }
-    const double sum = block_sum_d(acc, shd);
+    // row sum of |w| in fp64: waves, then the wave totals in wave order
+    acc = wave_sum(acc);
+    if ((threadIdx.x & 63) == 0) shd[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    double sum = 0.0;
+#pragma unroll
+    for (int w = 0; w < kT / 64; ++w) sum += shd[w];
     const float beta = (float)(sum / (double)q.cols);
     const float inv = __fdiv_rn(1.0f, beta);
     const bool ok = isfinite(inv);
@@ -388,20 +469,17 @@ __global__ __launch_bounds__(kT) void k_ternary(const QMat* __restrict__ mats,
         const int v = threadIdx.x + kT * k;
         if (v < nv) {
             float x[8];
-            QMat plain = q;
-            plain.rs = nullptr;
-            plain.ct = nullptr;
-            raw_to_x<DT>(raw[k], plain, 1.0f, 0, x);
+            unpack_raw<DT>(raw[k], x);
             uint32_t w = 0;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float t = ok ? clampf(rintf(__fmul_rn(x[e], inv)), -1.f, 1.f) : 0.f;
                 w |= (uint32_t)(int)(t + 1.0f) << (2 * e);
             }
-            *reinterpret_cast<uint16_t*>(q.codes + ((rbase + 8u * v) >> 2)) = (uint16_t)w;
+            gstore<uint16_t>(q.codes + ((rbase + 8u * v) >> 2), (uint16_t)w);
         }
     }
-    if (threadIdx.x == 0) q.scales[row] = beta;
+    if (threadIdx.x == 0) gstore<float>(q.scales + row, beta);
 }
 
 __global__ __launch_bounds__(kT) void k_recip(const RecipSeg* __restrict__ segs,
@@ -414,16 +492,40 @@ __global__ __launch_bounds__(kT) void k_recip(const RecipSeg* __restrict__ segs,
 }
 
 template <int DT>
-hipError_t quant_small_dt(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                          int bits, hipStream_t s) {
+hipError_t quant_tile_dt(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
+                         int bits, hipStream_t s) {
     const dim3 grid((unsigned)n_units), block(kT);
     switch (bits) {
-        case 2: k_quant_small<DT, 2><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
-        case 3: k_quant_small<DT, 3><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
-        case 4: k_quant_small<DT, 4><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
-        default: k_quant_small<DT, 8><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
+        case 2: k_quant_tile<DT, 2><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
+        case 3: k_quant_tile<DT, 3><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
+        case 4: k_quant_tile<DT, 4><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
+        default: k_quant_tile<DT, 8><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
     }
     return hipGetLastError();
+}
+
+template <int DT, int NVL>
+hipError_t quant_wave_nv(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
+                         int bits, hipStream_t s) {
+    const dim3 grid((unsigned)n_units), block(kT);
+    switch (bits) {
+        case 2: k_quant_wave<DT, 2, NVL><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
+        case 3: k_quant_wave<DT, 3, NVL><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
+        case 4: k_quant_wave<DT, 4, NVL><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
+        default: k_quant_wave<DT, 8, NVL><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
+    }
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t quant_wave_dt(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
+                         int bits, int nvl, hipStream_t s) {
+    switch (nvl) {
+        case 1: return quant_wave_nv<DT, 1>(mats, ubeg, nmat, n_units, bits, s);
+        case 2: return quant_wave_nv<DT, 2>(mats, ubeg, nmat, n_units, bits, s);
+        case 4: return quant_wave_nv<DT, 4>(mats, ubeg, nmat, n_units, bits, s);
+        default: return quant_wave_nv<DT, 8>(mats, ubeg, nmat, n_units, bits, s);
+    }
 }
 
 template <int DT>
@@ -462,11 +564,18 @@ hipError_t recip(const RecipSeg* segs, const int64_t* ubeg, int nseg, int64_t n_
     return hipGetLastError();
 }
 
-hipError_t quant_small(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                       int dtype, int bits, hipStream_t s) {
+hipError_t quant_tile(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
+                      int dtype, int bits, hipStream_t s) {
     if (n_units <= 0) return hipSuccess;
-    return dtype == WOQ_BF16 ? quant_small_dt<WOQ_BF16>(mats, ubeg, nmat, n_units, bits, s)
-                             : quant_small_dt<WOQ_F32>(mats, ubeg, nmat, n_units, bits, s);
+    return dtype == WOQ_BF16 ? quant_tile_dt<WOQ_BF16>(mats, ubeg, nmat, n_units, bits, s)
+                             : quant_tile_dt<WOQ_F32>(mats, ubeg, nmat, n_units, bits, s);
+}
+
+hipError_t quant_wave(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
+                      int dtype, int bits, int nvl, hipStream_t s) {
+    if (n_units <= 0) return hipSuccess;
+    return dtype == WOQ_BF16 ? quant_wave_dt<WOQ_BF16>(mats, ubeg, nmat, n_units, bits, nvl, s)
+                             : quant_wave_dt<WOQ_F32>(mats, ubeg, nmat, n_units, bits, nvl, s);
 }
 
 hipError_t quant_big(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,

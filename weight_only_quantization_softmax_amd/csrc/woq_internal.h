@@ -70,6 +70,7 @@ __device__ __forceinline__ float dpp(float v) {
 constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int kDppMirror8 = 0x141;     // row_half_mirror: lane i <-> 7 - i in each 8
+constexpr int kDppMirror16 = 0x140;    // row_mirror: lane i <-> 15 - i in each 16
 constexpr int kDppXor8 = 0x128;        // row_ror:8 within 16-lane rows
 __device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }

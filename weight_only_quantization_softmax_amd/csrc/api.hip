@@ -26,8 +26,8 @@ constexpr int32_t kMaxIters = 4096;
 // Sinkhorn: matrices of one shape class run in one launch per iteration
 // (MI355X's Infinity Cache serves re-reads barely faster than HBM, so there
 // is no point in cache-sized groups; one big launch amortises everything).
-constexpr int kSinqTargetWGs = 512;    // workgroup mode: ~2 resident per CU
-constexpr int kSinqTargetWaves = 2048; // wave mode: ~8 resident waves per CU
+constexpr int kSinqCUs = 256;          // MI355X compute units
+constexpr int kSinqWavesPerCU = 8;     // resident Sinkhorn waves per CU (2 per SIMD)
 
 size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 
@@ -152,23 +152,35 @@ SinqLayout sinq_layout(const woq_mat* mats, int32_t n) {
         g.first = p;
         g.dtype = mats[idx[p]].dtype;
         g.sh = sinq_shape((int)mats[idx[p]].cols, mats[idx[p]].dtype);
-        int64_t elems_g = 0;
         int q = p;
-        while (q < n && key(idx[q]) == key(idx[p])) {
-            elems_g += elems(mats[idx[q]]);
-            ++q;
-        }
+        while (q < n && key(idx[q]) == key(idx[p])) ++q;
         g.count = q - p;
+        // Strips of one height for the whole launch set: the smallest height
+        // (in register tiles of R rows) for which every workgroup is resident
+        // at once (about 8 waves per CU), so no workgroup runs in a second
+        // round.  Mode 0: a workgroup owns one strip.  Mode 1: its four waves
+        // own four consecutive strips.  A workgroup writes one partial row,
+        // so n_strips counts workgroups.
         const int R = g.sh.mode == 1 ? 1 : sinq_tile_rows(g.dtype, g.sh.nv);
-        const int target = g.sh.mode == 1 ? kSinqTargetWaves : kSinqTargetWGs;
+        const int per_wg = g.sh.mode == 1 ? 4 : 1;
+        const int waves_per_wg = g.sh.mode == 1 ? 4 : g.sh.nt / 64;
+        const int64_t cap = (int64_t)kSinqCUs * std::max(1, kSinqWavesPerCU / waves_per_wg);
+        auto wgs_for = [&](int64_t t) {
+            int64_t n_wg = 0;
+            for (int k = p; k < q; ++k) n_wg += cdiv(mats[idx[k]].rows, t * R * per_wg);
+            return n_wg;
+        };
+        int64_t lo = 1, hi = 1;
+        for (int k = p; k < q; ++k) hi = std::max<int64_t>(hi, cdiv(mats[idx[k]].rows, R));
+        while (lo < hi) {
+            const int64_t mid = (lo + hi) / 2;
+            if (wgs_for(mid) <= cap) hi = mid; else lo = mid + 1;
+        }
         for (int k = p; k < q; ++k) {
             const woq_mat& m = mats[idx[k]];
-            const double share = (double)elems(m) / (double)elems_g;
-            int64_t want = (int64_t)(share * target + 0.5);
-            want = std::max<int64_t>(1, std::min<int64_t>(want, cdiv(m.rows, R)));
-            int64_t srows = cdiv(cdiv(m.rows, want), R) * R;
+            const int64_t srows = lo * R;
             L.strip_rows[k] = (int32_t)srows;
-            L.n_strips[k] = (int32_t)cdiv(m.rows, srows);
+            L.n_strips[k] = (int32_t)cdiv(m.rows, srows * per_wg);
             g.n_strips += L.n_strips[k];
             g.n_cunits += cdiv(m.cols, 16);
             g.cols_max = std::max<int>(g.cols_max, (int)m.cols);

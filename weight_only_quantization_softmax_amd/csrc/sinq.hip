@@ -430,41 +430,42 @@ __global__ __launch_bounds__(kMaxT) void k_sinq_pass(const SinqMat* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Wave-per-row pass for rows of at most 4096 bf16 (2048 fp32) columns.  A
-// wave owns a strip of whole rows, lane l owns the 8-column vectors
-// l + 64 k (k < NVL), so row statistics need no workgroup barrier and the
-// column partials of the strip stay in the lane's registers.  Rows go
-// through two packed register buffers: row r + 1 is loaded while row r is
-// processed.  u = 1/t is staged in LDS, one copy per wave (the four waves of
-// a workgroup may serve different matrices).  RAG: the row is not a
+// Wave-per-row pass for rows of at most 4096 bf16 (1536 fp32) columns.  A
+// workgroup's four waves take four consecutive row strips of one matrix; lane
+// l owns the 8-column vectors l + 64 k (k < NVL), so row statistics need no
+// workgroup barrier and the column partials of a strip stay in the lane's
+// registers.  Rows go through two packed register buffers: row r + 1 is
+// loaded while row r is processed.  u = 1/t is staged once per workgroup in
+// LDS.  At the end the four waves add their column partials in LDS in wave
+// order and the workgroup writes one partial row.  RAG: the row is not a
 // multiple of 512 columns, so lanes own unequal numbers of vectors.
-constexpr int kWaveU = 4096 + 8;  // LDS floats per wave: u and a zero pad
+constexpr int kWaveU = 4096 + 8;  // LDS floats: u and a zero pad
 
 template <int DT, int NVL, bool FIRST, bool RAG>
 __global__ __launch_bounds__(256) void k_sinq_wave(const SinqMat* __restrict__ mats,
-                                                   const int64_t* __restrict__ wbeg, int nmat) {
+                                                   const int64_t* __restrict__ wgbeg, int nmat) {
     constexpr bool F32 = DT == WOQ_F32;
+    constexpr int NP = F32 ? 4 : 2;  // partial floats per column
     // wide bf16 rows keep only the packed row and unpack it once per pass
     constexpr bool KEEP = F32 || NVL <= 4;
-    extern __shared__ float ul[];
+    extern __shared__ float ul[];    // u [kWaveU], then the partial sum [cols][NP]
     const int lane = threadIdx.x & 63;
-    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);  // global wave index
-    const int m = find_unit_owner(wbeg, nmat, (int64_t)gw);
-    const bool live = gw < wbeg[nmat];
-    const SinqMat sm = mats[live ? m : 0];
+    const int wid = threadIdx.x >> 6;
+    const int m = find_unit_owner(wgbeg, nmat, (int64_t)blockIdx.x);
+    const SinqMat sm = mats[m];
+    const int wg = (int)(blockIdx.x - wgbeg[m]);
     const int cols = sm.cols;
     const int nvec = cols >> 3;
-    float* u = ul + (threadIdx.x >> 6) * kWaveU;
-    for (int j = 4 * lane; j < kWaveU; j += 256) {
+    float* u = ul;
+    float* cp = ul + kWaveU;
+    for (int j = 4 * threadIdx.x; j < kWaveU; j += 4 * 256) {
         f32x4 v = {0.f, 0.f, 0.f, 0.f};
         if (j < cols) v = FIRST ? f32x4{1.f, 1.f, 1.f, 1.f} : gload<f32x4>(sm.u + j);
         *reinterpret_cast<f32x4*>(u + j) = v;
     }
-    // the wave reads entries other lanes wrote: wait for its LDS writes
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (!live) return;
-    const int strip = gw - (int)wbeg[m];
-    const int r0 = strip * sm.strip_rows;
+    __syncthreads();
+    const int strip = 4 * wg + wid;
+    const int r0 = min(sm.rows, strip * sm.strip_rows);
     const int r1 = min(sm.rows, r0 + sm.strip_rows);
 
     int vk[NVL];
@@ -572,40 +573,49 @@ __global__ __launch_bounds__(256) void k_sinq_wave(const SinqMat* __restrict__ m
         if (row + 2 < r1) load_row(PA, row + 2);
         process(PB, row + 1);
     }
+    // the four waves' column partials, added in wave order in LDS
+    for (int w = 0; w < 4; ++w) {
+        if (wid == w) {
 #pragma unroll
-    for (int k = 0; k < NVL; ++k) {
-        if (!own[k]) continue;
-        const int64_t c0 = (int64_t)strip * cols + 8 * vk[k];
-        if constexpr (F32) {
-            float4* p = reinterpret_cast<float4*>(sm.part) + c0;
+            for (int k = 0; k < NVL; ++k) {
+                if (!own[k]) continue;
+                f32x4* p = reinterpret_cast<f32x4*>(cp + (size_t)NP * 8 * vk[k]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) gstore_f4(p + e, cs[k][e], cq[k][e], cmn[k][e], cmx[k][e]);
-        } else {
-            float4* p = reinterpret_cast<float4*>(reinterpret_cast<float2*>(sm.part) + c0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                gstore_f4(p + e, cs[k][2 * e], cq[k][2 * e], cs[k][2 * e + 1], cq[k][2 * e + 1]);
+                for (int i = 0; i < 2 * NP; ++i) {
+                    f32x4 v;
+                    if constexpr (F32) {
+                        v = f32x4{cs[k][i], cq[k][i], cmn[k][i], cmx[k][i]};
+                    } else {
+                        v = f32x4{cs[k][2 * i], cq[k][2 * i], cs[k][2 * i + 1], cq[k][2 * i + 1]};
+                    }
+                    if (w > 0) {
+                        const f32x4 o = p[i];
+                        if constexpr (F32) {
+                            v = f32x4{o.x + v.x, o.y + v.y, fminf(o.z, v.z), fmaxf(o.w, v.w)};
+                        } else {
+                            v = o + v;
+                        }
+                    }
+                    p[i] = v;
+                }
+            }
         }
+        __syncthreads();
     }
+    // one partial row per workgroup
+    const f32x4* c4 = reinterpret_cast<const f32x4*>(cp);
+    f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(sm.part) + (size_t)wg * cols * NP);
+    for (int j = threadIdx.x; j < cols * NP / 4; j += 256) gstore<f32x4>(dst + j, c4[j]);
 }
 
 template <int DT, int NVL, bool RAG>
-hipError_t launch_wave(const SinqMat* mats, const int64_t* wbeg, int nmat, int64_t n_waves,
+hipError_t launch_wave(const SinqMat* mats, const int64_t* wgbeg, int nmat, int64_t n_wgs,
                        bool first, hipStream_t s) {
-    const size_t lds = 4 * sizeof(float) * kWaveU;
-    const unsigned grid = (unsigned)((n_waves + 3) / 4);
-    if (first) k_sinq_wave<DT, NVL, true, RAG><<<dim3(grid), dim3(256), lds, s>>>(mats, wbeg, nmat);
-    else k_sinq_wave<DT, NVL, false, RAG><<<dim3(grid), dim3(256), lds, s>>>(mats, wbeg, nmat);
-    return hipGetLastError();
-}
-
-template <int DT, int NVL>
-hipError_t launch_wave(const SinqMat* mats, const int64_t* wbeg, int nmat, int64_t n_waves,
-                       bool first, hipStream_t s) {
-    const size_t lds = 4 * sizeof(float) * (4096 + 8);
-    const unsigned grid = (unsigned)((n_waves + 3) / 4);
-    if (first) k_sinq_wave<DT, NVL, true><<<dim3(grid), dim3(256), lds, s>>>(mats, wbeg, nmat);
-    else k_sinq_wave<DT, NVL, false><<<dim3(grid), dim3(256), lds, s>>>(mats, wbeg, nmat);
+    // u, then the workgroup's partial row (wave mode: <= 4096 bf16 / 1536 fp32 columns)
+    const size_t lds = sizeof(float) * (kWaveU + (DT == WOQ_F32 ? 4 * 1536 : 2 * 4096));
+    const unsigned grid = (unsigned)n_wgs;
+    if (first) k_sinq_wave<DT, NVL, true, RAG><<<dim3(grid), dim3(256), lds, s>>>(mats, wgbeg, nmat);
+    else k_sinq_wave<DT, NVL, false, RAG><<<dim3(grid), dim3(256), lds, s>>>(mats, wgbeg, nmat);
     return hipGetLastError();
 }
 

@@ -119,7 +119,7 @@ EntLayout ent_layout(const woq_mat* mats, int32_t n, int32_t n_blocks) {
 
 // ------------------------------------------------------------------ sinkhorn
 struct SinqGroup {
-    int first = 0, count = 0, dtype = 0, cols_max = 0;
+    int first = 0, count = 0, dtype = 0, cols_max = 0, max_strips = 0;
     SinqShape sh{0, 0, 0, 0};
     int64_t n_strips = 0, n_cunits = 0;
     size_t arr_off = 0;  // index of this group's first entry in sbeg / cbeg
@@ -182,9 +182,11 @@ SinqLayout sinq_layout(const woq_mat* mats, int32_t n) {
             L.strip_rows[k] = (int32_t)srows;
             L.n_strips[k] = (int32_t)cdiv(m.rows, srows * per_wg);
             g.n_strips += L.n_strips[k];
-            g.n_cunits += cdiv(m.cols, 16);
+            g.max_strips = std::max<int>(g.max_strips, L.n_strips[k]);
             g.cols_max = std::max<int>(g.cols_max, (int)m.cols);
         }
+        const int rcols = 256 / sinq_reduce_slices(g.max_strips);
+        for (int k = p; k < q; ++k) g.n_cunits += cdiv(mats[idx[k]].cols, rcols);
         L.groups.push_back(g);
         p = q;
     }
@@ -469,9 +471,10 @@ int32_t sinq_balance(const woq_mat* mats, int32_t n_mats, int32_t iters, float* 
         int64_t* gs = sb + g.arr_off;
         int64_t* gc = cb + g.arr_off;
         gs[0] = gc[0] = 0;
+        const int rcols = 256 / sinq_reduce_slices(g.max_strips);
         for (int k = 0; k < g.count; ++k) {
             gs[k + 1] = gs[k] + tab[g.first + k].n_strips;
-            gc[k + 1] = gc[k] + cdiv(tab[g.first + k].cols, 16);
+            gc[k + 1] = gc[k] + cdiv(tab[g.first + k].cols, rcols);
         }
     }
     WOQ_HIP(hipMemcpyAsync(ws, host.data(), L.table_end, hipMemcpyHostToDevice, stream));
@@ -481,8 +484,8 @@ int32_t sinq_balance(const woq_mat* mats, int32_t n_mats, int32_t iters, float* 
     for (const SinqGroup& g : L.groups)
         for (int32_t it = 0; it < iters; ++it)
             WOQ_HIP(sinq_iteration(dt + g.first, dsb + g.arr_off, dcb + g.arr_off, g.count,
-                                   g.n_strips, g.n_cunits, g.dtype, g.sh, g.cols_max, it == 0,
-                                   stream));
+                                   g.n_strips, g.n_cunits, g.max_strips, g.dtype, g.sh,
+                                   g.cols_max, it == 0, stream));
     return WOQ_OK;
 }
 

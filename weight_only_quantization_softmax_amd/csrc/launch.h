@@ -35,12 +35,16 @@ struct SinqShape { int nt, nv, mode, rag; };
 SinqShape sinq_shape(int cols, int dtype);
 // Rows per register tile of the fused pass (depends on dtype and nv).
 int sinq_tile_rows(int dtype, int nv);
+// Column reduction: slices of partial rows per column (a power of two, 1..16)
+// for a launch whose matrices have at most max_strips partial rows; a
+// reduction workgroup covers 256 / slices columns.
+int sinq_reduce_slices(int max_strips);
 // One iteration over a group of same-shape matrices: the fused row / column
-// pass (one workgroup per strip) then the fixed-order column reduction.
+// pass then the fixed-order column reduction.
 hipError_t sinq_iteration(const SinqMat* mats, const int64_t* strip_begin,
                           const int64_t* col_begin, int nmat, int64_t n_strips,
-                          int64_t n_col_units, int dtype, SinqShape sh, int cols_max,
-                          bool first, hipStream_t s);
+                          int64_t n_col_units, int max_strips, int dtype, SinqShape sh,
+                          int cols_max, bool first, hipStream_t s);
 
 // ---- quantise / dequantise / ternary
 constexpr int kQTile = 2048;          // elements per small-group work unit

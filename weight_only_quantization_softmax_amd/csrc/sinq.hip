@@ -651,33 +651,34 @@ hipError_t launch_wave_f32(const SinqMat* mats, const int64_t* wbeg, int nmat, i
     }
 }
 
-// Column combine: a workgroup takes 16 columns; 16 slices of threads each
-// sum every 16th strip (16 loads in flight), then slice totals are added in
-// slice order.  The summation order is fixed, so results are deterministic.
-constexpr int kRedCols = 16;
-constexpr int kRedSlices = 16;
+// Column combine: a workgroup takes 256 / S columns; S slices of threads
+// each sum every S-th partial row (16 loads in flight), then the slice totals
+// are added in slice order.  S (a power of two, 1..16) follows the number of
+// partial rows, so each thread handles about 16 of them.  The summation order
+// is fixed for a given launch plan, so results are deterministic.
 constexpr int kRedInflight = 16;
 
 template <int DT>
 __global__ __launch_bounds__(256) void k_sinq_reduce(const SinqMat* __restrict__ mats,
                                                      const int64_t* __restrict__ cbeg, int nmat,
-                                                     int first) {
-    __shared__ double sS[kRedSlices][kRedCols], sQ[kRedSlices][kRedCols];
-    __shared__ float sMn[kRedSlices][kRedCols], sMx[kRedSlices][kRedCols];
+                                                     int slices) {
+    __shared__ double sS[256], sQ[256];
+    __shared__ float sMn[256], sMx[256];
     const int64_t u = blockIdx.x;
     const int m = find_unit_owner(cbeg, nmat, u);
     const SinqMat sm = mats[m];
-    const int c = threadIdx.x % kRedCols, sl = threadIdx.x / kRedCols;
-    const int j = (int)(u - cbeg[m]) * kRedCols + c;
+    const int ncol = 256 / slices;
+    const int c = threadIdx.x % ncol, sl = threadIdx.x / ncol;
+    const int j = (int)(u - cbeg[m]) * ncol + c;
     double S = 0.0, Q = 0.0;
     float mn = INFINITY, mx = -INFINITY;
     if (j < sm.cols) {
-        for (int g0 = sl; g0 < sm.n_strips; g0 += kRedInflight * kRedSlices) {
+        for (int g0 = sl; g0 < sm.n_strips; g0 += kRedInflight * slices) {
             if constexpr (DT == WOQ_F32) {
                 float4 p[kRedInflight];
 #pragma unroll
                 for (int q = 0; q < kRedInflight; ++q) {
-                    const int g = g0 + q * kRedSlices;
+                    const int g = g0 + q * slices;
                     p[q] = g < sm.n_strips ? gload_f4(reinterpret_cast<const float4*>(sm.part) + (int64_t)g * sm.cols + j)
                                            : make_float4(0.f, 0.f, INFINITY, -INFINITY);
                 }
@@ -692,7 +693,7 @@ __global__ __launch_bounds__(256) void k_sinq_reduce(const SinqMat* __restrict__
                 float2 p[kRedInflight];
 #pragma unroll
                 for (int q = 0; q < kRedInflight; ++q) {
-                    const int g = g0 + q * kRedSlices;
+                    const int g = g0 + q * slices;
                     p[q] = g < sm.n_strips ? gload_f2(reinterpret_cast<const float2*>(sm.part) + (int64_t)g * sm.cols + j)
                                            : make_float2(0.f, 0.f);
                 }
@@ -701,21 +702,22 @@ __global__ __launch_bounds__(256) void k_sinq_reduce(const SinqMat* __restrict__
             }
         }
     }
-    sS[sl][c] = S;
-    sQ[sl][c] = Q;
-    sMn[sl][c] = mn;
-    sMx[sl][c] = mx;
-    __syncthreads();
-    if (sl != 0 || j >= sm.cols) return;
-    S = 0.0;
-    Q = 0.0;
-#pragma unroll
-    for (int q = 0; q < kRedSlices; ++q) {
-        S += sS[q][c];
-        Q += sQ[q][c];
-        mn = fminf(mn, sMn[q][c]);
-        mx = fmaxf(mx, sMx[q][c]);
+    if (slices > 1) {
+        sS[threadIdx.x] = S;
+        sQ[threadIdx.x] = Q;
+        sMn[threadIdx.x] = mn;
+        sMx[threadIdx.x] = mx;
+        __syncthreads();
+        if (sl != 0) return;
+        for (int q = 1; q < slices; ++q) {
+            const int t = q * ncol + c;
+            S += sS[t];
+            Q += sQ[t];
+            mn = fminf(mn, sMn[t]);
+            mx = fmaxf(mx, sMx[t]);
+        }
     }
+    if (j >= sm.cols) return;
     const double n = (double)sm.rows;
     const double mean = S / n;
     const double var = Q / n - mean * mean;
@@ -780,9 +782,15 @@ SinqShape sinq_shape(int cols, int dtype) {
 
 int sinq_tile_rows(int dtype, int nv) { return tile_rows(dtype, nv); }
 
+int sinq_reduce_slices(int max_strips) {
+    int sl = 1;
+    while (sl < 16 && sl * kRedInflight < max_strips) sl *= 2;
+    return sl;
+}
+
 hipError_t sinq_iteration(const SinqMat* mats, const int64_t* sbeg, const int64_t* cbeg, int nmat,
-                          int64_t n_strips, int64_t n_col_units, int dtype, SinqShape sh,
-                          int cols_max, bool first, hipStream_t s) {
+                          int64_t n_strips, int64_t n_col_units, int max_strips, int dtype,
+                          SinqShape sh, int cols_max, bool first, hipStream_t s) {
     hipError_t e;
     if (sh.mode == 1)
         e = dtype == WOQ_BF16 ? launch_wave_dt<WOQ_BF16>(mats, sbeg, nmat, n_strips, sh, first, s)
@@ -793,10 +801,11 @@ hipError_t sinq_iteration(const SinqMat* mats, const int64_t* sbeg, const int64_
                 ? launch_pass_dt<WOQ_BF16>(mats, sbeg, nmat, n_strips, sh, cols_max, first, s)
                 : launch_pass_dt<WOQ_F32>(mats, sbeg, nmat, n_strips, sh, cols_max, first, s);
     if (e != hipSuccess) return e;
+    const int slices = sinq_reduce_slices(max_strips);
     if (dtype == WOQ_BF16)
-        k_sinq_reduce<WOQ_BF16><<<dim3((unsigned)n_col_units), dim3(256), 0, s>>>(mats, cbeg, nmat, first ? 1 : 0);
+        k_sinq_reduce<WOQ_BF16><<<dim3((unsigned)n_col_units), dim3(256), 0, s>>>(mats, cbeg, nmat, slices);
     else
-        k_sinq_reduce<WOQ_F32><<<dim3((unsigned)n_col_units), dim3(256), 0, s>>>(mats, cbeg, nmat, first ? 1 : 0);
+        k_sinq_reduce<WOQ_F32><<<dim3((unsigned)n_col_units), dim3(256), 0, s>>>(mats, cbeg, nmat, slices);
     return hipGetLastError();
 }
 

@@ -91,7 +91,7 @@ struct EntLayout {
     int nb = 0, nf = 0;
     int64_t units_b = 0, units_f = 0;
     size_t tab_b, ubeg_b, tab_f, ubeg_f, bmats, bbeg, nsz, table_end;
-    size_t hb, keys, part_f, ghist, total;
+    size_t hb, keys, part_f, ghist, hpart, total;
 };
 
 EntLayout ent_layout(const woq_mat* mats, int32_t n, int32_t n_blocks) {
@@ -113,6 +113,7 @@ EntLayout ent_layout(const woq_mat* mats, int32_t n, int32_t n_blocks) {
     L.keys = a.take(sizeof(uint32_t) * 2 * L.nf);
     L.part_f = a.take(sizeof(double2) * L.units_f);
     L.ghist = a.take(sizeof(uint32_t) * 65536 * (size_t)std::min(L.nb, kHistSlots));
+    L.hpart = a.take(sizeof(double4) * kHistBinParts * (size_t)std::min(L.nb, kHistSlots), 64);
     L.total = a.end();
     return L;
 }
@@ -419,7 +420,7 @@ int32_t ewq_block_entropy(const woq_mat* mats, int32_t n_mats, const int32_t* bl
         const int b1 = std::min(L.nb, b0 + kHistSlots);
         WOQ_HIP(fill_u32(ghist, (size_t)(b1 - b0) * 65536, 0u, stream));
         WOQ_HIP(ent_hist_bf16(dtb + b0, dub + b0, b1 - b0, ub[b0], ub[b1] - ub[b0], ghist, stream));
-        WOQ_HIP(ent_hist_final(dtb + b0, b1 - b0, ghist, h_mat, stream));
+        WOQ_HIP(ent_hist_final(dtb + b0, b1 - b0, ghist, at<double4>(ws, L.hpart), h_mat, stream));
     }
     if (L.nf)
         WOQ_HIP(ent_f32(at<EntMat>(ws, L.tab_f), at<int64_t>(ws, L.ubeg_f), L.nf, L.units_f,

@@ -107,33 +107,46 @@ __device__ __forceinline__ float block_maxf(float v, float* sh) {
     return r;
 }
 
-__global__ __launch_bounds__(kT) void k_hist_final(const EntMat* __restrict__ mats,
-                                                   const uint32_t* __restrict__ ghist,
-                                                   double* __restrict__ h_mat) {
+// The 65,536 bins of a matrix are split into kHistParts parts of 4096 bins.
+// Part w takes the largest finite non-empty value c_w of its bins and sums,
+// relative to it, S_w = sum n_v e^{v - c_w} and U_w = sum n_v e^{v - c_w}
+// (v - c_w) in fp64.  The combine rescales to the matrix maximum c:
+//   S = sum_w S_w e^{c_w - c},  U = sum_w (U_w + (c_w - c) S_w) e^{c_w - c},
+// so H = ln S - U / S exactly as from one pass (up to fp64 rounding).
+constexpr int kHistParts = kHistBinParts;
+constexpr int kPartBins = 65536 / kHistParts;
+
+__global__ __launch_bounds__(kT) void k_hist_part(const uint32_t* __restrict__ ghist,
+                                                  double4* __restrict__ part) {
     __shared__ double shd[kT / 64];
     __shared__ float shf[kT / 64];
-    const int m = blockIdx.x;
-    const uint32_t* gh = ghist + (size_t)m * 65536;
-
+    const int m = blockIdx.x / kHistParts, w = blockIdx.x % kHistParts;
+    const uint32_t* gh = ghist + (size_t)m * 65536 + (size_t)w * kPartBins;
+    constexpr int PER = kPartBins / kT;
+    uint32_t cnt[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) cnt[i] = gload<uint32_t>(gh + threadIdx.x + kT * i);
     float mx = -INFINITY, bad = 0.f;
-    for (int b = threadIdx.x; b < 65536; b += kT) {
-        if (gh[b]) {
-            const float v = __uint_as_float((uint32_t)b << 16);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        if (cnt[i]) {
+            const uint32_t b = (uint32_t)(w * kPartBins) + threadIdx.x + kT * i;
+            const float v = __uint_as_float(b << 16);
             if (!isfinite(v)) bad = 1.f; else mx = fmaxf(mx, v);
         }
     }
     mx = block_maxf(mx, shf);
     bad = block_maxf(bad, shf);
-
     double S = 0.0, U = 0.0;
     const double c = (double)mx;
-    for (int b = threadIdx.x; b < 65536; b += kT) {
-        const uint32_t cnt = gh[b];
-        if (cnt) {
-            const float v = __uint_as_float((uint32_t)b << 16);
-            if (isfinite(v)) {
+    if (mx > -INFINITY) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const uint32_t b = (uint32_t)(w * kPartBins) + threadIdx.x + kT * i;
+            const float v = __uint_as_float(b << 16);
+            if (cnt[i] && isfinite(v)) {
                 const double d = (double)v - c;
-                const double e = (double)cnt * exp(d);
+                const double e = (double)cnt[i] * exp(d);
                 S += e;
                 U += e * d;
             }
@@ -141,7 +154,32 @@ __global__ __launch_bounds__(kT) void k_hist_final(const EntMat* __restrict__ ma
     }
     S = block_sum(S, shd);
     U = block_sum(U, shd);
-    if (threadIdx.x == 0) h_mat[mats[m].slot] = bad != 0.f ? (double)NAN : log(S) - U / S;
+    if (threadIdx.x == 0) part[blockIdx.x] = make_double4(c, S, U, (double)bad);
+}
+
+__global__ __launch_bounds__(kT) void k_hist_comb(const EntMat* __restrict__ mats, int nmat,
+                                                  const double4* __restrict__ part,
+                                                  double* __restrict__ h_mat) {
+    const int m = blockIdx.x * kT + threadIdx.x;
+    if (m >= nmat) return;
+    const double4* p = part + (size_t)m * kHistParts;
+    double c = -INFINITY;
+    bool bad = false;
+    for (int w = 0; w < kHistParts; ++w) {
+        const double4 q = p[w];
+        if (q.y > 0.0) c = fmax(c, q.x);
+        bad = bad || q.w != 0.0;
+    }
+    double S = 0.0, U = 0.0;
+    for (int w = 0; w < kHistParts; ++w) {
+        const double4 q = p[w];
+        if (q.y > 0.0) {
+            const double f = exp(q.x - c);
+            S += q.y * f;
+            U += (q.z + (q.x - c) * q.y) * f;
+        }
+    }
+    gstore<double>(h_mat + mats[m].slot, bad ? (double)NAN : log(S) - U / S);
 }
 
 // ---------------------------------------------------------------- fp32
@@ -286,10 +324,11 @@ hipError_t ent_hist_bf16(const EntMat* mats, const int64_t* ubeg, int nmat, int6
     return hipGetLastError();
 }
 
-hipError_t ent_hist_final(const EntMat* mats, int nmat, const uint32_t* ghist, double* h_mat,
-                          hipStream_t s) {
+hipError_t ent_hist_final(const EntMat* mats, int nmat, const uint32_t* ghist, double4* part,
+                          double* h_mat, hipStream_t s) {
     if (nmat <= 0) return hipSuccess;
-    k_hist_final<<<dim3(nmat), dim3(kT), 0, s>>>(mats, ghist, h_mat);
+    k_hist_part<<<dim3(nmat * kHistParts), dim3(kT), 0, s>>>(ghist, part);
+    k_hist_comb<<<dim3((nmat + kT - 1) / kT), dim3(kT), 0, s>>>(mats, nmat, part, h_mat);
     return hipGetLastError();
 }
 

@@ -16,8 +16,11 @@ hipError_t fill_f32(float* p, size_t n, float v, hipStream_t s);
 hipError_t ent_hist_bf16(const EntMat* mats, const int64_t* ubeg, int nmat,
                          int64_t u0, int64_t n_units, uint32_t* ghist,
                          hipStream_t s);
+// Entropy from the histograms: kHistBinParts parts per matrix (partials in
+// part[nmat * kHistBinParts]), then one combine per matrix.
+constexpr int kHistBinParts = 16;
 hipError_t ent_hist_final(const EntMat* mats, int nmat, const uint32_t* ghist,
-                          double* h_mat, hipStream_t s);
+                          double4* part, double* h_mat, hipStream_t s);
 hipError_t ent_f32(const EntMat* mats, const int64_t* ubeg, int nmat,
                    int64_t n_units, uint32_t* keys, double2* part,
                    double* h_mat, hipStream_t s);

@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 METRIC = "GB/s bf16 weights quantised (+% HBM peak), Llama-8B-shaped stack, 1 GPU"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sinq_sweep_stack8b_traffic.md")
+TRAFFIC_WORKLOAD = "stack8b"   # the workload the counter summary was taken on
 SINQ_SOURCES = [os.path.join(ROOT, "weight_only_quantization_softmax_amd", "csrc", f)
                 for f in ("sinq.hip", "api.hip", "woq_internal.h")]
 
@@ -50,18 +51,21 @@ def cpu_baseline(wl, specs, mats, qp, tiers):
     """The oracle (numpy fp64, fp32 where the decisions are fp32) on host
     cores over a bounded sample of the workload.
 
-    Sample: the attention matrices (q, k, v, o) and the gate projection of the
-    first block (5 of the 7 matrices, 92.3 M weights), each taken through
-    every stage the workload uses (entropy; Sinkhorn + int4 group RTN + pack;
-    int8 per-row + pack; ternary + pack).  Each stage's seconds per byte on
-    the sample are applied to the workload's own tier mix.
+    Sample: the first block's matrices in order until at least 60 M weights
+    (for the Llama-8B-shaped stack: q, k, v, o and gate, 92.3 M weights),
+    each taken through every stage the workload uses (entropy; Sinkhorn +
+    group RTN + pack; int8 per-row + pack; ternary + pack).  Each stage's
+    seconds per byte on the sample are applied to the workload's own tier mix.
     """
     import numpy as np
     import oracle
 
     first = specs[0].block
-    pick = [i for i, m in enumerate(specs)
-            if m.block == first and m.name.split(".")[-1] in ("q", "k", "v", "o", "gate")]
+    pick, n = [], 0
+    for i, m in enumerate(specs):
+        if m.block == first and n < 60_000_000:
+            pick.append(i)
+            n += mats[i].numel()
     t_ent = t_sinq = t_i8 = t_ter = 0.0
     nbytes = 0
     for i in pick:
@@ -93,7 +97,7 @@ def cpu_baseline(wl, specs, mats, qp, tiers):
         total += m.numel() * m.element_size() * per_byte[acts[sp.block]]
     return {"value": round(qp.bytes_in / total / 1e9, 6), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": (f"q, k, v, o and gate of block {first} ({nbytes / 1e9:.3f} GB bf16) through "
+            "sample": (f"{len(pick)} matrices of block {first} ({nbytes / 1e9:.3f} GB) through "
                        f"entropy ({t_ent:.1f}s), Sinkhorn K={wl.iters} + int{wl.bits} g{wl.group} "
                        f"({t_sinq:.1f}s), int8 per-row ({t_i8:.1f}s), ternary ({t_ter:.1f}s); "
                        "per-byte costs applied to the workload's tier mix; numpy, one thread")}
@@ -218,7 +222,7 @@ def main() -> int:
         # and the column reduction are not counted)
         alg = d["bytes"] * wl.iters
         kernel = "sinq_balance (K fused row/column sweeps + column reductions)"
-        traffic = measured_traffic()
+        traffic = measured_traffic() if args.workload == TRAFFIC_WORKLOAD else None
     else:
         alg = d["bytes"]
         kernel = {"entropy": "ewq_block_entropy"}.get(dominant, dominant)

@@ -27,7 +27,7 @@ constexpr int32_t kMaxIters = 4096;
 // (MI355X's Infinity Cache serves re-reads barely faster than HBM, so there
 // is no point in cache-sized groups; one big launch amortises everything).
 constexpr int kSinqCUs = 256;          // MI355X compute units
-constexpr int kSinqWavesPerCU = 8;     // resident Sinkhorn waves per CU (2 per SIMD)
+constexpr int kSinqWavesPerCU = 8;     // resident workgroup-pass waves per CU (2 per SIMD)
 
 size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 
@@ -165,7 +165,9 @@ SinqLayout sinq_layout(const woq_mat* mats, int32_t n) {
         const int R = g.sh.mode == 1 ? 1 : sinq_tile_rows(g.dtype, g.sh.nv);
         const int per_wg = g.sh.mode == 1 ? 4 : 1;
         const int waves_per_wg = g.sh.mode == 1 ? 4 : g.sh.nt / 64;
-        const int64_t cap = (int64_t)kSinqCUs * std::max(1, kSinqWavesPerCU / waves_per_wg);
+        const int waves_per_cu =
+            g.sh.mode == 1 ? 4 * sinq_wave_occupancy(g.dtype, g.sh.nv) : kSinqWavesPerCU;
+        const int64_t cap = (int64_t)kSinqCUs * std::max(1, waves_per_cu / waves_per_wg);
         auto wgs_for = [&](int64_t t) {
             int64_t n_wg = 0;
             for (int k = p; k < q; ++k) n_wg += cdiv(mats[idx[k]].rows, t * R * per_wg);

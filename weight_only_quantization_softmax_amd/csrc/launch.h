@@ -38,6 +38,8 @@ struct SinqShape { int nt, nv, mode, rag; };
 SinqShape sinq_shape(int cols, int dtype);
 // Rows per register tile of the fused pass (depends on dtype and nv).
 int sinq_tile_rows(int dtype, int nv);
+// Waves per SIMD the wave-per-row pass is built for (dtype, vectors per lane).
+int sinq_wave_occupancy(int dtype, int nv);
 // Column reduction: slices of partial rows per column (a power of two, 1..16)
 // for a launch whose matrices have at most max_strips partial rows; a
 // reduction workgroup covers 256 / slices columns.

@@ -439,15 +439,30 @@ __global__ __launch_bounds__(kMaxT) void k_sinq_pass(const SinqMat* __restrict__
 // LDS.  At the end the four waves add their column partials in LDS in wave
 // order and the workgroup writes one partial row.  RAG: the row is not a
 // multiple of 512 columns, so lanes own unequal numbers of vectors.
-constexpr int kWaveU = 4096 + 8;  // LDS floats: u and a zero pad
+// Shape constants of the wave pass.  KEEP: the row is kept unpacked between
+// the two passes (rows of at most 4 vectors per lane); wider bf16 rows keep
+// only the packed row and unpack it once per pass (register pressure).  Two
+// waves per SIMD throughout (measured: more waves with re-unpacked narrow
+// rows ran slower).
+template <int DT, int NVL>
+struct WaveCfg {
+    static constexpr bool F32 = DT == WOQ_F32;
+    static constexpr int OCC = 2;  // waves per SIMD
+    static constexpr bool KEEP = F32 || NVL <= 4;
+    static constexpr int NP = F32 ? 4 : 2;                  // partial floats per column
+    static constexpr int UW = NVL * 512 + 8;                // LDS floats of u and its zero pad
+    static constexpr size_t lds() { return sizeof(float) * ((size_t)UW + (size_t)NP * NVL * 512); }
+};
 
 template <int DT, int NVL, bool FIRST, bool RAG>
-__global__ __launch_bounds__(256) void k_sinq_wave(const SinqMat* __restrict__ mats,
-                                                   const int64_t* __restrict__ wgbeg, int nmat) {
-    constexpr bool F32 = DT == WOQ_F32;
-    constexpr int NP = F32 ? 4 : 2;  // partial floats per column
-    // wide bf16 rows keep only the packed row and unpack it once per pass
-    constexpr bool KEEP = F32 || NVL <= 4;
+__global__ __launch_bounds__(256, (WaveCfg<DT, NVL>::OCC)) void k_sinq_wave(
+    const SinqMat* __restrict__ mats, const int64_t* __restrict__ wgbeg, int nmat) {
+    using WC = WaveCfg<DT, NVL>;
+    constexpr bool F32 = WC::F32;
+    constexpr int NP = WC::NP;
+    constexpr int kWaveU = WC::UW;
+    // otherwise only the packed row is kept and unpacked once per pass
+    constexpr bool KEEP = WC::KEEP;
     extern __shared__ float ul[];    // u [kWaveU], then the partial sum [cols][NP]
     const int lane = threadIdx.x & 63;
     const int wid = threadIdx.x >> 6;
@@ -612,7 +627,7 @@ template <int DT, int NVL, bool RAG>
 hipError_t launch_wave(const SinqMat* mats, const int64_t* wgbeg, int nmat, int64_t n_wgs,
                        bool first, hipStream_t s) {
     // u, then the workgroup's partial row (wave mode: <= 4096 bf16 / 1536 fp32 columns)
-    const size_t lds = sizeof(float) * (kWaveU + (DT == WOQ_F32 ? 4 * 1536 : 2 * 4096));
+    const size_t lds = WaveCfg<DT, NVL>::lds();
     const unsigned grid = (unsigned)n_wgs;
     if (first) k_sinq_wave<DT, NVL, true, RAG><<<dim3(grid), dim3(256), lds, s>>>(mats, wgbeg, nmat);
     else k_sinq_wave<DT, NVL, false, RAG><<<dim3(grid), dim3(256), lds, s>>>(mats, wgbeg, nmat);
@@ -781,6 +796,8 @@ SinqShape sinq_shape(int cols, int dtype) {
 }
 
 int sinq_tile_rows(int dtype, int nv) { return tile_rows(dtype, nv); }
+
+int sinq_wave_occupancy(int, int) { return 2; }
 
 int sinq_reduce_slices(int max_strips) {
     int sl = 1;

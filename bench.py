@@ -151,6 +151,38 @@ def compulsory_bytes(mats, specs, acts, bits, group):
     return total
 
 
+def dequant_rate(qp, mats, wl, stream, reps=5):
+    """Decode the Sinkhorn tier's packed outputs back to bf16 with
+    dequant_unpack (outside the timed region) and time it with HIP events:
+    bytes = codes + deltas + zero-points + s + t read, 2 B per weight written."""
+    import torch
+    import weight_only_quantization_softmax_amd as woq
+
+    sel = [i for i, o in sorted(qp.outputs.items()) if o["action"] == "sinq"]
+    if not sel:
+        return None
+    o = [qp.outputs[i] for i in sel]
+    shapes = [tuple(mats[i].shape) for i in sel]
+    outs = [torch.empty_like(mats[i]) for i in sel]
+    args = dict(zeros=[x["zeros"] for x in o], row_scale=[x["s"] for x in o],
+                col_scale=[x["t"] for x in o], out_dtype=mats[sel[0]].dtype, out=outs,
+                stream=stream)
+    codes, scales = [x["codes"] for x in o], [x["scales"] for x in o]
+    woq.dequant_unpack(shapes, codes, scales, wl.bits, wl.group, **args)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        woq.dequant_unpack(shapes, codes, scales, wl.bits, wl.group, **args)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = sum(x["codes"].numel() + 5 * x["scales"].numel() + 4 * (x["s"].numel() + x["t"].numel())
+                 + 2 * m.numel() for x, m in zip(o, (mats[i] for i in sel)))
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"call": "dequant_unpack", "matrices": len(sel), "ms": round(ms, 4), "bytes": int(nbytes),
+            "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,6 +264,7 @@ def main() -> int:
             "algorithmic_bytes_per_launch": int(alg), "launch_ms": round(launch_ms, 4)}
     acts = qp.action_of_block(tiers)
     comp = compulsory_bytes(mats, specs, acts, wl.bits, wl.group)
+    deq = dequant_rate(qp, mats, wl, stream)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -247,6 +280,7 @@ def main() -> int:
         "step_ms": {"median": round(step_ms[len(step_ms) // 2], 3), "min": round(step_ms[0], 3),
                     "max": round(step_ms[-1], 3)},
         "roofline": roof,
+        "dequant": deq,
         "calls": {k: {"ms_per_step": round(v["ms_per_step"], 3), "calls": v["calls"]}
                   for k, v in per_kind.items()},
     }

@@ -200,19 +200,21 @@ def test_quant_batched_mixed_dtypes_and_edge_groups():
 
 
 # ------------------------------------------------------------------ dequant
-@pytest.mark.parametrize("bits,group", [(4, 64), (3, 128), (8, 0), (2, 32)])
-def test_dequant_matches_oracle(bits, group):
-    m = _rm(24, 1024, 61)
+@pytest.mark.parametrize("bits,group,rows,cols", [(4, 64, 24, 1024), (3, 128, 24, 1024),
+                                                  (8, 0, 24, 1024), (2, 32, 24, 1024),
+                                                  (4, 64, 13, 2560), (3, 128, 9, 6144)])
+def test_dequant_matches_oracle(bits, group, rows, cols):
+    m = _rm(rows, cols, 61)
     ss, tt = woq.sinq_balance([m], 2)
     codes, scales, zeros = woq.quant_pack_groupwise([m], bits, group, row_scale=ss, col_scale=tt)
-    g = group if group else 1024
-    q_ref = oracle.unpack_codes(codes[0].cpu().numpy(), bits, 1024)
+    g = group if group else cols
+    q_ref = oracle.unpack_codes(codes[0].cpu().numpy(), bits, cols)
     ref = oracle.dequantize_f32(q_ref, scales[0].cpu().numpy(), zeros[0].cpu().numpy(),
                                 ss[0].cpu().numpy(), tt[0].cpu().numpy(), g)
-    out32 = woq.dequant_unpack([(24, 1024)], codes, scales, bits, group, zeros=zeros,
+    out32 = woq.dequant_unpack([(rows, cols)], codes, scales, bits, group, zeros=zeros,
                                row_scale=ss, col_scale=tt)[0]
     assert np.array_equal(out32.cpu().numpy().view(np.uint32), ref.view(np.uint32))
-    out16 = woq.dequant_unpack([(24, 1024)], codes, scales, bits, group, zeros=zeros,
+    out16 = woq.dequant_unpack([(rows, cols)], codes, scales, bits, group, zeros=zeros,
                                row_scale=ss, col_scale=tt, out_dtype=torch.bfloat16)[0]
     assert torch.equal(out16.cpu(), torch.from_numpy(ref).to(torch.bfloat16))
     # error bound: |W - W'| <= s t delta / 2 (plus fp32 rounding)

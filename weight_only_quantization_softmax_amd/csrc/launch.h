@@ -52,7 +52,6 @@ hipError_t sinq_iteration(const SinqMat* mats, const int64_t* strip_begin,
                           int cols_max, bool first, hipStream_t s);
 
 // ---- quantise / dequantise / ternary
-constexpr int kQTile = 2048;          // elements per small-group work unit
 
 struct RecipSeg {
     const float* src;

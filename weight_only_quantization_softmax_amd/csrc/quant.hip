@@ -21,7 +21,7 @@
 //  k_quant_wave   groups of 513..4096 columns: one wave per group.
 //  k_quant_big    wider groups (e.g. one group per 14336-column row): one
 //                 workgroup per group, one LDS exchange.
-//  k_dequant      2048-element units, 8 elements per thread.
+//  k_dequant      the tiles of k_quant_tile (8 rows x 2048 columns).
 //  k_ternary      one workgroup per row.
 #include "launch.h"
 
@@ -61,26 +61,6 @@ __device__ __forceinline__ void store_codes(uint8_t* codes, uint32_t e0, const u
         gstore<uint8_t>(p, (uint8_t)w);
         gstore<uint8_t>(p + 1, (uint8_t)(w >> 8));
         gstore<uint8_t>(p + 2, (uint8_t)(w >> 16));
-    }
-}
-
-template <int BITS>
-__device__ __forceinline__ void load_codes(const uint8_t* codes, uint32_t e0, uint32_t (&c)[8]) {
-    constexpr uint32_t mask = (1u << BITS) - 1u;
-    if constexpr (BITS == 8) {
-        const uint2 w = *reinterpret_cast<const uint2*>(codes + e0);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) { c[k] = (w.x >> (8 * k)) & mask; c[k + 4] = (w.y >> (8 * k)) & mask; }
-    } else {
-        uint32_t w;
-        if constexpr (BITS == 4) w = *reinterpret_cast<const uint32_t*>(codes + (e0 >> 1));
-        else if constexpr (BITS == 2) w = *reinterpret_cast<const uint16_t*>(codes + (e0 >> 2));
-        else {
-            const uint8_t* p = codes + (size_t)(e0 >> 3) * 3;
-            w = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16);
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) c[k] = (w >> (BITS * k)) & mask;
     }
 }
 
@@ -376,6 +356,32 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Dequantisation W' = (((q - z) delta) s_i) t_j, one fp32 rounding per
+// product, then (bf16 output) one round-to-nearest-even.  Same tiles as
+// k_quant_tile: a workgroup takes 8 rows x 2048 columns, thread t the 8
+// columns 8t..; t_j is loaded once per tile, s_i once per row.
+template <int BITS>
+__device__ __forceinline__ void load_codes_g(const uint8_t* codes, uint32_t e0, uint32_t (&c)[8]) {
+    constexpr uint32_t mask = (1u << BITS) - 1u;
+    if constexpr (BITS == 8) {
+        const f32x2 w = gload<f32x2>(codes + e0);
+        const uint32_t lo = __float_as_uint(w.x), hi = __float_as_uint(w.y);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) { c[k] = (lo >> (8 * k)) & mask; c[k + 4] = (hi >> (8 * k)) & mask; }
+    } else {
+        uint32_t w;
+        if constexpr (BITS == 4) w = gload<uint32_t>(codes + (e0 >> 1));
+        else if constexpr (BITS == 2) w = gload<uint16_t>(codes + (e0 >> 2));
+        else {
+            const uint8_t* p = codes + (size_t)(e0 >> 3) * 3;
+            w = (uint32_t)gload<uint8_t>(p) | ((uint32_t)gload<uint8_t>(p + 1) << 8) |
+                ((uint32_t)gload<uint8_t>(p + 2) << 16);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) c[k] = (w >> (BITS * k)) & mask;
+    }
+}
+
 template <int BITS, int ODT>
 __global__ __launch_bounds__(kT) void k_dequant(const QMat* __restrict__ mats,
                                                 const int64_t* __restrict__ ubeg, int nmat,
@@ -383,46 +389,48 @@ __global__ __launch_bounds__(kT) void k_dequant(const QMat* __restrict__ mats,
     const int64_t u = blockIdx.x;
     const int m = find_unit_owner(ubeg, nmat, u);
     const QMat q = mats[m];
-    const int group = q.group;
-    const uint32_t n = (uint32_t)q.rows * (uint32_t)q.cols;
-    const uint32_t e0 = (uint32_t)(u - ubeg[m]) * kQTile + 8u * threadIdx.x;
-    if (e0 >= n) return;
-    uint32_t c[8];
-    load_codes<BITS>(q.codes, e0, c);
-    const uint32_t gi = e0 / (uint32_t)group;
-    const float delta = q.scales[gi];
-    const int z = q.zeros ? (int)q.zeros[gi] : zdef;
-    float y[8];
+    const int ctiles = (q.cols + kTileCols - 1) / kTileCols;
+    const int tl = (int)(u - ubeg[m]);
+    const int rt = tl / ctiles;
+    const uint32_t col = (uint32_t)(tl - rt * ctiles) * kTileCols + 8u * threadIdx.x;
+    if (col >= (uint32_t)q.cols) return;  // no cross-lane work below
+    const int r0 = rt * kTileRows;
+    const int nr = min(kTileRows, q.rows - r0);
+    const bool has_rs = q.rs != nullptr, has_ct = q.ct != nullptr;
+    float t8[8];
+    if (has_ct) load_ct(q.ct, col, t8);
+    uint32_t cw[kTileRows][8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) y[k] = __fmul_rn((float)((int)c[k] - z), delta);
-    if (q.rs || q.ct) {
-        const uint32_t row = e0 / (uint32_t)q.cols;
-        const uint32_t col = e0 - row * (uint32_t)q.cols;
-        if (q.rs) {
-            const float r = q.rs[row];
+    for (int r = 0; r < kTileRows; ++r)
+        if (r < nr) load_codes_g<BITS>(q.codes, (uint32_t)(r0 + r) * (uint32_t)q.cols + col, cw[r]);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) y[k] = __fmul_rn(y[k], r);
+    for (int r = 0; r < kTileRows; ++r) {
+        if (r >= nr) break;
+        const uint32_t row = (uint32_t)(r0 + r);
+        const uint32_t e0 = row * (uint32_t)q.cols + col;
+        const uint32_t gi = e0 / (uint32_t)q.group;
+        const float delta = gload<float>(q.scales + gi);
+        const int z = q.zeros ? (int)gload<uint8_t>(q.zeros + gi) : zdef;
+        const float rsv = has_rs ? gload<float>(q.rs + row) : 1.0f;
+        float y[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            y[k] = __fmul_rn((float)((int)cw[r][k] - z), delta);
+            if (has_rs) y[k] = __fmul_rn(y[k], rsv);
+            if (has_ct) y[k] = __fmul_rn(y[k], t8[k]);
         }
-        if (q.ct) {
-            float t[8];
-            load8f(q.ct + col, t);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) y[k] = __fmul_rn(y[k], t[k]);
+        if constexpr (ODT == WOQ_F32) {
+            float* o = const_cast<float*>(reinterpret_cast<const float*>(q.data)) + e0;
+            gstore_f4(o, y[0], y[1], y[2], y[3]);
+            gstore_f4(o + 4, y[4], y[5], y[6], y[7]);
+        } else {
+            u32x4 w;
+            w.x = f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16);
+            w.y = f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16);
+            w.z = f32_to_bf16_rne(y[4]) | (f32_to_bf16_rne(y[5]) << 16);
+            w.w = f32_to_bf16_rne(y[6]) | (f32_to_bf16_rne(y[7]) << 16);
+            gstore<u32x4>(const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(q.data)) + e0, w);
         }
-    }
-    if constexpr (ODT == WOQ_F32) {
-        float4* o = reinterpret_cast<float4*>(const_cast<float*>(
-            reinterpret_cast<const float*>(q.data)) + e0);
-        o[0] = make_float4(y[0], y[1], y[2], y[3]);
-        o[1] = make_float4(y[4], y[5], y[6], y[7]);
-    } else {
-        uint4 w;
-        w.x = f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16);
-        w.y = f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16);
-        w.z = f32_to_bf16_rne(y[4]) | (f32_to_bf16_rne(y[5]) << 16);
-        w.w = f32_to_bf16_rne(y[6]) | (f32_to_bf16_rne(y[7]) << 16);
-        *reinterpret_cast<uint4*>(const_cast<uint16_t*>(
-            reinterpret_cast<const uint16_t*>(q.data)) + e0) = w;
     }
 }
 

@@ -1,0 +1,79 @@
+"""Data-free quality report: how well the quantised weights reconstruct W.
+
+SINQ's claim is that balancing rows and columns before rounding spreads the
+rounding error more evenly and lowers it ([SINQ] "Huawei gioi thieu SINQ"
+(asiadaily.org), sections "Dinh ty le tren hai truc" and "Chuan hoa
+Sinkhorn Knopp").  This measures it on the weights alone, with no data: each
+matrix is balanced for K iterations, quantised and packed, then decoded with
+dequant_unpack, all through the library; the report gives, per matrix,
+scheme and K, the relative Frobenius error ||W - W'|| / ||W|| and the largest
+absolute error, both computed in fp64 on the device.  K = 0 is plain
+group-wise RTN (s = t = 1).  Ternary codes ([BitNet] "Khung Nguon
+BitNet.cpp" (unite.ai), "He Thong Trong So Ternary") use the per-row scale
+and no balancing.
+
+    python -m weight_only_quantization_softmax_amd.quality --workload block --blocks 0
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import sys
+from typing import Dict, List, Sequence, Tuple
+
+import torch
+
+from . import dequant_unpack, quant_pack_groupwise, sinq_balance, ternary_pack
+
+SCHEMES: Tuple[Tuple[int, int], ...] = ((4, 64), (3, 128))
+ITERS: Tuple[int, ...] = (0, 4, 16, 24)
+
+
+def _errors(w: torch.Tensor, wq: torch.Tensor) -> Dict[str, float]:
+    a = w.double()
+    d = wq.double() - a
+    return {"rel_fro": (torch.linalg.vector_norm(d) / torch.linalg.vector_norm(a)).item(),
+            "max_abs": d.abs().max().item()}
+
+
+def matrix_report(w: torch.Tensor, schemes: Sequence[Tuple[int, int]] = SCHEMES,
+                  iters: Sequence[int] = ITERS, ternary: bool = True) -> List[dict]:
+    """Rows of the report for one device-resident matrix (bf16 or fp32)."""
+    rows = []
+    shape = tuple(w.shape)
+    for bits, group in schemes:
+        for k in iters:
+            s, t = sinq_balance([w], k)
+            codes, scales, zeros = quant_pack_groupwise([w], bits, group, row_scale=s,
+                                                        col_scale=t)
+            wq = dequant_unpack([shape], codes, scales, bits, group, zeros=zeros, row_scale=s,
+                                col_scale=t, out_dtype=torch.float32)[0]
+            rows.append({"scheme": f"int{bits} g{group}", "iters": k, **_errors(w, wq)})
+    if ternary:
+        codes, beta = ternary_pack([w])
+        wq = dequant_unpack([shape], codes, [beta[0]], 2, 0, out_dtype=torch.float32)[0]
+        rows.append({"scheme": "ternary", "iters": 0, **_errors(w, wq)})
+    return rows
+
+
+def main(argv=None) -> int:
+    import woqdata
+
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--workload", default="block")
+    ap.add_argument("--blocks", type=int, nargs="*", default=[0])
+    ap.add_argument("--matrices", nargs="*", default=None,
+                    help="matrix name suffixes to include (e.g. k v gate); all if omitted")
+    args = ap.parse_args(argv)
+    torch.cuda.set_device(0)
+    wl, specs, mats = woqdata.generate(args.workload, device="cuda", blocks=args.blocks)
+    for spec, w in zip(specs, mats):
+        if args.matrices and spec.name.split(".")[-1] not in args.matrices:
+            continue
+        for r in matrix_report(w):
+            print(json.dumps({"matrix": spec.name, "shape": list(w.shape), **r}), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

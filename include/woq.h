@@ -9,7 +9,7 @@
  *
  * Sources, cited by page title and section:
  *  [EWQ]    "Giai ma EWQ & FastEWQ: Luong tu hoa LLM 'thong minh' hon, nhe hon
- *           ..." (2kvn.com), section "EWQ hoat dong nhu the nao?", steps 1-2.
+ *           ..." (2kvn.com), section "EWQ hoat dong nhu the nao?", steps 1-3.
  *  [SINQ]   "Huawei gioi thieu SINQ: phuong phap luong tu hoa ma nguon mo ..."
  *           (asiadaily.org), sections "Dinh ty le tren hai truc" (dual-axis
  *           scaling) and "Chuan hoa Sinkhorn Knopp".
@@ -58,6 +58,7 @@ extern "C" {
 #define WOQ_ERR_HIP       8  /* a HIP call or kernel launch failed           */
 #define WOQ_ERR_ALIGN     9  /* data pointer not 16-byte aligned             */
 #define WOQ_ERR_COUNT    10  /* n_mats / n_blocks out of range               */
+#define WOQ_ERR_VALUE    11  /* a host-side value is not finite              */
 
 /* element types */
 #define WOQ_F32  0
@@ -187,6 +188,35 @@ int32_t dequant_unpack(const woq_mat* out, int32_t n_mats,
 int32_t ternary_pack(const woq_mat* mats, int32_t n_mats,
                      uint8_t* const* codes, float* const* row_scale,
                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * ewq_budget_levels -- [EWQ] step 3 (budgeted placement in the serving
+ *  cluster): adjust the precision levels the tiers give so that the model
+ *  fits a storage budget.  Host-side only: every pointer is HOST memory and
+ *  no GPU work is enqueued.
+ *  Levels ascend in storage; level_bytes[b * n_levels + l] is block b's
+ *  storage at level l (for example 0 ternary, 1 int4 after balancing,
+ *  2 int8 per row, 3 kept bf16).  From level0, with total S:
+ *   S <= budget: repeatedly raise by one level the block of highest entropy
+ *     (ties: lower index) among those below the top level whose promotion
+ *     keeps S <= budget; stop when no promotion fits.
+ *   S >  budget: repeatedly lower by one level the block of lowest entropy
+ *     (ties: lower index) among those above level 0, until S <= budget or
+ *     every block is at level 0.
+ *  h_block     [n_blocks] block entropies (finite)
+ *  level_bytes [n_blocks * n_levels] (>= 0)
+ *  level0      [n_blocks] starting levels in [0, n_levels)
+ *  level_out   [n_blocks] (written)   total_out: final bytes (written)
+ *  fits_out    1 if the final total is within the budget, else 0 (written)
+ *  Errors: NULL pointer (WOQ_ERR_NULL); n_blocks outside [1, 2^20] or
+ *  n_levels outside [1, 64] (WOQ_ERR_COUNT); a level0 out of range, a
+ *  negative byte count or budget (WOQ_ERR_SHAPE); a non-finite entropy
+ *  (WOQ_ERR_VALUE).  Nothing is written on error.
+ */
+int32_t ewq_budget_levels(const double* h_block, const int64_t* level_bytes,
+                          int32_t n_blocks, int32_t n_levels, const int32_t* level0,
+                          int64_t budget, int32_t* level_out, int64_t* total_out,
+                          int32_t* fits_out);
 
 #ifdef __cplusplus
 }

@@ -13,8 +13,9 @@ Sources (cited by page title and section; the pages are Vietnamese):
 * [EWQ]  "Giải mã EWQ & FastEWQ: Lượng tử hóa LLM 'thông minh' hơn, nhẹ hơn
   mà không cần hy sinh hiệu suất" (2kvn.com), section "EWQ hoạt động như thế
   nào?" (how EWQ works): step 1 "Phân tích Entropy của từng Khối" (per-block
-  entropy) and step 2 "Tiêu chí lựa chọn khối để Lượng tử hóa" (block
-  selection criterion).
+  entropy), step 2 "Tiêu chí lựa chọn khối để Lượng tử hóa" (block
+  selection criterion) and step 3 (budgeted placement in the cluster,
+  "Algorithm 1").
 * [SINQ] "Huawei giới thiệu SINQ: phương pháp lượng tử hóa mã nguồn mở giúp LLM
   hoạt động hiệu quả hơn" (asiadaily.org), sections "Định tỷ lệ trên hai trục"
   (dual-axis scaling) and "Chuẩn hóa Sinkhorn Knopp" (Sinkhorn-Knopp
@@ -36,14 +37,14 @@ Parity pins: every function here is pinned by a ``-m "not gpu"`` test against
 closed forms, library routines, brute force (mpmath / exact fractions) or hand
 fixtures under ``tests/golden``.  No function is left "parity unpinned".
 """
-from .ewq import matrix_entropy, block_entropy, ewq_tiers, ewq_order
+from .ewq import matrix_entropy, block_entropy, ewq_tiers, ewq_order, ewq_budget
 from .sinq import sinkhorn_std, line_std
 from .rtn import (quantize_groupwise_f32, quantize_groupwise_f64, pack_codes,
                   unpack_codes, dequantize_f32, near_tie_fraction)
 from .ternary import ternary_quantize, ternary_dequantize
 
 __all__ = [
-    "matrix_entropy", "block_entropy", "ewq_tiers", "ewq_order",
+    "matrix_entropy", "block_entropy", "ewq_tiers", "ewq_order", "ewq_budget",
     "sinkhorn_std", "line_std",
     "quantize_groupwise_f32", "quantize_groupwise_f64", "pack_codes",
     "unpack_codes", "dequantize_f32", "near_tie_fraction",

@@ -64,3 +64,53 @@ def ewq_order(h_block) -> np.ndarray:
     """Blocks in ascending entropy order, ties broken by block index."""
     h = np.asarray(h_block, dtype=np.float64)
     return np.array(sorted(range(h.size), key=lambda b: (h[b], b)), dtype=np.int32)
+
+
+def ewq_budget(h_block, level_bytes, level0, budget: int):
+    """[EWQ] step 3 (budgeted placement, "Algorithm 1"): adjust the tiers'
+    precision levels to a memory budget.
+
+    ``level_bytes[b][l]`` is block b's storage at level l, levels in
+    ascending size (e.g. 0 ternary, 1 int4 after balancing, 2 int8 per row,
+    3 kept bf16); ``level0`` are the levels the tiers give.  The page says
+    that spare room goes to promoting the highest-entropy quantised blocks
+    to higher precision, and that a shortfall is met by demoting the
+    lowest-entropy blocks to lower precision.  Reading taken here, one level
+    at a time:
+
+    * total <= budget: repeatedly promote, by one level, the block of
+      highest entropy (ties: lower index) among those below the top level
+      whose promotion still fits; stop when none fits;
+    * total > budget: repeatedly demote, by one level, the block of lowest
+      entropy (ties: lower index) among those above the bottom level; stop
+      when the total fits or nothing can be demoted.
+
+    Returns (levels, total bytes, fits).
+    """
+    h = [float(v) for v in h_block]
+    lb = [[int(x) for x in row] for row in level_bytes]
+    lev = [int(v) for v in level0]
+    top = [len(row) - 1 for row in lb]
+    total = sum(lb[b][lev[b]] for b in range(len(h)))
+    if total <= budget:
+        while True:
+            best = None
+            for b in range(len(h)):
+                if lev[b] < top[b] and total - lb[b][lev[b]] + lb[b][lev[b] + 1] <= budget:
+                    if best is None or h[b] > h[best]:
+                        best = b
+            if best is None:
+                break
+            total += lb[best][lev[best] + 1] - lb[best][lev[best]]
+            lev[best] += 1
+    else:
+        while total > budget:
+            best = None
+            for b in range(len(h)):
+                if lev[b] > 0 and (best is None or h[b] < h[best]):
+                    best = b
+            if best is None:
+                break
+            total += lb[best][lev[best] - 1] - lb[best][lev[best]]
+            lev[best] -= 1
+    return np.array(lev, dtype=np.int32), total, total <= budget

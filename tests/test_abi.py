@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = _lib.load()
-    for code in range(0, 11):
+    for code in range(0, 12):
         s = lib.woq_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.woq_status_string(99).decode() == "unknown status"

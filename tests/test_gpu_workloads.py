@@ -183,3 +183,37 @@ def test_quality_report_rows():
                  * scales[0].double().repeat_interleave(64, dim=1)).max().item() / 2
         assert by[("int4 g64", k)]["max_abs"] <= bound * (1 + 1e-5)
     assert 0 < by[("ternary", 0)]["rel_fro"] < 1
+
+
+def test_budgeted_placement_moe_layers():
+    """EWQ step 3 on four MoE layers: a budget below the tiers' storage
+    demotes the lowest-entropy layers first; the pass then runs the moved
+    actions and every output is present and within the budget."""
+    import weight_only_quantization_softmax_amd as woq
+    wl, specs, mats = woqdata.generate("moe", device=DEV, blocks=[0, 1, 2, 3])
+    bid = [m.block for m in specs]
+    probe = QuantPass(mats, bid, 4, iters=wl.iters, bits=wl.bits, group=wl.group,
+                      actions=(wl.low_tier, wl.mid_tier, wl.high_tier))
+    tiers0 = probe.run()
+    torch.cuda.synchronize()
+    lb = probe.level_bytes()
+    from weight_only_quantization_softmax_amd.pipeline import ACTIONS
+    level0 = [ACTIONS.index(a) for a in probe.action_of_block(tiers0)]
+    start = sum(lb[b][level0[b]] for b in range(4))
+    hb = probe.h_block.cpu().tolist()
+    for budget in (start - 1, (start + sum(r[0] for r in lb)) // 2, start + 10**9):
+        qp = QuantPass(mats, bid, 4, iters=wl.iters, bits=wl.bits, group=wl.group,
+                       actions=(wl.low_tier, wl.mid_tier, wl.high_tier), budget_bytes=budget)
+        qp.run()
+        torch.cuda.synchronize()
+        ref_lev, ref_total, ref_fits = oracle.ewq_budget(hb, lb, level0, budget)
+        assert [ACTIONS.index(a) for a in qp.last_actions] == ref_lev.tolist()
+        assert qp.last_budget == (ref_total, ref_fits) and ref_fits
+        # storage actually produced equals the planned total
+        produced = 0
+        for i, m in enumerate(mats):
+            out = qp.outputs[i]
+            assert out["action"] == qp.last_actions[bid[i]]
+            produced += qp.action_bytes(out["action"], m)
+        assert produced == ref_total <= budget
+    assert woq.ewq_budget_levels(hb, lb, level0, 0)[2] is False

@@ -12,6 +12,8 @@ calls raise.
   quant_pack_groupwise  group-wise asymmetric RTN with LSB-first bit packing
   dequant_unpack        inverse map (codes -> weights)
   ternary_pack          ternary {-1, 0, +1} codes with a per-row scale
+  ewq_budget_levels     EWQ's budgeted placement: precision levels to a budget
+                        (host-side)
 """
 from __future__ import annotations
 
@@ -24,7 +26,7 @@ from . import _lib
 from ._lib import WoqError  # noqa: F401
 
 __all__ = ["ewq_block_entropy", "sinq_balance", "quant_pack_groupwise",
-           "dequant_unpack", "ternary_pack", "workspace_size", "WoqError"]
+           "dequant_unpack", "ternary_pack", "ewq_budget_levels", "workspace_size", "WoqError"]
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -170,3 +172,21 @@ def ternary_pack(mats: Sequence[torch.Tensor], *, codes=None, row_scale=None, ws
                           ws.numel(), _stream(stream))
     _lib.check("ternary_pack", st)
     return codes, row_scale
+
+
+def ewq_budget_levels(h_block: Sequence[float], level_bytes, level0: Sequence[int], budget: int):
+    """Levels adjusted to a storage budget: (levels list, total bytes, fits).
+
+    ``level_bytes[b][l]`` is block b's storage at level l (ascending)."""
+    lib = _lib.load()
+    n = len(h_block)
+    nl = len(level_bytes[0]) if n else 0
+    hb = (ctypes.c_double * n)(*[float(v) for v in h_block])
+    lb = (ctypes.c_int64 * (n * nl))(*[int(x) for row in level_bytes for x in row])
+    l0 = (ctypes.c_int32 * n)(*[int(v) for v in level0])
+    out = (ctypes.c_int32 * n)()
+    total = ctypes.c_int64(0)
+    fits = ctypes.c_int32(0)
+    _lib.check("ewq_budget_levels", lib.ewq_budget_levels(hb, lb, n, nl, l0, int(budget), out,
+                                                          ctypes.byref(total), ctypes.byref(fits)))
+    return list(out), total.value, bool(fits.value)

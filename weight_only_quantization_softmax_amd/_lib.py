@@ -16,13 +16,15 @@ STATUS = {
     0: "WOQ_OK", 1: "WOQ_ERR_NULL", 2: "WOQ_ERR_SHAPE", 3: "WOQ_ERR_DTYPE",
     4: "WOQ_ERR_BITS", 5: "WOQ_ERR_ITERS", 6: "WOQ_ERR_WORKSPACE",
     7: "WOQ_ERR_BLOCK", 8: "WOQ_ERR_HIP", 9: "WOQ_ERR_ALIGN", 10: "WOQ_ERR_COUNT",
+    11: "WOQ_ERR_VALUE",
 }
 WOQ_F32, WOQ_BF16 = 0, 1
 OP_ENTROPY, OP_SINQ, OP_QUANT, OP_DEQUANT, OP_TERNARY = 1, 2, 3, 4, 5
 
 # every symbol include/woq.h declares
 EXPORTS = ("woq_status_string", "woq_workspace_size", "ewq_block_entropy",
-           "sinq_balance", "quant_pack_groupwise", "dequant_unpack", "ternary_pack")
+           "sinq_balance", "quant_pack_groupwise", "dequant_unpack", "ternary_pack",
+           "ewq_budget_levels")
 
 
 class WoqMat(ctypes.Structure):
@@ -71,6 +73,11 @@ def load() -> ctypes.CDLL:
     lib.dequant_unpack.restype = I32
     lib.ternary_pack.argtypes = [ctypes.POINTER(WoqMat), I32, PP, PP, P, ctypes.c_size_t, P]
     lib.ternary_pack.restype = I32
+    lib.ewq_budget_levels.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
+                                      I32, I32, ctypes.POINTER(I32), ctypes.c_int64,
+                                      ctypes.POINTER(I32), ctypes.POINTER(ctypes.c_int64),
+                                      ctypes.POINTER(I32)]
+    lib.ewq_budget_levels.restype = I32
     _lib = lib
     return lib
 

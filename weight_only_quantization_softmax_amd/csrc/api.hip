@@ -10,6 +10,7 @@
 #include "launch.h"
 
 #include <algorithm>
+#include <cmath>
 #include <tuple>
 #include <cstring>
 #include <vector>
@@ -341,6 +342,7 @@ const char* woq_status_string(int32_t s) {
         case WOQ_ERR_HIP: return "HIP call or kernel launch failed";
         case WOQ_ERR_ALIGN: return "pointer not sufficiently aligned";
         case WOQ_ERR_COUNT: return "matrix or block count out of range";
+        case WOQ_ERR_VALUE: return "value not finite";
         default: return "unknown status";
     }
 }
@@ -655,6 +657,61 @@ int32_t ternary_pack(const woq_mat* mats, int32_t n_mats, uint8_t* const* codes,
     WOQ_HIP(hipMemcpyAsync(ws, host.data(), L.table_end, hipMemcpyHostToDevice, stream));
     if (L.nb) WOQ_HIP(ternary(at<QMat>(ws, L.tab_b), at<int64_t>(ws, L.ubeg_b), L.nb, ub[L.nb], WOQ_BF16, stream));
     if (L.nf) WOQ_HIP(ternary(at<QMat>(ws, L.tab_f), at<int64_t>(ws, L.ubeg_f), L.nf, uf[L.nf], WOQ_F32, stream));
+    return WOQ_OK;
+}
+
+int32_t ewq_budget_levels(const double* h_block, const int64_t* level_bytes, int32_t n_blocks,
+                          int32_t n_levels, const int32_t* level0, int64_t budget,
+                          int32_t* level_out, int64_t* total_out, int32_t* fits_out) {
+    if (!h_block || !level_bytes || !level0 || !level_out || !total_out || !fits_out)
+        return WOQ_ERR_NULL;
+    if (n_blocks < 1 || n_blocks > (1 << 20) || n_levels < 1 || n_levels > 64) return WOQ_ERR_COUNT;
+    if (budget < 0) return WOQ_ERR_SHAPE;
+    for (int32_t b = 0; b < n_blocks; ++b) {
+        if (level0[b] < 0 || level0[b] >= n_levels) return WOQ_ERR_SHAPE;
+        for (int32_t l = 0; l < n_levels; ++l)
+            if (level_bytes[(size_t)b * n_levels + l] < 0) return WOQ_ERR_SHAPE;
+        if (!std::isfinite(h_block[b])) return WOQ_ERR_VALUE;
+    }
+    auto bytes = [&](int32_t b, int32_t l) { return level_bytes[(size_t)b * n_levels + l]; };
+    std::vector<int32_t> lev(level0, level0 + n_blocks);
+    int64_t total = 0;
+    for (int32_t b = 0; b < n_blocks; ++b) total += bytes(b, lev[b]);
+    std::vector<int32_t> by_h(n_blocks);
+    for (int32_t b = 0; b < n_blocks; ++b) by_h[b] = b;
+    if (total <= budget) {
+        // promotion: scan blocks by descending entropy (ties: lower index);
+        // the first one whose next level fits is raised, then scan again
+        std::stable_sort(by_h.begin(), by_h.end(),
+                         [&](int32_t a, int32_t c) { return h_block[a] > h_block[c]; });
+        for (bool moved = true; moved;) {
+            moved = false;
+            for (int32_t b : by_h) {
+                if (lev[b] + 1 >= n_levels) continue;
+                const int64_t next = total - bytes(b, lev[b]) + bytes(b, lev[b] + 1);
+                if (next <= budget) {
+                    total = next;
+                    ++lev[b];
+                    moved = true;
+                    break;
+                }
+            }
+        }
+    } else {
+        // demotion: the lowest-entropy block above level 0 goes down a level
+        std::stable_sort(by_h.begin(), by_h.end(),
+                         [&](int32_t a, int32_t c) { return h_block[a] < h_block[c]; });
+        size_t i = 0;
+        while (total > budget && i < by_h.size()) {
+            const int32_t b = by_h[i];
+            if (lev[b] == 0) { ++i; continue; }
+            total += bytes(b, lev[b] - 1) - bytes(b, lev[b]);
+            --lev[b];
+        }
+    }
+    std::copy(lev.begin(), lev.end(), level_out);
+    *total_out = total;
+    *fits_out = total <= budget ? 1 : 0;
     return WOQ_OK;
 }
 

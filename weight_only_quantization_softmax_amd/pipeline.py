@@ -10,6 +10,12 @@ What each tier does is a parameter of the pass:
   "ternary"  ternary {-1, 0, +1} with a per-row scale
   "keep"     left as is
 
+With a storage budget, the tiers' choices are then moved along the ladder
+ACTIONS (ascending storage: ternary < Sinkhorn + low-bit < int8 per row <
+kept) by EWQ's budgeted placement (same page, step 3): spare room promotes
+the highest-entropy quantised blocks, a shortfall demotes the lowest-entropy
+ones (ewq_budget_levels, host-side in the library).
+
 A :class:`QuantPass` is prepared once for a fixed set of device-resident
 matrices: every output buffer and workspace is allocated up front (per tier
 assignment), so :meth:`QuantPass.run` only launches library calls and reads
@@ -24,7 +30,7 @@ import torch
 
 from . import _lib
 
-ACTIONS = ("sinq", "int8row", "ternary", "keep")
+ACTIONS = ("ternary", "sinq", "int8row", "keep")   # ascending storage per weight
 
 
 def _mat_arr(ts):
@@ -54,7 +60,7 @@ class QuantPass:
     def __init__(self, mats: Sequence[torch.Tensor], block_id: Sequence[int], n_blocks: int, *,
                  iters: int, bits: int, group: int, x: float = 1.0, tiered: bool = True,
                  actions: Sequence[str] = ("sinq", "int8row", "keep"),
-                 sinq_batch_bytes: int = 0):
+                 sinq_batch_bytes: int = 0, budget_bytes: Optional[int] = None):
         for a in actions:
             if a not in ACTIONS:
                 raise ValueError(a)
@@ -77,9 +83,12 @@ class QuantPass:
         self._ent_ws = _ws(_lib.OP_ENTROPY, self.mats, 0, dev)
         self._ent_mats = _mat_arr(self.mats)
         self._bid = (ctypes.c_int32 * n)(*self.block_id)
-        self._plans: Dict[tuple, List[_Call]] = {}
+        self._plans: Dict[tuple, tuple] = {}
         self.outputs: Dict[int, dict] = {}
         self.bytes_in = sum(m.numel() * m.element_size() for m in self.mats)
+        self.budget_bytes = budget_bytes
+        self.last_actions: Optional[List[str]] = None
+        self.last_budget: Optional[tuple] = None   # (total bytes, fits)
 
     # ------------------------------------------------------------ planning
     def _entropy_call(self) -> _Call:
@@ -170,16 +179,52 @@ class QuantPass:
                       (arr, len(mats), cp, bp, ws.data_ptr(), ws.numel()),
                       (arr, cp, bp, ws), "ternary", nb)]
 
+    def action_bytes(self, action: str, m: torch.Tensor) -> int:
+        """Storage of one matrix under an action (codes and per-group /
+        per-row / per-column metadata)."""
+        r, c = m.shape
+        if action == "ternary":
+            return r * c // 4 + 4 * r
+        if action == "sinq":
+            return r * c * self.bits // 8 + r * (c // self.group) * 5 + 4 * (r + c)
+        if action == "int8row":
+            return r * c + 5 * r
+        return m.numel() * m.element_size()
+
+    def level_bytes(self) -> List[List[int]]:
+        """Per block, its storage at each rung of ACTIONS."""
+        out = [[0] * len(ACTIONS) for _ in range(self.n_blocks)]
+        for m, b in zip(self.mats, self.block_id):
+            for lvl, a in enumerate(ACTIONS):
+                out[b][lvl] += self.action_bytes(a, m)
+        return out
+
     def action_of_block(self, tiers) -> List[str]:
         if not self.tiered:
             return [self.actions[0]] * self.n_blocks
         return [self.actions[int(t) - 1] for t in tiers]
 
+    def budgeted_actions(self, tiers, h_block) -> List[str]:
+        """EWQ step 3: the tiers' actions moved along ACTIONS to the budget."""
+        from . import ewq_budget_levels
+        level0 = [ACTIONS.index(a) for a in self.action_of_block(tiers)]
+        levels, total, fits = ewq_budget_levels(h_block, self.level_bytes(), level0,
+                                                self.budget_bytes)
+        self.last_budget = (total, fits)
+        return [ACTIONS[lv] for lv in levels]
+
     def plan(self, tiers) -> List[_Call]:
-        key = tuple(int(t) for t in tiers)
+        return self.plan_actions(self.action_of_block(tuple(int(t) for t in tiers)))
+
+    def plan_actions(self, acts) -> List[_Call]:
+        """Calls (and output buffers) for one action per block; cached per
+        assignment, and ``outputs`` always describes the latest plan used."""
+        key = tuple(acts)
         if key in self._plans:
-            return self._plans[key]
-        acts = self.action_of_block(key)
+            calls, outputs = self._plans[key]
+            self.outputs = outputs
+            return calls
+        self.outputs = {}
         by_action: Dict[str, List[int]] = {a: [] for a in ACTIONS}
         for i, b in enumerate(self.block_id):
             by_action[acts[b]].append(i)
@@ -192,7 +237,7 @@ class QuantPass:
             calls += self._ternary_calls(by_action["ternary"])
         for i in by_action["keep"]:
             self.outputs[i] = {"action": "keep"}
-        self._plans[key] = calls
+        self._plans[key] = (calls, self.outputs)
         return calls
 
     # ------------------------------------------------------------ running
@@ -204,7 +249,12 @@ class QuantPass:
         calls = [self._entropy_call()]
         self._run_calls(calls, stream, h, timers)
         tiers = self.tier.cpu().tolist()   # the one host synchronisation
-        self._run_calls(self.plan(tiers), stream, h, timers)
+        if self.budget_bytes is None:
+            acts = self.action_of_block(tiers)
+        else:
+            acts = self.budgeted_actions(tiers, self.h_block.cpu().tolist())
+        self.last_actions = acts
+        self._run_calls(self.plan_actions(acts), stream, h, timers)
         return tiers
 
     @staticmethod

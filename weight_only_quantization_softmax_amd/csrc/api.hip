@@ -182,7 +182,10 @@ SinqLayout sinq_layout(const woq_mat* mats, int32_t n) {
         }
         for (int k = p; k < q; ++k) {
             const woq_mat& m = mats[idx[k]];
-            const int64_t srows = lo * R;
+            // never taller than an even split of the matrix over one
+            // workgroup's strips (a matrix smaller than per_wg strips of the
+            // common height would otherwise leave waves of its workgroup idle)
+            const int64_t srows = std::min<int64_t>(lo, cdiv(m.rows, (int64_t)R * per_wg)) * R;
             L.strip_rows[k] = (int32_t)srows;
             L.n_strips[k] = (int32_t)cdiv(m.rows, srows * per_wg);
             g.n_strips += L.n_strips[k];

@@ -440,15 +440,19 @@ __global__ __launch_bounds__(kMaxT) void k_sinq_pass(const SinqMat* __restrict__
 // order and the workgroup writes one partial row.  RAG: the row is not a
 // multiple of 512 columns, so lanes own unequal numbers of vectors.
 // Shape constants of the wave pass.  KEEP: the row is kept unpacked between
-// the two passes (rows of at most 4 vectors per lane); wider bf16 rows keep
+// the two passes (rows of at most 3 vectors per lane); wider bf16 rows keep
 // only the packed row and unpack it once per pass (register pressure).  Two
 // waves per SIMD throughout (measured: more waves with re-unpacked narrow
-// rows ran slower).
+// rows ran slower); narrow rows instead take RW rows per step.
 template <int DT, int NVL>
 struct WaveCfg {
     static constexpr bool F32 = DT == WOQ_F32;
     static constexpr int OCC = 2;  // waves per SIMD
-    static constexpr bool KEEP = F32 || NVL <= 4;
+    static constexpr bool KEEP = F32 || NVL <= 3;
+    // rows per step: narrow bf16 rows go RW at a time, sharing each 1/t read
+    // among RW rows (measured on MoE shapes: 2 rows help 4-vector rows by 5%,
+    // and cost 3-vector ragged rows 4%)
+    static constexpr int RW = (F32 || NVL >= 5 || NVL == 3) ? 1 : (NVL == 4 ? 2 : (NVL == 2 ? 2 : 4));
     static constexpr int NP = F32 ? 4 : 2;                  // partial floats per column
     static constexpr int UW = NVL * 512 + 8;                // LDS floats of u and its zero pad
     static constexpr size_t lds() { return sizeof(float) * ((size_t)UW + (size_t)NP * NVL * 512); }
@@ -508,85 +512,110 @@ __global__ __launch_bounds__(256, (WaveCfg<DT, NVL>::OCC)) void k_sinq_wave(
             if constexpr (F32) { cmn[k][e] = INFINITY; cmx[k][e] = -INFINITY; }
         }
 
-    auto load_row = [&](Vec8<DT> (&P)[NVL], int row) {
+    constexpr int RW = WC::RW;
+    // rows row0 .. row0 + RW - 1 (clamped into the strip: loads stay in bounds)
+    auto load_rows = [&](Vec8<DT> (&P)[RW][NVL], int row0) {
 #pragma unroll
-        for (int k = 0; k < NVL; ++k) P[k] = ldv<DT>(sm.data, (int64_t)row * cols + 8 * vk[k]);
+        for (int rr = 0; rr < RW; ++rr) {
+            const int64_t row = min(row0 + rr, r1 - 1);
+#pragma unroll
+            for (int k = 0; k < NVL; ++k) P[rr][k] = ldv<DT>(sm.data, row * cols + 8 * vk[k]);
+        }
     };
-    auto process = [&](Vec8<DT> (&P)[NVL], int row) {
-        float xk[KEEP ? NVL : 1][8];
+    auto process = [&](Vec8<DT> (&P)[RW][NVL], int row0) {
+        float xk[KEEP ? RW : 1][KEEP ? NVL : 1][8];
         if constexpr (KEEP) {
 #pragma unroll
-            for (int k = 0; k < NVL; ++k) unpack<DT>(P[k], xk[k]);
+            for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+                for (int k = 0; k < NVL; ++k) unpack<DT>(P[rr][k], xk[rr][k]);
         } else {
 #pragma unroll
-            for (int k = 0; k < NVL; ++k) opaque<DT>(P[k]);
+            for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+                for (int k = 0; k < NVL; ++k) opaque<DT>(P[rr][k]);
         }
-        auto xval = [&](int k, float (&x)[8]) {
+        auto xval = [&](int rr, int k, float (&x)[8]) {
             if constexpr (KEEP) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = xk[k][e];
+                for (int e = 0; e < 8; ++e) x[e] = xk[rr][k][e];
             } else {
-                unpack<DT>(P[k], x);
+                unpack<DT>(P[rr][k], x);
             }
         };
-        // lane moments of x*u around K = the lane's first product
-        float S0 = 0.f, S1 = 0.f, Q0 = 0.f, Q1 = 0.f, K = 0.f;
+        // lane moments of x*u around K = the lane's first product, per row
+        float S0[RW], S1[RW], Q0[RW], Q1[RW], K[RW];
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr) S0[rr] = S1[rr] = Q0[rr] = Q1[rr] = K[rr] = 0.f;
 #pragma unroll
         for (int k = 0; k < NVL; ++k) {
-            float x[8];
-            xval(k, x);
             const f32x4 ua = u4[2 * vk[k]], ub = u4[2 * vk[k] + 1];
             const float uu[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
-            if (k == 0) K = x[0] * uu[0];
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                float y0 = fmaf(x[e], uu[e], -K), y1 = fmaf(x[e + 1], uu[e + 1], -K);
-                if (RAG && !own[k]) { y0 = 0.f; y1 = 0.f; }
-                S0 += y0;
-                S1 += y1;
-                Q0 = fmaf(y0, y0, Q0);
-                Q1 = fmaf(y1, y1, Q1);
+            for (int rr = 0; rr < RW; ++rr) {
+                float x[8];
+                xval(rr, k, x);
+                if (k == 0) K[rr] = x[0] * uu[0];
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    float y0 = fmaf(x[e], uu[e], -K[rr]), y1 = fmaf(x[e + 1], uu[e + 1], -K[rr]);
+                    if (RAG && !own[k]) { y0 = 0.f; y1 = 0.f; }
+                    S0[rr] += y0;
+                    S1[rr] += y1;
+                    Q0[rr] = fmaf(y0, y0, Q0[rr]);
+                    Q1[rr] = fmaf(y1, y1, Q1[rr]);
+                }
             }
         }
-        float mm, qq;
-        lane_moments(K, S0 + S1, Q0 + Q1, nl, rnl, mm, qq);
-        if constexpr (RAG) {
-            float nn = nl;
-            wave_moments_gen(mm, qq, nn);
-        } else {
-            wave_moments_eq(mm, qq, nl);
+        float v[RW];
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr) {
+            float mm, qq;
+            lane_moments(K[rr], S0[rr] + S1[rr], Q0[rr] + Q1[rr], nl, rnl, mm, qq);
+            if constexpr (RAG) {
+                float nn = nl;
+                wave_moments_gen(mm, qq, nn);
+            } else {
+                wave_moments_eq(mm, qq, nl);
+            }
+            const float var = first_lane(qq) / fn;
+            const float s = var > 0.f ? __fsqrt_rn(var) : 1.0f;
+            v[rr] = __fdiv_rn(1.0f, s);
+            if (lane == 0 && row0 + rr < r1) gstore<float>(sm.s + row0 + rr, s);
         }
-        const float var = first_lane(qq) / fn;
-        const float s = var > 0.f ? __fsqrt_rn(var) : 1.0f;
-        const float v = __fdiv_rn(1.0f, s);
-        if (lane == 0) gstore<float>(sm.s + row, s);
         if constexpr (!KEEP) {
 #pragma unroll
-            for (int k = 0; k < NVL; ++k) opaque<DT>(P[k]);
+            for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+                for (int k = 0; k < NVL; ++k) opaque<DT>(P[rr][k]);
         }
-        // column partials with this row's scale
+        // column partials with each row's scale (rows past the strip add nothing)
 #pragma unroll
-        for (int k = 0; k < NVL; ++k) {
-            float x[8];
-            xval(k, x);
+        for (int rr = 0; rr < RW; ++rr) {
+            if (row0 + rr >= r1) break;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float z = x[e] * v;
-                cs[k][e] += z;
-                cq[k][e] = fmaf(z, z, cq[k][e]);
-                if constexpr (F32) { cmn[k][e] = fminf(cmn[k][e], z); cmx[k][e] = fmaxf(cmx[k][e], z); }
+            for (int k = 0; k < NVL; ++k) {
+                float x[8];
+                xval(rr, k, x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float z = x[e] * v[rr];
+                    cs[k][e] += z;
+                    cq[k][e] = fmaf(z, z, cq[k][e]);
+                    if constexpr (F32) { cmn[k][e] = fminf(cmn[k][e], z); cmx[k][e] = fmaxf(cmx[k][e], z); }
+                }
             }
         }
     };
 
-    Vec8<DT> PA[NVL], PB[NVL];
-    if (r0 < r1) load_row(PA, r0);
-    for (int row = r0; row < r1; row += 2) {
-        if (row + 1 < r1) load_row(PB, row + 1);
+    Vec8<DT> PA[RW][NVL], PB[RW][NVL];
+    if (r0 < r1) load_rows(PA, r0);
+    for (int row = r0; row < r1; row += 2 * RW) {
+        if (row + RW < r1) load_rows(PB, row + RW);
         process(PA, row);
-        if (row + 1 >= r1) break;
-        if (row + 2 < r1) load_row(PA, row + 2);
-        process(PB, row + 1);
+        if (row + RW >= r1) break;
+        if (row + 2 * RW < r1) load_rows(PA, row + 2 * RW);
+        process(PB, row + RW);
     }
     // the four waves' column partials, added in wave order in LDS
     for (int w = 0; w < 4; ++w) {

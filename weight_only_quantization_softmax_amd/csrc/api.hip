@@ -157,35 +157,59 @@ SinqLayout sinq_layout(const woq_mat* mats, int32_t n) {
         int q = p;
         while (q < n && key(idx[q]) == key(idx[p])) ++q;
         g.count = q - p;
-        // Strips of one height for the whole launch set: the smallest height
-        // (in register tiles of R rows) for which every workgroup is resident
-        // at once (about 8 waves per CU), so no workgroup runs in a second
-        // round.  Mode 0: a workgroup owns one strip.  Mode 1: its four waves
-        // own four consecutive strips.  A workgroup writes one partial row,
-        // so n_strips counts workgroups.
+        // Row strips per matrix.  Mode 0: a workgroup owns one strip of whole
+        // register tiles (R rows).  Mode 1: its four waves own four
+        // consecutive strips.  A workgroup writes one partial row, so
+        // n_strips counts workgroups.  Two plans, the faster estimate wins
+        // (work counted in rows; cap = workgroups resident at once, about 8
+        // waves per CU):
+        //  A  one common strip height, the smallest for which every
+        //     workgroup is resident at once (a single round);
+        //  B  workgroups of about total / (4 cap) rows (at least 64), run in
+        //     several rounds and scheduled as slots free up - better when
+        //     the matrices are about as many as the slots, where plan A
+        //     must give a whole large matrix to one workgroup.
         const int R = g.sh.mode == 1 ? 1 : sinq_tile_rows(g.dtype, g.sh.nv);
         const int per_wg = g.sh.mode == 1 ? 4 : 1;
+        const int64_t unit = (int64_t)R * per_wg;  // rows per strip height step
         const int waves_per_wg = g.sh.mode == 1 ? 4 : g.sh.nt / 64;
         const int waves_per_cu =
             g.sh.mode == 1 ? 4 * sinq_wave_occupancy(g.dtype, g.sh.nv) : kSinqWavesPerCU;
         const int64_t cap = (int64_t)kSinqCUs * std::max(1, waves_per_cu / waves_per_wg);
-        auto wgs_for = [&](int64_t t) {
-            int64_t n_wg = 0;
-            for (int k = p; k < q; ++k) n_wg += cdiv(mats[idx[k]].rows, t * R * per_wg);
-            return n_wg;
+        int64_t total_rows = 0;
+        for (int k = p; k < q; ++k) total_rows += mats[idx[k]].rows;
+        // strip height (in tiles) of matrix k when its workgroups hold at
+        // most t tiles per strip: an even split of the matrix
+        auto height = [&](int64_t rows, int64_t t) {
+            const int64_t n_wg = cdiv(rows, t * unit);
+            return cdiv(cdiv(rows, n_wg), unit);
+        };
+        auto plan_cost = [&](int64_t t, int64_t* n_wg_out) {
+            int64_t n_wg = 0, most = 0;
+            for (int k = p; k < q; ++k) {
+                const int64_t rows = mats[idx[k]].rows;
+                const int64_t h = height(rows, t);
+                n_wg += cdiv(rows, h * unit);
+                most = std::max(most, h * unit);
+            }
+            *n_wg_out = n_wg;
+            return n_wg <= cap ? most : cdiv(total_rows, cap) + most;
         };
         int64_t lo = 1, hi = 1;
-        for (int k = p; k < q; ++k) hi = std::max<int64_t>(hi, cdiv(mats[idx[k]].rows, R));
+        for (int k = p; k < q; ++k) hi = std::max<int64_t>(hi, cdiv(mats[idx[k]].rows, unit));
         while (lo < hi) {
             const int64_t mid = (lo + hi) / 2;
-            if (wgs_for(mid) <= cap) hi = mid; else lo = mid + 1;
+            int64_t n_wg = 0;
+            plan_cost(mid, &n_wg);
+            if (n_wg <= cap) hi = mid; else lo = mid + 1;
         }
+        const int64_t t_b = std::max<int64_t>(cdiv(64, unit), cdiv(total_rows, 4 * cap * unit));
+        int64_t n_a = 0, n_b = 0;
+        const int64_t cost_a = plan_cost(lo, &n_a), cost_b = plan_cost(t_b, &n_b);
+        const int64_t t_sel = cost_b < cost_a ? t_b : lo;
         for (int k = p; k < q; ++k) {
             const woq_mat& m = mats[idx[k]];
-            // never taller than an even split of the matrix over one
-            // workgroup's strips (a matrix smaller than per_wg strips of the
-            // common height would otherwise leave waves of its workgroup idle)
-            const int64_t srows = std::min<int64_t>(lo, cdiv(m.rows, (int64_t)R * per_wg)) * R;
+            const int64_t srows = height(m.rows, t_sel) * R;
             L.strip_rows[k] = (int32_t)srows;
             L.n_strips[k] = (int32_t)cdiv(m.rows, srows * per_wg);
             g.n_strips += L.n_strips[k];

@@ -10,33 +10,38 @@
 // centred population std, zero std -> 1; t starts at 1.  Kernels hold
 // u = 1/t and v = 1/s (correctly rounded fp32) and form x = w * u (w * v).
 //
-// Fused pass (one read of W per iteration).  A workgroup owns a strip of
-// whole rows of one matrix; thread t owns the 8-column vectors t, t + NT,
-// ..., so its column partial sums stay in registers for the whole strip.
-// The strip is walked in tiles of R rows held in registers (the next tile's
-// loads are in flight while the current one is processed):
-//   1. row statistics in two passes over the registers: the row sums of
-//      x = w*u, then the centred sums of squares.  Each pass reduces the R
-//      per-thread partials over the wave with a butterfly reduce-scatter on
-//      permlane swaps and DPP, then over the waves through LDS (every wave
-//      adds the wave totals in wave order) -> s_i, v_i = 1/s_i;
+// Fused pass (one read of W per iteration), in two forms:
+//  - k_sinq_wave, rows of at most 4096 bf16 (1536 fp32) columns: a wave owns
+//    a strip of whole rows, lane l the 8-column vectors l + 64 k, so the row
+//    statistics are wave-local (no workgroup barrier);
+//  - k_sinq_pass, wider rows: a workgroup owns a strip of whole rows, thread
+//    t the vectors t + NT k, and the row statistics are combined over the
+//    waves through LDS (one barrier per tile of R rows).
+// In both, a thread's column partial sums stay in registers for the whole
+// strip, the next rows' loads are in flight while the current ones are
+// processed, and per row:
+//   1. row moments of x = w*u in one pass: each lane sums y = x*u - K around
+//      a lane-local shift K (its first product), giving its mean and centred
+//      sum of squares M2 = sum y^2 - (sum y)^2 / n; lanes (then waves) are
+//      merged with the pairwise update of Chan, Golub and LeVeque (1979)
+//      -> s_i, v_i = 1/s_i;
 //   2. the same registers give z = w*v_i, accumulated into the thread's
 //      column (sum, sum of squares).
-// At the end of the strip the column partials are written per strip; a
-// second kernel combines them per column in fp64 in strip order -> t_j, u_j.
+// At the end every workgroup writes one partial row; a second kernel combines
+// the partial rows per column in fp64 in a fixed order -> t_j, u_j.
 // Everything runs in a fixed order, so results are deterministic.
 //
-// Row variance is the centred second moment (two-pass: no cancellation,
-// exactly 0 for a constant row: bf16 sums of equal values are exact in fp32
-// for rows up to 2^15 wide; fp32 rows are first shifted by their first
-// element).  Column variance is E[z^2] - E[z]^2 in fp64 from fp32 strip
+// Accuracy.  Since K is one of the lane's own values, n (mean - K)^2 is at
+// most n M2_lane, so the shifted sums lose about eps (n + 1) of M2_lane
+// (n <= 64 per lane); a constant row at the first step gives y = 0 exactly
+// (std 0 -> scale 1).  Column variance is E[z^2] - E[z]^2 in fp64 from fp32
 // partials: relative accuracy ~1e-7 (1 + mean^2/var), ample for the
-// near-zero column means of weight matrices.  bf16 columns that are
-// constant at the first step (or all zero) sum exactly; fp32 inputs also
-// track per-column min/max (a constant column has std 0).
+// near-zero column means of weight matrices; bf16 columns that are constant
+// at the first step (or all zero) sum exactly, and fp32 inputs also track
+// per-column min/max (a constant column has std 0).
 //
-// Matrices of one launch share (NT, NV): NV = vectors per thread (1..8), NT =
-// threads per workgroup (<= 512).  For NV >= 3 the u vector lives in LDS.
+// Matrices of one launch share their shape class (wave or workgroup form,
+// vectors per lane / thread, threads per workgroup).
 #include "launch.h"
 
 #include <math.h>

@@ -71,12 +71,6 @@ __device__ __forceinline__ Vec8<DT> ldv(const void* base, int64_t e) {
 }
 
 template <int DT>
-__device__ __forceinline__ float ld1(const void* base, int64_t e) {
-    if constexpr (DT == WOQ_BF16) return __uint_as_float((uint32_t)gload<uint16_t>(reinterpret_cast<const uint16_t*>(base) + e) << 16);
-    else return gload<float>(reinterpret_cast<const float*>(base) + e);
-}
-
-template <int DT>
 __device__ __forceinline__ void unpack(const Vec8<DT>& r, float (&x)[8]) {
     if constexpr (DT == WOQ_BF16) {
         x[0] = bf_lo(r.v.x); x[1] = bf_hi(r.v.x); x[2] = bf_lo(r.v.y); x[3] = bf_hi(r.v.y);

@@ -75,39 +75,10 @@ constexpr int kDppXor8 = 0x128;        // row_ror:8 within 16-lane rows
 __device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
-// 8 consecutive elements (index e is a multiple of 8) of a BF16 / F32 matrix.
-template <int DT>
-__device__ __forceinline__ void load8(const void* base, int64_t e, float (&x)[8]) {
-    if constexpr (DT == WOQ_BF16) {
-        const uint4 v = *reinterpret_cast<const uint4*>(
-            reinterpret_cast<const uint16_t*>(base) + e);
-        x[0] = bf_lo(v.x); x[1] = bf_hi(v.x); x[2] = bf_lo(v.y); x[3] = bf_hi(v.y);
-        x[4] = bf_lo(v.z); x[5] = bf_hi(v.z); x[6] = bf_lo(v.w); x[7] = bf_hi(v.w);
-    } else {
-        const float4* p = reinterpret_cast<const float4*>(
-            reinterpret_cast<const float*>(base) + e);
-        const float4 a = p[0], b = p[1];
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-    }
-}
-
-__device__ __forceinline__ void load8f(const float* p, float (&x)[8]) {
-    const float4 a = reinterpret_cast<const float4*>(p)[0];
-    const float4 b = reinterpret_cast<const float4*>(p)[1];
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
-
 // Butterfly reductions over a full wave.  Every lane ends with the same
 // value (IEEE addition is commutative, so partners compute identical sums),
 // and the combination order is fixed, so results are deterministic.
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
-}
-__device__ __forceinline__ float wave_sumf(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
     return v;

@@ -128,19 +128,16 @@ __device__ __forceinline__ void load_ct(const float* ct, uint32_t col, float (&c
     c[4] = b.x; c[5] = b.y; c[6] = b.z; c[7] = b.w;
 }
 
-// x = (w * (1/s_i)) * (1/t_j), each product rounded once; absent scales skipped.
+// x = (w * (1/s_i)) * (1/t_j), each product rounded once.  An absent scale
+// is passed as 1.0f: multiplying by exactly 1 is the identity in IEEE
+// arithmetic, so the result equals skipping the product (and there is no
+// per-element select).
 template <int DT>
-__device__ __forceinline__ void balance(const Raw8<DT>& r, bool has_rs, float rsv, bool has_ct,
-                                        const float (&c)[8], float (&x)[8]) {
+__device__ __forceinline__ void balance(const Raw8<DT>& r, float rsv, const float (&c)[8],
+                                        float (&x)[8]) {
     unpack_raw<DT>(r, x);
-    if (has_rs) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = __fmul_rn(x[k], rsv);
-    }
-    if (has_ct) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = __fmul_rn(x[k], c[k]);
-    }
+    for (int k = 0; k < 8; ++k) x[k] = __fmul_rn(__fmul_rn(x[k], rsv), c[k]);
 }
 
 // min / max over aligned groups of `lanes` lanes (a power of two <= 64):
@@ -207,7 +204,7 @@ __global__ __launch_bounds__(kT) void k_quant_tile(const QMat* __restrict__ mats
         const uint32_t row = (uint32_t)(r0 + r);
         const float rsv = has_rs ? gload<float>(q.rs + row) : 1.0f;
         float x[8];
-        if (active) balance<DT>(raw[r], has_rs, rsv, has_ct, c, x);
+        if (active) balance<DT>(raw[r], rsv, c, x);
         else {
 #pragma unroll
             for (int k = 0; k < 8; ++k) x[k] = 0.f;
@@ -261,9 +258,9 @@ __global__ __launch_bounds__(kT) void k_quant_wave(const QMat* __restrict__ mats
     for (int k = 0; k < NVL; ++k) {
         const int v = lane + 64 * k;
         if (v < nvg) {
-            float c[8], x[8];
+            float c[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f}, x[8];
             if (has_ct) load_ct(q.ct, col0 + 8u * v, c);
-            balance<DT>(raw[k], has_rs, rsv, has_ct, c, x);
+            balance<DT>(raw[k], rsv, c, x);
 #pragma unroll
             for (int e = 0; e < 8; ++e) { lo = fminf(lo, x[e]); hi = fmaxf(hi, x[e]); }
         }
@@ -274,9 +271,9 @@ __global__ __launch_bounds__(kT) void k_quant_wave(const QMat* __restrict__ mats
     for (int k = 0; k < NVL; ++k) {
         const int v = lane + 64 * k;
         if (v < nvg) {
-            float c[8], x[8];
+            float c[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f}, x[8];
             if (has_ct) load_ct(q.ct, col0 + 8u * v, c);
-            balance<DT>(raw[k], has_rs, rsv, has_ct, c, x);
+            balance<DT>(raw[k], rsv, c, x);
             uint32_t cd[8];
             code8<BITS>(x, g, cd);
             store_codes<BITS>(q.codes, gbase + 8u * v, cd);
@@ -319,9 +316,9 @@ __global__ __launch_bounds__(kT) void k_quant_big(const QMat* __restrict__ mats,
     for (int k = 0; k < MAXV; ++k) {
         const int v = threadIdx.x + kT * k;
         if (v < nvg) {
-            float c[8], x[8];
+            float c[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f}, x[8];
             if (has_ct) load_ct(q.ct, col0 + 8u * v, c);
-            balance<DT>(raw[k], has_rs, rsv, has_ct, c, x);
+            balance<DT>(raw[k], rsv, c, x);
 #pragma unroll
             for (int e = 0; e < 8; ++e) { lo = fminf(lo, x[e]); hi = fmaxf(hi, x[e]); }
         }
@@ -336,9 +333,9 @@ __global__ __launch_bounds__(kT) void k_quant_big(const QMat* __restrict__ mats,
     for (int k = 0; k < MAXV; ++k) {
         const int v = threadIdx.x + kT * k;
         if (v < nvg) {
-            float c[8], x[8];
+            float c[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f}, x[8];
             if (has_ct) load_ct(q.ct, col0 + 8u * v, c);
-            balance<DT>(raw[k], has_rs, rsv, has_ct, c, x);
+            balance<DT>(raw[k], rsv, c, x);
             uint32_t cd[8];
             code8<BITS>(x, g, cd);
             store_codes<BITS>(q.codes, gbase + 8u * v, cd);
@@ -350,10 +347,11 @@ __global__ __launch_bounds__(kT) void k_quant_big(const QMat* __restrict__ mats,
     }
 }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// Two floats to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32,
+// packed low / high into 32 bits.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 // Dequantisation W' = (((q - z) delta) s_i) t_j, one fp32 rounding per
@@ -397,7 +395,7 @@ __global__ __launch_bounds__(kT) void k_dequant(const QMat* __restrict__ mats,
     const int r0 = rt * kTileRows;
     const int nr = min(kTileRows, q.rows - r0);
     const bool has_rs = q.rs != nullptr, has_ct = q.ct != nullptr;
-    float t8[8];
+    float t8[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
     if (has_ct) load_ct(q.ct, col, t8);
     uint32_t cw[kTileRows][8];
 #pragma unroll
@@ -414,21 +412,18 @@ __global__ __launch_bounds__(kT) void k_dequant(const QMat* __restrict__ mats,
         const float rsv = has_rs ? gload<float>(q.rs + row) : 1.0f;
         float y[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            y[k] = __fmul_rn((float)((int)cw[r][k] - z), delta);
-            if (has_rs) y[k] = __fmul_rn(y[k], rsv);
-            if (has_ct) y[k] = __fmul_rn(y[k], t8[k]);
-        }
+        for (int k = 0; k < 8; ++k)  // absent scales are exactly 1 (identity)
+            y[k] = __fmul_rn(__fmul_rn(__fmul_rn((float)((int)cw[r][k] - z), delta), rsv), t8[k]);
         if constexpr (ODT == WOQ_F32) {
             float* o = const_cast<float*>(reinterpret_cast<const float*>(q.data)) + e0;
             gstore_f4(o, y[0], y[1], y[2], y[3]);
             gstore_f4(o + 4, y[4], y[5], y[6], y[7]);
         } else {
             u32x4 w;
-            w.x = f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16);
-            w.y = f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16);
-            w.z = f32_to_bf16_rne(y[4]) | (f32_to_bf16_rne(y[5]) << 16);
-            w.w = f32_to_bf16_rne(y[6]) | (f32_to_bf16_rne(y[7]) << 16);
+            w.x = f32x2_to_bf16x2(y[0], y[1]);
+            w.y = f32x2_to_bf16x2(y[2], y[3]);
+            w.z = f32x2_to_bf16x2(y[4], y[5]);
+            w.w = f32x2_to_bf16x2(y[6], y[7]);
             gstore<u32x4>(const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(q.data)) + e0, w);
         }
     }

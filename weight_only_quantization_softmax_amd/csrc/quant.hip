@@ -195,16 +195,18 @@ __global__ __launch_bounds__(kT) void k_quant_tile(const QMat* __restrict__ mats
         for (int k = 0; k < 8; ++k) c[k] = 1.0f;
     }
     Raw8<DT> raw[kTileRows];
+    float rsv[kTileRows];  // every load is issued before the first use
 #pragma unroll
-    for (int r = 0; r < kTileRows; ++r)
+    for (int r = 0; r < kTileRows; ++r) {
         if (r < nr && active) raw[r] = load_raw<DT>(q.data, (uint32_t)(r0 + r) * (uint32_t)q.cols + col);
+        rsv[r] = has_rs && r < nr ? gload<float>(q.rs + r0 + r) : 1.0f;
+    }
 #pragma unroll
     for (int r = 0; r < kTileRows; ++r) {
         if (r >= nr) break;
         const uint32_t row = (uint32_t)(r0 + r);
-        const float rsv = has_rs ? gload<float>(q.rs + row) : 1.0f;
         float x[8];
-        if (active) balance<DT>(raw[r], rsv, c, x);
+        if (active) balance<DT>(raw[r], rsv[r], c, x);
         else {
 #pragma unroll
             for (int k = 0; k < 8; ++k) x[k] = 0.f;
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(kT) void k_quant_tile(const QMat* __restrict__ mats
             code8<BITS>(x, g, cd);
             store_codes<BITS>(q.codes, e0, cd);
             if ((threadIdx.x & (lanes - 1)) == 0) {
-                const uint32_t gi = e0 / (uint32_t)q.group;
+                const uint32_t gi = e0 >> __builtin_ctz((uint32_t)q.group);  // power-of-two group
                 gstore<float>(q.scales + gi, g.delta);
                 gstore<uint8_t>(q.zeros + gi, (uint8_t)g.z);
             }
@@ -397,23 +399,32 @@ __global__ __launch_bounds__(kT) void k_dequant(const QMat* __restrict__ mats,
     const bool has_rs = q.rs != nullptr, has_ct = q.ct != nullptr;
     float t8[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
     if (has_ct) load_ct(q.ct, col, t8);
+    // Every load of the tile (codes and the per-row group parameters) is
+    // issued before the first use.  The group divides the row and is a
+    // multiple of 8, so a thread's 8 columns share one group, whose index is
+    // row * (cols / group) + col / group.
+    const uint32_t gpr = (uint32_t)q.cols / (uint32_t)q.group, gcol = col / (uint32_t)q.group;
     uint32_t cw[kTileRows][8];
+    float delta[kTileRows], rsv[kTileRows];
+    int zr[kTileRows];
 #pragma unroll
-    for (int r = 0; r < kTileRows; ++r)
-        if (r < nr) load_codes_g<BITS>(q.codes, (uint32_t)(r0 + r) * (uint32_t)q.cols + col, cw[r]);
+    for (int r = 0; r < kTileRows; ++r) {
+        if (r < nr) {
+            const uint32_t row = (uint32_t)(r0 + r), gi = row * gpr + gcol;
+            load_codes_g<BITS>(q.codes, row * (uint32_t)q.cols + col, cw[r]);
+            delta[r] = gload<float>(q.scales + gi);
+            zr[r] = q.zeros ? (int)gload<uint8_t>(q.zeros + gi) : zdef;
+            rsv[r] = has_rs ? gload<float>(q.rs + row) : 1.0f;
+        }
+    }
 #pragma unroll
     for (int r = 0; r < kTileRows; ++r) {
         if (r >= nr) break;
-        const uint32_t row = (uint32_t)(r0 + r);
-        const uint32_t e0 = row * (uint32_t)q.cols + col;
-        const uint32_t gi = e0 / (uint32_t)q.group;
-        const float delta = gload<float>(q.scales + gi);
-        const int z = q.zeros ? (int)gload<uint8_t>(q.zeros + gi) : zdef;
-        const float rsv = has_rs ? gload<float>(q.rs + row) : 1.0f;
+        const uint32_t e0 = (uint32_t)(r0 + r) * (uint32_t)q.cols + col;
         float y[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k)  // absent scales are exactly 1 (identity)
-            y[k] = __fmul_rn(__fmul_rn(__fmul_rn((float)((int)cw[r][k] - z), delta), rsv), t8[k]);
+            y[k] = __fmul_rn(__fmul_rn(__fmul_rn((float)((int)cw[r][k] - zr[r]), delta[r]), rsv[r]), t8[k]);
         if constexpr (ODT == WOQ_F32) {
             float* o = const_cast<float*>(reinterpret_cast<const float*>(q.data)) + e0;
             gstore_f4(o, y[0], y[1], y[2], y[3]);

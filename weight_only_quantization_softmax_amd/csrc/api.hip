@@ -309,7 +309,7 @@ QLayout q_layout(const woq_mat* mats, int32_t n, int op, int32_t group,
     auto units = [&](const woq_mat& m) -> int64_t {
         if (op == 2) return m.rows;
         if (op == 0) return q_units(m, group);
-        return cdiv(m.rows, kQTileRows) * cdiv(m.cols, kQTileCols);
+        return cdiv(m.rows, kDTileRows) * cdiv(m.cols, kQTileCols);
     };
     for (int32_t i = 0; i < n; ++i) {
         if (op == 0 || mats[i].dtype == WOQ_BF16) { ++L.nb; L.units_b += units(mats[i]); }
@@ -641,7 +641,7 @@ int32_t dequant_unpack(const woq_mat* out, int32_t n_mats, const uint8_t* const*
         q.cols = (int32_t)m.cols;
         q.dtype = m.dtype;
         q.group = eff_group(m, group);
-        const int64_t u = cdiv(m.rows, kQTileRows) * cdiv(m.cols, kQTileCols);
+        const int64_t u = cdiv(m.rows, kDTileRows) * cdiv(m.cols, kQTileCols);
         if (m.dtype == WOQ_BF16) { tb[ib] = q; ub[ib + 1] = ub[ib] + u; ++ib; }
         else { tf[jf] = q; uf[jf + 1] = uf[jf] + u; ++jf; }
     }

@@ -67,6 +67,8 @@ hipError_t recip(const RecipSeg* segs, const int64_t* ubeg, int nseg,
 constexpr int kQTileRows = 8;
 constexpr int kQTileCols = 2048;
 constexpr int kQWaveMax = 4096;
+// dequant_unpack tiles: kDTileRows x kQTileCols (any group).
+constexpr int kDTileRows = 4;
 hipError_t quant_tile(const QMat* mats, const int64_t* ubeg, int nmat,
                       int64_t n_units, int dtype, int bits, hipStream_t s);
 hipError_t quant_wave(const QMat* mats, const int64_t* ubeg, int nmat,

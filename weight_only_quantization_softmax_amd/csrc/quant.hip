@@ -21,7 +21,8 @@
 //  k_quant_wave   groups of 513..4096 columns: one wave per group.
 //  k_quant_big    wider groups (e.g. one group per 14336-column row): one
 //                 workgroup per group, one LDS exchange.
-//  k_dequant      the tiles of k_quant_tile (8 rows x 2048 columns).
+//  k_dequant      tiles of kDTileRows rows x 2048 columns (measured on the
+//                 8B stack's int4 matrices: 4 rows beat 8 and 16).
 //  k_ternary      one workgroup per row.
 #include "launch.h"
 
@@ -394,8 +395,8 @@ __global__ __launch_bounds__(kT) void k_dequant(const QMat* __restrict__ mats,
     const int rt = tl / ctiles;
     const uint32_t col = (uint32_t)(tl - rt * ctiles) * kTileCols + 8u * threadIdx.x;
     if (col >= (uint32_t)q.cols) return;  // no cross-lane work below
-    const int r0 = rt * kTileRows;
-    const int nr = min(kTileRows, q.rows - r0);
+    const int r0 = rt * kDTileRows;
+    const int nr = min(kDTileRows, q.rows - r0);
     const bool has_rs = q.rs != nullptr, has_ct = q.ct != nullptr;
     float t8[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
     if (has_ct) load_ct(q.ct, col, t8);
@@ -404,11 +405,11 @@ __global__ __launch_bounds__(kT) void k_dequant(const QMat* __restrict__ mats,
     // multiple of 8, so a thread's 8 columns share one group, whose index is
     // row * (cols / group) + col / group.
     const uint32_t gpr = (uint32_t)q.cols / (uint32_t)q.group, gcol = col / (uint32_t)q.group;
-    uint32_t cw[kTileRows][8];
-    float delta[kTileRows], rsv[kTileRows];
-    int zr[kTileRows];
+    uint32_t cw[kDTileRows][8];
+    float delta[kDTileRows], rsv[kDTileRows];
+    int zr[kDTileRows];
 #pragma unroll
-    for (int r = 0; r < kTileRows; ++r) {
+    for (int r = 0; r < kDTileRows; ++r) {
         if (r < nr) {
             const uint32_t row = (uint32_t)(r0 + r), gi = row * gpr + gcol;
             load_codes_g<BITS>(q.codes, row * (uint32_t)q.cols + col, cw[r]);
@@ -418,7 +419,7 @@ __global__ __launch_bounds__(kT) void k_dequant(const QMat* __restrict__ mats,
         }
     }
 #pragma unroll
-    for (int r = 0; r < kTileRows; ++r) {
+    for (int r = 0; r < kDTileRows; ++r) {
         if (r >= nr) break;
         const uint32_t e0 = (uint32_t)(r0 + r) * (uint32_t)q.cols + col;
         float y[8];

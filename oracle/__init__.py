@@ -25,6 +25,9 @@ Sources (cited by page title and section; the pages are Vietnamese):
   Đến Thiết Bị Địa Phương" (unite.ai), sections "Hệ Thống Trọng Số Ternary"
   (the {-1, 0, +1} weight set) and "Lượng Tử Hóa Nhóm và Chuẩn Hóa" (groups
   are quantised independently).
+* [DF11] "DFloat11: Nén suy luận GPU không mất dữ liệu, giảm LLM xuống còn 70%
+  kích thước" (vi.news.hada.io): the lossless exponent code for the blocks
+  kept in bf16 (module ``oracle.df11``).
 
 Precision.  Everything is fp64 except where floating point decides an integer
 code: there the oracle takes the decision in fp32, with the same sequence of
@@ -50,3 +53,4 @@ __all__ = [
     "unpack_codes", "dequantize_f32", "near_tie_fraction",
     "ternary_quantize", "ternary_dequantize",
 ]
+from . import df11  # noqa: F401

@@ -15,6 +15,10 @@
  *           scaling) and "Chuan hoa Sinkhorn Knopp".
  *  [BitNet] "Khung Nguon BitNet.cpp Cua Microsoft ..." (unite.ai), sections
  *           "He Thong Trong So Ternary" and "Luong Tu Hoa Nhom va Chuan Hoa".
+ *  [DF11]   "DFloat11: Nen suy luan GPU khong mat du lieu, giam LLM xuong con
+ *           70% kich thuoc" (vi.news.hada.io), sections "Dinh dang DFloat11",
+ *           "Giai ma dua tren LUT phan cap" and "Kernel GPU hai giai doan va
+ *           metadata bo tro" (lossless code for the blocks kept in bf16).
  *
  * Conventions shared by every entry point
  *  - Matrices are row-major, contiguous, [rows, cols] = [out_features,
@@ -70,6 +74,9 @@ extern "C" {
 #define WOQ_OP_QUANT   3
 #define WOQ_OP_DEQUANT 4
 #define WOQ_OP_TERNARY 5
+#define WOQ_OP_DF11_HIST   6
+#define WOQ_OP_DF11_ENCODE 7
+#define WOQ_OP_DF11_DECODE 8
 
 /* One matrix.  For dequant_unpack it describes the OUTPUT (written). */
 typedef struct woq_mat {
@@ -217,6 +224,86 @@ int32_t ewq_budget_levels(const double* h_block, const int64_t* level_bytes,
                           int32_t n_blocks, int32_t n_levels, const int32_t* level0,
                           int64_t budget, int32_t* level_out, int64_t* total_out,
                           int32_t* fits_out);
+
+/*
+ * ---- Lossless exponent code for bf16 weights ([DF11]) ----
+ *
+ * A bf16 word is sign (1 bit), exponent (8) and mantissa (7).  The exponent
+ * of each weight is replaced by a prefix code built from the matrix's own
+ * exponent histogram; sign and mantissa are kept verbatim.  Format of one
+ * encoded matrix of n weights (every byte layout below is exact):
+ *  EncodedExponent   the codewords, in weight order, MSB-first (the first
+ *                    bit is bit 7 of byte 0); n_seg = ceil(total_bits / 64)
+ *                    segments of 8 bytes, buffer 8 n_seg + 8 bytes (zero
+ *                    padded).
+ *  PackedSignMantissa n bytes, byte i = sign_i << 7 | mantissa_i.
+ *  Gaps              per segment t, g_t = (first codeword start >= 64 t, or
+ *                    total_bits if none) - 64 t, 0 <= g_t <= 31, packed 5
+ *                    bits LSB-first (bits 5t..5t+4 of the array, bit k being
+ *                    bit k % 8 of byte k / 8); 4 ceil(5 n_seg / 32) + 4 bytes.
+ *  block_pos         n_blocks + 1 uint32, n_blocks = ceil(n_seg / 256):
+ *                    block_pos[b] = number of codewords starting before bit
+ *                    16384 b (the decoding block of 256 segments), last = n.
+ *  tables            n_tables (1..17) x 256 bytes: table 0 is indexed by the
+ *                    next 8 stream bits; an entry < 240 is the decoded
+ *                    exponent, an entry v >= 240 continues in table 256 - v
+ *                    with the following 8 bits.
+ *  CodeLengths       256 bytes, the codeword length of each exponent.
+ * Code: Huffman code lengths (merge the two nodes of least (count, order);
+ * leaves ordered by exponent, internal nodes after every leaf in creation
+ * order; a single used exponent gets length 1); when that exceeds 32 bits,
+ * the optimal code with lengths <= 32 (package-merge); canonical codewords
+ * by (length, exponent).  Exponents >= 240 (|w| >= 2^113, inf, NaN) cannot
+ * be coded (those table values are pointers).
+ */
+
+/* Sizes of the encoded buffers of a matrix of n weights whose codewords
+ * total total_bits (n <= total_bits <= 32 n).  Host-side.  WOQ_ERR_SHAPE on
+ * out-of-range arguments. */
+int32_t df11_buffer_sizes(int64_t n, int64_t total_bits, int64_t* n_seg,
+                          int64_t* enc_bytes, int64_t* gap_bytes, int64_t* n_blocks);
+
+/* Exponent histogram of each matrix: hist[i * 256 + e] = number of weights
+ * of matrix i with exponent field e (device uint32[n_mats * 256], 16-B
+ * aligned, written).  BF16 only (WOQ_ERR_DTYPE otherwise). */
+int32_t df11_exponent_histogram(const woq_mat* mats, int32_t n_mats, uint32_t* hist,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The code of one histogram.  Host-side: every pointer is HOST memory.
+ *  hist      [256] counts (>= 0)
+ *  code_len  [256] written (0 for unused exponents)
+ *  codeword  [256] written (right-aligned canonical codewords)
+ *  tables    [17 * 256] written; *n_tables of them are used
+ *  total_bits = sum hist[e] * code_len[e] (written)
+ * WOQ_ERR_VALUE when an exponent >= 240 occurs or the code would need more
+ * than 16 sub-tables; WOQ_ERR_SHAPE on negative or oversized counts. */
+int32_t df11_build_code(const int64_t* hist, uint8_t* code_len, uint32_t* codeword,
+                        uint8_t* tables, int32_t* n_tables, int64_t* total_bits);
+
+/* Encode each matrix with its own code (from df11_build_code on that
+ * matrix's histogram).  code_len / codeword: [n_mats] HOST arrays of HOST
+ * [256] arrays; total_bits [n_mats] host.  Outputs (device, sized by
+ * df11_buffer_sizes, written): enc (16-B aligned), sign_mant (n bytes, 16-B
+ * aligned), gaps (16-B aligned), block_pos (4-B aligned).  The codes are
+ * checked to be prefix codes without pointer exponents (WOQ_ERR_VALUE); a
+ * code or total that does not belong to the data gives unspecified output
+ * but every write stays inside the buffers' stated sizes. */
+int32_t df11_encode(const woq_mat* mats, int32_t n_mats, const uint8_t* const* code_len,
+                    const uint32_t* const* codeword, const int64_t* total_bits,
+                    uint8_t* const* enc, uint8_t* const* sign_mant, uint8_t* const* gaps,
+                    uint32_t* const* block_pos, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Decode a batch of matrices (for example all of one transformer block) back
+ * to their exact bf16 words.  out: BF16 matrices (written); enc, sign_mant
+ * (16-B aligned), gaps, block_pos (4-B), tables (4-B, n_tables[i] x 256) and
+ * code_len (4-B, 256 bytes) are DEVICE arrays per matrix; n_tables and
+ * total_bits are HOST arrays.  A corrupt stream gives unspecified weights
+ * but no access outside the stated buffers. */
+int32_t df11_decode(const woq_mat* out, int32_t n_mats, const uint8_t* const* enc,
+                    const uint8_t* const* sign_mant, const uint8_t* const* gaps,
+                    const uint32_t* const* block_pos, const uint8_t* const* tables,
+                    const int32_t* n_tables, const uint8_t* const* code_len,
+                    const int64_t* total_bits, void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -14,6 +14,10 @@ calls raise.
   ternary_pack          ternary {-1, 0, +1} codes with a per-row scale
   ewq_budget_levels     EWQ's budgeted placement: precision levels to a budget
                         (host-side)
+  df11_*                lossless exponent code for the blocks kept in bf16:
+                        df11_exponent_histogram, df11_build_code (host),
+                        df11_buffer_sizes (host), df11_encode, df11_decode;
+                        df11_compress chains the first three steps
 """
 from __future__ import annotations
 
@@ -26,7 +30,9 @@ from . import _lib
 from ._lib import WoqError  # noqa: F401
 
 __all__ = ["ewq_block_entropy", "sinq_balance", "quant_pack_groupwise",
-           "dequant_unpack", "ternary_pack", "ewq_budget_levels", "workspace_size", "WoqError"]
+           "dequant_unpack", "ternary_pack", "ewq_budget_levels", "workspace_size", "WoqError",
+           "df11_buffer_sizes", "df11_exponent_histogram", "df11_build_code", "df11_encode",
+           "df11_decode", "df11_compress"]
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -190,3 +196,114 @@ def ewq_budget_levels(h_block: Sequence[float], level_bytes, level0: Sequence[in
     _lib.check("ewq_budget_levels", lib.ewq_budget_levels(hb, lb, n, nl, l0, int(budget), out,
                                                           ctypes.byref(total), ctypes.byref(fits)))
     return list(out), total.value, bool(fits.value)
+
+
+# ------------------------------------------------------------------ DF11
+def df11_buffer_sizes(n: int, total_bits: int):
+    """(n_seg, enc_bytes, gap_bytes, n_blocks) of an encoded matrix (host-side)."""
+    lib = _lib.load()
+    out = [ctypes.c_int64(0) for _ in range(4)]
+    _lib.check("df11_buffer_sizes", lib.df11_buffer_sizes(int(n), int(total_bits),
+                                                          *[ctypes.byref(o) for o in out]))
+    return tuple(o.value for o in out)
+
+
+def df11_exponent_histogram(mats: Sequence[torch.Tensor], *, hist=None, ws=None, stream=None):
+    """Exponent counts per matrix: int32 tensor [n_mats, 256] on the device."""
+    lib = _lib.load()
+    dev = mats[0].device
+    arr = _mats(mats)
+    if hist is None:
+        hist = torch.empty(len(mats), 256, dtype=torch.int32, device=dev)
+    ws = _workspace(_lib.OP_DF11_HIST, mats, 0, ws, dev)
+    st = lib.df11_exponent_histogram(arr, len(mats), hist.data_ptr(), ws.data_ptr(), ws.numel(),
+                                     _stream(stream))
+    _lib.check("df11_exponent_histogram", st)
+    return hist
+
+
+def df11_build_code(hist):
+    """The code of one exponent histogram (host-side): dict with code_len
+    (uint8[256]), codeword (uint32[256]), tables (uint8[n_tables, 256]),
+    total_bits."""
+    import numpy as np
+    lib = _lib.load()
+    h = np.ascontiguousarray(np.asarray(hist, dtype=np.int64).reshape(256))
+    code_len = np.zeros(256, dtype=np.uint8)
+    codeword = np.zeros(256, dtype=np.uint32)
+    tables = np.zeros(17 * 256, dtype=np.uint8)
+    n_tables = ctypes.c_int32(0)
+    total = ctypes.c_int64(0)
+    st = lib.df11_build_code(h.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), code_len.ctypes.data,
+                             codeword.ctypes.data, tables.ctypes.data, ctypes.byref(n_tables),
+                             ctypes.byref(total))
+    _lib.check("df11_build_code", st)
+    return {"code_len": code_len, "codeword": codeword,
+            "tables": tables[:256 * n_tables.value].reshape(n_tables.value, 256),
+            "total_bits": total.value}
+
+
+def _host_ptrs(arrays):
+    arr = (ctypes.c_void_p * len(arrays))()
+    for i, a in enumerate(arrays):
+        arr[i] = a.ctypes.data
+    return ctypes.cast(arr, _lib.PP)
+
+
+def df11_encode(mats: Sequence[torch.Tensor], codes, *, ws=None, stream=None):
+    """Encode each bf16 matrix with its code (one df11_build_code dict per
+    matrix).  Returns one dict per matrix with the device buffers (enc, sm,
+    gaps, block_pos, tables, code_len) and n_tables, total_bits, shape."""
+    import numpy as np
+    lib = _lib.load()
+    dev = mats[0].device
+    arr = _mats(mats)
+    outs = []
+    for m, c in zip(mats, codes):
+        _, eb, gb, nb = df11_buffer_sizes(m.numel(), c["total_bits"])
+        outs.append({
+            "enc": torch.empty(eb, dtype=torch.uint8, device=dev),
+            "sm": torch.empty(m.numel(), dtype=torch.uint8, device=dev),
+            "gaps": torch.empty(gb, dtype=torch.uint8, device=dev),
+            "block_pos": torch.empty(nb + 1, dtype=torch.int32, device=dev),
+            "tables": torch.from_numpy(np.ascontiguousarray(c["tables"]).reshape(-1)).to(dev),
+            "code_len": torch.from_numpy(np.ascontiguousarray(c["code_len"])).to(dev),
+            "n_tables": int(c["tables"].shape[0]), "total_bits": int(c["total_bits"]),
+            "shape": tuple(m.shape)})
+    cl = [np.ascontiguousarray(c["code_len"], dtype=np.uint8) for c in codes]
+    cw = [np.ascontiguousarray(c["codeword"], dtype=np.uint32) for c in codes]
+    tb = (ctypes.c_int64 * len(mats))(*[c["total_bits"] for c in codes])
+    ws = _workspace(_lib.OP_DF11_ENCODE, mats, 0, ws, dev)
+    st = lib.df11_encode(arr, len(mats), _host_ptrs(cl), _host_ptrs(cw), tb,
+                         _ptrs([o["enc"] for o in outs]), _ptrs([o["sm"] for o in outs]),
+                         _ptrs([o["gaps"] for o in outs]), _ptrs([o["block_pos"] for o in outs]),
+                         ws.data_ptr(), ws.numel(), _stream(stream))
+    _lib.check("df11_encode", st)
+    return outs
+
+
+def df11_compress(mats: Sequence[torch.Tensor], *, stream=None):
+    """Histogram (device), codes (host; one synchronisation), encode (device)."""
+    hist = df11_exponent_histogram(mats, stream=stream).cpu().numpy()
+    codes = [df11_build_code(h) for h in hist]
+    return df11_encode(mats, codes, stream=stream)
+
+
+def df11_decode(encoded, *, out=None, ws=None, stream=None):
+    """Exact bf16 weights of a batch of encoded matrices (one launch)."""
+    lib = _lib.load()
+    dev = encoded[0]["enc"].device
+    if out is None:
+        out = [torch.empty(e["shape"], dtype=torch.bfloat16, device=dev) for e in encoded]
+    arr = _mats(out)
+    nt = (ctypes.c_int32 * len(out))(*[e["n_tables"] for e in encoded])
+    tb = (ctypes.c_int64 * len(out))(*[e["total_bits"] for e in encoded])
+    ws = _workspace(_lib.OP_DF11_DECODE, out, 0, ws, dev)
+    st = lib.df11_decode(arr, len(out), _ptrs([e["enc"] for e in encoded]),
+                         _ptrs([e["sm"] for e in encoded]), _ptrs([e["gaps"] for e in encoded]),
+                         _ptrs([e["block_pos"] for e in encoded]),
+                         _ptrs([e["tables"] for e in encoded]), nt,
+                         _ptrs([e["code_len"] for e in encoded]), tb,
+                         ws.data_ptr(), ws.numel(), _stream(stream))
+    _lib.check("df11_decode", st)
+    return out

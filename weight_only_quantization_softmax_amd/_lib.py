@@ -20,11 +20,13 @@ STATUS = {
 }
 WOQ_F32, WOQ_BF16 = 0, 1
 OP_ENTROPY, OP_SINQ, OP_QUANT, OP_DEQUANT, OP_TERNARY = 1, 2, 3, 4, 5
+OP_DF11_HIST, OP_DF11_ENCODE, OP_DF11_DECODE = 6, 7, 8
 
 # every symbol include/woq.h declares
 EXPORTS = ("woq_status_string", "woq_workspace_size", "ewq_block_entropy",
            "sinq_balance", "quant_pack_groupwise", "dequant_unpack", "ternary_pack",
-           "ewq_budget_levels")
+           "ewq_budget_levels", "df11_buffer_sizes", "df11_exponent_histogram",
+           "df11_build_code", "df11_encode", "df11_decode")
 
 
 class WoqMat(ctypes.Structure):
@@ -78,6 +80,19 @@ def load() -> ctypes.CDLL:
                                       ctypes.POINTER(I32), ctypes.POINTER(ctypes.c_int64),
                                       ctypes.POINTER(I32)]
     lib.ewq_budget_levels.restype = I32
+    I64P = ctypes.POINTER(ctypes.c_int64)
+    lib.df11_buffer_sizes.argtypes = [ctypes.c_int64, ctypes.c_int64, I64P, I64P, I64P, I64P]
+    lib.df11_buffer_sizes.restype = I32
+    lib.df11_exponent_histogram.argtypes = [ctypes.POINTER(WoqMat), I32, P, P, ctypes.c_size_t, P]
+    lib.df11_exponent_histogram.restype = I32
+    lib.df11_build_code.argtypes = [I64P, P, P, P, ctypes.POINTER(I32), I64P]
+    lib.df11_build_code.restype = I32
+    lib.df11_encode.argtypes = [ctypes.POINTER(WoqMat), I32, PP, PP, I64P, PP, PP, PP, PP,
+                                P, ctypes.c_size_t, P]
+    lib.df11_encode.restype = I32
+    lib.df11_decode.argtypes = [ctypes.POINTER(WoqMat), I32, PP, PP, PP, PP, PP,
+                                ctypes.POINTER(I32), PP, I64P, P, ctypes.c_size_t, P]
+    lib.df11_decode.restype = I32
     _lib = lib
     return lib
 

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libwoq.so")
-SOURCES = ["api.hip", "entropy.hip", "sinq.hip", "quant.hip"]
+SOURCES = ["api.hip", "entropy.hip", "sinq.hip", "quant.hip", "df11.hip"]
 ARCH = os.environ.get("WOQ_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -347,6 +347,61 @@ QLayout q_layout(const woq_mat* mats, int32_t n, int op, int32_t group,
     return L;
 }
 
+// ------------------------------------------------------------------ DF11
+struct DfSizes { int64_t n_seg, enc_bytes, gap_bytes, n_blocks; };
+DfSizes df_sizes(int64_t total_bits) {
+    DfSizes z;
+    z.n_seg = cdiv(total_bits, 64);
+    z.enc_bytes = 8 * z.n_seg + 8;
+    z.gap_bytes = 4 * cdiv(5 * z.n_seg, 32) + 4;
+    z.n_blocks = cdiv(z.n_seg, kDf11BlockSegs);
+    return z;
+}
+
+int32_t check_bf16(const woq_mat* mats, int32_t n) {
+    int32_t st = check_mats(mats, n, false);
+    if (st) return st;
+    for (int32_t i = 0; i < n; ++i)
+        if (mats[i].dtype != WOQ_BF16) return WOQ_ERR_DTYPE;
+    return WOQ_OK;
+}
+
+// op: 0 histogram, 1 encode, 2 decode.  Table region (copied in one go):
+// DfMat[n], DfCode[n] (encode), ubeg[n + 1], zbeg[n + 1] (encode); then the
+// encode scratch (chunk totals and bases).
+struct DfLayout {
+    size_t tab, codes, ubeg, zbeg, table_end, bits, base, total;
+    int64_t units = 0;
+};
+DfLayout df_layout(const woq_mat* mats, int32_t n, int op) {
+    DfLayout L;
+    Arena a;
+    L.tab = a.take(sizeof(DfMat) * n);
+    L.codes = op == 1 ? a.take(sizeof(DfCode) * n) : 0;
+    L.ubeg = a.take(sizeof(int64_t) * (n + 1));
+    L.zbeg = op == 1 ? a.take(sizeof(int64_t) * (n + 1)) : 0;
+    L.table_end = a.end();
+    for (int32_t i = 0; i < n; ++i) L.units += cdiv(elems(mats[i]), kDf11Chunk);
+    L.bits = op == 1 ? a.take(sizeof(uint32_t) * L.units) : 0;
+    L.base = op == 1 ? a.take(sizeof(int64_t) * L.units) : 0;
+    L.total = a.end();
+    return L;
+}
+
+// A codeword table must be a prefix code of lengths <= 32 with no code for
+// the pointer exponents (Kraft sum <= 1, codewords within their lengths).
+int32_t check_code(const uint8_t* len, const uint32_t* cw) {
+    uint64_t kraft = 0;
+    for (int s = 0; s < 256; ++s) {
+        if (len[s] > kDf11MaxLen) return WOQ_ERR_VALUE;
+        if (!len[s]) continue;
+        if (s >= kDf11PtrMin) return WOQ_ERR_VALUE;
+        if (len[s] < 32 && (cw[s] >> len[s])) return WOQ_ERR_VALUE;
+        kraft += uint64_t(1) << (32 - len[s]);
+    }
+    return kraft <= (uint64_t(1) << 32) ? WOQ_OK : WOQ_ERR_VALUE;
+}
+
 #define WOQ_HIP(call)                                  \
     do {                                               \
         if ((call) != hipSuccess) return WOQ_ERR_HIP;  \
@@ -377,7 +432,7 @@ const char* woq_status_string(int32_t s) {
 int32_t woq_workspace_size(int32_t op, const woq_mat* mats, int32_t n_mats, int32_t group,
                            size_t* bytes) {
     if (!bytes) return WOQ_ERR_NULL;
-    int32_t st = check_mats(mats, n_mats, op != WOQ_OP_ENTROPY);
+    int32_t st = check_mats(mats, n_mats, op != WOQ_OP_ENTROPY && op < WOQ_OP_DF11_HIST);
     if (st) return st;
     switch (op) {
         case WOQ_OP_ENTROPY: *bytes = ent_layout(mats, n_mats, kMaxBlocks).total; return WOQ_OK;
@@ -394,6 +449,9 @@ int32_t woq_workspace_size(int32_t op, const woq_mat* mats, int32_t n_mats, int3
             *bytes = q_layout(mats, n_mats, 1, group, nullptr, nullptr).total;
             return WOQ_OK;
         case WOQ_OP_TERNARY: *bytes = q_layout(mats, n_mats, 2, 0, nullptr, nullptr).total; return WOQ_OK;
+        case WOQ_OP_DF11_HIST: *bytes = df_layout(mats, n_mats, 0).total; return WOQ_OK;
+        case WOQ_OP_DF11_ENCODE: *bytes = df_layout(mats, n_mats, 1).total; return WOQ_OK;
+        case WOQ_OP_DF11_DECODE: *bytes = df_layout(mats, n_mats, 2).total; return WOQ_OK;
         default: return WOQ_ERR_SHAPE;
     }
 }
@@ -739,6 +797,156 @@ int32_t ewq_budget_levels(const double* h_block, const int64_t* level_bytes, int
     std::copy(lev.begin(), lev.end(), level_out);
     *total_out = total;
     *fits_out = total <= budget ? 1 : 0;
+    return WOQ_OK;
+}
+
+// ------------------------------------------------------------------ DF11
+int32_t df11_buffer_sizes(int64_t n, int64_t total_bits, int64_t* n_seg, int64_t* enc_bytes,
+                          int64_t* gap_bytes, int64_t* n_blocks) {
+    if (!n_seg || !enc_bytes || !gap_bytes || !n_blocks) return WOQ_ERR_NULL;
+    if (n < 1 || n > kMaxElems || total_bits < n || total_bits > kDf11MaxLen * n) return WOQ_ERR_SHAPE;
+    const DfSizes z = df_sizes(total_bits);
+    *n_seg = z.n_seg;
+    *enc_bytes = z.enc_bytes;
+    *gap_bytes = z.gap_bytes;
+    *n_blocks = z.n_blocks;
+    return WOQ_OK;
+}
+
+int32_t df11_build_code(const int64_t* hist, uint8_t* code_len, uint32_t* codeword,
+                        uint8_t* tables, int32_t* n_tables, int64_t* total_bits) {
+    if (!hist || !code_len || !codeword || !tables || !n_tables || !total_bits) return WOQ_ERR_NULL;
+    int64_t sum = 0;
+    for (int s = 0; s < 256; ++s) {
+        if (hist[s] < 0 || hist[s] > kMaxElems) return WOQ_ERR_SHAPE;
+        sum += hist[s];
+    }
+    if (sum > (int64_t(1) << 40)) return WOQ_ERR_SHAPE;
+    return df11_code_build(hist, code_len, codeword, tables, n_tables, total_bits);
+}
+
+int32_t df11_exponent_histogram(const woq_mat* mats, int32_t n_mats, uint32_t* hist, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+    int32_t st = check_bf16(mats, n_mats);
+    if (st) return st;
+    if (!hist) return WOQ_ERR_NULL;
+    if (!aligned(hist, 16)) return WOQ_ERR_ALIGN;
+    const DfLayout L = df_layout(mats, n_mats, 0);
+    if ((st = check_ws(ws, ws_bytes, L.total))) return st;
+    std::vector<char> host(L.table_end, 0);
+    DfMat* t = at<DfMat>(host.data(), L.tab);
+    int64_t* ub = at<int64_t>(host.data(), L.ubeg);
+    ub[0] = 0;
+    for (int32_t i = 0; i < n_mats; ++i) {
+        t[i].src = static_cast<const uint16_t*>(mats[i].data);
+        t[i].n = elems(mats[i]);
+        ub[i + 1] = ub[i] + cdiv(t[i].n, kDf11Chunk);
+    }
+    WOQ_HIP(hipMemcpyAsync(ws, host.data(), L.table_end, hipMemcpyHostToDevice, stream));
+    WOQ_HIP(fill_u32(hist, (size_t)n_mats * 256, 0u, stream));
+    WOQ_HIP(df11_hist(at<DfMat>(ws, L.tab), at<int64_t>(ws, L.ubeg), n_mats, ub[n_mats], hist, stream));
+    return WOQ_OK;
+}
+
+int32_t df11_encode(const woq_mat* mats, int32_t n_mats, const uint8_t* const* code_len,
+                    const uint32_t* const* codeword, const int64_t* total_bits,
+                    uint8_t* const* enc, uint8_t* const* sign_mant, uint8_t* const* gaps,
+                    uint32_t* const* block_pos, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int32_t st = check_bf16(mats, n_mats);
+    if (st) return st;
+    if (!code_len || !codeword || !total_bits) return WOQ_ERR_NULL;
+    for (int32_t i = 0; i < n_mats; ++i) {
+        if (!code_len[i] || !codeword[i]) return WOQ_ERR_NULL;
+        if ((st = check_code(code_len[i], codeword[i]))) return st;
+        const int64_t n = elems(mats[i]);
+        if (total_bits[i] < n || total_bits[i] > kDf11MaxLen * n) return WOQ_ERR_SHAPE;
+    }
+    if ((st = check_ptrs(reinterpret_cast<const void* const*>(enc), n_mats, 16))) return st;
+    if ((st = check_ptrs(reinterpret_cast<const void* const*>(sign_mant), n_mats, 16))) return st;
+    if ((st = check_ptrs(reinterpret_cast<const void* const*>(gaps), n_mats, 16))) return st;
+    if ((st = check_ptrs(reinterpret_cast<const void* const*>(block_pos), n_mats, 4))) return st;
+    const DfLayout L = df_layout(mats, n_mats, 1);
+    if ((st = check_ws(ws, ws_bytes, L.total))) return st;
+
+    std::vector<char> host(L.table_end, 0);
+    DfMat* t = at<DfMat>(host.data(), L.tab);
+    DfCode* c = at<DfCode>(host.data(), L.codes);
+    int64_t* ub = at<int64_t>(host.data(), L.ubeg);
+    int64_t* zb = at<int64_t>(host.data(), L.zbeg);
+    ub[0] = zb[0] = 0;
+    for (int32_t i = 0; i < n_mats; ++i) {
+        const DfSizes z = df_sizes(total_bits[i]);
+        DfMat& d = t[i];
+        d.src = static_cast<const uint16_t*>(mats[i].data);
+        d.enc = enc[i];
+        d.sm = sign_mant[i];
+        d.gaps = gaps[i];
+        d.bpos = block_pos[i];
+        d.n = elems(mats[i]);
+        d.total_bits = total_bits[i];
+        d.n_seg = z.n_seg;
+        d.n_blocks = z.n_blocks;
+        d.enc_bytes = z.enc_bytes;
+        d.gap_bytes = z.gap_bytes;
+        std::memcpy(c[i].code, codeword[i], sizeof(c[i].code));
+        std::memcpy(c[i].len, code_len[i], sizeof(c[i].len));
+        ub[i + 1] = ub[i] + cdiv(d.n, kDf11Chunk);
+        zb[i + 1] = zb[i] + cdiv((z.enc_bytes + z.gap_bytes) / 4, 4096);
+    }
+    WOQ_HIP(hipMemcpyAsync(ws, host.data(), L.table_end, hipMemcpyHostToDevice, stream));
+    WOQ_HIP(df11_encode_run(at<DfMat>(ws, L.tab), at<int64_t>(ws, L.ubeg), n_mats, ub[n_mats],
+                            at<int64_t>(ws, L.zbeg), zb[n_mats], at<DfCode>(ws, L.codes),
+                            at<uint32_t>(ws, L.bits), at<int64_t>(ws, L.base), stream));
+    return WOQ_OK;
+}
+
+int32_t df11_decode(const woq_mat* out, int32_t n_mats, const uint8_t* const* enc,
+                    const uint8_t* const* sign_mant, const uint8_t* const* gaps,
+                    const uint32_t* const* block_pos, const uint8_t* const* tables,
+                    const int32_t* n_tables, const uint8_t* const* code_len,
+                    const int64_t* total_bits, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int32_t st = check_bf16(out, n_mats);
+    if (st) return st;
+    if (!n_tables || !total_bits) return WOQ_ERR_NULL;
+    for (int32_t i = 0; i < n_mats; ++i) {
+        if (n_tables[i] < 1 || n_tables[i] > kDf11MaxSub + 1) return WOQ_ERR_SHAPE;
+        const int64_t n = elems(out[i]);
+        if (total_bits[i] < n || total_bits[i] > kDf11MaxLen * n) return WOQ_ERR_SHAPE;
+    }
+    if ((st = check_ptrs(reinterpret_cast<const void* const*>(enc), n_mats, 16))) return st;
+    if ((st = check_ptrs(reinterpret_cast<const void* const*>(sign_mant), n_mats, 16))) return st;
+    if ((st = check_ptrs(reinterpret_cast<const void* const*>(gaps), n_mats, 1))) return st;
+    if ((st = check_ptrs(reinterpret_cast<const void* const*>(block_pos), n_mats, 4))) return st;
+    if ((st = check_ptrs(reinterpret_cast<const void* const*>(tables), n_mats, 4))) return st;
+    if ((st = check_ptrs(reinterpret_cast<const void* const*>(code_len), n_mats, 4))) return st;
+    const DfLayout L = df_layout(out, n_mats, 2);
+    if ((st = check_ws(ws, ws_bytes, L.total))) return st;
+
+    std::vector<char> host(L.table_end, 0);
+    DfMat* t = at<DfMat>(host.data(), L.tab);
+    int64_t* ub = at<int64_t>(host.data(), L.ubeg);
+    ub[0] = 0;
+    for (int32_t i = 0; i < n_mats; ++i) {
+        const DfSizes z = df_sizes(total_bits[i]);
+        DfMat& d = t[i];
+        d.dst = static_cast<uint16_t*>(out[i].data);
+        d.enc = const_cast<uint8_t*>(enc[i]);
+        d.sm = const_cast<uint8_t*>(sign_mant[i]);
+        d.gaps = const_cast<uint8_t*>(gaps[i]);
+        d.bpos = const_cast<uint32_t*>(block_pos[i]);
+        d.tables = tables[i];
+        d.lens = code_len[i];
+        d.n = elems(out[i]);
+        d.total_bits = total_bits[i];
+        d.n_seg = z.n_seg;
+        d.n_blocks = z.n_blocks;
+        d.enc_bytes = z.enc_bytes;
+        d.gap_bytes = z.gap_bytes;
+        d.n_tables = n_tables[i];
+        ub[i + 1] = ub[i] + z.n_blocks;
+    }
+    WOQ_HIP(hipMemcpyAsync(ws, host.data(), L.table_end, hipMemcpyHostToDevice, stream));
+    WOQ_HIP(df11_decode_run(at<DfMat>(ws, L.tab), at<int64_t>(ws, L.ubeg), n_mats, ub[n_mats], stream));
     return WOQ_OK;
 }
 

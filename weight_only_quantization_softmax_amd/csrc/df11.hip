@@ -1,0 +1,601 @@
+// Lossless exponent coding of bf16 weights (DFloat11-style) for the blocks
+// that the tiers keep in bf16.
+//
+// [DF11] "DFloat11: Nen suy luan GPU khong mat du lieu, giam LLM xuong con
+// 70% kich thuoc" (vi.news.hada.io), sections "Du dia nen con lai trong
+// exponent cua BFloat16" (only the 8-bit exponent has low entropy),
+// "Dinh dang DFloat11" (Huffman-coded exponents in EncodedExponent, sign and
+// mantissa verbatim in PackedSignMantissa), "Giai ma dua tren LUT phan cap"
+// (height-8 subtrees as 256-entry tables, entries 240..255 as pointers,
+// CodeLengths), "Kernel GPU hai giai doan va metadata bo tro" (8 stream bytes
+// per thread, 5-bit Gaps, one output position per thread block) and "Giai
+// nen theo tung transformer block" (one batched call per block).
+//
+// Format (per matrix of n weights, one code per matrix):
+//  - code lengths: Huffman, merging the two nodes of least (weight, order)
+//    with leaves ordered by exponent and internal nodes after them; if that
+//    is deeper than 32 bits, the optimal 32-bit-limited code by
+//    package-merge.  Canonical codewords by (length, exponent).
+//  - EncodedExponent: the codes MSB-first (first bit = bit 7 of byte 0),
+//    8 n_seg + 8 bytes with n_seg = ceil(total_bits / 64), zero padded.
+//  - PackedSignMantissa: n bytes, sign << 7 | mantissa.
+//  - Gaps: per 64-bit segment t, (first code start >= 64 t, or total_bits)
+//    - 64 t, in [0, 31], packed 5 bits LSB-first; 4 ceil(5 n_seg / 32) + 4
+//    bytes.
+//  - block_pos: per decoding block of 256 segments, the number of codes that
+//    start before it; n_blocks + 1 entries, the last = n.
+//  - tables: root + up to 16 sub-tables of 256 bytes; an entry is an
+//    exponent (< 240) or 256 - k for sub-table k, numbered in the order that
+//    codes walked in canonical order first need them.
+//
+// Encoding (three kernels after the histogram): per chunk of 8192 weights
+// the total code length, a per-matrix scan of the chunk totals, then each
+// chunk assembles its bits in LDS and writes whole words, OR-ing only the
+// two words it may share with its neighbours.
+//
+// Decoding, one workgroup per 256 segments: a thread keeps its 16 stream
+// bytes (segment plus the overrun of its last code) in registers, walks the
+// codes that start in its segment through a fused root table (exponent and
+// length in one 16-bit LDS entry) and the byte sub-tables, and parks the
+// exponents in LDS; a workgroup scan of the counts gives each thread's
+// output offset, and the block's weights are written once, coalesced.  The
+// page decodes every segment twice (count, then write) to save on-chip
+// memory; with 160 KB of LDS per CU one decode and an LDS scatter suffice.
+#include "launch.h"
+
+#include <algorithm>
+#include <numeric>
+#include <queue>
+#include <tuple>
+#include <vector>
+
+namespace woq {
+
+// ====================================================================
+// Host: code construction
+// ====================================================================
+namespace {
+
+// Huffman depths by repeated merging of the two least (weight, order) nodes.
+void huffman_depths(const int64_t* hist, int32_t* len) {
+    struct Node { int64_t w; int order; };
+    auto greater = [](const Node& a, const Node& b) {
+        return std::tie(a.w, a.order) > std::tie(b.w, b.order);
+    };
+    std::priority_queue<Node, std::vector<Node>, decltype(greater)> pq(greater);
+    std::vector<int> parent(256 + 256, -1);
+    int used = 0;
+    for (int s = 0; s < 256; ++s) {
+        len[s] = 0;
+        if (hist[s] > 0) { pq.push(Node{hist[s], s}); ++used; }
+    }
+    if (used == 0) return;
+    if (used == 1) { len[pq.top().order] = 1; return; }
+    int next = 256;
+    while (pq.size() > 1) {
+        const Node a = pq.top(); pq.pop();
+        const Node b = pq.top(); pq.pop();
+        parent[a.order] = next;
+        parent[b.order] = next;
+        pq.push(Node{a.w + b.w, next});
+        ++next;
+    }
+    for (int s = 0; s < 256; ++s) {
+        if (hist[s] <= 0) continue;
+        int d = 0;
+        for (int v = s; parent[v] >= 0; v = parent[v]) ++d;
+        len[s] = d;
+    }
+}
+
+// Optimal lengths bounded by max_len (package-merge, Larmore and Hirschberg).
+// Leaves sorted by (weight, exponent); each level's list merges the leaves
+// with the previous level's packages (consecutive pairs), a leaf first on
+// equal weight; the first 2 (n - 1) items of the last list are selected and
+// a leaf's length is the number of selected items containing it.
+void package_merge(const int64_t* hist, int max_len, int32_t* len) {
+    std::vector<std::pair<int64_t, int>> leaves;
+    for (int s = 0; s < 256; ++s) {
+        len[s] = 0;
+        if (hist[s] > 0) leaves.push_back({hist[s], s});
+    }
+    std::sort(leaves.begin(), leaves.end());
+    const int n = (int)leaves.size();
+    if (n <= 1) {
+        if (n == 1) len[leaves[0].second] = 1;
+        return;
+    }
+    struct Item { int64_t w; std::vector<uint16_t> cnt; };
+    std::vector<Item> prev;
+    for (int level = 0; level < max_len; ++level) {
+        std::vector<Item> pk;
+        for (size_t i = 0; i + 1 < prev.size(); i += 2) {
+            Item it{prev[i].w + prev[i + 1].w, prev[i].cnt};
+            for (int k = 0; k < n; ++k) it.cnt[k] += prev[i + 1].cnt[k];
+            pk.push_back(std::move(it));
+        }
+        std::vector<Item> cur;
+        size_t i = 0, j = 0;
+        while (i < leaves.size() || j < pk.size()) {
+            if (j >= pk.size() || (i < leaves.size() && leaves[i].first <= pk[j].w)) {
+                Item it{leaves[i].first, std::vector<uint16_t>(n, 0)};
+                it.cnt[i] = 1;
+                cur.push_back(std::move(it));
+                ++i;
+            } else {
+                cur.push_back(std::move(pk[j]));
+                ++j;
+            }
+        }
+        prev = std::move(cur);
+    }
+    std::vector<int> total(n, 0);
+    for (int k = 0; k < 2 * (n - 1); ++k)
+        for (int q = 0; q < n; ++q) total[q] += prev[k].cnt[q];
+    for (int q = 0; q < n; ++q) len[leaves[q].second] = total[q];
+}
+
+}  // namespace
+
+int32_t df11_code_build(const int64_t* hist, uint8_t* code_len, uint32_t* codeword,
+                        uint8_t* tables, int32_t* n_tables, int64_t* total_bits) {
+    int32_t len[256];
+    huffman_depths(hist, len);
+    if (*std::max_element(len, len + 256) > kDf11MaxLen) package_merge(hist, kDf11MaxLen, len);
+    for (int s = kDf11PtrMin; s < 256; ++s)
+        if (len[s] > 0) return WOQ_ERR_VALUE;  // these exponents are table pointers
+    // canonical codewords in (length, exponent) order
+    std::vector<std::pair<int, int>> order;
+    for (int s = 0; s < 256; ++s)
+        if (len[s] > 0) order.push_back({len[s], s});
+    std::sort(order.begin(), order.end());
+    uint32_t cw[256] = {0};
+    uint64_t code = 0;
+    for (size_t k = 0; k < order.size(); ++k) {
+        if (k) code = (code + 1) << (order[k].first - order[k - 1].first);
+        cw[order[k].second] = (uint32_t)code;
+    }
+    // hierarchical tables
+    std::vector<uint8_t> tab(256, 0);
+    std::vector<bool> is_ptr(256, false);
+    int nt = 1;
+    for (const auto& o : order) {
+        const int L = o.first, s = o.second;
+        const uint32_t c = cw[s];
+        int t = 0, rem = L;
+        while (rem > 8) {
+            const int idx = (int)((c >> (rem - 8)) & 0xFFu);
+            if (!is_ptr[t * 256 + idx]) {
+                if (nt > kDf11MaxSub) return WOQ_ERR_VALUE;
+                tab.resize((size_t)(nt + 1) * 256, 0);
+                is_ptr.resize((size_t)(nt + 1) * 256, false);
+                tab[t * 256 + idx] = (uint8_t)(256 - nt);
+                is_ptr[t * 256 + idx] = true;
+                ++nt;
+            }
+            t = 256 - tab[t * 256 + idx];
+            rem -= 8;
+        }
+        const uint32_t low = c & ((1u << rem) - 1u);
+        for (uint32_t e = low << (8 - rem); e < ((low + 1) << (8 - rem)); ++e) tab[t * 256 + e] = (uint8_t)s;
+    }
+    int64_t tot = 0;
+    for (int s = 0; s < 256; ++s) {
+        code_len[s] = (uint8_t)len[s];
+        codeword[s] = cw[s];
+        tot += hist[s] * (int64_t)len[s];
+    }
+    std::copy(tab.begin(), tab.end(), tables);
+    *n_tables = nt;
+    *total_bits = tot;
+    return WOQ_OK;
+}
+
+// ====================================================================
+// Device
+// ====================================================================
+namespace {
+
+constexpr int kT = 256;
+constexpr int kChunk = kDf11Chunk;          // weights per encoding unit
+constexpr int kPerThread = kChunk / kT;     // 32 contiguous weights per thread
+
+__device__ __forceinline__ uint32_t exp_of(uint32_t b) { return (b >> 7) & 0xFFu; }
+
+// 32 contiguous bf16 words of one thread as 16 packed pairs; loads past n
+// are not issued and read as zero (callers mask by element index).
+__device__ __forceinline__ void load32(const uint16_t* src, int64_t e0, int64_t n, uint32_t (&w)[16]) {
+    if (e0 + kPerThread <= n) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint4 v = gload_u4(src + e0 + 8 * k);
+            w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int64_t e = e0 + 2 * k;
+            const uint32_t lo = e < n ? gload<uint16_t>(src + e) : 0u;
+            const uint32_t hi = e + 1 < n ? gload<uint16_t>(src + e + 1) : 0u;
+            w[k] = lo | (hi << 16);
+        }
+    }
+}
+__device__ __forceinline__ uint32_t half_of(const uint32_t (&w)[16], int j) {
+    return (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu);
+}
+
+// Exclusive workgroup scan (256 threads) of a 32-bit value; also returns the total.
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* sh, uint32_t& total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) sh[wid] = x;
+    __syncthreads();
+    uint32_t base = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kT / 64; ++w) {
+        const uint32_t t = sh[w];
+        if (w < wid) base += t;
+        total += t;
+    }
+    __syncthreads();
+    return base + x - v;
+}
+
+// ---- exponent histogram: per-wave LDS histograms, merged per workgroup
+__global__ __launch_bounds__(kT) void k_df11_hist(const DfMat* __restrict__ mats,
+                                                  const int64_t* __restrict__ ubeg, int nmat,
+                                                  uint32_t* __restrict__ hist) {
+    __shared__ uint32_t h[kT / 64][256];
+    const int m = find_unit_owner(ubeg, nmat, (int64_t)blockIdx.x);
+    const DfMat d = mats[m];
+    const int wid = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < (kT / 64) * 256; i += kT) (&h[0][0])[i] = 0u;
+    __syncthreads();
+    const int64_t e0 = (int64_t)(blockIdx.x - ubeg[m]) * kChunk + (int64_t)threadIdx.x * kPerThread;
+    uint32_t w[16];
+    load32(d.src, e0, d.n, w);
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j)
+        if (e0 + j < d.n) atomicAdd(&h[wid][exp_of(half_of(w, j))], 1u);
+    __syncthreads();
+    const uint32_t c = h[0][threadIdx.x] + h[1][threadIdx.x] + h[2][threadIdx.x] + h[3][threadIdx.x];
+    if (c) atomicAdd(hist + (size_t)m * 256 + threadIdx.x, c);
+}
+
+// ---- chunk totals of code length
+__global__ __launch_bounds__(kT) void k_df11_count(const DfMat* __restrict__ mats,
+                                                   const int64_t* __restrict__ ubeg, int nmat,
+                                                   const DfCode* __restrict__ codes,
+                                                   uint32_t* __restrict__ chunk_bits) {
+    __shared__ uint8_t L[256];
+    __shared__ uint32_t sh[kT / 64];
+    const int m = find_unit_owner(ubeg, nmat, (int64_t)blockIdx.x);
+    const DfMat d = mats[m];
+    L[threadIdx.x] = codes[m].len[threadIdx.x];
+    __syncthreads();
+    const int64_t e0 = (int64_t)(blockIdx.x - ubeg[m]) * kChunk + (int64_t)threadIdx.x * kPerThread;
+    uint32_t w[16];
+    load32(d.src, e0, d.n, w);
+    uint32_t s = 0;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j)
+        if (e0 + j < d.n) s += L[exp_of(half_of(w, j))];
+    uint32_t total;
+    block_scan(s, sh, total);
+    if (threadIdx.x == 0) chunk_bits[blockIdx.x] = total;
+}
+
+// ---- per-matrix exclusive scan of the chunk totals (one workgroup per matrix)
+__global__ __launch_bounds__(kT) void k_df11_scan(const int64_t* __restrict__ ubeg,
+                                                  const uint32_t* __restrict__ chunk_bits,
+                                                  int64_t* __restrict__ chunk_base) {
+    __shared__ uint32_t sh[kT / 64];
+    const int m = blockIdx.x;
+    const int64_t u0 = ubeg[m], u1 = ubeg[m + 1];
+    int64_t run = 0;
+    for (int64_t u = u0; u < u1; u += kT) {
+        const int64_t i = u + threadIdx.x;
+        const uint32_t v = i < u1 ? chunk_bits[i] : 0u;
+        uint32_t total;
+        const uint32_t ex = block_scan(v, sh, total);
+        if (i < u1) chunk_base[i] = run + ex;
+        run += total;
+    }
+}
+
+// ---- zero the stream and gap words (OR targets), batched over matrices
+__global__ __launch_bounds__(kT) void k_df11_zero(const DfMat* __restrict__ mats,
+                                                  const int64_t* __restrict__ zbeg, int nmat) {
+    const int m = find_unit_owner(zbeg, nmat, (int64_t)blockIdx.x);
+    const DfMat d = mats[m];
+    const int64_t enc_words = d.enc_bytes / 4, words = enc_words + d.gap_bytes / 4;
+    const int64_t i0 = (int64_t)(blockIdx.x - zbeg[m]) * (kT * 16) + threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int64_t i = i0 + (int64_t)kT * k;
+        if (i < enc_words) gstore<uint32_t>(reinterpret_cast<uint32_t*>(d.enc) + i, 0u);
+        else if (i < words) gstore<uint32_t>(reinterpret_cast<uint32_t*>(d.gaps) + (i - enc_words), 0u);
+    }
+}
+
+// OR a 5-bit gap into the LSB-first packed Gaps array (fields may straddle words).
+__device__ __forceinline__ void or_gap(const DfMat& d, int64_t seg, uint32_t gap) {
+    const int64_t bit = 5 * seg;
+    const int64_t wi = bit >> 5;
+    const uint32_t sb = (uint32_t)(bit & 31);
+    uint32_t* gw = reinterpret_cast<uint32_t*>(d.gaps) + wi;
+    if (wi < d.gap_bytes / 4) atomicOr(gw, gap << sb);
+    if (sb > 27 && wi + 1 < d.gap_bytes / 4) atomicOr(gw + 1, gap >> (32 - sb));
+}
+
+// ---- write: sign|mantissa bytes, stream bits, gaps, block positions
+__global__ __launch_bounds__(kT) void k_df11_write(const DfMat* __restrict__ mats,
+                                                   const int64_t* __restrict__ ubeg, int nmat,
+                                                   const DfCode* __restrict__ codes,
+                                                   const int64_t* __restrict__ chunk_base,
+                                                   const uint32_t* __restrict__ chunk_bits) {
+    __shared__ uint32_t cw[256];
+    __shared__ uint8_t L[256];
+    __shared__ uint32_t sh[kT / 64];
+    __shared__ uint32_t bitbuf[kChunk * kDf11MaxLen / 32 + 2];
+    const int m = find_unit_owner(ubeg, nmat, (int64_t)blockIdx.x);
+    const DfMat d = mats[m];
+    cw[threadIdx.x] = codes[m].code[threadIdx.x];
+    L[threadIdx.x] = codes[m].len[threadIdx.x];
+    const int64_t B0 = chunk_base[blockIdx.x];
+    const uint32_t nbits = chunk_bits[blockIdx.x];
+    const uint32_t head = (uint32_t)(B0 & 31);
+    const uint32_t nw = (head + nbits + 31) >> 5;
+    for (uint32_t i = threadIdx.x; i < nw; i += kT) bitbuf[i] = 0u;
+    __syncthreads();
+
+    const int64_t e0 = (int64_t)(blockIdx.x - ubeg[m]) * kChunk + (int64_t)threadIdx.x * kPerThread;
+    uint32_t w[16];
+    load32(d.src, e0, d.n, w);
+    uint32_t s = 0;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j)
+        if (e0 + j < d.n) s += L[exp_of(half_of(w, j))];
+    uint32_t dummy;
+    const uint32_t off = block_scan(s, sh, dummy);
+
+    // sign | mantissa bytes
+    if (e0 < d.n) {
+        uint32_t sm[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            uint32_t b = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t h = half_of(w, 4 * k + q);
+                b |= (((h >> 8) & 0x80u) | (h & 0x7Fu)) << (8 * q);
+            }
+            sm[k] = b;
+        }
+        if (e0 + kPerThread <= d.n) {
+            u32x4 a, c;
+            a.x = sm[0]; a.y = sm[1]; a.z = sm[2]; a.w = sm[3];
+            c.x = sm[4]; c.y = sm[5]; c.z = sm[6]; c.w = sm[7];
+            gstore<u32x4>(d.sm + e0, a);
+            gstore<u32x4>(d.sm + e0 + 16, c);
+        } else {
+            for (int j = 0; (int64_t)j + e0 < d.n; ++j)
+                gstore<uint8_t>(d.sm + e0 + j, (uint8_t)(sm[j >> 2] >> (8 * (j & 3))));
+        }
+    }
+
+    // previous weight's code length (for "first start in its segment / block")
+    uint32_t lprev = 0;
+    if (e0 > 0 && e0 < d.n) lprev = L[exp_of(gload<uint16_t>(d.src + e0 - 1))];
+
+    // bits into LDS: a 64-bit accumulator, MSB-aligned, flushed per word
+    uint32_t q = head + off;
+    uint32_t wi = q >> 5;
+    uint32_t fill = q & 31;
+    uint64_t acc = 0;
+    int64_t start = B0 + off;  // stream position of the current code
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+        const int64_t e = e0 + j;
+        if (e >= d.n) break;
+        const uint32_t ex = exp_of(half_of(w, j));
+        const uint32_t len = L[ex];
+        // gaps and block positions
+        if (e == 0 || (uint32_t)(start & 63) < lprev) {
+            const int64_t seg = start >> 6;
+            const uint32_t gap = (uint32_t)(start & 63);
+            if (seg < d.n_seg && gap) or_gap(d, seg, gap);
+            if ((e == 0 || (uint32_t)(start & 16383) < lprev) && (start >> 14) < d.n_blocks)
+                gstore<uint32_t>(d.bpos + (start >> 14), (uint32_t)e);
+        }
+        if (e == d.n - 1) {
+            // a last segment (and block) in which no code starts
+            if ((start >> 6) < d.n_seg - 1) {
+                const int64_t seg = d.n_seg - 1;
+                const int64_t gap = d.total_bits - 64 * seg;
+                if (gap > 0 && gap < 32) or_gap(d, seg, (uint32_t)gap);
+            }
+            for (int64_t b = std::max<int64_t>((start >> 14) + 1, 0); b <= d.n_blocks; ++b)
+                gstore<uint32_t>(d.bpos + b, (uint32_t)d.n);
+        }
+        if (len == 0) continue;  // no code for this exponent: not the matrix's own code
+        acc |= (uint64_t)cw[ex] << (64 - fill - len);
+        fill += len;
+        if (fill >= 32) {
+            atomicOr(&bitbuf[wi], (uint32_t)(acc >> 32));
+            ++wi;
+            acc <<= 32;
+            fill -= 32;
+        }
+        start += len;
+        lprev = len;
+    }
+    if (fill > 0 && e0 < d.n) atomicOr(&bitbuf[wi], (uint32_t)(acc >> 32));
+    __syncthreads();
+
+    // words out: the first and last may be shared with neighbouring chunks
+    uint32_t* gwords = reinterpret_cast<uint32_t*>(d.enc) + (B0 >> 5);
+    const bool shared_first = head != 0, shared_last = ((head + nbits) & 31) != 0;
+    const int64_t room = d.enc_bytes / 4 - (B0 >> 5);  // words left in the stream buffer
+    for (uint32_t i = threadIdx.x; i < nw && (int64_t)i < room; i += kT) {
+        const uint32_t v = __builtin_bswap32(bitbuf[i]);
+        if ((i == 0 && shared_first) || (i == nw - 1 && shared_last)) {
+            if (v) atomicOr(gwords + i, v);
+        } else {
+            gstore<uint32_t>(gwords + i, v);
+        }
+    }
+}
+
+// ---- decode
+constexpr int kMaxCodes = 64;   // codes that can start in one 64-bit segment
+
+__global__ __launch_bounds__(kT) void k_df11_decode(const DfMat* __restrict__ mats,
+                                                    const int64_t* __restrict__ ubeg, int nmat) {
+    __shared__ uint8_t tabs[(kDf11MaxSub + 1) * 256];
+    __shared__ uint16_t root[256];
+    __shared__ uint8_t L[256];
+    __shared__ uint32_t slots[kMaxCodes / 4][kT];
+    __shared__ uint8_t outb[kT * kMaxCodes];
+    __shared__ uint32_t sh[kT / 64];
+
+    const int m = find_unit_owner(ubeg, nmat, (int64_t)blockIdx.x);
+    const DfMat d = mats[m];
+    const int64_t lb = blockIdx.x - ubeg[m];
+    const int tid = threadIdx.x;
+    const int ntab = d.n_tables;
+
+    // tables into LDS (words), then the fused root: exponent | length << 8,
+    // length 0 marking a pointer entry
+    const uint32_t* gt = reinterpret_cast<const uint32_t*>(d.tables);
+    uint32_t* lt = reinterpret_cast<uint32_t*>(tabs);
+    for (int i = tid; i < ntab * 64; i += kT) lt[i] = gload<uint32_t>(gt + i);
+    if (tid < 64) reinterpret_cast<uint32_t*>(L)[tid] = gload<uint32_t>(reinterpret_cast<const uint32_t*>(d.lens) + tid);
+    __syncthreads();
+    {
+        const uint32_t v = tabs[tid];
+        root[tid] = (uint16_t)(v < kDf11PtrMin ? (v | ((uint32_t)L[v] << 8)) : v);
+    }
+
+    // this thread's segment: 16 stream bytes (segment + overrun) and its gap
+    const int64_t seg = lb * kT + tid;
+    uint64_t hi = 0, lo = 0;
+    uint32_t p = 0, lim = 0;
+    if (seg < d.n_seg) {
+        const uint8_t* p8 = d.enc + 8 * seg;
+        hi = __builtin_bswap64(gload<uint64_t>(p8));
+        lo = __builtin_bswap64(gload<uint64_t>(p8 + 8));
+        const int64_t gbit = 5 * seg;
+        const uint32_t g16 = (uint32_t)gload<uint8_t>(d.gaps + (gbit >> 3)) |
+                             ((uint32_t)gload<uint8_t>(d.gaps + (gbit >> 3) + 1) << 8);
+        p = (g16 >> (gbit & 7)) & 31u;
+        const int64_t rest = d.total_bits - 64 * seg;
+        lim = rest < 64 ? (uint32_t)rest : 64u;
+    }
+    __syncthreads();  // fused root table ready
+
+    uint32_t cnt = 0;
+    {
+        uint32_t packed = 0;
+        while (p < lim && cnt < kMaxCodes) {
+            const uint64_t w64 = p ? ((hi << p) | (lo >> (64 - p))) : hi;
+            const uint32_t win = (uint32_t)(w64 >> 32);
+            const uint32_t e = root[win >> 24];
+            uint32_t sym = e & 0xFFu, len = e >> 8;
+            if (len == 0) {
+                uint32_t t = 256u - sym;
+                int sh8 = 16;
+                for (;;) {
+                    if ((int)t >= ntab || sh8 < 0) { len = 0; break; }
+                    const uint32_t v = tabs[t * 256 + ((win >> sh8) & 0xFFu)];
+                    if (v < kDf11PtrMin) { sym = v; len = L[v]; break; }
+                    t = 256u - v;
+                    sh8 -= 8;
+                }
+                if (len == 0) break;  // not a code of this table set
+            }
+            packed |= sym << (8 * (cnt & 3));
+            if ((cnt & 3) == 3) { slots[cnt >> 2][tid] = packed; packed = 0; }
+            ++cnt;
+            p += len;
+        }
+        if (cnt & 3) slots[cnt >> 2][tid] = packed;
+    }
+
+    uint32_t total;
+    const uint32_t off = block_scan(cnt, sh, total);
+    for (uint32_t c = 0; c < cnt; ++c) outb[off + c] = (uint8_t)(slots[c >> 2][tid] >> (8 * (c & 3)));
+    __syncthreads();
+
+    // the block's weights, coalesced: [g0, g0 + count)
+    const int64_t g0 = gload<uint32_t>(d.bpos + lb);
+    int64_t g1 = gload<uint32_t>(d.bpos + lb + 1);
+    if (g1 > d.n) g1 = d.n;
+    if (g1 < g0) g1 = g0;
+    const int64_t count = std::min<int64_t>(g1 - g0, total);
+    if (count <= 0) return;
+    const int64_t v0 = g0 >> 3, v1 = (g0 + count + 7) >> 3;
+    for (int64_t v = v0 + tid; v < v1; v += kT) {
+        const int64_t i0 = 8 * v;
+        if (i0 >= g0 && i0 + 8 <= g0 + count) {
+            const f32x2 smv = gload<f32x2>(d.sm + i0);
+            const uint32_t s0 = __float_as_uint(smv.x), s1 = __float_as_uint(smv.y);
+            uint32_t o[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t sw = k < 2 ? s0 : s1;
+                const uint32_t a = (sw >> (16 * (k & 1))) & 0xFFu, b = (sw >> (16 * (k & 1) + 8)) & 0xFFu;
+                const uint32_t ea = outb[i0 - g0 + 2 * k], eb = outb[i0 - g0 + 2 * k + 1];
+                const uint32_t wa = ((a & 0x80u) << 8) | (ea << 7) | (a & 0x7Fu);
+                const uint32_t wb = ((b & 0x80u) << 8) | (eb << 7) | (b & 0x7Fu);
+                o[k] = wa | (wb << 16);
+            }
+            u32x4 st;
+            st.x = o[0]; st.y = o[1]; st.z = o[2]; st.w = o[3];
+            gstore<u32x4>(d.dst + i0, st);
+        } else {
+            for (int64_t i = std::max(i0, g0); i < std::min(i0 + 8, g0 + count); ++i) {
+                const uint32_t a = gload<uint8_t>(d.sm + i);
+                const uint32_t ea = outb[i - g0];
+                gstore<uint16_t>(d.dst + i, (uint16_t)(((a & 0x80u) << 8) | (ea << 7) | (a & 0x7Fu)));
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t df11_hist(const DfMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
+                     uint32_t* hist, hipStream_t s) {
+    if (n_units <= 0) return hipSuccess;
+    k_df11_hist<<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, hist);
+    return hipGetLastError();
+}
+
+hipError_t df11_encode_run(const DfMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
+                           const int64_t* zbeg, int64_t n_zunits, const DfCode* codes,
+                           uint32_t* chunk_bits, int64_t* chunk_base, hipStream_t s) {
+    if (n_units <= 0) return hipSuccess;
+    k_df11_zero<<<dim3((unsigned)n_zunits), dim3(kT), 0, s>>>(mats, zbeg, nmat);
+    k_df11_count<<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, codes, chunk_bits);
+    k_df11_scan<<<dim3((unsigned)nmat), dim3(kT), 0, s>>>(ubeg, chunk_bits, chunk_base);
+    k_df11_write<<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, codes, chunk_base,
+                                                               chunk_bits);
+    return hipGetLastError();
+}
+
+hipError_t df11_decode_run(const DfMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
+                           hipStream_t s) {
+    if (n_units <= 0) return hipSuccess;
+    k_df11_decode<<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat);
+    return hipGetLastError();
+}
+
+}  // namespace woq

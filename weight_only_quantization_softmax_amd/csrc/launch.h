@@ -80,4 +80,22 @@ hipError_t dequant(const QMat* mats, const int64_t* ubeg, int nmat,
 hipError_t ternary(const QMat* mats, const int64_t* ubeg, int nmat,
                    int64_t n_units, int dtype, hipStream_t s);
 
+// ---- lossless exponent code (DF11)
+// Host: code lengths, canonical codewords and hierarchical tables from an
+// exponent histogram (tables: up to (kDf11MaxSub + 1) * 256 bytes).
+int32_t df11_code_build(const int64_t* hist, uint8_t* code_len, uint32_t* codeword,
+                        uint8_t* tables, int32_t* n_tables, int64_t* total_bits);
+// Exponent histograms (hist[nmat * 256], zeroed by the caller); units of
+// kDf11Chunk weights.
+hipError_t df11_hist(const DfMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
+                     uint32_t* hist, hipStream_t s);
+// Encode: ubeg has nmat + 1 entries (units of kDf11Chunk weights); zbeg
+// covers the stream and gap words to clear (units of 4096 words).
+hipError_t df11_encode_run(const DfMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
+                           const int64_t* zbeg, int64_t n_zunits, const DfCode* codes,
+                           uint32_t* chunk_bits, int64_t* chunk_base, hipStream_t s);
+// Decode: one unit per decoding block.
+hipError_t df11_decode_run(const DfMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
+                           hipStream_t s);
+
 }  // namespace woq

@@ -136,4 +136,34 @@ struct QMat {
     int32_t group;      // group size for this matrix (cols for per-row groups)
 };
 
+// Lossless exponent code (DF11): one entry per matrix.
+constexpr int kDf11Chunk = 8192;   // weights per encoding work unit
+constexpr int kDf11MaxLen = 32;    // longest codeword (bits)
+constexpr int kDf11PtrMin = 240;   // table entries >= this are sub-table pointers
+constexpr int kDf11MaxSub = 16;    // sub-tables (pointer values 255 .. 240)
+constexpr int kDf11BlockSegs = 256;  // decoding threads (64-bit segments) per block
+struct DfMat {
+    const uint16_t* src;     // encode: bf16 weights
+    uint16_t* dst;           // decode: bf16 weights (written)
+    uint8_t* enc;            // EncodedExponent
+    uint8_t* sm;             // PackedSignMantissa
+    uint8_t* gaps;           // Gaps (5 bits per segment)
+    uint32_t* bpos;          // output position of each decoding block's first weight
+    const uint8_t* tables;   // decode: n_tables x 256 table bytes
+    const uint8_t* lens;     // decode: CodeLengths [256]
+    int64_t n;               // weights
+    int64_t total_bits;
+    int64_t n_seg;
+    int64_t n_blocks;
+    int64_t enc_bytes;
+    int64_t gap_bytes;
+    int32_t n_tables;
+    int32_t pad;
+};
+// Encode: the matrix's code (codewords right-aligned, lengths 0 = unused).
+struct DfCode {
+    uint32_t code[256];
+    uint8_t len[256];
+};
+
 }  // namespace woq

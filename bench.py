@@ -183,6 +183,48 @@ def dequant_rate(qp, mats, wl, stream, reps=5):
             "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def df11_rate(mats, specs, acts, stream, reps=3):
+    """Lossless code of the blocks the tiers keep in bf16: encode them (one
+    df11_compress per block, outside the timed region, wall clock including
+    the host-side code construction), then time decoding with one batched
+    df11_decode per transformer block (HIP events).  Bytes = encoded
+    exponents + sign/mantissa bytes + gaps + block positions read, 2 B per
+    weight written.  One block is checked bit for bit after decoding."""
+    import torch
+    import weight_only_quantization_softmax_amd as woq
+
+    keep = sorted(b for b, a in enumerate(acts) if a == "keep")
+    if not keep:
+        return None
+    per = [[m for m, sp in zip(mats, specs) if sp.block == b] for b in keep]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    enc = [woq.df11_compress(ms, stream=stream) for ms in per]
+    torch.cuda.synchronize()
+    t_enc = time.perf_counter() - t0
+    outs = [torch.empty_like(m) for m in per[0]]
+    woq.df11_decode(enc[0], out=outs, stream=stream)
+    torch.cuda.synchronize()
+    exact = all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(per[0], outs))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        for e in enc:
+            woq.df11_decode(e, out=outs, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    n = sum(m.numel() for ms_ in per for m in ms_)
+    stored = sum(x["enc"].numel() + x["sm"].numel() + x["gaps"].numel() + 4 * x["block_pos"].numel()
+                 for e in enc for x in e)
+    gbs = (stored + 2 * n) / (ms / 1e3) / 1e9
+    return {"call": "df11_decode", "blocks": len(keep), "weights": int(n), "exact": bool(exact),
+            "bits_per_weight": round(8 * stored / n, 3), "encode_s": round(t_enc, 4),
+            "decode_ms": round(ms, 4), "decode_ms_per_block": round(ms / len(keep), 4),
+            "bf16_GBps": round(2 * n / (ms / 1e3) / 1e9, 1), "GBps": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,6 +307,7 @@ def main() -> int:
     acts = qp.action_of_block(tiers)
     comp = compulsory_bytes(mats, specs, acts, wl.bits, wl.group)
     deq = dequant_rate(qp, mats, wl, stream)
+    df11 = df11_rate(mats, specs, acts, stream)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -281,6 +324,7 @@ def main() -> int:
                     "max": round(step_ms[-1], 3)},
         "roofline": roof,
         "dequant": deq,
+        "df11": df11,
         "calls": {k: {"ms_per_step": round(v["ms_per_step"], 3), "calls": v["calls"]}
                   for k, v in per_kind.items()},
     }

@@ -217,3 +217,20 @@ def test_budgeted_placement_moe_layers():
             produced += qp.action_bytes(out["action"], m)
         assert produced == ref_total <= budget
     assert woq.ewq_budget_levels(hb, lb, level0, 0)[2] is False
+
+
+def test_kept_blocks_lossless_code():
+    """The pass's kept blocks stored with the lossless exponent code: every
+    word decodes exactly and the kept storage is about 11 bits per weight."""
+    import weight_only_quantization_softmax_amd as woq
+    wl, specs, mats = woqdata.generate("stack8b", device=DEV, blocks=[0, 1, 2, 3])
+    qp, tiers = _pass(wl, specs, mats)
+    stored = qp.compress_kept()
+    torch.cuda.synchronize()
+    kept = [i for i, o in qp.outputs.items() if o["action"] == "keep"]
+    assert kept and all("df11" in qp.outputs[i] for i in kept)
+    outs = woq.df11_decode([qp.outputs[i]["df11"] for i in kept])
+    for i, o in zip(kept, outs):
+        assert torch.equal(o.view(torch.int16), mats[i].view(torch.int16))
+    n = sum(mats[i].numel() for i in kept)
+    assert 10.3 < 8 * stored / n < 11.3

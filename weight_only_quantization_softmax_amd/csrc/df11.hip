@@ -455,15 +455,41 @@ __global__ __launch_bounds__(kT) void k_df11_write(const DfMat* __restrict__ mat
 }
 
 // ---- decode
-constexpr int kMaxCodes = 64;   // codes that can start in one 64-bit segment
+constexpr int kMaxCodes = 64;                    // codes that can start in one 64-bit segment
+constexpr int kBlockMax = kT * kMaxCodes;        // weights one block can hold
+constexpr int kOutVecs = kBlockMax / 8 / kT + 1; // 8-weight output vectors per thread (bound)
+constexpr int kPre = 3;                           // of them loaded before decoding
+
+// One code at bit p (< 64) of the 128-bit window hi:lo: (exponent, length);
+// length 0 for a bit pattern that is no code of these tables.
+__device__ __forceinline__ uint32_t decode_one(uint64_t hi, uint64_t lo, uint32_t p,
+                                               const uint16_t* root, const uint8_t* tabs,
+                                               const uint8_t* L, int ntab, uint32_t& len) {
+    const uint64_t w64 = p ? ((hi << p) | (lo >> (64 - p))) : hi;
+    const uint32_t win = (uint32_t)(w64 >> 32);
+    const uint32_t e = root[win >> 24];
+    uint32_t sym = e & 0xFFu;
+    len = e >> 8;
+    if (len == 0) {
+        uint32_t t = 256u - sym;
+        for (int sh8 = 16; sh8 >= 0; sh8 -= 8) {
+            if ((int)t >= ntab) break;
+            const uint32_t v = tabs[t * 256 + ((win >> sh8) & 0xFFu)];
+            if (v < kDf11PtrMin) { sym = v; len = L[v]; break; }
+            t = 256u - v;
+        }
+    }
+    return sym;
+}
 
 __global__ __launch_bounds__(kT) void k_df11_decode(const DfMat* __restrict__ mats,
                                                     const int64_t* __restrict__ ubeg, int nmat) {
     __shared__ uint8_t tabs[(kDf11MaxSub + 1) * 256];
     __shared__ uint16_t root[256];
     __shared__ uint8_t L[256];
-    __shared__ uint32_t slots[kMaxCodes / 4][kT];
-    __shared__ uint8_t outb[kT * kMaxCodes];
+    // exponents of the block's weights; weight i sits at i - (g0 & ~7), so
+    // every 8-weight output vector is one aligned 8-byte LDS read
+    __shared__ __attribute__((aligned(16))) uint8_t outb[kBlockMax + 16];
     __shared__ uint32_t sh[kT / 64];
 
     const int m = find_unit_owner(ubeg, nmat, (int64_t)blockIdx.x);
@@ -472,19 +498,21 @@ __global__ __launch_bounds__(kT) void k_df11_decode(const DfMat* __restrict__ ma
     const int tid = threadIdx.x;
     const int ntab = d.n_tables;
 
-    // tables into LDS (words), then the fused root: exponent | length << 8,
-    // length 0 marking a pointer entry
-    const uint32_t* gt = reinterpret_cast<const uint32_t*>(d.tables);
-    uint32_t* lt = reinterpret_cast<uint32_t*>(tabs);
-    for (int i = tid; i < ntab * 64; i += kT) lt[i] = gload<uint32_t>(gt + i);
-    if (tid < 64) reinterpret_cast<uint32_t*>(L)[tid] = gload<uint32_t>(reinterpret_cast<const uint32_t*>(d.lens) + tid);
-    __syncthreads();
-    {
-        const uint32_t v = tabs[tid];
-        root[tid] = (uint16_t)(v < kDf11PtrMin ? (v | ((uint32_t)L[v] << 8)) : v);
+    // ---- every global load first: block range, this thread's sign|mantissa
+    //      vectors, its 16 stream bytes and gap, the tables
+    const int64_t g0 = gload<uint32_t>(d.bpos + lb);
+    int64_t g1 = gload<uint32_t>(d.bpos + lb + 1);
+    g1 = g1 > d.n ? d.n : g1;
+    g1 = g1 < g0 ? g0 : g1;
+    const int64_t base = g0 & ~int64_t(7);
+    const int64_t nvec = (g1 - base + 7) >> 3;
+    f32x2 smv[kPre];
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+        const int64_t v = tid + (int64_t)kT * k;
+        const int64_t i0 = base + 8 * v;
+        if (v < nvec && i0 >= g0 && i0 + 8 <= g1) smv[k] = gload<f32x2>(d.sm + i0);
     }
-
-    // this thread's segment: 16 stream bytes (segment + overrun) and its gap
     const int64_t seg = lb * kT + tid;
     uint64_t hi = 0, lo = 0;
     uint32_t p = 0, lim = 0;
@@ -499,71 +527,74 @@ __global__ __launch_bounds__(kT) void k_df11_decode(const DfMat* __restrict__ ma
         const int64_t rest = d.total_bits - 64 * seg;
         lim = rest < 64 ? (uint32_t)rest : 64u;
     }
-    __syncthreads();  // fused root table ready
-
-    uint32_t cnt = 0;
+    const uint32_t* gt = reinterpret_cast<const uint32_t*>(d.tables);
+    uint32_t* lt = reinterpret_cast<uint32_t*>(tabs);
+    for (int i = tid; i < ntab * 64; i += kT) lt[i] = gload<uint32_t>(gt + i);
+    if (tid < 64) reinterpret_cast<uint32_t*>(L)[tid] = gload<uint32_t>(reinterpret_cast<const uint32_t*>(d.lens) + tid);
+    __syncthreads();
+    // fused root: exponent | length << 8 (length 0 marks a pointer)
     {
-        uint32_t packed = 0;
-        while (p < lim && cnt < kMaxCodes) {
-            const uint64_t w64 = p ? ((hi << p) | (lo >> (64 - p))) : hi;
-            const uint32_t win = (uint32_t)(w64 >> 32);
-            const uint32_t e = root[win >> 24];
-            uint32_t sym = e & 0xFFu, len = e >> 8;
-            if (len == 0) {
-                uint32_t t = 256u - sym;
-                int sh8 = 16;
-                for (;;) {
-                    if ((int)t >= ntab || sh8 < 0) { len = 0; break; }
-                    const uint32_t v = tabs[t * 256 + ((win >> sh8) & 0xFFu)];
-                    if (v < kDf11PtrMin) { sym = v; len = L[v]; break; }
-                    t = 256u - v;
-                    sh8 -= 8;
-                }
-                if (len == 0) break;  // not a code of this table set
-            }
-            packed |= sym << (8 * (cnt & 3));
-            if ((cnt & 3) == 3) { slots[cnt >> 2][tid] = packed; packed = 0; }
-            ++cnt;
-            p += len;
-        }
-        if (cnt & 3) slots[cnt >> 2][tid] = packed;
+        const uint32_t v = tabs[tid];
+        root[tid] = (uint16_t)(v < kDf11PtrMin ? (v | ((uint32_t)L[v] << 8)) : v);
     }
-
-    uint32_t total;
-    const uint32_t off = block_scan(cnt, sh, total);
-    for (uint32_t c = 0; c < cnt; ++c) outb[off + c] = (uint8_t)(slots[c >> 2][tid] >> (8 * (c & 3)));
     __syncthreads();
 
-    // the block's weights, coalesced: [g0, g0 + count)
-    const int64_t g0 = gload<uint32_t>(d.bpos + lb);
-    int64_t g1 = gload<uint32_t>(d.bpos + lb + 1);
-    if (g1 > d.n) g1 = d.n;
-    if (g1 < g0) g1 = g0;
+    // ---- decode the codes that start in this segment, exponents in registers
+    uint32_t pk[kMaxCodes / 4];
+#pragma unroll
+    for (int k = 0; k < kMaxCodes / 4; ++k) pk[k] = 0;
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int c = 0; c < kMaxCodes; ++c) {
+        if (p >= lim) break;
+        uint32_t len;
+        const uint32_t sym = decode_one(hi, lo, p, root, tabs, L, ntab, len);
+        if (len == 0) break;  // not a code of this table set
+        pk[c >> 2] |= sym << (8 * (c & 3));
+        cnt = c + 1;
+        p += len;
+    }
+
+    // ---- output offsets, exponents into LDS in weight order
+    uint32_t total;
+    const uint32_t off = block_scan(cnt, sh, total) + (uint32_t)(g0 - base);
+#pragma unroll
+    for (int c = 0; c < kMaxCodes; ++c) {
+        if ((uint32_t)c >= cnt) break;
+        outb[off + c] = (uint8_t)(pk[c >> 2] >> (8 * (c & 3)));
+    }
+    __syncthreads();
+
+    // ---- the block's weights [g0, g0 + count), coalesced
     const int64_t count = std::min<int64_t>(g1 - g0, total);
     if (count <= 0) return;
-    const int64_t v0 = g0 >> 3, v1 = (g0 + count + 7) >> 3;
-    for (int64_t v = v0 + tid; v < v1; v += kT) {
-        const int64_t i0 = 8 * v;
-        if (i0 >= g0 && i0 + 8 <= g0 + count) {
-            const f32x2 smv = gload<f32x2>(d.sm + i0);
-            const uint32_t s0 = __float_as_uint(smv.x), s1 = __float_as_uint(smv.y);
+    const int64_t gend = g0 + count;
+#pragma unroll
+    for (int k = 0; k < kOutVecs; ++k) {
+        const int64_t v = tid + (int64_t)kT * k;
+        if (v >= nvec) break;
+        const int64_t i0 = base + 8 * v;
+        if (i0 >= gend) break;
+        if (i0 >= g0 && i0 + 8 <= gend) {
+            const uint2 ex = *reinterpret_cast<const uint2*>(outb + 8 * v);
+            const f32x2 sv = k < kPre ? smv[k < kPre ? k : 0] : gload<f32x2>(d.sm + i0);
+            const uint32_t s0 = __float_as_uint(sv.x), s1 = __float_as_uint(sv.y);
             uint32_t o[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t sw = k < 2 ? s0 : s1;
-                const uint32_t a = (sw >> (16 * (k & 1))) & 0xFFu, b = (sw >> (16 * (k & 1) + 8)) & 0xFFu;
-                const uint32_t ea = outb[i0 - g0 + 2 * k], eb = outb[i0 - g0 + 2 * k + 1];
-                const uint32_t wa = ((a & 0x80u) << 8) | (ea << 7) | (a & 0x7Fu);
-                const uint32_t wb = ((b & 0x80u) << 8) | (eb << 7) | (b & 0x7Fu);
-                o[k] = wa | (wb << 16);
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t sw = q < 2 ? s0 : s1, ew = q < 2 ? ex.x : ex.y;
+                const uint32_t a = (sw >> (16 * (q & 1))) & 0xFFu, b = (sw >> (16 * (q & 1) + 8)) & 0xFFu;
+                const uint32_t ea = (ew >> (16 * (q & 1))) & 0xFFu, eb = (ew >> (16 * (q & 1) + 8)) & 0xFFu;
+                o[q] = (((a & 0x80u) << 8) | (ea << 7) | (a & 0x7Fu)) |
+                       ((((b & 0x80u) << 8) | (eb << 7) | (b & 0x7Fu)) << 16);
             }
             u32x4 st;
             st.x = o[0]; st.y = o[1]; st.z = o[2]; st.w = o[3];
             gstore<u32x4>(d.dst + i0, st);
         } else {
-            for (int64_t i = std::max(i0, g0); i < std::min(i0 + 8, g0 + count); ++i) {
+            for (int64_t i = std::max(i0, g0); i < std::min(i0 + 8, gend); ++i) {
                 const uint32_t a = gload<uint8_t>(d.sm + i);
-                const uint32_t ea = outb[i - g0];
+                const uint32_t ea = outb[i - base];
                 gstore<uint16_t>(d.dst + i, (uint16_t)(((a & 0x80u) << 8) | (ea << 7) | (a & 0x7Fu)));
             }
         }

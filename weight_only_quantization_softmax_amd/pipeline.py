@@ -8,7 +8,9 @@ What each tier does is a parameter of the pass:
   "sinq"     SINQ Sinkhorn balancing, then group RTN at (bits, group)
   "int8row"  8-bit RTN with one group per row, no balancing
   "ternary"  ternary {-1, 0, +1} with a per-row scale
-  "keep"     left as is
+  "keep"     left as is (optionally stored with the lossless exponent code of
+             [DF11] "DFloat11: Nen suy luan GPU khong mat du lieu ..."
+             (vi.news.hada.io) by :meth:`QuantPass.compress_kept`)
 
 With a storage budget, the tiers' choices are then moved along the ladder
 ACTIONS (ascending storage: ternary < Sinkhorn + low-bit < int8 per row <
@@ -256,6 +258,26 @@ class QuantPass:
         self.last_actions = acts
         self._run_calls(self.plan_actions(acts), stream, h, timers)
         return tiers
+
+    def compress_kept(self, stream: Optional[torch.cuda.Stream] = None) -> int:
+        """Lossless exponent code for the matrices the last run kept in bf16:
+        one df11_compress per block (its code comes from the data, so this
+        step synchronises once per block).  Sets outputs[i]["df11"]; returns
+        the stored bytes of the kept matrices."""
+        from . import df11_compress
+        if self.last_actions is None:
+            raise RuntimeError("run() first")
+        stored = 0
+        for b, a in enumerate(self.last_actions):
+            if a != "keep":
+                continue
+            idx = [i for i, bb in enumerate(self.block_id) if bb == b]
+            enc = df11_compress([self.mats[i] for i in idx], stream=stream)
+            for i, e in zip(idx, enc):
+                self.outputs[i]["df11"] = e
+                stored += (e["enc"].numel() + e["sm"].numel() + e["gaps"].numel()
+                           + 4 * e["block_pos"].numel() + e["tables"].numel() + 256)
+        return stored
 
     @staticmethod
     def _run_calls(calls, stream, h, timers):

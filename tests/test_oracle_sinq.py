@@ -121,3 +121,32 @@ def test_line_std_constant_lines_exactly_zero():
     a = np.full((3, 1000), 0.1)
     assert np.all(oracle.line_std(a, 1) == 0)
     assert math.isclose(oracle.line_std(np.array([[1.0, 3.0]]), 1)[0], 1.0)
+
+
+def test_rms_variant_is_sinkhorn_knopp_on_squares():
+    """Uncentred variant: a_i = 1/s_i^2, b_j = 1/t_j^2 are the Sinkhorn-Knopp
+    factors of B = W o W with row sums = cols and column sums = rows, for any
+    W without zero lines (no structure needed, unlike the centred case)."""
+    rng = np.random.default_rng(12)
+    w = rng.normal(0.3, 1, size=(6, 9)) * rng.uniform(0.2, 3.0, size=(6, 1))
+    rows, cols = w.shape
+    for k in (1, 2, 5, 12):
+        s, t = oracle.sinkhorn_std(w, k, rms=True)
+        u, v = _brute.textbook_sinkhorn_knopp((w * w).tolist(), float(cols), float(rows), k)
+        assert (1 / s ** 2) == pytest.approx(u, rel=1e-12)
+        assert (1 / t ** 2) == pytest.approx(v, rel=1e-12)
+
+
+def test_rms_variant_brute_force_and_zero_lines():
+    # one iteration by plain Python sums, and a zero row / column -> scale 1
+    w = np.array([[1.0, -2.0, 0.5], [0.0, 0.0, 0.0], [3.0, 1.0, -1.0]])
+    s, t = oracle.sinkhorn_std(w, 1, rms=True)
+    rs = [math.sqrt(sum(x * x for x in row) / 3) or 1.0 for row in w.tolist()]
+    assert s == pytest.approx(rs, rel=1e-15)
+    cs = [math.sqrt(sum((w[i][j] / rs[i]) ** 2 for i in range(3)) / 3) or 1.0 for j in range(3)]
+    assert t == pytest.approx(cs, rel=1e-15)
+    assert s[1] == 1.0
+    # centred and uncentred agree on zero-mean lines, differ otherwise
+    z = np.array([[1.0, -1.0], [2.0, -2.0]])
+    assert np.allclose(oracle.sinkhorn_std(z, 1)[0], oracle.sinkhorn_std(z, 1, rms=True)[0])
+    assert not np.allclose(oracle.sinkhorn_std(w + 1, 3)[0], oracle.sinkhorn_std(w + 1, 3, rms=True)[0])

@@ -139,6 +139,15 @@ int32_t sinq_balance(const woq_mat* mats, int32_t n_mats, int32_t iters,
                      float* const* row_scale, float* const* col_scale,
                      void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* sinq_balance with options.  flags: 0 (as sinq_balance) or WOQ_SINQ_RMS:
+ *  the uncentred root mean square sqrt(mean x^2) in place of the centred std
+ *  in both steps (a zero line gets scale 1), for comparing the two readings
+ *  of the std in a quality report.  Other bits: WOQ_ERR_VALUE. */
+#define WOQ_SINQ_RMS 1
+int32_t sinq_balance_ex(const woq_mat* mats, int32_t n_mats, int32_t iters, int32_t flags,
+                        float* const* row_scale, float* const* col_scale,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
+
 /*
  * quant_pack_groupwise -- asymmetric round-to-nearest of the balanced matrix
  *  in groups of `group` consecutive columns of a row (groups are independent,

@@ -99,6 +99,10 @@ def test_entry_points_reject_before_any_hip_call():
     assert lib.sinq_balance(m, 1, 4, nullpp, pp, FAKE, 1 << 30, None) == 1
     assert lib.sinq_balance(_mat(cols=20), 1, 4, pp, pp, FAKE, 1 << 30, None) == 2
     assert lib.sinq_balance(m, 1, 4, pp, pp, FAKE, 8, None) == 6
+    # sinq_balance_ex: unknown flag bits, then the same checks as sinq_balance
+    assert lib.sinq_balance_ex(m, 1, 4, 2, pp, pp, FAKE, 1 << 30, None) == 11
+    assert lib.sinq_balance_ex(m, 1, -1, _lib.WOQ_SINQ_RMS, pp, pp, FAKE, 1 << 30, None) == 5
+    assert lib.sinq_balance_ex(m, 1, 4, _lib.WOQ_SINQ_RMS, nullpp, pp, FAKE, 1 << 30, None) == 1
     # quant: bits, group, NULL outputs
     assert lib.quant_pack_groupwise(m, 1, None, None, 5, 64, pp, pp, pp, FAKE, 1 << 30, None) == 4
     assert lib.quant_pack_groupwise(m, 1, None, None, 4, 24, pp, pp, pp, FAKE, 1 << 30, None) == 2

@@ -138,6 +138,26 @@ def test_sinq_degenerate_lines():
     assert t[2][77].item() == 1.0
 
 
+@pytest.mark.parametrize("iters", [1, 16])
+def test_sinq_rms_variant_matches_oracle(iters):
+    """sinq_balance_ex with the root mean square: both passes, both dtypes,
+    ragged rows, with a mean added so that centred and uncentred differ."""
+    mats = [(_rm(r, c, 40 + i, dt, frac=0.01, mult=20.0).float() + 0.01).to(dt)
+            for i, ((r, c), dt) in enumerate(SINQ_CASES)]
+    mats[1][7, :] = 0        # a zero row gets scale 1
+    s, t = woq.sinq_balance(mats, iters, rms=True)
+    for i, m in enumerate(mats):
+        s_ref, t_ref = oracle.sinkhorn_std(_np(m), iters, rms=True)
+        np.testing.assert_allclose(s[i].cpu().numpy(), s_ref, rtol=1e-4, err_msg=str(SINQ_CASES[i]))
+        np.testing.assert_allclose(t[i].cpu().numpy(), t_ref, rtol=1e-4, err_msg=str(SINQ_CASES[i]))
+        assert np.max(np.abs(s[i].cpu().numpy() / s_ref - 1)) < 2e-5
+        assert np.max(np.abs(t[i].cpu().numpy() / t_ref - 1)) < 2e-5
+    assert s[1][7].item() == 1.0
+    # the centred result differs (the stds differ by the mean)
+    s_c, _ = woq.sinq_balance(mats[:1], iters)
+    assert not torch.allclose(s_c[0], s[0], rtol=1e-3)
+
+
 def test_sinq_deterministic():
     mats = [_rm(512, 2048, 9)]
     a = woq.sinq_balance(mats, 16)

@@ -170,19 +170,20 @@ def test_quality_report_rows():
     from weight_only_quantization_softmax_amd import quality
     w = woqdata.random_matrix(256, 1024, 77, device=DEV)
     rows = quality.matrix_report(w)
-    assert len(rows) == len(quality.SCHEMES) * len(quality.ITERS) + 1
+    nk = sum(1 for k in quality.ITERS if k)
+    assert len(rows) == len(quality.SCHEMES) * (1 + nk * len(quality.STDS)) + 1
     assert all(np.isfinite(r["rel_fro"]) and np.isfinite(r["max_abs"]) for r in rows)
-    by = {(r["scheme"], r["iters"]): r for r in rows}
-    for k in quality.ITERS:
-        assert by[("int4 g64", k)]["rel_fro"] < by[("int3 g128", k)]["rel_fro"]
+    by = {(r["scheme"], r["iters"], r["std"]): r for r in rows}
     import weight_only_quantization_softmax_amd as woq
     for k in quality.ITERS:
-        s, t = woq.sinq_balance([w], k)
-        _, scales, _ = woq.quant_pack_groupwise([w], 4, 64, row_scale=s, col_scale=t)
-        bound = (s[0][:, None].double() * t[0][None, :].double()
-                 * scales[0].double().repeat_interleave(64, dim=1)).max().item() / 2
-        assert by[("int4 g64", k)]["max_abs"] <= bound * (1 + 1e-5)
-    assert 0 < by[("ternary", 0)]["rel_fro"] < 1
+        for std in (quality.STDS if k else ("none",)):
+            assert by[("int4 g64", k, std)]["rel_fro"] < by[("int3 g128", k, std)]["rel_fro"]
+            s, t = woq.sinq_balance([w], k, rms=(std == "rms"))
+            _, scales, _ = woq.quant_pack_groupwise([w], 4, 64, row_scale=s, col_scale=t)
+            bound = (s[0][:, None].double() * t[0][None, :].double()
+                     * scales[0].double().repeat_interleave(64, dim=1)).max().item() / 2
+            assert by[("int4 g64", k, std)]["max_abs"] <= bound * (1 + 1e-5)
+    assert 0 < by[("ternary", 0, "none")]["rel_fro"] < 1
 
 
 def test_budgeted_placement_moe_layers():

@@ -19,12 +19,13 @@ STATUS = {
     11: "WOQ_ERR_VALUE",
 }
 WOQ_F32, WOQ_BF16 = 0, 1
+WOQ_SINQ_RMS = 1
 OP_ENTROPY, OP_SINQ, OP_QUANT, OP_DEQUANT, OP_TERNARY = 1, 2, 3, 4, 5
 OP_DF11_HIST, OP_DF11_ENCODE, OP_DF11_DECODE = 6, 7, 8
 
 # every symbol include/woq.h declares
 EXPORTS = ("woq_status_string", "woq_workspace_size", "ewq_block_entropy",
-           "sinq_balance", "quant_pack_groupwise", "dequant_unpack", "ternary_pack",
+           "sinq_balance", "sinq_balance_ex", "quant_pack_groupwise", "dequant_unpack", "ternary_pack",
            "ewq_budget_levels", "df11_buffer_sizes", "df11_exponent_histogram",
            "df11_build_code", "df11_encode", "df11_decode")
 
@@ -67,6 +68,9 @@ def load() -> ctypes.CDLL:
     lib.ewq_block_entropy.restype = I32
     lib.sinq_balance.argtypes = [ctypes.POINTER(WoqMat), I32, I32, PP, PP, P, ctypes.c_size_t, P]
     lib.sinq_balance.restype = I32
+    lib.sinq_balance_ex.argtypes = [ctypes.POINTER(WoqMat), I32, I32, I32, PP, PP, P,
+                                    ctypes.c_size_t, P]
+    lib.sinq_balance_ex.restype = I32
     lib.quant_pack_groupwise.argtypes = [ctypes.POINTER(WoqMat), I32, PP, PP, I32, I32,
                                          PP, PP, PP, P, ctypes.c_size_t, P]
     lib.quant_pack_groupwise.restype = I32

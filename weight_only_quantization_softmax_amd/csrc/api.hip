@@ -522,9 +522,16 @@ int32_t ewq_block_entropy(const woq_mat* mats, int32_t n_mats, const int32_t* bl
 
 int32_t sinq_balance(const woq_mat* mats, int32_t n_mats, int32_t iters, float* const* row_scale,
                      float* const* col_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return sinq_balance_ex(mats, n_mats, iters, 0, row_scale, col_scale, ws, ws_bytes, stream);
+}
+
+int32_t sinq_balance_ex(const woq_mat* mats, int32_t n_mats, int32_t iters, int32_t flags,
+                        float* const* row_scale, float* const* col_scale, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
     int32_t st = check_mats(mats, n_mats, true);
     if (st) return st;
     if (iters < 0 || iters > kMaxIters) return WOQ_ERR_ITERS;
+    if (flags & ~WOQ_SINQ_RMS) return WOQ_ERR_VALUE;
     if ((st = check_ptrs(reinterpret_cast<const void* const*>(row_scale), n_mats, 4))) return st;
     if ((st = check_ptrs(reinterpret_cast<const void* const*>(col_scale), n_mats, 4))) return st;
     const SinqLayout L = sinq_layout(mats, n_mats);
@@ -555,6 +562,7 @@ int32_t sinq_balance(const woq_mat* mats, int32_t n_mats, int32_t iters, float* 
         sm.dtype = m.dtype;
         sm.n_strips = L.n_strips[k];
         sm.strip_rows = L.strip_rows[k];
+        sm.rms = (flags & WOQ_SINQ_RMS) ? 1 : 0;
         tab[k] = sm;
     }
     for (const SinqGroup& g : L.groups) {

@@ -7,7 +7,9 @@
 // standard deviations reach the target; not a doubly stochastic matrix).
 //
 // One iteration: s_i = std_j(W_ij / t_j), then t_j = std_i(W_ij / s_i),
-// centred population std, zero std -> 1; t starts at 1.  Kernels hold
+// centred population std, zero std -> 1; t starts at 1.  Variant: the root
+// mean square (uncentred) in place of the std, from the same moments
+// (M2 / n + mean^2 for rows, E[z^2] for columns).  Kernels hold
 // u = 1/t and v = 1/s (correctly rounded fp32) and form x = w * u (w * v).
 //
 // Fused pass (one read of W per iteration), in two forms:
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(kMaxT) void k_sinq_pass(const SinqMat* __restrict__
                 a = red[buf][w][lane];
                 merge_gen(M, Q, N, a.x, a.y, wave_count(w));
             }
-            const float var = Q / fn;
+            const float var = sm.rms ? fmaf(M, M, Q / fn) : Q / fn;
             const float s = var > 0.f ? __fsqrt_rn(var) : 1.0f;
             if (row < r1) {
                 vv = __fdiv_rn(1.0f, s);
@@ -577,7 +579,9 @@ __global__ __launch_bounds__(256, (WaveCfg<DT, NVL>::OCC)) void k_sinq_wave(
             } else {
                 wave_moments_eq(mm, qq, nl);
             }
-            const float var = first_lane(qq) / fn;
+            const float q1 = first_lane(qq) / fn;
+            const float m1 = first_lane(mm);
+            const float var = sm.rms ? fmaf(m1, m1, q1) : q1;
             const float s = var > 0.f ? __fsqrt_rn(var) : 1.0f;
             v[rr] = __fdiv_rn(1.0f, s);
             if (lane == 0 && row0 + rr < r1) gstore<float>(sm.s + row0 + rr, s);
@@ -763,8 +767,8 @@ __global__ __launch_bounds__(256) void k_sinq_reduce(const SinqMat* __restrict__
     if (j >= sm.cols) return;
     const double n = (double)sm.rows;
     const double mean = S / n;
-    const double var = Q / n - mean * mean;
-    const bool constant = (DT == WOQ_F32) && !(mx > mn);
+    const double var = sm.rms ? Q / n : Q / n - mean * mean;
+    const bool constant = (DT == WOQ_F32) && !sm.rms && !(mx > mn);
     const float t = (var > 0.0 && !constant) ? (float)sqrt(var) : 1.0f;
     gstore<float>(sm.t + j, t);
     gstore<float>(sm.u + j, __fdiv_rn(1.0f, t));

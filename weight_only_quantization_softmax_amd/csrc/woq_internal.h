@@ -120,7 +120,7 @@ struct SinqMat {
     int32_t dtype;
     int32_t n_strips;
     int32_t strip_rows;
-    int32_t pad;
+    int32_t rms;        // 1: root mean square in place of the centred std
 };
 
 // Quantise / dequantise / ternary: one entry per matrix.

@@ -4,10 +4,12 @@ SINQ's claim is that balancing rows and columns before rounding spreads the
 rounding error more evenly and lowers it ([SINQ] "Huawei gioi thieu SINQ"
 (asiadaily.org), sections "Dinh ty le tren hai truc" and "Chuan hoa
 Sinkhorn Knopp").  This measures it on the weights alone, with no data: each
-matrix is balanced for K iterations, quantised and packed, then decoded with
-dequant_unpack, all through the library; the report gives, per matrix,
-scheme and K, the relative Frobenius error ||W - W'|| / ||W|| and the largest
-absolute error, both computed in fp64 on the device.  K = 0 is plain
+matrix is balanced for K iterations (with the centred std, and with the
+uncentred root mean square for comparison), quantised and packed, then
+decoded with dequant_unpack, all through the library; the report gives, per
+matrix, scheme, K and std, the relative Frobenius error ||W - W'|| / ||W||
+and the largest absolute error, both computed in fp64 on the device.  K = 0
+is plain
 group-wise RTN (s = t = 1).  Ternary codes ([BitNet] "Khung Nguon
 BitNet.cpp" (unite.ai), "He Thong Trong So Ternary") use the per-row scale
 and no balancing.
@@ -27,6 +29,9 @@ from . import dequant_unpack, quant_pack_groupwise, sinq_balance, ternary_pack
 
 SCHEMES: Tuple[Tuple[int, int], ...] = ((4, 64), (3, 128))
 ITERS: Tuple[int, ...] = (0, 4, 16, 24)
+# the std used by the balancing: centred (the pass's reading) or the
+# uncentred root mean square
+STDS: Tuple[str, ...] = ("centred", "rms")
 
 
 def _errors(w: torch.Tensor, wq: torch.Tensor) -> Dict[str, float]:
@@ -37,22 +42,27 @@ def _errors(w: torch.Tensor, wq: torch.Tensor) -> Dict[str, float]:
 
 
 def matrix_report(w: torch.Tensor, schemes: Sequence[Tuple[int, int]] = SCHEMES,
-                  iters: Sequence[int] = ITERS, ternary: bool = True) -> List[dict]:
-    """Rows of the report for one device-resident matrix (bf16 or fp32)."""
+                  iters: Sequence[int] = ITERS, ternary: bool = True,
+                  stds: Sequence[str] = STDS) -> List[dict]:
+    """Rows of the report for one device-resident matrix (bf16 or fp32):
+    one per (scheme, K, std) with K > 0, one per scheme at K = 0 (plain RTN,
+    std "none"), and the ternary row."""
     rows = []
     shape = tuple(w.shape)
     for bits, group in schemes:
         for k in iters:
-            s, t = sinq_balance([w], k)
-            codes, scales, zeros = quant_pack_groupwise([w], bits, group, row_scale=s,
-                                                        col_scale=t)
-            wq = dequant_unpack([shape], codes, scales, bits, group, zeros=zeros, row_scale=s,
-                                col_scale=t, out_dtype=torch.float32)[0]
-            rows.append({"scheme": f"int{bits} g{group}", "iters": k, **_errors(w, wq)})
+            for std in (stds if k else ("none",)):
+                s, t = sinq_balance([w], k, rms=(std == "rms"))
+                codes, scales, zeros = quant_pack_groupwise([w], bits, group, row_scale=s,
+                                                            col_scale=t)
+                wq = dequant_unpack([shape], codes, scales, bits, group, zeros=zeros, row_scale=s,
+                                    col_scale=t, out_dtype=torch.float32)[0]
+                rows.append({"scheme": f"int{bits} g{group}", "iters": k, "std": std,
+                             **_errors(w, wq)})
     if ternary:
         codes, beta = ternary_pack([w])
         wq = dequant_unpack([shape], codes, [beta[0]], 2, 0, out_dtype=torch.float32)[0]
-        rows.append({"scheme": "ternary", "iters": 0, **_errors(w, wq)})
+        rows.append({"scheme": "ternary", "iters": 0, "std": "none", **_errors(w, wq)})
     return rows
 
 

@@ -36,9 +36,12 @@
 // Decoding, one workgroup per 256 segments: a thread keeps its 16 stream
 // bytes (segment plus the overrun of its last code) in registers, walks the
 // codes that start in its segment through a fused root table (exponent and
-// length in one 16-bit LDS entry) and the byte sub-tables, and parks the
-// exponents in LDS; a workgroup scan of the counts gives each thread's
-// output offset, and the block's weights are written once, coalesced.  The
+// length in one 16-bit LDS entry) and the byte sub-tables, in steps unrolled
+// at compile time so the exponents stay in registers; a workgroup scan of
+// the counts gives each thread's output offset, the exponents go to LDS in
+// weight order, and the block's weights are written once, coalesced, each
+// 8-weight vector assembled from its sign/mantissa and exponent bytes with
+// byte permutes.  The
 // page decodes every segment twice (count, then write) to save on-chip
 // memory; with 160 KB of LDS per CU one decode and an LDS scatter suffice.
 #include "launch.h"
@@ -460,29 +463,79 @@ constexpr int kBlockMax = kT * kMaxCodes;        // weights one block can hold
 constexpr int kOutVecs = kBlockMax / 8 / kT + 1; // 8-weight output vectors per thread (bound)
 constexpr int kPre = 3;                           // of them loaded before decoding
 
-// One code at bit p (< 64) of the 128-bit window hi:lo: (exponent, length);
-// length 0 for a bit pattern that is no code of these tables.
-__device__ __forceinline__ uint32_t decode_one(uint64_t hi, uint64_t lo, uint32_t p,
-                                               const uint16_t* root, const uint8_t* tabs,
-                                               const uint8_t* L, int ntab, uint32_t& len) {
-    const uint64_t w64 = p ? ((hi << p) | (lo >> (64 - p))) : hi;
-    const uint32_t win = (uint32_t)(w64 >> 32);
-    const uint32_t e = root[win >> 24];
-    uint32_t sym = e & 0xFFu;
-    len = e >> 8;
-    if (len == 0) {
-        uint32_t t = 256u - sym;
-        for (int sh8 = 16; sh8 >= 0; sh8 -= 8) {
-            if ((int)t >= ntab) break;
-            const uint32_t v = tabs[t * 256 + ((win >> sh8) & 0xFFu)];
-            if (v < kDf11PtrMin) { sym = v; len = L[v]; break; }
-            t = 256u - v;
-        }
+// Codes longer than 8 bits (rare): sub-tables on bits 8..15, 16..23, 24..31
+// of the window; length 0 for a pattern that is no code of these tables.
+__device__ __forceinline__ uint32_t decode_long(uint32_t win, uint32_t ptr, const uint8_t* tabs,
+                                                const uint8_t* L, int ntab, uint32_t& len) {
+    uint32_t t = 256u - ptr;
+    for (int sh8 = 16; sh8 >= 0; sh8 -= 8) {
+        if ((int)t >= ntab) break;
+        const uint32_t v = tabs[t * 256 + ((win >> sh8) & 0xFFu)];
+        if (v < kDf11PtrMin) { len = L[v]; return v; }
+        t = 256u - v;
     }
-    return sym;
+    len = 0;
+    return 0;
 }
 
-__global__ __launch_bounds__(kT) void k_df11_decode(const DfMat* __restrict__ mats,
+// Code C of a thread's segment (compile-time C: the packed exponents stay in
+// registers at static indices).  Every lane runs the step; a lane whose
+// position reached its bound (or that met a non-code pattern) commits
+// nothing and stops.  The 32-bit window at bit q of hi:lo is
+// (hi << q) | ((lo >> 1) >> (63 - q)), exact for every q in 0..63.
+template <int C>
+__device__ __forceinline__ void decode_step(uint32_t& p, uint32_t& lim, uint64_t hi, uint64_t lo,
+                                            const uint16_t* root, const uint8_t* tabs,
+                                            const uint8_t* L, int ntab,
+                                            uint32_t (&pk)[kMaxCodes / 4], uint32_t& cnt) {
+    const bool act = p < lim;
+    const uint32_t q = p & 63u;
+    const uint32_t win = (uint32_t)(((hi << q) | ((lo >> 1) >> (63u - q))) >> 32);
+    const uint32_t e = root[win >> 24];
+    uint32_t sym = e & 0xFFu, len = e >> 8;
+    if (len == 0 && act) sym = decode_long(win, sym, tabs, L, ntab, len);
+    const bool ok = act && len != 0;
+    pk[C >> 2] |= (ok ? sym : 0u) << (8 * (C & 3));
+    cnt = ok ? (uint32_t)(C + 1) : cnt;
+    p = ok ? p + len : p;
+    lim = ok ? lim : 0u;
+}
+
+template <int C>
+__device__ __forceinline__ void decode_steps(uint32_t& p, uint32_t& lim, uint64_t hi, uint64_t lo,
+                                             const uint16_t* root, const uint8_t* tabs,
+                                             const uint8_t* L, int ntab,
+                                             uint32_t (&pk)[kMaxCodes / 4], uint32_t& cnt) {
+    if constexpr (C < kMaxCodes) {
+        decode_step<C>(p, lim, hi, lo, root, tabs, L, ntab, pk, cnt);
+        if constexpr ((C & 3) == 3) {
+            if (__ballot(p < lim) == 0) return;  // the whole wave is done
+        }
+        decode_steps<C + 1>(p, lim, hi, lo, root, tabs, L, ntab, pk, cnt);
+    }
+}
+
+// 8 bf16 words from 8 sign|mantissa bytes (s0, s1) and 8 exponent bytes
+// (x0, x1): high byte = s & 0x80 | e >> 1, low byte = e << 7 & 0x80 | s & 0x7F,
+// four lanes of bytes at a time, interleaved by byte permutes.
+__device__ __forceinline__ u32x4 join8(uint32_t s0, uint32_t s1, uint32_t x0, uint32_t x1) {
+    const uint32_t hb0 = (s0 & 0x80808080u) | ((x0 >> 1) & 0x7F7F7F7Fu);
+    const uint32_t lb0 = ((x0 << 7) & 0x80808080u) | (s0 & 0x7F7F7F7Fu);
+    const uint32_t hb1 = (s1 & 0x80808080u) | ((x1 >> 1) & 0x7F7F7F7Fu);
+    const uint32_t lb1 = ((x1 << 7) & 0x80808080u) | (s1 & 0x7F7F7F7Fu);
+    u32x4 w;
+    // perm(a, b, sel): byte i of the result = byte sel_i of (a:b), b = bytes 0..3
+    w.x = __builtin_amdgcn_perm(hb0, lb0, 0x05010400u);
+    w.y = __builtin_amdgcn_perm(hb0, lb0, 0x07030602u);
+    w.z = __builtin_amdgcn_perm(hb1, lb1, 0x05010400u);
+    w.w = __builtin_amdgcn_perm(hb1, lb1, 0x07030602u);
+    return w;
+}
+
+// Seven waves per SIMD (the LDS limit at about 21 KB per workgroup): the
+// register cap of 72 costs a few spills of the prefetched vectors and still
+// measured faster than 5 waves without spills or 7 without the prefetch.
+__global__ __launch_bounds__(kT, 7) void k_df11_decode(const DfMat* __restrict__ mats,
                                                     const int64_t* __restrict__ ubeg, int nmat) {
     __shared__ uint8_t tabs[(kDf11MaxSub + 1) * 256];
     __shared__ uint16_t root[256];
@@ -544,16 +597,7 @@ __global__ __launch_bounds__(kT) void k_df11_decode(const DfMat* __restrict__ ma
 #pragma unroll
     for (int k = 0; k < kMaxCodes / 4; ++k) pk[k] = 0;
     uint32_t cnt = 0;
-#pragma unroll
-    for (int c = 0; c < kMaxCodes; ++c) {
-        if (p >= lim) break;
-        uint32_t len;
-        const uint32_t sym = decode_one(hi, lo, p, root, tabs, L, ntab, len);
-        if (len == 0) break;  // not a code of this table set
-        pk[c >> 2] |= sym << (8 * (c & 3));
-        cnt = c + 1;
-        p += len;
-    }
+    decode_steps<0>(p, lim, hi, lo, root, tabs, L, ntab, pk, cnt);
 
     // ---- output offsets, exponents into LDS in weight order
     uint32_t total;
@@ -578,19 +622,7 @@ __global__ __launch_bounds__(kT) void k_df11_decode(const DfMat* __restrict__ ma
         if (i0 >= g0 && i0 + 8 <= gend) {
             const uint2 ex = *reinterpret_cast<const uint2*>(outb + 8 * v);
             const f32x2 sv = k < kPre ? smv[k < kPre ? k : 0] : gload<f32x2>(d.sm + i0);
-            const uint32_t s0 = __float_as_uint(sv.x), s1 = __float_as_uint(sv.y);
-            uint32_t o[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t sw = q < 2 ? s0 : s1, ew = q < 2 ? ex.x : ex.y;
-                const uint32_t a = (sw >> (16 * (q & 1))) & 0xFFu, b = (sw >> (16 * (q & 1) + 8)) & 0xFFu;
-                const uint32_t ea = (ew >> (16 * (q & 1))) & 0xFFu, eb = (ew >> (16 * (q & 1) + 8)) & 0xFFu;
-                o[q] = (((a & 0x80u) << 8) | (ea << 7) | (a & 0x7Fu)) |
-                       ((((b & 0x80u) << 8) | (eb << 7) | (b & 0x7Fu)) << 16);
-            }
-            u32x4 st;
-            st.x = o[0]; st.y = o[1]; st.z = o[2]; st.w = o[3];
-            gstore<u32x4>(d.dst + i0, st);
+            gstore<u32x4>(d.dst + i0, join8(__float_as_uint(sv.x), __float_as_uint(sv.y), ex.x, ex.y));
         } else {
             for (int64_t i = std::max(i0, g0); i < std::min(i0 + 8, gend); ++i) {
                 const uint32_t a = gload<uint8_t>(d.sm + i);

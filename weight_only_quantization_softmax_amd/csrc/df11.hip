@@ -251,24 +251,31 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* sh, uint32_
     return base + x - v;
 }
 
-// ---- exponent histogram: per-wave LDS histograms, merged per workgroup
+// ---- exponent histogram.  Weights concentrate on a few exponents, so many
+//      lanes of a wave add to the same bin: 16 LDS copies, chosen by lane
+//      mod 16, with a row stride of 257 words (consecutive copies of a bin
+//      fall in different banks), leave at most 4 lanes on one address; the
+//      copies are summed per workgroup and added to the matrix's bins.
+constexpr int kHistCopies = 16;
 __global__ __launch_bounds__(kT) void k_df11_hist(const DfMat* __restrict__ mats,
                                                   const int64_t* __restrict__ ubeg, int nmat,
                                                   uint32_t* __restrict__ hist) {
-    __shared__ uint32_t h[kT / 64][256];
+    __shared__ uint32_t h[kHistCopies * 257];
     const int m = find_unit_owner(ubeg, nmat, (int64_t)blockIdx.x);
     const DfMat d = mats[m];
-    const int wid = threadIdx.x >> 6;
-    for (int i = threadIdx.x; i < (kT / 64) * 256; i += kT) (&h[0][0])[i] = 0u;
+    for (int i = threadIdx.x; i < kHistCopies * 257; i += kT) h[i] = 0u;
     __syncthreads();
     const int64_t e0 = (int64_t)(blockIdx.x - ubeg[m]) * kChunk + (int64_t)threadIdx.x * kPerThread;
     uint32_t w[16];
     load32(d.src, e0, d.n, w);
+    uint32_t* mine = h + (threadIdx.x & (kHistCopies - 1)) * 257;
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j)
-        if (e0 + j < d.n) atomicAdd(&h[wid][exp_of(half_of(w, j))], 1u);
+        if (e0 + j < d.n) atomicAdd(mine + exp_of(half_of(w, j)), 1u);
     __syncthreads();
-    const uint32_t c = h[0][threadIdx.x] + h[1][threadIdx.x] + h[2][threadIdx.x] + h[3][threadIdx.x];
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < kHistCopies; ++k) c += h[k * 257 + threadIdx.x];
     if (c) atomicAdd(hist + (size_t)m * 256 + threadIdx.x, c);
 }
 

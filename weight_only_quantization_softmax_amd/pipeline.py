@@ -261,22 +261,20 @@ class QuantPass:
 
     def compress_kept(self, stream: Optional[torch.cuda.Stream] = None) -> int:
         """Lossless exponent code for the matrices the last run kept in bf16:
-        one df11_compress per block (its code comes from the data, so this
-        step synchronises once per block).  Sets outputs[i]["df11"]; returns
-        the stored bytes of the kept matrices."""
+        one df11_compress over all of them (each matrix gets its own code,
+        which comes from the data, so this step synchronises once).  Sets
+        outputs[i]["df11"]; returns the stored bytes of the kept matrices."""
         from . import df11_compress
         if self.last_actions is None:
             raise RuntimeError("run() first")
+        idx = [i for i, b in enumerate(self.block_id) if self.last_actions[b] == "keep"]
+        if not idx:
+            return 0
         stored = 0
-        for b, a in enumerate(self.last_actions):
-            if a != "keep":
-                continue
-            idx = [i for i, bb in enumerate(self.block_id) if bb == b]
-            enc = df11_compress([self.mats[i] for i in idx], stream=stream)
-            for i, e in zip(idx, enc):
-                self.outputs[i]["df11"] = e
-                stored += (e["enc"].numel() + e["sm"].numel() + e["gaps"].numel()
-                           + 4 * e["block_pos"].numel() + e["tables"].numel() + 256)
+        for i, e in zip(idx, df11_compress([self.mats[i] for i in idx], stream=stream)):
+            self.outputs[i]["df11"] = e
+            stored += (e["enc"].numel() + e["sm"].numel() + e["gaps"].numel()
+                       + 4 * e["block_pos"].numel() + e["tables"].numel() + 256)
         return stored
 
     @staticmethod

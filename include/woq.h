@@ -132,8 +132,9 @@ int32_t ewq_block_entropy(const woq_mat* mats, int32_t n_mats,
  *  is W / (s t^T).
  *  row_scale [n_mats] host array of device float[rows]   (s, written)
  *  col_scale [n_mats] host array of device float[cols]   (t, written)
- *  Requires cols % 8 == 0.  fp32 element arithmetic with fp64 reductions in
- *  a fixed order (deterministic).
+ *  Requires cols % 8 == 0 and cols <= 32768 (WOQ_ERR_SHAPE otherwise: a
+ *  row is held by one workgroup).  fp32 element arithmetic with fp64
+ *  reductions in a fixed order (deterministic).
  */
 int32_t sinq_balance(const woq_mat* mats, int32_t n_mats, int32_t iters,
                      float* const* row_scale, float* const* col_scale,

@@ -98,6 +98,11 @@ def test_entry_points_reject_before_any_hip_call():
     assert lib.sinq_balance(m, 1, 5000, pp, pp, FAKE, 1 << 30, None) == 5
     assert lib.sinq_balance(m, 1, 4, nullpp, pp, FAKE, 1 << 30, None) == 1
     assert lib.sinq_balance(_mat(cols=20), 1, 4, pp, pp, FAKE, 1 << 30, None) == 2
+    # rows wider than one workgroup holds (512 threads x 8 vectors x 8 columns)
+    assert lib.sinq_balance(_mat(rows=2, cols=32776), 1, 4, pp, pp, FAKE, 1 << 30, None) == 2
+    assert lib.sinq_balance(_mat(rows=2, cols=65536, dtype=_lib.WOQ_F32), 1, 4, pp, pp, FAKE, 1 << 30, None) == 2
+    assert _ws_size(_lib.OP_SINQ, _mat(rows=2, cols=32776))[0] == 2
+    assert _ws_size(_lib.OP_SINQ, _mat(rows=2, cols=32768))[0] == 0
     assert lib.sinq_balance(m, 1, 4, pp, pp, FAKE, 8, None) == 6
     # sinq_balance_ex: unknown flag bits, then the same checks as sinq_balance
     assert lib.sinq_balance_ex(m, 1, 4, 2, pp, pp, FAKE, 1 << 30, None) == 11

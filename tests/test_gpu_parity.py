@@ -158,6 +158,22 @@ def test_sinq_rms_variant_matches_oracle(iters):
     assert not torch.allclose(s_c[0], s[0], rtol=1e-3)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_sinq_columns_with_large_means(dtype):
+    """Columns whose mean is ~100 standard deviations (a common offset; the
+    few-row case is in the limits tests): the reduction recomputes them
+    around their mean, so the scales stay within the bar instead of losing
+    eps * mean^2 / var."""
+    w = (_rm(256, 1024, 31, torch.float32) + 2.0).to(dtype)
+    w2 = (_rm(64, 14336, 33, torch.float32) - 1.5).to(dtype)     # workgroup pass
+    s, t = woq.sinq_balance([w, w2], 16)
+    for i, m in enumerate((w, w2)):
+        s_ref, t_ref = oracle.sinkhorn_std(_np(m), 16)
+        np.testing.assert_allclose(s[i].cpu().numpy(), s_ref, rtol=1e-4)
+        np.testing.assert_allclose(t[i].cpu().numpy(), t_ref, rtol=1e-4)
+        assert np.max(np.abs(t[i].cpu().numpy() / t_ref - 1)) < 2e-5
+
+
 def test_sinq_deterministic():
     mats = [_rm(512, 2048, 9)]
     a = woq.sinq_balance(mats, 16)

@@ -28,6 +28,9 @@ constexpr int32_t kMaxIters = 4096;
 // (MI355X's Infinity Cache serves re-reads barely faster than HBM, so there
 // is no point in cache-sized groups; one big launch amortises everything).
 constexpr int kSinqCUs = 256;          // MI355X compute units
+// Widest Sinkhorn row: a workgroup pass holds 512 threads x 8 vectors of 8
+// columns, with 1/t for the whole row in LDS.
+constexpr int64_t kSinqMaxCols = 32768;
 constexpr int kSinqWavesPerCU = 8;     // resident workgroup-pass waves per CU (2 per SIMD)
 
 size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
@@ -436,7 +439,11 @@ int32_t woq_workspace_size(int32_t op, const woq_mat* mats, int32_t n_mats, int3
     if (st) return st;
     switch (op) {
         case WOQ_OP_ENTROPY: *bytes = ent_layout(mats, n_mats, kMaxBlocks).total; return WOQ_OK;
-        case WOQ_OP_SINQ: *bytes = sinq_layout(mats, n_mats).total; return WOQ_OK;
+        case WOQ_OP_SINQ:
+            for (int32_t i = 0; i < n_mats; ++i)
+                if (mats[i].cols > kSinqMaxCols) return WOQ_ERR_SHAPE;
+            *bytes = sinq_layout(mats, n_mats).total;
+            return WOQ_OK;
         case WOQ_OP_QUANT: {
             if ((st = check_group(mats, n_mats, group, true))) return st;
             // worst case: every matrix has both scale vectors
@@ -530,6 +537,8 @@ int32_t sinq_balance_ex(const woq_mat* mats, int32_t n_mats, int32_t iters, int3
                         size_t ws_bytes, hipStream_t stream) {
     int32_t st = check_mats(mats, n_mats, true);
     if (st) return st;
+    for (int32_t i = 0; i < n_mats; ++i)
+        if (mats[i].cols > kSinqMaxCols) return WOQ_ERR_SHAPE;
     if (iters < 0 || iters > kMaxIters) return WOQ_ERR_ITERS;
     if (flags & ~WOQ_SINQ_RMS) return WOQ_ERR_VALUE;
     if ((st = check_ptrs(reinterpret_cast<const void* const*>(row_scale), n_mats, 4))) return st;

@@ -38,9 +38,11 @@
 // (n <= 64 per lane); a constant row at the first step gives y = 0 exactly
 // (std 0 -> scale 1).  Column variance is E[z^2] - E[z]^2 in fp64 from fp32
 // partials: relative accuracy ~1e-7 (1 + mean^2/var), ample for the
-// near-zero column means of weight matrices; bf16 columns that are constant
-// at the first step (or all zero) sum exactly, and fp32 inputs also track
-// per-column min/max (a constant column has std 0).
+// near-zero column means of weight matrices.  A column with mean^2 > 64 var
+// (few rows, or a large common offset) is recomputed by the reduction in one
+// pass around its mean.  bf16 columns that are constant at the first step
+// (or all zero) sum exactly, and fp32 inputs also track per-column min/max
+// (a constant column has std 0).
 //
 // Matrices of one launch share their shape class (wave or workgroup form,
 // vectors per lane / thread, threads per workgroup).
@@ -705,6 +707,10 @@ hipError_t launch_wave_f32(const SinqMat* mats, const int64_t* wbeg, int nmat, i
 // is fixed for a given launch plan, so results are deterministic.
 constexpr int kRedInflight = 16;
 
+// A column whose squared mean exceeds this multiple of its variance is
+// recomputed in the reduction (the fp32 partials would cost more than ~1e-5).
+constexpr double kIllCond = 64.0;
+
 template <int DT>
 __global__ __launch_bounds__(256) void k_sinq_reduce(const SinqMat* __restrict__ mats,
                                                      const int64_t* __restrict__ cbeg, int nmat,
@@ -767,7 +773,26 @@ __global__ __launch_bounds__(256) void k_sinq_reduce(const SinqMat* __restrict__
     if (j >= sm.cols) return;
     const double n = (double)sm.rows;
     const double mean = S / n;
-    const double var = sm.rms ? Q / n : Q / n - mean * mean;
+    double var = sm.rms ? Q / n : Q / n - mean * mean;
+    if (!sm.rms && mean * mean > kIllCond * var) {
+        // E[z^2] - E[z]^2 from fp32 partials loses about eps * mean^2 / var:
+        // recompute this column in one pass around the (accurate) mean, with
+        // the same z = w * (1/s_i) as the sweep (rows of the workgroup's
+        // columns are read contiguously).
+        double S2 = 0.0, Q2 = 0.0;
+        for (int i = 0; i < sm.rows; ++i) {
+            const float v = __fdiv_rn(1.0f, gload<float>(sm.s + i));
+            float x;
+            if constexpr (DT == WOQ_BF16)
+                x = __uint_as_float((uint32_t)gload<uint16_t>(reinterpret_cast<const uint16_t*>(sm.data) + (int64_t)i * sm.cols + j) << 16);
+            else
+                x = gload<float>(reinterpret_cast<const float*>(sm.data) + (int64_t)i * sm.cols + j);
+            const double dz = (double)(x * v) - mean;
+            S2 += dz;
+            Q2 += dz * dz;
+        }
+        var = Q2 / n - (S2 / n) * (S2 / n);
+    }
     const bool constant = (DT == WOQ_F32) && !sm.rms && !(mx > mn);
     const float t = (var > 0.0 && !constant) ? (float)sqrt(var) : 1.0f;
     gstore<float>(sm.t + j, t);

@@ -345,7 +345,13 @@ __device__ __forceinline__ void or_gap(const DfMat& d, int64_t seg, uint32_t gap
     if (sb > 27 && wi + 1 < d.gap_bytes / 4) atomicOr(gw + 1, gap >> (32 - sb));
 }
 
-// ---- write: sign|mantissa bytes, stream bits, gaps, block positions
+// ---- write: sign|mantissa bytes, stream bits, gaps, block positions.
+// Positions are chunk-local 32-bit bit offsets from the word that holds the
+// chunk's first bit (gbase = B0 rounded down to 32).  Every code is OR-ed
+// into a zeroed LDS bit buffer as two words (the second 0 unless the code
+// crosses a word), so the per-code work has no branch; the rare events (the
+// first code of a 64-bit segment or of a 16384-bit decoding block) are
+// collected in per-thread bit masks and written afterwards.
 __global__ __launch_bounds__(kT) void k_df11_write(const DfMat* __restrict__ mats,
                                                    const int64_t* __restrict__ ubeg, int nmat,
                                                    const DfCode* __restrict__ codes,
@@ -363,91 +369,100 @@ __global__ __launch_bounds__(kT) void k_df11_write(const DfMat* __restrict__ mat
     const uint32_t nbits = chunk_bits[blockIdx.x];
     const uint32_t head = (uint32_t)(B0 & 31);
     const uint32_t nw = (head + nbits + 31) >> 5;
-    for (uint32_t i = threadIdx.x; i < nw; i += kT) bitbuf[i] = 0u;
+    for (uint32_t i = threadIdx.x; i <= nw; i += kT) bitbuf[i] = 0u;  // + one spill word
     __syncthreads();
 
     const int64_t e0 = (int64_t)(blockIdx.x - ubeg[m]) * kChunk + (int64_t)threadIdx.x * kPerThread;
+    const int nv = (int)std::max<int64_t>(0, std::min<int64_t>(kPerThread, d.n - e0));  // valid weights
     uint32_t w[16];
     load32(d.src, e0, d.n, w);
+    // the previous weight decides "first code of a segment / block" for this
+    // thread's first code (loaded with the thread's own weights)
+    const uint32_t prev_bits = (e0 > 0 && nv > 0) ? (uint32_t)gload<uint16_t>(d.src + e0 - 1) : 0u;
+    uint32_t len[kPerThread], code[kPerThread];
     uint32_t s = 0;
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j)
-        if (e0 + j < d.n) s += L[exp_of(half_of(w, j))];
+    for (int j = 0; j < kPerThread; ++j) {
+        const uint32_t ex = exp_of(half_of(w, j));
+        len[j] = j < nv ? (uint32_t)L[ex] : 0u;
+        code[j] = len[j] ? cw[ex] : 0u;
+        s += len[j];
+    }
     uint32_t dummy;
     const uint32_t off = block_scan(s, sh, dummy);
 
-    // sign | mantissa bytes
-    if (e0 < d.n) {
+    // sign | mantissa bytes: high byte & 0x80 | low byte & 0x7F, four at a time
+    if (nv > 0) {
         uint32_t sm[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            uint32_t b = 0;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t h = half_of(w, 4 * k + q);
-                b |= (((h >> 8) & 0x80u) | (h & 0x7Fu)) << (8 * q);
-            }
-            sm[k] = b;
+            const uint32_t a = w[2 * k], b = w[2 * k + 1];
+            const uint32_t hi = __builtin_amdgcn_perm(b, a, 0x07050301u);  // bytes 1, 3 of a, b
+            const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x06040200u);  // bytes 0, 2 of a, b
+            sm[k] = (hi & 0x80808080u) | (lo & 0x7F7F7F7Fu);
         }
-        if (e0 + kPerThread <= d.n) {
+        if (nv == kPerThread) {
             u32x4 a, c;
             a.x = sm[0]; a.y = sm[1]; a.z = sm[2]; a.w = sm[3];
             c.x = sm[4]; c.y = sm[5]; c.z = sm[6]; c.w = sm[7];
             gstore<u32x4>(d.sm + e0, a);
             gstore<u32x4>(d.sm + e0 + 16, c);
         } else {
-            for (int j = 0; (int64_t)j + e0 < d.n; ++j)
-                gstore<uint8_t>(d.sm + e0 + j, (uint8_t)(sm[j >> 2] >> (8 * (j & 3))));
+#pragma unroll
+            for (int j = 0; j < kPerThread; ++j)
+                if (j < nv) gstore<uint8_t>(d.sm + e0 + j, (uint8_t)(sm[j >> 2] >> (8 * (j & 3))));
         }
     }
 
-    // previous weight's code length (for "first start in its segment / block")
-    uint32_t lprev = 0;
-    if (e0 > 0 && e0 < d.n) lprev = L[exp_of(gload<uint16_t>(d.src + e0 - 1))];
-
-    // bits into LDS: a 64-bit accumulator, MSB-aligned, flushed per word
-    uint32_t q = head + off;
-    uint32_t wi = q >> 5;
-    uint32_t fill = q & 31;
-    uint64_t acc = 0;
-    int64_t start = B0 + off;  // stream position of the current code
+    uint32_t lprev = (e0 > 0 && nv > 0) ? (uint32_t)L[exp_of(prev_bits)] : 0u;
+    const int64_t gbase = B0 - head;
+    const uint32_t g63 = (uint32_t)(gbase & 63), gblk = (uint32_t)(gbase & 16383);
+    uint32_t pos = head + off;  // bit offset of the thread's first code, from gbase
+    uint32_t seg_ev = 0, blk_ev = 0, lastlen = 0;
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
-        const int64_t e = e0 + j;
-        if (e >= d.n) break;
-        const uint32_t ex = exp_of(half_of(w, j));
-        const uint32_t len = L[ex];
-        // gaps and block positions
-        if (e == 0 || (uint32_t)(start & 63) < lprev) {
-            const int64_t seg = start >> 6;
-            const uint32_t gap = (uint32_t)(start & 63);
-            if (seg < d.n_seg && gap) or_gap(d, seg, gap);
-            if ((e == 0 || (uint32_t)(start & 16383) < lprev) && (start >> 14) < d.n_blocks)
-                gstore<uint32_t>(d.bpos + (start >> 14), (uint32_t)e);
-        }
-        if (e == d.n - 1) {
-            // a last segment (and block) in which no code starts
-            if ((start >> 6) < d.n_seg - 1) {
-                const int64_t seg = d.n_seg - 1;
-                const int64_t gap = d.total_bits - 64 * seg;
-                if (gap > 0 && gap < 32) or_gap(d, seg, (uint32_t)gap);
-            }
-            for (int64_t b = std::max<int64_t>((start >> 14) + 1, 0); b <= d.n_blocks; ++b)
-                gstore<uint32_t>(d.bpos + b, (uint32_t)d.n);
-        }
-        if (len == 0) continue;  // no code for this exponent: not the matrix's own code
-        acc |= (uint64_t)cw[ex] << (64 - fill - len);
-        fill += len;
-        if (fill >= 32) {
-            atomicOr(&bitbuf[wi], (uint32_t)(acc >> 32));
-            ++wi;
-            acc <<= 32;
-            fill -= 32;
-        }
-        start += len;
-        lprev = len;
+        lastlen = j == nv - 1 ? len[j] : lastlen;
+        const uint32_t wi = pos >> 5, o = pos & 31;
+        // the code's bits at o .. o + len - 1 of words wi, wi + 1 (MSB first)
+        const uint64_t v = len[j] ? (uint64_t)code[j] << (64 - o - len[j]) : 0u;
+        atomicOr(&bitbuf[wi], (uint32_t)(v >> 32));
+        atomicOr(&bitbuf[wi + 1], (uint32_t)v);
+        const bool fresh = len[j] && ((g63 + pos) & 63) < lprev;
+        const bool fblk = len[j] && ((gblk + pos) & 16383) < lprev;
+        seg_ev |= (fresh ? 1u : 0u) << j;
+        blk_ev |= (fblk ? 1u : 0u) << j;
+        lprev = len[j] ? len[j] : lprev;
+        pos += len[j];
     }
-    if (fill > 0 && e0 < d.n) atomicOr(&bitbuf[wi], (uint32_t)(acc >> 32));
+    if (e0 == 0 && nv > 0) { seg_ev |= 1u; blk_ev |= 1u; }  // the matrix's first code
+
+    // events: gaps (5 bits per segment) and block positions
+    if (seg_ev | blk_ev) {
+        uint32_t q = head + off;
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) {
+            const int64_t start = gbase + q;
+            if ((seg_ev >> j) & 1u) {
+                const int64_t seg = start >> 6;
+                const uint32_t gap = (uint32_t)(start & 63);
+                if (seg < d.n_seg && gap) or_gap(d, seg, gap);
+            }
+            if (((blk_ev >> j) & 1u) && (start >> 14) < d.n_blocks)
+                gstore<uint32_t>(d.bpos + (start >> 14), (uint32_t)(e0 + j));
+            q += len[j];
+        }
+    }
+    if (e0 <= d.n - 1 && d.n - 1 < e0 + kPerThread) {
+        // the matrix's last code: a last segment (and block) in which no code starts
+        const int64_t last_start = gbase + pos - lastlen;
+        if ((last_start >> 6) < d.n_seg - 1) {
+            const int64_t seg = d.n_seg - 1;
+            const int64_t gap = d.total_bits - 64 * seg;
+            if (gap > 0 && gap < 32) or_gap(d, seg, (uint32_t)gap);
+        }
+        for (int64_t b = std::max<int64_t>((last_start >> 14) + 1, 0); b <= d.n_blocks; ++b)
+            gstore<uint32_t>(d.bpos + b, (uint32_t)d.n);
+    }
     __syncthreads();
 
     // words out: the first and last may be shared with neighbouring chunks

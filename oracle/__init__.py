@@ -20,7 +20,9 @@ Sources (cited by page title and section; the pages are Vietnamese):
   hoạt động hiệu quả hơn" (asiadaily.org), sections "Định tỷ lệ trên hai trục"
   (dual-axis scaling) and "Chuẩn hóa Sinkhorn Knopp" (Sinkhorn-Knopp
   normalisation); the 4-bit / 3-bit integer targets in "Vì sao SINQ quan
-  trọng…" and "Những gì nhà phát triển có thể sử dụng ngay hôm nay".
+  trọng…" and "Những gì nhà phát triển có thể sử dụng ngay hôm nay"; the
+  non-uniform option in "Tiết kiệm bộ nhớ, tốc độ và chất lượng trong thử
+  nghiệm" (module ``oracle.codebook``).
 * [BitNet] "Khung Nguồn BitNet.cpp Của Microsoft Đưa Mô Hình Ngôn Ngữ Lớn 1-Bit
   Đến Thiết Bị Địa Phương" (unite.ai), sections "Hệ Thống Trọng Số Ternary"
   (the {-1, 0, +1} weight set) and "Lượng Tử Hóa Nhóm và Chuẩn Hóa" (groups
@@ -54,3 +56,4 @@ __all__ = [
     "ternary_quantize", "ternary_dequantize",
 ]
 from . import df11  # noqa: F401
+from . import codebook  # noqa: F401

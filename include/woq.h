@@ -12,7 +12,8 @@
  *           ..." (2kvn.com), section "EWQ hoat dong nhu the nao?", steps 1-3.
  *  [SINQ]   "Huawei gioi thieu SINQ: phuong phap luong tu hoa ma nguon mo ..."
  *           (asiadaily.org), sections "Dinh ty le tren hai truc" (dual-axis
- *           scaling) and "Chuan hoa Sinkhorn Knopp".
+ *           scaling), "Chuan hoa Sinkhorn Knopp" and "Tiet kiem bo nho, toc
+ *           do va chat luong trong thu nghiem" (non-uniform grids).
  *  [BitNet] "Khung Nguon BitNet.cpp Cua Microsoft ..." (unite.ai), sections
  *           "He Thong Trong So Ternary" and "Luong Tu Hoa Nhom va Chuan Hoa".
  *  [DF11]   "DFloat11: Nen suy luan GPU khong mat du lieu, giam LLM xuong con
@@ -55,7 +56,7 @@ extern "C" {
 #define WOQ_ERR_NULL      1  /* a required pointer is NULL                   */
 #define WOQ_ERR_SHAPE     2  /* rows/cols/group/size constraint violated     */
 #define WOQ_ERR_DTYPE     3  /* dtype not WOQ_F32 / WOQ_BF16                 */
-#define WOQ_ERR_BITS      4  /* bits not in {2, 3, 4, 8}                     */
+#define WOQ_ERR_BITS      4  /* bits not in {2, 3, 4, 8} ({2, 3, 4}: code book) */
 #define WOQ_ERR_ITERS     5  /* iters < 0 or > 4096                          */
 #define WOQ_ERR_WORKSPACE 6  /* ws NULL, misaligned or smaller than needed   */
 #define WOQ_ERR_BLOCK     7  /* block id out of range or empty block         */
@@ -205,6 +206,57 @@ int32_t dequant_unpack(const woq_mat* out, int32_t n_mats,
 int32_t ternary_pack(const woq_mat* mats, int32_t n_mats,
                      uint8_t* const* codes, float* const* row_scale,
                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * ---- Non-uniform (code-book) grid after balancing ----
+ * [SINQ], section "Tiet kiem bo nho, toc do va chat luong trong thu
+ * nghiem": the dual-axis scaling also serves non-uniform quantisation.  The
+ * page defines no grid; this one scales each group by its largest |x| and
+ * maps it to the nearest of 2^b levels given by the caller (for example the
+ * normal-quantile levels of woq_codebook_normal).
+ *
+ * quant_pack_codebook -- with x = (w * (1/s_i)) * (1/t_j) as in
+ *  quant_pack_groupwise: a = max |x| over the group, inv = 1/a (0 when not
+ *  finite), y = x * inv, code = #{k : y > m_k} with the fp32 midpoints m_k =
+ *  (l_k + l_{k+1}) * 0.5 (the nearest level, a tie to the lower one); every
+ *  operation one correctly rounded fp32 step.
+ *  levels  HOST float[2^bits], finite and strictly ascending (WOQ_ERR_VALUE
+ *          otherwise), read during the call.
+ *  codes   [n_mats] device uint8[rows * cols * bits / 8], packed as in
+ *          quant_pack_groupwise.
+ *  scales  [n_mats] device float[rows * cols / group]   (a, row-major)
+ *  bits in {2, 3, 4} (WOQ_ERR_BITS otherwise); group rules and workspace
+ *  (WOQ_OP_QUANT) as in quant_pack_groupwise.
+ */
+int32_t quant_pack_codebook(const woq_mat* mats, int32_t n_mats,
+                            const float* const* row_scale,
+                            const float* const* col_scale,
+                            int32_t bits, int32_t group, const float* levels,
+                            uint8_t* const* codes, float* const* scales,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * dequant_codebook -- inverse map of quant_pack_codebook: W'_ij =
+ *  ((a * l_q) * s_i) * t_j in fp32 (one rounding per product), written as
+ *  F32 or BF16 (round to nearest even) into out[m].  Arguments as in
+ *  dequant_unpack (workspace WOQ_OP_DEQUANT) with `levels` as in
+ *  quant_pack_codebook and no zero-points.
+ */
+int32_t dequant_codebook(const woq_mat* out, int32_t n_mats,
+                         const uint8_t* const* codes, const float* const* scales,
+                         const float* const* row_scale,
+                         const float* const* col_scale,
+                         int32_t bits, int32_t group, const float* levels,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * woq_codebook_normal -- the normal-quantile levels for 2^bits codes:
+ *  l_k = P((k + 1/2) / 2^bits) / P((2^bits - 1/2) / 2^bits), P the standard
+ *  normal quantile (cells of equal probability under N(0, 1), symmetric,
+ *  largest level 1), computed in fp64 and rounded to fp32.  Host only:
+ *  levels is HOST float[2^bits] (written); bits in {2, 3, 4}.
+ */
+int32_t woq_codebook_normal(int32_t bits, float* levels);
 
 /*
  * ewq_budget_levels -- [EWQ] step 3 (budgeted placement in the serving

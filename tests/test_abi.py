@@ -122,3 +122,49 @@ def test_entry_points_reject_before_any_hip_call():
     assert lib.ternary_pack(m, 1, nullpp, pp, FAKE, 1 << 30, None) == 1
     assert lib.ternary_pack(_mat(cols=1 << 16, rows=1), 1, pp, pp, FAKE, 1 << 30, None) == 2
     assert lib.ternary_pack(m, 1, pp, pp, FAKE, 4, None) == 6
+
+
+def _levels(vals):
+    return (ctypes.c_float * len(vals))(*vals)
+
+
+def test_codebook_entry_points_reject_before_any_hip_call():
+    lib = _lib.load()
+    m = _mat()
+    one = (ctypes.c_void_p * 1)(FAKE)
+    pp = ctypes.cast(one, _lib.PP)
+    ok4 = _levels([-1 + 2 * k / 15 for k in range(16)])
+    ws = 1 << 30
+    assert lib.quant_pack_codebook(m, 1, None, None, 4, 64, None, pp, pp, FAKE, ws, None) == 1
+    assert lib.quant_pack_codebook(m, 1, None, None, 8, 64, ok4, pp, pp, FAKE, ws, None) == 4
+    assert lib.quant_pack_codebook(m, 1, None, None, 1, 64, ok4, pp, pp, FAKE, ws, None) == 4
+    assert lib.quant_pack_codebook(m, 1, None, None, 4, 24, ok4, pp, pp, FAKE, ws, None) == 2
+    assert lib.quant_pack_codebook(m, 1, None, None, 4, 64, ok4, None, pp, FAKE, ws, None) == 1
+    assert lib.quant_pack_codebook(m, 1, None, None, 4, 64, ok4, pp, pp, FAKE, 64, None) == 6
+    # levels must be finite and strictly ascending
+    assert lib.quant_pack_codebook(m, 1, None, None, 2, 64, _levels([-1, 0, 0, 1]), pp, pp, FAKE, ws, None) == 11
+    assert lib.quant_pack_codebook(m, 1, None, None, 2, 64, _levels([1, 0.5, 0, -1]), pp, pp, FAKE, ws, None) == 11
+    assert lib.quant_pack_codebook(m, 1, None, None, 2, 64, _levels([-1, 0, float("nan"), 1]), pp, pp, FAKE, ws, None) == 11
+    assert lib.quant_pack_codebook(m, 1, None, None, 2, 64, _levels([-1, 0, 1, float("inf")]), pp, pp, FAKE, ws, None) == 11
+    assert lib.dequant_codebook(m, 1, pp, pp, None, None, 4, 64, None, FAKE, ws, None) == 1
+    assert lib.dequant_codebook(m, 1, pp, pp, None, None, 8, 64, ok4, FAKE, ws, None) == 4
+    assert lib.dequant_codebook(m, 1, None, pp, None, None, 4, 64, ok4, FAKE, ws, None) == 1
+    assert lib.dequant_codebook(m, 1, pp, pp, None, None, 2, 64, _levels([0, 0, 0, 0]), FAKE, ws, None) == 11
+    assert lib.dequant_codebook(m, 1, pp, pp, None, None, 4, 64, ok4, FAKE, 8, None) == 6
+    out = (ctypes.c_float * 16)()
+    assert lib.woq_codebook_normal(5, out) == 4
+    assert lib.woq_codebook_normal(4, None) == 1
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_normal_code_book_matches_oracle(bits):
+    """Host-only call: the library's normal-quantile levels equal the oracle's
+    bit for bit."""
+    import numpy as np
+    from oracle import codebook
+    lib = _lib.load()
+    out = (ctypes.c_float * (1 << bits))()
+    assert lib.woq_codebook_normal(bits, out) == 0
+    got = np.frombuffer(out, dtype=np.float32)
+    ref = codebook.normal_levels(bits)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))

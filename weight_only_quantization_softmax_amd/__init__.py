@@ -32,7 +32,8 @@ from ._lib import WoqError  # noqa: F401
 __all__ = ["ewq_block_entropy", "sinq_balance", "quant_pack_groupwise",
            "dequant_unpack", "ternary_pack", "ewq_budget_levels", "workspace_size", "WoqError",
            "df11_buffer_sizes", "df11_exponent_histogram", "df11_build_code", "df11_encode",
-           "df11_decode", "df11_compress"]
+           "df11_decode", "df11_compress", "codebook_normal", "quant_pack_codebook",
+           "dequant_codebook"]
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -165,6 +166,65 @@ def dequant_unpack(shapes, codes, scales, bits: int, group: int, *, zeros=None, 
                             _ptrs(row_scale), _ptrs(col_scale), int(bits), int(group),
                             ws.data_ptr(), ws.numel(), _stream(stream))
     _lib.check("dequant_unpack", st)
+    return out
+
+
+def codebook_normal(bits: int) -> list:
+    """The normal-quantile code book of 2^bits fp32 levels (ascending, largest 1)."""
+    lib = _lib.load()
+    buf = (ctypes.c_float * (1 << int(bits)))()
+    _lib.check("woq_codebook_normal", lib.woq_codebook_normal(int(bits), buf))
+    return list(buf)
+
+
+def _levels(bits: int, levels):
+    """Host fp32 array of the code book (default: the normal-quantile book)."""
+    lv = codebook_normal(bits) if levels is None else [float(v) for v in levels]
+    if len(lv) != 1 << int(bits):
+        raise ValueError(f"a {bits}-bit code book has {1 << int(bits)} levels, got {len(lv)}")
+    return (ctypes.c_float * len(lv))(*lv)
+
+
+def quant_pack_codebook(mats: Sequence[torch.Tensor], bits: int, group: int, *, levels=None,
+                        row_scale=None, col_scale=None, codes=None, scales=None, ws=None,
+                        stream=None):
+    """Packed codes (uint8 [rows, cols*bits/8]) of the nearest code-book level and the
+    per-group scales a = max |x| (fp32); levels default to the normal-quantile book."""
+    lib = _lib.load()
+    dev = mats[0].device
+    arr = _mats(mats)
+    lv = _levels(bits, levels)
+
+    def g(m):
+        return group if group else m.shape[1]
+    if codes is None:
+        codes = [torch.empty(m.shape[0], m.shape[1] * bits // 8, dtype=torch.uint8, device=dev)
+                 for m in mats]
+    if scales is None:
+        scales = [torch.empty(m.shape[0], m.shape[1] // g(m), dtype=torch.float32, device=dev)
+                  for m in mats]
+    ws = _workspace(_lib.OP_QUANT, mats, group, ws, dev)
+    st = lib.quant_pack_codebook(arr, len(mats), _ptrs(row_scale), _ptrs(col_scale), int(bits),
+                                 int(group), lv, _ptrs(codes), _ptrs(scales), ws.data_ptr(),
+                                 ws.numel(), _stream(stream))
+    _lib.check("quant_pack_codebook", st)
+    return codes, scales
+
+
+def dequant_codebook(shapes, codes, scales, bits: int, group: int, *, levels=None, row_scale=None,
+                     col_scale=None, out_dtype=torch.float32, out=None, ws=None, stream=None):
+    """Decode code-book codes back to weights W' = ((a l_q) s_i) t_j."""
+    lib = _lib.load()
+    dev = codes[0].device
+    lv = _levels(bits, levels)
+    if out is None:
+        out = [torch.empty(r, c, dtype=out_dtype, device=dev) for (r, c) in shapes]
+    arr = _mats(out)
+    ws = _workspace(_lib.OP_DEQUANT, out, group, ws, dev)
+    st = lib.dequant_codebook(arr, len(out), _ptrs(codes), _ptrs(scales), _ptrs(row_scale),
+                              _ptrs(col_scale), int(bits), int(group), lv, ws.data_ptr(),
+                              ws.numel(), _stream(stream))
+    _lib.check("dequant_codebook", st)
     return out
 
 

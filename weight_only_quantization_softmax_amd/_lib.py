@@ -27,7 +27,8 @@ OP_DF11_HIST, OP_DF11_ENCODE, OP_DF11_DECODE = 6, 7, 8
 EXPORTS = ("woq_status_string", "woq_workspace_size", "ewq_block_entropy",
            "sinq_balance", "sinq_balance_ex", "quant_pack_groupwise", "dequant_unpack", "ternary_pack",
            "ewq_budget_levels", "df11_buffer_sizes", "df11_exponent_histogram",
-           "df11_build_code", "df11_encode", "df11_decode")
+           "df11_build_code", "df11_encode", "df11_decode", "quant_pack_codebook",
+           "dequant_codebook", "woq_codebook_normal")
 
 
 class WoqMat(ctypes.Structure):
@@ -97,6 +98,15 @@ def load() -> ctypes.CDLL:
     lib.df11_decode.argtypes = [ctypes.POINTER(WoqMat), I32, PP, PP, PP, PP, PP,
                                 ctypes.POINTER(I32), PP, I64P, P, ctypes.c_size_t, P]
     lib.df11_decode.restype = I32
+    FP = ctypes.POINTER(ctypes.c_float)
+    lib.quant_pack_codebook.argtypes = [ctypes.POINTER(WoqMat), I32, PP, PP, I32, I32, FP,
+                                        PP, PP, P, ctypes.c_size_t, P]
+    lib.quant_pack_codebook.restype = I32
+    lib.dequant_codebook.argtypes = [ctypes.POINTER(WoqMat), I32, PP, PP, PP, PP, I32, I32, FP,
+                                     P, ctypes.c_size_t, P]
+    lib.dequant_codebook.restype = I32
+    lib.woq_codebook_normal.argtypes = [I32, FP]
+    lib.woq_codebook_normal.restype = I32
     _lib = lib
     return lib
 

@@ -267,7 +267,7 @@ int32_t check_group(const woq_mat* mats, int32_t n, int32_t group, bool quant) {
 // Matrices are split into a bf16 list and an f32 list (one launch each).
 struct QLayout {
     int nb = 0, nf = 0;
-    size_t tab_b, ubeg_b, tab_f, ubeg_f, segs, ubeg_s, table_end, total;
+    size_t tab_b, ubeg_b, tab_f, ubeg_f, segs, ubeg_s, book, table_end, total;
     int64_t units_b = 0, units_f = 0, units_s = 0;
     int nseg = 0;
     int nsets = 0;               // quant: number of launch sets
@@ -339,6 +339,7 @@ QLayout q_layout(const woq_mat* mats, int32_t n, int op, int32_t group,
     L.ubeg_f = a.take(sizeof(int64_t) * (L.nf + 1));
     L.segs = a.take(sizeof(RecipSeg) * L.nseg);
     L.ubeg_s = a.take(sizeof(int64_t) * (L.nseg + 1));
+    L.book = op < 2 ? a.take(sizeof(CbTable)) : 0;  // code-book grid (quant, dequant)
     L.table_end = a.end();
     if (op == 0) {
         for (int32_t i = 0; i < n; ++i) {
@@ -348,6 +349,41 @@ QLayout q_layout(const woq_mat* mats, int32_t n, int op, int32_t group,
     }
     L.total = a.end();
     return L;
+}
+
+// Code-book table from 2^bits levels (finite, strictly ascending): fp32
+// midpoints, +inf padding, and per cell c of [-1, 1] (width 1/128, left
+// edge E_c = -1 + c/128) the count of midpoints certainly below y.  The
+// kernel's cell index for y (mantissa bits 22..15 of the fp32 sum y + 3,
+// clamped to [2, 4)) is the true cell floor((y + 1) * 128) or a neighbour,
+// and |y| <= 1 + 2^-23, so y lies in [E_{c-1}, E_{c+2}):
+// midpoints below E_{c-1} are below y and midpoints at or above E_{c+2} are
+// not.  Returns the comparisons per value (the widest spread), or -1 for an
+// invalid book.
+int cb_build(const float* levels, int bits, CbTable* t) {
+    const int n = 1 << bits, nm = n - 1;
+    for (int k = 0; k < n; ++k) {
+        if (!std::isfinite(levels[k])) return -1;
+        if (k && !(levels[k] > levels[k - 1])) return -1;
+    }
+    for (int k = 0; k < kCbMax; ++k) {
+        t->level[k] = k < n ? levels[k] : 0.0f;
+        t->mid[k] = k < nm ? (levels[k] + levels[k + 1]) * 0.5f : INFINITY;
+    }
+    auto below = [&](double e) {
+        int c = 0;
+        while (c < nm && (double)t->mid[c] < e) ++c;
+        return c;
+    };
+    int steps = 1;
+    for (int c = 0; c < kCbCells; ++c) {
+        const double half = kCbCells / 2;
+        const int lo = below(-1.0 + (c - 1) / half), hi = below(-1.0 + (c + 2) / half);
+        t->cell[c].lo = (uint32_t)lo;
+        t->cell[c].thr = t->mid[lo];
+        steps = std::max(steps, hi - lo);
+    }
+    return steps;
 }
 
 // ------------------------------------------------------------------ DF11
@@ -596,23 +632,34 @@ int32_t sinq_balance_ex(const woq_mat* mats, int32_t n_mats, int32_t iters, int3
     return WOQ_OK;
 }
 
-int32_t quant_pack_groupwise(const woq_mat* mats, int32_t n_mats, const float* const* row_scale,
-                             const float* const* col_scale, int32_t bits, int32_t group,
-                             uint8_t* const* codes, float* const* scales, uint8_t* const* zeros,
-                             void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Quantisation on the affine grid (levels == NULL) or the code-book grid.
+int32_t quant_impl(const woq_mat* mats, int32_t n_mats, const float* const* row_scale,
+                   const float* const* col_scale, int32_t bits, int32_t group,
+                   const float* levels, uint8_t* const* codes, float* const* scales,
+                   uint8_t* const* zeros, void* ws, size_t ws_bytes, hipStream_t stream) {
     int32_t st = check_mats(mats, n_mats, true);
     if (st) return st;
-    if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return WOQ_ERR_BITS;
+    if (levels ? (bits < 2 || bits > 4) : (bits != 2 && bits != 3 && bits != 4 && bits != 8))
+        return WOQ_ERR_BITS;
     if ((st = check_group(mats, n_mats, group, true))) return st;
     if ((st = check_ptrs(reinterpret_cast<const void* const*>(codes), n_mats, 16))) return st;
     if ((st = check_ptrs(reinterpret_cast<const void* const*>(scales), n_mats, 4))) return st;
-    if ((st = check_ptrs(reinterpret_cast<const void* const*>(zeros), n_mats, 1))) return st;
+    if (!levels && (st = check_ptrs(reinterpret_cast<const void* const*>(zeros), n_mats, 1))) return st;
     if ((st = check_opt_ptrs(reinterpret_cast<const void* const*>(row_scale), n_mats, 4))) return st;
     if ((st = check_opt_ptrs(reinterpret_cast<const void* const*>(col_scale), n_mats, 4))) return st;
+    CbTable book;
+    int steps = 0;
+    if (levels && (steps = cb_build(levels, bits, &book)) < 0) return WOQ_ERR_VALUE;
     const QLayout L = q_layout(mats, n_mats, 0, group, row_scale, col_scale);
     if ((st = check_ws(ws, ws_bytes, L.total))) return st;
 
     std::vector<char> host(L.table_end, 0);
+    if (levels) std::memcpy(host.data() + L.book, &book, sizeof(CbTable));
+    const CbTable* dbook = levels ? at<CbTable>(ws, L.book) : nullptr;
     QMat* tb = at<QMat>(host.data(), L.tab_b);
     int64_t* ub = at<int64_t>(host.data(), L.ubeg_b);
     RecipSeg* sg = at<RecipSeg>(host.data(), L.segs);
@@ -654,7 +701,7 @@ int32_t quant_pack_groupwise(const woq_mat* mats, int32_t n_mats, const float* c
         q.data = m.data;
         q.codes = codes[i];
         q.scales = scales[i];
-        q.zeros = zeros[i];
+        q.zeros = levels ? nullptr : zeros[i];
         q.rs = L.rs[i] ? at<float>(ws, L.rs[i]) : nullptr;
         q.ct = L.ct[i] ? at<float>(ws, L.ct[i]) : nullptr;
         q.rows = (int32_t)m.rows;
@@ -672,31 +719,39 @@ int32_t quant_pack_groupwise(const woq_mat* mats, int32_t n_mats, const float* c
         const QMat* dt = at<QMat>(ws, L.tab_b) + st_.first;
         const int64_t* du = at<int64_t>(ws, L.ubeg_b) + st_.uoff;
         if (st_.key.kind == 0)
-            WOQ_HIP(quant_tile(dt, du, st_.count, st_.units, st_.key.dtype, bits, stream));
+            WOQ_HIP(quant_tile(dt, du, st_.count, st_.units, st_.key.dtype, bits, dbook, steps, stream));
         else if (st_.key.kind == 1)
-            WOQ_HIP(quant_wave(dt, du, st_.count, st_.units, st_.key.dtype, bits, st_.key.nvl, stream));
+            WOQ_HIP(quant_wave(dt, du, st_.count, st_.units, st_.key.dtype, bits, st_.key.nvl, dbook,
+                               steps, stream));
         else
-            WOQ_HIP(quant_big(dt, du, st_.count, st_.units, st_.key.dtype, bits, stream));
+            WOQ_HIP(quant_big(dt, du, st_.count, st_.units, st_.key.dtype, bits, dbook, steps, stream));
     }
     return WOQ_OK;
 }
 
-int32_t dequant_unpack(const woq_mat* out, int32_t n_mats, const uint8_t* const* codes,
-                       const float* const* scales, const uint8_t* const* zeros,
-                       const float* const* row_scale, const float* const* col_scale, int32_t bits,
-                       int32_t group, void* ws, size_t ws_bytes, hipStream_t stream) {
+// Dequantisation on the affine grid (levels == NULL) or the code-book grid.
+int32_t dequant_impl(const woq_mat* out, int32_t n_mats, const uint8_t* const* codes,
+                     const float* const* scales, const uint8_t* const* zeros,
+                     const float* const* row_scale, const float* const* col_scale, int32_t bits,
+                     int32_t group, const float* levels, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
     int32_t st = check_mats(out, n_mats, true);
     if (st) return st;
-    if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return WOQ_ERR_BITS;
+    if (levels ? (bits < 2 || bits > 4) : (bits != 2 && bits != 3 && bits != 4 && bits != 8))
+        return WOQ_ERR_BITS;
     if ((st = check_group(out, n_mats, group, false))) return st;
     if ((st = check_ptrs(reinterpret_cast<const void* const*>(codes), n_mats, 16))) return st;
     if ((st = check_ptrs(reinterpret_cast<const void* const*>(scales), n_mats, 4))) return st;
     if ((st = check_opt_ptrs(reinterpret_cast<const void* const*>(row_scale), n_mats, 4))) return st;
     if ((st = check_opt_ptrs(reinterpret_cast<const void* const*>(col_scale), n_mats, 16))) return st;
+    CbTable book;
+    if (levels && cb_build(levels, bits, &book) < 0) return WOQ_ERR_VALUE;
     const QLayout L = q_layout(out, n_mats, 1, group, nullptr, nullptr);
     if ((st = check_ws(ws, ws_bytes, L.total))) return st;
 
     std::vector<char> host(L.table_end, 0);
+    if (levels) std::memcpy(host.data() + L.book, &book, sizeof(CbTable));
+    const CbTable* dbook = levels ? at<CbTable>(ws, L.book) : nullptr;
     QMat* tb = at<QMat>(host.data(), L.tab_b);
     QMat* tf = at<QMat>(host.data(), L.tab_f);
     int64_t* ub = at<int64_t>(host.data(), L.ubeg_b);
@@ -709,7 +764,7 @@ int32_t dequant_unpack(const woq_mat* out, int32_t n_mats, const uint8_t* const*
         q.data = m.data;
         q.codes = const_cast<uint8_t*>(codes[i]);
         q.scales = const_cast<float*>(scales[i]);
-        q.zeros = zeros ? const_cast<uint8_t*>(zeros[i]) : nullptr;
+        q.zeros = zeros && !levels ? const_cast<uint8_t*>(zeros[i]) : nullptr;
         q.rs = row_scale ? row_scale[i] : nullptr;
         q.ct = col_scale ? col_scale[i] : nullptr;
         q.rows = (int32_t)m.rows;
@@ -721,8 +776,68 @@ int32_t dequant_unpack(const woq_mat* out, int32_t n_mats, const uint8_t* const*
         else { tf[jf] = q; uf[jf + 1] = uf[jf] + u; ++jf; }
     }
     WOQ_HIP(hipMemcpyAsync(ws, host.data(), L.table_end, hipMemcpyHostToDevice, stream));
-    if (L.nb) WOQ_HIP(dequant(at<QMat>(ws, L.tab_b), at<int64_t>(ws, L.ubeg_b), L.nb, ub[L.nb], WOQ_BF16, bits, stream));
-    if (L.nf) WOQ_HIP(dequant(at<QMat>(ws, L.tab_f), at<int64_t>(ws, L.ubeg_f), L.nf, uf[L.nf], WOQ_F32, bits, stream));
+    if (L.nb) WOQ_HIP(dequant(at<QMat>(ws, L.tab_b), at<int64_t>(ws, L.ubeg_b), L.nb, ub[L.nb], WOQ_BF16, bits, dbook, stream));
+    if (L.nf) WOQ_HIP(dequant(at<QMat>(ws, L.tab_f), at<int64_t>(ws, L.ubeg_f), L.nf, uf[L.nf], WOQ_F32, bits, dbook, stream));
+    return WOQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t quant_pack_groupwise(const woq_mat* mats, int32_t n_mats, const float* const* row_scale,
+                             const float* const* col_scale, int32_t bits, int32_t group,
+                             uint8_t* const* codes, float* const* scales, uint8_t* const* zeros,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+    return quant_impl(mats, n_mats, row_scale, col_scale, bits, group, nullptr, codes, scales,
+                      zeros, ws, ws_bytes, stream);
+}
+
+int32_t dequant_unpack(const woq_mat* out, int32_t n_mats, const uint8_t* const* codes,
+                       const float* const* scales, const uint8_t* const* zeros,
+                       const float* const* row_scale, const float* const* col_scale, int32_t bits,
+                       int32_t group, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return dequant_impl(out, n_mats, codes, scales, zeros, row_scale, col_scale, bits, group,
+                        nullptr, ws, ws_bytes, stream);
+}
+
+int32_t quant_pack_codebook(const woq_mat* mats, int32_t n_mats, const float* const* row_scale,
+                            const float* const* col_scale, int32_t bits, int32_t group,
+                            const float* levels, uint8_t* const* codes, float* const* scales,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!levels) return WOQ_ERR_NULL;
+    return quant_impl(mats, n_mats, row_scale, col_scale, bits, group, levels, codes, scales,
+                      nullptr, ws, ws_bytes, stream);
+}
+
+int32_t dequant_codebook(const woq_mat* out, int32_t n_mats, const uint8_t* const* codes,
+                         const float* const* scales, const float* const* row_scale,
+                         const float* const* col_scale, int32_t bits, int32_t group,
+                         const float* levels, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!levels) return WOQ_ERR_NULL;
+    return dequant_impl(out, n_mats, codes, scales, nullptr, row_scale, col_scale, bits, group,
+                        levels, ws, ws_bytes, stream);
+}
+
+// Normal-quantile levels: l_k = P((k + 1/2) / n) / P((n - 1/2) / n), n =
+// 2^bits, P the standard normal quantile, found by bisection on the normal
+// CDF 0.5 erfc(-x / sqrt 2) in fp64 (to the last bit of the bracket), then
+// rounded once to fp32.
+int32_t woq_codebook_normal(int32_t bits, float* levels) {
+    if (!levels) return WOQ_ERR_NULL;
+    if (bits < 2 || bits > 4) return WOQ_ERR_BITS;
+    const int n = 1 << bits;
+    auto quantile = [](double p) {
+        double lo = -40.0, hi = 40.0;
+        for (int it = 0; it < 200; ++it) {
+            const double mid = 0.5 * (lo + hi);
+            if (mid <= lo || mid >= hi) break;
+            if (0.5 * std::erfc(-mid / std::sqrt(2.0)) < p) lo = mid; else hi = mid;
+        }
+        return 0.5 * (lo + hi);
+    };
+    const double top = quantile((n - 0.5) / n);
+    for (int k = 0; k < n; ++k) levels[k] = (float)(quantile((k + 0.5) / n) / top);
     return WOQ_OK;
 }
 

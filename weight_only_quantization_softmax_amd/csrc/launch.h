@@ -69,14 +69,20 @@ constexpr int kQTileCols = 2048;
 constexpr int kQWaveMax = 4096;
 // dequant_unpack tiles: kDTileRows x kQTileCols (any group).
 constexpr int kDTileRows = 4;
+// book == NULL: the affine grid; else the code-book grid (bits 2..4) with
+// the table at `book` in device memory and `steps` comparisons per value.
 hipError_t quant_tile(const QMat* mats, const int64_t* ubeg, int nmat,
-                      int64_t n_units, int dtype, int bits, hipStream_t s);
+                      int64_t n_units, int dtype, int bits, const CbTable* book,
+                      int steps, hipStream_t s);
 hipError_t quant_wave(const QMat* mats, const int64_t* ubeg, int nmat,
-                      int64_t n_units, int dtype, int bits, int nvl, hipStream_t s);
+                      int64_t n_units, int dtype, int bits, int nvl,
+                      const CbTable* book, int steps, hipStream_t s);
 hipError_t quant_big(const QMat* mats, const int64_t* ubeg, int nmat,
-                     int64_t n_units, int dtype, int bits, hipStream_t s);
+                     int64_t n_units, int dtype, int bits, const CbTable* book,
+                     int steps, hipStream_t s);
 hipError_t dequant(const QMat* mats, const int64_t* ubeg, int nmat,
-                   int64_t n_units, int out_dtype, int bits, hipStream_t s);
+                   int64_t n_units, int out_dtype, int bits, const CbTable* book,
+                   hipStream_t s);
 hipError_t ternary(const QMat* mats, const int64_t* ubeg, int nmat,
                    int64_t n_units, int dtype, hipStream_t s);
 

@@ -24,6 +24,13 @@
 //  k_dequant      tiles of kDTileRows rows x 2048 columns (measured on the
 //                 8B stack's int4 matrices: 4 rows beat 8 and 16).
 //  k_ternary      one workgroup per row.
+//
+// The tile, wave and big kernels and k_dequant also serve the code-book
+// grid (template argument CB): a group is scaled by its largest |x| and each
+// value takes the nearest of 2^b caller-given levels (the [SINQ] page's
+// non-uniform option, same section as the low-bit codes).  The nearest level
+// is the number of level midpoints below y, found from a 256-cell table in
+// LDS and `steps` comparisons (one for the normal-quantile books).
 #include "launch.h"
 
 #include <math.h>
@@ -92,6 +99,115 @@ __device__ __forceinline__ void code8(const float (&x)[8], const GroupParams& g,
         c[k] = (uint32_t)t;
     }
 }
+
+// Code-book grid: a = max |x| of the group, inv = 1/a (0 when not finite,
+// so y = x * inv = 0 and the code is that of level nearest 0).
+struct CbParams {
+    float a, inv;
+};
+__device__ __forceinline__ CbParams cb_params(float lo, float hi) {
+    CbParams p;
+    p.a = fmaxf(hi, -lo);  // max |x| from the group's min and max
+    const float inv = __fdiv_rn(1.0f, p.a);
+    p.inv = isfinite(inv) ? inv : 0.0f;
+    return p;
+}
+
+// Copies the code book into LDS; every thread of the workgroup takes part,
+// before any early exit.  Called after the workgroup's data loads are issued,
+// so the table's load latency overlaps theirs.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+template <bool CB>
+__device__ __forceinline__ const CbTable* stage_book(const CbTable* g) {
+    if constexpr (!CB) {
+        return nullptr;
+    } else {
+        __shared__ CbTable sh;
+        static_assert(kCbCells == kT, "one cell per thread");
+        const u32x2 c = gload<u32x2>(&g->cell[threadIdx.x]);
+        sh.cell[threadIdx.x].lo = c.x;
+        sh.cell[threadIdx.x].thr = __uint_as_float(c.y);
+        if (threadIdx.x < kCbMax) {
+            sh.mid[threadIdx.x] = gload<float>(g->mid + threadIdx.x);
+            sh.level[threadIdx.x] = gload<float>(g->level + threadIdx.x);
+        }
+        __syncthreads();
+        return &sh;
+    }
+}
+
+// The levels alone (dequantisation), same rules as stage_book.
+template <bool CB>
+__device__ __forceinline__ const float* stage_levels(const CbTable* g) {
+    if constexpr (!CB) {
+        return nullptr;
+    } else {
+        __shared__ float lv[kCbMax];
+        if (threadIdx.x < kCbMax) lv[threadIdx.x] = gload<float>(g->level + threadIdx.x);
+        __syncthreads();
+        return lv;
+    }
+}
+
+// code = number of midpoints m_k with y > m_k (the nearest level; a tie
+// goes to the lower one).  The cell index comes from the bits of z = y + 3
+// (one rounding): z in [2, 4) has a fixed exponent, so mantissa bits 22..15
+// are floor((z - 2) * 128), which is the true cell floor((y + 1) * 128) or
+// a neighbour (the rounding moves it by at most 2^-16 of a cell), both of
+// which the table covers.  Clamping the bits to [2, 4) handles |y| up to
+// 1 + 2^-23 and keeps a NaN's index in the table, with no float-to-int
+// conversion.  The cell bounds the count to [cell.lo, cell.lo + steps];
+// the midpoints ascend, so each comparison either adds one or leaves the
+// code final.
+__device__ __forceinline__ void code8_cb(const float (&x)[8], float inv, const CbTable* bk,
+                                         int steps, uint32_t (&c)[8]) {
+    static_assert(kCbCells == 256, "8 mantissa bits index the table");
+    constexpr int lo_bits = 0x40000000, hi_bits = 0x407FFFFF;  // 2.0f, largest float below 4
+    // Three phases, so that the eight table reads are in flight together.
+    float y[8];
+    CbCell e[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        y[k] = __fmul_rn(x[k], inv);
+        const int zb = min(max(__float_as_int(__fadd_rn(y[k], 3.0f)), lo_bits), hi_bits);
+        e[k] = bk->cell[(zb >> 15) & (kCbCells - 1)];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) c[k] = e[k].lo + (y[k] > e[k].thr ? 1u : 0u);
+#pragma nounroll
+    for (int st = 1; st < steps; ++st) {
+        float m[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) m[k] = bk->mid[c[k]];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) c[k] += y[k] > m[k] ? 1u : 0u;
+    }
+}
+
+// A group's parameters on either grid: derived from the group's min / max,
+// coding 8 values, storing the per-group scale (and zero-point).
+template <bool CB, int BITS>
+struct Grid {
+    GroupParams g;
+    CbParams p;
+    __device__ __forceinline__ Grid(float lo, float hi) {
+        if constexpr (CB) p = cb_params(lo, hi);
+        else g = group_params<BITS>(lo, hi);
+    }
+    __device__ __forceinline__ void code(const float (&x)[8], const CbTable* bk, int steps,
+                                         uint32_t (&c)[8]) const {
+        if constexpr (CB) code8_cb(x, p.inv, bk, steps, c);
+        else code8<BITS>(x, g, c);
+    }
+    __device__ __forceinline__ void store(const QMat& q, uint32_t gi) const {
+        if constexpr (CB) {
+            gstore<float>(q.scales + gi, p.a);
+        } else {
+            gstore<float>(q.scales + gi, g.delta);
+            gstore<uint8_t>(q.zeros + gi, (uint8_t)g.z);
+        }
+    }
+};
 
 // Raw storage of 8 elements: a 16-byte bf16 vector or two float4.
 template <int DT> struct Raw8;
@@ -174,9 +290,10 @@ constexpr int kTileRows = kQTileRows;
 constexpr int kTileCols = kQTileCols;
 static_assert(kTileCols == 8 * kT, "one 8-column vector per thread");
 
-template <int DT, int BITS>
+template <int DT, int BITS, bool CB>
 __global__ __launch_bounds__(kT) void k_quant_tile(const QMat* __restrict__ mats,
-                                                   const int64_t* __restrict__ ubeg, int nmat) {
+                                                   const int64_t* __restrict__ ubeg, int nmat,
+                                                   const CbTable* __restrict__ book, int steps) {
     const int64_t u = blockIdx.x;
     const int m = find_unit_owner(ubeg, nmat, u);
     const QMat q = mats[m];
@@ -202,6 +319,7 @@ __global__ __launch_bounds__(kT) void k_quant_tile(const QMat* __restrict__ mats
         if (r < nr && active) raw[r] = load_raw<DT>(q.data, (uint32_t)(r0 + r) * (uint32_t)q.cols + col);
         rsv[r] = has_rs && r < nr ? gload<float>(q.rs + r0 + r) : 1.0f;
     }
+    const CbTable* bk = stage_book<CB>(book);
 #pragma unroll
     for (int r = 0; r < kTileRows; ++r) {
         if (r >= nr) break;
@@ -216,17 +334,14 @@ __global__ __launch_bounds__(kT) void k_quant_tile(const QMat* __restrict__ mats
 #pragma unroll
         for (int k = 1; k < 8; ++k) { lo = fminf(lo, x[k]); hi = fmaxf(hi, x[k]); }
         group_minmax(lo, hi, lanes);
-        const GroupParams g = group_params<BITS>(lo, hi);
+        const Grid<CB, BITS> g(lo, hi);
         if (active) {
             const uint32_t e0 = row * (uint32_t)q.cols + col;
             uint32_t cd[8];
-            code8<BITS>(x, g, cd);
+            g.code(x, bk, steps, cd);
             store_codes<BITS>(q.codes, e0, cd);
-            if ((threadIdx.x & (lanes - 1)) == 0) {
-                const uint32_t gi = e0 >> __builtin_ctz((uint32_t)q.group);  // power-of-two group
-                gstore<float>(q.scales + gi, g.delta);
-                gstore<uint8_t>(q.zeros + gi, (uint8_t)g.z);
-            }
+            if ((threadIdx.x & (lanes - 1)) == 0)
+                g.store(q, e0 >> __builtin_ctz((uint32_t)q.group));  // power-of-two group
         }
     }
 }
@@ -234,29 +349,32 @@ __global__ __launch_bounds__(kT) void k_quant_tile(const QMat* __restrict__ mats
 // Groups of more than 512 and at most 64 * 8 * NVL columns: one wave per
 // group (four per workgroup), values kept packed in registers between the
 // min / max reduction and the coding pass.
-template <int DT, int BITS, int NVL>
+template <int DT, int BITS, int NVL, bool CB>
 __global__ __launch_bounds__(kT) void k_quant_wave(const QMat* __restrict__ mats,
-                                                   const int64_t* __restrict__ ubeg, int nmat) {
+                                                   const int64_t* __restrict__ ubeg, int nmat,
+                                                   const CbTable* __restrict__ book, int steps) {
     const int64_t u = blockIdx.x;
     const int m = find_unit_owner(ubeg, nmat, u);
     const QMat q = mats[m];
     const int lane = threadIdx.x & 63;
     const uint32_t ng = (uint32_t)q.rows * (uint32_t)q.cols / (uint32_t)q.group;
     const uint32_t gi = (uint32_t)(u - ubeg[m]) * (kT / 64) + (threadIdx.x >> 6);
-    if (gi >= ng) return;  // whole wave; no workgroup barrier below
-    const uint32_t gbase = gi * (uint32_t)q.group;
+    const bool live = gi < ng;  // whole wave
+    const uint32_t gbase = live ? gi * (uint32_t)q.group : 0u;
     const uint32_t row = gbase / (uint32_t)q.cols;
     const uint32_t col0 = gbase - row * (uint32_t)q.cols;
     const int nvg = q.group >> 3;
     const bool has_rs = q.rs != nullptr, has_ct = q.ct != nullptr;
-    const float rsv = has_rs ? gload<float>(q.rs + row) : 1.0f;
+    const float rsv = has_rs && live ? gload<float>(q.rs + row) : 1.0f;
     Raw8<DT> raw[NVL];
     float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
     for (int k = 0; k < NVL; ++k) {
         const int v = lane + 64 * k;
-        if (v < nvg) raw[k] = load_raw<DT>(q.data, gbase + 8u * v);
+        if (live && v < nvg) raw[k] = load_raw<DT>(q.data, gbase + 8u * v);
     }
+    const CbTable* bk = stage_book<CB>(book);
+    if (!live) return;  // after the workgroup barrier; none below
 #pragma unroll
     for (int k = 0; k < NVL; ++k) {
         const int v = lane + 64 * k;
@@ -269,7 +387,7 @@ __global__ __launch_bounds__(kT) void k_quant_wave(const QMat* __restrict__ mats
         }
     }
     group_minmax(lo, hi, 64);
-    const GroupParams g = group_params<BITS>(lo, hi);
+    const Grid<CB, BITS> g(lo, hi);
 #pragma unroll
     for (int k = 0; k < NVL; ++k) {
         const int v = lane + 64 * k;
@@ -278,23 +396,21 @@ __global__ __launch_bounds__(kT) void k_quant_wave(const QMat* __restrict__ mats
             if (has_ct) load_ct(q.ct, col0 + 8u * v, c);
             balance<DT>(raw[k], rsv, c, x);
             uint32_t cd[8];
-            code8<BITS>(x, g, cd);
+            g.code(x, bk, steps, cd);
             store_codes<BITS>(q.codes, gbase + 8u * v, cd);
         }
     }
-    if (lane == 0) {
-        gstore<float>(q.scales + gi, g.delta);
-        gstore<uint8_t>(q.zeros + gi, (uint8_t)g.z);
-    }
+    if (lane == 0) g.store(q, gi);
 }
 
 // Wider groups (e.g. one group per row of 14336 columns): one workgroup per
 // group, raw values kept in registers between the min / max reduction
 // (waves, then one LDS exchange) and the coding pass.
-template <int DT, int BITS>
+template <int DT, int BITS, bool CB>
 __global__ __launch_bounds__(kT) void k_quant_big(const QMat* __restrict__ mats,
                                                   const int64_t* __restrict__ ubeg,
-                                                  int nmat) {
+                                                  int nmat, const CbTable* __restrict__ book,
+                                                  int steps) {
     constexpr int MAXV = (DT == WOQ_BF16) ? 16 : 8;
     __shared__ float2 sh[kT / 64];
     const int64_t u = blockIdx.x;
@@ -314,6 +430,7 @@ __global__ __launch_bounds__(kT) void k_quant_big(const QMat* __restrict__ mats,
         const int v = threadIdx.x + kT * k;
         if (v < nvg) raw[k] = load_raw<DT>(q.data, gbase + 8u * v);
     }
+    const CbTable* bk = stage_book<CB>(book);
     float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
     for (int k = 0; k < MAXV; ++k) {
@@ -331,7 +448,7 @@ __global__ __launch_bounds__(kT) void k_quant_big(const QMat* __restrict__ mats,
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < kT / 64; ++w) { lo = fminf(lo, sh[w].x); hi = fmaxf(hi, sh[w].y); }
-    const GroupParams g = group_params<BITS>(lo, hi);
+    const Grid<CB, BITS> g(lo, hi);
 #pragma unroll
     for (int k = 0; k < MAXV; ++k) {
         const int v = threadIdx.x + kT * k;
@@ -340,14 +457,11 @@ __global__ __launch_bounds__(kT) void k_quant_big(const QMat* __restrict__ mats,
             if (has_ct) load_ct(q.ct, col0 + 8u * v, c);
             balance<DT>(raw[k], rsv, c, x);
             uint32_t cd[8];
-            code8<BITS>(x, g, cd);
+            g.code(x, bk, steps, cd);
             store_codes<BITS>(q.codes, gbase + 8u * v, cd);
         }
     }
-    if (threadIdx.x == 0) {
-        gstore<float>(q.scales + gl, g.delta);
-        gstore<uint8_t>(q.zeros + gl, (uint8_t)g.z);
-    }
+    if (threadIdx.x == 0) g.store(q, gl);
 }
 
 // Two floats to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32,
@@ -357,8 +471,9 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-// Dequantisation W' = (((q - z) delta) s_i) t_j, one fp32 rounding per
-// product, then (bf16 output) one round-to-nearest-even.  Same tiles as
+// Dequantisation W' = (((q - z) delta) s_i) t_j (code book: ((a l_q) s_i)
+// t_j), one fp32 rounding per product, then (bf16 output) one
+// round-to-nearest-even.  Same tiles as
 // k_quant_tile: a workgroup takes 8 rows x 2048 columns, thread t the 8
 // columns 8t..; t_j is loaded once per tile, s_i once per row.
 template <int BITS>
@@ -383,10 +498,10 @@ __device__ __forceinline__ void load_codes_g(const uint8_t* codes, uint32_t e0, 
     }
 }
 
-template <int BITS, int ODT>
+template <int BITS, int ODT, bool CB>
 __global__ __launch_bounds__(kT) void k_dequant(const QMat* __restrict__ mats,
                                                 const int64_t* __restrict__ ubeg, int nmat,
-                                                int zdef) {
+                                                int zdef, const CbTable* __restrict__ book) {
     const int64_t u = blockIdx.x;
     const int m = find_unit_owner(ubeg, nmat, u);
     const QMat q = mats[m];
@@ -394,12 +509,17 @@ __global__ __launch_bounds__(kT) void k_dequant(const QMat* __restrict__ mats,
     const int tl = (int)(u - ubeg[m]);
     const int rt = tl / ctiles;
     const uint32_t col = (uint32_t)(tl - rt * ctiles) * kTileCols + 8u * threadIdx.x;
-    if (col >= (uint32_t)q.cols) return;  // no cross-lane work below
+    // Lanes past the matrix's edge exit at once on the affine grid; on the
+    // code-book grid they first join the workgroup barrier of the level table.
+    const bool active = col < (uint32_t)q.cols;
+    if constexpr (!CB) {
+        if (!active) return;
+    }
     const int r0 = rt * kDTileRows;
     const int nr = min(kDTileRows, q.rows - r0);
     const bool has_rs = q.rs != nullptr, has_ct = q.ct != nullptr;
     float t8[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
-    if (has_ct) load_ct(q.ct, col, t8);
+    if (has_ct && active) load_ct(q.ct, col, t8);
     // Every load of the tile (codes and the per-row group parameters) is
     // issued before the first use.  The group divides the row and is a
     // multiple of 8, so a thread's 8 columns share one group, whose index is
@@ -410,22 +530,29 @@ __global__ __launch_bounds__(kT) void k_dequant(const QMat* __restrict__ mats,
     int zr[kDTileRows];
 #pragma unroll
     for (int r = 0; r < kDTileRows; ++r) {
-        if (r < nr) {
+        if (r < nr && active) {
             const uint32_t row = (uint32_t)(r0 + r), gi = row * gpr + gcol;
             load_codes_g<BITS>(q.codes, row * (uint32_t)q.cols + col, cw[r]);
             delta[r] = gload<float>(q.scales + gi);
-            zr[r] = q.zeros ? (int)gload<uint8_t>(q.zeros + gi) : zdef;
+            if constexpr (!CB) zr[r] = q.zeros ? (int)gload<uint8_t>(q.zeros + gi) : zdef;
             rsv[r] = has_rs ? gload<float>(q.rs + row) : 1.0f;
         }
     }
+    const float* lv = stage_levels<CB>(book);
+    if (!active) return;
 #pragma unroll
     for (int r = 0; r < kDTileRows; ++r) {
         if (r >= nr) break;
         const uint32_t e0 = (uint32_t)(r0 + r) * (uint32_t)q.cols + col;
         float y[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k)  // absent scales are exactly 1 (identity)
-            y[k] = __fmul_rn(__fmul_rn(__fmul_rn((float)((int)cw[r][k] - zr[r]), delta[r]), rsv[r]), t8[k]);
+        for (int k = 0; k < 8; ++k) {  // absent scales are exactly 1 (identity)
+            // affine: (q - z) * delta; code book: a * level[q]
+            float v;
+            if constexpr (CB) v = __fmul_rn(delta[r], lv[cw[r][k]]);
+            else v = __fmul_rn((float)((int)cw[r][k] - zr[r]), delta[r]);
+            y[k] = __fmul_rn(__fmul_rn(v, rsv[r]), t8[k]);
+        }
         if constexpr (ODT == WOQ_F32) {
             float* o = const_cast<float*>(reinterpret_cast<const float*>(q.data)) + e0;
             gstore_f4(o, y[0], y[1], y[2], y[3]);
@@ -503,71 +630,71 @@ __global__ __launch_bounds__(kT) void k_recip(const RecipSeg* __restrict__ segs,
     const int s = find_unit_owner(ubeg, nseg, u);
     const RecipSeg sg = segs[s];
     const int64_t i = (u - ubeg[s]) * kT + threadIdx.x;
-    if (i < sg.n) sg.dst[i] = __fdiv_rn(1.0f, sg.src[i]);
+    if (i < sg.n) gstore<float>(sg.dst + i, __fdiv_rn(1.0f, gload<float>(sg.src + i)));
 }
 
-template <int DT>
-hipError_t quant_tile_dt(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                         int bits, hipStream_t s) {
-    const dim3 grid((unsigned)n_units), block(kT);
+// Calls f(Bits<b>{}) for the code width; the code-book grid has no 8-bit
+// form (the API admits 2, 3 and 4 bits for it).
+template <int B> struct Bits { static constexpr int value = B; };
+template <bool CB, class F>
+hipError_t by_bits(int bits, F&& f) {
     switch (bits) {
-        case 2: k_quant_tile<DT, 2><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
-        case 3: k_quant_tile<DT, 3><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
-        case 4: k_quant_tile<DT, 4><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
-        default: k_quant_tile<DT, 8><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
+        case 2: f(Bits<2>{}); break;
+        case 3: f(Bits<3>{}); break;
+        case 4: f(Bits<4>{}); break;
+        default:
+            if constexpr (CB) return hipErrorInvalidValue;
+            else f(Bits<8>{});
     }
     return hipGetLastError();
 }
 
-template <int DT, int NVL>
+template <int DT, bool CB>
+hipError_t quant_tile_g(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
+                        int bits, const CbTable* book, int steps, hipStream_t s) {
+    return by_bits<CB>(bits, [&](auto b) {
+        k_quant_tile<DT, decltype(b)::value, CB>
+            <<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, book, steps);
+    });
+}
+
+template <int DT, int NVL, bool CB>
+hipError_t quant_wave_g(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
+                        int bits, const CbTable* book, int steps, hipStream_t s) {
+    return by_bits<CB>(bits, [&](auto b) {
+        k_quant_wave<DT, decltype(b)::value, NVL, CB>
+            <<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, book, steps);
+    });
+}
+
+template <int DT, bool CB>
 hipError_t quant_wave_nv(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                         int bits, hipStream_t s) {
-    const dim3 grid((unsigned)n_units), block(kT);
-    switch (bits) {
-        case 2: k_quant_wave<DT, 2, NVL><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
-        case 3: k_quant_wave<DT, 3, NVL><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
-        case 4: k_quant_wave<DT, 4, NVL><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
-        default: k_quant_wave<DT, 8, NVL><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
-    }
-    return hipGetLastError();
-}
-
-template <int DT>
-hipError_t quant_wave_dt(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                         int bits, int nvl, hipStream_t s) {
+                         int bits, int nvl, const CbTable* book, int steps, hipStream_t s) {
     switch (nvl) {
-        case 1: return quant_wave_nv<DT, 1>(mats, ubeg, nmat, n_units, bits, s);
-        case 2: return quant_wave_nv<DT, 2>(mats, ubeg, nmat, n_units, bits, s);
-        case 4: return quant_wave_nv<DT, 4>(mats, ubeg, nmat, n_units, bits, s);
-        default: return quant_wave_nv<DT, 8>(mats, ubeg, nmat, n_units, bits, s);
+        case 1: return quant_wave_g<DT, 1, CB>(mats, ubeg, nmat, n_units, bits, book, steps, s);
+        case 2: return quant_wave_g<DT, 2, CB>(mats, ubeg, nmat, n_units, bits, book, steps, s);
+        case 4: return quant_wave_g<DT, 4, CB>(mats, ubeg, nmat, n_units, bits, book, steps, s);
+        default: return quant_wave_g<DT, 8, CB>(mats, ubeg, nmat, n_units, bits, book, steps, s);
     }
 }
 
-template <int DT>
-hipError_t quant_big_dt(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                        int bits, hipStream_t s) {
-    const dim3 grid((unsigned)n_units), block(kT);
-    switch (bits) {
-        case 2: k_quant_big<DT, 2><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
-        case 3: k_quant_big<DT, 3><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
-        case 4: k_quant_big<DT, 4><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
-        default: k_quant_big<DT, 8><<<grid, block, 0, s>>>(mats, ubeg, nmat); break;
-    }
-    return hipGetLastError();
+template <int DT, bool CB>
+hipError_t quant_big_g(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
+                       int bits, const CbTable* book, int steps, hipStream_t s) {
+    return by_bits<CB>(bits, [&](auto b) {
+        k_quant_big<DT, decltype(b)::value, CB>
+            <<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, book, steps);
+    });
 }
 
-template <int ODT>
-hipError_t dequant_dt(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                      int bits, hipStream_t s) {
-    const dim3 grid((unsigned)n_units), block(kT);
+template <int ODT, bool CB>
+hipError_t dequant_g(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
+                     int bits, const CbTable* book, hipStream_t s) {
     const int zdef = (1 << (bits - 1)) - 1;
-    switch (bits) {
-        case 2: k_dequant<2, ODT><<<grid, block, 0, s>>>(mats, ubeg, nmat, zdef); break;
-        case 3: k_dequant<3, ODT><<<grid, block, 0, s>>>(mats, ubeg, nmat, zdef); break;
-        case 4: k_dequant<4, ODT><<<grid, block, 0, s>>>(mats, ubeg, nmat, zdef); break;
-        default: k_dequant<8, ODT><<<grid, block, 0, s>>>(mats, ubeg, nmat, zdef); break;
-    }
-    return hipGetLastError();
+    return by_bits<CB>(bits, [&](auto b) {
+        k_dequant<decltype(b)::value, ODT, CB>
+            <<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, zdef, book);
+    });
 }
 
 }  // namespace
@@ -580,31 +707,52 @@ hipError_t recip(const RecipSeg* segs, const int64_t* ubeg, int nseg, int64_t n_
 }
 
 hipError_t quant_tile(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                      int dtype, int bits, hipStream_t s) {
+                      int dtype, int bits, const CbTable* book, int steps, hipStream_t s) {
     if (n_units <= 0) return hipSuccess;
-    return dtype == WOQ_BF16 ? quant_tile_dt<WOQ_BF16>(mats, ubeg, nmat, n_units, bits, s)
-                             : quant_tile_dt<WOQ_F32>(mats, ubeg, nmat, n_units, bits, s);
+    if (book)
+        return dtype == WOQ_BF16
+                   ? quant_tile_g<WOQ_BF16, true>(mats, ubeg, nmat, n_units, bits, book, steps, s)
+                   : quant_tile_g<WOQ_F32, true>(mats, ubeg, nmat, n_units, bits, book, steps, s);
+    return dtype == WOQ_BF16
+               ? quant_tile_g<WOQ_BF16, false>(mats, ubeg, nmat, n_units, bits, nullptr, 0, s)
+               : quant_tile_g<WOQ_F32, false>(mats, ubeg, nmat, n_units, bits, nullptr, 0, s);
 }
 
 hipError_t quant_wave(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                      int dtype, int bits, int nvl, hipStream_t s) {
+                      int dtype, int bits, int nvl, const CbTable* book, int steps,
+                      hipStream_t s) {
     if (n_units <= 0) return hipSuccess;
-    return dtype == WOQ_BF16 ? quant_wave_dt<WOQ_BF16>(mats, ubeg, nmat, n_units, bits, nvl, s)
-                             : quant_wave_dt<WOQ_F32>(mats, ubeg, nmat, n_units, bits, nvl, s);
+    if (book)
+        return dtype == WOQ_BF16
+                   ? quant_wave_nv<WOQ_BF16, true>(mats, ubeg, nmat, n_units, bits, nvl, book, steps, s)
+                   : quant_wave_nv<WOQ_F32, true>(mats, ubeg, nmat, n_units, bits, nvl, book, steps, s);
+    return dtype == WOQ_BF16
+               ? quant_wave_nv<WOQ_BF16, false>(mats, ubeg, nmat, n_units, bits, nvl, nullptr, 0, s)
+               : quant_wave_nv<WOQ_F32, false>(mats, ubeg, nmat, n_units, bits, nvl, nullptr, 0, s);
 }
 
 hipError_t quant_big(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                     int dtype, int bits, hipStream_t s) {
+                     int dtype, int bits, const CbTable* book, int steps, hipStream_t s) {
     if (n_units <= 0) return hipSuccess;
-    return dtype == WOQ_BF16 ? quant_big_dt<WOQ_BF16>(mats, ubeg, nmat, n_units, bits, s)
-                             : quant_big_dt<WOQ_F32>(mats, ubeg, nmat, n_units, bits, s);
+    if (book)
+        return dtype == WOQ_BF16
+                   ? quant_big_g<WOQ_BF16, true>(mats, ubeg, nmat, n_units, bits, book, steps, s)
+                   : quant_big_g<WOQ_F32, true>(mats, ubeg, nmat, n_units, bits, book, steps, s);
+    return dtype == WOQ_BF16
+               ? quant_big_g<WOQ_BF16, false>(mats, ubeg, nmat, n_units, bits, nullptr, 0, s)
+               : quant_big_g<WOQ_F32, false>(mats, ubeg, nmat, n_units, bits, nullptr, 0, s);
 }
 
 hipError_t dequant(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                   int out_dtype, int bits, hipStream_t s) {
+                   int out_dtype, int bits, const CbTable* book, hipStream_t s) {
     if (n_units <= 0) return hipSuccess;
-    return out_dtype == WOQ_BF16 ? dequant_dt<WOQ_BF16>(mats, ubeg, nmat, n_units, bits, s)
-                                 : dequant_dt<WOQ_F32>(mats, ubeg, nmat, n_units, bits, s);
+    if (book)
+        return out_dtype == WOQ_BF16
+                   ? dequant_g<WOQ_BF16, true>(mats, ubeg, nmat, n_units, bits, book, s)
+                   : dequant_g<WOQ_F32, true>(mats, ubeg, nmat, n_units, bits, book, s);
+    return out_dtype == WOQ_BF16
+               ? dequant_g<WOQ_BF16, false>(mats, ubeg, nmat, n_units, bits, nullptr, s)
+               : dequant_g<WOQ_F32, false>(mats, ubeg, nmat, n_units, bits, nullptr, s);
 }
 
 hipError_t ternary(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units, int dtype,

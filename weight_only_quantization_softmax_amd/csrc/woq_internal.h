@@ -136,6 +136,24 @@ struct QMat {
     int32_t group;      // group size for this matrix (cols for per-row groups)
 };
 
+// Non-uniform code book (code-book grid): up to kCbMax ascending levels,
+// their fp32 midpoints (+inf from the last midpoint on) and a table of
+// kCbCells cells of width 2 / kCbCells over [-1, 1].  For y whose true cell
+// floor((y + 1) * kCbCells / 2) is c or c + 1, at least cell[c].lo
+// midpoints lie below y and at most cell[c].lo + steps do, steps being the
+// largest such spread over all cells; cell[c].thr = mid[cell[c].lo].
+constexpr int kCbCells = 256;
+constexpr int kCbMax = 16;
+struct CbCell {
+    uint32_t lo;
+    float thr;
+};
+struct CbTable {
+    CbCell cell[kCbCells];
+    float mid[kCbMax];
+    float level[kCbMax];
+};
+
 // Lossless exponent code (DF11): one entry per matrix.
 constexpr int kDf11Chunk = 8192;   // weights per encoding work unit
 constexpr int kDf11MaxLen = 32;    // longest codeword (bits)

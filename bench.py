@@ -19,6 +19,11 @@ rocprofv3 FETCH_SIZE / WRITE_SIZE summary under profiles/, valid while the
 kernel source it was taken on is unchanged.  ``cpu_baseline`` times the CPU
 oracle on a bounded sample of the same workload.
 
+Outside the timed steps the line also carries ``dequant`` (the tier's codes
+decoded back to bf16), ``df11`` (the lossless code of the kept blocks) and
+``codebook`` (the same tier coded on the normal-quantile book and decoded),
+each timed with HIP events.
+
 Two "% of HBM peak" figures are given: input bytes / time, and compulsory
 traffic / time, where compulsory traffic is the entropy read of every
 weight, a second read of every weight that is quantised (the tiers need the
@@ -183,6 +188,54 @@ def dequant_rate(qp, mats, wl, stream, reps=5):
             "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def codebook_rate(qp, mats, wl, stream, reps=5):
+    """The non-uniform grid on the Sinkhorn tier: the same matrices, balancing
+    scales and width as the step, coded with the normal-quantile book
+    (quant_pack_codebook) and decoded back to bf16 (dequant_codebook), each
+    timed with HIP events.  Bytes: quantise reads 2 B per weight + s + t and
+    writes the codes + 4 B per group; dequantise the reverse."""
+    import torch
+    import weight_only_quantization_softmax_amd as woq
+
+    sel = [i for i, o in sorted(qp.outputs.items()) if o["action"] == "sinq"]
+    if not sel or wl.bits > 4:
+        return None
+    o = [qp.outputs[i] for i in sel]
+    ms_ = [mats[i] for i in sel]
+    rs, ct = [x["s"] for x in o], [x["t"] for x in o]
+    codes, scales = woq.quant_pack_codebook(ms_, wl.bits, wl.group, row_scale=rs, col_scale=ct,
+                                            stream=stream)
+    outs = [torch.empty_like(m) for m in ms_]
+    shapes = [tuple(m.shape) for m in ms_]
+
+    def quant():
+        woq.quant_pack_codebook(ms_, wl.bits, wl.group, row_scale=rs, col_scale=ct, codes=codes,
+                                scales=scales, stream=stream)
+
+    def dequant():
+        woq.dequant_codebook(shapes, codes, scales, wl.bits, wl.group, row_scale=rs, col_scale=ct,
+                             out_dtype=ms_[0].dtype, out=outs, stream=stream)
+
+    res = {"call": "quant_pack_codebook / dequant_codebook", "book": f"normal {wl.bits}-bit",
+           "matrices": len(sel)}
+    n = sum(m.numel() for m in ms_)
+    nbytes = (2 * n + sum(c.numel() + 4 * a.numel() for c, a in zip(codes, scales))
+              + 4 * sum(x.numel() + y.numel() for x, y in zip(rs, ct)))
+    for name, f in (("quant", quant), ("dequant", dequant)):
+        f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbs = nbytes / (ms / 1e3) / 1e9
+        res[name] = {"ms": round(ms, 4), "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    res["bytes"] = int(nbytes)
+    return res
+
+
 def df11_rate(mats, specs, acts, stream, reps=3):
     """Lossless code of the blocks the tiers keep in bf16: encode them (one
     df11_compress over all of them, outside the timed region, wall clock
@@ -312,6 +365,7 @@ def main() -> int:
     comp = compulsory_bytes(mats, specs, acts, wl.bits, wl.group)
     deq = dequant_rate(qp, mats, wl, stream)
     df11 = df11_rate(mats, specs, acts, stream)
+    book = codebook_rate(qp, mats, wl, stream)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -329,6 +383,7 @@ def main() -> int:
         "roofline": roof,
         "dequant": deq,
         "df11": df11,
+        "codebook": book,
         "calls": {k: {"ms_per_step": round(v["ms_per_step"], 3), "calls": v["calls"]}
                   for k, v in per_kind.items()},
     }

@@ -165,8 +165,9 @@ def test_moe_layers_tiered():
 
 def test_quality_report_rows():
     """The data-free report: one row per (scheme, K) plus ternary, all finite;
-    at every K the int4 g64 error is below the int3 g128 error, and each
-    error is within the per-element rounding bound max(s t delta) / 2."""
+    at every K the 4-bit g64 error is below the 3-bit g128 error on both
+    grids, and the largest error is within the per-element rounding bound
+    (max(s t delta) / 2 affine, max(s t a) G / 2 for the code book)."""
     from weight_only_quantization_softmax_amd import quality
     w = woqdata.random_matrix(256, 1024, 77, device=DEV)
     rows = quality.matrix_report(w)
@@ -183,6 +184,15 @@ def test_quality_report_rows():
             bound = (s[0][:, None].double() * t[0][None, :].double()
                      * scales[0].double().repeat_interleave(64, dim=1)).max().item() / 2
             assert by[("int4 g64", k, std)]["max_abs"] <= bound * (1 + 1e-5)
+            # the normal-quantile book: its error is within the bound that its
+            # widest level gap gives, s t a G / 2
+            assert by[("nf4 g64", k, std)]["rel_fro"] < by[("nf3 g128", k, std)]["rel_fro"]
+            _, a = woq.quant_pack_codebook([w], 4, 64, row_scale=s, col_scale=t)
+            lv = woq.codebook_normal(4)
+            gap = max(b - a_ for a_, b in zip(lv, lv[1:]))
+            bound = (s[0][:, None].double() * t[0][None, :].double()
+                     * a[0].double().repeat_interleave(64, dim=1)).max().item() * gap / 2
+            assert by[("nf4 g64", k, std)]["max_abs"] <= bound * (1 + 1e-5)
     assert 0 < by[("ternary", 0, "none")]["rel_fro"] < 1
 
 

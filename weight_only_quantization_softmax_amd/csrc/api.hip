@@ -379,8 +379,7 @@ int cb_build(const float* levels, int bits, CbTable* t) {
     for (int c = 0; c < kCbCells; ++c) {
         const double half = kCbCells / 2;
         const int lo = below(-1.0 + (c - 1) / half), hi = below(-1.0 + (c + 2) / half);
-        t->cell[c].lo = (uint32_t)lo;
-        t->cell[c].thr = t->mid[lo];
+        t->lo[c] = (uint8_t)lo;
         steps = std::max(steps, hi - lo);
     }
     return steps;

@@ -29,8 +29,8 @@
 // grid (template argument CB): a group is scaled by its largest |x| and each
 // value takes the nearest of 2^b caller-given levels (the [SINQ] page's
 // non-uniform option, same section as the low-bit codes).  The nearest level
-// is the number of level midpoints below y, found from a 256-cell table in
-// LDS and `steps` comparisons (one for the normal-quantile books).
+// is the number of level midpoints below y, found from a 256-byte cell table
+// in LDS and `steps` comparisons (one for the normal-quantile books).
 #include "launch.h"
 
 #include <math.h>
@@ -116,21 +116,17 @@ __device__ __forceinline__ CbParams cb_params(float lo, float hi) {
 // Copies the code book into LDS; every thread of the workgroup takes part,
 // before any early exit.  Called after the workgroup's data loads are issued,
 // so the table's load latency overlaps theirs.
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 template <bool CB>
 __device__ __forceinline__ const CbTable* stage_book(const CbTable* g) {
     if constexpr (!CB) {
         return nullptr;
     } else {
         __shared__ CbTable sh;
-        static_assert(kCbCells == kT, "one cell per thread");
-        const u32x2 c = gload<u32x2>(&g->cell[threadIdx.x]);
-        sh.cell[threadIdx.x].lo = c.x;
-        sh.cell[threadIdx.x].thr = __uint_as_float(c.y);
-        if (threadIdx.x < kCbMax) {
-            sh.mid[threadIdx.x] = gload<float>(g->mid + threadIdx.x);
-            sh.level[threadIdx.x] = gload<float>(g->level + threadIdx.x);
-        }
+        constexpr int kWords = sizeof(CbTable) / 4;
+        static_assert(kWords <= kT, "one word per thread");
+        if (threadIdx.x < kWords)
+            reinterpret_cast<uint32_t*>(&sh)[threadIdx.x] =
+                gload<uint32_t>(reinterpret_cast<const uint32_t*>(g) + threadIdx.x);
         __syncthreads();
         return &sh;
     }
@@ -156,26 +152,23 @@ __device__ __forceinline__ const float* stage_levels(const CbTable* g) {
 // a neighbour (the rounding moves it by at most 2^-16 of a cell), both of
 // which the table covers.  Clamping the bits to [2, 4) handles |y| up to
 // 1 + 2^-23 and keeps a NaN's index in the table, with no float-to-int
-// conversion.  The cell bounds the count to [cell.lo, cell.lo + steps];
-// the midpoints ascend, so each comparison either adds one or leaves the
+// conversion.  The cell bounds the count to [lo, lo + steps]; the midpoints
+// ascend, so each comparison with mid[code] either adds one or leaves the
 // code final.
 __device__ __forceinline__ void code8_cb(const float (&x)[8], float inv, const CbTable* bk,
                                          int steps, uint32_t (&c)[8]) {
     static_assert(kCbCells == 256, "8 mantissa bits index the table");
     constexpr int lo_bits = 0x40000000, hi_bits = 0x407FFFFF;  // 2.0f, largest float below 4
-    // Three phases, so that the eight table reads are in flight together.
+    // Phases, so that the eight reads of each kind are in flight together.
     float y[8];
-    CbCell e[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         y[k] = __fmul_rn(x[k], inv);
         const int zb = min(max(__float_as_int(__fadd_rn(y[k], 3.0f)), lo_bits), hi_bits);
-        e[k] = bk->cell[(zb >> 15) & (kCbCells - 1)];
+        c[k] = bk->lo[(zb >> 15) & (kCbCells - 1)];
     }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) c[k] = e[k].lo + (y[k] > e[k].thr ? 1u : 0u);
 #pragma nounroll
-    for (int st = 1; st < steps; ++st) {
+    for (int st = 0; st < steps; ++st) {
         float m[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) m[k] = bk->mid[c[k]];

@@ -139,20 +139,18 @@ struct QMat {
 // Non-uniform code book (code-book grid): up to kCbMax ascending levels,
 // their fp32 midpoints (+inf from the last midpoint on) and a table of
 // kCbCells cells of width 2 / kCbCells over [-1, 1].  For y whose true cell
-// floor((y + 1) * kCbCells / 2) is c or c + 1, at least cell[c].lo
-// midpoints lie below y and at most cell[c].lo + steps do, steps being the
-// largest such spread over all cells; cell[c].thr = mid[cell[c].lo].
+// floor((y + 1) * kCbCells / 2) is c or a neighbour, at least lo[c]
+// midpoints lie below y and at most lo[c] + steps do, steps being the
+// largest such spread over all cells.  One byte per cell keeps the whole
+// table in 64 LDS dwords, so random lookups meet few bank conflicts.
 constexpr int kCbCells = 256;
 constexpr int kCbMax = 16;
-struct CbCell {
-    uint32_t lo;
-    float thr;
-};
 struct CbTable {
-    CbCell cell[kCbCells];
     float mid[kCbMax];
     float level[kCbMax];
+    uint8_t lo[kCbCells];
 };
+static_assert(sizeof(CbTable) % 4 == 0, "copied as dwords");
 
 // Lossless exponent code (DF11): one entry per matrix.
 constexpr int kDf11Chunk = 8192;   // weights per encoding work unit

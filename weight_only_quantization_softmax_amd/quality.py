@@ -10,7 +10,11 @@ decoded with dequant_unpack, all through the library; the report gives, per
 matrix, scheme, K and std, the relative Frobenius error ||W - W'|| / ||W||
 and the largest absolute error, both computed in fp64 on the device.  K = 0
 is plain
-group-wise RTN (s = t = 1).  Ternary codes ([BitNet] "Khung Nguon
+group-wise RTN (s = t = 1).  Each width is reported on the affine grid
+(int, scale and zero-point per group) and on the normal-quantile code book
+(nf, the nearest of 2^b levels scaled by the group's largest |x|), the
+non-uniform option of [SINQ] section "Tiet kiem bo nho, toc do va chat
+luong trong thu nghiem".  Ternary codes ([BitNet] "Khung Nguon
 BitNet.cpp" (unite.ai), "He Thong Trong So Ternary") use the per-row scale
 and no balancing.
 
@@ -25,9 +29,13 @@ from typing import Dict, List, Sequence, Tuple
 
 import torch
 
-from . import dequant_unpack, quant_pack_groupwise, sinq_balance, ternary_pack
+from . import (dequant_codebook, dequant_unpack, quant_pack_codebook, quant_pack_groupwise,
+               sinq_balance, ternary_pack)
 
-SCHEMES: Tuple[Tuple[int, int], ...] = ((4, 64), (3, 128))
+# (bits, group, grid): grid "affine" (integer codes) or "normal" (the
+# normal-quantile code book)
+SCHEMES: Tuple[Tuple[int, int, str], ...] = ((4, 64, "affine"), (3, 128, "affine"),
+                                             (4, 64, "normal"), (3, 128, "normal"))
 ITERS: Tuple[int, ...] = (0, 4, 16, 24)
 # the std used by the balancing: centred (the pass's reading) or the
 # uncentred root mean square
@@ -41,7 +49,22 @@ def _errors(w: torch.Tensor, wq: torch.Tensor) -> Dict[str, float]:
             "max_abs": d.abs().max().item()}
 
 
-def matrix_report(w: torch.Tensor, schemes: Sequence[Tuple[int, int]] = SCHEMES,
+def scheme_name(bits: int, group: int, grid: str) -> str:
+    return f"{'int' if grid == 'affine' else 'nf'}{bits} g{group}"
+
+
+def _round_trip(w, bits, group, grid, s, t):
+    shape = tuple(w.shape)
+    if grid == "affine":
+        codes, scales, zeros = quant_pack_groupwise([w], bits, group, row_scale=s, col_scale=t)
+        return dequant_unpack([shape], codes, scales, bits, group, zeros=zeros, row_scale=s,
+                              col_scale=t, out_dtype=torch.float32)[0]
+    codes, scales = quant_pack_codebook([w], bits, group, row_scale=s, col_scale=t)
+    return dequant_codebook([shape], codes, scales, bits, group, row_scale=s, col_scale=t,
+                            out_dtype=torch.float32)[0]
+
+
+def matrix_report(w: torch.Tensor, schemes: Sequence[Tuple[int, int, str]] = SCHEMES,
                   iters: Sequence[int] = ITERS, ternary: bool = True,
                   stds: Sequence[str] = STDS) -> List[dict]:
     """Rows of the report for one device-resident matrix (bf16 or fp32):
@@ -49,15 +72,12 @@ def matrix_report(w: torch.Tensor, schemes: Sequence[Tuple[int, int]] = SCHEMES,
     std "none"), and the ternary row."""
     rows = []
     shape = tuple(w.shape)
-    for bits, group in schemes:
+    for bits, group, grid in schemes:
         for k in iters:
             for std in (stds if k else ("none",)):
                 s, t = sinq_balance([w], k, rms=(std == "rms"))
-                codes, scales, zeros = quant_pack_groupwise([w], bits, group, row_scale=s,
-                                                            col_scale=t)
-                wq = dequant_unpack([shape], codes, scales, bits, group, zeros=zeros, row_scale=s,
-                                    col_scale=t, out_dtype=torch.float32)[0]
-                rows.append({"scheme": f"int{bits} g{group}", "iters": k, "std": std,
+                wq = _round_trip(w, bits, group, grid, s, t)
+                rows.append({"scheme": scheme_name(bits, group, grid), "iters": k, "std": std,
                              **_errors(w, wq)})
     if ternary:
         codes, beta = ternary_pack([w])

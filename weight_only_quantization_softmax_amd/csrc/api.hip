@@ -352,11 +352,11 @@ QLayout q_layout(const woq_mat* mats, int32_t n, int op, int32_t group,
 }
 
 // Code-book table from 2^bits levels (finite, strictly ascending): fp32
-// midpoints, +inf padding, and per cell c of [-1, 1] (width 1/128, left
-// edge E_c = -1 + c/128) the count of midpoints certainly below y.  The
-// kernel's cell index for y (mantissa bits 22..15 of the fp32 sum y + 3,
-// clamped to [2, 4)) is the true cell floor((y + 1) * 128) or a neighbour,
-// and |y| <= 1 + 2^-23, so y lies in [E_{c-1}, E_{c+2}):
+// midpoints, +inf padding, and per cell c of [-1, 1] (width 2 / kCbCells,
+// left edge E_c = -1 + 2c / kCbCells) the count of midpoints certainly
+// below y.  The kernel's cell index for y (mantissa bits of the fp32 sum
+// y + 3, clamped to [2, 4)) is the true cell floor((y + 1) * kCbCells / 2)
+// or a neighbour, and |y| <= 1 + 2^-23, so y lies in [E_{c-1}, E_{c+2}):
 // midpoints below E_{c-1} are below y and midpoints at or above E_{c+2} are
 // not.  Returns the comparisons per value (the widest spread), or -1 for an
 // invalid book.

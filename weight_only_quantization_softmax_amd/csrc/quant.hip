@@ -29,7 +29,7 @@
 // grid (template argument CB): a group is scaled by its largest |x| and each
 // value takes the nearest of 2^b caller-given levels (the [SINQ] page's
 // non-uniform option, same section as the low-bit codes).  The nearest level
-// is the number of level midpoints below y, found from a 256-byte cell table
+// is the number of level midpoints below y, found from a 128-byte cell table
 // in LDS and `steps` comparisons (one for the normal-quantile books).
 #include "launch.h"
 
@@ -147,9 +147,9 @@ __device__ __forceinline__ const float* stage_levels(const CbTable* g) {
 
 // code = number of midpoints m_k with y > m_k (the nearest level; a tie
 // goes to the lower one).  The cell index comes from the bits of z = y + 3
-// (one rounding): z in [2, 4) has a fixed exponent, so mantissa bits 22..15
-// are floor((z - 2) * 128), which is the true cell floor((y + 1) * 128) or
-// a neighbour (the rounding moves it by at most 2^-16 of a cell), both of
+// (one rounding): z in [2, 4) has a fixed exponent, so mantissa bits 22..16
+// are floor((z - 2) * 64), which is the true cell floor((y + 1) * 64) or a
+// neighbour (the rounding moves it by at most 2^-17 of a cell), both of
 // which the table covers.  Clamping the bits to [2, 4) handles |y| up to
 // 1 + 2^-23 and keeps a NaN's index in the table, with no float-to-int
 // conversion.  The cell bounds the count to [lo, lo + steps]; the midpoints
@@ -157,7 +157,7 @@ __device__ __forceinline__ const float* stage_levels(const CbTable* g) {
 // code final.
 __device__ __forceinline__ void code8_cb(const float (&x)[8], float inv, const CbTable* bk,
                                          int steps, uint32_t (&c)[8]) {
-    static_assert(kCbCells == 256, "8 mantissa bits index the table");
+    static_assert(kCbCells == 128, "7 mantissa bits index the table");
     constexpr int lo_bits = 0x40000000, hi_bits = 0x407FFFFF;  // 2.0f, largest float below 4
     // Phases, so that the eight reads of each kind are in flight together.
     float y[8];
@@ -165,7 +165,7 @@ __device__ __forceinline__ void code8_cb(const float (&x)[8], float inv, const C
     for (int k = 0; k < 8; ++k) {
         y[k] = __fmul_rn(x[k], inv);
         const int zb = min(max(__float_as_int(__fadd_rn(y[k], 3.0f)), lo_bits), hi_bits);
-        c[k] = bk->lo[(zb >> 15) & (kCbCells - 1)];
+        c[k] = bk->lo[(zb >> 16) & (kCbCells - 1)];
     }
 #pragma nounroll
     for (int st = 0; st < steps; ++st) {

@@ -142,8 +142,8 @@ struct QMat {
 // floor((y + 1) * kCbCells / 2) is c or a neighbour, at least lo[c]
 // midpoints lie below y and at most lo[c] + steps do, steps being the
 // largest such spread over all cells.  One byte per cell keeps the whole
-// table in 64 LDS dwords, so random lookups meet few bank conflicts.
-constexpr int kCbCells = 256;
+// table in 32 LDS dwords, one per bank, so random lookups do not conflict.
+constexpr int kCbCells = 128;
 constexpr int kCbMax = 16;
 struct CbTable {
     float mid[kCbMax];

@@ -352,7 +352,8 @@ def main() -> int:
         # one read of every weight per iteration (row scales, column partials
         # and the column reduction are not counted)
         alg = d["bytes"] * wl.iters
-        kernel = "sinq_balance (K fused row/column sweeps + column reductions)"
+        kernel = ("sinq_balance (K fused row/column sweeps + column reductions; the tier's "
+                  "wave-form and wider matrices as two concurrent calls)")
         traffic = measured_traffic() if args.workload == TRAFFIC_WORKLOAD else None
     else:
         alg = d["bytes"]

@@ -92,7 +92,8 @@ typedef struct woq_mat {
 const char* woq_status_string(int32_t status);
 
 /* Workspace bytes needed by operation `op` on these matrices.  `group` is
- * used by WOQ_OP_QUANT / WOQ_OP_DEQUANT only.  Writes *bytes; returns status. */
+ * used by WOQ_OP_QUANT / WOQ_OP_DEQUANT only.  WOQ_OP_SINQ covers every
+ * sinq_balance_ex flag.  Writes *bytes; returns status. */
 int32_t woq_workspace_size(int32_t op, const woq_mat* mats, int32_t n_mats,
                            int32_t group, size_t* bytes);
 
@@ -141,11 +142,23 @@ int32_t sinq_balance(const woq_mat* mats, int32_t n_mats, int32_t iters,
                      float* const* row_scale, float* const* col_scale,
                      void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* sinq_balance with options.  flags: 0 (as sinq_balance) or WOQ_SINQ_RMS:
- *  the uncentred root mean square sqrt(mean x^2) in place of the centred std
- *  in both steps (a zero line gets scale 1), for comparing the two readings
- *  of the std in a quality report.  Other bits: WOQ_ERR_VALUE. */
+/* sinq_balance with options.  flags: 0 (as sinq_balance) or a combination of
+ *  WOQ_SINQ_RMS     the uncentred root mean square sqrt(mean x^2) in place of
+ *                   the centred std in both steps (a zero line gets scale 1),
+ *                   for comparing the two readings of the std in a quality
+ *                   report;
+ *  WOQ_SINQ_SHARED  the call will run concurrently with other work on the
+ *                   same GPU (typically a second sinq_balance on another
+ *                   stream): row strips are planned for half of the GPU's
+ *                   resident workgroups instead of all of them.  Scheduling
+ *                   only: the scales are those of the same iteration, with
+ *                   column partials summed over different strips (within
+ *                   fp32 rounding of the unflagged call; deterministic for a
+ *                   given flag).  Each concurrent call needs its own
+ *                   workspace.
+ *  Other bits: WOQ_ERR_VALUE. */
 #define WOQ_SINQ_RMS 1
+#define WOQ_SINQ_SHARED 2
 int32_t sinq_balance_ex(const woq_mat* mats, int32_t n_mats, int32_t iters, int32_t flags,
                         float* const* row_scale, float* const* col_scale,
                         void* ws, size_t ws_bytes, hipStream_t stream);

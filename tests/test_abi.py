@@ -105,7 +105,10 @@ def test_entry_points_reject_before_any_hip_call():
     assert _ws_size(_lib.OP_SINQ, _mat(rows=2, cols=32768))[0] == 0
     assert lib.sinq_balance(m, 1, 4, pp, pp, FAKE, 8, None) == 6
     # sinq_balance_ex: unknown flag bits, then the same checks as sinq_balance
-    assert lib.sinq_balance_ex(m, 1, 4, 2, pp, pp, FAKE, 1 << 30, None) == 11
+    assert lib.sinq_balance_ex(m, 1, 4, 4, pp, pp, FAKE, 1 << 30, None) == 11
+    assert lib.sinq_balance_ex(m, 1, 4, 8 | _lib.WOQ_SINQ_SHARED, pp, pp, FAKE, 1 << 30, None) == 11
+    assert lib.sinq_balance_ex(m, 1, 4, _lib.WOQ_SINQ_SHARED, pp, pp, FAKE, 8, None) == 6
+    assert lib.sinq_balance_ex(m, 1, -1, _lib.WOQ_SINQ_SHARED | _lib.WOQ_SINQ_RMS, pp, pp, FAKE, 1 << 30, None) == 5
     assert lib.sinq_balance_ex(m, 1, -1, _lib.WOQ_SINQ_RMS, pp, pp, FAKE, 1 << 30, None) == 5
     assert lib.sinq_balance_ex(m, 1, 4, _lib.WOQ_SINQ_RMS, nullpp, pp, FAKE, 1 << 30, None) == 1
     # quant: bits, group, NULL outputs

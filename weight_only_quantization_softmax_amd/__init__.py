@@ -103,10 +103,12 @@ def ewq_block_entropy(mats: Sequence[torch.Tensor], block_id: Optional[Sequence[
     return {"h_mat": h_mat, "h_block": h_block, "stats": stats, "tier": tier, "order": order}
 
 
-def sinq_balance(mats: Sequence[torch.Tensor], iters: int, *, rms: bool = False, row_scale=None,
-                 col_scale=None, ws=None, stream=None):
-    """Row scales s [rows] and column scales t [cols] (fp32) per matrix
-    (``rms``: root mean square in place of the centred std, sinq_balance_ex)."""
+def sinq_balance(mats: Sequence[torch.Tensor], iters: int, *, rms: bool = False,
+                 shared: bool = False, row_scale=None, col_scale=None, ws=None, stream=None):
+    """Row scales s [rows] and column scales t [cols] (fp32) per matrix.
+    ``rms``: root mean square in place of the centred std; ``shared``: the
+    call runs beside another on the same GPU, strips planned for half of it
+    (both through sinq_balance_ex)."""
     lib = _lib.load()
     dev = mats[0].device
     arr = _mats(mats)
@@ -115,8 +117,9 @@ def sinq_balance(mats: Sequence[torch.Tensor], iters: int, *, rms: bool = False,
     if col_scale is None:
         col_scale = [torch.empty(m.shape[1], dtype=torch.float32, device=dev) for m in mats]
     ws = _workspace(_lib.OP_SINQ, mats, 0, ws, dev)
-    if rms:
-        st = lib.sinq_balance_ex(arr, len(mats), int(iters), _lib.WOQ_SINQ_RMS, _ptrs(row_scale),
+    flags = (_lib.WOQ_SINQ_RMS if rms else 0) | (_lib.WOQ_SINQ_SHARED if shared else 0)
+    if flags:
+        st = lib.sinq_balance_ex(arr, len(mats), int(iters), flags, _ptrs(row_scale),
                                  _ptrs(col_scale), ws.data_ptr(), ws.numel(), _stream(stream))
         _lib.check("sinq_balance_ex", st)
     else:

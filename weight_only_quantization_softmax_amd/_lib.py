@@ -20,6 +20,7 @@ STATUS = {
 }
 WOQ_F32, WOQ_BF16 = 0, 1
 WOQ_SINQ_RMS = 1
+WOQ_SINQ_SHARED = 2
 OP_ENTROPY, OP_SINQ, OP_QUANT, OP_DEQUANT, OP_TERNARY = 1, 2, 3, 4, 5
 OP_DF11_HIST, OP_DF11_ENCODE, OP_DF11_DECODE = 6, 7, 8
 

@@ -138,7 +138,9 @@ struct SinqLayout {
     std::vector<size_t> u, part;     // per table position
 };
 
-SinqLayout sinq_layout(const woq_mat* mats, int32_t n) {
+// shared: the call runs beside another on the same GPU (WOQ_SINQ_SHARED), so
+// strips are planned for half of the resident workgroup slots.
+SinqLayout sinq_layout(const woq_mat* mats, int32_t n, bool shared) {
     SinqLayout L;
     // launch sets: same dtype and same (threads, vectors per thread)
     std::vector<int> idx(n);
@@ -178,7 +180,8 @@ SinqLayout sinq_layout(const woq_mat* mats, int32_t n) {
         const int waves_per_wg = g.sh.mode == 1 ? 4 : g.sh.nt / 64;
         const int waves_per_cu =
             g.sh.mode == 1 ? 4 * sinq_wave_occupancy(g.dtype, g.sh.nv) : kSinqWavesPerCU;
-        const int64_t cap = (int64_t)kSinqCUs * std::max(1, waves_per_cu / waves_per_wg);
+        const int64_t full = (int64_t)kSinqCUs * std::max(1, waves_per_cu / waves_per_wg);
+        const int64_t cap = shared ? std::max<int64_t>(1, full / 2) : full;
         int64_t total_rows = 0;
         for (int k = p; k < q; ++k) total_rows += mats[idx[k]].rows;
         // strip height (in tiles) of matrix k when its workgroups hold at
@@ -477,7 +480,9 @@ int32_t woq_workspace_size(int32_t op, const woq_mat* mats, int32_t n_mats, int3
         case WOQ_OP_SINQ:
             for (int32_t i = 0; i < n_mats; ++i)
                 if (mats[i].cols > kSinqMaxCols) return WOQ_ERR_SHAPE;
-            *bytes = sinq_layout(mats, n_mats).total;
+            // either plan (with or without WOQ_SINQ_SHARED)
+            *bytes = std::max(sinq_layout(mats, n_mats, false).total,
+                              sinq_layout(mats, n_mats, true).total);
             return WOQ_OK;
         case WOQ_OP_QUANT: {
             if ((st = check_group(mats, n_mats, group, true))) return st;
@@ -575,10 +580,10 @@ int32_t sinq_balance_ex(const woq_mat* mats, int32_t n_mats, int32_t iters, int3
     for (int32_t i = 0; i < n_mats; ++i)
         if (mats[i].cols > kSinqMaxCols) return WOQ_ERR_SHAPE;
     if (iters < 0 || iters > kMaxIters) return WOQ_ERR_ITERS;
-    if (flags & ~WOQ_SINQ_RMS) return WOQ_ERR_VALUE;
+    if (flags & ~(WOQ_SINQ_RMS | WOQ_SINQ_SHARED)) return WOQ_ERR_VALUE;
     if ((st = check_ptrs(reinterpret_cast<const void* const*>(row_scale), n_mats, 4))) return st;
     if ((st = check_ptrs(reinterpret_cast<const void* const*>(col_scale), n_mats, 4))) return st;
-    const SinqLayout L = sinq_layout(mats, n_mats);
+    const SinqLayout L = sinq_layout(mats, n_mats, (flags & WOQ_SINQ_SHARED) != 0);
     if ((st = check_ws(ws, ws_bytes, L.total))) return st;
 
     if (iters == 0) {

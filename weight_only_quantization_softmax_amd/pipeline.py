@@ -54,8 +54,43 @@ class _Call:
     def __init__(self, name: str, fn, args, keep, kind: str, nbytes: int):
         self.name, self.fn, self.args, self.keep, self.kind, self.nbytes = name, fn, args, keep, kind, nbytes
 
-    def __call__(self, stream_handle):
+    def __call__(self, stream_handle, stream=None):
         _lib.check(self.name, self.fn(*self.args, stream_handle))
+
+
+def _wave_form(m: torch.Tensor) -> bool:
+    """Rows the library's Sinkhorn sweep holds in one wave (at most 4096 bf16
+    or 1536 fp32 columns); wider rows take a workgroup per row strip."""
+    return m.shape[1] <= (4096 if m.dtype == torch.bfloat16 else 1536)
+
+
+class _SplitSinq:
+    """The Sinkhorn step of one tier as two concurrent sinq_balance calls:
+    the wave-form matrices on the caller's stream and the wider ones on a
+    second stream (default priority) with WOQ_SINQ_SHARED, so that the two
+    kernels share every CU instead of running one after the other (the
+    wide rows' sweep waits on workgroup barriers, the narrow rows' on HBM).
+    The second stream starts after, and the caller's stream continues after,
+    everything the other holds."""
+
+    kind = "sinq"
+
+    def __init__(self, narrow: _Call, wide: _Call, side: torch.cuda.Stream):
+        self.narrow, self.wide, self.side = narrow, wide, side
+        self.nbytes = narrow.nbytes + wide.nbytes
+        self.name = "sinq_balance x2"
+        self._fork = torch.cuda.Event()
+        self._join = torch.cuda.Event()
+
+    def __call__(self, stream_handle, stream=None):
+        if stream is None:
+            raise ValueError("the split Sinkhorn call needs the caller's torch stream")
+        self._fork.record(stream)
+        self.side.wait_event(self._fork)
+        self.wide(self.side.cuda_stream)
+        self.narrow(stream_handle)
+        self._join.record(self.side)
+        stream.wait_event(self._join)
 
 
 class QuantPass:
@@ -89,6 +124,7 @@ class QuantPass:
         self.outputs: Dict[int, dict] = {}
         self.bytes_in = sum(m.numel() * m.element_size() for m in self.mats)
         self.budget_bytes = budget_bytes
+        self._side: Optional[torch.cuda.Stream] = None   # second stream of the split Sinkhorn step
         self.last_actions: Optional[List[str]] = None
         self.last_budget: Optional[tuple] = None   # (total bytes, fits)
 
@@ -126,16 +162,32 @@ class QuantPass:
             cur_b += b
         if cur:
             batches.append(cur)
+        def sinq_call(ks, flags):
+            bm = [mats[k] for k in ks]
+            arr = _mat_arr(bm)
+            sp = _lib.ptr_array(s[k].data_ptr() for k in ks)
+            tp = _lib.ptr_array(t[k].data_ptr() for k in ks)
+            ws = _ws(_lib.OP_SINQ, bm, 0, dev)
+            nb = sum(m.numel() * m.element_size() for m in bm)
+            return _Call("sinq_balance_ex", self.lib.sinq_balance_ex,
+                         (arr, len(bm), self.iters, flags, sp, tp, ws.data_ptr(), ws.numel()),
+                         (arr, sp, tp, ws), "sinq", nb)
+
         for bk in batches:
             bm = [mats[k] for k in bk]
             arr = _mat_arr(bm)
             sp = _lib.ptr_array(s[k].data_ptr() for k in bk)
             tp = _lib.ptr_array(t[k].data_ptr() for k in bk)
-            ws = _ws(_lib.OP_SINQ, bm, 0, dev)
             nb = sum(m.numel() * m.element_size() for m in bm)
-            calls.append(_Call("sinq_balance", self.lib.sinq_balance,
-                               (arr, len(bm), self.iters, sp, tp, ws.data_ptr(), ws.numel()),
-                               (arr, sp, tp, ws), "sinq", nb))
+            narrow = [k for k in bk if _wave_form(mats[k])]
+            wide = [k for k in bk if not _wave_form(mats[k])]
+            if narrow and wide:
+                if self._side is None:
+                    self._side = torch.cuda.Stream(device=dev)
+                calls.append(_SplitSinq(sinq_call(narrow, 0),
+                                        sinq_call(wide, _lib.WOQ_SINQ_SHARED), self._side))
+            else:
+                calls.append(sinq_call(bk, 0))
             cp = _lib.ptr_array(codes[k].data_ptr() for k in bk)
             scp = _lib.ptr_array(scales[k].data_ptr() for k in bk)
             zp = _lib.ptr_array(zeros[k].data_ptr() for k in bk)
@@ -284,8 +336,8 @@ class QuantPass:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-                c(h)
+                c(h, stream)
                 e1.record(stream)
                 timers.setdefault(c.kind, []).append((e0, e1, c.nbytes))
             else:
-                c(h)
+                c(h, stream)

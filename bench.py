@@ -200,6 +200,20 @@ def codebook_rate(qp, mats, wl, stream, reps=5):
     sel = [i for i, o in sorted(qp.outputs.items()) if o["action"] == "sinq"]
     if not sel or wl.bits > 4:
         return None
+    # the matrices whose codes, scales and decoded copy fit in 90% of the free
+    # memory (all of them except on the 70B stack)
+    torch.cuda.synchronize()
+    free = 0.9 * torch.cuda.mem_get_info()[0]
+    need, fit = 0, []
+    for i in sel:
+        m = mats[i]
+        need += m.numel() * (m.element_size() + wl.bits / 8) + 4 * m.numel() / wl.group
+        if need > free:
+            break
+        fit.append(i)
+    if not fit:
+        return None
+    sel = fit
     o = [qp.outputs[i] for i in sel]
     ms_ = [mats[i] for i in sel]
     rs, ct = [x["s"] for x in o], [x["t"] for x in o]
@@ -217,7 +231,7 @@ def codebook_rate(qp, mats, wl, stream, reps=5):
                              out_dtype=ms_[0].dtype, out=outs, stream=stream)
 
     res = {"call": "quant_pack_codebook / dequant_codebook", "book": f"normal {wl.bits}-bit",
-           "matrices": len(sel)}
+           "matrices": len(sel), "of": sum(1 for o_ in qp.outputs.values() if o_["action"] == "sinq")}
     n = sum(m.numel() for m in ms_)
     nbytes = (2 * n + sum(c.numel() + 4 * a.numel() for c, a in zip(codes, scales))
               + 4 * sum(x.numel() + y.numel() for x, y in zip(rs, ct)))

@@ -85,10 +85,11 @@ class _SplitSinq:
     def __call__(self, stream_handle, stream=None):
         if stream is None:
             raise ValueError("the split Sinkhorn call needs the caller's torch stream")
+        # the wave-form call is the longer one: it is enqueued first
         self._fork.record(stream)
+        self.narrow(stream_handle)
         self.side.wait_event(self._fork)
         self.wide(self.side.cuda_stream)
-        self.narrow(stream_handle)
         self._join.record(self.side)
         stream.wait_event(self._join)
 

@@ -181,6 +181,47 @@ def test_sinq_deterministic():
     assert torch.equal(a[0][0], b[0][0]) and torch.equal(a[1][0], b[1][0])
 
 
+@pytest.mark.parametrize("iters", [1, 16])
+def test_sinq_shared_plan_matches_oracle(iters):
+    """WOQ_SINQ_SHARED plans taller strips (half of the GPU): the same scales
+    to within the same bar, and within fp32 rounding of the unflagged call."""
+    mats = [_rm(r, c, 20 + i, dt, frac=0.01, mult=20.0) for i, ((r, c), dt) in enumerate(SINQ_CASES)]
+    s, t = woq.sinq_balance(mats, iters, shared=True)
+    s0, t0 = woq.sinq_balance(mats, iters)
+    for i, m in enumerate(mats):
+        s_ref, t_ref = oracle.sinkhorn_std(_np(m), iters)
+        np.testing.assert_allclose(s[i].cpu().numpy(), s_ref, rtol=1e-4, err_msg=str(SINQ_CASES[i]))
+        np.testing.assert_allclose(t[i].cpu().numpy(), t_ref, rtol=1e-4, err_msg=str(SINQ_CASES[i]))
+        np.testing.assert_allclose(s[i].cpu().numpy(), s0[i].cpu().numpy(), rtol=2e-5)
+        np.testing.assert_allclose(t[i].cpu().numpy(), t0[i].cpu().numpy(), rtol=2e-5)
+
+
+def test_sinq_concurrent_calls_on_two_streams():
+    """The pipeline's split: wave-form matrices on one stream, wider ones with
+    WOQ_SINQ_SHARED on another, each with its own workspace.  Every result
+    equals the same call made alone, bit for bit, on every repetition."""
+    narrow = [_rm(1024, 4096, 31), _rm(4096, 4096, 32), _rm(300, 1024, 33)]
+    wide = [_rm(4096, 14336, 34), _rm(96, 14336, 35)]
+    ref_n = woq.sinq_balance(narrow, 16)
+    ref_w = woq.sinq_balance(wide, 16, shared=True)
+    from weight_only_quantization_softmax_amd import _lib
+    ws_n = torch.empty(woq.workspace_size(_lib.OP_SINQ, narrow), dtype=torch.uint8, device=DEV)
+    ws_w = torch.empty(woq.workspace_size(_lib.OP_SINQ, wide), dtype=torch.uint8, device=DEV)
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    for rep in range(3):
+        sn = [torch.empty_like(x) for x in ref_n[0]]
+        tn = [torch.empty_like(x) for x in ref_n[1]]
+        sw = [torch.empty_like(x) for x in ref_w[0]]
+        tw = [torch.empty_like(x) for x in ref_w[1]]
+        side.wait_stream(main)
+        woq.sinq_balance(narrow, 16, row_scale=sn, col_scale=tn, ws=ws_n, stream=main)
+        woq.sinq_balance(wide, 16, shared=True, row_scale=sw, col_scale=tw, ws=ws_w, stream=side)
+        main.wait_stream(side)
+        torch.cuda.synchronize()
+        for a, b in zip(sn + tn + sw + tw, ref_n[0] + ref_n[1] + ref_w[0] + ref_w[1]):
+            assert torch.equal(a, b), rep
+
+
 # ------------------------------------------------------------------ quant
 QUANT_CASES = [  # (rows, cols, bits, group, dtype)
     (16, 256, 4, 64, torch.bfloat16), (7, 96, 4, 32, torch.bfloat16),

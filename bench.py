@@ -296,6 +296,44 @@ def df11_rate(mats, specs, acts, stream, reps=3):
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def torch_reference(reps=20):
+    """Streaming rates of torch's stock kernels on the box (not the
+    library's), for comparison with the library's kernels: a 1 GiB device
+    copy (read + write), 1 GiB read-only reductions, and the same reduction
+    over a 128 MiB buffer that stays in the 256 MB Infinity Cache across
+    reps.  HIP events on the current stream, after one untimed run each."""
+    import torch
+    torch.cuda.set_device(0)
+    n = 1 << 30
+    a = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    small = a[: (128 << 20) // 2]
+    out = torch.empty((), dtype=torch.float32, device="cuda")
+    outb = torch.empty((), dtype=torch.bfloat16, device="cuda")
+
+    def rate(f, nbytes, r):
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(r):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / r
+        return {"ms": round(ms, 4), "GBps": round(nbytes / (ms / 1e3) / 1e9, 1)}
+
+    res = {
+        "copy_1GiB (read + write)": rate(lambda: b.copy_(a), 2 * n, reps),
+        "sum_1GiB (read)": rate(lambda: torch.sum(a, dim=0, dtype=torch.float32, out=out), n, reps),
+        "amax_1GiB (read)": rate(lambda: torch.amax(a, dim=0, out=outb), n, reps),
+        "sum_128MiB_cache_resident (read)": rate(lambda: torch.sum(small, dim=0, dtype=torch.float32, out=out),
+                                                 128 << 20, 10 * reps),
+    }
+    print(json.dumps({"torch_reference": res, "torch": torch.__version__}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,7 +344,11 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one device copy of this size first (counter calibration)")
+    ap.add_argument("--torch-reference", action="store_true",
+                    help="only measure torch's stock streaming kernels on the box")
     args = ap.parse_args()
+    if args.torch_reference:
+        return torch_reference()
     if args.gpus != 1:
         print(f"bench.py: this pass runs on one GPU; --gpus {args.gpus} is not supported "
               "(blocks are independent after tiering; see the sharding design)", file=sys.stderr)

@@ -51,6 +51,9 @@ CASES = [  # (rows, cols, bits, group, dtype)
     (10, 1800, 4, 600, torch.bfloat16), (20, 2048, 4, 1024, torch.bfloat16),
     (5, 4096, 3, 0, torch.bfloat16), (4, 3072, 4, 0, torch.float32),
     (4, 16384, 4, 8192, torch.bfloat16), (3, 14336, 4, 0, torch.bfloat16),
+    # fp32 groups wider than one wave (one workgroup per group); 2-bit codes
+    # over ragged 2048-column tiles
+    (3, 8192, 3, 0, torch.float32), (2, 16384, 4, 16384, torch.float32), (11, 2600, 2, 8, torch.bfloat16),
 ]
 
 

@@ -8,7 +8,8 @@ size without running the oracle on 2^31 weights:
   - Sinkhorn: every row (column) of W repeats a row (column) of B, so s and t
     are B's tiled; equal lines are reduced in the same order, so the tiles
     agree bit for bit;
-  - codes: rows are quantised independently, so code tiles repeat too;
+  - codes (affine and code-book grids): rows are quantised independently,
+    so code tiles repeat too;
   - the lossless code: W's exponent histogram is k times B's.
 B itself goes through the oracle.
 """
@@ -73,6 +74,21 @@ def test_sinkhorn_and_codes_of_a_2_31_matrix(tiled):
     last = out[(KR - 1) * RB:, (KC - 1) * CB:]          # the tile farthest into the buffer
     assert np.array_equal(last.cpu().numpy(), ref)
     del out, codes, scales, zeros
+
+    # the code-book grid on the same matrix: code tiles repeat, the first
+    # equals the oracle on B, the last tile decodes exactly
+    codes, scales = woq.quant_pack_codebook([w], 4, 64, row_scale=s, col_scale=t)
+    c = codes[0].view(KR, RB, KC, CB // 2)
+    assert torch.equal(c, c[:1, :, :1].expand_as(c))
+    lv = oracle.codebook.normal_levels(4)
+    qc, ac = oracle.codebook.quantize_codebook_f32(_np(b), sv[0].cpu().numpy(), tv[0].cpu().numpy(), 4, 64, lv)
+    assert np.array_equal(c[0, :, 0].cpu().numpy(), oracle.pack_codes(qc, 4))
+    av = scales[0].view(KR, RB, KC, CB // 64)
+    assert np.array_equal(av[KR - 1, :, KC - 1].cpu().numpy().view(np.uint32), ac.view(np.uint32))
+    out = woq.dequant_codebook([tuple(w.shape)], codes, scales, 4, 64, row_scale=s, col_scale=t)[0]
+    ref = oracle.codebook.dequantize_codebook_f32(qc, ac, sv[0].cpu().numpy(), tv[0].cpu().numpy(), 64, lv)
+    assert np.array_equal(out[(KR - 1) * RB:, (KC - 1) * CB:].cpu().numpy(), ref)
+    del out, codes, scales
 
 
 def test_lossless_code_of_a_2_31_matrix(tiled):

@@ -327,18 +327,25 @@ def df11_encode(mats: Sequence[torch.Tensor], codes, *, ws=None, stream=None):
     lib = _lib.load()
     dev = mats[0].device
     arr = _mats(mats)
-    outs = []
+    # every matrix's tables and code lengths in one host-to-device copy
+    host = np.concatenate([np.concatenate([np.ascontiguousarray(c["tables"], dtype=np.uint8).reshape(-1),
+                                           np.ascontiguousarray(c["code_len"], dtype=np.uint8)])
+                           for c in codes])
+    meta = torch.from_numpy(host).to(dev)
+    outs, off = [], 0
     for m, c in zip(mats, codes):
         _, eb, gb, nb = df11_buffer_sizes(m.numel(), c["total_bits"])
+        nt = int(c["tables"].shape[0])
         outs.append({
             "enc": torch.empty(eb, dtype=torch.uint8, device=dev),
             "sm": torch.empty(m.numel(), dtype=torch.uint8, device=dev),
             "gaps": torch.empty(gb, dtype=torch.uint8, device=dev),
             "block_pos": torch.empty(nb + 1, dtype=torch.int32, device=dev),
-            "tables": torch.from_numpy(np.ascontiguousarray(c["tables"]).reshape(-1)).to(dev),
-            "code_len": torch.from_numpy(np.ascontiguousarray(c["code_len"])).to(dev),
-            "n_tables": int(c["tables"].shape[0]), "total_bits": int(c["total_bits"]),
+            "tables": meta[off:off + 256 * nt],
+            "code_len": meta[off + 256 * nt:off + 256 * nt + 256],
+            "n_tables": nt, "total_bits": int(c["total_bits"]),
             "shape": tuple(m.shape)})
+        off += 256 * nt + 256
     cl = [np.ascontiguousarray(c["code_len"], dtype=np.uint8) for c in codes]
     cw = [np.ascontiguousarray(c["codeword"], dtype=np.uint32) for c in codes]
     tb = (ctypes.c_int64 * len(mats))(*[c["total_bits"] for c in codes])

@@ -163,8 +163,9 @@ SinqLayout sinq_layout(const woq_mat* mats, int32_t n, bool shared) {
         while (q < n && key(idx[q]) == key(idx[p])) ++q;
         g.count = q - p;
         // Row strips per matrix.  Mode 0: a workgroup owns one strip of whole
-        // register tiles (R rows).  Mode 1: its four waves own four
-        // consecutive strips.  A workgroup writes one partial row, so
+        // register tiles (R rows).  Mode 1: it owns four strips' worth of
+        // consecutive rows, dealt to its four waves in turn.  A workgroup
+        // writes one partial row, so
         // n_strips counts workgroups.  Two plans, the faster estimate wins
         // (work counted in rows; cap = workgroups resident at once, about 8
         // waves per CU):

@@ -13,9 +13,10 @@
 // u = 1/t and v = 1/s (correctly rounded fp32) and form x = w * u (w * v).
 //
 // Fused pass (one read of W per iteration), in two forms:
-//  - k_sinq_wave, rows of at most 4096 bf16 (1536 fp32) columns: a wave owns
-//    a strip of whole rows, lane l the 8-column vectors l + 64 k, so the row
-//    statistics are wave-local (no workgroup barrier);
+//  - k_sinq_wave, rows of at most 4096 bf16 (1536 fp32) columns: a
+//    workgroup owns a strip of whole rows, dealt to its four waves in turn,
+//    lane l the 8-column vectors l + 64 k, so the row statistics are
+//    wave-local (no workgroup barrier);
 //  - k_sinq_pass, wider rows: a workgroup owns a strip of whole rows, thread
 //    t the vectors t + NT k, and the row statistics are combined over the
 //    waves through LDS (one barrier per tile of R rows).
@@ -434,11 +435,15 @@ __global__ __launch_bounds__(kMaxT) void k_sinq_pass(const SinqMat* __restrict__
 
 // ---------------------------------------------------------------------------
 // Wave-per-row pass for rows of at most 4096 bf16 (1536 fp32) columns.  A
-// workgroup's four waves take four consecutive row strips of one matrix; lane
-// l owns the 8-column vectors l + 64 k (k < NVL), so row statistics need no
-// workgroup barrier and the column partials of a strip stay in the lane's
-// registers.  Rows go through two packed register buffers: row r + 1 is
-// loaded while row r is processed.  u = 1/t is staged once per workgroup in
+// workgroup owns 4 * strip_rows consecutive rows of one matrix, dealt to its
+// four waves in turn (chunks of RW rows: wave w takes chunks w, w + 4, ...),
+// so the workgroup streams one contiguous region; the same rows split into
+// four contiguous sub-strips, one per wave, streamed 7% slower (four times
+// as many separate streams across the chip).  Lane l owns the 8-column
+// vectors l + 64 k (k < NVL), so row statistics need no workgroup barrier and
+// the column partials of the wave's rows stay in the lane's registers.  Rows
+// go through two packed register buffers: the wave's next chunk is loaded
+// while the current one is processed.  u = 1/t is staged once per workgroup in
 // LDS.  At the end the four waves add their column partials in LDS in wave
 // order and the workgroup writes one partial row.  RAG: the row is not a
 // multiple of 512 columns, so lanes own unequal numbers of vectors.
@@ -486,9 +491,10 @@ __global__ __launch_bounds__(256, (WaveCfg<DT, NVL>::OCC)) void k_sinq_wave(
         *reinterpret_cast<f32x4*>(u + j) = v;
     }
     __syncthreads();
-    const int strip = 4 * wg + wid;
-    const int r0 = min(sm.rows, strip * sm.strip_rows);
-    const int r1 = min(sm.rows, r0 + sm.strip_rows);
+    // the workgroup's rows [g0, r1); this wave's chunks start at r0, 4 RW apart
+    const int g0 = min(sm.rows, 4 * wg * sm.strip_rows);
+    const int r1 = min(sm.rows, g0 + 4 * sm.strip_rows);
+    const int r0 = g0 + wid * WaveCfg<DT, NVL>::RW;
 
     int vk[NVL];
     bool own[NVL];
@@ -615,12 +621,12 @@ __global__ __launch_bounds__(256, (WaveCfg<DT, NVL>::OCC)) void k_sinq_wave(
 
     Vec8<DT> PA[RW][NVL], PB[RW][NVL];
     if (r0 < r1) load_rows(PA, r0);
-    for (int row = r0; row < r1; row += 2 * RW) {
-        if (row + RW < r1) load_rows(PB, row + RW);
+    for (int row = r0; row < r1; row += 8 * RW) {
+        if (row + 4 * RW < r1) load_rows(PB, row + 4 * RW);
         process(PA, row);
-        if (row + RW >= r1) break;
-        if (row + 2 * RW < r1) load_rows(PA, row + 2 * RW);
-        process(PB, row + RW);
+        if (row + 4 * RW >= r1) break;
+        if (row + 8 * RW < r1) load_rows(PA, row + 8 * RW);
+        process(PB, row + 4 * RW);
     }
     // the four waves' column partials, added in wave order in LDS
     for (int w = 0; w < 4; ++w) {

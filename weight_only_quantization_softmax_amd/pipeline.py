@@ -73,7 +73,8 @@ class _SplitSinq:
     - wave-form and wider matrices: the wider ones carry WOQ_SINQ_SHARED
       and are planned for half of the GPU, so every CU holds a barrier-bound
       workgroup of the wide rows beside a bandwidth-bound one of the narrow
-      rows (8B stack: 11.50 -> 10.89 ms);
+      rows (8B stack's low tier: 10.9 ms one after the other, 10.4-10.7 ms
+      side by side);
     - otherwise several row widths: the width with the most bytes in one
       call, the others in the other, neither flagged (their reductions and
       tails overlap: MoE layers 70.3 -> 67.3 ms, 70B blocks 103.5 -> 102.3).

@@ -17,7 +17,9 @@ launched on, against its algorithmic bytes (one read of every weight per
 iteration); ``traffic`` is the measured HBM traffic per call from the
 rocprofv3 FETCH_SIZE / WRITE_SIZE summary under profiles/, valid while the
 kernel source it was taken on is unchanged.  ``cpu_baseline`` times the CPU
-oracle on a bounded sample of the same workload.
+oracle on a bounded sample of the same workload, and ``parity`` compares the
+timed steps' own outputs on that sample with the oracle's (entropies, s and
+t, and the codes both stage-isolated and end to end).
 
 Outside the timed steps the line also carries ``dequant`` (the tier's codes
 decoded back to bf16), ``df11`` (the lossless code of the kept blocks) and
@@ -54,18 +56,23 @@ def _log(*a):
 
 def cpu_baseline(wl, specs, mats, qp, tiers):
     """The oracle (numpy fp64, fp32 where the decisions are fp32) on host
-    cores over a bounded sample of the workload.
+    cores over a bounded sample of the workload, and the parity of the
+    timed steps' own GPU outputs on that sample.
 
-    Sample: the first block's matrices in order until at least 60 M weights
-    (for the Llama-8B-shaped stack: q, k, v, o and gate, 92.3 M weights),
-    each taken through every stage the workload uses (entropy; Sinkhorn +
-    group RTN + pack; int8 per-row + pack; ternary + pack).  Each stage's
-    seconds per byte on the sample are applied to the workload's own tier mix.
+    Sample: the matrices of the first block of the Sinkhorn tier (else the
+    first block), in order, until at least 60 M weights (Llama-8B shapes: q,
+    k, v, o and gate, 92.3 M weights), each taken through every stage the
+    workload uses (entropy; Sinkhorn + group RTN + pack; int8 per-row +
+    pack; ternary + pack).  Each stage's seconds per byte on the sample are
+    applied to the workload's own tier mix.  Returns (baseline, parity); the
+    parity comparisons run outside the timed oracle work.
     """
     import numpy as np
     import oracle
 
-    first = specs[0].block
+    acts = qp.action_of_block(tiers)
+    sinq_blocks = [sp.block for sp in specs if acts[sp.block] == "sinq"]
+    first = sinq_blocks[0] if sinq_blocks else specs[0].block
     pick, n = [], 0
     for i, m in enumerate(specs):
         if m.block == first and n < 60_000_000:
@@ -73,19 +80,23 @@ def cpu_baseline(wl, specs, mats, qp, tiers):
             n += mats[i].numel()
     t_ent = t_sinq = t_i8 = t_ter = 0.0
     nbytes = 0
+    h_gpu = qp.h_mat.cpu().numpy()
+    par = {"matrices": len(pick), "block": first, "entropy_max_rel_err": 0.0}
+    s_err = t_err = 0.0
+    n_codes = iso_bad = e2e_bad = 0
     for i in pick:
         w = mats[i].float().cpu().numpy()
         nbytes += mats[i].numel() * mats[i].element_size()
         t0 = time.perf_counter()
-        oracle.matrix_entropy(w)
+        h = oracle.matrix_entropy(w)
         t1 = time.perf_counter()
         s, t = oracle.sinkhorn_std(w, wl.iters)
         q = oracle.quantize_groupwise_f32(w, s.astype(np.float32), t.astype(np.float32), wl.bits,
                                           wl.group)
         oracle.pack_codes(q[0], wl.bits)
         t2 = time.perf_counter()
-        q = oracle.quantize_groupwise_f32(w, None, None, 8, w.shape[1])
-        oracle.pack_codes(q[0], 8)
+        q8 = oracle.quantize_groupwise_f32(w, None, None, 8, w.shape[1])
+        oracle.pack_codes(q8[0], 8)
         t3 = time.perf_counter()
         qt, _ = oracle.ternary_quantize(w)
         oracle.pack_codes((qt + 1).astype(np.uint8), 2)
@@ -94,18 +105,35 @@ def cpu_baseline(wl, specs, mats, qp, tiers):
         t_sinq += t2 - t1
         t_i8 += t3 - t2
         t_ter += t4 - t3
+        # parity of the step's outputs (untimed)
+        if h != 0.0:
+            par["entropy_max_rel_err"] = max(par["entropy_max_rel_err"], abs(h_gpu[i] / h - 1.0))
+        o = qp.outputs.get(i)
+        if o is not None and o["action"] == "sinq":
+            sg, tg = o["s"].cpu().numpy(), o["t"].cpu().numpy()
+            s_err = max(s_err, float(np.max(np.abs(sg / s - 1.0))))
+            t_err = max(t_err, float(np.max(np.abs(tg / t - 1.0))))
+            cg = oracle.unpack_codes(o["codes"].cpu().numpy(), wl.bits, w.shape[1])
+            qi = oracle.quantize_groupwise_f32(w, sg, tg, wl.bits, wl.group)[0]
+            n_codes += cg.size
+            iso_bad += int(np.count_nonzero(cg != qi))
+            e2e_bad += int(np.count_nonzero(cg != q[0]))
+    if n_codes:
+        par.update({"s_max_rel_err": s_err, "t_max_rel_err": t_err, "codes": n_codes,
+                    "codes_mismatch_stage_isolated": iso_bad,
+                    "codes_mismatch_end_to_end": e2e_bad})
     per_byte = {"sinq": t_sinq / nbytes, "int8row": t_i8 / nbytes, "ternary": t_ter / nbytes,
                 "keep": 0.0}
-    acts = qp.action_of_block(tiers)
     total = qp.bytes_in * (t_ent / nbytes)
     for m, sp in zip(mats, specs):
         total += m.numel() * m.element_size() * per_byte[acts[sp.block]]
-    return {"value": round(qp.bytes_in / total / 1e9, 6), "unit": "GB/s", "cores": 1,
+    base = {"value": round(qp.bytes_in / total / 1e9, 6), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
             "sample": (f"{len(pick)} matrices of block {first} ({nbytes / 1e9:.3f} GB) through "
                        f"entropy ({t_ent:.1f}s), Sinkhorn K={wl.iters} + int{wl.bits} g{wl.group} "
                        f"({t_sinq:.1f}s), int8 per-row ({t_i8:.1f}s), ternary ({t_ter:.1f}s); "
                        "per-byte costs applied to the workload's tier mix; numpy, one thread")}
+    return base, par
 
 
 def _sources_hash() -> str:
@@ -449,7 +477,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         _log("[bench] cpu baseline (oracle on a sample)")
-        out["cpu_baseline"] = cpu_baseline(wl, specs, mats, qp, tiers)
+        out["cpu_baseline"], out["parity"] = cpu_baseline(wl, specs, mats, qp, tiers)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -37,4 +37,9 @@ def test_bench_line_fields():
     for k in ("value", "unit", "cores", "kind", "sample"):
         assert k in cb, k
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0
+    # the timed steps' own outputs against the oracle on the baseline's sample
+    pa = d["parity"]
+    assert pa["entropy_max_rel_err"] < 1e-5
+    assert pa["s_max_rel_err"] < 1e-4 and pa["t_max_rel_err"] < 1e-4
+    assert pa["codes_mismatch_stage_isolated"] == 0 and pa["codes"] == 256 * 512
 

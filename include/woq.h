@@ -5,7 +5,9 @@
  * their softmax (EWQ), tiers the blocks, balances the matrices chosen for
  * low-bit storage with SINQ's alternating row / column standard-deviation
  * scaling, and stores them as group-wise round-to-nearest integer codes packed
- * into bytes (or as ternary {-1, 0, +1} codes with a per-row scale).
+ * into bytes (or as ternary {-1, 0, +1} codes with a per-row scale, or as the
+ * nearest levels of a non-uniform code book).  The blocks kept in bf16 can be
+ * stored with a lossless exponent code.
  *
  * Sources, cited by page title and section:
  *  [EWQ]    "Giai ma EWQ & FastEWQ: Luong tu hoa LLM 'thong minh' hon, nhe hon

@@ -5,7 +5,10 @@ C ABI of include/woq.h).  Each function has the name of the C entry point it
 wraps and does argument marshalling only: torch tensors provide device memory
 and the current HIP stream; every step of the pass runs in the library's
 kernels.  There is no CPU or PyTorch fallback: if libwoq.so is missing the
-calls raise.
+calls raise.  Since the library takes raw pointers, the binding first checks
+that every tensor is on one GPU and that caller-supplied buffers come one per
+matrix, with the right dtype and at least the size the call reads or writes
+(ValueError / TypeError before anything is enqueued).
 
   ewq_block_entropy     EWQ per-matrix softmax entropy, block entropy, tiers
   sinq_balance          SINQ dual-axis Sinkhorn std balancing -> (s, t)
@@ -44,12 +47,66 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def _mats(tensors: Sequence[torch.Tensor]):
+def _check_mats(tensors: Sequence[torch.Tensor]) -> None:
+    if len(tensors) == 0:
+        raise ValueError("at least one matrix is required")
     for t in tensors:
         if t.dim() != 2 or not t.is_contiguous():
             raise ValueError("matrices must be 2-D and contiguous")
+        if t.shape[0] < 1 or t.shape[1] < 1:
+            raise ValueError(f"empty matrix of shape {tuple(t.shape)}")
+        _dtype_code(t)
+
+
+def _mats(tensors: Sequence[torch.Tensor]):
+    _check_mats(tensors)
     return _lib.mat_array((t.data_ptr(), _dtype_code(t), t.shape[0], t.shape[1])
                           for t in tensors)
+
+
+def _check_bufs(name: str, ts, sizes, dtype) -> None:
+    """Caller-supplied per-matrix buffers: one per matrix, of the dtype,
+    contiguous and large enough, since the library reads or writes that many
+    elements through the raw pointer.  None (the whole list or an entry) is
+    left to the library's own NULL checks."""
+    if ts is None:
+        return
+    if len(ts) != len(sizes):
+        raise ValueError(f"{name}: {len(ts)} tensors for {len(sizes)} matrices")
+    for i, (t, n) in enumerate(zip(ts, sizes)):
+        if t is None:
+            continue
+        if t.dtype != dtype:
+            raise TypeError(f"{name}[{i}]: dtype {t.dtype}, expected {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}[{i}] must be contiguous")
+        if t.numel() < n:
+            raise ValueError(f"{name}[{i}] holds {t.numel()} elements, {n} needed")
+
+
+def _device(*groups):
+    """The one GPU every given tensor lives on (the library takes raw device
+    pointers, so a host tensor must never reach it)."""
+    dev = None
+    for g in groups:
+        if g is None:
+            continue
+        for t in (g if isinstance(g, (list, tuple)) else [g]):
+            if t is None:
+                continue
+            if t.device.type != "cuda":
+                raise ValueError(f"tensors must be on a GPU, got one on {t.device}")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise ValueError(f"tensors on two devices: {dev} and {t.device}")
+    if dev is None:
+        raise ValueError("no GPU tensor given")
+    return dev
+
+
+def _group_cols(m: torch.Tensor, group: int) -> int:
+    return group if group > 0 else m.shape[1]
 
 
 def _stream(stream) -> Optional[int]:
@@ -74,6 +131,8 @@ def workspace_size(op: int, mats: Sequence[torch.Tensor], group: int = 0) -> int
 
 
 def _workspace(op, mats, group, ws, device):
+    if ws is not None and ws.dtype != torch.uint8:
+        raise TypeError(f"workspace must be uint8 (bytes), got {ws.dtype}")
     need = workspace_size(op, mats, group)
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
@@ -84,9 +143,12 @@ def ewq_block_entropy(mats: Sequence[torch.Tensor], block_id: Optional[Sequence[
                       n_blocks: int = 1, x: float = 1.0, *, ws=None, stream=None):
     """Per-matrix entropy, block entropy, (mu, sigma, T), tiers and order (device tensors)."""
     lib = _lib.load()
-    dev = mats[0].device
-    arr = _mats(mats)
+    _check_mats(mats)
     n = len(mats)
+    if block_id is not None and len(block_id) != n:
+        raise ValueError(f"block_id: {len(block_id)} ids for {n} matrices")
+    dev = _device(mats, ws)
+    arr = _mats(mats)
     h_mat = torch.empty(n, dtype=torch.float64, device=dev)
     h_block = torch.empty(n_blocks, dtype=torch.float64, device=dev)
     stats = torch.empty(3, dtype=torch.float64, device=dev)
@@ -110,7 +172,10 @@ def sinq_balance(mats: Sequence[torch.Tensor], iters: int, *, rms: bool = False,
     call runs beside another on the same GPU, strips planned for half of it
     (both through sinq_balance_ex)."""
     lib = _lib.load()
-    dev = mats[0].device
+    _check_mats(mats)
+    _check_bufs("row_scale", row_scale, [m.shape[0] for m in mats], torch.float32)
+    _check_bufs("col_scale", col_scale, [m.shape[1] for m in mats], torch.float32)
+    dev = _device(mats, row_scale, col_scale, ws)
     arr = _mats(mats)
     if row_scale is None:
         row_scale = [torch.empty(m.shape[0], dtype=torch.float32, device=dev) for m in mats]
@@ -134,11 +199,17 @@ def quant_pack_groupwise(mats: Sequence[torch.Tensor], bits: int, group: int, *,
                          ws=None, stream=None):
     """Packed codes (uint8 [rows, cols*bits/8]), deltas (fp32) and zero-points (uint8)."""
     lib = _lib.load()
-    dev = mats[0].device
-    arr = _mats(mats)
+    _check_mats(mats)
 
     def g(m):
-        return group if group else m.shape[1]
+        return _group_cols(m, group)
+    _check_bufs("row_scale", row_scale, [m.shape[0] for m in mats], torch.float32)
+    _check_bufs("col_scale", col_scale, [m.shape[1] for m in mats], torch.float32)
+    _check_bufs("codes", codes, [m.shape[0] * (m.shape[1] * bits // 8) for m in mats], torch.uint8)
+    _check_bufs("scales", scales, [m.shape[0] * (m.shape[1] // g(m)) for m in mats], torch.float32)
+    _check_bufs("zeros", zeros, [m.shape[0] * (m.shape[1] // g(m)) for m in mats], torch.uint8)
+    dev = _device(mats, row_scale, col_scale, codes, scales, zeros, ws)
+    arr = _mats(mats)
     if codes is None:
         codes = [torch.empty(m.shape[0], m.shape[1] * bits // 8, dtype=torch.uint8, device=dev)
                  for m in mats]
@@ -160,7 +231,20 @@ def dequant_unpack(shapes, codes, scales, bits: int, group: int, *, zeros=None, 
                    col_scale=None, out_dtype=torch.float32, out=None, ws=None, stream=None):
     """Decode packed codes back to weights W' = (((q - z) delta) s_i) t_j."""
     lib = _lib.load()
-    dev = codes[0].device
+    shapes = [(int(r), int(c)) for (r, c) in shapes]
+    if len(shapes) == 0 or min(min(rc) for rc in shapes) < 1:
+        raise ValueError("at least one matrix is required, none of them empty")
+
+    def g(rc):
+        return group if group > 0 else rc[1]
+    _check_bufs("codes", codes, [r * (c * bits // 8) for r, c in shapes], torch.uint8)
+    _check_bufs("scales", scales, [r * (c // g((r, c))) for r, c in shapes], torch.float32)
+    _check_bufs("zeros", zeros, [r * (c // g((r, c))) for r, c in shapes], torch.uint8)
+    _check_bufs("row_scale", row_scale, [r for r, _ in shapes], torch.float32)
+    _check_bufs("col_scale", col_scale, [c for _, c in shapes], torch.float32)
+    if out is not None and [tuple(o.shape) for o in out] != shapes:
+        raise ValueError("out: tensors do not have the given shapes")
+    dev = _device(codes, scales, zeros, row_scale, col_scale, out, ws)
     if out is None:
         out = [torch.empty(r, c, dtype=out_dtype, device=dev) for (r, c) in shapes]
     arr = _mats(out)
@@ -194,12 +278,17 @@ def quant_pack_codebook(mats: Sequence[torch.Tensor], bits: int, group: int, *, 
     """Packed codes (uint8 [rows, cols*bits/8]) of the nearest code-book level and the
     per-group scales a = max |x| (fp32); levels default to the normal-quantile book."""
     lib = _lib.load()
-    dev = mats[0].device
-    arr = _mats(mats)
+    _check_mats(mats)
     lv = _levels(bits, levels)
 
     def g(m):
-        return group if group else m.shape[1]
+        return _group_cols(m, group)
+    _check_bufs("row_scale", row_scale, [m.shape[0] for m in mats], torch.float32)
+    _check_bufs("col_scale", col_scale, [m.shape[1] for m in mats], torch.float32)
+    _check_bufs("codes", codes, [m.shape[0] * (m.shape[1] * bits // 8) for m in mats], torch.uint8)
+    _check_bufs("scales", scales, [m.shape[0] * (m.shape[1] // g(m)) for m in mats], torch.float32)
+    dev = _device(mats, row_scale, col_scale, codes, scales, ws)
+    arr = _mats(mats)
     if codes is None:
         codes = [torch.empty(m.shape[0], m.shape[1] * bits // 8, dtype=torch.uint8, device=dev)
                  for m in mats]
@@ -218,8 +307,20 @@ def dequant_codebook(shapes, codes, scales, bits: int, group: int, *, levels=Non
                      col_scale=None, out_dtype=torch.float32, out=None, ws=None, stream=None):
     """Decode code-book codes back to weights W' = ((a l_q) s_i) t_j."""
     lib = _lib.load()
-    dev = codes[0].device
     lv = _levels(bits, levels)
+    shapes = [(int(r), int(c)) for (r, c) in shapes]
+    if len(shapes) == 0 or min(min(rc) for rc in shapes) < 1:
+        raise ValueError("at least one matrix is required, none of them empty")
+
+    def g(rc):
+        return group if group > 0 else rc[1]
+    _check_bufs("codes", codes, [r * (c * bits // 8) for r, c in shapes], torch.uint8)
+    _check_bufs("scales", scales, [r * (c // g((r, c))) for r, c in shapes], torch.float32)
+    _check_bufs("row_scale", row_scale, [r for r, _ in shapes], torch.float32)
+    _check_bufs("col_scale", col_scale, [c for _, c in shapes], torch.float32)
+    if out is not None and [tuple(o.shape) for o in out] != shapes:
+        raise ValueError("out: tensors do not have the given shapes")
+    dev = _device(codes, scales, row_scale, col_scale, out, ws)
     if out is None:
         out = [torch.empty(r, c, dtype=out_dtype, device=dev) for (r, c) in shapes]
     arr = _mats(out)
@@ -235,7 +336,10 @@ def ternary_pack(mats: Sequence[torch.Tensor], *, codes=None, row_scale=None, ws
                  stream=None):
     """2-bit ternary codes (q + 1) and per-row beta."""
     lib = _lib.load()
-    dev = mats[0].device
+    _check_mats(mats)
+    _check_bufs("codes", codes, [m.shape[0] * (m.shape[1] // 4) for m in mats], torch.uint8)
+    _check_bufs("row_scale", row_scale, [m.shape[0] for m in mats], torch.float32)
+    dev = _device(mats, codes, row_scale, ws)
     arr = _mats(mats)
     if codes is None:
         codes = [torch.empty(m.shape[0], m.shape[1] // 4, dtype=torch.uint8, device=dev)
@@ -280,7 +384,10 @@ def df11_buffer_sizes(n: int, total_bits: int):
 def df11_exponent_histogram(mats: Sequence[torch.Tensor], *, hist=None, ws=None, stream=None):
     """Exponent counts per matrix: int32 tensor [n_mats, 256] on the device."""
     lib = _lib.load()
-    dev = mats[0].device
+    _check_mats(mats)
+    if hist is not None:
+        _check_bufs("hist", [hist], [256 * len(mats)], torch.int32)
+    dev = _device(mats, hist, ws)
     arr = _mats(mats)
     if hist is None:
         hist = torch.empty(len(mats), 256, dtype=torch.int32, device=dev)
@@ -325,7 +432,10 @@ def df11_encode(mats: Sequence[torch.Tensor], codes, *, ws=None, stream=None):
     gaps, block_pos, tables, code_len) and n_tables, total_bits, shape."""
     import numpy as np
     lib = _lib.load()
-    dev = mats[0].device
+    _check_mats(mats)
+    if len(codes) != len(mats):
+        raise ValueError(f"codes: {len(codes)} codes for {len(mats)} matrices")
+    dev = _device(mats, ws)
     arr = _mats(mats)
     # every matrix's tables and code lengths in one host-to-device copy
     host = np.concatenate([np.concatenate([np.ascontiguousarray(c["tables"], dtype=np.uint8).reshape(-1),
@@ -368,7 +478,12 @@ def df11_compress(mats: Sequence[torch.Tensor], *, stream=None):
 def df11_decode(encoded, *, out=None, ws=None, stream=None):
     """Exact bf16 weights of a batch of encoded matrices (one launch)."""
     lib = _lib.load()
-    dev = encoded[0]["enc"].device
+    if len(encoded) == 0:
+        raise ValueError("at least one encoded matrix is required")
+    if out is not None and [tuple(o.shape) for o in out] != [tuple(e["shape"]) for e in encoded]:
+        raise ValueError("out: tensors do not have the encoded shapes")
+    dev = _device([e[k] for e in encoded for k in ("enc", "sm", "gaps", "block_pos", "tables",
+                                                    "code_len")], out, ws)
     if out is None:
         out = [torch.empty(e["shape"], dtype=torch.bfloat16, device=dev) for e in encoded]
     arr = _mats(out)

@@ -31,6 +31,7 @@ from typing import Dict, List, Optional, Sequence
 import torch
 
 from . import _lib
+from . import _check_mats, _device
 
 ACTIONS = ("ternary", "sinq", "int8row", "keep")   # ascending storage per weight
 
@@ -113,7 +114,11 @@ class QuantPass:
                 raise ValueError(a)
         self.lib = _lib.load()
         self.mats = list(mats)
+        _check_mats(self.mats)
+        _device(self.mats)
         self.block_id = [int(b) for b in block_id]
+        if len(self.block_id) != len(self.mats):
+            raise ValueError(f"block_id: {len(self.block_id)} ids for {len(self.mats)} matrices")
         self.n_blocks = n_blocks
         self.iters, self.bits, self.group, self.x = iters, bits, group, x
         self.tiered = tiered

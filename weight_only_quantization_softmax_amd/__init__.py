@@ -109,9 +109,11 @@ def _group_cols(m: torch.Tensor, group: int) -> int:
     return group if group > 0 else m.shape[1]
 
 
-def _stream(stream) -> Optional[int]:
+def _stream(stream, device=None) -> Optional[int]:
+    """The HIP stream handle: the given stream, else the current stream of the
+    tensors' device."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(device)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
@@ -160,7 +162,7 @@ def ewq_block_entropy(mats: Sequence[torch.Tensor], block_id: Optional[Sequence[
         bid = (ctypes.c_int32 * n)(*[int(b) for b in block_id])
     st = lib.ewq_block_entropy(arr, n, bid, n_blocks, float(x), h_mat.data_ptr(),
                                h_block.data_ptr(), stats.data_ptr(), tier.data_ptr(),
-                               order.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream))
+                               order.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream, dev))
     _lib.check("ewq_block_entropy", st)
     return {"h_mat": h_mat, "h_block": h_block, "stats": stats, "tier": tier, "order": order}
 
@@ -185,11 +187,11 @@ def sinq_balance(mats: Sequence[torch.Tensor], iters: int, *, rms: bool = False,
     flags = (_lib.WOQ_SINQ_RMS if rms else 0) | (_lib.WOQ_SINQ_SHARED if shared else 0)
     if flags:
         st = lib.sinq_balance_ex(arr, len(mats), int(iters), flags, _ptrs(row_scale),
-                                 _ptrs(col_scale), ws.data_ptr(), ws.numel(), _stream(stream))
+                                 _ptrs(col_scale), ws.data_ptr(), ws.numel(), _stream(stream, dev))
         _lib.check("sinq_balance_ex", st)
     else:
         st = lib.sinq_balance(arr, len(mats), int(iters), _ptrs(row_scale), _ptrs(col_scale),
-                              ws.data_ptr(), ws.numel(), _stream(stream))
+                              ws.data_ptr(), ws.numel(), _stream(stream, dev))
         _lib.check("sinq_balance", st)
     return row_scale, col_scale
 
@@ -222,7 +224,7 @@ def quant_pack_groupwise(mats: Sequence[torch.Tensor], bits: int, group: int, *,
     ws = _workspace(_lib.OP_QUANT, mats, group, ws, dev)
     st = lib.quant_pack_groupwise(arr, len(mats), _ptrs(row_scale), _ptrs(col_scale), int(bits),
                                   int(group), _ptrs(codes), _ptrs(scales), _ptrs(zeros),
-                                  ws.data_ptr(), ws.numel(), _stream(stream))
+                                  ws.data_ptr(), ws.numel(), _stream(stream, dev))
     _lib.check("quant_pack_groupwise", st)
     return codes, scales, zeros
 
@@ -251,7 +253,7 @@ def dequant_unpack(shapes, codes, scales, bits: int, group: int, *, zeros=None, 
     ws = _workspace(_lib.OP_DEQUANT, out, group, ws, dev)
     st = lib.dequant_unpack(arr, len(out), _ptrs(codes), _ptrs(scales), _ptrs(zeros),
                             _ptrs(row_scale), _ptrs(col_scale), int(bits), int(group),
-                            ws.data_ptr(), ws.numel(), _stream(stream))
+                            ws.data_ptr(), ws.numel(), _stream(stream, dev))
     _lib.check("dequant_unpack", st)
     return out
 
@@ -298,7 +300,7 @@ def quant_pack_codebook(mats: Sequence[torch.Tensor], bits: int, group: int, *, 
     ws = _workspace(_lib.OP_QUANT, mats, group, ws, dev)
     st = lib.quant_pack_codebook(arr, len(mats), _ptrs(row_scale), _ptrs(col_scale), int(bits),
                                  int(group), lv, _ptrs(codes), _ptrs(scales), ws.data_ptr(),
-                                 ws.numel(), _stream(stream))
+                                 ws.numel(), _stream(stream, dev))
     _lib.check("quant_pack_codebook", st)
     return codes, scales
 
@@ -327,7 +329,7 @@ def dequant_codebook(shapes, codes, scales, bits: int, group: int, *, levels=Non
     ws = _workspace(_lib.OP_DEQUANT, out, group, ws, dev)
     st = lib.dequant_codebook(arr, len(out), _ptrs(codes), _ptrs(scales), _ptrs(row_scale),
                               _ptrs(col_scale), int(bits), int(group), lv, ws.data_ptr(),
-                              ws.numel(), _stream(stream))
+                              ws.numel(), _stream(stream, dev))
     _lib.check("dequant_codebook", st)
     return out
 
@@ -348,7 +350,7 @@ def ternary_pack(mats: Sequence[torch.Tensor], *, codes=None, row_scale=None, ws
         row_scale = [torch.empty(m.shape[0], dtype=torch.float32, device=dev) for m in mats]
     ws = _workspace(_lib.OP_TERNARY, mats, 0, ws, dev)
     st = lib.ternary_pack(arr, len(mats), _ptrs(codes), _ptrs(row_scale), ws.data_ptr(),
-                          ws.numel(), _stream(stream))
+                          ws.numel(), _stream(stream, dev))
     _lib.check("ternary_pack", st)
     return codes, row_scale
 
@@ -393,7 +395,7 @@ def df11_exponent_histogram(mats: Sequence[torch.Tensor], *, hist=None, ws=None,
         hist = torch.empty(len(mats), 256, dtype=torch.int32, device=dev)
     ws = _workspace(_lib.OP_DF11_HIST, mats, 0, ws, dev)
     st = lib.df11_exponent_histogram(arr, len(mats), hist.data_ptr(), ws.data_ptr(), ws.numel(),
-                                     _stream(stream))
+                                     _stream(stream, dev))
     _lib.check("df11_exponent_histogram", st)
     return hist
 
@@ -463,7 +465,7 @@ def df11_encode(mats: Sequence[torch.Tensor], codes, *, ws=None, stream=None):
     st = lib.df11_encode(arr, len(mats), _host_ptrs(cl), _host_ptrs(cw), tb,
                          _ptrs([o["enc"] for o in outs]), _ptrs([o["sm"] for o in outs]),
                          _ptrs([o["gaps"] for o in outs]), _ptrs([o["block_pos"] for o in outs]),
-                         ws.data_ptr(), ws.numel(), _stream(stream))
+                         ws.data_ptr(), ws.numel(), _stream(stream, dev))
     _lib.check("df11_encode", st)
     return outs
 
@@ -495,6 +497,6 @@ def df11_decode(encoded, *, out=None, ws=None, stream=None):
                          _ptrs([e["block_pos"] for e in encoded]),
                          _ptrs([e["tables"] for e in encoded]), nt,
                          _ptrs([e["code_len"] for e in encoded]), tb,
-                         ws.data_ptr(), ws.numel(), _stream(stream))
+                         ws.data_ptr(), ws.numel(), _stream(stream, dev))
     _lib.check("df11_decode", st)
     return out

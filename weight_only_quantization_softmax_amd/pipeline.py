@@ -333,7 +333,7 @@ class QuantPass:
     def run(self, stream: Optional[torch.cuda.Stream] = None, timers: Optional[dict] = None):
         """One whole pass; returns the tiers (host list).  ``timers`` collects
         (kind -> list of (start_event, end_event, bytes)) around each call."""
-        stream = stream or torch.cuda.current_stream()
+        stream = stream or torch.cuda.current_stream(self.device)
         h = stream.cuda_stream
         calls = [self._entropy_call()]
         self._run_calls(calls, stream, h, timers)

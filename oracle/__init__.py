@@ -45,15 +45,17 @@ fixtures under ``tests/golden``.  No function is left "parity unpinned".
 from .ewq import matrix_entropy, block_entropy, ewq_tiers, ewq_order, ewq_budget
 from .sinq import sinkhorn_std, line_std
 from .rtn import (quantize_groupwise_f32, quantize_groupwise_f64, pack_codes,
-                  unpack_codes, dequantize_f32, near_tie_fraction)
-from .ternary import ternary_quantize, ternary_dequantize
+                  unpack_codes, dequantize_f32, near_tie_mask)
+from .ternary import (ternary_quantize, ternary_dequantize, ternary_quantize_f64,
+                      ternary_near_tie_mask)
 
 __all__ = [
     "matrix_entropy", "block_entropy", "ewq_tiers", "ewq_order", "ewq_budget",
     "sinkhorn_std", "line_std",
     "quantize_groupwise_f32", "quantize_groupwise_f64", "pack_codes",
-    "unpack_codes", "dequantize_f32", "near_tie_fraction",
-    "ternary_quantize", "ternary_dequantize",
+    "unpack_codes", "dequantize_f32", "near_tie_mask",
+    "ternary_quantize", "ternary_dequantize", "ternary_quantize_f64",
+    "ternary_near_tie_mask",
 ]
 from . import df11  # noqa: F401
 from . import codebook  # noqa: F401

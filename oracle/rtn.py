@@ -21,9 +21,13 @@ Hóa").  They leave the affine details open; the reading used here:
 
 ``quantize_groupwise_f32`` takes every rounding decision in fp32 with the
 exact operation sequence the kernels use (reciprocals 1/s, 1/t and 1/delta,
-each correctly rounded; products rounded once each), so its codes, deltas
-and zero-points are bit-identical to a correct kernel's.
-``quantize_groupwise_f64`` is the same definition with true fp64 divisions.
+each correctly rounded; products rounded once each; the zero-point ratio and
+any element ratio near a half-way point by one correctly rounded division),
+so its codes, deltas and zero-points are bit-identical to a correct
+kernel's.
+``quantize_groupwise_f64`` is the plain definition with true fp64 divisions
+(the reference for the spec code bar: codes bit-exact except near
+ties, see ``near_tie_mask``).
 """
 from __future__ import annotations
 
@@ -60,8 +64,25 @@ def _check_shape(rows: int, cols: int, bits: int, group: int):
         raise ValueError("cols*bits must be a whole number of bytes")
 
 
+# A fast ratio u = x * (1/delta) is within a few fp32 ulps of the exact ratio
+# (2^b - 1) * x / (hi - lo): at most about 6.8e-5 away for 8-bit codes.  When
+# u lies within NEAR_HALF of a half-way point the ratio is recomputed with one
+# correctly rounded division, which returns exactly k + 1/2 whenever the exact
+# ratio is k + 1/2 and its operands are exact (bf16 / fp32 inputs without
+# scales).
+NEAR_HALF = F32(0.5 - 2.0 ** -13)
+
+
 def quantize_groupwise_f32(w, s=None, t=None, bits: int = 4, group: int = 64):
-    """Codes q (uint8 [rows, cols]), delta (f32 [rows, cols/group]), z (uint8)."""
+    """Codes q (uint8 [rows, cols]), delta (f32 [rows, cols/group]), z (uint8).
+
+    The fp32 decision sequence (every step one correctly rounded fp32
+    operation): x = (w * (1/s_i)) * (1/t_j); per group lo = min(0, min x),
+    hi = max(0, max x), d = hi - lo, delta = d / (2^b - 1), inv = 1 / delta;
+    a group whose inv is not finite gets z = 0 and q = 0; otherwise
+    z = clamp(rne(((2^b - 1) * -lo) / d)), and per element u = x * inv, or
+    u = ((2^b - 1) * x) / d when |u - rne(u)| > NEAR_HALF, then
+    q = clamp(rne(u) + z, 0, 2^b - 1)."""
     x = balanced_f32(w, s, t)
     rows, cols = x.shape
     _check_shape(rows, cols, bits, group)
@@ -75,58 +96,85 @@ def quantize_groupwise_f32(w, s=None, t=None, bits: int = 4, group: int = 64):
         inv = (F32(1.0) / delta).astype(F32)
         ok = np.isfinite(inv)
         inv_s = np.where(ok, inv, F32(0))
-        z = np.clip(np.rint((-lo) * inv_s), 0, qmax)
-        q = np.clip(np.rint(xg * inv_s[:, :, None]) + z[:, :, None], 0, qmax)
+        ds = np.where(ok & (d > 0), d, F32(1))
+        z = np.clip(np.rint((qmax * -lo) / ds), 0, qmax)
+        u = xg * inv_s[:, :, None]
+        r = np.rint(u)
+        near = np.abs(u - r) > NEAR_HALF
+        r = np.where(near, np.rint((qmax * xg) / ds[:, :, None]), r)
+        q = np.clip(r + z[:, :, None], 0, qmax)
     z = np.where(ok, z, 0)
     q = np.where(ok[:, :, None], q, 0)
     return (q.reshape(rows, cols).astype(np.uint8), delta.astype(F32),
             z.astype(np.uint8))
 
 
-def quantize_groupwise_f64(w, s=None, t=None, bits: int = 4, group: int = 64):
-    """Same definition with fp64 divisions: W / (s t^T), x / delta, -lo / delta."""
+def balanced_f64(w, s=None, t=None) -> np.ndarray:
+    """x_ij = w_ij / (s_i t_j) in fp64 (true divisions)."""
     x = np.asarray(w, dtype=np.float64)
     if s is not None:
         x = x / np.asarray(s, dtype=np.float64)[:, None]
     if t is not None:
         x = x / np.asarray(t, dtype=np.float64)[None, :]
+    return x
+
+
+def _group_ratios_f64(x, bits: int, group: int):
+    """Per group: span = hi - lo, the zero-point argument -lo / delta and every
+    element's x / delta, in fp64.  Since delta = span / (2^b - 1), the ratios
+    are evaluated as (2^b - 1) * value / span: the numerator and the span are
+    exact in fp64 for bf16 / fp32 inputs without scales, so a ratio whose exact
+    value is a half-way point k + 1/2 comes out as exactly k + 1/2 and is
+    rounded as the definition says (half to even).  Returns (lo, span, uz, u)
+    with uz and u set to 0 where span = 0."""
     rows, cols = x.shape
     _check_shape(rows, cols, bits, group)
     qmax = float(2 ** bits - 1)
     xg = x.reshape(rows, cols // group, group)
     lo = np.minimum(0.0, xg.min(axis=2))
     hi = np.maximum(0.0, xg.max(axis=2))
-    delta = (hi - lo) / qmax
-    ok = delta > 0
-    ds = np.where(ok, delta, 1.0)
-    z = np.where(ok, np.clip(np.rint(-lo / ds), 0, qmax), 0)
-    q = np.clip(np.rint(xg / ds[:, :, None]) + z[:, :, None], 0, qmax)
-    q = np.where(ok[:, :, None], q, 0)
-    return q.reshape(rows, cols).astype(np.uint8), delta, z.astype(np.uint8)
+    span = hi - lo
+    ok = span > 0
+    sp = np.where(ok, span, 1.0)
+    uz = np.where(ok, (qmax * -lo) / sp, 0.0)
+    u = np.where(ok[:, :, None], (qmax * xg) / sp[:, :, None], 0.0)
+    return lo, span, uz, u
 
 
-def near_tie_fraction(w, s, t, delta, z, bits: int, group: int, eps: float = 1e-5):
-    """Mask of elements whose rounding is a near tie, in fp64 from given s, t, delta.
-
-    An element is a near tie if u = x / delta has |u - floor(u) - 0.5| < eps;
-    every element of a group whose zero-point argument -lo / delta is a near
-    tie counts as well (the whole group may then shift by one code).
-    """
-    x = np.asarray(w, dtype=np.float64)
-    if s is not None:
-        x = x / np.asarray(s, dtype=np.float64)[:, None]
-    if t is not None:
-        x = x / np.asarray(t, dtype=np.float64)[None, :]
+def quantize_groupwise_f64(w, s=None, t=None, bits: int = 4, group: int = 64):
+    """The plain definition in fp64: x = W / (s t^T) with true divisions,
+    delta = (hi - lo) / (2^b - 1), z = clamp(rne(-lo / delta)), q = clamp(rne(x /
+    delta) + z); the two ratios are evaluated without rounding delta first
+    (``_group_ratios_f64``).  Returns q (uint8), delta (fp64), z (uint8)."""
+    x = balanced_f64(w, s, t)
     rows, cols = x.shape
-    xg = x.reshape(rows, cols // group, group)
-    d = np.asarray(delta, dtype=np.float64)
-    ds = np.where(d > 0, d, 1.0)
-    u = xg / ds[:, :, None]
-    tie = np.abs(u - np.floor(u) - 0.5) < eps
-    lo = np.minimum(0.0, xg.min(axis=2))
-    uz = -lo / ds
-    ztie = np.abs(uz - np.floor(uz) - 0.5) < eps
-    tie |= ztie[:, :, None]
+    qmax = float(2 ** bits - 1)
+    lo, span, uz, u = _group_ratios_f64(x, bits, group)
+    ok = span > 0
+    z = np.where(ok, np.clip(np.rint(uz), 0, qmax), 0)
+    q = np.clip(np.rint(u) + z[:, :, None], 0, qmax)
+    q = np.where(ok[:, :, None], q, 0)
+    return q.reshape(rows, cols).astype(np.uint8), span / qmax, z.astype(np.uint8)
+
+
+def near_tie_mask(w, s, t, bits: int, group: int, eps: float = 1e-5) -> np.ndarray:
+    """Elements whose code the definition decides within ``eps`` of a rounding
+    boundary, from the plain fp64 definition with the given s and t.
+
+    An element is a near tie if its ratio u = x / delta has
+    |u - floor(u) - 0.5| < eps.  When the zero-point's ratio -lo / delta is a
+    near tie, the whole group may shift by one code, so every element of that
+    group counts as well.  bool [rows, cols].
+    """
+    x = balanced_f64(w, s, t)
+    rows, cols = x.shape
+    _, span, uz, u = _group_ratios_f64(x, bits, group)
+
+    def near(v):
+        return np.abs(v - np.floor(v) - 0.5) < eps
+
+    ok = (span > 0)[:, :, None]
+    tie = ok & (near(u) | near(uz)[:, :, None])
     return tie.reshape(rows, cols)
 
 

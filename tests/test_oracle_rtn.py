@@ -81,10 +81,112 @@ def test_f32_and_f64_agree_except_near_ties():
     q32, d32, z32 = oracle.quantize_groupwise_f32(w, s, t, 4, 64)
     q64, d64, z64 = oracle.quantize_groupwise_f64(w, s, t, 4, 64)
     assert np.allclose(d32, d64, rtol=1e-6)
-    tie = oracle.near_tie_fraction(w, s, t, d64, z64, 4, 64)
+    tie = oracle.near_tie_mask(w, s, t, 4, 64)
     diff = q32 != q64
     assert np.all(~diff | tie)
     assert np.all(np.abs(q32.astype(int) - q64.astype(int)) <= 1)
+
+
+def test_near_tie_mask_hand_cases():
+    # bits 4 (2^b - 1 = 15), groups of 8; every group spans hi - lo = 15, so
+    # u = x / delta = x and the zero-point ratio is -lo.
+    w = np.array([
+        # lo = 0: z ratio 0 (no tie).  Exact halves flag; +-2e-5 away does not;
+        # an integer (6.0) is not a tie; 5e-6 from a half is.
+        [0.0, 15.0, 2.5, 3.5 + 2e-5, 7.25, 4.5 - 2e-5, 6.0, 5.5 + 5e-6],
+        # lo = -3 (z ratio 3, no tie): negative halves flag as well
+        [-3.0, 12.0, -2.5, -1.5 - 2e-5, 0.5, 1.0, -0.25, 11.5],
+        # lo = -1.5: the zero-point ratio 1.5 is a tie, so the whole group is
+        [-1.5, 13.5, 0.3, 1.0, 2.0, 3.7, 4.1, 5.2],
+    ])
+    m = oracle.near_tie_mask(w, None, None, 4, 8)
+    assert m.tolist() == [
+        [False, False, True, False, False, False, False, True],
+        [False, False, True, False, True, False, False, True],
+        [True] * 8,
+    ]
+    # scales enter through x = w / (s t): doubling s and w leaves the mask
+    s2 = np.full(3, 2.0)
+    assert np.array_equal(oracle.near_tie_mask(2 * w, s2, None, 4, 8), m)
+    # a group of zeros (span 0) has no rounding at all
+    assert not oracle.near_tie_mask(np.zeros((1, 8)), None, None, 4, 8).any()
+
+
+def test_near_tie_rate_on_a_balanced_bf16_matrix():
+    # After balancing, x / delta has no lattice structure, so a fraction
+    # close to 2 eps of the elements lies within eps of a half-way point
+    # (element ties), and a fraction close to 2 eps of the groups has a
+    # near-tie zero-point.  A mask that is too permissive (a larger eps, the
+    # distance to the nearest integer instead of the nearest half) or that
+    # misses the group rule fails these bounds.
+    w = woqdata.random_matrix(1024, 4096, 7).float().numpy()
+    s, t = oracle.sinkhorn_std(w, 4)
+    eps = 1e-5
+    m = oracle.near_tie_mask(w, s, t, 4, 64, eps)
+    me = oracle.near_tie_mask(w, s, t, 4, 64, eps) & ~_zero_point_tie(w, s, t, 4, 64, eps)
+    n = w.size
+    assert 0.6 * 2 * eps < me.sum() / n < 1.5 * 2 * eps
+    assert m.sum() / n < 2e-4
+    groups = _zero_point_tie(w, s, t, 4, 64, eps).reshape(1024, 64, 64)[:, :, 0]
+    # the whole group of a zero-point tie is flagged
+    assert np.all(m.reshape(1024, 64, 64)[groups])
+
+
+def _zero_point_tie(w, s, t, bits, group, eps):
+    """Reference for the group rule in plain loops over the groups."""
+    x = np.asarray(w, np.float64) / np.outer(np.asarray(s, np.float64), np.asarray(t, np.float64))
+    qmax = 2 ** bits - 1
+    out = np.zeros(x.shape, bool)
+    for i in range(x.shape[0]):
+        for k in range(x.shape[1] // group):
+            g = x[i, k * group:(k + 1) * group]
+            lo, hi = min(0.0, g.min()), max(0.0, g.max())
+            if hi > lo:
+                uz = qmax * -lo / (hi - lo)
+                if abs(uz - np.floor(uz) - 0.5) < eps:
+                    out[i, k * group:(k + 1) * group] = True
+    return out
+
+
+def _exact_codes(x, bits, group):
+    """The definition in exact rational arithmetic: delta = (hi - lo) / qmax,
+    z = rne(-lo / delta), q = clamp(rne(x / delta) + z); Python's round() of a
+    Fraction rounds half to even."""
+    from fractions import Fraction
+    qmax = 2 ** bits - 1
+    rows, cols = x.shape
+    q = np.zeros((rows, cols), np.int64)
+    z = np.zeros((rows, cols // group), np.int64)
+    for i in range(rows):
+        for k in range(cols // group):
+            g = [Fraction(float(v)) for v in x[i, k * group:(k + 1) * group]]
+            lo, hi = min(Fraction(0), min(g)), max(Fraction(0), max(g))
+            if hi == lo:
+                continue
+            d = (hi - lo) / qmax
+            zk = min(max(round(-lo / d), 0), qmax)
+            z[i, k] = zk
+            for j, v in enumerate(g):
+                q[i, k * group + j] = min(max(round(v / d) + zk, 0), qmax)
+    return q, z
+
+
+@pytest.mark.parametrize("bits,group", [(8, 64), (4, 16), (3, 8), (2, 8)])
+def test_f64_decides_exact_half_way_points(bits, group):
+    # bf16 values on a coarse lattice (small integers times a power of two)
+    # and symmetric groups make many ratios exact half-way points; the fp64
+    # definition must round every one of them as exact arithmetic does.
+    rng = np.random.default_rng(bits * 100 + group)
+    x = rng.integers(-24, 25, size=(6, 4 * group)).astype(np.float64) * 2.0 ** -7
+    x[0, :group] = np.linspace(-1, 1, group)       # hi = -lo: z ratio = qmax / 2
+    x[1, group - 1] = -x[1, :group - 1].max()      # another symmetric group
+    x = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    q_ref, z_ref = _exact_codes(x, bits, group)
+    q, d, z = oracle.quantize_groupwise_f64(x, None, None, bits, group)
+    assert np.array_equal(z.astype(np.int64), z_ref)
+    assert np.array_equal(q.astype(np.int64), q_ref)
+    # the fixture does contain exact ties, in the elements and the zero-points
+    assert oracle.near_tie_mask(x, None, None, bits, group, 1e-12).sum() >= group
 
 
 def test_zero_delta_groups():
@@ -109,7 +211,7 @@ def test_int8_per_row_matches_torch_affine():
     tq = torch.quantize_per_channel(torch.from_numpy(w), torch.from_numpy(d[:, 0].astype(np.float64)),
                                     torch.from_numpy(z[:, 0].astype(np.int64)), 0, torch.quint8)
     tqi = tq.int_repr().numpy()
-    tie = oracle.near_tie_fraction(w, None, None, d, z, 8, 4096)
+    tie = oracle.near_tie_mask(w, None, None, 8, 4096)
     diff = tqi != q
     assert np.all(~diff | tie)
     assert diff.mean() < 1e-3

@@ -44,3 +44,40 @@ def test_zero_row():
     # codes q + 1 pack as 2-bit LSB-first
     packed = oracle.pack_codes((q + 1).astype(np.uint8), 2)
     assert packed.shape == (2, 4) and packed[0].tobytes() == bytes([0x55] * 4)
+
+
+def test_f64_definition_brute_force():
+    # exact rational arithmetic: beta = mean |W|, q = clamp(rne(W / beta))
+    from fractions import Fraction
+    w = woqdata.random_matrix(6, 64, 5).float().numpy()
+    w[2, :] = np.repeat([0.25, -0.5, 0.125, 0.0], 16)   # beta = 0.21875: exact ratios
+    w[3, :] = 0.0
+    q, beta = oracle.ternary_quantize_f64(w)
+    for i in range(6):
+        row = [Fraction(float(v)) for v in w[i]]
+        b = sum(abs(v) for v in row) / len(row)
+        assert beta[i] == float(b) or abs(beta[i] / float(b) - 1) < 1e-15
+        for j, v in enumerate(row):
+            ref = 0 if b == 0 else min(max(round(v / b), -1), 1)
+            assert q[i, j] == ref, (i, j)
+
+
+def test_near_tie_mask_hand_cases():
+    beta = np.array([1.0, 2.0, 0.0])
+    w = np.array([[0.5, 0.5 + 2e-5, 0.5 - 5e-6, 1.5, 0.2, -0.5],
+                  [1.0, -1.0, 3.0, 1.00004, 0.0, 2.5],
+                  [0.5, 0.0, 0.0, 0.0, 0.0, 0.0]])
+    m = oracle.ternary_near_tie_mask(w, beta)
+    assert m.tolist() == [[True, False, True, True, False, True],
+                          [True, True, True, False, False, False],
+                          [False] * 6]
+
+
+def test_f32_decisions_agree_with_f64_except_near_ties():
+    w = woqdata.random_matrix(256, 2048, 9).float().numpy()
+    q32, b32 = oracle.ternary_quantize(w)
+    q64, b64 = oracle.ternary_quantize_f64(w)
+    assert np.allclose(b32, b64, rtol=2 ** -24)
+    diff = q32 != q64
+    assert np.all(~diff | oracle.ternary_near_tie_mask(w))
+    assert diff.mean() <= 1e-5

@@ -3,8 +3,9 @@
 Bars: entropies within 1e-5 relative (the kernels reach ~1e-12); Sinkhorn
 scales within 1e-4 relative; codes, deltas and zero-points bit-exact against
 the oracle's fp32 decision sequence fed with the GPU's own upstream scales
-(stage isolation); against the fp64 oracle end to end, code differences are
-allowed only at near ties and must be <= 1e-5 of all elements.
+(stage isolation); against the plain fp64 definition (the GPU's scales),
+code differences are allowed only at near ties, by one, and must be <= 1e-5
+of all elements; end to end (the oracle's own scales) by one, <= 1e-5.
 """
 import math
 
@@ -15,6 +16,7 @@ import torch
 import oracle
 import woqdata
 import weight_only_quantization_softmax_amd as woq
+from tests import _codes
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -252,6 +254,7 @@ def _check_quant(m, s, t, bits, group, codes, scales, zeros):
 
 @pytest.mark.parametrize("with_scales", [False, True])
 def test_quant_bit_exact(with_scales):
+    counts = []
     for i, (r, c, bits, group, dt) in enumerate(QUANT_CASES):
         m = _rm(r, c, 40 + i, dt, frac=0.01, mult=20.0)
         s = t = None
@@ -262,6 +265,33 @@ def test_quant_bit_exact(with_scales):
             [m], bits, group, row_scale=None if s is None else [s],
             col_scale=None if t is None else [t])
         _check_quant(m, s, t, bits, group, codes[0], scales[0], zeros[0])
+        g = group if group else c
+        q = oracle.unpack_codes(codes[0].cpu().numpy(), bits, c)
+        counts.append(_codes.affine(_np(m), None if s is None else s.cpu().numpy(),
+                                    None if t is None else t.cpu().numpy(), bits, g, q))
+    _codes.within_budget(counts)
+
+
+def test_quant_exact_half_way_points():
+    """bf16 weights on a coarse lattice, symmetric groups and per-row groups
+    whose largest and smallest weights cancel: many ratios are exact half-way
+    points.  The kernels decide every one as the fp64 definition does (the
+    zero-point and near-half ratios by a correctly rounded division): no
+    difference at all, on all three quantise kernels."""
+    g = torch.Generator(device="cpu").manual_seed(5)
+    for rows, cols, bits, group in [(64, 1024, 4, 64), (48, 4096, 8, 0), (16, 14336, 8, 0),
+                                    (32, 1800, 8, 600), (64, 512, 3, 128), (64, 256, 2, 32)]:
+        x = torch.randint(-24, 25, (rows, cols), generator=g).float() * 2.0 ** -7
+        gg = group if group else cols
+        x[:, gg - 1] = -x[:, :gg - 1].abs().amax(dim=1)     # hi = -lo in the first group
+        x[0, :gg] = torch.linspace(-1, 1, gg)
+        m = x.to(torch.bfloat16).to(DEV)
+        codes, scales, zeros = woq.quant_pack_groupwise([m], bits, group)
+        _check_quant(m, None, None, bits, group, codes[0], scales[0], zeros[0])
+        q = oracle.unpack_codes(codes[0].cpu().numpy(), bits, cols)
+        w = _np(m)
+        assert np.array_equal(q, oracle.quantize_groupwise_f64(w, None, None, bits, gg)[0]), (rows, cols)
+        assert oracle.near_tie_mask(w, None, None, bits, gg, 1e-12).any()
 
 
 def test_quant_batched_mixed_dtypes_and_edge_groups():
@@ -311,6 +341,9 @@ def test_ternary_matches_oracle(shape, dtype):
     assert np.array_equal(beta[0].cpu().numpy().view(np.uint32), b_ref.view(np.uint32))
     packed = oracle.pack_codes((q_ref + 1).astype(np.uint8), 2)
     assert np.array_equal(codes[0].cpu().numpy(), packed)
+    q_gpu = oracle.unpack_codes(codes[0].cpu().numpy(), 2, shape[1]).astype(np.int8) - 1
+    n, tot = _codes.ternary(_np(m), q_gpu)
+    assert n <= max(1, 1e-5 * tot)
     deq = woq.dequant_unpack([shape], codes, [beta[0]], 2, 0)[0]
     assert np.array_equal(deq.cpu().numpy(), oracle.ternary_dequantize(q_ref, b_ref))
 
@@ -327,14 +360,12 @@ def test_single_matrix_workload_end_to_end():
     np.testing.assert_allclose(t[0].cpu().numpy(), t_ref, rtol=1e-4)
     codes, scales, zeros = woq.quant_pack_groupwise([w], wl.bits, wl.group, row_scale=s, col_scale=t)
     _check_quant(w, s[0], t[0], wl.bits, wl.group, codes[0], scales[0], zeros[0])
-    # the fp64 quantiser fed with the same scales: only near ties may differ
+    # the fp64 definition fed with the same scales: only near ties may differ
     sg, tg = s[0].cpu().numpy(), t[0].cpu().numpy()
-    q64, d64, z64 = oracle.quantize_groupwise_f64(w.cpu().numpy(), sg, tg, wl.bits, wl.group)
     q_gpu = oracle.unpack_codes(codes[0].cpu().numpy(), wl.bits, 512)
-    diff = q_gpu != q64
-    tie = oracle.near_tie_fraction(w.cpu().numpy(), sg, tg, d64, z64, wl.bits, wl.group)
-    assert np.all(~diff | tie)
-    assert diff.mean() <= 1e-5
-    # fully independent fp64 path (its own scales): a handful of boundary flips at most
-    q_ind = oracle.quantize_groupwise_f64(w.cpu().numpy(), s_ref, t_ref, wl.bits, wl.group)[0]
-    assert (q_ind != q_gpu).mean() < 1e-3
+    _codes.within_budget([_codes.affine(w.cpu().numpy(), sg, tg, wl.bits, wl.group, q_gpu)])
+    # fully independent fp64 path (its own scales): codes move by at most
+    # one, on at most 1e-4 of the 131,072 (13 codes; the 1e-5 bar is
+    # checked on the full-size workloads, where it is meaningful)
+    n, tot = _codes.end_to_end(w.cpu().numpy(), s_ref, t_ref, wl.bits, wl.group, q_gpu)
+    assert n <= 1e-4 * tot

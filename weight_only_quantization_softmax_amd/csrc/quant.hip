@@ -10,7 +10,9 @@
 //
 // Every rounding decision is a fixed sequence of correctly rounded fp32
 // operations (__fmul_rn, __fsub_rn, __fdiv_rn, rintf = round half to even),
-// so codes, deltas and zero-points are reproducible bit for bit.
+// so codes, deltas and zero-points are reproducible bit for bit; ratios at or
+// next to a half-way point are taken by a correctly rounded division, so
+// exact half-way points round as the definition says (half to even).
 //
 // Work mapping:
 //  k_quant_tile   groups of 8..512 columns (powers of two): a workgroup
@@ -73,31 +75,59 @@ __device__ __forceinline__ void store_codes(uint8_t* codes, uint32_t e0, const u
 }
 
 struct GroupParams {
-    float delta, inv, z;
+    float delta, inv, z, d;
     bool ok;
 };
 
+// Per group: d = hi - lo, delta = d / (2^b - 1), inv = 1 / delta.  The
+// zero-point ratio -lo / delta is evaluated as ((2^b - 1) * -lo) / d with one
+// correctly rounded division: for bf16 / fp32 inputs without scales the
+// numerator and d are exact, so an exact half-way ratio (for example a group
+// with hi = -lo, ratio (2^b - 1) / 2) comes out as exactly k + 1/2 and rounds
+// half to even as the definition says.
 template <int BITS>
 __device__ __forceinline__ GroupParams group_params(float lo, float hi) {
     constexpr float qmax = (float)((1 << BITS) - 1);
     GroupParams g;
     lo = fminf(lo, 0.f);
     hi = fmaxf(hi, 0.f);
-    g.delta = __fdiv_rn(__fsub_rn(hi, lo), qmax);
+    g.d = __fsub_rn(hi, lo);
+    g.delta = __fdiv_rn(g.d, qmax);
     g.inv = __fdiv_rn(1.0f, g.delta);
     g.ok = isfinite(g.inv);
-    g.z = g.ok ? clampf(rintf(__fmul_rn(-lo, g.inv)), 0.f, qmax) : 0.f;
+    g.z = g.ok ? clampf(rintf(__fdiv_rn(__fmul_rn(-lo, qmax), g.d)), 0.f, qmax) : 0.f;
     return g;
 }
+
+// A fast ratio u = x * inv lies within a few ulps of the exact ratio
+// (2^b - 1) * x / d (about 6.8e-5 for 8-bit codes), so its rounding can
+// differ from the exact one only when u is within that distance of a
+// half-way point.  Such ratios (|u - rne(u)| > kNearHalf, rare) are
+// recomputed with one correctly rounded division, exact at exact half-way
+// points as for the zero-point.
+constexpr float kNearHalf = 0.5f - 0x1p-13f;
 
 template <int BITS>
 __device__ __forceinline__ void code8(const float (&x)[8], const GroupParams& g, uint32_t (&c)[8]) {
     constexpr float qmax = (float)((1 << BITS) - 1);
+    float r[8];
+    bool near = false;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        const float t = g.ok ? clampf(rintf(__fmul_rn(x[k], g.inv)) + g.z, 0.f, qmax) : 0.f;
-        c[k] = (uint32_t)t;
+        const float u = __fmul_rn(x[k], g.inv);
+        r[k] = rintf(u);
+        near |= fabsf(__fsub_rn(u, r[k])) > kNearHalf;
     }
+    if (near) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float u = __fmul_rn(x[k], g.inv);
+            if (fabsf(__fsub_rn(u, rintf(u))) > kNearHalf)
+                r[k] = rintf(__fdiv_rn(__fmul_rn(x[k], qmax), g.d));
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) c[k] = g.ok ? (uint32_t)clampf(r[k] + g.z, 0.f, qmax) : 0u;
 }
 
 // Code-book grid: a = max |x| of the group, inv = 1/a (0 when not finite,
@@ -309,7 +339,7 @@ __global__ __launch_bounds__(kT) void k_quant_tile(const QMat* __restrict__ mats
     float rsv[kTileRows];  // every load is issued before the first use
 #pragma unroll
     for (int r = 0; r < kTileRows; ++r) {
-        if (r < nr && active) raw[r] = load_raw<DT>(q.data, (uint32_t)(r0 + r) * (uint32_t)q.cols + col);
+        if (r < nr && active) raw[r] = load_raw<DT>(q.data, (uint32_t)(r0 + r) * (uint32_t)q.ld + col);
         rsv[r] = has_rs && r < nr ? gload<float>(q.rs + r0 + r) : 1.0f;
     }
     const CbTable* bk = stage_book<CB>(book);
@@ -353,9 +383,10 @@ __global__ __launch_bounds__(kT) void k_quant_wave(const QMat* __restrict__ mats
     const uint32_t ng = (uint32_t)q.rows * (uint32_t)q.cols / (uint32_t)q.group;
     const uint32_t gi = (uint32_t)(u - ubeg[m]) * (kT / 64) + (threadIdx.x >> 6);
     const bool live = gi < ng;  // whole wave
-    const uint32_t gbase = live ? gi * (uint32_t)q.group : 0u;
+    const uint32_t gbase = live ? gi * (uint32_t)q.group : 0u;  // codes (contiguous)
     const uint32_t row = gbase / (uint32_t)q.cols;
     const uint32_t col0 = gbase - row * (uint32_t)q.cols;
+    const uint32_t ibase = row * (uint32_t)q.ld + col0;           // weights (row stride ld)
     const int nvg = q.group >> 3;
     const bool has_rs = q.rs != nullptr, has_ct = q.ct != nullptr;
     const float rsv = has_rs && live ? gload<float>(q.rs + row) : 1.0f;
@@ -364,7 +395,7 @@ __global__ __launch_bounds__(kT) void k_quant_wave(const QMat* __restrict__ mats
 #pragma unroll
     for (int k = 0; k < NVL; ++k) {
         const int v = lane + 64 * k;
-        if (live && v < nvg) raw[k] = load_raw<DT>(q.data, gbase + 8u * v);
+        if (live && v < nvg) raw[k] = load_raw<DT>(q.data, ibase + 8u * v);
     }
     const CbTable* bk = stage_book<CB>(book);
     if (!live) return;  // after the workgroup barrier; none below
@@ -410,9 +441,10 @@ __global__ __launch_bounds__(kT) void k_quant_big(const QMat* __restrict__ mats,
     const int m = find_unit_owner(ubeg, nmat, u);
     const QMat q = mats[m];
     const uint32_t gl = (uint32_t)(u - ubeg[m]);
-    const uint32_t gbase = gl * (uint32_t)q.group;
+    const uint32_t gbase = gl * (uint32_t)q.group;               // codes (contiguous)
     const uint32_t row = gbase / (uint32_t)q.cols;
     const uint32_t col0 = gbase - row * (uint32_t)q.cols;
+    const uint32_t ibase = row * (uint32_t)q.ld + col0;          // weights (row stride ld)
     const int nvg = q.group >> 3;
     const bool has_rs = q.rs != nullptr, has_ct = q.ct != nullptr;
     const float rsv = has_rs ? gload<float>(q.rs + row) : 1.0f;
@@ -421,7 +453,7 @@ __global__ __launch_bounds__(kT) void k_quant_big(const QMat* __restrict__ mats,
 #pragma unroll
     for (int k = 0; k < MAXV; ++k) {
         const int v = threadIdx.x + kT * k;
-        if (v < nvg) raw[k] = load_raw<DT>(q.data, gbase + 8u * v);
+        if (v < nvg) raw[k] = load_raw<DT>(q.data, ibase + 8u * v);
     }
     const CbTable* bk = stage_book<CB>(book);
     float lo = INFINITY, hi = -INFINITY;
@@ -536,7 +568,7 @@ __global__ __launch_bounds__(kT) void k_dequant(const QMat* __restrict__ mats,
 #pragma unroll
     for (int r = 0; r < kDTileRows; ++r) {
         if (r >= nr) break;
-        const uint32_t e0 = (uint32_t)(r0 + r) * (uint32_t)q.cols + col;
+        const uint32_t e0 = (uint32_t)(r0 + r) * (uint32_t)q.ld + col;  // output row stride ld
         float y[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {  // absent scales are exactly 1 (identity)
@@ -570,13 +602,14 @@ __global__ __launch_bounds__(kT) void k_ternary(const QMat* __restrict__ mats,
     const int m = find_unit_owner(ubeg, nmat, u);
     const QMat q = mats[m];
     const uint32_t row = (uint32_t)(u - ubeg[m]);
-    const uint32_t rbase = row * (uint32_t)q.cols;
+    const uint32_t rbase = row * (uint32_t)q.cols;   // codes (contiguous)
+    const uint32_t ibase = row * (uint32_t)q.ld;     // weights (row stride ld)
     const int nv = q.cols >> 3;
     Raw8<DT> raw[MAXV];
 #pragma unroll
     for (int k = 0; k < MAXV; ++k) {
         const int v = threadIdx.x + kT * k;
-        if (v < nv) raw[k] = load_raw<DT>(q.data, rbase + 8u * v);
+        if (v < nv) raw[k] = load_raw<DT>(q.data, ibase + 8u * v);
     }
     double acc = 0.0;
 #pragma unroll

@@ -24,8 +24,14 @@
  *           metadata bo tro" (lossless code for the blocks kept in bf16).
  *
  * Conventions shared by every entry point
- *  - Matrices are row-major, contiguous, [rows, cols] = [out_features,
- *    in_features]; dtype WOQ_F32 or WOQ_BF16; data 16-byte aligned.
+ *  - Matrices are row-major, [rows, cols] = [out_features, in_features], with
+ *    a row stride `ld` (elements between the starts of consecutive rows):
+ *    contiguous (ld = 0 or ld = cols), or ld > cols with ld % 8 == 0 and
+ *    cols % 8 == 0 (16-byte rows; for example the q, k or v columns of a fused
+ *    [d, 3d] projection weight, or one expert of a [rows, E * cols] tensor);
+ *    dtype WOQ_F32 or WOQ_BF16; data 16-byte aligned.  Outputs the library
+ *    writes (codes, scales, zero-points) are always contiguous; the lossless
+ *    exponent code (df11_*) takes contiguous matrices only.
  *  - Every tensor pointer (inputs, outputs, workspace) is a DEVICE pointer
  *    owned by the caller.  Arrays of descriptors / pointers (the woq_mat
  *    arrays, the `float* const*` style arrays, block_id) are HOST memory read
@@ -36,11 +42,19 @@
  *    outputs are valid once the stream has synchronised.  Calls that share a
  *    workspace must be ordered on one stream.
  *  - `ws`/`ws_bytes` is a caller-provided device workspace of at least
- *    woq_workspace_size() bytes (256-byte aligned).
+ *    woq_workspace_size() bytes (256-byte aligned).  Its first WOQ_WS_HEAD
+ *    bytes are a status head: ewq_block_entropy and sinq_balance[_ex] write
+ *    there, as a uint64 at byte 0, the number of non-finite weights (NaN,
+ *    +-inf) among those the call reads (every weight once, however many
+ *    iterations), valid once the stream has synchronised.  Other calls leave
+ *    the head untouched.
  *  - Every argument error is detected on the host BEFORE anything is
  *    enqueued and before any HIP call; the return value is a WOQ_* status.
- *  - Non-finite weights give NaN entropies / scales and unspecified codes.
- *  - Limits: rows, cols >= 1; rows*cols < 2^31 per matrix; n_mats <= 2^20.
+ *  - Non-finite weights give NaN entropies / scales and unspecified codes
+ *    (and are counted in the workspace head, above).
+ *  - Limits: rows, cols >= 1; rows * max(ld, cols) < 2^31 per matrix;
+ *    n_mats <= 2^20.  WOQ_ERR_SHAPE otherwise, and for an ld that is neither
+ *    0, cols, nor a multiple of 8 above cols (with cols % 8 == 0).
  */
 #ifndef WOQ_H_
 #define WOQ_H_
@@ -71,6 +85,9 @@ extern "C" {
 #define WOQ_F32  0
 #define WOQ_BF16 1
 
+/* bytes at the start of every workspace reserved for the status head */
+#define WOQ_WS_HEAD 256
+
 /* operation ids for woq_workspace_size */
 #define WOQ_OP_ENTROPY 1
 #define WOQ_OP_SINQ    2
@@ -81,13 +98,16 @@ extern "C" {
 #define WOQ_OP_DF11_ENCODE 7
 #define WOQ_OP_DF11_DECODE 8
 
-/* One matrix.  For dequant_unpack it describes the OUTPUT (written). */
+/* One matrix.  For dequant_unpack / dequant_codebook / df11_decode it
+ * describes the OUTPUT (written). */
 typedef struct woq_mat {
-    void*   data;      /* device pointer, row-major contiguous, 16-B aligned */
+    void*   data;      /* device pointer, row-major, 16-B aligned */
     int32_t dtype;     /* WOQ_F32 or WOQ_BF16 */
     int32_t reserved;  /* must be 0 */
     int64_t rows;
     int64_t cols;
+    int64_t ld;        /* row stride in elements: 0 or cols (contiguous), or
+                          > cols, a multiple of 8 (then cols % 8 == 0) */
 } woq_mat;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -138,7 +158,8 @@ int32_t ewq_block_entropy(const woq_mat* mats, int32_t n_mats,
  *  col_scale [n_mats] host array of device float[cols]   (t, written)
  *  Requires cols % 8 == 0 and cols <= 32768 (WOQ_ERR_SHAPE otherwise: a
  *  row is held by one workgroup).  fp32 element arithmetic with fp64
- *  reductions in a fixed order (deterministic).
+ *  reductions in a fixed order (deterministic).  The non-finite weights are
+ *  counted during the first iteration (workspace head).
  */
 int32_t sinq_balance(const woq_mat* mats, int32_t n_mats, int32_t iters,
                      float* const* row_scale, float* const* col_scale,
@@ -180,8 +201,11 @@ int32_t sinq_balance_ex(const woq_mat* mats, int32_t n_mats, int32_t iters, int3
  *         bits [b*j, b*j + b) of its row's little-endian byte string.
  *  scales [n_mats] device float[rows * cols / group]   (delta, row-major)
  *  zeros  [n_mats] device uint8[rows * cols / group]   (z)
- *  bits in {2, 3, 4, 8}; group % 8 == 0, cols % group == 0, group <= 32768.
- *  group == cols gives one scale per row (EWQ's 8-bit tier).
+ *  bits in {2, 3, 4, 8}; group % 8 == 0, cols % group == 0; group == 0
+ *  means group = cols, one scale per row (EWQ's 8-bit tier).  Groups that
+ *  are not a power of two of at most 512 columns are held by one workgroup:
+ *  at most 32768 columns for BF16 and 16384 for F32 (WOQ_ERR_SHAPE above,
+ *  including group == 0 on wider rows).
  */
 int32_t quant_pack_groupwise(const woq_mat* mats, int32_t n_mats,
                              const float* const* row_scale,
@@ -192,7 +216,12 @@ int32_t quant_pack_groupwise(const woq_mat* mats, int32_t n_mats,
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * dequant_unpack -- inverse map of quant_pack_groupwise / ternary_pack:
+ * dequant_unpack -- inverse map of quant_pack_groupwise / ternary_pack: the
+ *  integer codes back to weights, the reverse of the float -> low-bit
+ *  integer mapping of [QG] "Giai thich ve Quantization: huong dan ngan gon
+ *  cho LLMs" (kungfutech.edu.vn), section "Luong Tu Hoa La Gi?", with the
+ *  balancing undone ([SINQ] "Dinh ty le tren hai truc": W = s t^T o
+ *  balanced matrix):
  *  W'_ij = (((q - z) * delta) * s_i) * t_j in fp32 (one rounding per
  *  product), written as F32 or BF16 (round to nearest even) into out[m].
  *  zeros NULL (array or entry) means z = 2^(b-1) - 1 for every group, which
@@ -216,7 +245,8 @@ int32_t dequant_unpack(const woq_mat* out, int32_t n_mats,
  *  LSB-first per row (cols / 4 bytes per row).
  *  codes     [n_mats] device uint8[rows * cols / 4]
  *  row_scale [n_mats] device float[rows]  (beta, written)
- *  Requires cols % 8 == 0.
+ *  Requires cols % 8 == 0 and a row held by one workgroup: cols <= 32768
+ *  for BF16 and <= 16384 for F32 (WOQ_ERR_SHAPE otherwise).
  */
 int32_t ternary_pack(const woq_mat* mats, int32_t n_mats,
                      uint8_t* const* codes, float* const* row_scale,

@@ -171,3 +171,58 @@ def test_normal_code_book_matches_oracle(bits):
     got = np.frombuffer(out, dtype=np.float32)
     ref = codebook.normal_levels(bits)
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def _smat(rows, cols, ld, dtype=_lib.WOQ_BF16):
+    return _lib.mat_array([(FAKE, dtype, rows, cols, ld)])
+
+
+def test_row_stride_rules():
+    # 0 or cols: contiguous; above cols: a multiple of 8 with cols % 8 == 0
+    for op in (_lib.OP_ENTROPY, _lib.OP_SINQ, _lib.OP_TERNARY):
+        assert _ws_size(op, _smat(16, 64, 0))[0] == 0
+        assert _ws_size(op, _smat(16, 64, 64))[0] == 0
+        assert _ws_size(op, _smat(16, 64, 192))[0] == 0
+        assert _ws_size(op, _smat(16, 64, 72))[0] == 0
+        assert _ws_size(op, _smat(16, 64, 68))[0] == 2      # not a multiple of 8
+        assert _ws_size(op, _smat(16, 64, 56))[0] == 2      # shorter than a row
+        assert _ws_size(op, _smat(16, 64, -8))[0] == 2
+    assert _ws_size(_lib.OP_ENTROPY, _smat(16, 60, 60))[0] == 0    # contiguous, any width
+    assert _ws_size(_lib.OP_ENTROPY, _smat(16, 60, 64))[0] == 2    # strided needs cols % 8
+    # rows * ld must stay below 2^31
+    assert _ws_size(_lib.OP_ENTROPY, _smat(1 << 15, 64, (1 << 16) - 8))[0] == 0
+    assert _ws_size(_lib.OP_ENTROPY, _smat(1 << 15, 64, 1 << 16))[0] == 2
+    assert _ws_size(_lib.OP_QUANT, _smat(16, 128, 256), group=64)[0] == 0
+    # the lossless exponent code takes contiguous matrices only
+    lib = _lib.load()
+    assert lib.df11_exponent_histogram(_smat(16, 64, 128), 1, FAKE, FAKE, 1 << 30, None) == 2
+    assert lib.df11_exponent_histogram(_smat(16, 64, 64), 1, FAKE, FAKE, 8, None) == 6
+
+
+def test_workspace_head_is_reserved():
+    # every layout starts after the status head, so the smallest workspace
+    # is larger than the head
+    for op in (_lib.OP_ENTROPY, _lib.OP_SINQ, _lib.OP_QUANT, _lib.OP_DEQUANT, _lib.OP_TERNARY,
+               _lib.OP_DF11_HIST, _lib.OP_DF11_ENCODE, _lib.OP_DF11_DECODE):
+        st, b = _ws_size(op, _mat(), group=64)
+        assert st == 0 and b > _lib.WS_HEAD, op
+
+
+def test_documented_group_and_row_limits():
+    # groups that are not a power of two <= 512 are held by one workgroup:
+    # at most 32768 columns (bf16) and 16384 (fp32); group 0 means cols
+    bf, f32 = _lib.WOQ_BF16, _lib.WOQ_F32
+    assert _ws_size(_lib.OP_QUANT, _smat(2, 32768, 0, bf), group=0)[0] == 0
+    assert _ws_size(_lib.OP_QUANT, _smat(2, 32776, 0, bf), group=0)[0] == 2
+    assert _ws_size(_lib.OP_QUANT, _smat(2, 16384, 0, f32), group=0)[0] == 0
+    assert _ws_size(_lib.OP_QUANT, _smat(2, 16392, 0, f32), group=0)[0] == 2
+    assert _ws_size(_lib.OP_QUANT, _smat(2, 2 * 16392, 0, f32), group=16392)[0] == 2
+    assert _ws_size(_lib.OP_QUANT, _smat(2, 2 * 16392, 0, bf), group=16392)[0] == 0
+    # power-of-two groups <= 512 take row tiles: any row width
+    assert _ws_size(_lib.OP_QUANT, _smat(2, 65536, 0, f32), group=512)[0] == 0
+    # ternary: one workgroup per row
+    lib = _lib.load()
+    one = (ctypes.c_void_p * 1)(FAKE)
+    pp = ctypes.cast(one, _lib.PP)
+    assert lib.ternary_pack(_smat(2, 32776, 0, bf), 1, pp, pp, FAKE, 1 << 30, None) == 2
+    assert lib.ternary_pack(_smat(2, 16392, 0, f32), 1, pp, pp, FAKE, 1 << 30, None) == 2

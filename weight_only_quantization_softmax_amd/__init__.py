@@ -8,7 +8,12 @@ kernels.  There is no CPU or PyTorch fallback: if libwoq.so is missing the
 calls raise.  Since the library takes raw pointers, the binding first checks
 that every tensor is on one GPU and that caller-supplied buffers come one per
 matrix, with the right dtype and at least the size the call reads or writes
-(ValueError / TypeError before anything is enqueued).
+(ValueError / TypeError before anything is enqueued).  Input matrices may be
+row-strided views (unit column stride, row stride >= cols, for example a
+column slice of a fused projection weight); they are passed with their row
+stride.  Workspaces and outputs the binding allocates are allocated on the
+stream the call runs on, so the caching allocator never hands their memory
+to another stream while the call's kernels may still use it.
 
   ewq_block_entropy     EWQ per-matrix softmax entropy, block entropy, tiers
   sinq_balance          SINQ dual-axis Sinkhorn std balancing -> (s, t)
@@ -24,6 +29,7 @@ matrix, with the right dtype and at least the size the call reads or writes
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 from typing import Optional, Sequence
 
@@ -36,7 +42,7 @@ __all__ = ["ewq_block_entropy", "sinq_balance", "quant_pack_groupwise",
            "dequant_unpack", "ternary_pack", "ewq_budget_levels", "workspace_size", "WoqError",
            "df11_buffer_sizes", "df11_exponent_histogram", "df11_build_code", "df11_encode",
            "df11_decode", "df11_compress", "codebook_normal", "quant_pack_codebook",
-           "dequant_codebook"]
+           "dequant_codebook", "nonfinite_count"]
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -47,20 +53,29 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _ld(t: torch.Tensor) -> int:
+    """Row stride passed to the library: 0 for a contiguous matrix, else the
+    tensor's row stride (the library checks its rules)."""
+    return 0 if t.is_contiguous() else int(t.stride(0))
+
+
 def _check_mats(tensors: Sequence[torch.Tensor]) -> None:
     if len(tensors) == 0:
         raise ValueError("at least one matrix is required")
     for t in tensors:
-        if t.dim() != 2 or not t.is_contiguous():
-            raise ValueError("matrices must be 2-D and contiguous")
+        if t.dim() != 2:
+            raise ValueError("matrices must be 2-D")
         if t.shape[0] < 1 or t.shape[1] < 1:
             raise ValueError(f"empty matrix of shape {tuple(t.shape)}")
+        if not t.is_contiguous() and (t.stride(1) != 1 or t.stride(0) < t.shape[1]):
+            raise ValueError("matrices must be contiguous or row-strided views "
+                             f"(unit column stride), got strides {tuple(t.stride())}")
         _dtype_code(t)
 
 
 def _mats(tensors: Sequence[torch.Tensor]):
     _check_mats(tensors)
-    return _lib.mat_array((t.data_ptr(), _dtype_code(t), t.shape[0], t.shape[1])
+    return _lib.mat_array((t.data_ptr(), _dtype_code(t), t.shape[0], t.shape[1], _ld(t))
                           for t in tensors)
 
 
@@ -117,6 +132,23 @@ def _stream(stream, device=None) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _on(stream, device):
+    """Context for the binding's own allocations: the call's stream when one is
+    given (a torch stream or a raw handle), so that the caching allocator
+    keeps the memory for that stream; otherwise the current stream."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream), device=device)
+    return torch.cuda.stream(stream)
+
+
+def nonfinite_count(ws: torch.Tensor) -> torch.Tensor:
+    """The non-finite weight count that ewq_block_entropy and sinq_balance
+    write into the head of their workspace: an int64 view of ws[0:8]."""
+    return ws[:8].view(torch.int64)
+
+
 def _ptrs(ts):
     if ts is None:
         return None
@@ -133,11 +165,15 @@ def workspace_size(op: int, mats: Sequence[torch.Tensor], group: int = 0) -> int
 
 
 def _workspace(op, mats, group, ws, device):
+    """The caller's workspace, or a new one on the current stream (callers
+    allocate inside ``_on``)."""
     if ws is not None and ws.dtype != torch.uint8:
         raise TypeError(f"workspace must be uint8 (bytes), got {ws.dtype}")
+    if ws is not None and not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     need = workspace_size(op, mats, group)
     if ws is None or ws.numel() < need:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(need, _lib.WS_HEAD), dtype=torch.uint8, device=device)
     return ws
 
 
@@ -151,12 +187,13 @@ def ewq_block_entropy(mats: Sequence[torch.Tensor], block_id: Optional[Sequence[
         raise ValueError(f"block_id: {len(block_id)} ids for {n} matrices")
     dev = _device(mats, ws)
     arr = _mats(mats)
-    h_mat = torch.empty(n, dtype=torch.float64, device=dev)
-    h_block = torch.empty(n_blocks, dtype=torch.float64, device=dev)
-    stats = torch.empty(3, dtype=torch.float64, device=dev)
-    tier = torch.empty(n_blocks, dtype=torch.int32, device=dev)
-    order = torch.empty(n_blocks, dtype=torch.int32, device=dev)
-    ws = _workspace(_lib.OP_ENTROPY, mats, 0, ws, dev)
+    with _on(stream, dev):
+        h_mat = torch.empty(n, dtype=torch.float64, device=dev)
+        h_block = torch.empty(n_blocks, dtype=torch.float64, device=dev)
+        stats = torch.empty(3, dtype=torch.float64, device=dev)
+        tier = torch.empty(n_blocks, dtype=torch.int32, device=dev)
+        order = torch.empty(n_blocks, dtype=torch.int32, device=dev)
+        ws = _workspace(_lib.OP_ENTROPY, mats, 0, ws, dev)
     bid = None
     if block_id is not None:
         bid = (ctypes.c_int32 * n)(*[int(b) for b in block_id])
@@ -164,7 +201,8 @@ def ewq_block_entropy(mats: Sequence[torch.Tensor], block_id: Optional[Sequence[
                                h_block.data_ptr(), stats.data_ptr(), tier.data_ptr(),
                                order.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream, dev))
     _lib.check("ewq_block_entropy", st)
-    return {"h_mat": h_mat, "h_block": h_block, "stats": stats, "tier": tier, "order": order}
+    return {"h_mat": h_mat, "h_block": h_block, "stats": stats, "tier": tier, "order": order,
+            "nonfinite": nonfinite_count(ws)}
 
 
 def sinq_balance(mats: Sequence[torch.Tensor], iters: int, *, rms: bool = False,
@@ -179,11 +217,12 @@ def sinq_balance(mats: Sequence[torch.Tensor], iters: int, *, rms: bool = False,
     _check_bufs("col_scale", col_scale, [m.shape[1] for m in mats], torch.float32)
     dev = _device(mats, row_scale, col_scale, ws)
     arr = _mats(mats)
-    if row_scale is None:
-        row_scale = [torch.empty(m.shape[0], dtype=torch.float32, device=dev) for m in mats]
-    if col_scale is None:
-        col_scale = [torch.empty(m.shape[1], dtype=torch.float32, device=dev) for m in mats]
-    ws = _workspace(_lib.OP_SINQ, mats, 0, ws, dev)
+    with _on(stream, dev):
+        if row_scale is None:
+            row_scale = [torch.empty(m.shape[0], dtype=torch.float32, device=dev) for m in mats]
+        if col_scale is None:
+            col_scale = [torch.empty(m.shape[1], dtype=torch.float32, device=dev) for m in mats]
+        ws = _workspace(_lib.OP_SINQ, mats, 0, ws, dev)
     flags = (_lib.WOQ_SINQ_RMS if rms else 0) | (_lib.WOQ_SINQ_SHARED if shared else 0)
     if flags:
         st = lib.sinq_balance_ex(arr, len(mats), int(iters), flags, _ptrs(row_scale),
@@ -212,16 +251,17 @@ def quant_pack_groupwise(mats: Sequence[torch.Tensor], bits: int, group: int, *,
     _check_bufs("zeros", zeros, [m.shape[0] * (m.shape[1] // g(m)) for m in mats], torch.uint8)
     dev = _device(mats, row_scale, col_scale, codes, scales, zeros, ws)
     arr = _mats(mats)
-    if codes is None:
-        codes = [torch.empty(m.shape[0], m.shape[1] * bits // 8, dtype=torch.uint8, device=dev)
-                 for m in mats]
-    if scales is None:
-        scales = [torch.empty(m.shape[0], m.shape[1] // g(m), dtype=torch.float32, device=dev)
-                  for m in mats]
-    if zeros is None:
-        zeros = [torch.empty(m.shape[0], m.shape[1] // g(m), dtype=torch.uint8, device=dev)
-                 for m in mats]
-    ws = _workspace(_lib.OP_QUANT, mats, group, ws, dev)
+    with _on(stream, dev):
+        if codes is None:
+            codes = [torch.empty(m.shape[0], m.shape[1] * bits // 8, dtype=torch.uint8, device=dev)
+                     for m in mats]
+        if scales is None:
+            scales = [torch.empty(m.shape[0], m.shape[1] // g(m), dtype=torch.float32, device=dev)
+                      for m in mats]
+        if zeros is None:
+            zeros = [torch.empty(m.shape[0], m.shape[1] // g(m), dtype=torch.uint8, device=dev)
+                     for m in mats]
+        ws = _workspace(_lib.OP_QUANT, mats, group, ws, dev)
     st = lib.quant_pack_groupwise(arr, len(mats), _ptrs(row_scale), _ptrs(col_scale), int(bits),
                                   int(group), _ptrs(codes), _ptrs(scales), _ptrs(zeros),
                                   ws.data_ptr(), ws.numel(), _stream(stream, dev))
@@ -247,10 +287,11 @@ def dequant_unpack(shapes, codes, scales, bits: int, group: int, *, zeros=None, 
     if out is not None and [tuple(o.shape) for o in out] != shapes:
         raise ValueError("out: tensors do not have the given shapes")
     dev = _device(codes, scales, zeros, row_scale, col_scale, out, ws)
-    if out is None:
-        out = [torch.empty(r, c, dtype=out_dtype, device=dev) for (r, c) in shapes]
-    arr = _mats(out)
-    ws = _workspace(_lib.OP_DEQUANT, out, group, ws, dev)
+    with _on(stream, dev):
+        if out is None:
+            out = [torch.empty(r, c, dtype=out_dtype, device=dev) for (r, c) in shapes]
+        arr = _mats(out)
+        ws = _workspace(_lib.OP_DEQUANT, out, group, ws, dev)
     st = lib.dequant_unpack(arr, len(out), _ptrs(codes), _ptrs(scales), _ptrs(zeros),
                             _ptrs(row_scale), _ptrs(col_scale), int(bits), int(group),
                             ws.data_ptr(), ws.numel(), _stream(stream, dev))
@@ -291,13 +332,14 @@ def quant_pack_codebook(mats: Sequence[torch.Tensor], bits: int, group: int, *, 
     _check_bufs("scales", scales, [m.shape[0] * (m.shape[1] // g(m)) for m in mats], torch.float32)
     dev = _device(mats, row_scale, col_scale, codes, scales, ws)
     arr = _mats(mats)
-    if codes is None:
-        codes = [torch.empty(m.shape[0], m.shape[1] * bits // 8, dtype=torch.uint8, device=dev)
-                 for m in mats]
-    if scales is None:
-        scales = [torch.empty(m.shape[0], m.shape[1] // g(m), dtype=torch.float32, device=dev)
-                  for m in mats]
-    ws = _workspace(_lib.OP_QUANT, mats, group, ws, dev)
+    with _on(stream, dev):
+        if codes is None:
+            codes = [torch.empty(m.shape[0], m.shape[1] * bits // 8, dtype=torch.uint8, device=dev)
+                     for m in mats]
+        if scales is None:
+            scales = [torch.empty(m.shape[0], m.shape[1] // g(m), dtype=torch.float32, device=dev)
+                      for m in mats]
+        ws = _workspace(_lib.OP_QUANT, mats, group, ws, dev)
     st = lib.quant_pack_codebook(arr, len(mats), _ptrs(row_scale), _ptrs(col_scale), int(bits),
                                  int(group), lv, _ptrs(codes), _ptrs(scales), ws.data_ptr(),
                                  ws.numel(), _stream(stream, dev))
@@ -323,10 +365,11 @@ def dequant_codebook(shapes, codes, scales, bits: int, group: int, *, levels=Non
     if out is not None and [tuple(o.shape) for o in out] != shapes:
         raise ValueError("out: tensors do not have the given shapes")
     dev = _device(codes, scales, row_scale, col_scale, out, ws)
-    if out is None:
-        out = [torch.empty(r, c, dtype=out_dtype, device=dev) for (r, c) in shapes]
-    arr = _mats(out)
-    ws = _workspace(_lib.OP_DEQUANT, out, group, ws, dev)
+    with _on(stream, dev):
+        if out is None:
+            out = [torch.empty(r, c, dtype=out_dtype, device=dev) for (r, c) in shapes]
+        arr = _mats(out)
+        ws = _workspace(_lib.OP_DEQUANT, out, group, ws, dev)
     st = lib.dequant_codebook(arr, len(out), _ptrs(codes), _ptrs(scales), _ptrs(row_scale),
                               _ptrs(col_scale), int(bits), int(group), lv, ws.data_ptr(),
                               ws.numel(), _stream(stream, dev))
@@ -343,12 +386,13 @@ def ternary_pack(mats: Sequence[torch.Tensor], *, codes=None, row_scale=None, ws
     _check_bufs("row_scale", row_scale, [m.shape[0] for m in mats], torch.float32)
     dev = _device(mats, codes, row_scale, ws)
     arr = _mats(mats)
-    if codes is None:
-        codes = [torch.empty(m.shape[0], m.shape[1] // 4, dtype=torch.uint8, device=dev)
-                 for m in mats]
-    if row_scale is None:
-        row_scale = [torch.empty(m.shape[0], dtype=torch.float32, device=dev) for m in mats]
-    ws = _workspace(_lib.OP_TERNARY, mats, 0, ws, dev)
+    with _on(stream, dev):
+        if codes is None:
+            codes = [torch.empty(m.shape[0], m.shape[1] // 4, dtype=torch.uint8, device=dev)
+                     for m in mats]
+        if row_scale is None:
+            row_scale = [torch.empty(m.shape[0], dtype=torch.float32, device=dev) for m in mats]
+        ws = _workspace(_lib.OP_TERNARY, mats, 0, ws, dev)
     st = lib.ternary_pack(arr, len(mats), _ptrs(codes), _ptrs(row_scale), ws.data_ptr(),
                           ws.numel(), _stream(stream, dev))
     _lib.check("ternary_pack", st)
@@ -391,9 +435,10 @@ def df11_exponent_histogram(mats: Sequence[torch.Tensor], *, hist=None, ws=None,
         _check_bufs("hist", [hist], [256 * len(mats)], torch.int32)
     dev = _device(mats, hist, ws)
     arr = _mats(mats)
-    if hist is None:
-        hist = torch.empty(len(mats), 256, dtype=torch.int32, device=dev)
-    ws = _workspace(_lib.OP_DF11_HIST, mats, 0, ws, dev)
+    with _on(stream, dev):
+        if hist is None:
+            hist = torch.empty(len(mats), 256, dtype=torch.int32, device=dev)
+        ws = _workspace(_lib.OP_DF11_HIST, mats, 0, ws, dev)
     st = lib.df11_exponent_histogram(arr, len(mats), hist.data_ptr(), ws.data_ptr(), ws.numel(),
                                      _stream(stream, dev))
     _lib.check("df11_exponent_histogram", st)
@@ -443,25 +488,26 @@ def df11_encode(mats: Sequence[torch.Tensor], codes, *, ws=None, stream=None):
     host = np.concatenate([np.concatenate([np.ascontiguousarray(c["tables"], dtype=np.uint8).reshape(-1),
                                            np.ascontiguousarray(c["code_len"], dtype=np.uint8)])
                            for c in codes])
-    meta = torch.from_numpy(host).to(dev)
     outs, off = [], 0
-    for m, c in zip(mats, codes):
-        _, eb, gb, nb = df11_buffer_sizes(m.numel(), c["total_bits"])
-        nt = int(c["tables"].shape[0])
-        outs.append({
-            "enc": torch.empty(eb, dtype=torch.uint8, device=dev),
-            "sm": torch.empty(m.numel(), dtype=torch.uint8, device=dev),
-            "gaps": torch.empty(gb, dtype=torch.uint8, device=dev),
-            "block_pos": torch.empty(nb + 1, dtype=torch.int32, device=dev),
-            "tables": meta[off:off + 256 * nt],
-            "code_len": meta[off + 256 * nt:off + 256 * nt + 256],
-            "n_tables": nt, "total_bits": int(c["total_bits"]),
-            "shape": tuple(m.shape)})
-        off += 256 * nt + 256
+    with _on(stream, dev):
+        meta = torch.from_numpy(host).to(dev)
+        for m, c in zip(mats, codes):
+            _, eb, gb, nb = df11_buffer_sizes(m.numel(), c["total_bits"])
+            nt = int(c["tables"].shape[0])
+            outs.append({
+                "enc": torch.empty(eb, dtype=torch.uint8, device=dev),
+                "sm": torch.empty(m.numel(), dtype=torch.uint8, device=dev),
+                "gaps": torch.empty(gb, dtype=torch.uint8, device=dev),
+                "block_pos": torch.empty(nb + 1, dtype=torch.int32, device=dev),
+                "tables": meta[off:off + 256 * nt],
+                "code_len": meta[off + 256 * nt:off + 256 * nt + 256],
+                "n_tables": nt, "total_bits": int(c["total_bits"]),
+                "shape": tuple(m.shape)})
+            off += 256 * nt + 256
+        ws = _workspace(_lib.OP_DF11_ENCODE, mats, 0, ws, dev)
     cl = [np.ascontiguousarray(c["code_len"], dtype=np.uint8) for c in codes]
     cw = [np.ascontiguousarray(c["codeword"], dtype=np.uint32) for c in codes]
     tb = (ctypes.c_int64 * len(mats))(*[c["total_bits"] for c in codes])
-    ws = _workspace(_lib.OP_DF11_ENCODE, mats, 0, ws, dev)
     st = lib.df11_encode(arr, len(mats), _host_ptrs(cl), _host_ptrs(cw), tb,
                          _ptrs([o["enc"] for o in outs]), _ptrs([o["sm"] for o in outs]),
                          _ptrs([o["gaps"] for o in outs]), _ptrs([o["block_pos"] for o in outs]),
@@ -486,12 +532,13 @@ def df11_decode(encoded, *, out=None, ws=None, stream=None):
         raise ValueError("out: tensors do not have the encoded shapes")
     dev = _device([e[k] for e in encoded for k in ("enc", "sm", "gaps", "block_pos", "tables",
                                                     "code_len")], out, ws)
-    if out is None:
-        out = [torch.empty(e["shape"], dtype=torch.bfloat16, device=dev) for e in encoded]
-    arr = _mats(out)
+    with _on(stream, dev):
+        if out is None:
+            out = [torch.empty(e["shape"], dtype=torch.bfloat16, device=dev) for e in encoded]
+        arr = _mats(out)
+        ws = _workspace(_lib.OP_DF11_DECODE, out, 0, ws, dev)
     nt = (ctypes.c_int32 * len(out))(*[e["n_tables"] for e in encoded])
     tb = (ctypes.c_int64 * len(out))(*[e["total_bits"] for e in encoded])
-    ws = _workspace(_lib.OP_DF11_DECODE, out, 0, ws, dev)
     st = lib.df11_decode(arr, len(out), _ptrs([e["enc"] for e in encoded]),
                          _ptrs([e["sm"] for e in encoded]), _ptrs([e["gaps"] for e in encoded]),
                          _ptrs([e["block_pos"] for e in encoded]),

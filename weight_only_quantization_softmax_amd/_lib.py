@@ -32,10 +32,13 @@ EXPORTS = ("woq_status_string", "woq_workspace_size", "ewq_block_entropy",
            "dequant_codebook", "woq_codebook_normal")
 
 
+WS_HEAD = 256   # WOQ_WS_HEAD: the workspace's status head (non-finite count at byte 0)
+
+
 class WoqMat(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
                 ("reserved", ctypes.c_int32), ("rows", ctypes.c_int64),
-                ("cols", ctypes.c_int64)]
+                ("cols", ctypes.c_int64), ("ld", ctypes.c_int64)]
 
 
 class WoqError(RuntimeError):
@@ -118,15 +121,18 @@ def check(fn: str, status: int) -> None:
 
 
 def mat_array(descs):
-    """descs: iterable of (data_ptr, dtype, rows, cols) -> ctypes WoqMat array."""
+    """descs: iterable of (data_ptr, dtype, rows, cols[, ld]) -> ctypes WoqMat
+    array (ld 0 = contiguous)."""
     descs = list(descs)
     arr = (WoqMat * len(descs))()
-    for i, (ptr, dt, r, c) in enumerate(descs):
+    for i, d in enumerate(descs):
+        ptr, dt, r, c = d[:4]
         arr[i].data = ptr
         arr[i].dtype = dt
         arr[i].reserved = 0
         arr[i].rows = r
         arr[i].cols = c
+        arr[i].ld = d[4] if len(d) > 4 else 0
     return arr
 
 

@@ -2,11 +2,13 @@
 // descriptor staging and kernel sequencing on the caller's stream.
 //
 // Every argument check runs on the host before the first HIP call, so an
-// invalid call enqueues nothing.  Descriptor tables are built in host memory
-// and copied into the head of the caller's workspace with one
-// hipMemcpyAsync (pageable source: the runtime stages it before returning,
-// so the host vector may go out of scope).  The rest of the workspace holds
-// per-call scratch (histograms, reciprocal scales, Sinkhorn partials).
+// invalid call enqueues nothing.  The first WOQ_WS_HEAD bytes of the
+// caller's workspace are the status head (the non-finite weight count of the
+// entropy and Sinkhorn calls).  Descriptor tables are built in host memory
+// and copied in right after the head with one hipMemcpyAsync (pageable
+// source: the runtime stages it before returning, so the host vector may go
+// out of scope).  The rest of the workspace holds per-call scratch
+// (histograms, reciprocal scales, Sinkhorn partials).
 #include "launch.h"
 
 #include <algorithm>
@@ -35,8 +37,9 @@ constexpr int kSinqWavesPerCU = 8;     // resident workgroup-pass waves per CU (
 
 size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 
+// Workspace layouts start after the status head.
 struct Arena {
-    size_t off = 0;
+    size_t off = WOQ_WS_HEAD;
     size_t take(size_t bytes, size_t a = kAlign) {
         off = align_up(off, a);
         const size_t o = off;
@@ -48,6 +51,9 @@ struct Arena {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Row stride in elements (0 means contiguous).
+int64_t eff_ld(const woq_mat& m) { return m.ld ? m.ld : m.cols; }
+
 int32_t check_mats(const woq_mat* mats, int32_t n, bool cols8) {
     if (!mats) return WOQ_ERR_NULL;
     if (n < 1 || n > kMaxMats) return WOQ_ERR_COUNT;
@@ -55,13 +61,27 @@ int32_t check_mats(const woq_mat* mats, int32_t n, bool cols8) {
         const woq_mat& m = mats[i];
         if (!m.data) return WOQ_ERR_NULL;
         if (m.dtype != WOQ_F32 && m.dtype != WOQ_BF16) return WOQ_ERR_DTYPE;
-        if (m.reserved != 0 || m.rows < 1 || m.cols < 1) return WOQ_ERR_SHAPE;
-        if (m.rows > kMaxElems / m.cols) return WOQ_ERR_SHAPE;
+        if (m.reserved != 0 || m.rows < 1 || m.cols < 1 || m.ld < 0) return WOQ_ERR_SHAPE;
+        const int64_t ld = eff_ld(m);
+        // a strided matrix has 16-byte rows: ld and cols multiples of 8
+        if (ld != m.cols && (ld < m.cols || ld % 8 || m.cols % 8)) return WOQ_ERR_SHAPE;
+        if (m.rows > kMaxElems / ld) return WOQ_ERR_SHAPE;
         if (cols8 && (m.cols % 8)) return WOQ_ERR_SHAPE;
         if (!aligned(m.data, 16)) return WOQ_ERR_ALIGN;
     }
     return WOQ_OK;
 }
+
+// Copies the host-built descriptor tables [WOQ_WS_HEAD, end) into the
+// workspace; the status head itself is not written.
+hipError_t stage_tables(void* ws, const std::vector<char>& host, size_t end, hipStream_t s) {
+    if (end <= WOQ_WS_HEAD) return hipSuccess;
+    return hipMemcpyAsync(static_cast<char*>(ws) + WOQ_WS_HEAD, host.data() + WOQ_WS_HEAD,
+                          end - WOQ_WS_HEAD, hipMemcpyHostToDevice, s);
+}
+
+// The call's non-finite weight counter (uint64 at byte 0 of the workspace).
+unsigned long long* nonfinite_counter(void* ws) { return static_cast<unsigned long long*>(ws); }
 
 int32_t check_ptrs(const void* const* arr, int32_t n, size_t align) {
     if (!arr) return WOQ_ERR_NULL;
@@ -98,11 +118,21 @@ struct EntLayout {
     size_t hb, keys, part_f, ghist, hpart, total;
 };
 
+// Rows per entropy work unit of a strided matrix (0 for a contiguous one),
+// and the matrix's number of work units.
+int32_t ent_rpu(const woq_mat& m) {
+    return eff_ld(m) == m.cols ? 0 : (int32_t)std::max<int64_t>(1, kEntChunk / m.cols);
+}
+int64_t ent_units(const woq_mat& m) {
+    const int32_t rpu = ent_rpu(m);
+    return rpu ? cdiv(m.rows, rpu) : cdiv(elems(m), kEntChunk);
+}
+
 EntLayout ent_layout(const woq_mat* mats, int32_t n, int32_t n_blocks) {
     EntLayout L;
     for (int32_t i = 0; i < n; ++i) {
-        if (mats[i].dtype == WOQ_BF16) { ++L.nb; L.units_b += cdiv(elems(mats[i]), kEntChunk); }
-        else { ++L.nf; L.units_f += cdiv(elems(mats[i]), kEntChunk); }
+        if (mats[i].dtype == WOQ_BF16) { ++L.nb; L.units_b += ent_units(mats[i]); }
+        else { ++L.nf; L.units_f += ent_units(mats[i]); }
     }
     Arena a;
     L.tab_b = a.take(sizeof(EntMat) * L.nb);
@@ -400,11 +430,15 @@ DfSizes df_sizes(int64_t total_bits) {
     return z;
 }
 
+// The lossless exponent code: contiguous BF16 matrices (the stream is in
+// weight order, rows back to back).
 int32_t check_bf16(const woq_mat* mats, int32_t n) {
     int32_t st = check_mats(mats, n, false);
     if (st) return st;
-    for (int32_t i = 0; i < n; ++i)
+    for (int32_t i = 0; i < n; ++i) {
         if (mats[i].dtype != WOQ_BF16) return WOQ_ERR_DTYPE;
+        if (eff_ld(mats[i]) != mats[i].cols) return WOQ_ERR_SHAPE;
+    }
     return WOQ_OK;
 }
 
@@ -533,8 +567,9 @@ int32_t ewq_block_entropy(const woq_mat* mats, int32_t n_mats, const int32_t* bl
     ub[0] = 0;
     uf[0] = 0;
     for (int32_t i = 0; i < n_mats; ++i) {
-        EntMat e{mats[i].data, elems(mats[i]), mats[i].dtype, i};
-        const int64_t u = cdiv(e.n, kEntChunk);
+        const woq_mat& m = mats[i];
+        EntMat e{m.data, elems(m), m.cols, eff_ld(m), m.dtype, i, (int32_t)m.rows, ent_rpu(m)};
+        const int64_t u = ent_units(m);
         if (e.dtype == WOQ_BF16) { tb[ib] = e; ub[ib + 1] = ub[ib] + u; ++ib; }
         else { tf[jf] = e; uf[jf + 1] = uf[jf] + u; ++jf; }
     }
@@ -549,7 +584,9 @@ int32_t ewq_block_entropy(const woq_mat* mats, int32_t n_mats, const int32_t* bl
         nsz[i] = (double)elems(mats[i]);
     }
 
-    WOQ_HIP(hipMemcpyAsync(ws, host.data(), L.table_end, hipMemcpyHostToDevice, stream));
+    WOQ_HIP(stage_tables(ws, host, L.table_end, stream));
+    unsigned long long* nf = nonfinite_counter(ws);
+    WOQ_HIP(fill_u32(reinterpret_cast<uint32_t*>(nf), 2, 0u, stream));
     const EntMat* dtb = at<EntMat>(ws, L.tab_b);
     const int64_t* dub = at<int64_t>(ws, L.ubeg_b);
     uint32_t* ghist = at<uint32_t>(ws, L.ghist);
@@ -557,11 +594,11 @@ int32_t ewq_block_entropy(const woq_mat* mats, int32_t n_mats, const int32_t* bl
         const int b1 = std::min(L.nb, b0 + kHistSlots);
         WOQ_HIP(fill_u32(ghist, (size_t)(b1 - b0) * 65536, 0u, stream));
         WOQ_HIP(ent_hist_bf16(dtb + b0, dub + b0, b1 - b0, ub[b0], ub[b1] - ub[b0], ghist, stream));
-        WOQ_HIP(ent_hist_final(dtb + b0, b1 - b0, ghist, at<double4>(ws, L.hpart), h_mat, stream));
+        WOQ_HIP(ent_hist_final(dtb + b0, b1 - b0, ghist, at<double4>(ws, L.hpart), h_mat, nf, stream));
     }
     if (L.nf)
         WOQ_HIP(ent_f32(at<EntMat>(ws, L.tab_f), at<int64_t>(ws, L.ubeg_f), L.nf, L.units_f,
-                        at<uint32_t>(ws, L.keys), at<double2>(ws, L.part_f), h_mat, stream));
+                        at<uint32_t>(ws, L.keys), at<double2>(ws, L.part_f), h_mat, nf, stream));
     WOQ_HIP(ent_blocks(at<int32_t>(ws, L.bmats), at<int32_t>(ws, L.bbeg), at<double>(ws, L.nsz),
                        h_mat, n_blocks, x, at<double>(ws, L.hb), h_block, stats, tier, order,
                        stream));
@@ -587,7 +624,9 @@ int32_t sinq_balance_ex(const woq_mat* mats, int32_t n_mats, int32_t iters, int3
     const SinqLayout L = sinq_layout(mats, n_mats, (flags & WOQ_SINQ_SHARED) != 0);
     if ((st = check_ws(ws, ws_bytes, L.total))) return st;
 
-    if (iters == 0) {
+    unsigned long long* nf = nonfinite_counter(ws);
+    WOQ_HIP(fill_u32(reinterpret_cast<uint32_t*>(nf), 2, 0u, stream));
+    if (iters == 0) {  // no weight is read
         for (int32_t i = 0; i < n_mats; ++i) {
             WOQ_HIP(fill_f32(row_scale[i], (size_t)mats[i].rows, 1.0f, stream));
             WOQ_HIP(fill_f32(col_scale[i], (size_t)mats[i].cols, 1.0f, stream));
@@ -609,6 +648,7 @@ int32_t sinq_balance_ex(const woq_mat* mats, int32_t n_mats, int32_t iters, int3
         sm.part = at<void>(ws, L.part[k]);
         sm.rows = (int32_t)m.rows;
         sm.cols = (int32_t)m.cols;
+        sm.ld = (int32_t)eff_ld(m);
         sm.dtype = m.dtype;
         sm.n_strips = L.n_strips[k];
         sm.strip_rows = L.strip_rows[k];
@@ -625,7 +665,7 @@ int32_t sinq_balance_ex(const woq_mat* mats, int32_t n_mats, int32_t iters, int3
             gc[k + 1] = gc[k] + cdiv(tab[g.first + k].cols, rcols);
         }
     }
-    WOQ_HIP(hipMemcpyAsync(ws, host.data(), L.table_end, hipMemcpyHostToDevice, stream));
+    WOQ_HIP(stage_tables(ws, host, L.table_end, stream));
     const SinqMat* dt = at<SinqMat>(ws, L.tab);
     const int64_t* dsb = at<int64_t>(ws, L.sbeg);
     const int64_t* dcb = at<int64_t>(ws, L.cbeg);
@@ -633,7 +673,7 @@ int32_t sinq_balance_ex(const woq_mat* mats, int32_t n_mats, int32_t iters, int3
         for (int32_t it = 0; it < iters; ++it)
             WOQ_HIP(sinq_iteration(dt + g.first, dsb + g.arr_off, dcb + g.arr_off, g.count,
                                    g.n_strips, g.n_cunits, g.max_strips, g.dtype, g.sh,
-                                   g.cols_max, it == 0, stream));
+                                   g.cols_max, it == 0, nf, stream));
     return WOQ_OK;
 }
 
@@ -711,6 +751,7 @@ int32_t quant_impl(const woq_mat* mats, int32_t n_mats, const float* const* row_
         q.ct = L.ct[i] ? at<float>(ws, L.ct[i]) : nullptr;
         q.rows = (int32_t)m.rows;
         q.cols = (int32_t)m.cols;
+        q.ld = (int32_t)eff_ld(m);
         q.dtype = m.dtype;
         q.group = eff_group(m, group);
         tb[p] = q;
@@ -718,7 +759,7 @@ int32_t quant_impl(const woq_mat* mats, int32_t n_mats, const float* const* row_
         ++st_.count;
         st_.units = ub[uoff + st_.count];
     }
-    WOQ_HIP(hipMemcpyAsync(ws, host.data(), L.table_end, hipMemcpyHostToDevice, stream));
+    WOQ_HIP(stage_tables(ws, host, L.table_end, stream));
     if (L.nseg) WOQ_HIP(recip(at<RecipSeg>(ws, L.segs), at<int64_t>(ws, L.ubeg_s), L.nseg, us[L.nseg], stream));
     for (const Set& st_ : sets) {
         const QMat* dt = at<QMat>(ws, L.tab_b) + st_.first;
@@ -774,13 +815,14 @@ int32_t dequant_impl(const woq_mat* out, int32_t n_mats, const uint8_t* const* c
         q.ct = col_scale ? col_scale[i] : nullptr;
         q.rows = (int32_t)m.rows;
         q.cols = (int32_t)m.cols;
+        q.ld = (int32_t)eff_ld(m);
         q.dtype = m.dtype;
         q.group = eff_group(m, group);
         const int64_t u = cdiv(m.rows, kDTileRows) * cdiv(m.cols, kQTileCols);
         if (m.dtype == WOQ_BF16) { tb[ib] = q; ub[ib + 1] = ub[ib] + u; ++ib; }
         else { tf[jf] = q; uf[jf + 1] = uf[jf] + u; ++jf; }
     }
-    WOQ_HIP(hipMemcpyAsync(ws, host.data(), L.table_end, hipMemcpyHostToDevice, stream));
+    WOQ_HIP(stage_tables(ws, host, L.table_end, stream));
     if (L.nb) WOQ_HIP(dequant(at<QMat>(ws, L.tab_b), at<int64_t>(ws, L.ubeg_b), L.nb, ub[L.nb], WOQ_BF16, bits, dbook, stream));
     if (L.nf) WOQ_HIP(dequant(at<QMat>(ws, L.tab_f), at<int64_t>(ws, L.ubeg_f), L.nf, uf[L.nf], WOQ_F32, bits, dbook, stream));
     return WOQ_OK;
@@ -872,11 +914,12 @@ int32_t ternary_pack(const woq_mat* mats, int32_t n_mats, uint8_t* const* codes,
         q.scales = row_scale[i];
         q.rows = (int32_t)m.rows;
         q.cols = (int32_t)m.cols;
+        q.ld = (int32_t)eff_ld(m);
         q.dtype = m.dtype;
         if (m.dtype == WOQ_BF16) { tb[ib] = q; ub[ib + 1] = ub[ib] + m.rows; ++ib; }
         else { tf[jf] = q; uf[jf + 1] = uf[jf] + m.rows; ++jf; }
     }
-    WOQ_HIP(hipMemcpyAsync(ws, host.data(), L.table_end, hipMemcpyHostToDevice, stream));
+    WOQ_HIP(stage_tables(ws, host, L.table_end, stream));
     if (L.nb) WOQ_HIP(ternary(at<QMat>(ws, L.tab_b), at<int64_t>(ws, L.ubeg_b), L.nb, ub[L.nb], WOQ_BF16, stream));
     if (L.nf) WOQ_HIP(ternary(at<QMat>(ws, L.tab_f), at<int64_t>(ws, L.ubeg_f), L.nf, uf[L.nf], WOQ_F32, stream));
     return WOQ_OK;
@@ -979,7 +1022,7 @@ int32_t df11_exponent_histogram(const woq_mat* mats, int32_t n_mats, uint32_t* h
         t[i].n = elems(mats[i]);
         ub[i + 1] = ub[i] + cdiv(t[i].n, kDf11Chunk);
     }
-    WOQ_HIP(hipMemcpyAsync(ws, host.data(), L.table_end, hipMemcpyHostToDevice, stream));
+    WOQ_HIP(stage_tables(ws, host, L.table_end, stream));
     WOQ_HIP(fill_u32(hist, (size_t)n_mats * 256, 0u, stream));
     WOQ_HIP(df11_hist(at<DfMat>(ws, L.tab), at<int64_t>(ws, L.ubeg), n_mats, ub[n_mats], hist, stream));
     return WOQ_OK;
@@ -1030,7 +1073,7 @@ int32_t df11_encode(const woq_mat* mats, int32_t n_mats, const uint8_t* const* c
         ub[i + 1] = ub[i] + cdiv(d.n, kDf11Chunk);
         zb[i + 1] = zb[i] + cdiv((z.enc_bytes + z.gap_bytes) / 4, 4096);
     }
-    WOQ_HIP(hipMemcpyAsync(ws, host.data(), L.table_end, hipMemcpyHostToDevice, stream));
+    WOQ_HIP(stage_tables(ws, host, L.table_end, stream));
     WOQ_HIP(df11_encode_run(at<DfMat>(ws, L.tab), at<int64_t>(ws, L.ubeg), n_mats, ub[n_mats],
                             at<int64_t>(ws, L.zbeg), zb[n_mats], at<DfCode>(ws, L.codes),
                             at<uint32_t>(ws, L.bits), at<int64_t>(ws, L.base), stream));
@@ -1082,7 +1125,7 @@ int32_t df11_decode(const woq_mat* out, int32_t n_mats, const uint8_t* const* en
         d.n_tables = n_tables[i];
         ub[i + 1] = ub[i] + z.n_blocks;
     }
-    WOQ_HIP(hipMemcpyAsync(ws, host.data(), L.table_end, hipMemcpyHostToDevice, stream));
+    WOQ_HIP(stage_tables(ws, host, L.table_end, stream));
     WOQ_HIP(df11_decode_run(at<DfMat>(ws, L.tab), at<int64_t>(ws, L.ubeg), n_mats, ub[n_mats], stream));
     return WOQ_OK;
 }

@@ -19,6 +19,12 @@
 //
 // fp32 path: two passes (max, then fp64 sums of exp(w - c) per work unit),
 // partials combined in a fixed order.
+//
+// A work unit is kEntChunk consecutive elements of a contiguous matrix, or
+// rpu whole rows of a strided one (row stride ld > cols).  Non-finite
+// weights (NaN, +-inf) make the entropy NaN and are counted into the
+// caller's uint64 counter: for bf16 from the histogram bins with an all-ones
+// exponent, for fp32 in the max pass.
 #include "launch.h"
 
 #include <math.h>
@@ -60,19 +66,33 @@ __global__ __launch_bounds__(kT) void k_hist_bf16(const EntMat* __restrict__ mat
     const int m = find_unit_owner(ubeg, nmat, u);
     const EntMat em = mats[m];
     uint32_t* gh = ghist + (size_t)m * 65536;
-    const int64_t start = (u - ubeg[m]) * kEntChunk;
-    const int64_t cnt = min(kEntChunk, em.n - start);
-    const uint16_t* p = reinterpret_cast<const uint16_t*>(em.data) + start;
-    const uint4* pv = reinterpret_cast<const uint4*>(p);
-    const int64_t nv = cnt >> 3;
+    if (em.rpu == 0) {
+        const int64_t start = (u - ubeg[m]) * kEntChunk;
+        const int64_t cnt = min(kEntChunk, em.n - start);
+        const uint16_t* p = reinterpret_cast<const uint16_t*>(em.data) + start;
+        const uint4* pv = reinterpret_cast<const uint4*>(p);
+        const int64_t nv = cnt >> 3;
 
-    int64_t i = threadIdx.x;
-    for (; i + 3 * kT < nv; i += 4 * kT) {
-        const uint4 a = pv[i], b = pv[i + kT], c = pv[i + 2 * kT], d = pv[i + 3 * kT];
-        hist8(a, lh, gh); hist8(b, lh, gh); hist8(c, lh, gh); hist8(d, lh, gh);
+        int64_t i = threadIdx.x;
+        for (; i + 3 * kT < nv; i += 4 * kT) {
+            const uint4 a = pv[i], b = pv[i + kT], c = pv[i + 2 * kT], d = pv[i + 3 * kT];
+            hist8(a, lh, gh); hist8(b, lh, gh); hist8(c, lh, gh); hist8(d, lh, gh);
+        }
+        for (; i < nv; i += kT) hist8(pv[i], lh, gh);
+        for (int64_t e = nv * 8 + threadIdx.x; e < cnt; e += kT) hist_one(p[e], lh, gh);
+    } else {
+        // rows [r0, r1) of a strided matrix (cols % 8 == 0): vector idx of the
+        // unit is row r0 + idx / vpr, columns 8 (idx % vpr) ..
+        const int r0 = (int)(u - ubeg[m]) * em.rpu;
+        const int r1 = min(em.rows, r0 + em.rpu);
+        const uint32_t vpr = (uint32_t)(em.cols >> 3);
+        const uint32_t nvu = (uint32_t)(r1 - r0) * vpr;
+        const uint16_t* base = reinterpret_cast<const uint16_t*>(em.data);
+        for (uint32_t idx = threadIdx.x; idx < nvu; idx += kT) {
+            const uint32_t r = idx / vpr, v = idx - r * vpr;
+            hist8(*reinterpret_cast<const uint4*>(base + (int64_t)(r0 + r) * em.ld + 8 * v), lh, gh);
+        }
     }
-    for (; i < nv; i += kT) hist8(pv[i], lh, gh);
-    for (int64_t e = nv * 8 + threadIdx.x; e < cnt; e += kT) hist_one(p[e], lh, gh);
     __syncthreads();
 
     for (int b = threadIdx.x; b < kWinBins; b += kT) {
@@ -126,17 +146,18 @@ __global__ __launch_bounds__(kT) void k_hist_part(const uint32_t* __restrict__ g
     uint32_t cnt[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) cnt[i] = gload<uint32_t>(gh + threadIdx.x + kT * i);
-    float mx = -INFINITY, bad = 0.f;
+    float mx = -INFINITY;
+    double bad = 0.0;  // weights whose bin has an all-ones exponent (NaN, inf)
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         if (cnt[i]) {
             const uint32_t b = (uint32_t)(w * kPartBins) + threadIdx.x + kT * i;
             const float v = __uint_as_float(b << 16);
-            if (!isfinite(v)) bad = 1.f; else mx = fmaxf(mx, v);
+            if (!isfinite(v)) bad += (double)cnt[i]; else mx = fmaxf(mx, v);
         }
     }
     mx = block_maxf(mx, shf);
-    bad = block_maxf(bad, shf);
+    bad = block_sum(bad, shd);
     double S = 0.0, U = 0.0;
     const double c = (double)mx;
     if (mx > -INFINITY) {
@@ -154,22 +175,24 @@ __global__ __launch_bounds__(kT) void k_hist_part(const uint32_t* __restrict__ g
     }
     S = block_sum(S, shd);
     U = block_sum(U, shd);
-    if (threadIdx.x == 0) part[blockIdx.x] = make_double4(c, S, U, (double)bad);
+    if (threadIdx.x == 0) part[blockIdx.x] = make_double4(c, S, U, bad);
 }
 
 __global__ __launch_bounds__(kT) void k_hist_comb(const EntMat* __restrict__ mats, int nmat,
                                                   const double4* __restrict__ part,
-                                                  double* __restrict__ h_mat) {
+                                                  double* __restrict__ h_mat,
+                                                  unsigned long long* __restrict__ nonfinite) {
     const int m = blockIdx.x * kT + threadIdx.x;
     if (m >= nmat) return;
     const double4* p = part + (size_t)m * kHistParts;
-    double c = -INFINITY;
-    bool bad = false;
+    double c = -INFINITY, nbad = 0.0;
     for (int w = 0; w < kHistParts; ++w) {
         const double4 q = p[w];
         if (q.y > 0.0) c = fmax(c, q.x);
-        bad = bad || q.w != 0.0;
+        nbad += q.w;  // integer counts below 2^31: exact in fp64
     }
+    const bool bad = nbad != 0.0;
+    if (bad) atomicAdd(nonfinite, (unsigned long long)nbad);
     double S = 0.0, U = 0.0;
     for (int w = 0; w < kHistParts; ++w) {
         const double4 q = p[w];
@@ -191,23 +214,43 @@ __device__ __forceinline__ float key_value(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+// Calls f(value) for every element of work unit u of an fp32 matrix, thread
+// t taking elements t, t + kT, ... of the unit.
+template <class F>
+__device__ __forceinline__ void f32_unit(const EntMat& em, int64_t ul, F&& f) {
+    const float* base = reinterpret_cast<const float*>(em.data);
+    if (em.rpu == 0) {
+        const int64_t start = ul * kEntChunk;
+        const int64_t cnt = min(kEntChunk, em.n - start);
+        for (int64_t e = threadIdx.x; e < cnt; e += kT) f(base[start + e]);
+    } else {
+        const int r0 = (int)ul * em.rpu;
+        const int r1 = min(em.rows, r0 + em.rpu);
+        const uint32_t cols = (uint32_t)em.cols;
+        const uint32_t ne = (uint32_t)(r1 - r0) * cols;
+        for (uint32_t e = threadIdx.x; e < ne; e += kT) {
+            const uint32_t r = e / cols, c = e - r * cols;
+            f(base[(int64_t)(r0 + r) * em.ld + c]);
+        }
+    }
+}
+
 __global__ __launch_bounds__(kT) void k_f32_max(const EntMat* __restrict__ mats,
                                                 const int64_t* __restrict__ ubeg, int nmat,
-                                                uint32_t* __restrict__ keys) {
+                                                uint32_t* __restrict__ keys,
+                                                unsigned long long* __restrict__ nonfinite) {
     __shared__ float shf[kT / 64];
     const int64_t u = blockIdx.x;
     const int m = find_unit_owner(ubeg, nmat, u);
     const EntMat em = mats[m];
-    const int64_t start = (u - ubeg[m]) * kEntChunk;
-    const int64_t cnt = min(kEntChunk, em.n - start);
-    const float* p = reinterpret_cast<const float*>(em.data) + start;
-    float mx = -INFINITY, bad = 0.f;
-    for (int64_t e = threadIdx.x; e < cnt; e += kT) {
-        const float v = p[e];
-        if (!isfinite(v)) bad = 1.f; else mx = fmaxf(mx, v);
-    }
+    float mx = -INFINITY;
+    uint32_t nbad = 0;
+    f32_unit(em, u - ubeg[m], [&](float v) {
+        if (!isfinite(v)) ++nbad; else mx = fmaxf(mx, v);
+    });
+    if (nbad) atomicAdd(nonfinite, (unsigned long long)nbad);
     mx = block_maxf(mx, shf);
-    bad = block_maxf(bad, shf);
+    const float bad = block_maxf(nbad ? 1.f : 0.f, shf);
     if (threadIdx.x == 0) {
         atomicMax(&keys[2 * m], order_key(mx));
         if (bad != 0.f) atomicOr(&keys[2 * m + 1], 1u);
@@ -222,20 +265,16 @@ __global__ __launch_bounds__(kT) void k_f32_sum(const EntMat* __restrict__ mats,
     const int64_t u = blockIdx.x;
     const int m = find_unit_owner(ubeg, nmat, u);
     const EntMat em = mats[m];
-    const int64_t start = (u - ubeg[m]) * kEntChunk;
-    const int64_t cnt = min(kEntChunk, em.n - start);
-    const float* p = reinterpret_cast<const float*>(em.data) + start;
     const double c = (double)key_value(keys[2 * m]);
     double S = 0.0, U = 0.0;
-    for (int64_t e = threadIdx.x; e < cnt; e += kT) {
-        const float v = p[e];
+    f32_unit(em, u - ubeg[m], [&](float v) {
         if (isfinite(v)) {
             const double d = (double)v - c;
             const double x = exp(d);
             S += x;
             U += x * d;
         }
-    }
+    });
     S = block_sum(S, shd);
     U = block_sum(U, shd);
     if (threadIdx.x == 0) part[u] = make_double2(S, U);
@@ -325,19 +364,20 @@ hipError_t ent_hist_bf16(const EntMat* mats, const int64_t* ubeg, int nmat, int6
 }
 
 hipError_t ent_hist_final(const EntMat* mats, int nmat, const uint32_t* ghist, double4* part,
-                          double* h_mat, hipStream_t s) {
+                          double* h_mat, unsigned long long* nonfinite, hipStream_t s) {
     if (nmat <= 0) return hipSuccess;
     k_hist_part<<<dim3(nmat * kHistParts), dim3(kT), 0, s>>>(ghist, part);
-    k_hist_comb<<<dim3((nmat + kT - 1) / kT), dim3(kT), 0, s>>>(mats, nmat, part, h_mat);
+    k_hist_comb<<<dim3((nmat + kT - 1) / kT), dim3(kT), 0, s>>>(mats, nmat, part, h_mat, nonfinite);
     return hipGetLastError();
 }
 
 hipError_t ent_f32(const EntMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                   uint32_t* keys, double2* part, double* h_mat, hipStream_t s) {
+                   uint32_t* keys, double2* part, double* h_mat, unsigned long long* nonfinite,
+                   hipStream_t s) {
     if (nmat <= 0) return hipSuccess;
     hipError_t e = fill_u32(keys, 2 * (size_t)nmat, 0u, s);
     if (e != hipSuccess) return e;
-    k_f32_max<<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, keys);
+    k_f32_max<<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, keys, nonfinite);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     k_f32_sum<<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, keys, part);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -19,11 +19,13 @@ hipError_t ent_hist_bf16(const EntMat* mats, const int64_t* ubeg, int nmat,
 // Entropy from the histograms: kHistBinParts parts per matrix (partials in
 // part[nmat * kHistBinParts]), then one combine per matrix.
 constexpr int kHistBinParts = 16;
+// nonfinite: the call's uint64 counter of NaN / inf weights (added to).
 hipError_t ent_hist_final(const EntMat* mats, int nmat, const uint32_t* ghist,
-                          double4* part, double* h_mat, hipStream_t s);
+                          double4* part, double* h_mat, unsigned long long* nonfinite,
+                          hipStream_t s);
 hipError_t ent_f32(const EntMat* mats, const int64_t* ubeg, int nmat,
                    int64_t n_units, uint32_t* keys, double2* part,
-                   double* h_mat, hipStream_t s);
+                   double* h_mat, unsigned long long* nonfinite, hipStream_t s);
 hipError_t ent_blocks(const int32_t* bmats, const int32_t* bbeg,
                       const double* nsz, const double* h_mat, int n_blocks,
                       double x, double* hb, double* h_block, double* stats,
@@ -45,11 +47,13 @@ int sinq_wave_occupancy(int dtype, int nv);
 // reduction workgroup covers 256 / slices columns.
 int sinq_reduce_slices(int max_strips);
 // One iteration over a group of same-shape matrices: the fused row / column
-// pass then the fixed-order column reduction.
+// pass then the fixed-order column reduction.  The first iteration adds the
+// NaN / inf weights it reads to *nonfinite.
 hipError_t sinq_iteration(const SinqMat* mats, const int64_t* strip_begin,
                           const int64_t* col_begin, int nmat, int64_t n_strips,
                           int64_t n_col_units, int max_strips, int dtype, SinqShape sh,
-                          int cols_max, bool first, hipStream_t s);
+                          int cols_max, bool first, unsigned long long* nonfinite,
+                          hipStream_t s);
 
 // ---- quantise / dequantise / ternary
 

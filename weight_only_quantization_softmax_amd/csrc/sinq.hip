@@ -46,7 +46,14 @@
 // (a constant column has std 0).
 //
 // Matrices of one launch share their shape class (wave or workgroup form,
-// vectors per lane / thread, threads per workgroup).
+// vectors per lane / thread, threads per workgroup).  Rows are addressed
+// through the matrix's row stride ld.
+//
+// Non-finite weights.  In the first iteration (t = 1) a NaN or inf weight
+// makes its row's moments non-finite (so does a finite row whose squares
+// overflow fp32), so the rows to inspect are known from the moments alone;
+// only those rows are scanned element by element, and their NaN / inf
+// weights are added to the call's uint64 counter.
 #include "launch.h"
 
 #include <math.h>
@@ -186,6 +193,32 @@ __device__ __forceinline__ float first_lane(float v) {
     return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(v)));
 }
 
+// NaN / inf weights among 8, from the packed bits (an all-ones exponent
+// field), without unpacking.
+__device__ __forceinline__ uint32_t nonfinite_bf16x2(uint32_t w) {
+    return ((w & 0x7f80u) == 0x7f80u ? 1u : 0u) + ((w & 0x7f800000u) == 0x7f800000u ? 1u : 0u);
+}
+__device__ __forceinline__ uint32_t nonfinite_f32(float f) {
+    return (__float_as_uint(f) & 0x7f800000u) == 0x7f800000u ? 1u : 0u;
+}
+template <int DT>
+__device__ __forceinline__ uint32_t nonfinite8(const Vec8<DT>& r) {
+    if constexpr (DT == WOQ_BF16) {
+        return nonfinite_bf16x2(r.v.x) + nonfinite_bf16x2(r.v.y) + nonfinite_bf16x2(r.v.z) +
+               nonfinite_bf16x2(r.v.w);
+    } else {
+        return nonfinite_f32(r.a.x) + nonfinite_f32(r.a.y) + nonfinite_f32(r.a.z) +
+               nonfinite_f32(r.a.w) + nonfinite_f32(r.b.x) + nonfinite_f32(r.b.y) +
+               nonfinite_f32(r.b.z) + nonfinite_f32(r.b.w);
+    }
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
 // Lane moments from the shifted sums: mean K + S/n and M2 = Q - S^2/n
 // (clamped at 0 against rounding); a lane without elements gives (0, 0).
 __device__ __forceinline__ void lane_moments(float K, float S, float Q, float n, float rn,
@@ -203,7 +236,8 @@ __device__ __forceinline__ void lane_moments(float K, float S, float Q, float n,
 // exceeds the row's vectors, so threads own unequal numbers of them.
 template <int DT, int NV, bool FIRST, bool RAG>
 __global__ __launch_bounds__(kMaxT) void k_sinq_pass(const SinqMat* __restrict__ mats,
-                                                     const int64_t* __restrict__ sbeg, int nmat) {
+                                                     const int64_t* __restrict__ sbeg, int nmat,
+                                                     unsigned long long* __restrict__ nonfinite) {
     using C = PassCfg<DT, NV>;
     constexpr int R = C::R;
     __shared__ float2 red[2][kMaxT / 64][R];
@@ -219,7 +253,9 @@ __global__ __launch_bounds__(kMaxT) void k_sinq_pass(const SinqMat* __restrict__
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int nvec = sm.cols >> 3;
     const int64_t cols = sm.cols;
+    const int64_t ld = sm.ld;
     const float fn = (float)sm.cols;
+    uint32_t nbad = 0;  // first iteration: NaN / inf weights this thread saw
 
     int vk[NV], ui[NV];
     bool own[NV];
@@ -291,7 +327,7 @@ __global__ __launch_bounds__(kMaxT) void k_sinq_pass(const SinqMat* __restrict__
         for (int r = 0; r < R; ++r) {
             const int64_t row = min(rb + r, r1 - 1);  // clamped into the strip
 #pragma unroll
-            for (int k = 0; k < NV; ++k) d[r][k] = ldv<DT>(sm.data, row * cols + 8 * vk[k]);
+            for (int k = 0; k < NV; ++k) d[r][k] = ldv<DT>(sm.data, row * ld + 8 * vk[k]);
         }
     };
 
@@ -350,6 +386,7 @@ __global__ __launch_bounds__(kMaxT) void k_sinq_pass(const SinqMat* __restrict__
         lds_barrier();
         // ---- lane r < R merges row r over the waves in wave order
         float vv = 0.f;
+        bool rbad = false;  // first iteration: the row's moments are not finite
         if (lane < R) {
             const int row = rb + lane;
             float2 a = red[buf][0][lane];
@@ -363,6 +400,20 @@ __global__ __launch_bounds__(kMaxT) void k_sinq_pass(const SinqMat* __restrict__
             if (row < r1) {
                 vv = __fdiv_rn(1.0f, s);
                 if (wid == 0) gstore<float>(sm.s + row, s);
+                rbad = FIRST && !(isfinite(M) && isfinite(Q));
+            }
+        }
+        if constexpr (FIRST) {
+            // the tile's rows whose moments are not finite: count their NaN /
+            // inf weights (each thread its own vectors; rare)
+            const uint64_t badm = __ballot(rbad);
+            if (badm) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    if ((badm >> r) & 1u)
+#pragma unroll
+                        for (int k = 0; k < NV; ++k)
+                            if (!RAG || own[k]) nbad += nonfinite8<DT>(d[r][k]);
             }
         }
         buf ^= 1;
@@ -416,6 +467,9 @@ __global__ __launch_bounds__(kMaxT) void k_sinq_pass(const SinqMat* __restrict__
         rb = rn2;
     }
 
+    if constexpr (FIRST) {
+        if (nbad) atomicAdd(nonfinite, (unsigned long long)nbad);
+    }
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
         if (!own[k]) continue;
@@ -468,7 +522,8 @@ struct WaveCfg {
 
 template <int DT, int NVL, bool FIRST, bool RAG>
 __global__ __launch_bounds__(256, (WaveCfg<DT, NVL>::OCC)) void k_sinq_wave(
-    const SinqMat* __restrict__ mats, const int64_t* __restrict__ wgbeg, int nmat) {
+    const SinqMat* __restrict__ mats, const int64_t* __restrict__ wgbeg, int nmat,
+    unsigned long long* __restrict__ nonfinite) {
     using WC = WaveCfg<DT, NVL>;
     constexpr bool F32 = WC::F32;
     constexpr int NP = WC::NP;
@@ -482,7 +537,9 @@ __global__ __launch_bounds__(256, (WaveCfg<DT, NVL>::OCC)) void k_sinq_wave(
     const SinqMat sm = mats[m];
     const int wg = (int)(blockIdx.x - wgbeg[m]);
     const int cols = sm.cols;
+    const int64_t ld = sm.ld;
     const int nvec = cols >> 3;
+    uint32_t nbad = 0;  // first iteration: NaN / inf weights of this wave's bad rows
     float* u = ul;
     float* cp = ul + kWaveU;
     for (int j = 4 * threadIdx.x; j < kWaveU; j += 4 * 256) {
@@ -528,7 +585,7 @@ __global__ __launch_bounds__(256, (WaveCfg<DT, NVL>::OCC)) void k_sinq_wave(
         for (int rr = 0; rr < RW; ++rr) {
             const int64_t row = min(row0 + rr, r1 - 1);
 #pragma unroll
-            for (int k = 0; k < NVL; ++k) P[rr][k] = ldv<DT>(sm.data, row * cols + 8 * vk[k]);
+            for (int k = 0; k < NVL; ++k) P[rr][k] = ldv<DT>(sm.data, row * ld + 8 * vk[k]);
         }
     };
     auto process = [&](Vec8<DT> (&P)[RW][NVL], int row0) {
@@ -593,6 +650,14 @@ __global__ __launch_bounds__(256, (WaveCfg<DT, NVL>::OCC)) void k_sinq_wave(
             const float s = var > 0.f ? __fsqrt_rn(var) : 1.0f;
             v[rr] = __fdiv_rn(1.0f, s);
             if (lane == 0 && row0 + rr < r1) gstore<float>(sm.s + row0 + rr, s);
+            if constexpr (FIRST) {
+                // wave-uniform: a row whose moments are not finite (rare)
+                if (row0 + rr < r1 && !(isfinite(m1) && isfinite(q1))) {
+#pragma unroll
+                    for (int k = 0; k < NVL; ++k)
+                        if (!RAG || own[k]) nbad += nonfinite8<DT>(P[rr][k]);
+                }
+            }
         }
         if constexpr (!KEEP) {
 #pragma unroll
@@ -627,6 +692,9 @@ __global__ __launch_bounds__(256, (WaveCfg<DT, NVL>::OCC)) void k_sinq_wave(
         if (row + 4 * RW >= r1) break;
         if (row + 8 * RW < r1) load_rows(PA, row + 8 * RW);
         process(PB, row + 4 * RW);
+    }
+    if constexpr (FIRST) {
+        if (nbad) atomicAdd(nonfinite, (unsigned long long)nbad);
     }
     // the four waves' column partials, added in wave order in LDS
     for (int w = 0; w < 4; ++w) {
@@ -665,44 +733,44 @@ __global__ __launch_bounds__(256, (WaveCfg<DT, NVL>::OCC)) void k_sinq_wave(
 
 template <int DT, int NVL, bool RAG>
 hipError_t launch_wave(const SinqMat* mats, const int64_t* wgbeg, int nmat, int64_t n_wgs,
-                       bool first, hipStream_t s) {
+                       bool first, unsigned long long* nf, hipStream_t s) {
     // u, then the workgroup's partial row (wave mode: <= 4096 bf16 / 1536 fp32 columns)
     const size_t lds = WaveCfg<DT, NVL>::lds();
     const unsigned grid = (unsigned)n_wgs;
-    if (first) k_sinq_wave<DT, NVL, true, RAG><<<dim3(grid), dim3(256), lds, s>>>(mats, wgbeg, nmat);
-    else k_sinq_wave<DT, NVL, false, RAG><<<dim3(grid), dim3(256), lds, s>>>(mats, wgbeg, nmat);
+    if (first) k_sinq_wave<DT, NVL, true, RAG><<<dim3(grid), dim3(256), lds, s>>>(mats, wgbeg, nmat, nf);
+    else k_sinq_wave<DT, NVL, false, RAG><<<dim3(grid), dim3(256), lds, s>>>(mats, wgbeg, nmat, nf);
     return hipGetLastError();
 }
 
 template <int DT, bool RAG>
 hipError_t launch_wave_nv(const SinqMat* mats, const int64_t* wbeg, int nmat, int64_t n_waves,
-                          int nvl, bool first, hipStream_t s) {
+                          int nvl, bool first, unsigned long long* nf, hipStream_t s) {
     switch (nvl) {
-        case 1: return launch_wave<DT, 1, RAG>(mats, wbeg, nmat, n_waves, first, s);
-        case 2: return launch_wave<DT, 2, RAG>(mats, wbeg, nmat, n_waves, first, s);
-        case 3: return launch_wave<DT, 3, RAG>(mats, wbeg, nmat, n_waves, first, s);
-        case 4: return launch_wave<DT, 4, RAG>(mats, wbeg, nmat, n_waves, first, s);
-        case 5: return launch_wave<DT, 5, RAG>(mats, wbeg, nmat, n_waves, first, s);
-        case 6: return launch_wave<DT, 6, RAG>(mats, wbeg, nmat, n_waves, first, s);
-        case 7: return launch_wave<DT, 7, RAG>(mats, wbeg, nmat, n_waves, first, s);
-        default: return launch_wave<DT, 8, RAG>(mats, wbeg, nmat, n_waves, first, s);
+        case 1: return launch_wave<DT, 1, RAG>(mats, wbeg, nmat, n_waves, first, nf, s);
+        case 2: return launch_wave<DT, 2, RAG>(mats, wbeg, nmat, n_waves, first, nf, s);
+        case 3: return launch_wave<DT, 3, RAG>(mats, wbeg, nmat, n_waves, first, nf, s);
+        case 4: return launch_wave<DT, 4, RAG>(mats, wbeg, nmat, n_waves, first, nf, s);
+        case 5: return launch_wave<DT, 5, RAG>(mats, wbeg, nmat, n_waves, first, nf, s);
+        case 6: return launch_wave<DT, 6, RAG>(mats, wbeg, nmat, n_waves, first, nf, s);
+        case 7: return launch_wave<DT, 7, RAG>(mats, wbeg, nmat, n_waves, first, nf, s);
+        default: return launch_wave<DT, 8, RAG>(mats, wbeg, nmat, n_waves, first, nf, s);
     }
 }
 
 template <int DT>
 hipError_t launch_wave_dt(const SinqMat* mats, const int64_t* wbeg, int nmat, int64_t n_waves,
-                          SinqShape sh, bool first, hipStream_t s) {
-    if (sh.rag) return launch_wave_nv<DT, true>(mats, wbeg, nmat, n_waves, sh.nv, first, s);
-    return launch_wave_nv<DT, false>(mats, wbeg, nmat, n_waves, sh.nv, first, s);
+                          SinqShape sh, bool first, unsigned long long* nf, hipStream_t s) {
+    if (sh.rag) return launch_wave_nv<DT, true>(mats, wbeg, nmat, n_waves, sh.nv, first, nf, s);
+    return launch_wave_nv<DT, false>(mats, wbeg, nmat, n_waves, sh.nv, first, nf, s);
 }
 // fp32 rows use the wave pass up to kWaveMaxF32 vectors per lane only.
 template <bool RAG>
 hipError_t launch_wave_f32(const SinqMat* mats, const int64_t* wbeg, int nmat, int64_t n_waves,
-                           int nvl, bool first, hipStream_t s) {
+                           int nvl, bool first, unsigned long long* nf, hipStream_t s) {
     switch (nvl) {
-        case 1: return launch_wave<WOQ_F32, 1, RAG>(mats, wbeg, nmat, n_waves, first, s);
-        case 2: return launch_wave<WOQ_F32, 2, RAG>(mats, wbeg, nmat, n_waves, first, s);
-        default: return launch_wave<WOQ_F32, 3, RAG>(mats, wbeg, nmat, n_waves, first, s);
+        case 1: return launch_wave<WOQ_F32, 1, RAG>(mats, wbeg, nmat, n_waves, first, nf, s);
+        case 2: return launch_wave<WOQ_F32, 2, RAG>(mats, wbeg, nmat, n_waves, first, nf, s);
+        default: return launch_wave<WOQ_F32, 3, RAG>(mats, wbeg, nmat, n_waves, first, nf, s);
     }
 }
 
@@ -790,9 +858,9 @@ __global__ __launch_bounds__(256) void k_sinq_reduce(const SinqMat* __restrict__
             const float v = __fdiv_rn(1.0f, gload<float>(sm.s + i));
             float x;
             if constexpr (DT == WOQ_BF16)
-                x = __uint_as_float((uint32_t)gload<uint16_t>(reinterpret_cast<const uint16_t*>(sm.data) + (int64_t)i * sm.cols + j) << 16);
+                x = __uint_as_float((uint32_t)gload<uint16_t>(reinterpret_cast<const uint16_t*>(sm.data) + (int64_t)i * sm.ld + j) << 16);
             else
-                x = gload<float>(reinterpret_cast<const float*>(sm.data) + (int64_t)i * sm.cols + j);
+                x = gload<float>(reinterpret_cast<const float*>(sm.data) + (int64_t)i * sm.ld + j);
             const double dz = (double)(x * v) - mean;
             S2 += dz;
             Q2 += dz * dz;
@@ -807,35 +875,37 @@ __global__ __launch_bounds__(256) void k_sinq_reduce(const SinqMat* __restrict__
 
 template <int DT, int NV, bool RAG>
 hipError_t launch_pass(const SinqMat* mats, const int64_t* sbeg, int nmat, int64_t n_strips,
-                       int nt, int cols_max, bool first, hipStream_t s) {
+                       int nt, int cols_max, bool first, unsigned long long* nf, hipStream_t s) {
     const size_t lds = PassCfg<DT, NV>::U_LDS ? sizeof(float) * ((size_t)cols_max + 8) : 0;
     if (first)
-        k_sinq_pass<DT, NV, true, RAG><<<dim3((unsigned)n_strips), dim3(nt), lds, s>>>(mats, sbeg, nmat);
+        k_sinq_pass<DT, NV, true, RAG><<<dim3((unsigned)n_strips), dim3(nt), lds, s>>>(mats, sbeg, nmat, nf);
     else
-        k_sinq_pass<DT, NV, false, RAG><<<dim3((unsigned)n_strips), dim3(nt), lds, s>>>(mats, sbeg, nmat);
+        k_sinq_pass<DT, NV, false, RAG><<<dim3((unsigned)n_strips), dim3(nt), lds, s>>>(mats, sbeg, nmat, nf);
     return hipGetLastError();
 }
 
 template <int DT, bool RAG>
 hipError_t launch_pass_nv(const SinqMat* mats, const int64_t* sbeg, int nmat, int64_t n_strips,
-                          SinqShape sh, int cols_max, bool first, hipStream_t s) {
+                          SinqShape sh, int cols_max, bool first, unsigned long long* nf,
+                          hipStream_t s) {
     switch (sh.nv) {
-        case 1: return launch_pass<DT, 1, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
-        case 2: return launch_pass<DT, 2, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
-        case 3: return launch_pass<DT, 3, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
-        case 4: return launch_pass<DT, 4, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
-        case 5: return launch_pass<DT, 5, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
-        case 6: return launch_pass<DT, 6, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
-        case 7: return launch_pass<DT, 7, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
-        default: return launch_pass<DT, 8, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, s);
+        case 1: return launch_pass<DT, 1, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, nf, s);
+        case 2: return launch_pass<DT, 2, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, nf, s);
+        case 3: return launch_pass<DT, 3, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, nf, s);
+        case 4: return launch_pass<DT, 4, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, nf, s);
+        case 5: return launch_pass<DT, 5, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, nf, s);
+        case 6: return launch_pass<DT, 6, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, nf, s);
+        case 7: return launch_pass<DT, 7, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, nf, s);
+        default: return launch_pass<DT, 8, RAG>(mats, sbeg, nmat, n_strips, sh.nt, cols_max, first, nf, s);
     }
 }
 
 template <int DT>
 hipError_t launch_pass_dt(const SinqMat* mats, const int64_t* sbeg, int nmat, int64_t n_strips,
-                          SinqShape sh, int cols_max, bool first, hipStream_t s) {
-    if (sh.rag) return launch_pass_nv<DT, true>(mats, sbeg, nmat, n_strips, sh, cols_max, first, s);
-    return launch_pass_nv<DT, false>(mats, sbeg, nmat, n_strips, sh, cols_max, first, s);
+                          SinqShape sh, int cols_max, bool first, unsigned long long* nf,
+                          hipStream_t s) {
+    if (sh.rag) return launch_pass_nv<DT, true>(mats, sbeg, nmat, n_strips, sh, cols_max, first, nf, s);
+    return launch_pass_nv<DT, false>(mats, sbeg, nmat, n_strips, sh, cols_max, first, nf, s);
 }
 
 }  // namespace
@@ -870,16 +940,18 @@ int sinq_reduce_slices(int max_strips) {
 
 hipError_t sinq_iteration(const SinqMat* mats, const int64_t* sbeg, const int64_t* cbeg, int nmat,
                           int64_t n_strips, int64_t n_col_units, int max_strips, int dtype,
-                          SinqShape sh, int cols_max, bool first, hipStream_t s) {
+                          SinqShape sh, int cols_max, bool first, unsigned long long* nonfinite,
+                          hipStream_t s) {
     hipError_t e;
+    unsigned long long* nf = nonfinite;
     if (sh.mode == 1)
-        e = dtype == WOQ_BF16 ? launch_wave_dt<WOQ_BF16>(mats, sbeg, nmat, n_strips, sh, first, s)
-                              : (sh.rag ? launch_wave_f32<true>(mats, sbeg, nmat, n_strips, sh.nv, first, s)
-                                        : launch_wave_f32<false>(mats, sbeg, nmat, n_strips, sh.nv, first, s));
+        e = dtype == WOQ_BF16 ? launch_wave_dt<WOQ_BF16>(mats, sbeg, nmat, n_strips, sh, first, nf, s)
+                              : (sh.rag ? launch_wave_f32<true>(mats, sbeg, nmat, n_strips, sh.nv, first, nf, s)
+                                        : launch_wave_f32<false>(mats, sbeg, nmat, n_strips, sh.nv, first, nf, s));
     else
         e = dtype == WOQ_BF16
-                ? launch_pass_dt<WOQ_BF16>(mats, sbeg, nmat, n_strips, sh, cols_max, first, s)
-                : launch_pass_dt<WOQ_F32>(mats, sbeg, nmat, n_strips, sh, cols_max, first, s);
+                ? launch_pass_dt<WOQ_BF16>(mats, sbeg, nmat, n_strips, sh, cols_max, first, nf, s)
+                : launch_pass_dt<WOQ_F32>(mats, sbeg, nmat, n_strips, sh, cols_max, first, nf, s);
     if (e != hipSuccess) return e;
     const int slices = sinq_reduce_slices(max_strips);
     if (dtype == WOQ_BF16)

@@ -100,12 +100,18 @@ __device__ __forceinline__ int find_unit_owner(const int64_t* begin, int n, int6
 }
 
 // ------------------------------------------------------------ descriptors
-// Entropy: one entry per matrix.
+// Entropy: one entry per matrix.  A contiguous matrix (ld == cols) is read
+// in work units of kEntChunk consecutive elements; a strided one in units of
+// rpu whole rows (rpu * cols about kEntChunk).
 struct EntMat {
     const void* data;
     int64_t n;          // rows * cols
+    int64_t cols;
+    int64_t ld;         // row stride (elements)
     int32_t dtype;
     int32_t slot;       // index of this matrix in the caller's h_mat
+    int32_t rows;
+    int32_t rpu;        // rows per work unit when strided (0: contiguous)
 };
 
 // Sinkhorn: one entry per matrix.  A matrix is cut into row strips, one
@@ -117,10 +123,12 @@ struct SinqMat {
     float* u;           // workspace 1/t [cols]
     void* part;         // workspace column partials [n_strips][cols] (float2 / float4)
     int32_t rows, cols;
+    int32_t ld;         // row stride of data (elements)
     int32_t dtype;
     int32_t n_strips;
     int32_t strip_rows;
     int32_t rms;        // 1: root mean square in place of the centred std
+    int32_t pad;
 };
 
 // Quantise / dequantise / ternary: one entry per matrix.
@@ -132,8 +140,10 @@ struct QMat {
     const float* rs;    // 1/s (quant) or s (dequant), NULL = 1
     const float* ct;    // 1/t (quant) or t (dequant), NULL = 1
     int32_t rows, cols;
+    int32_t ld;         // row stride of data (elements); codes stay contiguous
     int32_t dtype;
     int32_t group;      // group size for this matrix (cols for per-row groups)
+    int32_t pad;
 };
 
 // Non-uniform code book (code-book grid): up to kCbMax ascending levels,

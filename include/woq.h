@@ -37,7 +37,8 @@
  *    arrays, the `float* const*` style arrays, block_id) are HOST memory read
  *    during the call only.  The library allocates no device memory, keeps no
  *    pointer after the enqueued work completes and has no mutable global
- *    state; calls are thread-safe when they use distinct workspaces.
+ *    state (except the static scratch array of ewq_block_entropy_static);
+ *    calls are thread-safe when they use distinct workspaces.
  *  - Work is enqueued on `stream` (0 = null stream) and the call returns;
  *    outputs are valid once the stream has synchronised.  Calls that share a
  *    workspace must be ordered on one stream.
@@ -80,6 +81,7 @@ extern "C" {
 #define WOQ_ERR_ALIGN     9  /* data pointer not 16-byte aligned             */
 #define WOQ_ERR_COUNT    10  /* n_mats / n_blocks out of range               */
 #define WOQ_ERR_VALUE    11  /* a host-side value is not finite              */
+#define WOQ_ERR_SCRATCH  12  /* more than the static scratch array holds     */
 
 /* element types */
 #define WOQ_F32  0
@@ -146,6 +148,28 @@ int32_t ewq_block_entropy(const woq_mat* mats, int32_t n_mats,
                           double* h_mat, double* h_block, double* stats,
                           int32_t* tier, int32_t* order,
                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * ewq_block_entropy_static -- ewq_block_entropy for callers that cannot
+ *  allocate device memory (code under HIP graph capture, tight serving
+ *  loops, harnesses that forbid hipMalloc): no workspace argument, and no
+ *  hipMalloc, hipFree or allocating library routine.  Its scratch is a
+ *  32 MiB array in the library's device memory, one per GPU the library
+ *  runs on (on the device current at the call; `stream` must belong to it),
+ *  held until the process ends and located on the first call on each device.
+ *  Histograms pass through it in batches of as many matrices as fit, so any
+ *  number of matrices works; WOQ_ERR_SCRATCH (before any HIP call) when the
+ *  descriptor tables, fp32 partials and one histogram do not fit (about
+ *  400,000 matrices).  Arguments, results and other errors as for
+ *  ewq_block_entropy; the non-finite count is not reported.  Every call on
+ *  a GPU uses that GPU's one array: calls that overlap on one GPU (two host
+ *  threads, or two streams without ordering between them) race; calls
+ *  ordered on one stream do not.
+ */
+int32_t ewq_block_entropy_static(const woq_mat* mats, int32_t n_mats,
+                                 const int32_t* block_id, int32_t n_blocks, double x,
+                                 double* h_mat, double* h_block, double* stats,
+                                 int32_t* tier, int32_t* order, hipStream_t stream);
 
 /*
  * sinq_balance -- [SINQ] dual-axis scaling by Sinkhorn-Knopp-style

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = _lib.load()
-    for code in range(0, 12):
+    for code in range(0, 13):
         s = lib.woq_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.woq_status_string(99).decode() == "unknown status"
@@ -226,3 +226,18 @@ def test_documented_group_and_row_limits():
     pp = ctypes.cast(one, _lib.PP)
     assert lib.ternary_pack(_smat(2, 32776, 0, bf), 1, pp, pp, FAKE, 1 << 30, None) == 2
     assert lib.ternary_pack(_smat(2, 16392, 0, f32), 1, pp, pp, FAKE, 1 << 30, None) == 2
+
+
+def test_static_entropy_rejects_before_any_hip_call():
+    """ewq_block_entropy_static: the same argument checks, and tables that do
+    not fit the 32 MiB static array are refused before any HIP call."""
+    lib = _lib.load()
+    f = lib.ewq_block_entropy_static
+    m = _mat()
+    assert f(None, 1, None, 1, 1.0, FAKE, None, None, None, None, None) == 1
+    assert f(m, 1, None, 1, 1.0, None, None, None, None, None, None) == 1
+    assert f(m, 1, None, 2, 1.0, FAKE, None, None, None, None, None) == 7
+    assert f(m, 0, None, 1, 1.0, FAKE, None, None, None, None, None) == 10
+    n = 600_000
+    many = _lib.mat_array([(FAKE, _lib.WOQ_BF16, 16, 64)] * n)
+    assert f(many, n, None, 1, 1.0, FAKE, None, None, None, None, None) == 12

@@ -16,7 +16,7 @@ STATUS = {
     0: "WOQ_OK", 1: "WOQ_ERR_NULL", 2: "WOQ_ERR_SHAPE", 3: "WOQ_ERR_DTYPE",
     4: "WOQ_ERR_BITS", 5: "WOQ_ERR_ITERS", 6: "WOQ_ERR_WORKSPACE",
     7: "WOQ_ERR_BLOCK", 8: "WOQ_ERR_HIP", 9: "WOQ_ERR_ALIGN", 10: "WOQ_ERR_COUNT",
-    11: "WOQ_ERR_VALUE",
+    11: "WOQ_ERR_VALUE", 12: "WOQ_ERR_SCRATCH",
 }
 WOQ_F32, WOQ_BF16 = 0, 1
 WOQ_SINQ_RMS = 1
@@ -29,7 +29,7 @@ EXPORTS = ("woq_status_string", "woq_workspace_size", "ewq_block_entropy",
            "sinq_balance", "sinq_balance_ex", "quant_pack_groupwise", "dequant_unpack", "ternary_pack",
            "ewq_budget_levels", "df11_buffer_sizes", "df11_exponent_histogram",
            "df11_build_code", "df11_encode", "df11_decode", "quant_pack_codebook",
-           "dequant_codebook", "woq_codebook_normal")
+           "dequant_codebook", "woq_codebook_normal", "ewq_block_entropy_static")
 
 
 WS_HEAD = 256   # WOQ_WS_HEAD: the workspace's status head (non-finite count at byte 0)
@@ -71,6 +71,9 @@ def load() -> ctypes.CDLL:
     lib.ewq_block_entropy.argtypes = [ctypes.POINTER(WoqMat), I32, ctypes.POINTER(I32), I32,
                                       ctypes.c_double, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.ewq_block_entropy.restype = I32
+    lib.ewq_block_entropy_static.argtypes = [ctypes.POINTER(WoqMat), I32, ctypes.POINTER(I32), I32,
+                                             ctypes.c_double, P, P, P, P, P, P]
+    lib.ewq_block_entropy_static.restype = I32
     lib.sinq_balance.argtypes = [ctypes.POINTER(WoqMat), I32, I32, PP, PP, P, ctypes.c_size_t, P]
     lib.sinq_balance.restype = I32
     lib.sinq_balance_ex.argtypes = [ctypes.POINTER(WoqMat), I32, I32, I32, PP, PP, P,

@@ -13,6 +13,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <tuple>
 #include <cstring>
 #include <vector>
@@ -113,6 +114,7 @@ T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(b
 // ------------------------------------------------------------------ entropy
 struct EntLayout {
     int nb = 0, nf = 0;
+    int slots = 0;          // bf16 histograms per batch
     int64_t units_b = 0, units_f = 0;
     size_t tab_b, ubeg_b, tab_f, ubeg_f, bmats, bbeg, nsz, table_end;
     size_t hb, keys, part_f, ghist, hpart, total;
@@ -128,7 +130,8 @@ int64_t ent_units(const woq_mat& m) {
     return rpu ? cdiv(m.rows, rpu) : cdiv(elems(m), kEntChunk);
 }
 
-EntLayout ent_layout(const woq_mat* mats, int32_t n, int32_t n_blocks) {
+// max_slots: at most this many bf16 histograms (256 KiB each) per batch.
+EntLayout ent_layout(const woq_mat* mats, int32_t n, int32_t n_blocks, int max_slots = kHistSlots) {
     EntLayout L;
     for (int32_t i = 0; i < n; ++i) {
         if (mats[i].dtype == WOQ_BF16) { ++L.nb; L.units_b += ent_units(mats[i]); }
@@ -146,8 +149,9 @@ EntLayout ent_layout(const woq_mat* mats, int32_t n, int32_t n_blocks) {
     L.hb = a.take(sizeof(double) * n_blocks);
     L.keys = a.take(sizeof(uint32_t) * 2 * L.nf);
     L.part_f = a.take(sizeof(double2) * L.units_f);
-    L.ghist = a.take(sizeof(uint32_t) * 65536 * (size_t)std::min(L.nb, kHistSlots));
-    L.hpart = a.take(sizeof(double4) * kHistBinParts * (size_t)std::min(L.nb, kHistSlots), 64);
+    L.slots = std::min(L.nb, max_slots);
+    L.ghist = a.take(sizeof(uint32_t) * 65536 * (size_t)L.slots);
+    L.hpart = a.take(sizeof(double4) * kHistBinParts * (size_t)L.slots, 64);
     L.total = a.end();
     return L;
 }
@@ -483,6 +487,106 @@ int32_t check_code(const uint8_t* len, const uint32_t* cw) {
         if ((call) != hipSuccess) return WOQ_ERR_HIP;  \
     } while (0)
 
+
+// ------------------------------------------------------------ entropy calls
+int32_t ent_check(const woq_mat* mats, int32_t n_mats, const int32_t* block_id, int32_t n_blocks,
+                  const double* h_mat) {
+    int32_t st = check_mats(mats, n_mats, false);
+    if (st) return st;
+    if (!h_mat) return WOQ_ERR_NULL;
+    if (n_blocks < 1 || n_blocks > kMaxBlocks) return WOQ_ERR_COUNT;
+    if (!block_id && n_blocks != 1) return WOQ_ERR_BLOCK;
+    std::vector<int32_t> cnt(n_blocks, 0);
+    for (int32_t i = 0; i < n_mats; ++i) {
+        const int32_t b = block_id ? block_id[i] : 0;
+        if (b < 0 || b >= n_blocks) return WOQ_ERR_BLOCK;
+        ++cnt[b];
+    }
+    for (int32_t b = 0; b < n_blocks; ++b)
+        if (!cnt[b]) return WOQ_ERR_BLOCK;
+    return WOQ_OK;
+}
+
+// Enqueues the entropy computation with layout L in the scratch at ws
+// (checked arguments).
+int32_t ent_run(const EntLayout& L, const woq_mat* mats, int32_t n_mats, const int32_t* block_id,
+                int32_t n_blocks, double x, double* h_mat, double* h_block, double* stats,
+                int32_t* tier, int32_t* order, void* ws, hipStream_t stream) {
+    std::vector<int32_t> cnt(n_blocks, 0);
+    for (int32_t i = 0; i < n_mats; ++i) ++cnt[block_id ? block_id[i] : 0];
+    std::vector<char> host(L.table_end, 0);
+    EntMat* tb = at<EntMat>(host.data(), L.tab_b);
+    EntMat* tf = at<EntMat>(host.data(), L.tab_f);
+    int64_t* ub = at<int64_t>(host.data(), L.ubeg_b);
+    int64_t* uf = at<int64_t>(host.data(), L.ubeg_f);
+    int ib = 0, jf = 0;
+    ub[0] = 0;
+    uf[0] = 0;
+    for (int32_t i = 0; i < n_mats; ++i) {
+        const woq_mat& m = mats[i];
+        EntMat e{m.data, elems(m), m.cols, eff_ld(m), m.dtype, i, (int32_t)m.rows, ent_rpu(m)};
+        const int64_t u = ent_units(m);
+        if (e.dtype == WOQ_BF16) { tb[ib] = e; ub[ib + 1] = ub[ib] + u; ++ib; }
+        else { tf[jf] = e; uf[jf + 1] = uf[jf] + u; ++jf; }
+    }
+    int32_t* bm = at<int32_t>(host.data(), L.bmats);
+    int32_t* bb = at<int32_t>(host.data(), L.bbeg);
+    double* nsz = at<double>(host.data(), L.nsz);
+    bb[0] = 0;
+    for (int32_t b = 0; b < n_blocks; ++b) bb[b + 1] = bb[b] + cnt[b];
+    std::vector<int32_t> fillp(bb, bb + n_blocks);
+    for (int32_t i = 0; i < n_mats; ++i) {
+        bm[fillp[block_id ? block_id[i] : 0]++] = i;
+        nsz[i] = (double)elems(mats[i]);
+    }
+
+    WOQ_HIP(stage_tables(ws, host, L.table_end, stream));
+    unsigned long long* nf = nonfinite_counter(ws);
+    WOQ_HIP(fill_u32(reinterpret_cast<uint32_t*>(nf), 2, 0u, stream));
+    const EntMat* dtb = at<EntMat>(ws, L.tab_b);
+    const int64_t* dub = at<int64_t>(ws, L.ubeg_b);
+    uint32_t* ghist = at<uint32_t>(ws, L.ghist);
+    for (int b0 = 0; b0 < L.nb; b0 += L.slots) {
+        const int b1 = std::min(L.nb, b0 + L.slots);
+        WOQ_HIP(fill_u32(ghist, (size_t)(b1 - b0) * 65536, 0u, stream));
+        WOQ_HIP(ent_hist_bf16(dtb + b0, dub + b0, b1 - b0, ub[b0], ub[b1] - ub[b0], ghist, stream));
+        WOQ_HIP(ent_hist_final(dtb + b0, b1 - b0, ghist, at<double4>(ws, L.hpart), h_mat, nf, stream));
+    }
+    if (L.nf)
+        WOQ_HIP(ent_f32(at<EntMat>(ws, L.tab_f), at<int64_t>(ws, L.ubeg_f), L.nf, L.units_f,
+                        at<uint32_t>(ws, L.keys), at<double2>(ws, L.part_f), h_mat, nf, stream));
+    WOQ_HIP(ent_blocks(at<int32_t>(ws, L.bmats), at<int32_t>(ws, L.bbeg), at<double>(ws, L.nsz),
+                       h_mat, n_blocks, x, at<double>(ws, L.hb), h_block, stats, tier, order,
+                       stream));
+    return WOQ_OK;
+}
+
+// ------------------------------------------------------- static scratch
+// Scratch of ewq_block_entropy_static, for callers that cannot allocate:
+// one array per GPU the library runs on, held until the process ends.  In
+// host code `scratch` names only a host-side stand-in; its device address
+// is looked up once per device (with that device current) and kept in
+// g_scratch, which is what kernels and copies receive.
+constexpr size_t kStaticScratch = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratch];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+int32_t static_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return WOQ_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return WOQ_ERR_HIP;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return WOQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -501,6 +605,7 @@ const char* woq_status_string(int32_t s) {
         case WOQ_ERR_ALIGN: return "pointer not sufficiently aligned";
         case WOQ_ERR_COUNT: return "matrix or block count out of range";
         case WOQ_ERR_VALUE: return "value not finite";
+        case WOQ_ERR_SCRATCH: return "the call needs more than the library's static scratch array";
         default: return "unknown status";
     }
 }
@@ -542,67 +647,36 @@ int32_t ewq_block_entropy(const woq_mat* mats, int32_t n_mats, const int32_t* bl
                           int32_t n_blocks, double x, double* h_mat, double* h_block,
                           double* stats, int32_t* tier, int32_t* order, void* ws,
                           size_t ws_bytes, hipStream_t stream) {
-    int32_t st = check_mats(mats, n_mats, false);
+    int32_t st = ent_check(mats, n_mats, block_id, n_blocks, h_mat);
     if (st) return st;
-    if (!h_mat) return WOQ_ERR_NULL;
-    if (n_blocks < 1 || n_blocks > kMaxBlocks) return WOQ_ERR_COUNT;
-    if (!block_id && n_blocks != 1) return WOQ_ERR_BLOCK;
-    std::vector<int32_t> cnt(n_blocks, 0);
-    for (int32_t i = 0; i < n_mats; ++i) {
-        const int32_t b = block_id ? block_id[i] : 0;
-        if (b < 0 || b >= n_blocks) return WOQ_ERR_BLOCK;
-        ++cnt[b];
-    }
-    for (int32_t b = 0; b < n_blocks; ++b)
-        if (!cnt[b]) return WOQ_ERR_BLOCK;
     const EntLayout L = ent_layout(mats, n_mats, n_blocks);
     if ((st = check_ws(ws, ws_bytes, L.total))) return st;
+    return ent_run(L, mats, n_mats, block_id, n_blocks, x, h_mat, h_block, stats, tier, order, ws,
+                   stream);
+}
 
-    std::vector<char> host(L.table_end, 0);
-    EntMat* tb = at<EntMat>(host.data(), L.tab_b);
-    EntMat* tf = at<EntMat>(host.data(), L.tab_f);
-    int64_t* ub = at<int64_t>(host.data(), L.ubeg_b);
-    int64_t* uf = at<int64_t>(host.data(), L.ubeg_f);
-    int ib = 0, jf = 0;
-    ub[0] = 0;
-    uf[0] = 0;
-    for (int32_t i = 0; i < n_mats; ++i) {
-        const woq_mat& m = mats[i];
-        EntMat e{m.data, elems(m), m.cols, eff_ld(m), m.dtype, i, (int32_t)m.rows, ent_rpu(m)};
-        const int64_t u = ent_units(m);
-        if (e.dtype == WOQ_BF16) { tb[ib] = e; ub[ib + 1] = ub[ib] + u; ++ib; }
-        else { tf[jf] = e; uf[jf + 1] = uf[jf] + u; ++jf; }
+// The same computation with the library's static scratch array in place of
+// a caller workspace (for callers that cannot allocate).  Histograms go
+// through the array in batches of as many slots as fit beside the tables.
+int32_t ewq_block_entropy_static(const woq_mat* mats, int32_t n_mats, const int32_t* block_id,
+                                 int32_t n_blocks, double x, double* h_mat, double* h_block,
+                                 double* stats, int32_t* tier, int32_t* order,
+                                 hipStream_t stream) {
+    int32_t st = ent_check(mats, n_mats, block_id, n_blocks, h_mat);
+    if (st) return st;
+    EntLayout L = ent_layout(mats, n_mats, n_blocks, 0);   // tables and fp32 partials only
+    if (L.total > kStaticScratch) return WOQ_ERR_SCRATCH;
+    if (L.nb) {
+        const size_t per_slot = sizeof(uint32_t) * 65536 + sizeof(double4) * kHistBinParts + kAlign;
+        const size_t fit = (kStaticScratch - L.total) / per_slot;
+        if (fit < 1) return WOQ_ERR_SCRATCH;
+        L = ent_layout(mats, n_mats, n_blocks, (int)std::min<size_t>(fit, kHistSlots));
+        if (L.total > kStaticScratch) return WOQ_ERR_SCRATCH;
     }
-    int32_t* bm = at<int32_t>(host.data(), L.bmats);
-    int32_t* bb = at<int32_t>(host.data(), L.bbeg);
-    double* nsz = at<double>(host.data(), L.nsz);
-    bb[0] = 0;
-    for (int32_t b = 0; b < n_blocks; ++b) bb[b + 1] = bb[b] + cnt[b];
-    std::vector<int32_t> fillp(bb, bb + n_blocks);
-    for (int32_t i = 0; i < n_mats; ++i) {
-        bm[fillp[block_id ? block_id[i] : 0]++] = i;
-        nsz[i] = (double)elems(mats[i]);
-    }
-
-    WOQ_HIP(stage_tables(ws, host, L.table_end, stream));
-    unsigned long long* nf = nonfinite_counter(ws);
-    WOQ_HIP(fill_u32(reinterpret_cast<uint32_t*>(nf), 2, 0u, stream));
-    const EntMat* dtb = at<EntMat>(ws, L.tab_b);
-    const int64_t* dub = at<int64_t>(ws, L.ubeg_b);
-    uint32_t* ghist = at<uint32_t>(ws, L.ghist);
-    for (int b0 = 0; b0 < L.nb; b0 += kHistSlots) {
-        const int b1 = std::min(L.nb, b0 + kHistSlots);
-        WOQ_HIP(fill_u32(ghist, (size_t)(b1 - b0) * 65536, 0u, stream));
-        WOQ_HIP(ent_hist_bf16(dtb + b0, dub + b0, b1 - b0, ub[b0], ub[b1] - ub[b0], ghist, stream));
-        WOQ_HIP(ent_hist_final(dtb + b0, b1 - b0, ghist, at<double4>(ws, L.hpart), h_mat, nf, stream));
-    }
-    if (L.nf)
-        WOQ_HIP(ent_f32(at<EntMat>(ws, L.tab_f), at<int64_t>(ws, L.ubeg_f), L.nf, L.units_f,
-                        at<uint32_t>(ws, L.keys), at<double2>(ws, L.part_f), h_mat, nf, stream));
-    WOQ_HIP(ent_blocks(at<int32_t>(ws, L.bmats), at<int32_t>(ws, L.bbeg), at<double>(ws, L.nsz),
-                       h_mat, n_blocks, x, at<double>(ws, L.hb), h_block, stats, tier, order,
-                       stream));
-    return WOQ_OK;
+    void* ws = nullptr;
+    if ((st = static_scratch(&ws))) return st;
+    return ent_run(L, mats, n_mats, block_id, n_blocks, x, h_mat, h_block, stats, tier, order, ws,
+                   stream);
 }
 
 int32_t sinq_balance(const woq_mat* mats, int32_t n_mats, int32_t iters, float* const* row_scale,

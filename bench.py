@@ -30,6 +30,12 @@ Two "% of HBM peak" figures are given: input bytes / time, and compulsory
 traffic / time, where compulsory traffic is the entropy read of every
 weight, a second read of every weight that is quantised (the tiers need the
 global entropy statistics first) and every output written.
+
+``ceilings`` gives what plain kernels with no arithmetic reach on the same
+GPU in the same run (libwoq_probe.so): an 8 GiB read from HBM, a 1 GiB copy,
+128 MiB re-read from the Infinity Cache, 16 MiB from the L2 caches, and the
+fp32 FMA issue rate; the dominant call's rate is also given against the HBM
+read ceiling.
 """
 from __future__ import annotations
 
@@ -54,85 +60,128 @@ def _log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(wl, specs, mats, qp, tiers):
-    """The oracle (numpy fp64, fp32 where the decisions are fp32) on host
-    cores over a bounded sample of the workload, and the parity of the
-    timed steps' own GPU outputs on that sample.
+def _host_f32(t):
+    """A device matrix as host fp32 (bf16 widened exactly, in numpy)."""
+    import numpy as np
+    import torch
+    if t.dtype == torch.bfloat16:
+        u = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return (u.astype(np.uint32) << 16).view(np.float32)
+    return t.contiguous().cpu().numpy()
 
-    Sample: the matrices of the first block of the Sinkhorn tier (else the
-    first block), in order, until at least 60 M weights (Llama-8B shapes: q,
-    k, v, o and gate, 92.3 M weights), each taken through every stage the
-    workload uses (entropy; Sinkhorn + group RTN + pack; int8 per-row +
-    pack; ternary + pack).  Each stage's seconds per byte on the sample are
-    applied to the workload's own tier mix.  Returns (baseline, parity); the
-    parity comparisons run outside the timed oracle work.
+
+def cpu_workers() -> int:
+    """Host cores this process may use, at most 16 (one GPU's share of a box)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def cpu_baseline(wl, specs, mats, qp, tiers, blocks_per_action=2):
+    """The oracle (numpy fp64; fp32 where the decisions are fp32) on the host
+    cores, over a bounded sample of the workload, and the parity of the timed
+    steps' own GPU outputs on that sample.
+
+    Sample: the first ``blocks_per_action`` blocks of every action the tiers
+    chose, each matrix taken through exactly what the pass does for it
+    (entropy, then Sinkhorn + group RTN + pack, int8 per-row + pack, ternary +
+    pack, or nothing).  The matrices of one action run concurrently on a
+    thread pool of ``cpu_workers()`` threads: the oracle is numpy array
+    kernels, which release the GIL, so the threads use that many cores.
+    Each action's seconds per byte (wall clock of its pool) are applied to
+    the workload's own tier mix.  Returns (baseline, parity); the parity
+    comparisons run after the timed oracle work.
     """
+    import concurrent.futures as cf
     import numpy as np
     import oracle
 
     acts = qp.action_of_block(tiers)
-    sinq_blocks = [sp.block for sp in specs if acts[sp.block] == "sinq"]
-    first = sinq_blocks[0] if sinq_blocks else specs[0].block
-    pick, n = [], 0
-    for i, m in enumerate(specs):
-        if m.block == first and n < 60_000_000:
-            pick.append(i)
-            n += mats[i].numel()
-    t_ent = t_sinq = t_i8 = t_ter = 0.0
-    nbytes = 0
-    h_gpu = qp.h_mat.cpu().numpy()
-    par = {"matrices": len(pick), "block": first, "entropy_max_rel_err": 0.0}
-    s_err = t_err = 0.0
-    n_codes = iso_bad = e2e_bad = 0
-    for i in pick:
-        w = mats[i].float().cpu().numpy()
-        nbytes += mats[i].numel() * mats[i].element_size()
-        t0 = time.perf_counter()
-        h = oracle.matrix_entropy(w)
-        t1 = time.perf_counter()
-        s, t = oracle.sinkhorn_std(w, wl.iters)
-        q = oracle.quantize_groupwise_f32(w, s.astype(np.float32), t.astype(np.float32), wl.bits,
-                                          wl.group)
-        oracle.pack_codes(q[0], wl.bits)
-        t2 = time.perf_counter()
-        q8 = oracle.quantize_groupwise_f32(w, None, None, 8, w.shape[1])
-        oracle.pack_codes(q8[0], 8)
-        t3 = time.perf_counter()
-        qt, _ = oracle.ternary_quantize(w)
-        oracle.pack_codes((qt + 1).astype(np.uint8), 2)
-        t4 = time.perf_counter()
-        t_ent += t1 - t0
-        t_sinq += t2 - t1
-        t_i8 += t3 - t2
-        t_ter += t4 - t3
-        # parity of the step's outputs (untimed)
-        if h != 0.0:
-            par["entropy_max_rel_err"] = max(par["entropy_max_rel_err"], abs(h_gpu[i] / h - 1.0))
-        o = qp.outputs.get(i)
-        if o is not None and o["action"] == "sinq":
-            sg, tg = o["s"].cpu().numpy(), o["t"].cpu().numpy()
-            s_err = max(s_err, float(np.max(np.abs(sg / s - 1.0))))
-            t_err = max(t_err, float(np.max(np.abs(tg / t - 1.0))))
-            cg = oracle.unpack_codes(o["codes"].cpu().numpy(), wl.bits, w.shape[1])
-            qi = oracle.quantize_groupwise_f32(w, sg, tg, wl.bits, wl.group)[0]
-            n_codes += cg.size
-            iso_bad += int(np.count_nonzero(cg != qi))
-            e2e_bad += int(np.count_nonzero(cg != q[0]))
-    if n_codes:
-        par.update({"s_max_rel_err": s_err, "t_max_rel_err": t_err, "codes": n_codes,
-                    "codes_mismatch_stage_isolated": iso_bad,
-                    "codes_mismatch_end_to_end": e2e_bad})
-    per_byte = {"sinq": t_sinq / nbytes, "int8row": t_i8 / nbytes, "ternary": t_ter / nbytes,
-                "keep": 0.0}
-    total = qp.bytes_in * (t_ent / nbytes)
+    nw = cpu_workers()
+    by_act = {}
+    for b, a in enumerate(acts):
+        if len(by_act.setdefault(a, [])) < blocks_per_action:
+            by_act[a].append(b)
+    sample = {a: [i for i, sp in enumerate(specs) if sp.block in bl] for a, bl in by_act.items()}
+    host = {i: _host_f32(mats[i]) for idx in sample.values() for i in idx}   # untimed copies
+
+    def run(i, a):
+        w = host[i]
+        r = {"h": oracle.matrix_entropy(w)}
+        if a == "sinq":
+            s, t = oracle.sinkhorn_std(w, wl.iters)
+            q = oracle.quantize_groupwise_f32(w, s.astype(np.float32), t.astype(np.float32),
+                                              wl.bits, wl.group)[0]
+            oracle.pack_codes(q, wl.bits)
+            r.update(s=s, t=t, q=q)
+        elif a == "int8row":
+            q = oracle.quantize_groupwise_f32(w, None, None, 8, w.shape[1])[0]
+            oracle.pack_codes(q, 8)
+            r.update(q=q)
+        elif a == "ternary":
+            q, _ = oracle.ternary_quantize(w)
+            oracle.pack_codes((q + 1).astype(np.uint8), 2)
+            r.update(q=q)
+        return r
+
+    secs, nbytes, res = {}, {}, {}
+    with cf.ThreadPoolExecutor(nw) as ex:
+        for a, idx in sample.items():
+            t0 = time.perf_counter()
+            out = list(ex.map(lambda i: run(i, a), idx))
+            secs[a] = time.perf_counter() - t0
+            nbytes[a] = sum(mats[i].numel() * mats[i].element_size() for i in idx)
+            res.update(zip(idx, out))
+    total = 0.0
     for m, sp in zip(mats, specs):
-        total += m.numel() * m.element_size() * per_byte[acts[sp.block]]
-    base = {"value": round(qp.bytes_in / total / 1e9, 6), "unit": "GB/s", "cores": 1,
+        a = acts[sp.block]
+        total += m.numel() * m.element_size() * secs[a] / nbytes[a]
+    base = {"value": round(qp.bytes_in / total / 1e9, 6), "unit": "GB/s", "cores": nw,
             "kind": "oracle",
-            "sample": (f"{len(pick)} matrices of block {first} ({nbytes / 1e9:.3f} GB) through "
-                       f"entropy ({t_ent:.1f}s), Sinkhorn K={wl.iters} + int{wl.bits} g{wl.group} "
-                       f"({t_sinq:.1f}s), int8 per-row ({t_i8:.1f}s), ternary ({t_ter:.1f}s); "
-                       "per-byte costs applied to the workload's tier mix; numpy, one thread")}
+            "sample": ("; ".join(f"{a}: blocks {by_act[a]} ({nbytes[a] / 1e9:.3f} GB, {secs[a]:.1f} s)"
+                                 for a in sample)
+                       + f"; each matrix through entropy and its action's steps (Sinkhorn K={wl.iters} "
+                       f"+ int{wl.bits} g{wl.group}, int8 per-row, ternary or none), the matrices of "
+                       f"an action on {nw} threads (numpy array kernels release the GIL); per-action "
+                       "seconds per byte applied to the workload's tier mix")}
+
+    # parity of the timed steps' own outputs on the sample (untimed)
+    h_gpu = qp.h_mat.cpu().numpy()
+    par = {"matrices": len(res), "blocks": {a: by_act[a] for a in by_act},
+           "entropy_max_rel_err": max(abs(h_gpu[i] / r["h"] - 1.0) for i, r in res.items())}
+
+    def codes(i):
+        o, r, w = qp.outputs[i], res[i], host[i]
+        a = o["action"]
+        if a == "sinq":
+            sg, tg = o["s"].cpu().numpy(), o["t"].cpu().numpy()
+            cg = oracle.unpack_codes(o["codes"].cpu().numpy().reshape(w.shape[0], -1), wl.bits, w.shape[1])
+            qi = oracle.quantize_groupwise_f32(w, sg, tg, wl.bits, wl.group)[0]
+            q64 = oracle.quantize_groupwise_f64(w, sg, tg, wl.bits, wl.group)[0]
+            diff = cg != q64
+            tie_ok = bool(np.all(~diff | oracle.near_tie_mask(w, sg, tg, wl.bits, wl.group))) if diff.any() else True
+            e2e = cg != r["q"]
+            return {"n": cg.size, "iso": int(np.count_nonzero(cg != qi)), "def": int(diff.sum()),
+                    "tie_ok": tie_ok, "e2e": int(e2e.sum()),
+                    "e2e_step": int(np.max(np.abs(cg.astype(np.int16) - r["q"].astype(np.int16)))),
+                    "s": float(np.max(np.abs(sg / r["s"] - 1))), "t": float(np.max(np.abs(tg / r["t"] - 1)))}
+        if a == "int8row":
+            cg = o["codes"].cpu().numpy().reshape(w.shape)
+            q64 = oracle.quantize_groupwise_f64(w, None, None, 8, w.shape[1])[0]
+            return {"n": cg.size, "iso": int(np.count_nonzero(cg != r["q"])),
+                    "def": int(np.count_nonzero(cg != q64)), "tie_ok": True, "e2e": 0, "e2e_step": 0}
+        return None
+
+    with cf.ThreadPoolExecutor(nw) as ex:
+        cres = [c for c in ex.map(codes, sorted(res)) if c is not None]
+    if cres:
+        sq = [c for c in cres if "s" in c]
+        par.update({"codes": sum(c["n"] for c in cres),
+                    "codes_mismatch_stage_isolated": sum(c["iso"] for c in cres),
+                    "codes_vs_fp64_definition": sum(c["def"] for c in cres),
+                    "definition_mismatches_all_near_ties": all(c["tie_ok"] for c in cres),
+                    "codes_mismatch_end_to_end": sum(c["e2e"] for c in cres),
+                    "end_to_end_max_code_step": max(c["e2e_step"] for c in cres)})
+        if sq:
+            par.update({"s_max_rel_err": max(c["s"] for c in sq), "t_max_rel_err": max(c["t"] for c in sq)})
     return base, par
 
 
@@ -327,6 +376,157 @@ def df11_rate(mats, specs, acts, stream, reps=3):
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+PROBE_LIB = os.path.join(ROOT, "weight_only_quantization_softmax_amd", "libwoq_probe.so")
+
+
+def _probe():
+    import ctypes
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError(f"{PROBE_LIB} is missing: build it with "
+                           "python -m weight_only_quantization_softmax_amd.build")
+    lib = ctypes.CDLL(PROBE_LIB)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.probe_read.argtypes = [vp, sz, i32, i32, i32, vp, vp]
+    lib.probe_copy.argtypes = [vp, vp, sz, i32, vp]
+    lib.probe_fma.argtypes = [vp, i32, i32, vp]
+    lib.probe_barrier.argtypes = [vp, vp, i32, i32, i32, ctypes.c_uint, vp]
+    for f in (lib.probe_read, lib.probe_copy, lib.probe_fma, lib.probe_barrier):
+        f.restype = i32
+    return lib
+
+
+def barrier_us(lib, grid, team, n_bar=2000, spin_limit=1 << 22):
+    """Microseconds per barrier among teams of `team` workgroups in one
+    cooperative launch of `grid` workgroups (n_bar barriers minus one,
+    HIP events); None if a wait gave up."""
+    import torch
+    stream = torch.cuda.current_stream()
+    sh = ctypes_stream(stream)
+    cnt = torch.zeros((grid // team) * 64, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def run(n):
+        cnt.zero_()
+        err.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = lib.probe_barrier(cnt.data_ptr(), err.data_ptr(), n, grid, team, spin_limit, sh)
+        e1.record(stream)
+        e1.synchronize()
+        if rc != 0:
+            raise RuntimeError(f"probe_barrier failed: {rc}")
+        return e0.elapsed_time(e1), int(err.item())
+    run(8)
+    t1, e_1 = run(1)
+    tn, e_n = run(n_bar)
+    if e_1 or e_n:
+        return None
+    return round((tn - t1) * 1e3 / (n_bar - 1), 3)
+
+
+def probe_rate(lib, kind, nbytes, passes=1, grid=2048, chunked=0, reps=5, bufs=None):
+    """GB/s of one probe kernel (median of `reps` launches, HIP events on the
+    stream the probe is launched on).  kind: "read", "copy" or "fma" (for
+    "fma", nbytes is the iteration count and the result is T lane-ops/s)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    sh = ctypes_stream(stream)
+    sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+    src, dst = bufs if bufs else (None, None)
+
+    def launch():
+        if kind == "read":
+            rc = lib.probe_read(src.data_ptr(), nbytes, passes, grid, chunked, sink.data_ptr(), sh)
+        elif kind == "copy":
+            rc = lib.probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, grid, sh)
+        else:
+            rc = lib.probe_fma(sink.data_ptr(), nbytes, grid, sh)
+        if rc != 0:
+            raise RuntimeError(f"probe_{kind} failed: {rc}")
+
+    launch()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = sorted(times)[len(times) // 2]
+    if kind == "fma":
+        ops = 8 * nbytes * grid * 256
+        return {"ms": round(ms, 4), "T_lane_ops_per_s": round(ops / (ms / 1e3) / 1e12, 2)}
+    moved = nbytes * passes * (2 if kind == "copy" else 1)
+    return {"ms": round(ms, 4), "GBps": round(moved / (ms / 1e3) / 1e9, 1)}
+
+
+def ctypes_stream(stream):
+    import ctypes
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def ceilings():
+    """What plain kernels with no arithmetic reach on this GPU (the library's
+    streaming kernels are judged against these, not only against the
+    8 TB/s spec): a grid-stride read of 8 GiB from HBM, a 1 GiB copy (read +
+    write), re-reads of a 128 MiB buffer that stays in the 256 MB Infinity
+    Cache (32 passes in one launch; grid-stride and per-workgroup contiguous
+    order), a 16 MiB buffer re-read from the L2 caches, and the fp32 FMA issue
+    rate without packed instructions."""
+    import torch
+    lib = _probe()
+    big = torch.empty(8 << 30, dtype=torch.uint8, device="cuda")
+    big.fill_(1)
+    res = {"hbm_read_8GiB": probe_rate(lib, "read", 8 << 30, bufs=(big, None))}
+    a = big[: 1 << 30]
+    b = big[1 << 30: 2 << 30]
+    res["hbm_copy_1GiB"] = probe_rate(lib, "copy", 1 << 30, bufs=(a, b))
+    res["mall_reread_128MiB_x32"] = probe_rate(lib, "read", 128 << 20, passes=32, bufs=(a, None))
+    res["mall_reread_128MiB_x32_chunked"] = probe_rate(lib, "read", 128 << 20, passes=32, chunked=1,
+                                                      bufs=(a, None))
+    res["l2_reread_16MiB_x64"] = probe_rate(lib, "read", 16 << 20, passes=64, bufs=(a, None))
+    res["fp32_fma"] = probe_rate(lib, "fma", 4096, grid=4096)
+    res["grid_barrier_us_512wg"] = barrier_us(lib, 512, 512)
+    del big
+    torch.cuda.synchronize()
+    return res
+
+
+def ceilings_sweep():
+    """The probes over buffer sizes, grids and access orders (re-reads of
+    8 MiB .. 1 GiB: L2-resident up to 32 MiB, Infinity-Cache-resident up to
+    256 MiB), the 1 GiB copy per grid, the fp32 FMA rate, and barriers among
+    teams of workgroups of one cooperative launch.  One JSON line each."""
+    import torch
+    lib = _probe()
+    big = torch.empty(8 << 30, dtype=torch.uint8, device="cuda")
+    big.fill_(1)
+    out = {f"hbm_read_8GiB_g{g}": probe_rate(lib, "read", 8 << 30, grid=g, bufs=(big, None))["GBps"]
+           for g in (1024, 2048, 4096)}
+    out["hbm_read_4GiB_chunked_g2048"] = probe_rate(lib, "read", 4 << 30, chunked=1,
+                                                    bufs=(big, None))["GBps"]
+    print(json.dumps(out), flush=True)
+    for mb in (8, 16, 32, 48, 64, 96, 128, 160, 192, 224, 256, 320, 384, 512, 1024):
+        passes = max(2, min(64, 4096 // mb))
+        r = {"MiB": mb, "passes": passes}
+        for g in (1024, 2048, 4096):
+            for ch in (0, 1):
+                r[f"g{g}{'_chunked' if ch else ''}"] = probe_rate(
+                    lib, "read", mb << 20, passes=passes, grid=g, chunked=ch, bufs=(big, None))["GBps"]
+        print(json.dumps(r), flush=True)
+    for g in (1024, 2048, 4096):
+        print(json.dumps({"copy_1GiB_grid": g, **probe_rate(lib, "copy", 1 << 30, grid=g,
+                                                            bufs=(big[:1 << 30], big[1 << 30:2 << 30]))}),
+              flush=True)
+    print(json.dumps({"fp32_fma": probe_rate(lib, "fma", 8192, grid=8192)}), flush=True)
+    for grid, team in ((256, 256), (512, 512), (1024, 1024), (2048, 2048), (512, 128), (512, 64),
+                       (512, 32), (512, 8)):
+        print(json.dumps({"barrier_grid": grid, "team": team, "us": barrier_us(lib, grid, team)}),
+              flush=True)
+    return 0
+
+
 def torch_reference(reps=20):
     """Streaming rates of torch's stock kernels on the box (not the
     library's), for comparison with the library's kernels: a 1 GiB device
@@ -373,13 +573,28 @@ def main() -> int:
     ap.add_argument("--workload", default="stack8b")
     ap.add_argument("--sinq-batch-mb", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the streaming-ceiling probes (libwoq_probe.so)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one device copy of this size first (counter calibration)")
     ap.add_argument("--torch-reference", action="store_true",
                     help="only measure torch's stock streaming kernels on the box")
+    ap.add_argument("--ceilings-only", action="store_true",
+                    help="only measure the streaming ceilings (libwoq_probe.so)")
+    ap.add_argument("--ceilings-sweep", action="store_true",
+                    help="only sweep the probes over sizes, grids and barrier teams")
     args = ap.parse_args()
+    if args.ceilings_sweep:
+        import torch
+        torch.cuda.set_device(0)
+        return ceilings_sweep()
     if args.torch_reference:
         return torch_reference()
+    if args.ceilings_only:
+        import torch
+        torch.cuda.set_device(0)
+        print(json.dumps({"ceilings": ceilings()}), flush=True)
+        return 0
     if args.gpus != 1:
         print(f"bench.py: this pass runs on one GPU; --gpus {args.gpus} is not supported "
               "(blocks are independent after tiering; see the sharding design)", file=sys.stderr)
@@ -475,6 +690,11 @@ def main() -> int:
         "calls": {k: {"ms_per_step": round(v["ms_per_step"], 3), "calls": v["calls"]}
                   for k, v in per_kind.items()},
     }
+    if not args.no_ceilings:
+        _log("[bench] streaming ceilings")
+        ceil = ceilings()
+        ceil["dominant_vs_hbm_read_ceiling"] = round(achieved / ceil["hbm_read_8GiB"]["GBps"], 4)
+        out["ceilings"] = ceil
     if not args.no_cpu_baseline:
         _log("[bench] cpu baseline (oracle on a sample)")
         out["cpu_baseline"], out["parity"] = cpu_baseline(wl, specs, mats, qp, tiers)

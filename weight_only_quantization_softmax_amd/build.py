@@ -2,8 +2,10 @@
 
     python -m weight_only_quantization_softmax_amd.build
 
-Objects go to ``_build/`` at the repository root; the shared library is
-written next to this file.  hipcc cross-compiles without a GPU.
+Objects go to ``_build/`` at the repository root; the shared libraries are
+written next to this file: ``libwoq.so`` (the pass) and ``libwoq_probe.so``
+(streaming ceilings used by the benchmark only).  hipcc cross-compiles
+without a GPU.
 """
 from __future__ import annotations
 
@@ -20,6 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libwoq.so")
 SOURCES = ["api.hip", "entropy.hip", "sinq.hip", "quant.hip", "df11.hip"]
+PROBE_LIB = os.path.join(PKG, "libwoq_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 ARCH = os.environ.get("WOQ_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
@@ -51,18 +55,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(6, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB, verbose)
     return LIB
 
 

@@ -19,6 +19,12 @@ BitNet.cpp" (unite.ai), "He Thong Trong So Ternary") use the per-row scale
 and no balancing.
 
     python -m weight_only_quantization_softmax_amd.quality --workload block --blocks 0
+    python -m weight_only_quantization_softmax_amd.quality --channels 1 1 --shape 1024 4096
+
+The second form reports on weights with outlier channels (woqdata's
+channel_matrix: rows and columns scaled by random log-normal factors), the
+case the page names: some rows with outliers, some columns with larger
+variance.
 """
 from __future__ import annotations
 
@@ -94,8 +100,19 @@ def main(argv=None) -> int:
     ap.add_argument("--blocks", type=int, nargs="*", default=[0])
     ap.add_argument("--matrices", nargs="*", default=None,
                     help="matrix name suffixes to include (e.g. k v gate); all if omitted")
+    ap.add_argument("--channels", type=float, nargs=2, default=None, metavar=("ROW_SIGMA", "COL_SIGMA"),
+                    help="report on a channel_matrix with these log-normal spreads instead")
+    ap.add_argument("--shape", type=int, nargs=2, default=(1024, 4096))
+    ap.add_argument("--seed", type=int, default=0)
     args = ap.parse_args(argv)
     torch.cuda.set_device(0)
+    if args.channels is not None:
+        w = woqdata.channel_matrix(*args.shape, args.seed, row_sigma=args.channels[0],
+                                   col_sigma=args.channels[1], device="cuda")
+        name = f"channels(row {args.channels[0]}, col {args.channels[1]})"
+        for r in matrix_report(w):
+            print(json.dumps({"matrix": name, "shape": list(w.shape), **r}), flush=True)
+        return 0
     wl, specs, mats = woqdata.generate(args.workload, device="cuda", blocks=args.blocks)
     for spec, w in zip(specs, mats):
         if args.matrices and spec.name.split(".")[-1] not in args.matrices:

@@ -38,7 +38,7 @@ import torch
 
 __all__ = [
     "MatSpec", "Workload", "WORKLOADS", "workload", "weights", "generate",
-    "draw_matrix",
+    "draw_matrix", "random_matrix", "channel_matrix",
 ]
 
 
@@ -199,6 +199,22 @@ def random_matrix(rows: int, cols: int, seed: int, dtype=torch.bfloat16,
     """A free-shape matrix with the workloads' value distribution (test sizes)."""
     return draw_matrix(rows, cols, std, outlier_frac, outlier_mult, dtype,
                        (7 << 40) | (int(seed) & ((1 << 40) - 1)), device)
+
+
+def channel_matrix(rows: int, cols: int, seed: int, dtype=torch.bfloat16, std: float = 0.02,
+                   row_sigma: float = 1.0, col_sigma: float = 1.0, device="cpu") -> torch.Tensor:
+    """Weights with outlier channels: N(0, std^2) draws whose rows and columns
+    are multiplied by random log-normal factors exp(row_sigma a_i) and
+    exp(col_sigma b_j), a, b ~ N(0, 1) (some rows and some columns much larger
+    than the rest).  Random draws only; one CPU generator, so the values do
+    not depend on the device."""
+    g = torch.Generator("cpu")
+    g.manual_seed((6 << 40) | (int(seed) & ((1 << 40) - 1)))
+    w = torch.randn(rows, cols, generator=g, dtype=torch.float32) * std
+    a = torch.randn(rows, generator=g, dtype=torch.float32)
+    b = torch.randn(cols, generator=g, dtype=torch.float32)
+    w = w * torch.exp(row_sigma * a)[:, None] * torch.exp(col_sigma * b)[None, :]
+    return w.to(dtype).to(device)
 
 
 def _check() -> None:  # shapes sanity, used by tests

@@ -65,7 +65,7 @@ def _check_shape(rows: int, cols: int, bits: int, group: int):
 
 
 # A fast ratio u = x * (1/delta) is within a few fp32 ulps of the exact ratio
-# (2^b - 1) * x / (hi - lo): at most about 6.8e-5 away for 8-bit codes.  When
+# (2^b - 1) * x / (hi - lo): at most about 6.1e-5 away for 8-bit codes.  When
 # u lies within NEAR_HALF of a half-way point the ratio is recomputed with one
 # correctly rounded division, which returns exactly k + 1/2 whenever the exact
 # ratio is k + 1/2 and its operands are exact (bf16 / fp32 inputs without
@@ -80,13 +80,17 @@ def quantize_groupwise_f32(w, s=None, t=None, bits: int = 4, group: int = 64):
     operation): x = (w * (1/s_i)) * (1/t_j); per group lo = min(0, min x),
     hi = max(0, max x), d = hi - lo, delta = d / (2^b - 1), inv = 1 / delta;
     a group whose inv is not finite gets z = 0 and q = 0; otherwise
-    z = clamp(rne(((2^b - 1) * -lo) / d)), and per element u = x * inv, or
-    u = ((2^b - 1) * x) / d when |u - rne(u)| > NEAR_HALF, then
+    z = clamp(rne(uz)) with uz = -lo * inv, or uz = ((2^b - 1) * -lo) / d when
+    |uz - rne(uz)| > NEAR_HALF; per element u = x * inv, and when the
+    matrix has no scales or b = 8 (where ratios can be exact half-way points,
+    or the fast ratio's error can exceed the 1e-5 near-tie window) u =
+    ((2^b - 1) * x) / d when |u - rne(u)| > NEAR_HALF; then
     q = clamp(rne(u) + z, 0, 2^b - 1)."""
     x = balanced_f32(w, s, t)
     rows, cols = x.shape
     _check_shape(rows, cols, bits, group)
     qmax = F32(2 ** bits - 1)
+    exact = (s is None and t is None) or bits == 8
     xg = x.reshape(rows, cols // group, group)
     lo = np.minimum(F32(0), xg.min(axis=2))
     hi = np.maximum(F32(0), xg.max(axis=2))
@@ -97,11 +101,15 @@ def quantize_groupwise_f32(w, s=None, t=None, bits: int = 4, group: int = 64):
         ok = np.isfinite(inv)
         inv_s = np.where(ok, inv, F32(0))
         ds = np.where(ok & (d > 0), d, F32(1))
-        z = np.clip(np.rint((qmax * -lo) / ds), 0, qmax)
+        uz = (-lo) * inv_s
+        rz = np.rint(uz)
+        rz = np.where(np.abs(uz - rz) > NEAR_HALF, np.rint((qmax * -lo) / ds), rz)
+        z = np.clip(rz, 0, qmax)
         u = xg * inv_s[:, :, None]
         r = np.rint(u)
-        near = np.abs(u - r) > NEAR_HALF
-        r = np.where(near, np.rint((qmax * xg) / ds[:, :, None]), r)
+        if exact:
+            near = np.abs(u - r) > NEAR_HALF
+            r = np.where(near, np.rint((qmax * xg) / ds[:, :, None]), r)
         q = np.clip(r + z[:, :, None], 0, qmax)
     z = np.where(ok, z, 0)
     q = np.where(ok[:, :, None], q, 0)

@@ -511,7 +511,7 @@ int32_t ent_check(const woq_mat* mats, int32_t n_mats, const int32_t* block_id, 
 // (checked arguments).
 int32_t ent_run(const EntLayout& L, const woq_mat* mats, int32_t n_mats, const int32_t* block_id,
                 int32_t n_blocks, double x, double* h_mat, double* h_block, double* stats,
-                int32_t* tier, int32_t* order, void* ws, hipStream_t stream) {
+                int32_t* tier, int32_t* order, uint32_t* exp_hist, void* ws, hipStream_t stream) {
     std::vector<int32_t> cnt(n_blocks, 0);
     for (int32_t i = 0; i < n_mats; ++i) ++cnt[block_id ? block_id[i] : 0];
     std::vector<char> host(L.table_end, 0);
@@ -543,6 +543,7 @@ int32_t ent_run(const EntLayout& L, const woq_mat* mats, int32_t n_mats, const i
     WOQ_HIP(stage_tables(ws, host, L.table_end, stream));
     unsigned long long* nf = nonfinite_counter(ws);
     WOQ_HIP(fill_u32(reinterpret_cast<uint32_t*>(nf), 2, 0u, stream));
+    if (exp_hist) WOQ_HIP(fill_u32(exp_hist, (size_t)n_mats * 256, 0u, stream));
     const EntMat* dtb = at<EntMat>(ws, L.tab_b);
     const int64_t* dub = at<int64_t>(ws, L.ubeg_b);
     uint32_t* ghist = at<uint32_t>(ws, L.ghist);
@@ -550,7 +551,8 @@ int32_t ent_run(const EntLayout& L, const woq_mat* mats, int32_t n_mats, const i
         const int b1 = std::min(L.nb, b0 + L.slots);
         WOQ_HIP(fill_u32(ghist, (size_t)(b1 - b0) * 65536, 0u, stream));
         WOQ_HIP(ent_hist_bf16(dtb + b0, dub + b0, b1 - b0, ub[b0], ub[b1] - ub[b0], ghist, stream));
-        WOQ_HIP(ent_hist_final(dtb + b0, b1 - b0, ghist, at<double4>(ws, L.hpart), h_mat, nf, stream));
+        WOQ_HIP(ent_hist_final(dtb + b0, b1 - b0, ghist, at<double4>(ws, L.hpart), h_mat, nf,
+                               exp_hist, stream));
     }
     if (L.nf)
         WOQ_HIP(ent_f32(at<EntMat>(ws, L.tab_f), at<int64_t>(ws, L.ubeg_f), L.nf, L.units_f,
@@ -651,8 +653,21 @@ int32_t ewq_block_entropy(const woq_mat* mats, int32_t n_mats, const int32_t* bl
     if (st) return st;
     const EntLayout L = ent_layout(mats, n_mats, n_blocks);
     if ((st = check_ws(ws, ws_bytes, L.total))) return st;
-    return ent_run(L, mats, n_mats, block_id, n_blocks, x, h_mat, h_block, stats, tier, order, ws,
-                   stream);
+    return ent_run(L, mats, n_mats, block_id, n_blocks, x, h_mat, h_block, stats, tier, order,
+                   nullptr, ws, stream);
+}
+
+int32_t ewq_block_entropy_ex(const woq_mat* mats, int32_t n_mats, const int32_t* block_id,
+                             int32_t n_blocks, double x, double* h_mat, double* h_block,
+                             double* stats, int32_t* tier, int32_t* order, uint32_t* exp_hist,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+    int32_t st = ent_check(mats, n_mats, block_id, n_blocks, h_mat);
+    if (st) return st;
+    if (exp_hist && !aligned(exp_hist, 16)) return WOQ_ERR_ALIGN;
+    const EntLayout L = ent_layout(mats, n_mats, n_blocks);
+    if ((st = check_ws(ws, ws_bytes, L.total))) return st;
+    return ent_run(L, mats, n_mats, block_id, n_blocks, x, h_mat, h_block, stats, tier, order,
+                   exp_hist, ws, stream);
 }
 
 // The same computation with the library's static scratch array in place of
@@ -675,8 +690,8 @@ int32_t ewq_block_entropy_static(const woq_mat* mats, int32_t n_mats, const int3
     }
     void* ws = nullptr;
     if ((st = static_scratch(&ws))) return st;
-    return ent_run(L, mats, n_mats, block_id, n_blocks, x, h_mat, h_block, stats, tier, order, ws,
-                   stream);
+    return ent_run(L, mats, n_mats, block_id, n_blocks, x, h_mat, h_block, stats, tier, order,
+                   nullptr, ws, stream);
 }
 
 int32_t sinq_balance(const woq_mat* mats, int32_t n_mats, int32_t iters, float* const* row_scale,
@@ -803,7 +818,7 @@ int32_t quant_impl(const woq_mat* mats, int32_t n_mats, const float* const* row_
     for (int32_t i = 0; i < n_mats; ++i) idx[i] = i;
     std::stable_sort(idx.begin(), idx.end(),
                      [&](int a, int b) { return q_key(mats[a], group) < q_key(mats[b], group); });
-    struct Set { QKey key; int first, count; size_t uoff; int64_t units; };
+    struct Set { QKey key; int first, count; size_t uoff; int64_t units; bool tie; };
     std::vector<Set> sets;
     size_t uoff = 0;
     for (int p = 0; p < n_mats; ++p) {
@@ -812,7 +827,7 @@ int32_t quant_impl(const woq_mat* mats, int32_t n_mats, const float* const* row_
         const QKey key = q_key(m, group);
         if (sets.empty() || !(sets.back().key == key)) {
             if (!sets.empty()) uoff += sets.back().count + 1;
-            sets.push_back(Set{key, p, 0, uoff, 0});
+            sets.push_back(Set{key, p, 0, uoff, 0, bits == 8});
             ub[uoff] = 0;
         }
         Set& st_ = sets.back();
@@ -829,6 +844,7 @@ int32_t quant_impl(const woq_mat* mats, int32_t n_mats, const float* const* row_
         q.dtype = m.dtype;
         q.group = eff_group(m, group);
         tb[p] = q;
+        if (!q.rs && !q.ct) st_.tie = true;   // ratios of unscaled inputs can be exact halves
         ub[uoff + st_.count + 1] = ub[uoff + st_.count] + q_units(m, group);
         ++st_.count;
         st_.units = ub[uoff + st_.count];
@@ -839,12 +855,14 @@ int32_t quant_impl(const woq_mat* mats, int32_t n_mats, const float* const* row_
         const QMat* dt = at<QMat>(ws, L.tab_b) + st_.first;
         const int64_t* du = at<int64_t>(ws, L.ubeg_b) + st_.uoff;
         if (st_.key.kind == 0)
-            WOQ_HIP(quant_tile(dt, du, st_.count, st_.units, st_.key.dtype, bits, dbook, steps, stream));
+            WOQ_HIP(quant_tile(dt, du, st_.count, st_.units, st_.key.dtype, bits, dbook, steps,
+                               st_.tie, stream));
         else if (st_.key.kind == 1)
             WOQ_HIP(quant_wave(dt, du, st_.count, st_.units, st_.key.dtype, bits, st_.key.nvl, dbook,
-                               steps, stream));
+                               steps, st_.tie, stream));
         else
-            WOQ_HIP(quant_big(dt, du, st_.count, st_.units, st_.key.dtype, bits, dbook, steps, stream));
+            WOQ_HIP(quant_big(dt, du, st_.count, st_.units, st_.key.dtype, bits, dbook, steps,
+                              st_.tie, stream));
     }
     return WOQ_OK;
 }

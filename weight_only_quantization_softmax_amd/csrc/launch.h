@@ -20,9 +20,10 @@ hipError_t ent_hist_bf16(const EntMat* mats, const int64_t* ubeg, int nmat,
 // part[nmat * kHistBinParts]), then one combine per matrix.
 constexpr int kHistBinParts = 16;
 // nonfinite: the call's uint64 counter of NaN / inf weights (added to).
+// exp_hist (may be NULL): per matrix slot 256 exponent-field counts, added to.
 hipError_t ent_hist_final(const EntMat* mats, int nmat, const uint32_t* ghist,
                           double4* part, double* h_mat, unsigned long long* nonfinite,
-                          hipStream_t s);
+                          uint32_t* exp_hist, hipStream_t s);
 hipError_t ent_f32(const EntMat* mats, const int64_t* ubeg, int nmat,
                    int64_t n_units, uint32_t* keys, double2* part,
                    double* h_mat, unsigned long long* nonfinite, hipStream_t s);
@@ -75,15 +76,17 @@ constexpr int kQWaveMax = 4096;
 constexpr int kDTileRows = 4;
 // book == NULL: the affine grid; else the code-book grid (bits 2..4) with
 // the table at `book` in device memory and `steps` comparisons per value.
+// tie: some matrix of the launch has no scales, or bits == 8, so element
+// ratios near a half-way point must be re-decided by division (affine grid).
 hipError_t quant_tile(const QMat* mats, const int64_t* ubeg, int nmat,
                       int64_t n_units, int dtype, int bits, const CbTable* book,
-                      int steps, hipStream_t s);
+                      int steps, bool tie, hipStream_t s);
 hipError_t quant_wave(const QMat* mats, const int64_t* ubeg, int nmat,
                       int64_t n_units, int dtype, int bits, int nvl,
-                      const CbTable* book, int steps, hipStream_t s);
+                      const CbTable* book, int steps, bool tie, hipStream_t s);
 hipError_t quant_big(const QMat* mats, const int64_t* ubeg, int nmat,
                      int64_t n_units, int dtype, int bits, const CbTable* book,
-                     int steps, hipStream_t s);
+                     int steps, bool tie, hipStream_t s);
 hipError_t dequant(const QMat* mats, const int64_t* ubeg, int nmat,
                    int64_t n_units, int out_dtype, int bits, const CbTable* book,
                    hipStream_t s);

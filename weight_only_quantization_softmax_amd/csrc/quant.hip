@@ -37,6 +37,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace woq {
 namespace {
 
@@ -79,12 +81,21 @@ struct GroupParams {
     bool ok;
 };
 
-// Per group: d = hi - lo, delta = d / (2^b - 1), inv = 1 / delta.  The
-// zero-point ratio -lo / delta is evaluated as ((2^b - 1) * -lo) / d with one
-// correctly rounded division: for bf16 / fp32 inputs without scales the
-// numerator and d are exact, so an exact half-way ratio (for example a group
-// with hi = -lo, ratio (2^b - 1) / 2) comes out as exactly k + 1/2 and rounds
-// half to even as the definition says.
+// A fast ratio v * inv (inv = 1/delta) lies within about 4 ulps of the
+// exact ratio (2^b - 1) * v / d, d = hi - lo: within 6.1e-5 for |ratio| <=
+// 255.  Its rounding can differ from the exact one only when it lies within
+// that distance of a half-way point, so such ratios (|u - rne(u)| >
+// kNearHalf, rare) are recomputed with one correctly rounded division, which
+// for exact operands (inputs without scales) returns an exact half-way ratio
+// as exactly k + 1/2, rounded half to even as the definition says.
+constexpr float kNearHalf = 0.5f - 0x1p-13f;
+
+__device__ __forceinline__ bool near_half(float u, float r) { return fabsf(__fsub_rn(u, r)) > kNearHalf; }
+
+// Per group: d = hi - lo, delta = d / (2^b - 1), inv = 1 / delta, and the
+// zero-point rne(-lo / delta) from the fast ratio -lo * inv, or from
+// ((2^b - 1) * -lo) / d when that is near a half-way point (the same
+// rounding as always dividing: away from a half-way point both round alike).
 template <int BITS>
 __device__ __forceinline__ GroupParams group_params(float lo, float hi) {
     constexpr float qmax = (float)((1 << BITS) - 1);
@@ -95,20 +106,22 @@ __device__ __forceinline__ GroupParams group_params(float lo, float hi) {
     g.delta = __fdiv_rn(g.d, qmax);
     g.inv = __fdiv_rn(1.0f, g.delta);
     g.ok = isfinite(g.inv);
-    g.z = g.ok ? clampf(rintf(__fdiv_rn(__fmul_rn(-lo, qmax), g.d)), 0.f, qmax) : 0.f;
+    const float uz = __fmul_rn(-lo, g.inv);
+    float rz = rintf(uz);
+    if (near_half(uz, rz)) rz = rintf(__fdiv_rn(__fmul_rn(-lo, qmax), g.d));
+    g.z = g.ok ? clampf(rz, 0.f, qmax) : 0.f;
     return g;
 }
 
-// A fast ratio u = x * inv lies within a few ulps of the exact ratio
-// (2^b - 1) * x / d (about 6.8e-5 for 8-bit codes), so its rounding can
-// differ from the exact one only when u is within that distance of a
-// half-way point.  Such ratios (|u - rne(u)| > kNearHalf, rare) are
-// recomputed with one correctly rounded division, exact at exact half-way
-// points as for the zero-point.
-constexpr float kNearHalf = 0.5f - 0x1p-13f;
-
+// Codes of 8 values.  exact: element ratios near a half-way point are
+// recomputed by the division (matrices without scales, whose ratios can be
+// exact half-way points, and 8-bit codes, where the fast ratio's error can
+// exceed the 1e-5 near-tie window).  Otherwise (2-4-bit codes of a balanced
+// matrix) the fast ratio is within 4 ulps * 15 = 3.6e-6 of the exact one, so
+// the two can differ only at near ties of the definition.
 template <int BITS>
-__device__ __forceinline__ void code8(const float (&x)[8], const GroupParams& g, uint32_t (&c)[8]) {
+__device__ __forceinline__ void code8(const float (&x)[8], const GroupParams& g, bool exact,
+                                      uint32_t (&c)[8]) {
     constexpr float qmax = (float)((1 << BITS) - 1);
     float r[8];
     bool near = false;
@@ -116,14 +129,13 @@ __device__ __forceinline__ void code8(const float (&x)[8], const GroupParams& g,
     for (int k = 0; k < 8; ++k) {
         const float u = __fmul_rn(x[k], g.inv);
         r[k] = rintf(u);
-        near |= fabsf(__fsub_rn(u, r[k])) > kNearHalf;
+        if (exact) near |= near_half(u, r[k]);
     }
     if (near) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const float u = __fmul_rn(x[k], g.inv);
-            if (fabsf(__fsub_rn(u, rintf(u))) > kNearHalf)
-                r[k] = rintf(__fdiv_rn(__fmul_rn(x[k], qmax), g.d));
+            if (near_half(u, rintf(u))) r[k] = rintf(__fdiv_rn(__fmul_rn(x[k], qmax), g.d));
         }
     }
 #pragma unroll
@@ -218,9 +230,9 @@ struct Grid {
         else g = group_params<BITS>(lo, hi);
     }
     __device__ __forceinline__ void code(const float (&x)[8], const CbTable* bk, int steps,
-                                         uint32_t (&c)[8]) const {
+                                         bool exact, uint32_t (&c)[8]) const {
         if constexpr (CB) code8_cb(x, p.inv, bk, steps, c);
-        else code8<BITS>(x, g, c);
+        else code8<BITS>(x, g, exact, c);
     }
     __device__ __forceinline__ void store(const QMat& q, uint32_t gi) const {
         if constexpr (CB) {
@@ -313,7 +325,9 @@ constexpr int kTileRows = kQTileRows;
 constexpr int kTileCols = kQTileCols;
 static_assert(kTileCols == 8 * kT, "one 8-column vector per thread");
 
-template <int DT, int BITS, bool CB>
+// TIE: the launch may hold matrices whose ratios need the near-half
+// fallback of code8 (no scales, or 8-bit codes); without it no check is made.
+template <int DT, int BITS, bool CB, bool TIE>
 __global__ __launch_bounds__(kT) void k_quant_tile(const QMat* __restrict__ mats,
                                                    const int64_t* __restrict__ ubeg, int nmat,
                                                    const CbTable* __restrict__ book, int steps) {
@@ -329,6 +343,7 @@ __global__ __launch_bounds__(kT) void k_quant_tile(const QMat* __restrict__ mats
     const int nr = min(kTileRows, q.rows - r0);
     const int lanes = q.group >> 3;
     const bool has_rs = q.rs != nullptr, has_ct = q.ct != nullptr;
+    const bool exact = TIE && ((!has_rs && !has_ct) || BITS == 8);  // near-half fallback (code8)
     float c[8];
     if (has_ct && active) load_ct(q.ct, col, c);
     else {
@@ -361,7 +376,7 @@ __global__ __launch_bounds__(kT) void k_quant_tile(const QMat* __restrict__ mats
         if (active) {
             const uint32_t e0 = row * (uint32_t)q.cols + col;
             uint32_t cd[8];
-            g.code(x, bk, steps, cd);
+            g.code(x, bk, steps, exact, cd);
             store_codes<BITS>(q.codes, e0, cd);
             if ((threadIdx.x & (lanes - 1)) == 0)
                 g.store(q, e0 >> __builtin_ctz((uint32_t)q.group));  // power-of-two group
@@ -372,7 +387,7 @@ __global__ __launch_bounds__(kT) void k_quant_tile(const QMat* __restrict__ mats
 // Groups of more than 512 and at most 64 * 8 * NVL columns: one wave per
 // group (four per workgroup), values kept packed in registers between the
 // min / max reduction and the coding pass.
-template <int DT, int BITS, int NVL, bool CB>
+template <int DT, int BITS, int NVL, bool CB, bool TIE>
 __global__ __launch_bounds__(kT) void k_quant_wave(const QMat* __restrict__ mats,
                                                    const int64_t* __restrict__ ubeg, int nmat,
                                                    const CbTable* __restrict__ book, int steps) {
@@ -389,6 +404,7 @@ __global__ __launch_bounds__(kT) void k_quant_wave(const QMat* __restrict__ mats
     const uint32_t ibase = row * (uint32_t)q.ld + col0;           // weights (row stride ld)
     const int nvg = q.group >> 3;
     const bool has_rs = q.rs != nullptr, has_ct = q.ct != nullptr;
+    const bool exact = TIE && ((!has_rs && !has_ct) || BITS == 8);  // near-half fallback (code8)
     const float rsv = has_rs && live ? gload<float>(q.rs + row) : 1.0f;
     Raw8<DT> raw[NVL];
     float lo = INFINITY, hi = -INFINITY;
@@ -420,7 +436,7 @@ __global__ __launch_bounds__(kT) void k_quant_wave(const QMat* __restrict__ mats
             if (has_ct) load_ct(q.ct, col0 + 8u * v, c);
             balance<DT>(raw[k], rsv, c, x);
             uint32_t cd[8];
-            g.code(x, bk, steps, cd);
+            g.code(x, bk, steps, exact, cd);
             store_codes<BITS>(q.codes, gbase + 8u * v, cd);
         }
     }
@@ -430,7 +446,7 @@ __global__ __launch_bounds__(kT) void k_quant_wave(const QMat* __restrict__ mats
 // Wider groups (e.g. one group per row of 14336 columns): one workgroup per
 // group, raw values kept in registers between the min / max reduction
 // (waves, then one LDS exchange) and the coding pass.
-template <int DT, int BITS, bool CB>
+template <int DT, int BITS, bool CB, bool TIE>
 __global__ __launch_bounds__(kT) void k_quant_big(const QMat* __restrict__ mats,
                                                   const int64_t* __restrict__ ubeg,
                                                   int nmat, const CbTable* __restrict__ book,
@@ -447,6 +463,7 @@ __global__ __launch_bounds__(kT) void k_quant_big(const QMat* __restrict__ mats,
     const uint32_t ibase = row * (uint32_t)q.ld + col0;          // weights (row stride ld)
     const int nvg = q.group >> 3;
     const bool has_rs = q.rs != nullptr, has_ct = q.ct != nullptr;
+    const bool exact = TIE && ((!has_rs && !has_ct) || BITS == 8);  // near-half fallback (code8)
     const float rsv = has_rs ? gload<float>(q.rs + row) : 1.0f;
 
     Raw8<DT> raw[MAXV];
@@ -482,7 +499,7 @@ __global__ __launch_bounds__(kT) void k_quant_big(const QMat* __restrict__ mats,
             if (has_ct) load_ct(q.ct, col0 + 8u * v, c);
             balance<DT>(raw[k], rsv, c, x);
             uint32_t cd[8];
-            g.code(x, bk, steps, cd);
+            g.code(x, bk, steps, exact, cd);
             store_codes<BITS>(q.codes, gbase + 8u * v, cd);
         }
     }
@@ -675,41 +692,55 @@ hipError_t by_bits(int bits, F&& f) {
     return hipGetLastError();
 }
 
+// Calls f(std::bool_constant<tie>) (the code-book grid has no fallback).
+template <bool CB, class F>
+void by_tie(bool tie, F&& f) {
+    if constexpr (CB) f(std::false_type{});
+    else if (tie) f(std::true_type{});
+    else f(std::false_type{});
+}
+
 template <int DT, bool CB>
 hipError_t quant_tile_g(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                        int bits, const CbTable* book, int steps, hipStream_t s) {
+                        int bits, const CbTable* book, int steps, bool tie, hipStream_t s) {
     return by_bits<CB>(bits, [&](auto b) {
-        k_quant_tile<DT, decltype(b)::value, CB>
-            <<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, book, steps);
+        by_tie<CB>(tie, [&](auto t) {
+            k_quant_tile<DT, decltype(b)::value, CB, decltype(t)::value>
+                <<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, book, steps);
+        });
     });
 }
 
 template <int DT, int NVL, bool CB>
 hipError_t quant_wave_g(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                        int bits, const CbTable* book, int steps, hipStream_t s) {
+                        int bits, const CbTable* book, int steps, bool tie, hipStream_t s) {
     return by_bits<CB>(bits, [&](auto b) {
-        k_quant_wave<DT, decltype(b)::value, NVL, CB>
-            <<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, book, steps);
+        by_tie<CB>(tie, [&](auto t) {
+            k_quant_wave<DT, decltype(b)::value, NVL, CB, decltype(t)::value>
+                <<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, book, steps);
+        });
     });
 }
 
 template <int DT, bool CB>
 hipError_t quant_wave_nv(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                         int bits, int nvl, const CbTable* book, int steps, hipStream_t s) {
+                         int bits, int nvl, const CbTable* book, int steps, bool tie, hipStream_t s) {
     switch (nvl) {
-        case 1: return quant_wave_g<DT, 1, CB>(mats, ubeg, nmat, n_units, bits, book, steps, s);
-        case 2: return quant_wave_g<DT, 2, CB>(mats, ubeg, nmat, n_units, bits, book, steps, s);
-        case 4: return quant_wave_g<DT, 4, CB>(mats, ubeg, nmat, n_units, bits, book, steps, s);
-        default: return quant_wave_g<DT, 8, CB>(mats, ubeg, nmat, n_units, bits, book, steps, s);
+        case 1: return quant_wave_g<DT, 1, CB>(mats, ubeg, nmat, n_units, bits, book, steps, tie, s);
+        case 2: return quant_wave_g<DT, 2, CB>(mats, ubeg, nmat, n_units, bits, book, steps, tie, s);
+        case 4: return quant_wave_g<DT, 4, CB>(mats, ubeg, nmat, n_units, bits, book, steps, tie, s);
+        default: return quant_wave_g<DT, 8, CB>(mats, ubeg, nmat, n_units, bits, book, steps, tie, s);
     }
 }
 
 template <int DT, bool CB>
 hipError_t quant_big_g(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                       int bits, const CbTable* book, int steps, hipStream_t s) {
+                       int bits, const CbTable* book, int steps, bool tie, hipStream_t s) {
     return by_bits<CB>(bits, [&](auto b) {
-        k_quant_big<DT, decltype(b)::value, CB>
-            <<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, book, steps);
+        by_tie<CB>(tie, [&](auto t) {
+            k_quant_big<DT, decltype(b)::value, CB, decltype(t)::value>
+                <<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, book, steps);
+        });
     });
 }
 
@@ -733,40 +764,41 @@ hipError_t recip(const RecipSeg* segs, const int64_t* ubeg, int nseg, int64_t n_
 }
 
 hipError_t quant_tile(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                      int dtype, int bits, const CbTable* book, int steps, hipStream_t s) {
-    if (n_units <= 0) return hipSuccess;
-    if (book)
-        return dtype == WOQ_BF16
-                   ? quant_tile_g<WOQ_BF16, true>(mats, ubeg, nmat, n_units, bits, book, steps, s)
-                   : quant_tile_g<WOQ_F32, true>(mats, ubeg, nmat, n_units, bits, book, steps, s);
-    return dtype == WOQ_BF16
-               ? quant_tile_g<WOQ_BF16, false>(mats, ubeg, nmat, n_units, bits, nullptr, 0, s)
-               : quant_tile_g<WOQ_F32, false>(mats, ubeg, nmat, n_units, bits, nullptr, 0, s);
-}
-
-hipError_t quant_wave(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                      int dtype, int bits, int nvl, const CbTable* book, int steps,
+                      int dtype, int bits, const CbTable* book, int steps, bool tie,
                       hipStream_t s) {
     if (n_units <= 0) return hipSuccess;
     if (book)
         return dtype == WOQ_BF16
-                   ? quant_wave_nv<WOQ_BF16, true>(mats, ubeg, nmat, n_units, bits, nvl, book, steps, s)
-                   : quant_wave_nv<WOQ_F32, true>(mats, ubeg, nmat, n_units, bits, nvl, book, steps, s);
+                   ? quant_tile_g<WOQ_BF16, true>(mats, ubeg, nmat, n_units, bits, book, steps, false, s)
+                   : quant_tile_g<WOQ_F32, true>(mats, ubeg, nmat, n_units, bits, book, steps, false, s);
     return dtype == WOQ_BF16
-               ? quant_wave_nv<WOQ_BF16, false>(mats, ubeg, nmat, n_units, bits, nvl, nullptr, 0, s)
-               : quant_wave_nv<WOQ_F32, false>(mats, ubeg, nmat, n_units, bits, nvl, nullptr, 0, s);
+               ? quant_tile_g<WOQ_BF16, false>(mats, ubeg, nmat, n_units, bits, nullptr, 0, tie, s)
+               : quant_tile_g<WOQ_F32, false>(mats, ubeg, nmat, n_units, bits, nullptr, 0, tie, s);
 }
 
-hipError_t quant_big(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                     int dtype, int bits, const CbTable* book, int steps, hipStream_t s) {
+hipError_t quant_wave(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
+                      int dtype, int bits, int nvl, const CbTable* book, int steps, bool tie,
+                      hipStream_t s) {
     if (n_units <= 0) return hipSuccess;
     if (book)
         return dtype == WOQ_BF16
-                   ? quant_big_g<WOQ_BF16, true>(mats, ubeg, nmat, n_units, bits, book, steps, s)
-                   : quant_big_g<WOQ_F32, true>(mats, ubeg, nmat, n_units, bits, book, steps, s);
+                   ? quant_wave_nv<WOQ_BF16, true>(mats, ubeg, nmat, n_units, bits, nvl, book, steps, false, s)
+                   : quant_wave_nv<WOQ_F32, true>(mats, ubeg, nmat, n_units, bits, nvl, book, steps, false, s);
     return dtype == WOQ_BF16
-               ? quant_big_g<WOQ_BF16, false>(mats, ubeg, nmat, n_units, bits, nullptr, 0, s)
-               : quant_big_g<WOQ_F32, false>(mats, ubeg, nmat, n_units, bits, nullptr, 0, s);
+               ? quant_wave_nv<WOQ_BF16, false>(mats, ubeg, nmat, n_units, bits, nvl, nullptr, 0, tie, s)
+               : quant_wave_nv<WOQ_F32, false>(mats, ubeg, nmat, n_units, bits, nvl, nullptr, 0, tie, s);
+}
+
+hipError_t quant_big(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
+                     int dtype, int bits, const CbTable* book, int steps, bool tie, hipStream_t s) {
+    if (n_units <= 0) return hipSuccess;
+    if (book)
+        return dtype == WOQ_BF16
+                   ? quant_big_g<WOQ_BF16, true>(mats, ubeg, nmat, n_units, bits, book, steps, false, s)
+                   : quant_big_g<WOQ_F32, true>(mats, ubeg, nmat, n_units, bits, book, steps, false, s);
+    return dtype == WOQ_BF16
+               ? quant_big_g<WOQ_BF16, false>(mats, ubeg, nmat, n_units, bits, nullptr, 0, tie, s)
+               : quant_big_g<WOQ_F32, false>(mats, ubeg, nmat, n_units, bits, nullptr, 0, tie, s);
 }
 
 hipError_t dequant(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,

@@ -327,9 +327,10 @@ def codebook_rate(qp, mats, wl, stream, reps=5):
     return res
 
 
-def df11_rate(mats, specs, acts, stream, reps=3):
+def df11_rate(qp, mats, specs, acts, stream, reps=3):
     """Lossless code of the blocks the tiers keep in bf16: encode them (one
-    df11_compress over all of them, outside the timed region, after one
+    df11_compress over all of them from the exponent histograms the timed
+    pass's entropy call already counted, outside the timed region, after one
     untimed call; wall clock including the host-side code construction and
     its one synchronisation), then time decoding with one batched
     df11_decode per transformer block (HIP events).  Bytes = encoded
@@ -341,12 +342,14 @@ def df11_rate(mats, specs, acts, stream, reps=3):
     keep = sorted(b for b, a in enumerate(acts) if a == "keep")
     if not keep:
         return None
-    per = [[m for m, sp in zip(mats, specs) if sp.block == b] for b in keep]
+    per_idx = [[i for i, sp in enumerate(specs) if sp.block == b] for b in keep]
+    per = [[mats[i] for i in ix] for ix in per_idx]
     allm = [m for ms in per for m in ms]
-    woq.df11_compress(allm, stream=stream)       # untimed: the allocator's first growth
+    hist = qp.exp_hist[[i for ix in per_idx for i in ix]]
+    woq.df11_compress(allm, hist=hist, stream=stream)   # untimed: the allocator's first growth
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    flat = woq.df11_compress(allm, stream=stream)
+    flat = woq.df11_compress(allm, hist=hist, stream=stream)
     torch.cuda.synchronize()
     t_enc = time.perf_counter() - t0
     enc, i = [], 0
@@ -667,7 +670,7 @@ def main() -> int:
     acts = qp.action_of_block(tiers)
     comp = compulsory_bytes(mats, specs, acts, wl.bits, wl.group)
     deq = dequant_rate(qp, mats, wl, stream)
-    df11 = df11_rate(mats, specs, acts, stream)
+    df11 = df11_rate(qp, mats, specs, acts, stream)
     book = codebook_rate(qp, mats, wl, stream)
 
     out = {

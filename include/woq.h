@@ -150,6 +150,25 @@ int32_t ewq_block_entropy(const woq_mat* mats, int32_t n_mats,
                           void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * ewq_block_entropy_ex -- ewq_block_entropy that also writes each BF16
+ *  matrix's exponent histogram, taken from the entropy histogram with no
+ *  further read of the weights: the counts the lossless exponent code of the
+ *  blocks the tiers keep is built from ([DF11], "Du dia nen con lai trong
+ *  exponent cua BFloat16": the exponent carries far fewer than 8 bits of
+ *  information), so df11_build_code needs no df11_exponent_histogram pass.
+ *  exp_hist  device uint32[n_mats * 256] (16-B aligned, may be NULL):
+ *            exp_hist[i * 256 + e] = number of weights of matrix i whose
+ *            exponent field is e (as df11_exponent_histogram); zeros for F32
+ *            matrices.
+ *  Other arguments, results and errors as for ewq_block_entropy.
+ */
+int32_t ewq_block_entropy_ex(const woq_mat* mats, int32_t n_mats,
+                             const int32_t* block_id, int32_t n_blocks, double x,
+                             double* h_mat, double* h_block, double* stats,
+                             int32_t* tier, int32_t* order, uint32_t* exp_hist,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * ewq_block_entropy_static -- ewq_block_entropy for callers that cannot
  *  allocate device memory (code under HIP graph capture, tight serving
  *  loops, harnesses that forbid hipMalloc): no workspace argument, and no

@@ -150,3 +150,30 @@ def test_full_llama8b_block_round_trip():
     nbytes = sum(e["enc"].numel() + e["sm"].numel() + e["gaps"].numel() + 4 * e["block_pos"].numel()
                  + e["tables"].numel() + 256 for e in enc)
     assert 10.3 < 8 * nbytes / n < 11.3
+
+
+def test_exponent_histograms_from_the_entropy_pass():
+    """ewq_block_entropy_ex: each bf16 matrix's exponent histogram, summed
+    from the entropy histogram, equals df11_exponent_histogram's and the
+    oracle's (strided views included, more matrices than one histogram batch
+    on the path with few, fp32 matrices all zero); the entropies are those of
+    ewq_block_entropy."""
+    import woqdata
+    mats = [woqdata.random_matrix(64 + 8 * i, 512, 700 + i, std=0.005 * (1 + i % 4)).to(DEV)
+            for i in range(6)]
+    big = woqdata.random_matrix(256, 3 * 1024, 710).to(DEV)
+    mats += [big[:, 1024:2048], woqdata.random_matrix(33, 64, 711, dtype=torch.float32).to(DEV)]
+    mats[0][3, :5] = torch.tensor([0.0, -0.0, 1e-30, 3e5, -7e4], device=DEV).to(torch.bfloat16)
+    out = woq.ewq_block_entropy(mats, exp_hist=True)
+    ref = woq.ewq_block_entropy(mats)
+    assert torch.equal(out["h_mat"], ref["h_mat"])
+    eh = out["exp_hist"].cpu().numpy()
+    bf = [m for m in mats if m.dtype == torch.bfloat16]
+    dh = woq.df11_exponent_histogram([m.contiguous() for m in bf]).cpu().numpy()
+    for i, m in enumerate(mats):
+        if m.dtype == torch.float32:
+            assert not eh[i].any()
+            continue
+        bits = m.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
+        assert np.array_equal(eh[i], df11.exponent_histogram(bits)), i
+        assert np.array_equal(eh[i], dh[i]), i

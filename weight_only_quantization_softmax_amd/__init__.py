@@ -178,14 +178,22 @@ def _workspace(op, mats, group, ws, device):
 
 
 def ewq_block_entropy(mats: Sequence[torch.Tensor], block_id: Optional[Sequence[int]] = None,
-                      n_blocks: int = 1, x: float = 1.0, *, ws=None, stream=None):
-    """Per-matrix entropy, block entropy, (mu, sigma, T), tiers and order (device tensors)."""
+                      n_blocks: int = 1, x: float = 1.0, *, exp_hist=None, ws=None, stream=None):
+    """Per-matrix entropy, block entropy, (mu, sigma, T), tiers and order (device
+    tensors), and the count of NaN / inf weights (``nonfinite``, a view of the
+    workspace head).  ``exp_hist``: True, or an int32 device tensor of
+    n_mats * 256 elements, to also get each bf16 matrix's exponent histogram
+    from the same pass (ewq_block_entropy_ex); returned as ``exp_hist``
+    [n_mats, 256]."""
     lib = _lib.load()
     _check_mats(mats)
     n = len(mats)
     if block_id is not None and len(block_id) != n:
         raise ValueError(f"block_id: {len(block_id)} ids for {n} matrices")
-    dev = _device(mats, ws)
+    eh = exp_hist if isinstance(exp_hist, torch.Tensor) else None
+    if eh is not None:
+        _check_bufs("exp_hist", [eh], [256 * n], torch.int32)
+    dev = _device(mats, ws, eh)
     arr = _mats(mats)
     with _on(stream, dev):
         h_mat = torch.empty(n, dtype=torch.float64, device=dev)
@@ -193,16 +201,27 @@ def ewq_block_entropy(mats: Sequence[torch.Tensor], block_id: Optional[Sequence[
         stats = torch.empty(3, dtype=torch.float64, device=dev)
         tier = torch.empty(n_blocks, dtype=torch.int32, device=dev)
         order = torch.empty(n_blocks, dtype=torch.int32, device=dev)
+        if exp_hist is True:
+            eh = torch.empty(n, 256, dtype=torch.int32, device=dev)
         ws = _workspace(_lib.OP_ENTROPY, mats, 0, ws, dev)
     bid = None
     if block_id is not None:
         bid = (ctypes.c_int32 * n)(*[int(b) for b in block_id])
-    st = lib.ewq_block_entropy(arr, n, bid, n_blocks, float(x), h_mat.data_ptr(),
-                               h_block.data_ptr(), stats.data_ptr(), tier.data_ptr(),
-                               order.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream, dev))
-    _lib.check("ewq_block_entropy", st)
-    return {"h_mat": h_mat, "h_block": h_block, "stats": stats, "tier": tier, "order": order,
-            "nonfinite": nonfinite_count(ws)}
+    ptrs = (h_mat.data_ptr(), h_block.data_ptr(), stats.data_ptr(), tier.data_ptr(),
+            order.data_ptr())
+    if eh is None:
+        st = lib.ewq_block_entropy(arr, n, bid, n_blocks, float(x), *ptrs, ws.data_ptr(),
+                                   ws.numel(), _stream(stream, dev))
+        _lib.check("ewq_block_entropy", st)
+    else:
+        st = lib.ewq_block_entropy_ex(arr, n, bid, n_blocks, float(x), *ptrs, eh.data_ptr(),
+                                      ws.data_ptr(), ws.numel(), _stream(stream, dev))
+        _lib.check("ewq_block_entropy_ex", st)
+    out = {"h_mat": h_mat, "h_block": h_block, "stats": stats, "tier": tier, "order": order,
+           "nonfinite": nonfinite_count(ws)}
+    if eh is not None:
+        out["exp_hist"] = eh.view(n, 256)
+    return out
 
 
 def sinq_balance(mats: Sequence[torch.Tensor], iters: int, *, rms: bool = False,
@@ -516,9 +535,16 @@ def df11_encode(mats: Sequence[torch.Tensor], codes, *, ws=None, stream=None):
     return outs
 
 
-def df11_compress(mats: Sequence[torch.Tensor], *, stream=None):
-    """Histogram (device), codes (host; one synchronisation), encode (device)."""
-    hist = df11_exponent_histogram(mats, stream=stream).cpu().numpy()
+def df11_compress(mats: Sequence[torch.Tensor], *, hist=None, stream=None):
+    """Histogram (device; skipped when ``hist`` [n_mats, 256] is given, for
+    example the exponent histograms of the entropy pass), codes (host; one
+    synchronisation), encode (device)."""
+    if hist is None:
+        hist = df11_exponent_histogram(mats, stream=stream)
+    if isinstance(hist, torch.Tensor):
+        hist = hist.cpu().numpy()
+    if len(hist) != len(mats):
+        raise ValueError(f"hist: {len(hist)} histograms for {len(mats)} matrices")
     codes = [df11_build_code(h) for h in hist]
     return df11_encode(mats, codes, stream=stream)
 

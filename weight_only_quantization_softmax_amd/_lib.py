@@ -29,7 +29,8 @@ EXPORTS = ("woq_status_string", "woq_workspace_size", "ewq_block_entropy",
            "sinq_balance", "sinq_balance_ex", "quant_pack_groupwise", "dequant_unpack", "ternary_pack",
            "ewq_budget_levels", "df11_buffer_sizes", "df11_exponent_histogram",
            "df11_build_code", "df11_encode", "df11_decode", "quant_pack_codebook",
-           "dequant_codebook", "woq_codebook_normal", "ewq_block_entropy_static")
+           "dequant_codebook", "woq_codebook_normal", "ewq_block_entropy_static",
+           "ewq_block_entropy_ex")
 
 
 WS_HEAD = 256   # WOQ_WS_HEAD: the workspace's status head (non-finite count at byte 0)
@@ -71,6 +72,9 @@ def load() -> ctypes.CDLL:
     lib.ewq_block_entropy.argtypes = [ctypes.POINTER(WoqMat), I32, ctypes.POINTER(I32), I32,
                                       ctypes.c_double, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.ewq_block_entropy.restype = I32
+    lib.ewq_block_entropy_ex.argtypes = [ctypes.POINTER(WoqMat), I32, ctypes.POINTER(I32), I32,
+                                         ctypes.c_double, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.ewq_block_entropy_ex.restype = I32
     lib.ewq_block_entropy_static.argtypes = [ctypes.POINTER(WoqMat), I32, ctypes.POINTER(I32), I32,
                                              ctypes.c_double, P, P, P, P, P, P]
     lib.ewq_block_entropy_static.restype = I32

@@ -20,6 +20,10 @@
 // fp32 path: two passes (max, then fp64 sums of exp(w - c) per work unit),
 // partials combined in a fixed order.
 //
+// The histogram also gives each bf16 matrix's exponent histogram (the counts
+// of its 256 exponent fields) for the lossless exponent code of the kept
+// blocks, summed per part when the caller asks for it.
+//
 // A work unit is kEntChunk consecutive elements of a contiguous matrix, or
 // rpu whole rows of a strided one (row stride ld > cols).  Non-finite
 // weights (NaN, +-inf) make the entropy NaN and are counted into the
@@ -136,16 +140,33 @@ __device__ __forceinline__ float block_maxf(float v, float* sh) {
 constexpr int kHistParts = kHistBinParts;
 constexpr int kPartBins = 65536 / kHistParts;
 
-__global__ __launch_bounds__(kT) void k_hist_part(const uint32_t* __restrict__ ghist,
-                                                  double4* __restrict__ part) {
+__global__ __launch_bounds__(kT) void k_hist_part(const EntMat* __restrict__ mats,
+                                                  const uint32_t* __restrict__ ghist,
+                                                  double4* __restrict__ part,
+                                                  uint32_t* __restrict__ exp_hist) {
     __shared__ double shd[kT / 64];
     __shared__ float shf[kT / 64];
+    __shared__ uint32_t lexp[32];
     const int m = blockIdx.x / kHistParts, w = blockIdx.x % kHistParts;
     const uint32_t* gh = ghist + (size_t)m * 65536 + (size_t)w * kPartBins;
     constexpr int PER = kPartBins / kT;
     uint32_t cnt[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) cnt[i] = gload<uint32_t>(gh + threadIdx.x + kT * i);
+    if (exp_hist) {
+        // the part holds one sign and 32 exponent fields (128 mantissas
+        // each): bin threadIdx.x + kT i has exponent 32 (w % 8) + 2 i +
+        // threadIdx.x / 128
+        if (threadIdx.x < 32) lexp[threadIdx.x] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            if (cnt[i]) atomicAdd(&lexp[2 * i + (threadIdx.x >> 7)], cnt[i]);
+        __syncthreads();
+        if (threadIdx.x < 32 && lexp[threadIdx.x])
+            atomicAdd(exp_hist + (size_t)mats[m].slot * 256 + 32 * (w % 8) + threadIdx.x,
+                      lexp[threadIdx.x]);
+    }
     float mx = -INFINITY;
     double bad = 0.0;  // weights whose bin has an all-ones exponent (NaN, inf)
 #pragma unroll
@@ -364,9 +385,10 @@ hipError_t ent_hist_bf16(const EntMat* mats, const int64_t* ubeg, int nmat, int6
 }
 
 hipError_t ent_hist_final(const EntMat* mats, int nmat, const uint32_t* ghist, double4* part,
-                          double* h_mat, unsigned long long* nonfinite, hipStream_t s) {
+                          double* h_mat, unsigned long long* nonfinite, uint32_t* exp_hist,
+                          hipStream_t s) {
     if (nmat <= 0) return hipSuccess;
-    k_hist_part<<<dim3(nmat * kHistParts), dim3(kT), 0, s>>>(ghist, part);
+    k_hist_part<<<dim3(nmat * kHistParts), dim3(kT), 0, s>>>(mats, ghist, part, exp_hist);
     k_hist_comb<<<dim3((nmat + kT - 1) / kT), dim3(kT), 0, s>>>(mats, nmat, part, h_mat, nonfinite);
     return hipGetLastError();
 }

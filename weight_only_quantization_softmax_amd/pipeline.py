@@ -132,6 +132,9 @@ class QuantPass:
         self.stats = torch.empty(3, dtype=torch.float64, device=dev)
         self.tier = torch.empty(n_blocks, dtype=torch.int32, device=dev)
         self.order = torch.empty(n_blocks, dtype=torch.int32, device=dev)
+        # each bf16 matrix's exponent histogram, from the entropy pass (the
+        # input of the lossless code of the kept blocks)
+        self.exp_hist = torch.empty(n, 256, dtype=torch.int32, device=dev)
         self._ent_ws = _ws(_lib.OP_ENTROPY, self.mats, 0, dev)
         self._ent_mats = _mat_arr(self.mats)
         self._bid = (ctypes.c_int32 * n)(*self.block_id)
@@ -147,9 +150,9 @@ class QuantPass:
     def _entropy_call(self) -> _Call:
         args = (self._ent_mats, len(self.mats), self._bid, self.n_blocks, float(self.x),
                 self.h_mat.data_ptr(), self.h_block.data_ptr(), self.stats.data_ptr(),
-                self.tier.data_ptr(), self.order.data_ptr(), self._ent_ws.data_ptr(),
-                self._ent_ws.numel())
-        return _Call("ewq_block_entropy", self.lib.ewq_block_entropy, args, None, "entropy",
+                self.tier.data_ptr(), self.order.data_ptr(), self.exp_hist.data_ptr(),
+                self._ent_ws.data_ptr(), self._ent_ws.numel())
+        return _Call("ewq_block_entropy_ex", self.lib.ewq_block_entropy_ex, args, None, "entropy",
                      self.bytes_in)
 
     def _sinq_calls(self, idx: List[int]) -> List[_Call]:
@@ -348,9 +351,11 @@ class QuantPass:
 
     def compress_kept(self, stream: Optional[torch.cuda.Stream] = None) -> int:
         """Lossless exponent code for the matrices the last run kept in bf16:
-        one df11_compress over all of them (each matrix gets its own code,
-        which comes from the data, so this step synchronises once).  Sets
-        outputs[i]["df11"]; returns the stored bytes of the kept matrices."""
+        one df11_compress over all of them, from the exponent histograms the
+        entropy pass already counted (no second read of the kept weights
+        before encoding; each matrix gets its own code, which comes from the
+        data, so this step synchronises once).  Sets outputs[i]["df11"];
+        returns the stored bytes of the kept matrices."""
         from . import df11_compress
         if self.last_actions is None:
             raise RuntimeError("run() first")
@@ -358,7 +363,8 @@ class QuantPass:
         if not idx:
             return 0
         stored = 0
-        for i, e in zip(idx, df11_compress([self.mats[i] for i in idx], stream=stream)):
+        hist = self.exp_hist[idx]
+        for i, e in zip(idx, df11_compress([self.mats[i] for i in idx], hist=hist, stream=stream)):
             self.outputs[i]["df11"] = e
             stored += (e["enc"].numel() + e["sm"].numel() + e["gaps"].numel()
                        + 4 * e["block_pos"].numel() + e["tables"].numel() + 256)

@@ -20,9 +20,10 @@
 //   probe_barrier(counters, err, n_bar, grid, team, spin_limit, stream)
 //       `n_bar` barriers among the workgroups of one cooperative launch of
 //       `grid` workgroups of 256 threads: teams of `team` workgroups
-//       (team = grid: a grid-wide barrier; workgroups g, g + grid/team, ...
-//       form one team, so a team of grid/8 ... shares an XCD when the
-//       workgroups are dealt to the 8 XCDs in turn).  Each arrival is an
+//       (team = grid: a grid-wide barrier).  Teams are strided: workgroup b
+//       is in team b mod (grid / team), so when grid / team is a multiple of
+//       8 and workgroups are dealt to the 8 XCDs in turn, each team sits on
+//       one XCD.  Each arrival is an
 //       agent-scope atomic add on the team's counter; each wait polls it
 //       with agent-scope loads and gives up after spin_limit polls, setting
 //       *err and returning (so a launch that cannot meet never hangs).

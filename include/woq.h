@@ -41,7 +41,11 @@
  *    calls are thread-safe when they use distinct workspaces.
  *  - Work is enqueued on `stream` (0 = null stream) and the call returns;
  *    outputs are valid once the stream has synchronised.  Calls that share a
- *    workspace must be ordered on one stream.
+ *    workspace must be ordered on one stream.  Every GPU call can be
+ *    captured into a HIP graph (stream capture): while the stream is
+ *    capturing, the descriptor tables reach the workspace through kernel
+ *    arguments instead of a host copy, and only kernels are enqueued (no
+ *    memset nodes); a replay repeats the captured call on the same buffers.
  *  - `ws`/`ws_bytes` is a caller-provided device workspace of at least
  *    woq_workspace_size() bytes (256-byte aligned).  Its first WOQ_WS_HEAD
  *    bytes are a status head: ewq_block_entropy and sinq_balance[_ex] write

@@ -74,9 +74,18 @@ int32_t check_mats(const woq_mat* mats, int32_t n, bool cols8) {
 }
 
 // Copies the host-built descriptor tables [WOQ_WS_HEAD, end) into the
-// workspace; the status head itself is not written.
+// workspace; the status head itself is not written.  On a stream that is
+// being captured into a graph the bytes travel in kernel arguments (a
+// captured copy from this pageable, short-lived buffer would be replayed
+// after the buffer is gone); otherwise one asynchronous copy.
 hipError_t stage_tables(void* ws, const std::vector<char>& host, size_t end, hipStream_t s) {
     if (end <= WOQ_WS_HEAD) return hipSuccess;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const hipError_t e = hipStreamIsCapturing(s, &cs);
+    if (e != hipSuccess) return e;
+    if (cs != hipStreamCaptureStatusNone)
+        return stage_bytes(static_cast<char*>(ws) + WOQ_WS_HEAD, host.data() + WOQ_WS_HEAD,
+                           end - WOQ_WS_HEAD, s);
     return hipMemcpyAsync(static_cast<char*>(ws) + WOQ_WS_HEAD, host.data() + WOQ_WS_HEAD,
                           end - WOQ_WS_HEAD, hipMemcpyHostToDevice, s);
 }

@@ -356,6 +356,16 @@ __global__ __launch_bounds__(kT) void k_blocks(const int32_t* __restrict__ bmats
     }
 }
 
+// Copies one chunk of bytes carried in the kernel's arguments (the staging
+// path for calls captured into a graph: a captured kernel keeps its
+// arguments by value, a copy from pageable host memory would not).
+struct StageChunk {
+    uint32_t w[kStageChunk / 4];
+};
+__global__ __launch_bounds__(256) void k_stage(uint32_t* dst, uint32_t nw, StageChunk c) {
+    for (uint32_t i = threadIdx.x; i < nw; i += 256) dst[i] = c.w[i];
+}
+
 __global__ void k_fill_u32(uint32_t* p, size_t n, uint32_t v) {
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
          i += (size_t)gridDim.x * blockDim.x)
@@ -369,6 +379,20 @@ hipError_t fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s) {
     const size_t blocks = min((n + 255) / 256, (size_t)4096);
     k_fill_u32<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p, n, v);
     return hipGetLastError();
+}
+
+hipError_t stage_bytes(void* dst, const void* src, size_t n, hipStream_t s) {
+    for (size_t off = 0; off < n; off += kStageChunk) {
+        StageChunk c;
+        const size_t m = n - off < (size_t)kStageChunk ? n - off : (size_t)kStageChunk;
+        memset(&c, 0, sizeof(c));
+        memcpy(c.w, static_cast<const char*>(src) + off, m);
+        k_stage<<<dim3(1), dim3(256), 0, s>>>(
+            reinterpret_cast<uint32_t*>(static_cast<char*>(dst) + off), (uint32_t)(m / 4), c);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t fill_f32(float* p, size_t n, float v, hipStream_t s) {

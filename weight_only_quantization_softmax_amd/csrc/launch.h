@@ -11,6 +11,10 @@ constexpr int64_t kEntChunk = int64_t(1) << 19;   // elements per work unit
 constexpr int kHistSlots = 256;                    // bf16 matrices per batch
 
 hipError_t fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
+// Host bytes to device memory through kernel arguments, kStageChunk bytes
+// per launch (n a multiple of 4): safe to capture into a graph.
+constexpr int kStageChunk = 1024;
+hipError_t stage_bytes(void* dst, const void* src, size_t n, hipStream_t s);
 hipError_t fill_f32(float* p, size_t n, float v, hipStream_t s);
 
 hipError_t ent_hist_bf16(const EntMat* mats, const int64_t* ubeg, int nmat,

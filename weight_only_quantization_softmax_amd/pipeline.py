@@ -292,6 +292,8 @@ class QuantPass:
         return out
 
     def action_of_block(self, tiers) -> List[str]:
+        """The action of every block: the first action for an untiered pass
+        (``tiers`` unused), else the action of each block's tier."""
         if not self.tiered:
             return [self.actions[0]] * self.n_blocks
         return [self.actions[int(t) - 1] for t in tiers]
@@ -333,21 +335,49 @@ class QuantPass:
         return calls
 
     # ------------------------------------------------------------ running
-    def run(self, stream: Optional[torch.cuda.Stream] = None, timers: Optional[dict] = None):
+    def run(self, stream: Optional[torch.cuda.Stream] = None, timers: Optional[dict] = None,
+            read_tiers: bool = True):
         """One whole pass; returns the tiers (host list).  ``timers`` collects
-        (kind -> list of (start_event, end_event, bytes)) around each call."""
+        (kind -> list of (start_event, end_event, bytes)) around each call.
+        When the tiers decide nothing (an untiered pass without a budget) the
+        pass enqueues everything without waiting for the GPU; with
+        ``read_tiers=False`` it then returns None and never synchronises (as
+        needed to capture it into a graph)."""
         stream = stream or torch.cuda.current_stream(self.device)
         h = stream.cuda_stream
         calls = [self._entropy_call()]
         self._run_calls(calls, stream, h, timers)
-        tiers = self.tier.cpu().tolist()   # the one host synchronisation
-        if self.budget_bytes is None:
-            acts = self.action_of_block(tiers)
+        fixed = not self.tiered and self.budget_bytes is None
+        tiers = None
+        if fixed:
+            acts = self.action_of_block(None)
         else:
-            acts = self.budgeted_actions(tiers, self.h_block.cpu().tolist())
+            tiers = self.tier.cpu().tolist()   # the one host synchronisation
+            if self.budget_bytes is None:
+                acts = self.action_of_block(tiers)
+            else:
+                acts = self.budgeted_actions(tiers, self.h_block.cpu().tolist())
         self.last_actions = acts
         self._run_calls(self.plan_actions(acts), stream, h, timers)
+        if tiers is None and read_tiers:
+            tiers = self.tier.cpu().tolist()
         return tiers
+
+    def graph(self, stream: Optional[torch.cuda.Stream] = None) -> "torch.cuda.CUDAGraph":
+        """The whole pass captured into a HIP graph (untiered passes without a
+        budget only: a tiered pass reads the tiers back on the host).  One
+        eager pass first prepares every buffer; the graph's replay then runs
+        the same kernels on the same buffers, with no host work per kernel."""
+        if self.tiered or self.budget_bytes is not None:
+            raise ValueError("only an untiered pass without a budget can be captured")
+        stream = stream or torch.cuda.current_stream(self.device)
+        self.run(stream=stream)
+        torch.cuda.synchronize(self.device)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=torch.cuda.Stream(device=self.device)):
+            self.run(read_tiers=False)
+        torch.cuda.synchronize(self.device)
+        return g
 
     def compress_kept(self, stream: Optional[torch.cuda.Stream] = None) -> int:
         """Lossless exponent code for the matrices the last run kept in bf16:

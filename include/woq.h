@@ -144,8 +144,11 @@ int32_t woq_workspace_size(int32_t op, const woq_mat* mats, int32_t n_mats,
  *  tier      device int32[n_blocks]           (may be NULL)
  *  order     device int32[n_blocks]           (may be NULL)
  *  1 <= n_blocks <= 4096.  Results are deterministic (bf16 inputs are
- *  counted exactly in a histogram of their 65,536 bit patterns; all sums are
- *  fp64 in a fixed order).
+ *  counted exactly by bit pattern; all sums are fp64 in a fixed order).
+ *  Speed: a BF16 matrix with many values that are neither zero, NaN / inf
+ *  nor of magnitude in [2^-25, 64) (more than 8,192, or more than 240 in
+ *  the part one workgroup reads) is recounted with sixteen further reads of
+ *  its weights; the results are the same.
  */
 int32_t ewq_block_entropy(const woq_mat* mats, int32_t n_mats,
                           const int32_t* block_id, int32_t n_blocks, double x,
@@ -155,8 +158,8 @@ int32_t ewq_block_entropy(const woq_mat* mats, int32_t n_mats,
 
 /*
  * ewq_block_entropy_ex -- ewq_block_entropy that also writes each BF16
- *  matrix's exponent histogram, taken from the entropy histogram with no
- *  further read of the weights: the counts the lossless exponent code of the
+ *  matrix's exponent histogram, taken from the entropy pass's counts with
+ *  no further read of the weights: the counts the lossless exponent code of the
  *  blocks the tiers keep is built from ([DF11], "Du dia nen con lai trong
  *  exponent cua BFloat16": the exponent carries far fewer than 8 bits of
  *  information), so df11_build_code needs no df11_exponent_histogram pass.
@@ -180,10 +183,10 @@ int32_t ewq_block_entropy_ex(const woq_mat* mats, int32_t n_mats,
  *  32 MiB array in the library's device memory, one per GPU the library
  *  runs on (on the device current at the call; `stream` must belong to it),
  *  held until the process ends and located on the first call on each device.
- *  Histograms pass through it in batches of as many matrices as fit, so any
- *  number of matrices works; WOQ_ERR_SCRATCH (before any HIP call) when the
- *  descriptor tables, fp32 partials and one histogram do not fit (about
- *  400,000 matrices).  Arguments, results and other errors as for
+ *  BF16 matrices pass through it in batches of as many as fit (about 48 KB
+ *  of counts each), so any number of matrices works; WOQ_ERR_SCRATCH
+ *  (before any HIP call) when the descriptor tables, fp32 partials and the
+ *  counts of one matrix do not fit (about 400,000 matrices).  Arguments, results and other errors as for
  *  ewq_block_entropy; the non-finite count is not reported.  Every call on
  *  a GPU uses that GPU's one array: calls that overlap on one GPU (two host
  *  threads, or two streams without ordering between them) race; calls

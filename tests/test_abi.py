@@ -59,7 +59,7 @@ def _ws_size(op, mats, n=1, group=0):
 
 def test_workspace_size_and_validation():
     st, b = _ws_size(_lib.OP_ENTROPY, _mat())
-    assert st == 0 and b >= 65536 * 4
+    assert st == 0 and b >= 8128 * 4 + 8192 * 2     # a bf16 record and list
     st, b = _ws_size(_lib.OP_SINQ, _mat())
     assert st == 0 and b > 0
     assert _ws_size(_lib.OP_QUANT, _mat(), group=64)[0] == 0

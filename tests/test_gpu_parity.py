@@ -331,8 +331,13 @@ def test_dequant_matches_oracle(bits, group, rows, cols):
 
 
 # ------------------------------------------------------------------ ternary
+# rows of up to 4096 columns take one wave per row (8-column vectors per
+# lane: 1, 2, 4, 8), wider rows one workgroup per row; row counts off the
+# 16-row unit
 @pytest.mark.parametrize("shape,dtype", [((64, 2048), torch.bfloat16), ((33, 1408), torch.bfloat16),
-                                         ((7, 4096), torch.float32), ((3, 16), torch.bfloat16)])
+                                         ((7, 4096), torch.float32), ((3, 16), torch.bfloat16),
+                                         ((17, 512), torch.bfloat16), ((100, 1024), torch.float32),
+                                         ((5, 4104), torch.bfloat16), ((40, 6144), torch.float32)])
 def test_ternary_matches_oracle(shape, dtype):
     m = _rm(*shape, 71, dtype)
     m[0] = 0  # beta = 0 row
@@ -346,6 +351,21 @@ def test_ternary_matches_oracle(shape, dtype):
     assert n <= max(1, 1e-5 * tot)
     deq = woq.dequant_unpack([shape], codes, [beta[0]], 2, 0)[0]
     assert np.array_equal(deq.cpu().numpy(), oracle.ternary_dequantize(q_ref, b_ref))
+
+
+def test_ternary_batch_of_launch_sets_equals_single_calls():
+    """One call over matrices of every launch set (both dtypes, wave and
+    workgroup forms, interleaved) gives each matrix what a call on it alone
+    gives."""
+    shapes = [(33, 1408, torch.bfloat16), (9, 8192, torch.bfloat16), (48, 512, torch.float32),
+              (16, 2048, torch.bfloat16), (2, 4104, torch.float32), (70, 1024, torch.bfloat16),
+              (1, 8, torch.float32)]
+    mats = [_rm(r, c, 80 + i, dt) for i, (r, c, dt) in enumerate(shapes)]
+    codes, beta = woq.ternary_pack(mats)
+    for i, m in enumerate(mats):
+        c1, b1 = woq.ternary_pack([m])
+        assert torch.equal(codes[i], c1[0]), shapes[i]
+        assert torch.equal(beta[i].view(torch.int32), b1[0].view(torch.int32)), shapes[i]
 
 
 # ------------------------------------------------------------------ end to end (single fp32 workload)

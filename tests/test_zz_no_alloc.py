@@ -46,10 +46,10 @@ def _compare(mats, block_id, n_blocks):
 
 
 def test_static_entropy_matches_the_workspace_call_twice():
-    # 300 bf16 matrices (more than the 120-odd histograms one batch of the
+    # 900 bf16 matrices (more than the 680-odd whose counts one batch of the
     # 32 MiB array holds), fp32 matrices, and column blocks of a fused tensor
     mats, bid = [], []
-    for i in range(300):
+    for i in range(900):
         mats.append(woqdata.random_matrix(64 + (i % 7) * 16, 256 + 64 * (i % 5), 1000 + i,
                                           std=0.01 + 0.0001 * i).to(DEV))
         bid.append(i % 37)

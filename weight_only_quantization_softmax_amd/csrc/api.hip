@@ -126,11 +126,12 @@ struct EntLayout {
     int slots = 0;          // bf16 histograms per batch
     int64_t units_b = 0, units_f = 0;
     size_t tab_b, ubeg_b, tab_f, ubeg_f, bmats, bbeg, nsz, table_end;
-    size_t hb, keys, part_f, ghist, hpart, total;
+    size_t hb, keys, part_f, recs, lists, total;
 };
 
-// Rows per entropy work unit of a strided matrix (0 for a contiguous one),
-// and the matrix's number of work units.
+// fp32: rows per entropy work unit of a strided matrix (0 for a contiguous
+// one), and the matrix's number of work units.  bf16: the matrix's number
+// of 16-byte vectors (the counting pass shares them out evenly).
 int32_t ent_rpu(const woq_mat& m) {
     return eff_ld(m) == m.cols ? 0 : (int32_t)std::max<int64_t>(1, kEntChunk / m.cols);
 }
@@ -138,12 +139,21 @@ int64_t ent_units(const woq_mat& m) {
     const int32_t rpu = ent_rpu(m);
     return rpu ? cdiv(m.rows, rpu) : cdiv(elems(m), kEntChunk);
 }
+// Elements per work unit of a contiguous matrix: the matrix split evenly
+// (rounded up to a multiple of 8, so every unit starts 16-byte aligned).
+int64_t ent_chunk(const woq_mat& m) {
+    return ent_rpu(m) ? 0 : cdiv(cdiv(elems(m), ent_units(m)), 8) * 8;
+}
+int64_t ent_vectors(const woq_mat& m) {
+    return eff_ld(m) == m.cols ? cdiv(elems(m), 8) : m.rows * (m.cols / 8);
+}
 
-// max_slots: at most this many bf16 histograms (256 KiB each) per batch.
+// max_slots: at most this many bf16 matrices (a record and a list each,
+// about 48 KiB) per batch.
 EntLayout ent_layout(const woq_mat* mats, int32_t n, int32_t n_blocks, int max_slots = kHistSlots) {
     EntLayout L;
     for (int32_t i = 0; i < n; ++i) {
-        if (mats[i].dtype == WOQ_BF16) { ++L.nb; L.units_b += ent_units(mats[i]); }
+        if (mats[i].dtype == WOQ_BF16) { ++L.nb; L.units_b += ent_vectors(mats[i]); }
         else { ++L.nf; L.units_f += ent_units(mats[i]); }
     }
     Arena a;
@@ -159,8 +169,8 @@ EntLayout ent_layout(const woq_mat* mats, int32_t n, int32_t n_blocks, int max_s
     L.keys = a.take(sizeof(uint32_t) * 2 * L.nf);
     L.part_f = a.take(sizeof(double2) * L.units_f);
     L.slots = std::min(L.nb, max_slots);
-    L.ghist = a.take(sizeof(uint32_t) * 65536 * (size_t)L.slots);
-    L.hpart = a.take(sizeof(double4) * kHistBinParts * (size_t)L.slots, 64);
+    L.recs = a.take(sizeof(uint32_t) * kEntRecWords * (size_t)L.slots);
+    L.lists = a.take(sizeof(uint16_t) * kEntListCap * (size_t)L.slots);
     L.total = a.end();
     return L;
 }
@@ -351,23 +361,38 @@ int64_t q_units(const woq_mat& m, int32_t group) {
     return ng;
 }
 
-// op: 0 quant, 1 dequant, 2 ternary.  For quant every matrix goes to the
-// "b" table, ordered by launch set, and ubeg_b holds one offset run per set.
+// Ternary launch set: kind 1 = one wave per row (rows of at most
+// kTernWaveMax columns, nvl 8-column vectors per lane), kind 2 = one
+// workgroup per row.
+QKey t_key(const woq_mat& m) {
+    if (m.cols > kTernWaveMax) return QKey{m.dtype, 2, 0};
+    int nvl = 1;
+    while (nvl * 64 * 8 < m.cols) nvl *= 2;
+    return QKey{m.dtype, 1, nvl};
+}
+
+int64_t t_units(const woq_mat& m) {
+    return t_key(m).kind == 1 ? cdiv(m.rows, kTernRows) : m.rows;
+}
+
+// op: 0 quant, 1 dequant, 2 ternary.  For quant and ternary every matrix
+// goes to the "b" table, ordered by launch set, and ubeg_b holds one offset
+// run per set.
 QLayout q_layout(const woq_mat* mats, int32_t n, int op, int32_t group,
                  const float* const* row_scale, const float* const* col_scale) {
     QLayout L;
     auto units = [&](const woq_mat& m) -> int64_t {
-        if (op == 2) return m.rows;
+        if (op == 2) return t_units(m);
         if (op == 0) return q_units(m, group);
         return cdiv(m.rows, kDTileRows) * cdiv(m.cols, kQTileCols);
     };
     for (int32_t i = 0; i < n; ++i) {
-        if (op == 0 || mats[i].dtype == WOQ_BF16) { ++L.nb; L.units_b += units(mats[i]); }
+        if (op != 1 || mats[i].dtype == WOQ_BF16) { ++L.nb; L.units_b += units(mats[i]); }
         else { ++L.nf; L.units_f += units(mats[i]); }
     }
-    if (op == 0) {
+    if (op != 1) {
         std::vector<QKey> keys;
-        for (int32_t i = 0; i < n; ++i) keys.push_back(q_key(mats[i], group));
+        for (int32_t i = 0; i < n; ++i) keys.push_back(op == 0 ? q_key(mats[i], group) : t_key(mats[i]));
         std::sort(keys.begin(), keys.end());
         L.nsets = (int)(std::unique(keys.begin(), keys.end()) - keys.begin());
     }
@@ -533,10 +558,10 @@ int32_t ent_run(const EntLayout& L, const woq_mat* mats, int32_t n_mats, const i
     uf[0] = 0;
     for (int32_t i = 0; i < n_mats; ++i) {
         const woq_mat& m = mats[i];
-        EntMat e{m.data, elems(m), m.cols, eff_ld(m), m.dtype, i, (int32_t)m.rows, ent_rpu(m)};
-        const int64_t u = ent_units(m);
-        if (e.dtype == WOQ_BF16) { tb[ib] = e; ub[ib + 1] = ub[ib] + u; ++ib; }
-        else { tf[jf] = e; uf[jf + 1] = uf[jf] + u; ++jf; }
+        EntMat e{m.data, elems(m), m.cols, eff_ld(m), m.dtype, i, (int32_t)m.rows, ent_rpu(m),
+                 ent_chunk(m)};
+        if (e.dtype == WOQ_BF16) { tb[ib] = e; ub[ib + 1] = ub[ib] + ent_vectors(m); ++ib; }
+        else { tf[jf] = e; uf[jf + 1] = uf[jf] + ent_units(m); ++jf; }
     }
     int32_t* bm = at<int32_t>(host.data(), L.bmats);
     int32_t* bb = at<int32_t>(host.data(), L.bbeg);
@@ -555,13 +580,15 @@ int32_t ent_run(const EntLayout& L, const woq_mat* mats, int32_t n_mats, const i
     if (exp_hist) WOQ_HIP(fill_u32(exp_hist, (size_t)n_mats * 256, 0u, stream));
     const EntMat* dtb = at<EntMat>(ws, L.tab_b);
     const int64_t* dub = at<int64_t>(ws, L.ubeg_b);
-    uint32_t* ghist = at<uint32_t>(ws, L.ghist);
-    for (int b0 = 0; b0 < L.nb; b0 += L.slots) {
-        const int b1 = std::min(L.nb, b0 + L.slots);
-        WOQ_HIP(fill_u32(ghist, (size_t)(b1 - b0) * 65536, 0u, stream));
-        WOQ_HIP(ent_hist_bf16(dtb + b0, dub + b0, b1 - b0, ub[b0], ub[b1] - ub[b0], ghist, stream));
-        WOQ_HIP(ent_hist_final(dtb + b0, b1 - b0, ghist, at<double4>(ws, L.hpart), h_mat, nf,
-                               exp_hist, stream));
+    uint32_t* recs = at<uint32_t>(ws, L.recs);
+    uint16_t* lists = at<uint16_t>(ws, L.lists);
+    // batches of equal size, at most L.slots matrices each
+    const int per = L.nb ? (int)cdiv(L.nb, cdiv(L.nb, L.slots)) : 0;
+    for (int b0 = 0; b0 < L.nb; b0 += per) {
+        const int b1 = std::min(L.nb, b0 + per);
+        WOQ_HIP(fill_u32(recs, (size_t)(b1 - b0) * kEntRecWords, 0u, stream));
+        WOQ_HIP(ent_hist_bf16(dtb + b0, dub + b0, b1 - b0, ub[b1] - ub[b0], recs, lists, stream));
+        WOQ_HIP(ent_hist_final(dtb + b0, b1 - b0, recs, lists, h_mat, nf, exp_hist, stream));
     }
     if (L.nf)
         WOQ_HIP(ent_f32(at<EntMat>(ws, L.tab_f), at<int64_t>(ws, L.ubeg_f), L.nf, L.units_f,
@@ -681,7 +708,7 @@ int32_t ewq_block_entropy_ex(const woq_mat* mats, int32_t n_mats, const int32_t*
 
 // The same computation with the library's static scratch array in place of
 // a caller workspace (for callers that cannot allocate).  Histograms go
-// through the array in batches of as many slots as fit beside the tables.
+// through the array in batches of as many matrices as fit beside the tables.
 int32_t ewq_block_entropy_static(const woq_mat* mats, int32_t n_mats, const int32_t* block_id,
                                  int32_t n_blocks, double x, double* h_mat, double* h_block,
                                  double* stats, int32_t* tier, int32_t* order,
@@ -691,7 +718,8 @@ int32_t ewq_block_entropy_static(const woq_mat* mats, int32_t n_mats, const int3
     EntLayout L = ent_layout(mats, n_mats, n_blocks, 0);   // tables and fp32 partials only
     if (L.total > kStaticScratch) return WOQ_ERR_SCRATCH;
     if (L.nb) {
-        const size_t per_slot = sizeof(uint32_t) * 65536 + sizeof(double4) * kHistBinParts + kAlign;
+        const size_t per_slot =
+            sizeof(uint32_t) * kEntRecWords + sizeof(uint16_t) * kEntListCap + 2 * kAlign;
         const size_t fit = (kStaticScratch - L.total) / per_slot;
         if (fit < 1) return WOQ_ERR_SCRATCH;
         L = ent_layout(mats, n_mats, n_blocks, (int)std::min<size_t>(fit, kHistSlots));
@@ -1002,13 +1030,25 @@ int32_t ternary_pack(const woq_mat* mats, int32_t n_mats, uint8_t* const* codes,
 
     std::vector<char> host(L.table_end, 0);
     QMat* tb = at<QMat>(host.data(), L.tab_b);
-    QMat* tf = at<QMat>(host.data(), L.tab_f);
     int64_t* ub = at<int64_t>(host.data(), L.ubeg_b);
-    int64_t* uf = at<int64_t>(host.data(), L.ubeg_f);
-    ub[0] = uf[0] = 0;
-    int ib = 0, jf = 0;
-    for (int32_t i = 0; i < n_mats; ++i) {
+    // matrices in launch-set order; each set has its own run of offsets
+    std::vector<int> idx(n_mats);
+    for (int32_t i = 0; i < n_mats; ++i) idx[i] = i;
+    std::stable_sort(idx.begin(), idx.end(),
+                     [&](int a, int b) { return t_key(mats[a]) < t_key(mats[b]); });
+    struct Set { QKey key; int first, count; size_t uoff; int64_t units; };
+    std::vector<Set> sets;
+    size_t uoff = 0;
+    for (int p = 0; p < n_mats; ++p) {
+        const int i = idx[p];
         const woq_mat& m = mats[i];
+        const QKey key = t_key(m);
+        if (sets.empty() || !(sets.back().key == key)) {
+            if (!sets.empty()) uoff += sets.back().count + 1;
+            sets.push_back(Set{key, p, 0, uoff, 0});
+            ub[uoff] = 0;
+        }
+        Set& st_ = sets.back();
         QMat q{};
         q.data = m.data;
         q.codes = codes[i];
@@ -1017,12 +1057,20 @@ int32_t ternary_pack(const woq_mat* mats, int32_t n_mats, uint8_t* const* codes,
         q.cols = (int32_t)m.cols;
         q.ld = (int32_t)eff_ld(m);
         q.dtype = m.dtype;
-        if (m.dtype == WOQ_BF16) { tb[ib] = q; ub[ib + 1] = ub[ib] + m.rows; ++ib; }
-        else { tf[jf] = q; uf[jf + 1] = uf[jf] + m.rows; ++jf; }
+        tb[p] = q;
+        ub[uoff + st_.count + 1] = ub[uoff + st_.count] + t_units(m);
+        ++st_.count;
+        st_.units = ub[uoff + st_.count];
     }
     WOQ_HIP(stage_tables(ws, host, L.table_end, stream));
-    if (L.nb) WOQ_HIP(ternary(at<QMat>(ws, L.tab_b), at<int64_t>(ws, L.ubeg_b), L.nb, ub[L.nb], WOQ_BF16, stream));
-    if (L.nf) WOQ_HIP(ternary(at<QMat>(ws, L.tab_f), at<int64_t>(ws, L.ubeg_f), L.nf, uf[L.nf], WOQ_F32, stream));
+    for (const Set& st_ : sets) {
+        const QMat* dt = at<QMat>(ws, L.tab_b) + st_.first;
+        const int64_t* du = at<int64_t>(ws, L.ubeg_b) + st_.uoff;
+        if (st_.key.kind == 1)
+            WOQ_HIP(ternary_wave(dt, du, st_.count, st_.units, st_.key.dtype, st_.key.nvl, stream));
+        else
+            WOQ_HIP(ternary(dt, du, st_.count, st_.units, st_.key.dtype, stream));
+    }
     return WOQ_OK;
 }
 

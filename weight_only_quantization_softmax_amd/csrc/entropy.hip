@@ -10,105 +10,250 @@
 //
 // bf16 path: a bf16 weight has only 65,536 bit patterns, so S and U are sums
 // over the distinct values weighted by exact integer counts.  One HBM pass
-// counts occurrences: patterns whose magnitude lies in a 32-binade window
-// ([2^-26, 2^6), where trained and synthetic weights live) go to an 8192-bin
-// LDS histogram; the rest (zeros, tiny, huge, inf/nan) go straight to the
-// matrix's global 65,536-bin histogram.  A second small kernel evaluates the
-// fp64 sums over the non-empty bins.  Results are exact up to fp64 rounding
-// and independent of scheduling (integer counts).
+// (k_hist_bf16, one workgroup per work unit) counts them: patterns whose
+// magnitude lies in a 31-binade window ([2^-25, 2^6), where trained and
+// synthetic weights live) in a 7,936-bin LDS histogram, added at the end to
+// the matrix's window record; zeros and NaN / inf are counted; every other
+// value (tiny, subnormal, |w| >= 64: rare) is appended to the matrix's list
+// as its bit pattern.  A unit that meets more such values than its LDS list
+// holds, or a matrix whose list fills, is marked spilled, and the final
+// kernel recounts that matrix's other values from the weights (sixteen
+// re-reads, each counting a sixteenth of the pattern space in LDS) - slow,
+// and only for matrices full of values far outside the window.  The final
+// kernel (k_hist_final, one workgroup per matrix) evaluates the fp64 sums
+// over the window bins, the zeros and the sorted list.  Results are exact
+// up to fp64 rounding and independent of scheduling (integer counts, sums
+// in a fixed order).  A matrix needs a 32 KB record and a 16 KB list, not
+// a 256 KB histogram, so the matrices of a whole model share one launch.
 //
 // fp32 path: two passes (max, then fp64 sums of exp(w - c) per work unit),
 // partials combined in a fixed order.
 //
-// The histogram also gives each bf16 matrix's exponent histogram (the counts
+// The counts also give each bf16 matrix's exponent histogram (the counts
 // of its 256 exponent fields) for the lossless exponent code of the kept
-// blocks, summed per part when the caller asks for it.
+// blocks, when the caller asks for it.
 //
-// A work unit is kEntChunk consecutive elements of a contiguous matrix, or
-// rpu whole rows of a strided one (row stride ld > cols).  Non-finite
-// weights (NaN, +-inf) make the entropy NaN and are counted into the
-// caller's uint64 counter: for bf16 from the histogram bins with an all-ones
-// exponent, for fp32 in the max pass.
+// A work unit is an equal share (at most kEntChunk elements, a multiple of
+// 8) of a contiguous matrix, or rpu whole rows of a strided one (row stride
+// ld > cols).  Non-finite weights (NaN, +-inf) make the entropy NaN and are
+// counted into the caller's uint64 counter: for bf16 in the counting pass,
+// for fp32 in the max pass.
 #include "launch.h"
 
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+
 namespace woq {
 namespace {
 
 constexpr int kT = 256;
-constexpr uint32_t kWinLo = 101u << 7;  // |w| bits in [101<<7, 133<<7)
-constexpr int kWinBins = 8192;          // 2 signs x 32 binades x 128 mantissas
+// Monotone unsigned key of a float (larger value, larger key; never 0 for
+// a non-NaN value), and its inverse.
+__device__ __forceinline__ uint32_t order_key(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
 
-__device__ __forceinline__ void hist_one(uint32_t h, uint32_t* lh, uint32_t* gh) {
+// ---------------------------------------------------------------- bf16
+// Window: bf16 patterns whose magnitude bits lie in [kWinLo, kWinLo +
+// kWinSpan), exponent fields 102..132 (|w| in [2^-25, 2^6)).  Window
+// pattern h has bin (|h| - kWinLo) | sign << 12, in LDS and in the
+// matrix's record alike (bins 3968..4095 of each sign unused).
+constexpr uint32_t kWinLo = 102u << 7;
+constexpr uint32_t kWinSpan = 31u << 7;
+constexpr int kWinBins = 4096 + (int)kWinSpan;   // 8064
+// LDS of the counting kernel: the window, then kExtra words: [0] +0 count,
+// [1] -0 count, [2] non-finite count, [3] order key of the largest other
+// value, [4] number of other values, [5] broadcast, then up to kLdsList
+// other values as 16-bit patterns.  32 KiB in all.
+constexpr int kExtra = 128;
+constexpr uint32_t kLdsList = 2 * (kExtra - 8);  // 240
+static_assert((kWinBins + kExtra) * 4 == 32768, "LDS of k_hist_bf16");
+static_assert(kWinBins % 2 == 0, "bins are added in pairs");
+// A matrix's record: the window counts, then kRecHdr words: [0..3] as the
+// LDS words, [4] values appended to the matrix's list, [5] spilled flag.
+constexpr int kRecHdr = 64;
+constexpr int kRecWords = kWinBins + kRecHdr;
+static_assert(kRecWords == kEntRecWords, "record size");
+constexpr uint32_t kListCap = (uint32_t)kEntListCap;
+
+// Values outside the window: zeros and non-finite values are counted; any
+// other value (tiny, subnormal or |w| >= 64) is kept as its pattern, and
+// the largest is tracked.
+__device__ __forceinline__ void hist_other(uint32_t h, uint32_t* ex) {
+    const uint32_t a = h & 0x7fffu;
+    if (a == 0) {
+        __hip_atomic_fetch_add(&ex[h >> 15], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else if (a >= 0x7f80u) {
+        __hip_atomic_fetch_add(&ex[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else {
+        __hip_atomic_fetch_max(&ex[3], order_key(__uint_as_float(h << 16)), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+        const uint32_t i =
+            __hip_atomic_fetch_add(&ex[4], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (i < kLdsList) reinterpret_cast<uint16_t*>(ex + 8)[i] = (uint16_t)h;
+    }
+}
+
+__device__ __forceinline__ void hist_one(uint32_t h, uint32_t* lh, uint32_t* ex) {
     const uint32_t t = (h & 0x7fffu) - kWinLo;
-    if (t < 4096u) {
+    if (t < kWinSpan)
         __hip_atomic_fetch_add(&lh[t | ((h >> 3) & 0x1000u)], 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_WORKGROUP);
+    else
+        hist_other(h, ex);
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Eight patterns (two per word).  Both halves of a word are tested at once
+// with 16-bit packed integer arithmetic: t = |h| - kWinLo (mod 2^16) is
+// below kWinSpan exactly for window patterns, and t | sign << 12 is the
+// bin.  One branch per eight patterns: when all eight are in the window
+// (nearly always) each takes one LDS add; otherwise each goes through
+// hist_one.
+__device__ __forceinline__ void hist8(const uint4 v, uint32_t* lh, uint32_t* ex) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const u16x2 lo = {(unsigned short)kWinLo, (unsigned short)kWinLo};
+    uint32_t bin[4];
+    u16x2 mx = {0, 0};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const u16x2 t = __builtin_bit_cast(u16x2, w[k] & 0x7fff7fffu) - lo;
+        mx = __builtin_elementwise_max(mx, t);
+        bin[k] = __builtin_bit_cast(uint32_t, t) | ((w[k] >> 3) & 0x10001000u);
+    }
+    if (max((uint32_t)mx.x, (uint32_t)mx.y) < kWinSpan) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            __hip_atomic_fetch_add(&lh[bin[k] & 0xffffu], 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_fetch_add(&lh[bin[k] >> 16], 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
     } else {
-        __hip_atomic_fetch_add(&gh[h], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            hist_one(w[k] & 0xffffu, lh, ex);
+            hist_one(w[k] >> 16, lh, ex);
+        }
     }
 }
 
-__device__ __forceinline__ void hist8(const uint4 v, uint32_t* lh, uint32_t* gh) {
-    hist_one(v.x & 0xffffu, lh, gh); hist_one(v.x >> 16, lh, gh);
-    hist_one(v.y & 0xffffu, lh, gh); hist_one(v.y >> 16, lh, gh);
-    hist_one(v.z & 0xffffu, lh, gh); hist_one(v.z >> 16, lh, gh);
-    hist_one(v.w & 0xffffu, lh, gh); hist_one(v.w >> 16, lh, gh);
+// Number of 16-byte vectors of a bf16 matrix: ceil(n / 8) when contiguous
+// (the last one may be partial), rows * cols / 8 when strided.
+__device__ __forceinline__ int64_t bf16_vectors(const EntMat& em) {
+    return em.ld == em.cols ? (em.n + 7) >> 3 : (int64_t)em.rows * (em.cols >> 3);
 }
 
-__global__ __launch_bounds__(kT) void k_hist_bf16(const EntMat* __restrict__ mats,
-                                                  const int64_t* __restrict__ ubeg,
-                                                  int nmat, int64_t u0,
-                                                  uint32_t* __restrict__ ghist) {
-    __shared__ uint32_t lh[kWinBins];
-    for (int i = threadIdx.x; i < kWinBins; i += kT) lh[i] = 0;
-    __syncthreads();
-
-    const int64_t u = u0 + blockIdx.x;
-    const int m = find_unit_owner(ubeg, nmat, u);
-    const EntMat em = mats[m];
-    uint32_t* gh = ghist + (size_t)m * 65536;
-    if (em.rpu == 0) {
-        const int64_t start = (u - ubeg[m]) * kEntChunk;
-        const int64_t cnt = min(kEntChunk, em.n - start);
-        const uint16_t* p = reinterpret_cast<const uint16_t*>(em.data) + start;
-        const uint4* pv = reinterpret_cast<const uint4*>(p);
-        const int64_t nv = cnt >> 3;
-
-        int64_t i = threadIdx.x;
-        for (; i + 3 * kT < nv; i += 4 * kT) {
-            const uint4 a = pv[i], b = pv[i + kT], c = pv[i + 2 * kT], d = pv[i + 3 * kT];
-            hist8(a, lh, gh); hist8(b, lh, gh); hist8(c, lh, gh); hist8(d, lh, gh);
+// Calls f(v) for each full 8-pattern vector of vectors [a, b) of a bf16
+// matrix and g(h) for each pattern of a partial last vector (thread t takes
+// vectors a + t, a + t + kT, ...).
+template <class F, class G>
+__device__ __forceinline__ void bf16_vecs(const EntMat& em, int64_t a, int64_t b, F&& f, G&& g) {
+    const uint16_t* base = reinterpret_cast<const uint16_t*>(em.data);
+    if (em.ld == em.cols) {
+        const int64_t nfull = em.n >> 3;
+        const int64_t bf = min(b, nfull);
+        int64_t i = a + threadIdx.x;
+        for (; i + 3 * kT < bf; i += 4 * kT) {
+            const uint4 v0 = gload_u4(base + 8 * i), v1 = gload_u4(base + 8 * (i + kT)),
+                        v2 = gload_u4(base + 8 * (i + 2 * kT)), v3 = gload_u4(base + 8 * (i + 3 * kT));
+            f(v0); f(v1); f(v2); f(v3);
         }
-        for (; i < nv; i += kT) hist8(pv[i], lh, gh);
-        for (int64_t e = nv * 8 + threadIdx.x; e < cnt; e += kT) hist_one(p[e], lh, gh);
+        for (; i < bf; i += kT) f(gload_u4(base + 8 * i));
+        if (b > nfull)
+            for (int64_t e = 8 * nfull + threadIdx.x; e < em.n; e += kT)
+                g((uint32_t)gload<uint16_t>(base + e));
     } else {
-        // rows [r0, r1) of a strided matrix (cols % 8 == 0): vector idx of the
-        // unit is row r0 + idx / vpr, columns 8 (idx % vpr) ..
-        const int r0 = (int)(u - ubeg[m]) * em.rpu;
-        const int r1 = min(em.rows, r0 + em.rpu);
+        // strided (cols % 8 == 0): vector idx is row idx / vpr, columns
+        // 8 (idx % vpr) ..
         const uint32_t vpr = (uint32_t)(em.cols >> 3);
-        const uint32_t nvu = (uint32_t)(r1 - r0) * vpr;
-        const uint16_t* base = reinterpret_cast<const uint16_t*>(em.data);
-        for (uint32_t idx = threadIdx.x; idx < nvu; idx += kT) {
+        for (uint32_t idx = (uint32_t)a + threadIdx.x; idx < (uint32_t)b; idx += kT) {
             const uint32_t r = idx / vpr, v = idx - r * vpr;
-            hist8(*reinterpret_cast<const uint4*>(base + (int64_t)(r0 + r) * em.ld + 8 * v), lh, gh);
-        }
-    }
-    __syncthreads();
-
-    for (int b = threadIdx.x; b < kWinBins; b += kT) {
-        const uint32_t c = lh[b];
-        if (c) {
-            const uint32_t bits = ((uint32_t)(b >> 12) << 15) | ((uint32_t)(b & 4095) + kWinLo);
-            __hip_atomic_fetch_add(&gh[bits], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            f(gload_u4(base + (int64_t)r * em.ld + 8 * v));
         }
     }
 }
 
-// Block-wide reductions for kT threads; every thread gets the result.
+// Adds a segment's LDS counts to matrix m's record and its other values to
+// the matrix's list (or marks the matrix spilled when they do not fit).
+// Called by the whole workgroup after a barrier.
+__device__ __forceinline__ void hist_flush(const uint32_t* lh, uint32_t* ex, uint32_t* rec,
+                                           uint16_t* list) {
+    uint32_t* hdr = rec + kWinBins;
+    // two bins per 64-bit add (a matrix's counts stay below 2^31, so no
+    // carry crosses into the upper bin)
+    const unsigned long long* lh2 = reinterpret_cast<const unsigned long long*>(lh);
+    unsigned long long* rec2 = reinterpret_cast<unsigned long long*>(rec);
+    for (int b = threadIdx.x; b < kWinBins / 2; b += kT) {
+        const unsigned long long c = lh2[b];
+        if (c) __hip_atomic_fetch_add(&rec2[b], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (threadIdx.x < 3 && ex[threadIdx.x])
+        __hip_atomic_fetch_add(&hdr[threadIdx.x], ex[threadIdx.x], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 3 && ex[3])
+        __hip_atomic_fetch_max(&hdr[3], ex[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t n = ex[4];   // the same for every thread
+    if (n == 0) return;
+    if (n > kLdsList) {
+        if (threadIdx.x == 0)
+            __hip_atomic_fetch_or(&hdr[5], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    if (threadIdx.x == 0)
+        ex[5] = __hip_atomic_fetch_add(&hdr[4], n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const uint32_t pos = ex[5];
+    if (pos + n > kListCap) {
+        if (threadIdx.x == 0)
+            __hip_atomic_fetch_or(&hdr[5], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    const uint16_t* ll = reinterpret_cast<const uint16_t*>(ex + 8);
+    for (uint32_t i = threadIdx.x; i < n; i += kT) list[pos + i] = ll[i];
+}
+
+// The counting pass over all bf16 matrices of a batch, as one sequence of
+// vectors (vbeg[m] = first vector of matrix m; vbeg[nmat] - vbeg[0] = the
+// total).  Workgroup g takes an equal share, [vbeg[0] + V g / G, vbeg[0] +
+// V (g + 1) / G) with G = gridDim.x, a few times the workgroups the GPU
+// holds at once: every workgroup streams the same number of bytes, and a
+// matrix segment costs one clearing of the LDS counts and one flush.
+__global__ __launch_bounds__(kT) void k_hist_bf16(const EntMat* __restrict__ mats,
+                                                  const int64_t* __restrict__ vbeg, int nmat,
+                                                  uint32_t* __restrict__ recs,
+                                                  uint16_t* __restrict__ lists) {
+    __shared__ __align__(8) uint32_t lh[kWinBins + kExtra];
+    uint32_t* ex = lh + kWinBins;
+    const int64_t V = vbeg[nmat] - vbeg[0];
+    const int64_t v0 = vbeg[0] + V * (int64_t)blockIdx.x / gridDim.x;
+    const int64_t v1 = vbeg[0] + V * (int64_t)(blockIdx.x + 1) / gridDim.x;
+    if (v0 >= v1) return;
+    int m = find_unit_owner(vbeg, nmat, v0);
+    for (int64_t v = v0; v < v1; ++m) {
+        const int64_t mb = vbeg[m];
+        const int64_t e = min(v1, vbeg[m + 1]);
+        for (int i = threadIdx.x; i < kWinBins + 8; i += kT) lh[i] = 0;
+        __syncthreads();
+        const EntMat em = mats[m];
+        bf16_vecs(em, v - mb, e - mb, [&](const uint4 x) { hist8(x, lh, ex); },
+                  [&](uint32_t h) { hist_one(h, lh, ex); });
+        __syncthreads();
+        hist_flush(lh, ex, recs + (size_t)m * kRecWords, lists + (size_t)m * kListCap);
+        __syncthreads();
+        v = e;
+    }
+}
+
+// Block-wide reductions for NT threads; every thread gets the result.
+template <int NT = kT>
 __device__ __forceinline__ double block_sum(double v, double* sh) {
     v = wave_sum(v);
     __syncthreads();
@@ -116,7 +261,7 @@ __device__ __forceinline__ double block_sum(double v, double* sh) {
     __syncthreads();
     double r = 0.0;
 #pragma unroll
-    for (int w = 0; w < kT / 64; ++w) r += sh[w];
+    for (int w = 0; w < NT / 64; ++w) r += sh[w];
     return r;
 }
 
@@ -131,109 +276,149 @@ __device__ __forceinline__ float block_maxf(float v, float* sh) {
     return r;
 }
 
-// The 65,536 bins of a matrix are split into kHistParts parts of 4096 bins.
-// Part w takes the largest finite non-empty value c_w of its bins and sums,
-// relative to it, S_w = sum n_v e^{v - c_w} and U_w = sum n_v e^{v - c_w}
-// (v - c_w) in fp64.  The combine rescales to the matrix maximum c:
-//   S = sum_w S_w e^{c_w - c},  U = sum_w (U_w + (c_w - c) S_w) e^{c_w - c},
-// so H = ln S - U / S exactly as from one pass (up to fp64 rounding).
-constexpr int kHistParts = kHistBinParts;
-constexpr int kPartBins = 65536 / kHistParts;
+__device__ __forceinline__ float win_value(int b) {
+    const uint32_t h = ((uint32_t)(b >> 12) << 15) | ((uint32_t)(b & 4095) + kWinLo);
+    return __uint_as_float(h << 16);
+}
 
-__global__ __launch_bounds__(kT) void k_hist_part(const EntMat* __restrict__ mats,
-                                                  const uint32_t* __restrict__ ghist,
-                                                  double4* __restrict__ part,
-                                                  uint32_t* __restrict__ exp_hist) {
+// Adds n e^{v - c} to S and n e^{v - c} (v - c) to U (fp64).
+__device__ __forceinline__ void add_term(double n, float v, double c, double& S, double& U) {
+    const double d = (double)v - c;
+    const double e = n * exp(d);
+    S += e;
+    U += e * d;
+}
+
+// One workgroup per matrix: c = the largest finite value (window bins,
+// the largest other value, zeros), then S = sum_v n_v e^{v - c} and U =
+// sum_v n_v e^{v - c} (v - c) in fp64 over the window bins (bin order), the
+// zeros, and the other values: from the list sorted by pattern, or, when
+// the matrix spilled, from sixteen re-reads of the matrix that each count
+// the other values of one sixteenth of the pattern space in LDS.  H = ln S -
+// U / S, NaN when the matrix holds a non-finite value.  Every sum has a
+// fixed order, so the result does not depend on scheduling.
+__global__ __launch_bounds__(kT) void k_hist_final(const EntMat* __restrict__ mats,
+                                                   const uint32_t* __restrict__ recs,
+                                                   const uint16_t* __restrict__ lists,
+                                                   double* __restrict__ h_mat,
+                                                   unsigned long long* __restrict__ nonfinite,
+                                                   uint32_t* __restrict__ exp_hist) {
     __shared__ double shd[kT / 64];
     __shared__ float shf[kT / 64];
-    __shared__ uint32_t lexp[32];
-    const int m = blockIdx.x / kHistParts, w = blockIdx.x % kHistParts;
-    const uint32_t* gh = ghist + (size_t)m * 65536 + (size_t)w * kPartBins;
-    constexpr int PER = kPartBins / kT;
+    __shared__ uint32_t lexp[256];
+    __shared__ uint32_t big[4096];   // the sorted list (16-bit) or one sixteenth's counts
+    const int m = blockIdx.x;
+    const EntMat em = mats[m];
+    const uint32_t* rec = recs + (size_t)m * kRecWords;
+    const uint32_t* hdr = rec + kWinBins;
+    const uint32_t zp = hdr[0], zn = hdr[1], nf = hdr[2], mk = hdr[3], nl = hdr[4];
+    const bool spilled = hdr[5] != 0 || nl > kListCap;
+    constexpr int PER = (kWinBins + kT - 1) / kT;   // 32
     uint32_t cnt[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) cnt[i] = gload<uint32_t>(gh + threadIdx.x + kT * i);
-    if (exp_hist) {
-        // the part holds one sign and 32 exponent fields (128 mantissas
-        // each): bin threadIdx.x + kT i has exponent 32 (w % 8) + 2 i +
-        // threadIdx.x / 128
-        if (threadIdx.x < 32) lexp[threadIdx.x] = 0;
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < PER; ++i)
-            if (cnt[i]) atomicAdd(&lexp[2 * i + (threadIdx.x >> 7)], cnt[i]);
-        __syncthreads();
-        if (threadIdx.x < 32 && lexp[threadIdx.x])
-            atomicAdd(exp_hist + (size_t)mats[m].slot * 256 + 32 * (w % 8) + threadIdx.x,
-                      lexp[threadIdx.x]);
-    }
     float mx = -INFINITY;
-    double bad = 0.0;  // weights whose bin has an all-ones exponent (NaN, inf)
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        if (cnt[i]) {
-            const uint32_t b = (uint32_t)(w * kPartBins) + threadIdx.x + kT * i;
-            const float v = __uint_as_float(b << 16);
-            if (!isfinite(v)) bad += (double)cnt[i]; else mx = fmaxf(mx, v);
-        }
+        const int b = threadIdx.x + kT * i;
+        cnt[i] = (b < kWinBins && (uint32_t)(b & 4095) < kWinSpan) ? rec[b] : 0u;
+        if (cnt[i]) mx = fmaxf(mx, win_value(b));
     }
-    mx = block_maxf(mx, shf);
-    bad = block_sum(bad, shd);
-    double S = 0.0, U = 0.0;
-    const double c = (double)mx;
-    if (mx > -INFINITY) {
+    if (threadIdx.x == 0) {
+        if (mk) mx = fmaxf(mx, key_value(mk));
+        if (zp + zn) mx = fmaxf(mx, 0.0f);
+    }
+    if (exp_hist) {
+        // the 64 bins of a wave share one exponent field: one sum per wave
+        lexp[threadIdx.x] = 0;
+        __syncthreads();
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const uint32_t b = (uint32_t)(w * kPartBins) + threadIdx.x + kT * i;
-            const float v = __uint_as_float(b << 16);
-            if (cnt[i] && isfinite(v)) {
-                const double d = (double)v - c;
-                const double e = (double)cnt[i] * exp(d);
-                S += e;
-                U += e * d;
+            const int b = (threadIdx.x & ~63) + kT * i;
+            if (b < kWinBins && (uint32_t)(b & 4095) < kWinSpan) {
+                const double w = wave_sum((double)cnt[i]);   // integer counts: exact
+                if ((threadIdx.x & 63) == 0 && w != 0.0)
+                    atomicAdd(&lexp[102 + ((b & 4095) >> 7)], (uint32_t)w);
+            }
+        }
+        if (threadIdx.x == 0) {
+            lexp[0] += zp + zn;
+            lexp[255] += nf;
+        }
+    }
+    const double c = (double)block_maxf(mx, shf);
+    double S = 0.0, U = 0.0;
+    if (c > -INFINITY) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            if (cnt[i]) add_term((double)cnt[i], win_value(threadIdx.x + kT * i), c, S, U);
+        if (threadIdx.x == 0 && zp + zn) add_term((double)(zp + zn), 0.0f, c, S, U);
+    }
+    if (!spilled && nl) {
+        // sort the list (bitonic, padded to a power of two with 0xffff,
+        // a pattern the list never holds), then thread t takes sorted
+        // entries t, t + kT, ...
+        uint16_t* s = reinterpret_cast<uint16_t*>(big);
+        uint32_t n2 = 2;
+        while (n2 < nl) n2 <<= 1;
+        const uint16_t* src = lists + (size_t)m * kListCap;
+        for (uint32_t i = threadIdx.x; i < n2; i += kT) s[i] = i < nl ? src[i] : (uint16_t)0xffff;
+        __syncthreads();
+        for (uint32_t k = 2; k <= n2; k <<= 1) {
+            for (uint32_t j = k >> 1; j > 0; j >>= 1) {
+                for (uint32_t i = threadIdx.x; i < n2; i += kT) {
+                    const uint32_t l = i ^ j;
+                    if (l > i) {
+                        const uint16_t a = s[i], b = s[l];
+                        if ((a > b) == ((i & k) == 0)) { s[i] = b; s[l] = a; }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        for (uint32_t i = threadIdx.x; i < nl; i += kT) {
+            const uint32_t h = s[i];
+            add_term(1.0, __uint_as_float(h << 16), c, S, U);
+            if (exp_hist) atomicAdd(&lexp[(h >> 7) & 0xffu], 1u);
+        }
+    } else if (spilled) {
+        for (uint32_t r = 0; r < 16; ++r) {
+            __syncthreads();
+            for (int i = threadIdx.x; i < 4096; i += kT) big[i] = 0;
+            __syncthreads();
+            auto one = [&](uint32_t h) {
+                const uint32_t a = h & 0x7fffu;
+                if ((h >> 12) == r && a - kWinLo >= kWinSpan && a != 0 && a < 0x7f80u)
+                    atomicAdd(&big[h & 4095u], 1u);
+            };
+            bf16_vecs(em, 0, bf16_vectors(em),
+                      [&](const uint4 v) {
+                          one(v.x & 0xffffu); one(v.x >> 16); one(v.y & 0xffffu); one(v.y >> 16);
+                          one(v.z & 0xffffu); one(v.z >> 16); one(v.w & 0xffffu); one(v.w >> 16);
+                      },
+                      one);
+            __syncthreads();
+            for (int i = threadIdx.x; i < 4096; i += kT) {
+                const uint32_t n = big[i];
+                if (n) {
+                    const uint32_t h = (r << 12) | (uint32_t)i;
+                    add_term((double)n, __uint_as_float(h << 16), c, S, U);
+                    if (exp_hist) atomicAdd(&lexp[(h >> 7) & 0xffu], n);
+                }
             }
         }
     }
     S = block_sum(S, shd);
     U = block_sum(U, shd);
-    if (threadIdx.x == 0) part[blockIdx.x] = make_double4(c, S, U, bad);
-}
-
-__global__ __launch_bounds__(kT) void k_hist_comb(const EntMat* __restrict__ mats, int nmat,
-                                                  const double4* __restrict__ part,
-                                                  double* __restrict__ h_mat,
-                                                  unsigned long long* __restrict__ nonfinite) {
-    const int m = blockIdx.x * kT + threadIdx.x;
-    if (m >= nmat) return;
-    const double4* p = part + (size_t)m * kHistParts;
-    double c = -INFINITY, nbad = 0.0;
-    for (int w = 0; w < kHistParts; ++w) {
-        const double4 q = p[w];
-        if (q.y > 0.0) c = fmax(c, q.x);
-        nbad += q.w;  // integer counts below 2^31: exact in fp64
+    if (exp_hist) {
+        __syncthreads();
+        gstore<uint32_t>(exp_hist + (size_t)em.slot * 256 + threadIdx.x, lexp[threadIdx.x]);
     }
-    const bool bad = nbad != 0.0;
-    if (bad) atomicAdd(nonfinite, (unsigned long long)nbad);
-    double S = 0.0, U = 0.0;
-    for (int w = 0; w < kHistParts; ++w) {
-        const double4 q = p[w];
-        if (q.y > 0.0) {
-            const double f = exp(q.x - c);
-            S += q.y * f;
-            U += (q.z + (q.x - c) * q.y) * f;
-        }
+    if (threadIdx.x == 0) {
+        if (nf) atomicAdd(nonfinite, (unsigned long long)nf);
+        gstore<double>(h_mat + em.slot, nf ? (double)NAN : log(S) - U / S);
     }
-    gstore<double>(h_mat + mats[m].slot, bad ? (double)NAN : log(S) - U / S);
 }
 
 // ---------------------------------------------------------------- fp32
-__device__ __forceinline__ uint32_t order_key(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_value(uint32_t k) {
-    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
 
 // Calls f(value) for every element of work unit u of an fp32 matrix, thread
 // t taking elements t, t + kT, ... of the unit.
@@ -241,8 +426,8 @@ template <class F>
 __device__ __forceinline__ void f32_unit(const EntMat& em, int64_t ul, F&& f) {
     const float* base = reinterpret_cast<const float*>(em.data);
     if (em.rpu == 0) {
-        const int64_t start = ul * kEntChunk;
-        const int64_t cnt = min(kEntChunk, em.n - start);
+        const int64_t start = ul * em.chunk;
+        const int64_t cnt = min(em.chunk, em.n - start);
         for (int64_t e = threadIdx.x; e < cnt; e += kT) f(base[start + e]);
     } else {
         const int r0 = (int)ul * em.rpu;
@@ -312,7 +497,9 @@ __global__ void k_f32_final(const EntMat* __restrict__ mats, const int64_t* __re
 }
 
 // ---------------------------------------------------------------- blocks
-__global__ __launch_bounds__(kT) void k_blocks(const int32_t* __restrict__ bmats,
+constexpr int kBT = 1024;   // threads of k_blocks
+
+__global__ __launch_bounds__(kBT) void k_blocks(const int32_t* __restrict__ bmats,
                                                const int32_t* __restrict__ bbeg,
                                                const double* __restrict__ nsz,
                                                const double* __restrict__ h_mat, int nb,
@@ -321,28 +508,35 @@ __global__ __launch_bounds__(kT) void k_blocks(const int32_t* __restrict__ bmats
                                                double* __restrict__ stats,
                                                int32_t* __restrict__ tier,
                                                int32_t* __restrict__ order) {
-    __shared__ double shd[kT / 64];
-    for (int b = threadIdx.x; b < nb; b += kT) {
+    __shared__ double shd[kBT / 64];
+    // one wave per block: lane j takes the block's matrices j, j + 64, ...,
+    // then the lanes' sums are combined in a fixed order
+    const int lane = threadIdx.x & 63;
+    for (int b = threadIdx.x >> 6; b < nb; b += kBT / 64) {
         double num = 0.0, den = 0.0;
-        for (int i = bbeg[b]; i < bbeg[b + 1]; ++i) {
+        for (int i = bbeg[b] + lane; i < bbeg[b + 1]; i += 64) {
             const int m = bmats[i];
             num += nsz[m] * h_mat[m];
             den += nsz[m];
         }
-        const double h = num / den;
-        hb[b] = h;
-        if (h_block) h_block[b] = h;
+        num = wave_sum(num);
+        den = wave_sum(den);
+        if (lane == 0) {
+            const double h = num / den;
+            hb[b] = h;
+            if (h_block) h_block[b] = h;
+        }
     }
     __syncthreads();
     double acc = 0.0;
-    for (int b = threadIdx.x; b < nb; b += kT) acc += hb[b];
-    const double mu = block_sum(acc, shd) / nb;
+    for (int b = threadIdx.x; b < nb; b += kBT) acc += hb[b];
+    const double mu = block_sum<kBT>(acc, shd) / nb;
     acc = 0.0;
-    for (int b = threadIdx.x; b < nb; b += kT) { const double d = hb[b] - mu; acc += d * d; }
-    const double sigma = sqrt(block_sum(acc, shd) / nb);
+    for (int b = threadIdx.x; b < nb; b += kBT) { const double d = hb[b] - mu; acc += d * d; }
+    const double sigma = sqrt(block_sum<kBT>(acc, shd) / nb);
     const double t = mu - x * sigma;
     if (stats && threadIdx.x == 0) { stats[0] = mu; stats[1] = sigma; stats[2] = t; }
-    for (int b = threadIdx.x; b < nb; b += kT) {
+    for (int b = threadIdx.x; b < nb; b += kBT) {
         const double h = hb[b];
         if (tier) tier[b] = (h <= t) ? 1 : ((h < mu) ? 2 : 3);
         if (order) {
@@ -366,17 +560,26 @@ __global__ __launch_bounds__(256) void k_stage(uint32_t* dst, uint32_t nw, Stage
     for (uint32_t i = threadIdx.x; i < nw; i += 256) dst[i] = c.w[i];
 }
 
+// p 16-byte aligned: 16-byte stores, then the last n % 4 words.
 __global__ void k_fill_u32(uint32_t* p, size_t n, uint32_t v) {
-    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
-         i += (size_t)gridDim.x * blockDim.x)
-        p[i] = v;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    const size_t t = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+    if ((reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+        const uint4 w = make_uint4(v, v, v, v);
+        uint4* q = reinterpret_cast<uint4*>(p);
+        const size_t n4 = n >> 2;
+        for (size_t i = t; i < n4; i += stride) q[i] = w;
+        for (size_t i = 4 * n4 + t; i < n; i += stride) p[i] = v;
+    } else {
+        for (size_t i = t; i < n; i += stride) p[i] = v;
+    }
 }
 
 }  // namespace
 
 hipError_t fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s) {
     if (n == 0) return hipSuccess;
-    const size_t blocks = min((n + 255) / 256, (size_t)4096);
+    const size_t blocks = min((n / 4 + 255) / 256 + 1, (size_t)4096);
     k_fill_u32<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p, n, v);
     return hipGetLastError();
 }
@@ -401,19 +604,40 @@ hipError_t fill_f32(float* p, size_t n, float v, hipStream_t s) {
     return fill_u32(reinterpret_cast<uint32_t*>(p), n, bits, s);
 }
 
-hipError_t ent_hist_bf16(const EntMat* mats, const int64_t* ubeg, int nmat, int64_t u0,
-                         int64_t n_units, uint32_t* ghist, hipStream_t s) {
-    if (n_units <= 0) return hipSuccess;
-    k_hist_bf16<<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, u0, ghist);
+hipError_t ent_hist_bf16(const EntMat* mats, const int64_t* vbeg, int nmat, int64_t n_vec,
+                         uint32_t* recs, uint16_t* lists, hipStream_t s) {
+    if (n_vec <= 0) return hipSuccess;
+    // kHistWaves x the workgroups of k_hist_bf16 the device holds at once
+    // (measured on the 8B and MoE stacks: 4 beat 1, 2 and 8 - shares small
+    // enough that the last ones to finish leave little idle, large enough
+    // that a matrix segment's clearing and flush stay rare)
+    constexpr int kHistWaves = 4;
+    static int resident[64] = {0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (resident[dev] == 0) {
+        int per_cu = 0, cus = 0;
+        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                 &per_cu, reinterpret_cast<const void*>(k_hist_bf16), kT, 0)) != hipSuccess)
+            return e;
+        if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) !=
+            hipSuccess)
+            return e;
+        resident[dev] = kHistWaves * std::max(1, per_cu) * std::max(1, cus);
+    }
+    const int64_t g = std::min<int64_t>(resident[dev], (n_vec + kT - 1) / kT);
+    k_hist_bf16<<<dim3((unsigned)g), dim3(kT), 0, s>>>(mats, vbeg, nmat, recs, lists);
     return hipGetLastError();
 }
 
-hipError_t ent_hist_final(const EntMat* mats, int nmat, const uint32_t* ghist, double4* part,
-                          double* h_mat, unsigned long long* nonfinite, uint32_t* exp_hist,
-                          hipStream_t s) {
+hipError_t ent_hist_final(const EntMat* mats, int nmat, const uint32_t* recs,
+                          const uint16_t* lists, double* h_mat, unsigned long long* nonfinite,
+                          uint32_t* exp_hist, hipStream_t s) {
     if (nmat <= 0) return hipSuccess;
-    k_hist_part<<<dim3(nmat * kHistParts), dim3(kT), 0, s>>>(mats, ghist, part, exp_hist);
-    k_hist_comb<<<dim3((nmat + kT - 1) / kT), dim3(kT), 0, s>>>(mats, nmat, part, h_mat, nonfinite);
+    k_hist_final<<<dim3((unsigned)nmat), dim3(kT), 0, s>>>(mats, recs, lists, h_mat, nonfinite,
+                                                          exp_hist);
     return hipGetLastError();
 }
 
@@ -435,7 +659,7 @@ hipError_t ent_blocks(const int32_t* bmats, const int32_t* bbeg, const double* n
                       const double* h_mat, int n_blocks, double x, double* hb,
                       double* h_block, double* stats, int32_t* tier, int32_t* order,
                       hipStream_t s) {
-    k_blocks<<<dim3(1), dim3(kT), 0, s>>>(bmats, bbeg, nsz, h_mat, n_blocks, x, hb, h_block,
+    k_blocks<<<dim3(1), dim3(kBT), 0, s>>>(bmats, bbeg, nsz, h_mat, n_blocks, x, hb, h_block,
                                            stats, tier, order);
     return hipGetLastError();
 }

@@ -7,8 +7,13 @@
 namespace woq {
 
 // ---- entropy ([EWQ] step 1 and 2)
-constexpr int64_t kEntChunk = int64_t(1) << 19;   // elements per work unit
-constexpr int kHistSlots = 256;                    // bf16 matrices per batch
+constexpr int64_t kEntChunk = int64_t(1) << 19;   // elements per work unit (at most)
+constexpr int kHistSlots = 8192;                   // bf16 matrices per batch
+// Per bf16 matrix of a batch: a record of kEntRecWords uint32 (window
+// counts and a header; zeroed before counting) and a list of up to
+// kEntListCap 16-bit patterns of values outside the window.
+constexpr int kEntRecWords = 8128;
+constexpr int kEntListCap = 8192;
 
 hipError_t fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 // Host bytes to device memory through kernel arguments, kStageChunk bytes
@@ -17,17 +22,18 @@ constexpr int kStageChunk = 1024;
 hipError_t stage_bytes(void* dst, const void* src, size_t n, hipStream_t s);
 hipError_t fill_f32(float* p, size_t n, float v, hipStream_t s);
 
-hipError_t ent_hist_bf16(const EntMat* mats, const int64_t* ubeg, int nmat,
-                         int64_t u0, int64_t n_units, uint32_t* ghist,
-                         hipStream_t s);
-// Entropy from the histograms: kHistBinParts parts per matrix (partials in
-// part[nmat * kHistBinParts]), then one combine per matrix.
-constexpr int kHistBinParts = 16;
+// Counting pass over the bf16 matrices mats[0, nmat): vbeg[m] is the first
+// 16-byte vector of matrix m in one sequence over the batch (vbeg[nmat] -
+// vbeg[0] = n_vec); records and lists indexed by the batch position m.
+hipError_t ent_hist_bf16(const EntMat* mats, const int64_t* vbeg, int nmat, int64_t n_vec,
+                         uint32_t* recs, uint16_t* lists, hipStream_t s);
+// Entropy from the records: one workgroup per matrix.
 // nonfinite: the call's uint64 counter of NaN / inf weights (added to).
-// exp_hist (may be NULL): per matrix slot 256 exponent-field counts, added to.
-hipError_t ent_hist_final(const EntMat* mats, int nmat, const uint32_t* ghist,
-                          double4* part, double* h_mat, unsigned long long* nonfinite,
-                          uint32_t* exp_hist, hipStream_t s);
+// exp_hist (may be NULL): per matrix slot 256 exponent-field counts (written).
+hipError_t ent_hist_final(const EntMat* mats, int nmat, const uint32_t* recs,
+                          const uint16_t* lists, double* h_mat,
+                          unsigned long long* nonfinite, uint32_t* exp_hist,
+                          hipStream_t s);
 hipError_t ent_f32(const EntMat* mats, const int64_t* ubeg, int nmat,
                    int64_t n_units, uint32_t* keys, double2* part,
                    double* h_mat, unsigned long long* nonfinite, hipStream_t s);
@@ -94,6 +100,13 @@ hipError_t quant_big(const QMat* mats, const int64_t* ubeg, int nmat,
 hipError_t dequant(const QMat* mats, const int64_t* ubeg, int nmat,
                    int64_t n_units, int out_dtype, int bits, const CbTable* book,
                    hipStream_t s);
+// Ternary, rows of at most kTernWaveMax columns: one wave per row,
+// kTernRows rows per unit; nvl = 8-column vectors per lane (1, 2, 4 or 8).
+constexpr int kTernRows = 16;
+constexpr int kTernWaveMax = 4096;
+hipError_t ternary_wave(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
+                        int dtype, int nvl, hipStream_t s);
+// Ternary, wider rows: one workgroup per row (one unit per row).
 hipError_t ternary(const QMat* mats, const int64_t* ubeg, int nmat,
                    int64_t n_units, int dtype, hipStream_t s);
 

@@ -25,7 +25,10 @@
 //                 workgroup per group, one LDS exchange.
 //  k_dequant      tiles of kDTileRows rows x 2048 columns (measured on the
 //                 8B stack's int4 matrices: 4 rows beat 8 and 16).
-//  k_ternary      one workgroup per row.
+//  k_ternary_wave rows of up to 4096 columns: one wave per row, 16 rows
+//                 per workgroup (the MoE experts' 1408- and 2048-column
+//                 rows are 3-4 KB: a workgroup each left most of it idle).
+//  k_ternary      wider rows: one workgroup per row.
 //
 // The tile, wave and big kernels and k_dequant also serve the code-book
 // grid (template argument CB): a group is scaled by its largest |x| and each
@@ -667,6 +670,70 @@ __global__ __launch_bounds__(kT) void k_ternary(const QMat* __restrict__ mats,
     if (threadIdx.x == 0) gstore<float>(q.scales + row, beta);
 }
 
+// Ternary codes for rows of at most 64 * 8 * NVL columns: one wave per row,
+// kTernRows rows per workgroup (wave w takes rows w, w + 4, ...), the next
+// row's loads issued before the current row is coded.  Same arithmetic as
+// k_ternary: beta = (sum |w| in fp64, lanes then the wave) / cols, rounded
+// once to fp32; code q + 1 with q = clamp(rne(w * (1/beta)), -1, 1).
+template <int DT, int NVL>
+__global__ __launch_bounds__(kT) void k_ternary_wave(const QMat* __restrict__ mats,
+                                                     const int64_t* __restrict__ ubeg, int nmat) {
+    constexpr int RPW = kTernRows / 4;  // rows per wave
+    const int64_t u = blockIdx.x;
+    const int m = find_unit_owner(ubeg, nmat, u);
+    const QMat q = mats[m];
+    const int lane = threadIdx.x & 63;
+    const int nv = q.cols >> 3;
+    const int r0 = (int)(u - ubeg[m]) * kTernRows + (threadIdx.x >> 6);
+    Raw8<DT> buf[2][NVL];
+    auto load = [&](Raw8<DT> (&b)[NVL], int row) {
+#pragma unroll
+        for (int k = 0; k < NVL; ++k) {
+            const int v = lane + 64 * k;
+            if (v < nv) b[k] = load_raw<DT>(q.data, (uint32_t)row * (uint32_t)q.ld + 8u * v);
+        }
+    };
+    if (r0 < q.rows) load(buf[0], r0);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int row = r0 + 4 * i;
+        if (row >= q.rows) break;  // wave-uniform
+        if (i + 1 < RPW && row + 4 < q.rows) load(buf[(i + 1) & 1], row + 4);
+        Raw8<DT>(&b)[NVL] = buf[i & 1];
+        double acc = 0.0;
+#pragma unroll
+        for (int k = 0; k < NVL; ++k) {
+            if (lane + 64 * k < nv) {
+                float x[8];
+                unpack_raw<DT>(b[k], x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc += (double)fabsf(x[e]);
+            }
+        }
+        acc = wave_sum(acc);
+        const float beta = (float)(acc / (double)q.cols);
+        const float inv = __fdiv_rn(1.0f, beta);
+        const bool ok = isfinite(inv);
+        const uint32_t rbase = (uint32_t)row * (uint32_t)q.cols;   // codes (contiguous)
+#pragma unroll
+        for (int k = 0; k < NVL; ++k) {
+            const int v = lane + 64 * k;
+            if (v < nv) {
+                float x[8];
+                unpack_raw<DT>(b[k], x);
+                uint32_t w = 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float t = ok ? clampf(rintf(__fmul_rn(x[e], inv)), -1.f, 1.f) : 0.f;
+                    w |= (uint32_t)(int)(t + 1.0f) << (2 * e);
+                }
+                gstore<uint16_t>(q.codes + ((rbase + 8u * v) >> 2), (uint16_t)w);
+            }
+        }
+        if (lane == 0) gstore<float>(q.scales + row, beta);
+    }
+}
+
 __global__ __launch_bounds__(kT) void k_recip(const RecipSeg* __restrict__ segs,
                                               const int64_t* __restrict__ ubeg, int nseg) {
     const int64_t u = blockIdx.x;
@@ -821,6 +888,26 @@ hipError_t ternary(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_un
     else
         k_ternary<WOQ_F32><<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat);
     return hipGetLastError();
+}
+
+template <int DT>
+hipError_t ternary_wave_dt(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
+                           int nvl, hipStream_t s) {
+    const dim3 g((unsigned)n_units), b(kT);
+    switch (nvl) {
+        case 1: k_ternary_wave<DT, 1><<<g, b, 0, s>>>(mats, ubeg, nmat); break;
+        case 2: k_ternary_wave<DT, 2><<<g, b, 0, s>>>(mats, ubeg, nmat); break;
+        case 4: k_ternary_wave<DT, 4><<<g, b, 0, s>>>(mats, ubeg, nmat); break;
+        default: k_ternary_wave<DT, 8><<<g, b, 0, s>>>(mats, ubeg, nmat); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t ternary_wave(const QMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
+                        int dtype, int nvl, hipStream_t s) {
+    if (n_units <= 0) return hipSuccess;
+    return dtype == WOQ_BF16 ? ternary_wave_dt<WOQ_BF16>(mats, ubeg, nmat, n_units, nvl, s)
+                             : ternary_wave_dt<WOQ_F32>(mats, ubeg, nmat, n_units, nvl, s);
 }
 
 }  // namespace woq

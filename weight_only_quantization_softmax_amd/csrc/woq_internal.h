@@ -112,6 +112,7 @@ struct EntMat {
     int32_t slot;       // index of this matrix in the caller's h_mat
     int32_t rows;
     int32_t rpu;        // rows per work unit when strided (0: contiguous)
+    int64_t chunk;      // elements per work unit when contiguous (a multiple of 8)
 };
 
 // Sinkhorn: one entry per matrix.  A matrix is cut into row strips, one

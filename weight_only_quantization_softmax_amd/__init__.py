@@ -31,7 +31,7 @@ from __future__ import annotations
 
 import contextlib
 import ctypes
-from typing import Optional, Sequence
+from typing import List, Optional, Sequence
 
 import torch
 
@@ -59,24 +59,35 @@ def _ld(t: torch.Tensor) -> int:
     return 0 if t.is_contiguous() else int(t.stride(0))
 
 
-def _check_mats(tensors: Sequence[torch.Tensor]) -> None:
+def _descs(tensors: Sequence[torch.Tensor]) -> List[tuple]:
+    """Checks the matrices and returns their (data_ptr, dtype code, rows,
+    cols, ld) descriptors (one pass over the list)."""
     if len(tensors) == 0:
         raise ValueError("at least one matrix is required")
+    out = []
     for t in tensors:
         if t.dim() != 2:
             raise ValueError("matrices must be 2-D")
-        if t.shape[0] < 1 or t.shape[1] < 1:
+        r, c = t.shape
+        if r < 1 or c < 1:
             raise ValueError(f"empty matrix of shape {tuple(t.shape)}")
-        if not t.is_contiguous() and (t.stride(1) != 1 or t.stride(0) < t.shape[1]):
-            raise ValueError("matrices must be contiguous or row-strided views "
-                             f"(unit column stride), got strides {tuple(t.stride())}")
-        _dtype_code(t)
+        ld = 0
+        if not t.is_contiguous():
+            s0, s1 = t.stride()
+            if s1 != 1 or s0 < c:
+                raise ValueError("matrices must be contiguous or row-strided views "
+                                 f"(unit column stride), got strides {(s0, s1)}")
+            ld = s0
+        out.append((t.data_ptr(), _dtype_code(t), r, c, ld))
+    return out
+
+
+def _check_mats(tensors: Sequence[torch.Tensor]) -> None:
+    _descs(tensors)
 
 
 def _mats(tensors: Sequence[torch.Tensor]):
-    _check_mats(tensors)
-    return _lib.mat_array((t.data_ptr(), _dtype_code(t), t.shape[0], t.shape[1], _ld(t))
-                          for t in tensors)
+    return _lib.mat_array(_descs(tensors))
 
 
 def _check_bufs(name: str, ts, sizes, dtype) -> None:

@@ -9,6 +9,8 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
+
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwoq.so")
 
 WOQ_OK = 0
@@ -127,20 +129,25 @@ def check(fn: str, status: int) -> None:
         raise WoqError(fn, status)
 
 
+# numpy view of the woq_mat layout (filled column-wise, then shared with a
+# ctypes array without a copy)
+_MAT_NP = np.dtype({"names": ["data", "dtype", "reserved", "rows", "cols", "ld"],
+                    "formats": ["<u8", "<i4", "<i4", "<i8", "<i8", "<i8"],
+                    "offsets": [0, 8, 12, 16, 24, 32], "itemsize": ctypes.sizeof(WoqMat)})
+
+
 def mat_array(descs):
     """descs: iterable of (data_ptr, dtype, rows, cols[, ld]) -> ctypes WoqMat
     array (ld 0 = contiguous)."""
     descs = list(descs)
-    arr = (WoqMat * len(descs))()
-    for i, d in enumerate(descs):
-        ptr, dt, r, c = d[:4]
-        arr[i].data = ptr
-        arr[i].dtype = dt
-        arr[i].reserved = 0
-        arr[i].rows = r
-        arr[i].cols = c
-        arr[i].ld = d[4] if len(d) > 4 else 0
-    return arr
+    a = np.zeros(len(descs), dtype=_MAT_NP)
+    if descs:
+        a["data"] = [d[0] or 0 for d in descs]
+        a["dtype"] = [d[1] for d in descs]
+        a["rows"] = [d[2] for d in descs]
+        a["cols"] = [d[3] for d in descs]
+        a["ld"] = [d[4] if len(d) > 4 else 0 for d in descs]
+    return (WoqMat * len(descs)).from_buffer(a)
 
 
 def ptr_array(ptrs):

@@ -44,6 +44,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 
 namespace woq {
 namespace {
@@ -612,12 +613,13 @@ hipError_t ent_hist_bf16(const EntMat* mats, const int64_t* vbeg, int nmat, int6
     // enough that the last ones to finish leave little idle, large enough
     // that a matrix segment's clearing and flush stay rare)
     constexpr int kHistWaves = 4;
-    static int resident[64] = {0};
+    static std::atomic<int> resident[64];   // per device, 0 until first looked up
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (resident[dev] == 0) {
+    int g_max = resident[dev].load(std::memory_order_relaxed);
+    if (g_max == 0) {
         int per_cu = 0, cus = 0;
         if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
                  &per_cu, reinterpret_cast<const void*>(k_hist_bf16), kT, 0)) != hipSuccess)
@@ -625,9 +627,10 @@ hipError_t ent_hist_bf16(const EntMat* mats, const int64_t* vbeg, int nmat, int6
         if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) !=
             hipSuccess)
             return e;
-        resident[dev] = kHistWaves * std::max(1, per_cu) * std::max(1, cus);
+        g_max = kHistWaves * std::max(1, per_cu) * std::max(1, cus);
+        resident[dev].store(g_max, std::memory_order_relaxed);
     }
-    const int64_t g = std::min<int64_t>(resident[dev], (n_vec + kT - 1) / kT);
+    const int64_t g = std::min<int64_t>(g_max, (n_vec + kT - 1) / kT);
     k_hist_bf16<<<dim3((unsigned)g), dim3(kT), 0, s>>>(mats, vbeg, nmat, recs, lists);
     return hipGetLastError();
 }

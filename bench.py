@@ -71,7 +71,7 @@ def _host_f32(t):
 
 
 def cpu_workers() -> int:
-    """Host cores this process may use, at most 16 (one GPU's share of a box)."""
+    """Host cores this process may use, at most 16 (one GPU's share of the machine)."""
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
@@ -482,7 +482,7 @@ def ctypes_stream(stream):
 
 def ceilings():
     """What plain kernels with no arithmetic reach on this GPU (the library's
-    streaming kernels are judged against these, not only against the
+    streaming kernels are compared with these, not only with the
     8 TB/s spec): a grid-stride read of 8 GiB from HBM, a 1 GiB copy (read +
     write), re-reads of a 128 MiB buffer that stays in the 256 MB Infinity
     Cache (32 passes in one launch; grid-stride and per-workgroup contiguous
@@ -542,7 +542,7 @@ def ceilings_sweep():
 
 
 def torch_reference(reps=20):
-    """Streaming rates of torch's stock kernels on the box (not the
+    """Streaming rates of torch's stock kernels on this GPU (not the
     library's), for comparison with the library's kernels: a 1 GiB device
     copy (read + write), 1 GiB read-only reductions, and the same reduction
     over a 128 MiB buffer that stays in the 256 MB Infinity Cache across
@@ -594,7 +594,7 @@ def main() -> int:
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one device copy of this size first (counter calibration)")
     ap.add_argument("--torch-reference", action="store_true",
-                    help="only measure torch's stock streaming kernels on the box")
+                    help="only measure torch's stock streaming kernels on this GPU")
     ap.add_argument("--ceilings-only", action="store_true",
                     help="only measure the streaming ceilings (libwoq_probe.so)")
     ap.add_argument("--ceilings-sweep", action="store_true",

@@ -3,7 +3,7 @@
 The oracle's work is numpy array kernels, which release the GIL, so a thread
 pool runs it on all host cores without starting processes from a program
 that has initialised the GPU.  Workers: the host cores this process may use,
-at most 16 (a one-GPU machine's CPU share)."""
+at most 16 (one GPU's share of a machine's cores)."""
 from __future__ import annotations
 
 import concurrent.futures as cf

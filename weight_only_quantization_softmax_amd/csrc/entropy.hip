@@ -314,35 +314,41 @@ __global__ __launch_bounds__(kT) void k_hist_final(const EntMat* __restrict__ ma
     const uint32_t* hdr = rec + kWinBins;
     const uint32_t zp = hdr[0], zn = hdr[1], nf = hdr[2], mk = hdr[3], nl = hdr[4];
     const bool spilled = hdr[5] != 0 || nl > kListCap;
-    constexpr int PER = (kWinBins + kT - 1) / kT;   // 32
+    // thread t holds the 32 consecutive bins [32 t, 32 t + 32): one
+    // exponent field, wholly inside or outside the window's used bins
+    constexpr int PER = 32;
+    static_assert(kWinBins <= PER * kT && kWinSpan % PER == 0, "bin ownership");
+    const int b0 = PER * threadIdx.x;
+    const bool own = b0 < kWinBins && (uint32_t)(b0 & 4095) < kWinSpan;
     uint32_t cnt[PER];
+    if (own) {
+#pragma unroll
+        for (int i = 0; i < PER / 4; ++i) {
+            const uint4 v = gload_u4(rec + b0 + 4 * i);
+            cnt[4 * i] = v.x; cnt[4 * i + 1] = v.y; cnt[4 * i + 2] = v.z; cnt[4 * i + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) cnt[i] = 0u;
+    }
     float mx = -INFINITY;
+    uint32_t tot = 0;   // the thread's count (< 2^31: one matrix)
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int b = threadIdx.x + kT * i;
-        cnt[i] = (b < kWinBins && (uint32_t)(b & 4095) < kWinSpan) ? rec[b] : 0u;
-        if (cnt[i]) mx = fmaxf(mx, win_value(b));
+        if (cnt[i]) mx = fmaxf(mx, win_value(b0 + i));
+        tot += cnt[i];
     }
     if (threadIdx.x == 0) {
         if (mk) mx = fmaxf(mx, key_value(mk));
         if (zp + zn) mx = fmaxf(mx, 0.0f);
     }
     if (exp_hist) {
-        // the 64 bins of a wave share one exponent field: one sum per wave
         lexp[threadIdx.x] = 0;
         __syncthreads();
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int b = (threadIdx.x & ~63) + kT * i;
-            if (b < kWinBins && (uint32_t)(b & 4095) < kWinSpan) {
-                const double w = wave_sum((double)cnt[i]);   // integer counts: exact
-                if ((threadIdx.x & 63) == 0 && w != 0.0)
-                    atomicAdd(&lexp[102 + ((b & 4095) >> 7)], (uint32_t)w);
-            }
-        }
+        if (tot) atomicAdd(&lexp[102 + ((b0 & 4095) >> 7)], tot);
         if (threadIdx.x == 0) {
-            lexp[0] += zp + zn;
-            lexp[255] += nf;
+            atomicAdd(&lexp[0], zp + zn);
+            atomicAdd(&lexp[255], nf);
         }
     }
     const double c = (double)block_maxf(mx, shf);
@@ -350,7 +356,7 @@ __global__ __launch_bounds__(kT) void k_hist_final(const EntMat* __restrict__ ma
     if (c > -INFINITY) {
 #pragma unroll
         for (int i = 0; i < PER; ++i)
-            if (cnt[i]) add_term((double)cnt[i], win_value(threadIdx.x + kT * i), c, S, U);
+            if (cnt[i]) add_term((double)cnt[i], win_value(b0 + i), c, S, U);
         if (threadIdx.x == 0 && zp + zn) add_term((double)(zp + zn), 0.0f, c, S, U);
     }
     if (!spilled && nl) {

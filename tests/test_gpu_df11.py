@@ -154,10 +154,10 @@ def test_full_llama8b_block_round_trip():
 
 def test_exponent_histograms_from_the_entropy_pass():
     """ewq_block_entropy_ex: each bf16 matrix's exponent histogram, summed
-    from the entropy histogram, equals df11_exponent_histogram's and the
-    oracle's (strided views included, more matrices than one histogram batch
-    on the path with few, fp32 matrices all zero); the entropies are those of
-    ewq_block_entropy."""
+    from the entropy pass's counts (window bins, zeros, NaN / inf, the list
+    of other values), equals df11_exponent_histogram's and the oracle's
+    (strided views included, fp32 matrices all zero); the entropies are
+    those of ewq_block_entropy."""
     import woqdata
     mats = [woqdata.random_matrix(64 + 8 * i, 512, 700 + i, std=0.005 * (1 + i % 4)).to(DEV)
             for i in range(6)]

@@ -277,7 +277,9 @@ SinqLayout sinq_layout(const woq_mat* mats, int32_t n, bool shared) {
             g.cols_max = std::max<int>(g.cols_max, (int)m.cols);
         }
         const int rcols = 256 / sinq_reduce_slices(g.max_strips);
-        for (int k = p; k < q; ++k) g.n_cunits += cdiv(mats[idx[k]].cols, rcols);
+        // a wave-form matrix swept by one workgroup finishes its own columns
+        for (int k = p; k < q; ++k)
+            if (!(g.sh.mode == 1 && L.n_strips[k] == 1)) g.n_cunits += cdiv(mats[idx[k]].cols, rcols);
         L.groups.push_back(g);
         p = q;
     }
@@ -787,8 +789,9 @@ int32_t sinq_balance_ex(const woq_mat* mats, int32_t n_mats, int32_t iters, int3
         gs[0] = gc[0] = 0;
         const int rcols = 256 / sinq_reduce_slices(g.max_strips);
         for (int k = 0; k < g.count; ++k) {
-            gs[k + 1] = gs[k] + tab[g.first + k].n_strips;
-            gc[k + 1] = gc[k] + cdiv(tab[g.first + k].cols, rcols);
+            const SinqMat& sm = tab[g.first + k];
+            gs[k + 1] = gs[k] + sm.n_strips;
+            gc[k + 1] = gc[k] + ((g.sh.mode == 1 && sm.n_strips == 1) ? 0 : cdiv(sm.cols, rcols));
         }
     }
     WOQ_HIP(stage_tables(ws, host, L.table_end, stream));

@@ -58,7 +58,10 @@ int sinq_wave_occupancy(int dtype, int nv);
 // reduction workgroup covers 256 / slices columns.
 int sinq_reduce_slices(int max_strips);
 // One iteration over a group of same-shape matrices: the fused row / column
-// pass then the fixed-order column reduction.  The first iteration adds the
+// pass then the fixed-order column reduction.  A wave-form matrix swept by
+// a single workgroup (n_strips == 1) has its columns finished by that
+// workgroup and no units in col_begin; n_col_units == 0 launches no
+// reduction.  The first iteration adds the
 // NaN / inf weights it reads to *nonfinite.
 hipError_t sinq_iteration(const SinqMat* mats, const int64_t* strip_begin,
                           const int64_t* col_begin, int nmat, int64_t n_strips,

@@ -31,7 +31,9 @@
 //   2. the same registers give z = w*v_i, accumulated into the thread's
 //      column (sum, sum of squares).
 // At the end every workgroup writes one partial row; a second kernel combines
-// the partial rows per column in fp64 in a fixed order -> t_j, u_j.
+// the partial rows per column in fp64 in a fixed order -> t_j, u_j.  (A
+// wave-form matrix swept by one workgroup is finished by that workgroup
+// from the same sums, with the same arithmetic.)
 // Everything runs in a fixed order, so results are deterministic.
 //
 // Accuracy.  Since K is one of the lane's own values, n (mean - K)^2 is at
@@ -487,6 +489,42 @@ __global__ __launch_bounds__(kMaxT) void k_sinq_pass(const SinqMat* __restrict__
     }
 }
 
+// A column whose squared mean exceeds this multiple of its variance is
+// recomputed in the reduction (the fp32 partials would cost more than ~1e-5).
+constexpr double kIllCond = 64.0;
+
+// t_j and u_j = 1/t_j of column j from its fp64 sums S = sum z, Q = sum z^2
+// over all rows (and, for fp32, the column's min and max of z).
+template <int DT>
+__device__ __forceinline__ void col_finish(const SinqMat& sm, int j, double S, double Q, float mn,
+                                           float mx) {
+    const double n = (double)sm.rows;
+    const double mean = S / n;
+    double var = sm.rms ? Q / n : Q / n - mean * mean;
+    if (!sm.rms && mean * mean > kIllCond * var) {
+        // E[z^2] - E[z]^2 from fp32 partials loses about eps * mean^2 / var:
+        // recompute this column in one pass around the (accurate) mean, with
+        // the same z = w * (1/s_i) as the sweep.
+        double S2 = 0.0, Q2 = 0.0;
+        for (int i = 0; i < sm.rows; ++i) {
+            const float v = __fdiv_rn(1.0f, gload<float>(sm.s + i));
+            float x;
+            if constexpr (DT == WOQ_BF16)
+                x = __uint_as_float((uint32_t)gload<uint16_t>(reinterpret_cast<const uint16_t*>(sm.data) + (int64_t)i * sm.ld + j) << 16);
+            else
+                x = gload<float>(reinterpret_cast<const float*>(sm.data) + (int64_t)i * sm.ld + j);
+            const double dz = (double)(x * v) - mean;
+            S2 += dz;
+            Q2 += dz * dz;
+        }
+        var = Q2 / n - (S2 / n) * (S2 / n);
+    }
+    const bool constant = (DT == WOQ_F32) && !sm.rms && !(mx > mn);
+    const float t = (var > 0.0 && !constant) ? (float)sqrt(var) : 1.0f;
+    gstore<float>(sm.t + j, t);
+    gstore<float>(sm.u + j, __fdiv_rn(1.0f, t));
+}
+
 // ---------------------------------------------------------------------------
 // Wave-per-row pass for rows of at most 4096 bf16 (1536 fp32) columns.  A
 // workgroup owns 4 * strip_rows consecutive rows of one matrix, dealt to its
@@ -725,6 +763,17 @@ __global__ __launch_bounds__(256, (WaveCfg<DT, NVL>::OCC)) void k_sinq_wave(
         }
         __syncthreads();
     }
+    if (sm.n_strips == 1) {
+        // this workgroup sweeps the whole matrix, so its partial row is the
+        // column sums: t and u from them directly, with the arithmetic of
+        // k_sinq_reduce for one partial row (the reduction skips the matrix)
+        for (int j = threadIdx.x; j < cols; j += 256) {
+            const float* pc = cp + (size_t)NP * j;
+            col_finish<DT>(sm, j, (double)pc[0], (double)pc[1], F32 ? pc[2] : INFINITY,
+                           F32 ? pc[3] : -INFINITY);
+        }
+        return;
+    }
     // one partial row per workgroup
     const f32x4* c4 = reinterpret_cast<const f32x4*>(cp);
     f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(sm.part) + (size_t)wg * cols * NP);
@@ -781,9 +830,6 @@ hipError_t launch_wave_f32(const SinqMat* mats, const int64_t* wbeg, int nmat, i
 // is fixed for a given launch plan, so results are deterministic.
 constexpr int kRedInflight = 16;
 
-// A column whose squared mean exceeds this multiple of its variance is
-// recomputed in the reduction (the fp32 partials would cost more than ~1e-5).
-constexpr double kIllCond = 64.0;
 
 template <int DT>
 __global__ __launch_bounds__(256) void k_sinq_reduce(const SinqMat* __restrict__ mats,
@@ -845,32 +891,7 @@ __global__ __launch_bounds__(256) void k_sinq_reduce(const SinqMat* __restrict__
         }
     }
     if (j >= sm.cols) return;
-    const double n = (double)sm.rows;
-    const double mean = S / n;
-    double var = sm.rms ? Q / n : Q / n - mean * mean;
-    if (!sm.rms && mean * mean > kIllCond * var) {
-        // E[z^2] - E[z]^2 from fp32 partials loses about eps * mean^2 / var:
-        // recompute this column in one pass around the (accurate) mean, with
-        // the same z = w * (1/s_i) as the sweep (rows of the workgroup's
-        // columns are read contiguously).
-        double S2 = 0.0, Q2 = 0.0;
-        for (int i = 0; i < sm.rows; ++i) {
-            const float v = __fdiv_rn(1.0f, gload<float>(sm.s + i));
-            float x;
-            if constexpr (DT == WOQ_BF16)
-                x = __uint_as_float((uint32_t)gload<uint16_t>(reinterpret_cast<const uint16_t*>(sm.data) + (int64_t)i * sm.ld + j) << 16);
-            else
-                x = gload<float>(reinterpret_cast<const float*>(sm.data) + (int64_t)i * sm.ld + j);
-            const double dz = (double)(x * v) - mean;
-            S2 += dz;
-            Q2 += dz * dz;
-        }
-        var = Q2 / n - (S2 / n) * (S2 / n);
-    }
-    const bool constant = (DT == WOQ_F32) && !sm.rms && !(mx > mn);
-    const float t = (var > 0.0 && !constant) ? (float)sqrt(var) : 1.0f;
-    gstore<float>(sm.t + j, t);
-    gstore<float>(sm.u + j, __fdiv_rn(1.0f, t));
+    col_finish<DT>(sm, j, S, Q, mn, mx);
 }
 
 template <int DT, int NV, bool RAG>
@@ -953,6 +974,7 @@ hipError_t sinq_iteration(const SinqMat* mats, const int64_t* sbeg, const int64_
                 ? launch_pass_dt<WOQ_BF16>(mats, sbeg, nmat, n_strips, sh, cols_max, first, nf, s)
                 : launch_pass_dt<WOQ_F32>(mats, sbeg, nmat, n_strips, sh, cols_max, first, nf, s);
     if (e != hipSuccess) return e;
+    if (n_col_units == 0) return hipSuccess;   // every matrix finished by its sweep
     const int slices = sinq_reduce_slices(max_strips);
     if (dtype == WOQ_BF16)
         k_sinq_reduce<WOQ_BF16><<<dim3((unsigned)n_col_units), dim3(256), 0, s>>>(mats, cbeg, nmat, slices);

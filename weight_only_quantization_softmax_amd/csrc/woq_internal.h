@@ -92,19 +92,7 @@ __device__ __forceinline__ float wave_maxf(float v) {
 // Largest m in [0, n) with begin[m] <= u (begin ascending, n + 1 entries,
 // begin[0] <= u < begin[n]).
 __device__ __forceinline__ int find_unit_owner(const int64_t* begin, int n, int64_t u) {
-    // first guess from u's position in the whole range (exact when the
-    // matrices have equal unit counts, as a model's repeated layers do),
-    // then a binary search on the side that holds u
-    const int64_t b0 = begin[0], tot = begin[n] - b0;
-    int g = tot > 0 ? (int)(((u - b0) * (int64_t)n) / tot) : 0;
-    g = g < 0 ? 0 : (g > n - 1 ? n - 1 : g);
     int lo = 0, hi = n - 1;
-    if (begin[g] <= u) {
-        if (g == n - 1 || begin[g + 1] > u) return g;
-        lo = g + 1;
-    } else {
-        hi = g - 1;
-    }
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (begin[mid] <= u) lo = mid; else hi = mid - 1;

@@ -132,12 +132,15 @@ struct EntLayout {
 // fp32: rows per entropy work unit of a strided matrix (0 for a contiguous
 // one), and the matrix's number of work units.  bf16: the matrix's number
 // of 16-byte vectors (the counting pass shares them out evenly).
+int64_t ent_target(const woq_mat& m) {
+    return std::min(kEntChunk, std::max(kEntMinChunk, cdiv(elems(m), kEntSplit)));
+}
 int32_t ent_rpu(const woq_mat& m) {
-    return eff_ld(m) == m.cols ? 0 : (int32_t)std::max<int64_t>(1, kEntChunk / m.cols);
+    return eff_ld(m) == m.cols ? 0 : (int32_t)std::max<int64_t>(1, ent_target(m) / m.cols);
 }
 int64_t ent_units(const woq_mat& m) {
     const int32_t rpu = ent_rpu(m);
-    return rpu ? cdiv(m.rows, rpu) : cdiv(elems(m), kEntChunk);
+    return rpu ? cdiv(m.rows, rpu) : cdiv(elems(m), ent_target(m));
 }
 // Elements per work unit of a contiguous matrix: the matrix split evenly
 // (rounded up to a multiple of 8, so every unit starts 16-byte aligned).

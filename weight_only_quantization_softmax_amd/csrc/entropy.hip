@@ -33,9 +33,9 @@
 // of its 256 exponent fields) for the lossless exponent code of the kept
 // blocks, when the caller asks for it.
 //
-// A work unit is an equal share (at most kEntChunk elements, a multiple of
-// 8) of a contiguous matrix, or rpu whole rows of a strided one (row stride
-// ld > cols).  Non-finite weights (NaN, +-inf) make the entropy NaN and are
+// An fp32 work unit is an equal share (a multiple of 8 elements, between
+// kEntMinChunk and kEntChunk) of a contiguous matrix, or rpu whole rows of a
+// strided one (row stride ld > cols).  Non-finite weights (NaN, +-inf) make the entropy NaN and are
 // counted into the caller's uint64 counter: for bf16 in the counting pass,
 // for fp32 in the max pass.
 #include "launch.h"

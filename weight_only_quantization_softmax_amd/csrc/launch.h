@@ -7,7 +7,12 @@
 namespace woq {
 
 // ---- entropy ([EWQ] step 1 and 2)
-constexpr int64_t kEntChunk = int64_t(1) << 19;   // elements per work unit (at most)
+// fp32 work units: at most kEntChunk and at least kEntMinChunk elements,
+// a matrix split into about kEntSplit units between these bounds, so that a
+// small matrix is still shared among several workgroups.
+constexpr int64_t kEntChunk = int64_t(1) << 19;
+constexpr int64_t kEntMinChunk = 4096;
+constexpr int64_t kEntSplit = 128;
 constexpr int kHistSlots = 8192;                   // bf16 matrices per batch
 // Per bf16 matrix of a batch: a record of kEntRecWords uint32 (window
 // counts and a header; zeroed before counting) and a list of up to

@@ -101,9 +101,10 @@ __device__ __forceinline__ int find_unit_owner(const int64_t* begin, int n, int6
 }
 
 // ------------------------------------------------------------ descriptors
-// Entropy: one entry per matrix.  A contiguous matrix (ld == cols) is read
-// in work units of kEntChunk consecutive elements; a strided one in units of
-// rpu whole rows (rpu * cols about kEntChunk).
+// Entropy: one entry per matrix.  An fp32 contiguous matrix (ld == cols) is
+// read in work units of `chunk` consecutive elements; a strided one in units
+// of rpu whole rows.  bf16 matrices are read as 16-byte vectors shared out
+// evenly over the counting pass.
 struct EntMat {
     const void* data;
     int64_t n;          // rows * cols

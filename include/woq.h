@@ -185,8 +185,10 @@ int32_t ewq_block_entropy_ex(const woq_mat* mats, int32_t n_mats,
  *  held until the process ends and located on the first call on each device.
  *  BF16 matrices pass through it in batches of as many as fit (about 48 KB
  *  of counts each), so any number of matrices works; WOQ_ERR_SCRATCH
- *  (before any HIP call) when the descriptor tables, fp32 partials and the
- *  counts of one matrix do not fit (about 400,000 matrices).  Arguments, results and other errors as for
+ *  (before any HIP call) when the descriptor tables, fp32 partials (24
+ *  bytes per fp32 work unit: at most 128 units in a matrix of up to 2^26
+ *  elements) and the counts of one matrix do not fit (about 400,000 bf16
+ *  matrices).  Arguments, results and other errors as for
  *  ewq_block_entropy; the non-finite count is not reported.  Every call on
  *  a GPU uses that GPU's one array: calls that overlap on one GPU (two host
  *  threads, or two streams without ordering between them) race; calls

@@ -69,6 +69,43 @@ def test_entropy_special_values_and_windows():
     assert math.isnan(h[0]) and math.isnan(h[1])
 
 
+def test_fp32_entropy_running_maximum():
+    """fp32 matrices are read once, each thread keeping a running maximum
+    that rescales its sums: values rising along every thread's elements (a
+    new maximum at each one), falling, spread so widely that most
+    exponentials underflow, one outlier far above the rest, all equal, and
+    NaN / inf inside one work unit of many-unit matrices."""
+    rng = np.random.default_rng(41)
+    rise = np.linspace(-30.0, 30.0, 512 * 1024).astype(np.float32).reshape(512, 1024)
+    fall = rise[::-1, ::-1].copy()
+    wide = ((rng.random((300, 1000)) * 2 - 1) * 3e3).astype(np.float32)
+    out1 = (rng.standard_normal((1024, 640)) * 0.02).astype(np.float32)
+    out1[700, 33] = 700.0
+    out2 = out1.copy()
+    out2[5, 5] = 1e4
+    flat = np.full((1000, 777), 0.37, dtype=np.float32)
+    mats = [torch.from_numpy(a).to(DEV) for a in (rise, fall, wide, out1, out2, flat)]
+    h = woq.ewq_block_entropy(mats)["h_mat"].cpu().numpy()
+    for i, m in enumerate(mats):
+        ref = oracle.matrix_entropy(m.cpu().numpy())
+        assert abs(h[i] - ref) <= 1e-12 * ref + 1e-14, (i, h[i], ref)
+    assert h[5] == pytest.approx(math.log(1000 * 777), rel=1e-14)
+    view = mats[0][:, 256:768]
+    assert not view.is_contiguous()
+    a = woq.ewq_block_entropy([view])["h_mat"]
+    b = woq.ewq_block_entropy([view.contiguous()])["h_mat"]
+    assert torch.equal(a.view(torch.int64), b.view(torch.int64))
+    bad = torch.from_numpy((rng.standard_normal((2048, 1024)) * 0.02).astype(np.float32)).to(DEV)
+    bad2 = bad.clone()
+    bad[1500, 3] = float("nan")
+    bad2[2047, 1023] = float("-inf")
+    bad2[0, 0] = float("inf")
+    out = woq.ewq_block_entropy([bad, mats[3], bad2])
+    h = out["h_mat"].cpu().numpy()
+    assert math.isnan(h[0]) and math.isnan(h[2]) and h[1] == woq.ewq_block_entropy([mats[3]])["h_mat"].item()
+    assert out["nonfinite"].item() == 3
+
+
 def test_block_entropy_tiers_order():
     rng = np.random.default_rng(5)
     mats, bid = [], []

@@ -126,7 +126,7 @@ struct EntLayout {
     int slots = 0;          // bf16 histograms per batch
     int64_t units_b = 0, units_f = 0;
     size_t tab_b, ubeg_b, tab_f, ubeg_f, bmats, bbeg, nsz, table_end;
-    size_t hb, keys, part_f, recs, lists, total;
+    size_t hb, part_f, recs, lists, total;
 };
 
 // fp32: rows per entropy work unit of a strided matrix (0 for a contiguous
@@ -169,8 +169,7 @@ EntLayout ent_layout(const woq_mat* mats, int32_t n, int32_t n_blocks, int max_s
     L.nsz = a.take(sizeof(double) * n);
     L.table_end = a.end();
     L.hb = a.take(sizeof(double) * n_blocks);
-    L.keys = a.take(sizeof(uint32_t) * 2 * L.nf);
-    L.part_f = a.take(sizeof(double2) * L.units_f);
+    L.part_f = a.take(sizeof(double) * 3 * L.units_f);
     L.slots = std::min(L.nb, max_slots);
     L.recs = a.take(sizeof(uint32_t) * kEntRecWords * (size_t)L.slots);
     L.lists = a.take(sizeof(uint16_t) * kEntListCap * (size_t)L.slots);
@@ -597,7 +596,7 @@ int32_t ent_run(const EntLayout& L, const woq_mat* mats, int32_t n_mats, const i
     }
     if (L.nf)
         WOQ_HIP(ent_f32(at<EntMat>(ws, L.tab_f), at<int64_t>(ws, L.ubeg_f), L.nf, L.units_f,
-                        at<uint32_t>(ws, L.keys), at<double2>(ws, L.part_f), h_mat, nf, stream));
+                        at<double>(ws, L.part_f), h_mat, nf, stream));
     WOQ_HIP(ent_blocks(at<int32_t>(ws, L.bmats), at<int32_t>(ws, L.bbeg), at<double>(ws, L.nsz),
                        h_mat, n_blocks, x, at<double>(ws, L.hb), h_block, stats, tier, order,
                        stream));

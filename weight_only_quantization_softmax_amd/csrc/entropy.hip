@@ -26,8 +26,9 @@
 // in a fixed order).  A matrix needs a 32 KB record and a 16 KB list, not
 // a 256 KB histogram, so the matrices of a whole model share one launch.
 //
-// fp32 path: two passes (max, then fp64 sums of exp(w - c) per work unit),
-// partials combined in a fixed order.
+// fp32 path: one pass per work unit (a running maximum with fp64 sums of
+// exp(w - m), rescaled when the maximum grows), the units' partials
+// combined in a fixed order.
 //
 // The counts also give each bf16 matrix's exponent histogram (the counts
 // of its 256 exponent fields) for the lossless exponent code of the kept
@@ -37,7 +38,7 @@
 // kEntMinChunk and kEntChunk) of a contiguous matrix, or rpu whole rows of a
 // strided one (row stride ld > cols).  Non-finite weights (NaN, +-inf) make the entropy NaN and are
 // counted into the caller's uint64 counter: for bf16 in the counting pass,
-// for fp32 in the max pass.
+// for fp32 in the one pass.
 #include "launch.h"
 
 #include <math.h>
@@ -427,80 +428,156 @@ __global__ __launch_bounds__(kT) void k_hist_final(const EntMat* __restrict__ ma
 
 // ---------------------------------------------------------------- fp32
 
-// Calls f(value) for every element of work unit u of an fp32 matrix, thread
-// t taking elements t, t + kT, ... of the unit.
-template <class F>
-__device__ __forceinline__ void f32_unit(const EntMat& em, int64_t ul, F&& f) {
+// Running sums of one thread over fp32 values: the largest finite value mx
+// met so far, S = sum exp(w - mx) and U = sum exp(w - mx) (w - mx) over the
+// finite values, nbad the NaN / inf values.  Values arrive in batches: the
+// batch's maximum first, the sums moved to it when it is larger
+// (exp(w - m') = exp(w - m) exp(m - m')), then one exponential per value.
+struct F32Acc {
+    float mx = -INFINITY;
+    double S = 0.0, U = 0.0;
+    uint32_t nbad = 0;
+
+    __device__ __forceinline__ void rebase(float m) {
+        if (S != 0.0) {
+            const double d = (double)mx - (double)m;   // <= 0
+            const double r = exp(d);
+            U = r * (U + S * d);
+            S = r * S;
+        }
+        mx = m;
+    }
+    template <int K>
+    __device__ __forceinline__ void add(const float (&v)[K]) {
+        float bm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+            if (isfinite(v[i])) bm = fmaxf(bm, v[i]);
+            else ++nbad;
+        }
+        if (bm > mx) rebase(bm);
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+            if (isfinite(v[i])) {
+                const double d = (double)v[i] - (double)mx;
+                const double x = exp(d);
+                S += x;
+                U += x * d;
+            }
+        }
+    }
+};
+
+__device__ __forceinline__ void f32_load4(const float* p, bool vec, float* v) {
+    if (vec) {
+        const float4 a = gload_f4(p);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    } else {
+        v[0] = p[0]; v[1] = p[1]; v[2] = p[2]; v[3] = p[3];
+    }
+}
+
+// Thread t's groups of work unit ul: group g is 4 consecutive elements of a
+// row at addr(g); the thread takes g = t, t + kT, ... in that order, four
+// groups per batch while they last.  vec: every group is 16-byte aligned.
+template <class A>
+__device__ __forceinline__ void f32_groups(int ng, bool vec, A&& addr, F32Acc& acc) {
+    int g = threadIdx.x;
+    for (; g + 3 * kT < ng; g += 4 * kT) {
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f32_load4(addr(g + j * kT), vec, v + 4 * j);
+        acc.add<16>(v);
+    }
+    for (; g < ng; g += kT) {
+        float v[4];
+        f32_load4(addr(g), vec, v);
+        acc.add<4>(v);
+    }
+}
+
+// Adds work unit ul of an fp32 matrix to acc.  A contiguous unit is `chunk`
+// consecutive elements (a multiple of 8 but in the last unit); a strided one
+// is rpu whole rows (cols a multiple of 8).  The order in which a thread
+// meets its values depends only on the unit's rows and columns, not on the
+// row stride or the alignment, so a strided view and its contiguous copy
+// with the same units give the same sums.
+__device__ __forceinline__ void f32_unit(const EntMat& em, int64_t ul, F32Acc& acc) {
     const float* base = reinterpret_cast<const float*>(em.data);
     if (em.rpu == 0) {
         const int64_t start = ul * em.chunk;
-        const int64_t cnt = min(em.chunk, em.n - start);
-        for (int64_t e = threadIdx.x; e < cnt; e += kT) f(base[start + e]);
+        const int cnt = (int)min(em.chunk, em.n - start);
+        const float* p = base + start;
+        const int ng = cnt >> 2;
+        f32_groups(ng, (reinterpret_cast<uintptr_t>(p) & 15) == 0,
+                   [&](int g) { return p + 4 * g; }, acc);
+        const int e = 4 * ng + (int)threadIdx.x;
+        if (e < cnt) {
+            const float v[1] = {p[e]};
+            acc.add<1>(v);
+        }
     } else {
         const int r0 = (int)ul * em.rpu;
         const int r1 = min(em.rows, r0 + em.rpu);
-        const uint32_t cols = (uint32_t)em.cols;
-        const uint32_t ne = (uint32_t)(r1 - r0) * cols;
-        for (uint32_t e = threadIdx.x; e < ne; e += kT) {
-            const uint32_t r = e / cols, c = e - r * cols;
-            f(base[(int64_t)(r0 + r) * em.ld + c]);
-        }
+        const uint32_t gpr = (uint32_t)em.cols >> 2;
+        const float* p = base + (int64_t)r0 * em.ld;
+        const int64_t ld = em.ld;
+        f32_groups((int)((uint32_t)(r1 - r0) * gpr),
+                   (reinterpret_cast<uintptr_t>(base) & 15) == 0 && (ld & 3) == 0,
+                   [&](int g) {
+                       const uint32_t r = (uint32_t)g / gpr, c = (uint32_t)g - r * gpr;
+                       return p + (int64_t)r * ld + 4 * c;
+                   },
+                   acc);
     }
 }
 
-__global__ __launch_bounds__(kT) void k_f32_max(const EntMat* __restrict__ mats,
-                                                const int64_t* __restrict__ ubeg, int nmat,
-                                                uint32_t* __restrict__ keys,
-                                                unsigned long long* __restrict__ nonfinite) {
+// One pass per work unit: each thread's running sums (F32Acc), moved to the
+// unit's maximum and added in a fixed order.  part[3u .. 3u + 2] = (unit
+// maximum, S, U); S is NaN when the unit holds a NaN or +-inf.
+__global__ __launch_bounds__(kT) void k_f32_part(const EntMat* __restrict__ mats,
+                                                 const int64_t* __restrict__ ubeg, int nmat,
+                                                 double* __restrict__ part,
+                                                 unsigned long long* __restrict__ nonfinite) {
     __shared__ float shf[kT / 64];
-    const int64_t u = blockIdx.x;
-    const int m = find_unit_owner(ubeg, nmat, u);
-    const EntMat em = mats[m];
-    float mx = -INFINITY;
-    uint32_t nbad = 0;
-    f32_unit(em, u - ubeg[m], [&](float v) {
-        if (!isfinite(v)) ++nbad; else mx = fmaxf(mx, v);
-    });
-    if (nbad) atomicAdd(nonfinite, (unsigned long long)nbad);
-    mx = block_maxf(mx, shf);
-    const float bad = block_maxf(nbad ? 1.f : 0.f, shf);
-    if (threadIdx.x == 0) {
-        atomicMax(&keys[2 * m], order_key(mx));
-        if (bad != 0.f) atomicOr(&keys[2 * m + 1], 1u);
-    }
-}
-
-__global__ __launch_bounds__(kT) void k_f32_sum(const EntMat* __restrict__ mats,
-                                                const int64_t* __restrict__ ubeg, int nmat,
-                                                const uint32_t* __restrict__ keys,
-                                                double2* __restrict__ part) {
     __shared__ double shd[kT / 64];
     const int64_t u = blockIdx.x;
     const int m = find_unit_owner(ubeg, nmat, u);
     const EntMat em = mats[m];
-    const double c = (double)key_value(keys[2 * m]);
-    double S = 0.0, U = 0.0;
-    f32_unit(em, u - ubeg[m], [&](float v) {
-        if (isfinite(v)) {
-            const double d = (double)v - c;
-            const double x = exp(d);
-            S += x;
-            U += x * d;
-        }
-    });
-    S = block_sum(S, shd);
-    U = block_sum(U, shd);
-    if (threadIdx.x == 0) part[u] = make_double2(S, U);
+    F32Acc acc;
+    f32_unit(em, u - ubeg[m], acc);
+    if (acc.nbad) atomicAdd(nonfinite, (unsigned long long)acc.nbad);
+    const float c = block_maxf(acc.mx, shf);
+    const float bad = block_maxf(acc.nbad ? 1.f : 0.f, shf);
+    acc.rebase(c);
+    const double S = block_sum(acc.S, shd);
+    const double U = block_sum(acc.U, shd);
+    if (threadIdx.x == 0) {
+        part[3 * u] = (double)c;
+        part[3 * u + 1] = bad != 0.f ? (double)NAN : S;
+        part[3 * u + 2] = U;
+    }
 }
 
+// A matrix's units combined in order, each moved to the matrix maximum c.
 __global__ void k_f32_final(const EntMat* __restrict__ mats, const int64_t* __restrict__ ubeg,
-                            int nmat, const uint32_t* __restrict__ keys,
-                            const double2* __restrict__ part, double* __restrict__ h_mat) {
+                            int nmat, const double* __restrict__ part,
+                            double* __restrict__ h_mat) {
     const int m = blockIdx.x * blockDim.x + threadIdx.x;
     if (m >= nmat) return;
+    double c = -INFINITY;
+    for (int64_t u = ubeg[m]; u < ubeg[m + 1]; ++u) c = fmax(c, part[3 * u]);
     double S = 0.0, U = 0.0;
-    for (int64_t u = ubeg[m]; u < ubeg[m + 1]; ++u) { S += part[u].x; U += part[u].y; }
-    h_mat[mats[m].slot] = keys[2 * m + 1] ? (double)NAN : log(S) - U / S;
+    for (int64_t u = ubeg[m]; u < ubeg[m + 1]; ++u) {
+        const double su = part[3 * u + 1];
+        if (su != 0.0) {
+            const double d = part[3 * u] - c;
+            const double r = exp(d);
+            S += r * su;
+            U += r * (part[3 * u + 2] + su * d);
+        }
+    }
+    h_mat[mats[m].slot] = log(S) - U / S;
 }
 
 // ---------------------------------------------------------------- blocks
@@ -651,16 +728,12 @@ hipError_t ent_hist_final(const EntMat* mats, int nmat, const uint32_t* recs,
 }
 
 hipError_t ent_f32(const EntMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                   uint32_t* keys, double2* part, double* h_mat, unsigned long long* nonfinite,
-                   hipStream_t s) {
+                   double* part, double* h_mat, unsigned long long* nonfinite, hipStream_t s) {
     if (nmat <= 0) return hipSuccess;
-    hipError_t e = fill_u32(keys, 2 * (size_t)nmat, 0u, s);
+    k_f32_part<<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, part, nonfinite);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    k_f32_max<<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, keys, nonfinite);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    k_f32_sum<<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, keys, part);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    k_f32_final<<<dim3((nmat + 63) / 64), dim3(64), 0, s>>>(mats, ubeg, nmat, keys, part, h_mat);
+    k_f32_final<<<dim3((nmat + 63) / 64), dim3(64), 0, s>>>(mats, ubeg, nmat, part, h_mat);
     return hipGetLastError();
 }
 

@@ -39,9 +39,10 @@ hipError_t ent_hist_final(const EntMat* mats, int nmat, const uint32_t* recs,
                           const uint16_t* lists, double* h_mat,
                           unsigned long long* nonfinite, uint32_t* exp_hist,
                           hipStream_t s);
+// fp32: part holds 3 doubles per work unit.
 hipError_t ent_f32(const EntMat* mats, const int64_t* ubeg, int nmat,
-                   int64_t n_units, uint32_t* keys, double2* part,
-                   double* h_mat, unsigned long long* nonfinite, hipStream_t s);
+                   int64_t n_units, double* part, double* h_mat,
+                   unsigned long long* nonfinite, hipStream_t s);
 hipError_t ent_blocks(const int32_t* bmats, const int32_t* bbeg,
                       const double* nsz, const double* h_mat, int n_blocks,
                       double x, double* hb, double* h_block, double* stats,

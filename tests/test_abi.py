@@ -89,6 +89,9 @@ def test_entry_points_reject_before_any_hip_call():
     bid = (ctypes.c_int32 * 1)(0)
     assert lib.ewq_block_entropy(m, 1, bid, 2, 1.0, FAKE, None, None, None, None, FAKE, 1 << 30, None) == 7
     assert lib.ewq_block_entropy(m, 1, None, 0, 1.0, FAKE, None, None, None, None, FAKE, 1 << 30, None) == 10
+    big = (ctypes.c_int32 * 1)(0)
+    assert lib.ewq_block_entropy(m, 1, big, 4097, 1.0, FAKE, None, None, None, None, FAKE, 1 << 30, None) == 10
+    assert lib.ewq_block_entropy_static(m, 1, big, 4097, 1.0, FAKE, None, None, None, None, None) == 10
     assert lib.ewq_block_entropy(m, 0, None, 1, 1.0, FAKE, None, None, None, None, FAKE, 1 << 30, None) == 10
     assert lib.ewq_block_entropy(m, 1, None, 1, 1.0, FAKE, None, None, None, None, FAKE, 16, None) == 6
     assert lib.ewq_block_entropy(m, 1, None, 1, 1.0, FAKE, None, None, None, None, None, 1 << 30, None) == 6

@@ -126,6 +126,27 @@ def test_block_entropy_tiers_order():
     assert out["order"].cpu().tolist() == oracle.ewq_order(hb_ref).tolist()
 
 
+@pytest.mark.parametrize("nb", [1000, 4096])
+def test_block_statistics_many_blocks(nb):
+    """Up to the largest block count (4,096, all kept in LDS by the tier
+    kernel), with ties between blocks (every tenth block a copy of the one
+    before it): entropies, statistics, tiers and order against the oracle."""
+    rng = np.random.default_rng(nb)
+    base = [_rm(8, 16, 1000 + i, std=float(rng.uniform(0.005, 0.05))) for i in range(nb)]
+    for i in range(10, nb, 10):
+        base[i] = base[i - 1].clone()
+    out = woq.ewq_block_entropy(base, list(range(nb)), nb, x=0.5)
+    hb = out["h_block"].cpu().numpy()
+    h_ref = np.array([oracle.matrix_entropy(_np(m)) for m in base])
+    np.testing.assert_allclose(hb, h_ref, rtol=1e-12)
+    mu, sigma, t, tiers = oracle.ewq_tiers(hb, 0.5)
+    np.testing.assert_allclose(out["stats"].cpu().numpy(), [mu, sigma, t], rtol=1e-12)
+    got = out["tier"].cpu().numpy()
+    near = (np.abs(hb - t) <= 1e-12 * abs(t)) | (np.abs(hb - mu) <= 1e-12 * abs(mu))
+    assert np.array_equal(got[~near], tiers[~near])
+    assert out["order"].cpu().tolist() == oracle.ewq_order(hb).tolist()
+
+
 def test_single_block_is_tier_one():
     out = woq.ewq_block_entropy([_rm(8, 16, 1), _rm(8, 16, 2)])
     assert out["tier"].cpu().tolist() == [1]

@@ -25,7 +25,6 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
 constexpr int32_t kMaxMats = 1 << 20;
-constexpr int32_t kMaxBlocks = 4096;
 constexpr int32_t kMaxIters = 4096;
 // Sinkhorn: matrices of one shape class run in one launch per iteration
 // (MI355X's Infinity Cache serves re-reads barely faster than HBM, so there
@@ -126,7 +125,7 @@ struct EntLayout {
     int slots = 0;          // bf16 histograms per batch
     int64_t units_b = 0, units_f = 0;
     size_t tab_b, ubeg_b, tab_f, ubeg_f, bmats, bbeg, nsz, table_end;
-    size_t hb, part_f, recs, lists, total;
+    size_t part_f, recs, lists, total;
 };
 
 // fp32: rows per entropy work unit of a strided matrix (0 for a contiguous
@@ -168,7 +167,6 @@ EntLayout ent_layout(const woq_mat* mats, int32_t n, int32_t n_blocks, int max_s
     L.bbeg = a.take(sizeof(int32_t) * (n_blocks + 1));
     L.nsz = a.take(sizeof(double) * n);
     L.table_end = a.end();
-    L.hb = a.take(sizeof(double) * n_blocks);
     L.part_f = a.take(sizeof(double) * 3 * L.units_f);
     L.slots = std::min(L.nb, max_slots);
     L.recs = a.take(sizeof(uint32_t) * kEntRecWords * (size_t)L.slots);
@@ -598,7 +596,7 @@ int32_t ent_run(const EntLayout& L, const woq_mat* mats, int32_t n_mats, const i
         WOQ_HIP(ent_f32(at<EntMat>(ws, L.tab_f), at<int64_t>(ws, L.ubeg_f), L.nf, L.units_f,
                         at<double>(ws, L.part_f), h_mat, nf, stream));
     WOQ_HIP(ent_blocks(at<int32_t>(ws, L.bmats), at<int32_t>(ws, L.bbeg), at<double>(ws, L.nsz),
-                       h_mat, n_blocks, x, at<double>(ws, L.hb), h_block, stats, tier, order,
+                       h_mat, n_blocks, x, h_block, stats, tier, order,
                        stream));
     return WOQ_OK;
 }

@@ -587,12 +587,12 @@ __global__ __launch_bounds__(kBT) void k_blocks(const int32_t* __restrict__ bmat
                                                const int32_t* __restrict__ bbeg,
                                                const double* __restrict__ nsz,
                                                const double* __restrict__ h_mat, int nb,
-                                               double x, double* __restrict__ hb,
-                                               double* __restrict__ h_block,
+                                               double x, double* __restrict__ h_block,
                                                double* __restrict__ stats,
                                                int32_t* __restrict__ tier,
                                                int32_t* __restrict__ order) {
     __shared__ double shd[kBT / 64];
+    __shared__ double H[kMaxBlocks];   // the block entropies (32 KB)
     // one wave per block: lane j takes the block's matrices j, j + 64, ...,
     // then the lanes' sums are combined in a fixed order
     const int lane = threadIdx.x & 63;
@@ -607,26 +607,26 @@ __global__ __launch_bounds__(kBT) void k_blocks(const int32_t* __restrict__ bmat
         den = wave_sum(den);
         if (lane == 0) {
             const double h = num / den;
-            hb[b] = h;
+            H[b] = h;
             if (h_block) h_block[b] = h;
         }
     }
     __syncthreads();
     double acc = 0.0;
-    for (int b = threadIdx.x; b < nb; b += kBT) acc += hb[b];
+    for (int b = threadIdx.x; b < nb; b += kBT) acc += H[b];
     const double mu = block_sum<kBT>(acc, shd) / nb;
     acc = 0.0;
-    for (int b = threadIdx.x; b < nb; b += kBT) { const double d = hb[b] - mu; acc += d * d; }
+    for (int b = threadIdx.x; b < nb; b += kBT) { const double d = H[b] - mu; acc += d * d; }
     const double sigma = sqrt(block_sum<kBT>(acc, shd) / nb);
     const double t = mu - x * sigma;
     if (stats && threadIdx.x == 0) { stats[0] = mu; stats[1] = sigma; stats[2] = t; }
     for (int b = threadIdx.x; b < nb; b += kBT) {
-        const double h = hb[b];
+        const double h = H[b];
         if (tier) tier[b] = (h <= t) ? 1 : ((h < mu) ? 2 : 3);
         if (order) {
             int rank = 0;
             for (int o = 0; o < nb; ++o) {
-                const double g = hb[o];
+                const double g = H[o];
                 rank += (g < h) || (g == h && o < b);
             }
             order[rank] = b;
@@ -691,18 +691,22 @@ hipError_t fill_f32(float* p, size_t n, float v, hipStream_t s) {
 hipError_t ent_hist_bf16(const EntMat* mats, const int64_t* vbeg, int nmat, int64_t n_vec,
                          uint32_t* recs, uint16_t* lists, hipStream_t s) {
     if (n_vec <= 0) return hipSuccess;
-    // kHistWaves x the workgroups of k_hist_bf16 the device holds at once
-    // (measured on the 8B and MoE stacks: 4 beat 1, 2 and 8 - shares small
-    // enough that the last ones to finish leave little idle, large enough
-    // that a matrix segment's clearing and flush stay rare)
+    // Workgroups: one per 1 MiB of weights, at least the number the device
+    // holds at once and at most kHistWaves times that (measured on the 8B
+    // and MoE stacks: 4 beat 1, 2 and 8 - shares small enough that the last
+    // ones to finish leave little idle, large enough that a matrix
+    // segment's clearing and flush stay rare; on one 8B block, 436 MB, one
+    // round of 340 KB shares takes 0.138 ms against 0.170 with four rounds
+    // of 85 KB)
     constexpr int kHistWaves = 4;
+    constexpr int64_t kHistShareVecs = (int64_t(1) << 20) / 16;
     static std::atomic<int> resident[64];   // per device, 0 until first looked up
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    int g_max = resident[dev].load(std::memory_order_relaxed);
-    if (g_max == 0) {
+    int g_res = resident[dev].load(std::memory_order_relaxed);
+    if (g_res == 0) {
         int per_cu = 0, cus = 0;
         if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
                  &per_cu, reinterpret_cast<const void*>(k_hist_bf16), kT, 0)) != hipSuccess)
@@ -710,10 +714,13 @@ hipError_t ent_hist_bf16(const EntMat* mats, const int64_t* vbeg, int nmat, int6
         if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) !=
             hipSuccess)
             return e;
-        g_max = kHistWaves * std::max(1, per_cu) * std::max(1, cus);
-        resident[dev].store(g_max, std::memory_order_relaxed);
+        g_res = std::max(1, per_cu) * std::max(1, cus);
+        resident[dev].store(g_res, std::memory_order_relaxed);
     }
-    const int64_t g = std::min<int64_t>(g_max, (n_vec + kT - 1) / kT);
+    const int64_t by_bytes = (n_vec + kHistShareVecs - 1) / kHistShareVecs;
+    const int64_t g_want =
+        std::min<int64_t>((int64_t)kHistWaves * g_res, std::max<int64_t>(g_res, by_bytes));
+    const int64_t g = std::min<int64_t>(g_want, (n_vec + kT - 1) / kT);
     k_hist_bf16<<<dim3((unsigned)g), dim3(kT), 0, s>>>(mats, vbeg, nmat, recs, lists);
     return hipGetLastError();
 }
@@ -738,10 +745,10 @@ hipError_t ent_f32(const EntMat* mats, const int64_t* ubeg, int nmat, int64_t n_
 }
 
 hipError_t ent_blocks(const int32_t* bmats, const int32_t* bbeg, const double* nsz,
-                      const double* h_mat, int n_blocks, double x, double* hb,
+                      const double* h_mat, int n_blocks, double x,
                       double* h_block, double* stats, int32_t* tier, int32_t* order,
                       hipStream_t s) {
-    k_blocks<<<dim3(1), dim3(kBT), 0, s>>>(bmats, bbeg, nsz, h_mat, n_blocks, x, hb, h_block,
+    k_blocks<<<dim3(1), dim3(kBT), 0, s>>>(bmats, bbeg, nsz, h_mat, n_blocks, x, h_block,
                                            stats, tier, order);
     return hipGetLastError();
 }

@@ -43,9 +43,12 @@ hipError_t ent_hist_final(const EntMat* mats, int nmat, const uint32_t* recs,
 hipError_t ent_f32(const EntMat* mats, const int64_t* ubeg, int nmat,
                    int64_t n_units, double* part, double* h_mat,
                    unsigned long long* nonfinite, hipStream_t s);
+// Blocks per entropy call (the entry points reject more); the tier kernel
+// keeps every block entropy in LDS.
+constexpr int kMaxBlocks = 4096;
 hipError_t ent_blocks(const int32_t* bmats, const int32_t* bbeg,
                       const double* nsz, const double* h_mat, int n_blocks,
-                      double x, double* hb, double* h_block, double* stats,
+                      double x, double* h_block, double* stats,
                       int32_t* tier, int32_t* order, hipStream_t s);
 
 // ---- Sinkhorn ([SINQ])

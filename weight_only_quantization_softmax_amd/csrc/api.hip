@@ -77,16 +77,19 @@ int32_t check_mats(const woq_mat* mats, int32_t n, bool cols8) {
 // being captured into a graph the bytes travel in kernel arguments (a
 // captured copy from this pageable, short-lived buffer would be replayed
 // after the buffer is gone); otherwise one asynchronous copy.
-hipError_t stage_tables(void* ws, const std::vector<char>& host, size_t end, hipStream_t s) {
-    if (end <= WOQ_WS_HEAD) return hipSuccess;
+// zero_head: the copy starts at byte 0, so the status head is cleared by it
+// (host[0, WOQ_WS_HEAD) holds zeros) instead of by a kernel of its own.
+hipError_t stage_tables(void* ws, const std::vector<char>& host, size_t end, hipStream_t s,
+                        bool zero_head = false) {
+    const size_t from = zero_head ? 0 : WOQ_WS_HEAD;
+    if (end <= from) return hipSuccess;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     const hipError_t e = hipStreamIsCapturing(s, &cs);
     if (e != hipSuccess) return e;
     if (cs != hipStreamCaptureStatusNone)
-        return stage_bytes(static_cast<char*>(ws) + WOQ_WS_HEAD, host.data() + WOQ_WS_HEAD,
-                           end - WOQ_WS_HEAD, s);
-    return hipMemcpyAsync(static_cast<char*>(ws) + WOQ_WS_HEAD, host.data() + WOQ_WS_HEAD,
-                          end - WOQ_WS_HEAD, hipMemcpyHostToDevice, s);
+        return stage_bytes(static_cast<char*>(ws) + from, host.data() + from, end - from, s);
+    return hipMemcpyAsync(static_cast<char*>(ws) + from, host.data() + from, end - from,
+                          hipMemcpyHostToDevice, s);
 }
 
 // The call's non-finite weight counter (uint64 at byte 0 of the workspace).
@@ -576,10 +579,8 @@ int32_t ent_run(const EntLayout& L, const woq_mat* mats, int32_t n_mats, const i
         nsz[i] = (double)elems(mats[i]);
     }
 
-    WOQ_HIP(stage_tables(ws, host, L.table_end, stream));
+    WOQ_HIP(stage_tables(ws, host, L.table_end, stream, true));   // and the zeroed head
     unsigned long long* nf = nonfinite_counter(ws);
-    WOQ_HIP(fill_u32(reinterpret_cast<uint32_t*>(nf), 2, 0u, stream));
-    if (exp_hist) WOQ_HIP(fill_u32(exp_hist, (size_t)n_mats * 256, 0u, stream));
     const EntMat* dtb = at<EntMat>(ws, L.tab_b);
     const int64_t* dub = at<int64_t>(ws, L.ubeg_b);
     uint32_t* recs = at<uint32_t>(ws, L.recs);
@@ -594,7 +595,7 @@ int32_t ent_run(const EntLayout& L, const woq_mat* mats, int32_t n_mats, const i
     }
     if (L.nf)
         WOQ_HIP(ent_f32(at<EntMat>(ws, L.tab_f), at<int64_t>(ws, L.ubeg_f), L.nf, L.units_f,
-                        at<double>(ws, L.part_f), h_mat, nf, stream));
+                        at<double>(ws, L.part_f), h_mat, nf, exp_hist, stream));
     WOQ_HIP(ent_blocks(at<int32_t>(ws, L.bmats), at<int32_t>(ws, L.bbeg), at<double>(ws, L.nsz),
                        h_mat, n_blocks, x, h_block, stats, tier, order,
                        stream));
@@ -753,8 +754,8 @@ int32_t sinq_balance_ex(const woq_mat* mats, int32_t n_mats, int32_t iters, int3
     if ((st = check_ws(ws, ws_bytes, L.total))) return st;
 
     unsigned long long* nf = nonfinite_counter(ws);
-    WOQ_HIP(fill_u32(reinterpret_cast<uint32_t*>(nf), 2, 0u, stream));
     if (iters == 0) {  // no weight is read
+        WOQ_HIP(fill_u32(reinterpret_cast<uint32_t*>(nf), 2, 0u, stream));
         for (int32_t i = 0; i < n_mats; ++i) {
             WOQ_HIP(fill_f32(row_scale[i], (size_t)mats[i].rows, 1.0f, stream));
             WOQ_HIP(fill_f32(col_scale[i], (size_t)mats[i].cols, 1.0f, stream));
@@ -794,7 +795,7 @@ int32_t sinq_balance_ex(const woq_mat* mats, int32_t n_mats, int32_t iters, int3
             gc[k + 1] = gc[k] + ((g.sh.mode == 1 && sm.n_strips == 1) ? 0 : cdiv(sm.cols, rcols));
         }
     }
-    WOQ_HIP(stage_tables(ws, host, L.table_end, stream));
+    WOQ_HIP(stage_tables(ws, host, L.table_end, stream, true));   // and the zeroed head
     const SinqMat* dt = at<SinqMat>(ws, L.tab);
     const int64_t* dsb = at<int64_t>(ws, L.sbeg);
     const int64_t* dcb = at<int64_t>(ws, L.cbeg);
@@ -889,7 +890,8 @@ int32_t quant_impl(const woq_mat* mats, int32_t n_mats, const float* const* row_
         ++st_.count;
         st_.units = ub[uoff + st_.count];
     }
-    WOQ_HIP(stage_tables(ws, host, L.table_end, stream));
+    // the code-book table, last in the tables, only when a book is used
+    WOQ_HIP(stage_tables(ws, host, levels ? L.table_end : L.book, stream));
     if (L.nseg) WOQ_HIP(recip(at<RecipSeg>(ws, L.segs), at<int64_t>(ws, L.ubeg_s), L.nseg, us[L.nseg], stream));
     for (const Set& st_ : sets) {
         const QMat* dt = at<QMat>(ws, L.tab_b) + st_.first;
@@ -954,7 +956,8 @@ int32_t dequant_impl(const woq_mat* out, int32_t n_mats, const uint8_t* const* c
         if (m.dtype == WOQ_BF16) { tb[ib] = q; ub[ib + 1] = ub[ib] + u; ++ib; }
         else { tf[jf] = q; uf[jf + 1] = uf[jf] + u; ++jf; }
     }
-    WOQ_HIP(stage_tables(ws, host, L.table_end, stream));
+    // the code-book table, last in the tables, only when a book is used
+    WOQ_HIP(stage_tables(ws, host, levels ? L.table_end : L.book, stream));
     if (L.nb) WOQ_HIP(dequant(at<QMat>(ws, L.tab_b), at<int64_t>(ws, L.ubeg_b), L.nb, ub[L.nb], WOQ_BF16, bits, dbook, stream));
     if (L.nf) WOQ_HIP(dequant(at<QMat>(ws, L.tab_f), at<int64_t>(ws, L.ubeg_f), L.nf, uf[L.nf], WOQ_F32, bits, dbook, stream));
     return WOQ_OK;

@@ -560,11 +560,17 @@ __global__ __launch_bounds__(kT) void k_f32_part(const EntMat* __restrict__ mats
 }
 
 // A matrix's units combined in order, each moved to the matrix maximum c.
+// exp_hist (may be NULL): the matrix's row of exponent counts is zeroed (the
+// counts are kept for bf16 matrices only).
 __global__ void k_f32_final(const EntMat* __restrict__ mats, const int64_t* __restrict__ ubeg,
                             int nmat, const double* __restrict__ part,
-                            double* __restrict__ h_mat) {
+                            double* __restrict__ h_mat, uint32_t* __restrict__ exp_hist) {
     const int m = blockIdx.x * blockDim.x + threadIdx.x;
     if (m >= nmat) return;
+    if (exp_hist) {
+        uint32_t* row = exp_hist + (size_t)mats[m].slot * 256;
+        for (int i = 0; i < 256; i += 4) gstore<u32x4>(row + i, u32x4{0u, 0u, 0u, 0u});
+    }
     double c = -INFINITY;
     for (int64_t u = ubeg[m]; u < ubeg[m + 1]; ++u) c = fmax(c, part[3 * u]);
     double S = 0.0, U = 0.0;
@@ -735,12 +741,14 @@ hipError_t ent_hist_final(const EntMat* mats, int nmat, const uint32_t* recs,
 }
 
 hipError_t ent_f32(const EntMat* mats, const int64_t* ubeg, int nmat, int64_t n_units,
-                   double* part, double* h_mat, unsigned long long* nonfinite, hipStream_t s) {
+                   double* part, double* h_mat, unsigned long long* nonfinite,
+                   uint32_t* exp_hist, hipStream_t s) {
     if (nmat <= 0) return hipSuccess;
     k_f32_part<<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, part, nonfinite);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    k_f32_final<<<dim3((nmat + 63) / 64), dim3(64), 0, s>>>(mats, ubeg, nmat, part, h_mat);
+    k_f32_final<<<dim3((nmat + 63) / 64), dim3(64), 0, s>>>(mats, ubeg, nmat, part, h_mat,
+                                                            exp_hist);
     return hipGetLastError();
 }
 

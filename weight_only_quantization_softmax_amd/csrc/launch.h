@@ -23,7 +23,7 @@ constexpr int kEntListCap = 8192;
 hipError_t fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 // Host bytes to device memory through kernel arguments, kStageChunk bytes
 // per launch (n a multiple of 4): safe to capture into a graph.
-constexpr int kStageChunk = 1024;
+constexpr int kStageChunk = 2048;
 hipError_t stage_bytes(void* dst, const void* src, size_t n, hipStream_t s);
 hipError_t fill_f32(float* p, size_t n, float v, hipStream_t s);
 
@@ -39,10 +39,11 @@ hipError_t ent_hist_final(const EntMat* mats, int nmat, const uint32_t* recs,
                           const uint16_t* lists, double* h_mat,
                           unsigned long long* nonfinite, uint32_t* exp_hist,
                           hipStream_t s);
-// fp32: part holds 3 doubles per work unit.
+// fp32: part holds 3 doubles per work unit; exp_hist (may be NULL): the
+// matrices' rows of exponent counts are zeroed.
 hipError_t ent_f32(const EntMat* mats, const int64_t* ubeg, int nmat,
                    int64_t n_units, double* part, double* h_mat,
-                   unsigned long long* nonfinite, hipStream_t s);
+                   unsigned long long* nonfinite, uint32_t* exp_hist, hipStream_t s);
 // Blocks per entropy call (the entry points reject more); the tier kernel
 // keeps every block entropy in LDS.
 constexpr int kMaxBlocks = 4096;

@@ -176,6 +176,20 @@ def test_sinq_matches_oracle(iters):
         assert np.max(np.abs(t[i].cpu().numpy() / t_ref - 1)) < 2e-5
 
 
+@pytest.mark.parametrize("shared", [False, True])
+def test_sinq_plan_of_several_rounds(shared):
+    """More same-shape wave-form matrices than the GPU holds workgroups at
+    once (600 x 64 x 512 bf16: one workgroup sweeps each whole, except the
+    last round's matrices, cut in two strips and combined by the reduction
+    kernel); the first, middle and last matrices against the oracle."""
+    mats = [_rm(64, 512, 3000 + i, std=0.02 * (1 + i % 5)) for i in range(600)]
+    s, t = woq.sinq_balance(mats, 6, shared=shared)
+    for i in list(range(0, 600, 37)) + list(range(560, 600)):
+        s_ref, t_ref = oracle.sinkhorn_std(_np(mats[i]), 6)
+        assert np.max(np.abs(s[i].cpu().numpy() / s_ref - 1)) < 2e-5, i
+        assert np.max(np.abs(t[i].cpu().numpy() / t_ref - 1)) < 2e-5, i
+
+
 def test_sinq_degenerate_lines():
     w = _rm(64, 256, 7).float()
     w[3, :] = 0

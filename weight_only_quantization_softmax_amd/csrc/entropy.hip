@@ -428,12 +428,37 @@ __global__ __launch_bounds__(kT) void k_hist_final(const EntMat* __restrict__ ma
 
 // ---------------------------------------------------------------- fp32
 
+// exp(x) for x <= 0 in fp64, by Tang's table-driven method (P. T. P. Tang,
+// ACM TOMS 15(2), 1989): x = (64 M + j) ln2 / 64 + r with |r| <= ln2 / 128,
+// exp(x) = 2^M 2^(j/64) exp(r), exp(r) - 1 by its Taylor series to r^5
+// (the next term is below 4e-17 relative), 2^(j/64) from a 64-entry table
+// (tab, in LDS).  ln2 / 64 is split into a 36-bit head, exact when
+// multiplied by |n| < 2^17, and a tail.  x is clamped to -746 first (exp
+// below that is 0 in fp64), so n stays small.  About 1 ulp from exp.
+__device__ __forceinline__ double exp_nonpos(double x, const double* tab) {
+    constexpr double kInvLn2x64 = 0x1.71547652b82fep+6;    // 64 / ln 2
+    constexpr double kLn2d64Hi = 0x1.62e42fefa0000p-7;     // ln 2 / 64, head
+    constexpr double kLn2d64Lo = 0x1.cf79abc9e3b3ap-46;    // ln 2 / 64, tail
+    x = fmax(x, -746.0);
+    const double n = rint(x * kInvLn2x64);
+    const int ni = (int)n;
+    const double r = fma(-n, kLn2d64Lo, fma(-n, kLn2d64Hi, x));
+    double p = fma(r, 1.0 / 120.0, 1.0 / 24.0);
+    p = fma(p, r, 1.0 / 6.0);
+    p = fma(p, r, 0.5);
+    p = fma(p, r, 1.0);
+    p *= r;
+    const double t = tab[ni & 63];
+    return ldexp(fma(t, p, t), ni >> 6);
+}
+
 // Running sums of one thread over fp32 values: the largest finite value mx
 // met so far, S = sum exp(w - mx) and U = sum exp(w - mx) (w - mx) over the
 // finite values, nbad the NaN / inf values.  Values arrive in batches: the
 // batch's maximum first, the sums moved to it when it is larger
 // (exp(w - m') = exp(w - m) exp(m - m')), then one exponential per value.
 struct F32Acc {
+    const double* tab;   // 2^(j/64), j < 64, for exp_nonpos
     float mx = -INFINITY;
     double S = 0.0, U = 0.0;
     uint32_t nbad = 0;
@@ -441,7 +466,7 @@ struct F32Acc {
     __device__ __forceinline__ void rebase(float m) {
         if (S != 0.0) {
             const double d = (double)mx - (double)m;   // <= 0
-            const double r = exp(d);
+            const double r = exp_nonpos(d, tab);
             U = r * (U + S * d);
             S = r * S;
         }
@@ -460,7 +485,7 @@ struct F32Acc {
         for (int i = 0; i < K; ++i) {
             if (isfinite(v[i])) {
                 const double d = (double)v[i] - (double)mx;
-                const double x = exp(d);
+                const double x = exp_nonpos(d, tab);
                 S += x;
                 U += x * d;
             }
@@ -541,10 +566,14 @@ __global__ __launch_bounds__(kT) void k_f32_part(const EntMat* __restrict__ mats
                                                  unsigned long long* __restrict__ nonfinite) {
     __shared__ float shf[kT / 64];
     __shared__ double shd[kT / 64];
+    __shared__ double tab[64];
+    if (threadIdx.x < 64) tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+    __syncthreads();
     const int64_t u = blockIdx.x;
     const int m = find_unit_owner(ubeg, nmat, u);
     const EntMat em = mats[m];
     F32Acc acc;
+    acc.tab = tab;
     f32_unit(em, u - ubeg[m], acc);
     if (acc.nbad) atomicAdd(nonfinite, (unsigned long long)acc.nbad);
     const float c = block_maxf(acc.mx, shf);

@@ -588,22 +588,26 @@ __global__ __launch_bounds__(kT) void k_f32_part(const EntMat* __restrict__ mats
     }
 }
 
-// A matrix's units combined in order, each moved to the matrix maximum c.
-// exp_hist (may be NULL): the matrix's row of exponent counts is zeroed (the
-// counts are kept for bf16 matrices only).
-__global__ void k_f32_final(const EntMat* __restrict__ mats, const int64_t* __restrict__ ubeg,
-                            int nmat, const double* __restrict__ part,
-                            double* __restrict__ h_mat, uint32_t* __restrict__ exp_hist) {
-    const int m = blockIdx.x * blockDim.x + threadIdx.x;
-    if (m >= nmat) return;
-    if (exp_hist) {
-        uint32_t* row = exp_hist + (size_t)mats[m].slot * 256;
-        for (int i = 0; i < 256; i += 4) gstore<u32x4>(row + i, u32x4{0u, 0u, 0u, 0u});
-    }
+// One wave per matrix: lane l takes the matrix's units l, l + 64, ... in
+// order, each moved to the matrix maximum c, and the lanes' sums are added
+// in a fixed order.  exp_hist (may be NULL): the matrix's row of exponent
+// counts is zeroed (the counts are kept for bf16 matrices only).
+__global__ __launch_bounds__(64) void k_f32_final(const EntMat* __restrict__ mats,
+                                                  const int64_t* __restrict__ ubeg, int nmat,
+                                                  const double* __restrict__ part,
+                                                  double* __restrict__ h_mat,
+                                                  uint32_t* __restrict__ exp_hist) {
+    const int m = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int64_t u0 = ubeg[m], u1 = ubeg[m + 1];
+    const int slot = mats[m].slot;
+    if (exp_hist) gstore<u32x4>(exp_hist + (size_t)slot * 256 + 4 * lane, u32x4{0u, 0u, 0u, 0u});
     double c = -INFINITY;
-    for (int64_t u = ubeg[m]; u < ubeg[m + 1]; ++u) c = fmax(c, part[3 * u]);
+    for (int64_t u = u0 + lane; u < u1; u += 64) c = fmax(c, part[3 * u]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) c = fmax(c, __shfl_xor(c, o, 64));
     double S = 0.0, U = 0.0;
-    for (int64_t u = ubeg[m]; u < ubeg[m + 1]; ++u) {
+    for (int64_t u = u0 + lane; u < u1; u += 64) {
         const double su = part[3 * u + 1];
         if (su != 0.0) {
             const double d = part[3 * u] - c;
@@ -612,7 +616,9 @@ __global__ void k_f32_final(const EntMat* __restrict__ mats, const int64_t* __re
             U += r * (part[3 * u + 2] + su * d);
         }
     }
-    h_mat[mats[m].slot] = log(S) - U / S;
+    S = wave_sum(S);
+    U = wave_sum(U);
+    if (lane == 0) h_mat[slot] = log(S) - U / S;
 }
 
 // ---------------------------------------------------------------- blocks
@@ -776,8 +782,7 @@ hipError_t ent_f32(const EntMat* mats, const int64_t* ubeg, int nmat, int64_t n_
     k_f32_part<<<dim3((unsigned)n_units), dim3(kT), 0, s>>>(mats, ubeg, nmat, part, nonfinite);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    k_f32_final<<<dim3((nmat + 63) / 64), dim3(64), 0, s>>>(mats, ubeg, nmat, part, h_mat,
-                                                            exp_hist);
+    k_f32_final<<<dim3((unsigned)nmat), dim3(64), 0, s>>>(mats, ubeg, nmat, part, h_mat, exp_hist);
     return hipGetLastError();
 }
 

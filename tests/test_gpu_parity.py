@@ -176,13 +176,15 @@ def test_sinq_matches_oracle(iters):
         assert np.max(np.abs(t[i].cpu().numpy() / t_ref - 1)) < 2e-5
 
 
+@pytest.mark.parametrize("shape", [(64, 512), (16, 8192)])
 @pytest.mark.parametrize("shared", [False, True])
-def test_sinq_plan_of_several_rounds(shared):
-    """More same-shape wave-form matrices than the GPU holds workgroups at
-    once (600 x 64 x 512 bf16: one workgroup sweeps each whole, except the
-    last round's matrices, cut in two strips and combined by the reduction
-    kernel); the first, middle and last matrices against the oracle."""
-    mats = [_rm(64, 512, 3000 + i, std=0.02 * (1 + i % 5)) for i in range(600)]
+def test_sinq_plan_of_several_rounds(shared, shape):
+    """More same-shape matrices than the GPU holds workgroups at once (600
+    of them, wave form and workgroup form: one workgroup sweeps each whole,
+    except the last round's matrices, swept in strips of half the height and
+    combined by the reduction kernel); the first, middle and last matrices
+    against the oracle."""
+    mats = [_rm(*shape, 3000 + i, std=0.02 * (1 + i % 5)) for i in range(600)]
     s, t = woq.sinq_balance(mats, 6, shared=shared)
     for i in list(range(0, 600, 37)) + list(range(560, 600)):
         s_ref, t_ref = oracle.sinkhorn_std(_np(mats[i]), 6)

@@ -279,22 +279,24 @@ SinqLayout sinq_layout(const woq_mat* mats, int32_t n, bool shared) {
             g.max_strips = std::max<int>(g.max_strips, L.n_strips[k]);
             g.cols_max = std::max<int>(g.cols_max, (int)m.cols);
         }
-        // A wave-form plan of several rounds (more workgroups than cap) ends
-        // in a partial round.  The matrices dispatched in it (the last
-        // n_wg mod cap, in table order), if swept whole, are cut in two
-        // strips, so the last round runs half-size pieces (MoE stack:
-        // 85.7 -> 84.5 ms per pass; three strips measured the same).
-        if (g.sh.mode == 1 && g.n_strips > cap) {
+        // A plan of several rounds (more workgroups than cap) ends in a
+        // partial round.  The matrices dispatched in it (the last n_wg mod
+        // cap workgroups, in table order) get strips of half the height, so
+        // the last round runs half-size pieces (MoE stack: 85.7 -> 84.5 ms
+        // per pass; 70B stack: 714-718 -> 702 ms; quarter-height strips, or
+        // the last round and a half, measured the same or slower).
+        if (g.n_strips > cap) {
             int64_t rem = g.n_strips % cap;
             for (int k = q - 1; k >= p && rem > 0; --k) {
                 rem -= L.n_strips[k];
-                if (L.n_strips[k] != 1) continue;
                 const woq_mat& m = mats[idx[k]];
-                const int64_t srows = cdiv(m.rows, 2 * (int64_t)per_wg);
+                const int64_t h = L.strip_rows[k] / R;   // register tiles per strip
+                if (h < 2) continue;
+                const int64_t srows = cdiv(h, 2) * R;
                 const int32_t ns = (int32_t)cdiv(m.rows, srows * per_wg);
+                g.n_strips += ns - L.n_strips[k];
                 L.strip_rows[k] = (int32_t)srows;
                 L.n_strips[k] = ns;
-                g.n_strips += ns - 1;
                 g.max_strips = std::max<int>(g.max_strips, ns);
             }
         }

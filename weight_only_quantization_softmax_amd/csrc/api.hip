@@ -227,8 +227,8 @@ SinqLayout sinq_layout(const woq_mat* mats, int32_t n, bool shared) {
         // waves per CU):
         //  A  one common strip height, the smallest for which every
         //     workgroup is resident at once (a single round);
-        //  B  workgroups of about total / (4 cap) rows (at least 64), run in
-        //     several rounds and scheduled as slots free up - better when
+        //  B  workgroups of about total / (rounds x cap) rows (at least 64),
+        //     run in several rounds and scheduled as slots free up - better when
         //     the matrices are about as many as the slots, where plan A
         //     must give a whole large matrix to one workgroup.
         const int R = g.sh.mode == 1 ? 1 : sinq_tile_rows(g.dtype, g.sh.nv);
@@ -266,7 +266,11 @@ SinqLayout sinq_layout(const woq_mat* mats, int32_t n, bool shared) {
             plan_cost(mid, &n_wg);
             if (n_wg <= cap) hi = mid; else lo = mid + 1;
         }
-        const int64_t t_b = std::max<int64_t>(cdiv(64, unit), cdiv(total_rows, 4 * cap * unit));
+        // plan B's rounds: 4 for the wave form (MoE stack: 3, 4, 6 rounds gave
+        // 85.8, 84.0, 85.2 ms), 6 for the workgroup form (70B stack: 2, 4, 6,
+        // 8 rounds gave 754, 712, 698-702, 702-703 ms)
+        const int64_t rounds = g.sh.mode == 0 ? 6 : 4;
+        const int64_t t_b = std::max<int64_t>(cdiv(64, unit), cdiv(total_rows, rounds * cap * unit));
         int64_t n_a = 0, n_b = 0;
         const int64_t cost_a = plan_cost(lo, &n_a), cost_b = plan_cost(t_b, &n_b);
         const int64_t t_sel = cost_b < cost_a ? t_b : lo;

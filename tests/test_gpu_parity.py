@@ -310,6 +310,8 @@ QUANT_CASES = [  # (rows, cols, bits, group, dtype)
     # wave, lanes with no vector); two 8192-column groups per row (workgroup)
     (13, 2560, 4, 64, torch.bfloat16), (9, 6144, 4, 128, torch.bfloat16),
     (10, 1800, 4, 600, torch.bfloat16), (4, 16384, 4, 8192, torch.bfloat16),
+    # 3-bit rows whose codes start at odd byte offsets, ragged tiles
+    (7, 136, 3, 8, torch.bfloat16), (5, 2600, 3, 8, torch.float32), (6, 4104, 3, 8, torch.bfloat16),
 ]
 
 

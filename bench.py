@@ -403,20 +403,22 @@ def _probe():
     lib.probe_read.argtypes = [vp, sz, i32, i32, i32, vp, vp]
     lib.probe_copy.argtypes = [vp, vp, sz, i32, vp]
     lib.probe_fma.argtypes = [vp, i32, i32, vp]
-    lib.probe_barrier.argtypes = [vp, vp, i32, i32, i32, ctypes.c_uint, vp]
+    lib.probe_barrier.argtypes = [vp, vp, i32, i32, i32, ctypes.c_uint, i32, vp]
     for f in (lib.probe_read, lib.probe_copy, lib.probe_fma, lib.probe_barrier):
         f.restype = i32
     return lib
 
 
-def barrier_us(lib, grid, team, n_bar=2000, spin_limit=1 << 22):
+def barrier_us(lib, grid, team, mode=0, n_bar=2000, spin_limit=1 << 22):
     """Microseconds per barrier among teams of `team` workgroups in one
     cooperative launch of `grid` workgroups (n_bar barriers minus one,
-    HIP events); None if a wait gave up."""
+    HIP events); None if a wait gave up.  mode 0: every poll an acquire
+    load; 1: relaxed polls and one acquire fence; 2: as 1, arrivals on eight
+    sub-counters first."""
     import torch
     stream = torch.cuda.current_stream()
     sh = ctypes_stream(stream)
-    cnt = torch.zeros((grid // team) * 64, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((grid // team) * 9 * 64, dtype=torch.int32, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
 
     def run(n):
@@ -424,7 +426,7 @@ def barrier_us(lib, grid, team, n_bar=2000, spin_limit=1 << 22):
         err.zero_()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        rc = lib.probe_barrier(cnt.data_ptr(), err.data_ptr(), n, grid, team, spin_limit, sh)
+        rc = lib.probe_barrier(cnt.data_ptr(), err.data_ptr(), n, grid, team, spin_limit, mode, sh)
         e1.record(stream)
         e1.synchronize()
         if rc != 0:
@@ -502,6 +504,8 @@ def ceilings():
     res["l2_reread_16MiB_x64"] = probe_rate(lib, "read", 16 << 20, passes=64, bufs=(a, None))
     res["fp32_fma"] = probe_rate(lib, "fma", 4096, grid=4096)
     res["grid_barrier_us_512wg"] = barrier_us(lib, 512, 512)
+    res["grid_barrier_us_512wg_relaxed_polls"] = barrier_us(lib, 512, 512, mode=1)
+    res["grid_barrier_us_512wg_two_level"] = barrier_us(lib, 512, 512, mode=2)
     del big
     torch.cuda.synchronize()
     return res
@@ -534,10 +538,14 @@ def ceilings_sweep():
                                                             bufs=(big[:1 << 30], big[1 << 30:2 << 30]))}),
               flush=True)
     print(json.dumps({"fp32_fma": probe_rate(lib, "fma", 8192, grid=8192)}), flush=True)
-    for grid, team in ((256, 256), (512, 512), (1024, 1024), (2048, 2048), (512, 128), (512, 64),
-                       (512, 32), (512, 8)):
-        print(json.dumps({"barrier_grid": grid, "team": team, "us": barrier_us(lib, grid, team)}),
-              flush=True)
+    for grid, team in ((16, 16), (32, 32), (64, 64), (256, 256), (512, 512), (1024, 1024),
+                       (2048, 2048), (512, 128), (512, 64), (512, 32), (512, 8)):
+        r = {"barrier_grid": grid, "team": team}
+        for mode in (0, 1, 2):
+            if mode == 2 and team % 8:
+                continue
+            r[f"us_mode{mode}"] = barrier_us(lib, grid, team, mode=mode)
+        print(json.dumps(r), flush=True)
     return 0
 
 

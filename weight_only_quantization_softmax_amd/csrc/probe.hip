@@ -17,17 +17,20 @@
 //       `iters` dependent-chain steps of 8 independent fp32 FMAs per lane
 //       (no packed fp32): the plain VALU issue rate.  out: device
 //       float[grid * 256] (written).
-//   probe_barrier(counters, err, n_bar, grid, team, spin_limit, stream)
+//   probe_barrier(counters, err, n_bar, grid, team, spin_limit, mode, stream)
 //       `n_bar` barriers among the workgroups of one cooperative launch of
 //       `grid` workgroups of 256 threads: teams of `team` workgroups
 //       (team = grid: a grid-wide barrier).  Teams are strided: workgroup b
 //       is in team b mod (grid / team), so when grid / team is a multiple of
 //       8 and workgroups are dealt to the 8 XCDs in turn, each team sits on
 //       one XCD.  Each arrival is an
-//       agent-scope atomic add on the team's counter; each wait polls it
-//       with agent-scope loads and gives up after spin_limit polls, setting
-//       *err and returning (so a launch that cannot meet never hangs).
-//       counters: device uint32[grid / team * 64] (zeroed by the caller);
+//       agent-scope atomic add on the team's counter (mode 2: first on one
+//       of eight sub-counters); each wait polls it with agent-scope loads
+//       (mode 0: acquire loads; modes 1, 2: relaxed loads, then one acquire
+//       fence) and gives up after spin_limit polls, setting *err and
+//       returning (so a launch that cannot meet never hangs).  Mode 2
+//       needs team % 8 == 0.
+//       counters: device uint32[grid / team * 9 * 64] (zeroed by the caller);
 //       err: device uint32 (zeroed by the caller).
 // Each returns the hipError_t of its launch (0 = success) and -1 on an
 // argument error (NULL pointer, a size not a multiple of 16, grid < 1 or
@@ -126,20 +129,43 @@ __global__ __launch_bounds__(kT) void k_fma(float* out, int iters) {
 }
 
 // Teams are strided: workgroup b belongs to team b % n_teams, and its rank
-// among the team is b / n_teams.  Counters sit 256 bytes apart.
+// among the team is b / n_teams.  Counters sit 256 bytes apart; a team's
+// eight sub-counters (mode 2) follow its counter, 256 bytes apart too.
+//   mode 0: arrival = release add on the team counter; each poll is an
+//           acquire load (every poll invalidates the XCD's L2);
+//   mode 1: the same arrival; relaxed polls, then one acquire fence;
+//   mode 2: mode 1 with two-level arrival: rank r adds to sub-counter r % 8
+//           (acquire-release), and the last of each sub-counter's arrivals
+//           adds to the team counter, so at most team / 8 + 8 adds meet on
+//           any one address.
 __global__ __launch_bounds__(kT) void k_barrier(unsigned* counters, unsigned* err, int n_bar,
-                                                int team, unsigned spin_limit) {
+                                                int team, unsigned spin_limit, int mode) {
     const unsigned n_teams = gridDim.x / (unsigned)team;
-    unsigned* c = counters + (blockIdx.x % n_teams) * 64u;
+    const unsigned tm = blockIdx.x % n_teams, rank = blockIdx.x / n_teams;
+    unsigned* c = counters + tm * 9u * 64u;
+    unsigned* sub = c + 64u * (1u + rank % 8u);
+    const unsigned per_sub = (unsigned)team / 8u;
     __shared__ unsigned bad;
     for (int b = 1; b <= n_bar; ++b) {
         __syncthreads();
         if (threadIdx.x == 0) {
             bad = 0;
-            __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-            const unsigned target = (unsigned)b * (unsigned)team;
+            unsigned target = (unsigned)b * (unsigned)team;
+            if (mode == 2) {
+                const unsigned old =
+                    __hip_atomic_fetch_add(sub, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+                if (old + 1u == (unsigned)b * per_sub)
+                    __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                target = (unsigned)b * 8u;
+            } else {
+                __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            }
             unsigned spins = 0;
-            while (__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            for (;;) {
+                const unsigned v = mode == 0
+                                       ? __hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT)
+                                       : __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (v >= target) break;
                 if (++spins > spin_limit ||
                     __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
                     __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -148,6 +174,7 @@ __global__ __launch_bounds__(kT) void k_barrier(unsigned* counters, unsigned* er
                 }
                 __builtin_amdgcn_s_sleep(1);
             }
+            if (mode != 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
         __syncthreads();
         if (bad) return;
@@ -179,10 +206,11 @@ int probe_copy(const void* src, void* dst, size_t bytes, int grid, hipStream_t s
 }
 
 int probe_barrier(unsigned* counters, unsigned* err, int n_bar, int grid, int team,
-                  unsigned spin_limit, hipStream_t stream) {
-    if (!counters || !err || n_bar < 1 || grid < 1 || team < 1 || grid % team || spin_limit < 1)
+                  unsigned spin_limit, int mode, hipStream_t stream) {
+    if (!counters || !err || n_bar < 1 || grid < 1 || team < 1 || grid % team || spin_limit < 1 ||
+        mode < 0 || mode > 2 || (mode == 2 && team % 8))
         return -1;
-    void* args[] = {&counters, &err, &n_bar, &team, &spin_limit};
+    void* args[] = {&counters, &err, &n_bar, &team, &spin_limit, &mode};
     return (int)hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_barrier), dim3((unsigned)grid),
                                            dim3(kT), args, 0, stream);
 }

@@ -159,7 +159,7 @@ def test_single_block_is_tier_one():
 SINQ_CASES = [((256, 512), torch.float32), ((300, 1024), torch.bfloat16),
               ((64, 2056), torch.bfloat16), ((129, 4104), torch.bfloat16),
               ((1408, 2048), torch.bfloat16), ((2048, 1408), torch.bfloat16), ((5, 8), torch.float32),
-              ((96, 14336), torch.bfloat16), ((17, 8192), torch.bfloat16),
+              ((96, 14336), torch.bfloat16), ((17, 8192), torch.bfloat16), ((70, 6000), torch.bfloat16),
               ((40, 2048), torch.float32), ((33, 3000), torch.float32)]
 
 

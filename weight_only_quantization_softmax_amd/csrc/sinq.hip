@@ -931,16 +931,25 @@ hipError_t launch_pass_dt(const SinqMat* mats, const int64_t* sbeg, int nmat, in
 
 }  // namespace
 
-// NV = ceil(vectors / 256) (up to 256 threads, two workgroups per CU) while
-// that is <= 8 (bf16) or 4 (fp32), else ceil(vectors / 512) (up to 512
-// threads); NT is the
-// smallest multiple of 64 covering the row, e.g. 14336 columns -> 256
-// threads x 7 vectors.
+// Wider rows: bf16 rows of at most 8192 columns take NV = ceil(vectors / 128)
+// (up to 128 threads, four workgroups per CU); otherwise NV = ceil(vectors /
+// 256) (up to 256 threads, two workgroups per CU) while that is <= 8 (bf16)
+// or 4 (fp32), else ceil(vectors / 512) (up to 512 threads).  NT is the
+// smallest multiple of 64 covering the row, e.g. 8192 columns -> 128 threads
+// x 8 vectors, 14336 columns -> 256 threads x 7 vectors.
 SinqShape sinq_shape(int cols, int dtype) {
     const int nvec = cols / 8;
     if (cols <= (dtype == WOQ_BF16 ? 4096 : 1536)) {
         const int nvl = (nvec + 63) / 64;
         return SinqShape{256, nvl < 1 ? 1 : nvl, 1, (nvec % 64) != 0};
+    }
+    if (dtype == WOQ_BF16 && nvec <= 1024) {
+        // at most 8192 bf16 columns: two-wave workgroups of up to 8 vectors
+        // per thread (70B stack, 8192 columns: the Sinkhorn step 596 ms per
+        // pass against 630 with 256 threads x 4 vectors)
+        const int nv = (nvec + 127) / 128;
+        const int nt = ((nvec + nv - 1) / nv + 63) / 64 * 64;
+        return SinqShape{nt, nv, 0, nt * nv != nvec};
     }
     int nv = (nvec + 255) / 256;
     if (nv > (dtype == WOQ_BF16 ? 8 : 4)) nv = (nvec + 511) / 512;

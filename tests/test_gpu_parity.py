@@ -160,6 +160,7 @@ SINQ_CASES = [((256, 512), torch.float32), ((300, 1024), torch.bfloat16),
               ((64, 2056), torch.bfloat16), ((129, 4104), torch.bfloat16),
               ((1408, 2048), torch.bfloat16), ((2048, 1408), torch.bfloat16), ((5, 8), torch.float32),
               ((96, 14336), torch.bfloat16), ((17, 8192), torch.bfloat16), ((70, 6000), torch.bfloat16),
+              ((31, 7000), torch.bfloat16), ((12, 5000), torch.bfloat16),
               ((40, 2048), torch.float32), ((33, 3000), torch.float32)]
 
 

@@ -414,7 +414,8 @@ def barrier_us(lib, grid, team, mode=0, n_bar=2000, spin_limit=1 << 22):
     cooperative launch of `grid` workgroups (n_bar barriers minus one,
     HIP events); None if a wait gave up.  mode 0: every poll an acquire
     load; 1: relaxed polls and one acquire fence; 2: as 1, arrivals on eight
-    sub-counters first."""
+    sub-counters first; 3: as 1, with a release and an acquire by every
+    wave (the form that publishes data written by all waves)."""
     import torch
     stream = torch.cuda.current_stream()
     sh = ctypes_stream(stream)
@@ -506,6 +507,7 @@ def ceilings():
     res["grid_barrier_us_512wg"] = barrier_us(lib, 512, 512)
     res["grid_barrier_us_512wg_relaxed_polls"] = barrier_us(lib, 512, 512, mode=1)
     res["grid_barrier_us_512wg_two_level"] = barrier_us(lib, 512, 512, mode=2)
+    res["grid_barrier_us_512wg_every_wave"] = barrier_us(lib, 512, 512, mode=3)
     del big
     torch.cuda.synchronize()
     return res
@@ -541,7 +543,7 @@ def ceilings_sweep():
     for grid, team in ((16, 16), (32, 32), (64, 64), (256, 256), (512, 512), (1024, 1024),
                        (2048, 2048), (512, 128), (512, 64), (512, 32), (512, 8)):
         r = {"barrier_grid": grid, "team": team}
-        for mode in (0, 1, 2):
+        for mode in (0, 1, 2, 3):
             if mode == 2 and team % 8:
                 continue
             r[f"us_mode{mode}"] = barrier_us(lib, grid, team, mode=mode)

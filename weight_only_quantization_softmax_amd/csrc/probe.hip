@@ -26,10 +26,10 @@
 //       one XCD.  Each arrival is an
 //       agent-scope atomic add on the team's counter (mode 2: first on one
 //       of eight sub-counters); each wait polls it with agent-scope loads
-//       (mode 0: acquire loads; modes 1, 2: relaxed loads, then one acquire
-//       fence) and gives up after spin_limit polls, setting *err and
-//       returning (so a launch that cannot meet never hangs).  Mode 2
-//       needs team % 8 == 0.
+//       (mode 0: acquire loads; modes 1-3: relaxed loads, then one acquire
+//       fence; mode 3 adds a release and an acquire by every wave) and gives
+//       up after spin_limit polls, setting *err and returning (so a launch
+//       that cannot meet never hangs).  Mode 2 needs team % 8 == 0.
 //       counters: device uint32[grid / team * 9 * 64] (zeroed by the caller);
 //       err: device uint32 (zeroed by the caller).
 // Each returns the hipError_t of its launch (0 = success) and -1 on an
@@ -137,7 +137,13 @@ __global__ __launch_bounds__(kT) void k_fma(float* out, int iters) {
 //   mode 2: mode 1 with two-level arrival: rank r adds to sub-counter r % 8
 //           (acquire-release), and the last of each sub-counter's arrivals
 //           adds to the team counter, so at most team / 8 + 8 adds meet on
-//           any one address.
+//           any one address;
+//   mode 3: mode 1, and every wave releases at agent scope before the
+//           workgroup barrier and acquires after it.  The workgroup barrier
+//           compiles to a bare s_barrier (no wait for the other waves'
+//           stores), so one thread's release publishes only its own wave's
+//           writes: a step that hands data written by all waves to other
+//           workgroups needs this form.
 __global__ __launch_bounds__(kT) void k_barrier(unsigned* counters, unsigned* err, int n_bar,
                                                 int team, unsigned spin_limit, int mode) {
     const unsigned n_teams = gridDim.x / (unsigned)team;
@@ -147,6 +153,7 @@ __global__ __launch_bounds__(kT) void k_barrier(unsigned* counters, unsigned* er
     const unsigned per_sub = (unsigned)team / 8u;
     __shared__ unsigned bad;
     for (int b = 1; b <= n_bar; ++b) {
+        if (mode == 3) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         __syncthreads();
         if (threadIdx.x == 0) {
             bad = 0;
@@ -177,6 +184,7 @@ __global__ __launch_bounds__(kT) void k_barrier(unsigned* counters, unsigned* er
             if (mode != 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
         __syncthreads();
+        if (mode == 3) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         if (bad) return;
     }
 }
@@ -208,7 +216,7 @@ int probe_copy(const void* src, void* dst, size_t bytes, int grid, hipStream_t s
 int probe_barrier(unsigned* counters, unsigned* err, int n_bar, int grid, int team,
                   unsigned spin_limit, int mode, hipStream_t stream) {
     if (!counters || !err || n_bar < 1 || grid < 1 || team < 1 || grid % team || spin_limit < 1 ||
-        mode < 0 || mode > 2 || (mode == 2 && team % 8))
+        mode < 0 || mode > 3 || (mode == 2 && team % 8))
         return -1;
     void* args[] = {&counters, &err, &n_bar, &team, &spin_limit, &mode};
     return (int)hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_barrier), dim3((unsigned)grid),

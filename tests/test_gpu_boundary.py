@@ -31,9 +31,10 @@ def _fused():
     gu = _rm(256, 2 * 14336, 2)               # two 14336-column halves, ld = 28672
     f32 = _rm(64, 3 * 512, 3, torch.float32)  # fp32, ld = 1536
     rows = _rm(3 * 512, 1024, 4)              # [3d, d] row blocks: contiguous views
+    two = _rm(48, 2 * 8192, 6)                # 8192-column halves (two-wave workgroups), ld = 16384
     views = [qkv[:, :1024], qkv[:, 1024:2048], qkv[:, 2048:], gu[:, 14336:], f32[:, 512:1024],
-             rows[512:1024]]
-    assert not any(v.is_contiguous() for v in views[:5]) and views[5].is_contiguous()
+             two[:, 8192:], rows[512:1024]]
+    assert not any(v.is_contiguous() for v in views[:6]) and views[6].is_contiguous()
     return views, [v.contiguous() for v in views]
 
 
@@ -88,7 +89,8 @@ def _plant(m, pos, vals):
 def test_nonfinite_counts():
     """NaN and +-inf weights planted at known positions are counted exactly
     by the entropy call (bf16 histogram, fp32 max pass) and by the first
-    Sinkhorn iteration (wave form, workgroup form, fp32, a strided view); a
+    Sinkhorn iteration (wave form, workgroup form of four and of two waves,
+    fp32, a strided view); a
     row whose squares overflow fp32 without any non-finite weight adds
     nothing; a second call on the same workspace starts from zero."""
     nan, inf = float("nan"), float("inf")
@@ -100,19 +102,21 @@ def test_nonfinite_counts():
     e = _rm(32, 1024, 15)
     e[3, 0::2] = 3e38                          # finite weights whose shifted squares overflow
     e[3, 1::2] = -3e38
+    f = _rm(40, 8192, 18)                      # workgroup form, two-wave workgroups
     _plant(a, [(0, 0), (7, 1023), (299, 511)], [nan, inf, -inf])
+    _plant(f, [(0, 8191), (39, 4096), (17, 0)], [inf, nan, -inf])
     _plant(b, [(5, 14335), (95, 0)], [nan, -inf])
     _plant(c, [(1, 1), (63, 511), (20, 7), (20, 8)], [inf, nan, -inf, nan])
     _plant(d, [(0, 1), (127, 1023)], [inf, nan])
-    mats = [a, b, c, d, e]
-    planted = 3 + 2 + 4 + 2
+    mats = [a, b, c, d, e, f]
+    planted = 3 + 2 + 4 + 2 + 3
     ws = torch.empty(woq.workspace_size(_lib.OP_ENTROPY, mats), dtype=torch.uint8, device=DEV)
     out = woq.ewq_block_entropy(mats, ws=ws)
     assert woq.nonfinite_count(ws).item() == planted
     assert out["nonfinite"].item() == planted
     h = out["h_mat"].cpu().numpy()
-    assert np.all(np.isnan(h[:4])) and np.isfinite(h[4])
-    for sub, n in (([a], 3), ([b], 2), ([c], 4), ([d], 2), ([e], 0), (mats, planted)):
+    assert np.all(np.isnan(h[:4])) and np.isfinite(h[4]) and np.isnan(h[5])
+    for sub, n in (([a], 3), ([b], 2), ([c], 4), ([d], 2), ([e], 0), ([f], 3), (mats, planted)):
         wsq = torch.empty(woq.workspace_size(_lib.OP_SINQ, sub), dtype=torch.uint8, device=DEV)
         wsq.fill_(0xFF)
         woq.sinq_balance(sub, 16, ws=wsq)

@@ -243,8 +243,9 @@ def test_sinq_columns_with_large_means(dtype):
     eps * mean^2 / var."""
     w = (_rm(256, 1024, 31, torch.float32) + 2.0).to(dtype)
     w2 = (_rm(64, 14336, 33, torch.float32) - 1.5).to(dtype)     # workgroup pass
-    s, t = woq.sinq_balance([w, w2], 16)
-    for i, m in enumerate((w, w2)):
+    w3 = (_rm(48, 8192, 34, torch.float32) + 0.75).to(dtype)     # two-wave workgroups (bf16)
+    s, t = woq.sinq_balance([w, w2, w3], 16)
+    for i, m in enumerate((w, w2, w3)):
         s_ref, t_ref = oracle.sinkhorn_std(_np(m), 16)
         np.testing.assert_allclose(s[i].cpu().numpy(), s_ref, rtol=1e-4)
         np.testing.assert_allclose(t[i].cpu().numpy(), t_ref, rtol=1e-4)
@@ -252,10 +253,11 @@ def test_sinq_columns_with_large_means(dtype):
 
 
 def test_sinq_deterministic():
-    mats = [_rm(512, 2048, 9)]
+    mats = [_rm(512, 2048, 9), _rm(300, 8192, 10), _rm(200, 14336, 11)]
     a = woq.sinq_balance(mats, 16)
     b = woq.sinq_balance(mats, 16)
-    assert torch.equal(a[0][0], b[0][0]) and torch.equal(a[1][0], b[1][0])
+    for i in range(len(mats)):
+        assert torch.equal(a[0][i], b[0][i]) and torch.equal(a[1][i], b[1][i]), i
 
 
 @pytest.mark.parametrize("iters", [1, 16])
